@@ -1,0 +1,263 @@
+/*
+ * kdn_oracle.c -- plain fp64 CPU oracle of the Kalman Delta Network (KDN)
+ * layer forward pass and of its one-token decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file exists so that tests, the smoke check
+ * and the benchmark's CPU-baseline leg can check the GPU library against an
+ * obviously correct reference.  No product code path may link, load or call
+ * it, and it shares no code, header, table or helper with the GPU library.
+ *
+ * What it computes (sources: "Kalman Delta Networks: Uncertainty-aware
+ * Associative Memory", English abstract; ai-feeds.com summary, section
+ * "方法 / 关键模块" steps 1-3):
+ *
+ *   Each head carries a memory S (d_v x d_k).  The memory is the latent state
+ *   of a linear-Gaussian state-space model and every token is a noisy linear
+ *   observation of it:  v_t = S k_t + N(0, r_t I).  The transition scales the
+ *   mean by a_t and adds process noise of variance nu_t.  The rows of S share
+ *   one covariance, kept either diagonal (precision lambda, one value per key
+ *   dimension: "Diagonal KDN", online mean-field projection of each one-step
+ *   posterior) or isotropic (one precision scalar per head: "Isotropic KDN").
+ *
+ *   Per token, in this order (plain reading of predict -> update):
+ *     predict:    lambda^-   = lambda / (a^2 + nu * lambda)         (elementwise)
+ *                 P^-        = 1 / lambda^-
+ *     gain:       diagonal:  w = (P^- . k) / (sum_i k_i^2 P^-_i + r)
+ *                 isotropic: w = P^- k / (P^- |k|^2 + r)
+ *     projection: diagonal:  lambda = lambda^- + k.k / r
+ *                 isotropic: lambda = lambda^- + |k|^2 / (d_k r)
+ *     mean:       S <- a S;  u = v - S k;  S <- S + u w^T;  o = S q
+ *
+ *   The gain is the exact Kalman gain of the projected predictive prior; the
+ *   projection keeps the diagonal of the posterior precision (diagonal) or
+ *   its mean over the key dimensions (isotropic), which are the reverse-KL
+ *   optima over diagonal / isotropic Gaussians.  The read-out uses the
+ *   memory after the write.  lambda0 and S0 are the posterior at t = 0, so
+ *   token 1 starts with a prediction step.
+ *
+ * Layouts (all contiguous, head-major):
+ *   q, k  [B,H,T,d_k]    v [B,H,T,d_v]    a, nu, r [B,H,T]
+ *   lambda0 [B,H,d_k] (diagonal) or [B,H] (isotropic), NULL -> all ones
+ *   S0 [B,H,d_v,d_k] row-major, NULL -> zeros
+ *   o [B,H,T,d_v]   S_T like S0   lambda_T like lambda0
+ *   dbg_lambda_minus: NULL or [B,H,T,d_k] (diagonal) / [B,H,T] (isotropic)
+ *   dbg_w: NULL or [B,H,T,d_k]
+ * Inputs are single precision (bf16 inputs arrive already widened to float,
+ * exactly); every operation is done in double.
+ *
+ * Return value: 0 on success, negative on a rejected argument:
+ *   -1 bad sizes or variant, -2 NULL pointer, -3 a precondition on the input
+ *   values failed (need 0 < a <= 1, nu >= 0, r > 0, lambda0 > 0).
+ */
+#include <pthread.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#define KDN_ORACLE_DIAGONAL 0
+#define KDN_ORACLE_ISOTROPIC 1
+
+typedef struct {
+    int H, T, dk, dv, variant;
+    const float *q, *k, *v, *a, *nu, *r, *lambda0, *S0;
+    double *o, *S_T, *lambda_T, *dbg_lm, *dbg_w;
+    int n_heads, n_threads, tid;
+} job_t;
+
+/* One token of the filter for one head.  S is d_v x d_k row-major, lam is
+ * d_k values (diagonal) or one value (isotropic).  lm and w are d_k scratch
+ * values; on return lm holds lambda^- and w the gain key. */
+static void kdn_token(int dk, int dv, int variant, const float *qt, const float *kt,
+                      const float *vt, double a, double nu, double r, double *S,
+                      double *lam, double *lm, double *w, double *ot)
+{
+    int i, j;
+    if (variant == KDN_ORACLE_DIAGONAL) {
+        double den = r;
+        for (i = 0; i < dk; ++i) {
+            lm[i] = lam[i] / (a * a + nu * lam[i]);
+            den += (double)kt[i] * (double)kt[i] / lm[i];
+        }
+        for (i = 0; i < dk; ++i) {
+            w[i] = ((double)kt[i] / lm[i]) / den;
+            lam[i] = lm[i] + (double)kt[i] * (double)kt[i] / r;
+        }
+    } else {
+        double kk = 0.0, lmin, pmin;
+        for (i = 0; i < dk; ++i) kk += (double)kt[i] * (double)kt[i];
+        lmin = lam[0] / (a * a + nu * lam[0]);
+        pmin = 1.0 / lmin;
+        for (i = 0; i < dk; ++i) {
+            lm[i] = lmin;
+            w[i] = pmin * (double)kt[i] / (pmin * kk + r);
+        }
+        lam[0] = lmin + kk / ((double)dk * r);
+    }
+    for (j = 0; j < dv; ++j) {
+        double *row = S + (size_t)j * dk;
+        double sk = 0.0, sq = 0.0, u;
+        for (i = 0; i < dk; ++i) {
+            row[i] *= a;
+            sk += row[i] * (double)kt[i];
+        }
+        u = (double)vt[j] - sk;
+        for (i = 0; i < dk; ++i) {
+            row[i] += u * w[i];
+            sq += row[i] * (double)qt[i];
+        }
+        ot[j] = sq;
+    }
+}
+
+static void *run_heads(void *arg)
+{
+    const job_t *J = (const job_t *)arg;
+    const int dk = J->dk, dv = J->dv, T = J->T;
+    const int nl = (J->variant == KDN_ORACLE_DIAGONAL) ? dk : 1;
+    double *lm = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *w = (double *)malloc(sizeof(double) * (size_t)dk);
+    int bh, t, i;
+    for (bh = J->tid; bh < J->n_heads; bh += J->n_threads) {
+        double *S = J->S_T + (size_t)bh * dv * dk;
+        double *lam = J->lambda_T + (size_t)bh * nl;
+        for (i = 0; i < dv * dk; ++i)
+            S[i] = J->S0 ? (double)J->S0[(size_t)bh * dv * dk + i] : 0.0;
+        for (i = 0; i < nl; ++i)
+            lam[i] = J->lambda0 ? (double)J->lambda0[(size_t)bh * nl + i] : 1.0;
+        for (t = 0; t < T; ++t) {
+            size_t tok = (size_t)bh * T + t;
+            kdn_token(dk, dv, J->variant, J->q + tok * dk, J->k + tok * dk, J->v + tok * dv,
+                      (double)J->a[tok], (double)J->nu[tok], (double)J->r[tok], S, lam, lm, w,
+                      J->o + tok * dv);
+            if (J->dbg_lm)
+                for (i = 0; i < nl; ++i) J->dbg_lm[tok * nl + i] = lm[i];
+            if (J->dbg_w)
+                for (i = 0; i < dk; ++i) J->dbg_w[tok * dk + i] = w[i];
+        }
+    }
+    free(lm);
+    free(w);
+    return NULL;
+}
+
+static int check_values(size_t n_tok, size_t n_lam, const float *a, const float *nu,
+                        const float *r, const float *lambda0)
+{
+    size_t i;
+    for (i = 0; i < n_tok; ++i)
+        if (!(a[i] > 0.0f && a[i] <= 1.0f && nu[i] >= 0.0f && r[i] > 0.0f)) return -3;
+    if (lambda0)
+        for (i = 0; i < n_lam; ++i)
+            if (!(lambda0[i] > 0.0f)) return -3;
+    return 0;
+}
+
+static int run_threads(job_t *base, int n_threads)
+{
+    pthread_t *th;
+    job_t *jobs;
+    int i;
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > base->n_heads) n_threads = base->n_heads > 0 ? base->n_heads : 1;
+    th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+    jobs = (job_t *)malloc(sizeof(job_t) * (size_t)n_threads);
+    for (i = 0; i < n_threads; ++i) {
+        jobs[i] = *base;
+        jobs[i].tid = i;
+        jobs[i].n_threads = n_threads;
+    }
+    for (i = 1; i < n_threads; ++i) pthread_create(&th[i], NULL, run_heads, &jobs[i]);
+    run_heads(&jobs[0]);
+    for (i = 1; i < n_threads; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+    return 0;
+}
+
+int kdn_oracle_forward(int B, int H, int T, int dk, int dv, int variant, const float *q,
+                       const float *k, const float *v, const float *a, const float *nu,
+                       const float *r, const float *lambda0, const float *S0, double *o,
+                       double *S_T, double *lambda_T, double *dbg_lambda_minus, double *dbg_w,
+                       int n_threads)
+{
+    job_t J;
+    int rc;
+    size_t nl;
+    if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1) return -1;
+    if (variant != KDN_ORACLE_DIAGONAL && variant != KDN_ORACLE_ISOTROPIC) return -1;
+    if (!S_T || !lambda_T) return -2;
+    if (T > 0 && (!q || !k || !v || !a || !nu || !r || !o)) return -2;
+    nl = (variant == KDN_ORACLE_DIAGONAL) ? (size_t)dk : 1;
+    rc = check_values((size_t)B * H * T, (size_t)B * H * nl, a, nu, r, lambda0);
+    if (rc) return rc;
+    J.H = H; J.T = T; J.dk = dk; J.dv = dv; J.variant = variant;
+    J.q = q; J.k = k; J.v = v; J.a = a; J.nu = nu; J.r = r;
+    J.lambda0 = lambda0; J.S0 = S0;
+    J.o = o; J.S_T = S_T; J.lambda_T = lambda_T;
+    J.dbg_lm = dbg_lambda_minus; J.dbg_w = dbg_w;
+    J.n_heads = B * H; J.n_threads = n_threads; J.tid = 0;
+    return run_threads(&J, n_threads);
+}
+
+/* One decode step in place: the t-loop body above applied once to cached
+ * (S, lambda) of N sequences x H heads.  q, k [N,H,d_k]; v [N,H,d_v];
+ * a, nu, r [N,H]; S [N,H,d_v,d_k] and lambda [N,H,d_k] or [N,H] are read
+ * and overwritten; o [N,H,d_v]. */
+typedef struct {
+    int dk, dv, variant, n_states, n_threads, tid;
+    const float *q, *k, *v, *a, *nu, *r;
+    double *S, *lam, *o;
+} djob_t;
+
+static void *run_decode(void *arg)
+{
+    const djob_t *J = (const djob_t *)arg;
+    const int dk = J->dk, dv = J->dv;
+    const int nl = (J->variant == KDN_ORACLE_DIAGONAL) ? dk : 1;
+    double *lm = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *w = (double *)malloc(sizeof(double) * (size_t)dk);
+    int s;
+    for (s = J->tid; s < J->n_states; s += J->n_threads)
+        kdn_token(dk, dv, J->variant, J->q + (size_t)s * dk, J->k + (size_t)s * dk,
+                  J->v + (size_t)s * dv, (double)J->a[s], (double)J->nu[s], (double)J->r[s],
+                  J->S + (size_t)s * dv * dk, J->lam + (size_t)s * nl, lm, w,
+                  J->o + (size_t)s * dv);
+    free(lm);
+    free(w);
+    return NULL;
+}
+
+int kdn_oracle_decode_step(int N, int H, int dk, int dv, int variant, const float *q,
+                           const float *k, const float *v, const float *a, const float *nu,
+                           const float *r, double *S, double *lambda, double *o, int n_threads)
+{
+    djob_t base, *jobs;
+    pthread_t *th;
+    int i, n_states = N * H;
+    size_t s;
+    if (N < 0 || H < 0 || dk < 1 || dv < 1) return -1;
+    if (variant != KDN_ORACLE_DIAGONAL && variant != KDN_ORACLE_ISOTROPIC) return -1;
+    if (n_states == 0) return 0;
+    if (!q || !k || !v || !a || !nu || !r || !S || !lambda || !o) return -2;
+    if (check_values((size_t)n_states, 0, a, nu, r, NULL)) return -3;
+    for (s = 0; s < (size_t)n_states * ((variant == KDN_ORACLE_DIAGONAL) ? dk : 1); ++s)
+        if (!(lambda[s] > 0.0)) return -3;
+    base.dk = dk; base.dv = dv; base.variant = variant; base.n_states = n_states;
+    base.q = q; base.k = k; base.v = v; base.a = a; base.nu = nu; base.r = r;
+    base.S = S; base.lam = lambda; base.o = o;
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > n_states) n_threads = n_states;
+    th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+    jobs = (djob_t *)malloc(sizeof(djob_t) * (size_t)n_threads);
+    for (i = 0; i < n_threads; ++i) {
+        jobs[i] = base;
+        jobs[i].tid = i;
+        jobs[i].n_threads = n_threads;
+    }
+    for (i = 1; i < n_threads; ++i) pthread_create(&th[i], NULL, run_decode, &jobs[i]);
+    run_decode(&jobs[0]);
+    for (i = 1; i < n_threads; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+    return 0;
+}
