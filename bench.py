@@ -1,0 +1,234 @@
+"""Benchmark of the KDN layer forward (and decode step) on one MI355X.
+
+Default run (no flags): the diagonal KDN forward with bf16 q/k/v/a/nu/r and
+float32 state at B=8, H=16, T=4096, d_k=d_v=128, chunk 64 -- one step is one
+full layer forward over that batch (scan, gain, chunk prep, chunk state).
+Prints ONE JSON line with tokens/s (tokens = B*T positions, all 16 heads),
+the roofline of the dominant kernel timed with HIP events on the stream the
+kernels run on, the per-kernel breakdown, the decode step's bandwidth, and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+
+WL = dict(B=8, H=16, T=4096, dk=128, dv=128, chunk=64)
+KERNELS = ("scan_reduce", "scan_carry", "chunk_prep", "chunk_state")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(B, H, T, dk, dv, C):
+    """Algorithmic bytes and flops of each forward kernel (bf16 inputs)."""
+    n = B * H * T           # token-heads
+    nc = -(-T // C)
+    bh = B * H
+    e = 2                   # bf16 bytes
+    g = 3 * e               # a, nu, r per token-head
+    by = {
+        # read k and the three gates, write one float4 Moebius product per (chunk, key dim)
+        "scan_reduce": n * (dk * e + g) + bh * nc * dk * 16,
+        # read the chunk products, write chunk-boundary precisions
+        "scan_carry": bh * nc * dk * 16 + bh * (nc + 1) * dk * 4 + bh * dk * 4 * 2,
+        # read k, gates, boundary precisions; write w and T
+        "chunk_prep": n * (dk * e + g) + bh * nc * dk * 4 + n * dk * e + bh * nc * C * C * e,
+        # read q, k, v, w, a, T, S0; write o, S_T
+        "chunk_state": n * (3 * dk + dv) * e + n * e + bh * nc * C * C * e + n * dv * e
+        + 2 * bh * dv * dk * 4,
+    }
+    fl = {
+        "scan_reduce": n * dk * 12,
+        "scan_carry": bh * nc * dk * 5,
+        # gain (~8 dk), A = tril(K W^T) (C dk), T solve (~C^2/3)
+        "chunk_prep": n * (8 * dk + C * dk + C * C // 3),
+        # K S^T, S Q^T, S update (2 dk dv each), tril(Q W^T) (C dk),
+        # U = T R and tril(M) U (C dv each)
+        "chunk_state": n * (6 * dk * dv + C * dk + 2 * C * dv),
+    }
+    return by, fl
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import kalman_filter_memory_amd as kdn
+    from kdn_inputs import config_inputs
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    B, H, T, dk, dv, C = (WL[x] for x in ("B", "H", "T", "dk", "dv", "chunk"))
+    log("generating inputs")
+    inp = config_inputs(2)
+    bf = torch.bfloat16
+    t = {n: torch.from_numpy(inp[n]).to(dev, bf) for n in ("q", "k", "v", "a", "nu", "r")}
+    lam0 = torch.from_numpy(inp["lambda0"]).to(dev)
+    S0 = torch.from_numpy(inp["S0"]).to(dev)
+    d = kdn.make_desc(B, H, T, dk, dv, C, "diagonal", kdn.BF16, kdn.BF16)
+    ws = torch.empty(kdn.forward_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    out = (torch.empty((B, H, T, dv), dtype=bf, device=dev),
+           torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev),
+           torch.empty((B, H, dk), dtype=torch.float32, device=dev))
+
+    def step(events=None):
+        kdn.forward(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], lam0, S0, "diagonal", C,
+                    workspace=ws, out=out, events=events)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # per-kernel durations: events recorded between the kernels on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for row in evs:
+        step(events=row)
+    torch.cuda.synchronize()
+    kern_ms = {k: float(np.mean([row[i].elapsed_time(row[i + 1]) for row in evs]))
+               for i, k in enumerate(KERNELS)}
+    by, fl = algorithmic(B, H, T, dk, dv, C)
+    kernels = {}
+    for k in KERNELS:
+        s = kern_ms[k] * 1e-3
+        kernels[k] = {"us": round(kern_ms[k] * 1e3, 2),
+                      "GB/s": round(by[k] / s / 1e9, 1),
+                      "TFLOP/s": round(fl[k] / s / 1e12, 2)}
+    dom = max(KERNELS, key=lambda k: kern_ms[k])
+    s_dom = kern_ms[dom] * 1e-3
+    ach_gbs = by[dom] / s_dom / 1e9
+    roofline = {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": dom,
+                "mfma_frac_bf16": round(fl[dom] / s_dom / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+    res = {
+        "metric": "KDN fwd tokens/s (B8 T4096 H16 d128); % MFMA peak; decode GB/s",
+        "value": round(B * T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "diag_bf16_B8_H16_T4096_d128", "variant": "diagonal",
+                   "B": B, "H": H, "T": T, "d_k": dk, "d_v": dv, "chunk": C,
+                   "state_dtype": "f32"},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    del t, ws, out
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        res["decode"] = bench_decode(args)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, args)
+    print(json.dumps(res), flush=True)
+
+
+def bench_decode(args):
+    """Decode step at 256 sequences x 16 heads x d 128, 128 steps in place."""
+    import numpy as np
+    import torch
+
+    import kalman_filter_memory_amd as kdn
+    from kdn_inputs import config_inputs
+
+    dev = torch.device("cuda:0")
+    log("generating decode inputs")
+    dd = config_inputs(4)
+    steps, N, H, dk = dd["q"].shape
+    dv = dd["v"].shape[-1]
+    S = torch.from_numpy(dd["S0"]).to(dev)
+    lam = torch.from_numpy(dd["lambda0"]).to(dev)
+    x = {n: torch.from_numpy(dd[n]).to(dev, torch.bfloat16 if n in "qkv" else torch.float32)
+         for n in ("q", "k", "v", "a", "nu", "r")}
+    o = torch.empty((N, H, dv), dtype=torch.bfloat16, device=dev)
+
+    def one(s):
+        kdn.decode_step(x["q"][s], x["k"][s], x["v"][s], x["a"][s], x["nu"][s], x["r"][s], S,
+                        lam, "diagonal", out=o)
+
+    for s in range(4):
+        one(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        one(s)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = N * H * (2 * dv * dk * 4 + 2 * dk * 4 + (2 * dk + 2 * dv) * 2 + 3 * 4)
+    return {"workload": "decode_diag_N256_H16_d128", "steps": steps,
+            "us_per_step": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "tokens_per_s": round(N / (us * 1e-6), 1), "bytes_per_step": nbytes,
+            "timing": "128 back-to-back launches between two HIP events"}
+
+
+def cpu_baseline(inp, args):
+    """The fp64 oracle on a bounded sample of heads of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    heads = max(1, args.cpu_heads)
+    sel = [(i % WL["B"], (i * 5) % WL["H"]) for i in range(heads)]
+    sub = {n: np.stack([inp[n][b, h] for b, h in sel])[:, None] for n in
+           ("q", "k", "v", "a", "nu", "r", "lambda0", "S0")}
+    log(f"cpu baseline: oracle on {heads} heads x T={WL['T']} with {threads} threads")
+    t0 = time.perf_counter()
+    oracle.forward(sub["q"], sub["k"], sub["v"], sub["a"], sub["nu"], sub["r"], sub["lambda0"],
+                   sub["S0"], "diagonal", threads=threads)
+    sec = time.perf_counter() - t0
+    tokens = heads * WL["T"] / WL["H"]  # a token carries all H heads
+    return {"value": round(tokens / sec, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads} of {WL['B'] * WL['H']} heads, all {WL['T']} tokens each "
+                      f"({sec:.1f} s); tokens/s counts H={WL['H']} heads as one token"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards over heads with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+/*
+ * kdn.h -- C ABI of libkdn, a gfx950 (MI355X) implementation of the forward
+ * pass and the one-token decode step of the Kalman Delta Network (KDN) layer.
+ *
+ * Model (sources: "Kalman Delta Networks: Uncertainty-aware Associative
+ * Memory", English abstract; ai-feeds.com summary of the same paper, section
+ * "方法 / 关键模块", steps 1-3):
+ *   Each head keeps a memory S (d_v x d_k) read as the latent state of a
+ *   linear-Gaussian state-space model; token t is the noisy observation
+ *   v_t = S k_t + N(0, r_t).  The transition scales the memory by a_t and adds
+ *   process noise of variance qnoise_t.  The rows of S share one covariance,
+ *   approximated as diagonal (one precision per key dimension, "Diagonal
+ *   KDN") or isotropic (one precision per head, "Isotropic KDN").  Per token:
+ *     lambda^- = lambda / (a^2 + qnoise * lambda)                (predict)
+ *     w        = P^- k / (k^T P^- k + r),   P^- = 1 / lambda^-   (Kalman gain)
+ *     lambda   = lambda^- + k.k / r     (diagonal: keep the posterior diagonal)
+ *              = lambda^- + |k|^2 / (d_k r)   (isotropic: mean over key dims)
+ *     S_t      = a S_{t-1} + (v - a S_{t-1} k) w^T,   o_t = S_t q_t
+ *   The precision recurrence is the Moebius map of the 2x2 matrix
+ *   [[1 + b qnoise, b a^2], [qnoise, a^2]] (b = k_i^2 / r, or |k|^2/(d_k r)),
+ *   so it is computed with an associative scan (same pages: the uncertainty
+ *   recurrences are Moebius maps admitting log-depth associative scans).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers, contiguous, head-major:
+ *       q, k [B,H,T,d_k]   v, o [B,H,T,d_v]   a, qnoise, r [B,H,T]
+ *       lambda [B,H,d_k] (diagonal) or [B,H] (isotropic), float32
+ *       S [B,H,d_v,d_k] row-major, float32
+ *   - Element types come from the descriptor (KDN_F32 = float,
+ *     KDN_BF16 = bfloat16 stored as uint16).  State (S, lambda) is float32.
+ *   - The caller owns every buffer, including the workspace; the library
+ *     never allocates device memory, never synchronises the stream and keeps
+ *     no state between calls.  Work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the default stream) and is asynchronous.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued and reported as a kdn_status; KDN_ERR_HIP means a launch was
+ *     rejected by the HIP runtime.  Faults inside a kernel surface at the
+ *     caller's next synchronisation.  No C++ exception crosses this ABI.
+ *   - Preconditions that are not checked on the device: r > 0, 0 < a <= 1,
+ *     qnoise >= 0, lambda0 > 0, all inputs finite.
+ */
+#ifndef KDN_H
+#define KDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDN_DIAGONAL = 0, KDN_ISOTROPIC = 1 } kdn_variant;
+typedef enum { KDN_F32 = 0, KDN_BF16 = 1 } kdn_dtype;
+typedef enum {
+    KDN_OK = 0,
+    KDN_ERR_NULL = 1,        /* a required pointer is NULL */
+    KDN_ERR_SHAPE = 2,       /* negative or inconsistent sizes */
+    KDN_ERR_UNSUPPORTED = 3, /* size / dtype / chunk combination not built */
+    KDN_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace_bytes answer */
+    KDN_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+    KDN_ERR_HIP = 6          /* the HIP runtime rejected a launch */
+} kdn_status;
+
+/* Problem description.  Supported: d_k, d_v in {32, 64, 128}; chunk in
+ * {16, 32, 64} (float32 inputs with d_k = 128 need chunk <= 32: the
+ * chunk kernel's LDS budget); any T >= 0 (a last partial chunk is masked);
+ * B, H >= 0 with B*H <= 65535 for the chunked entry points.
+ * qkv_dtype is the type of q, k, v and o; gate_dtype the type of a, qnoise
+ * and r; gain_dtype the type of the gain keys w that kdn_gain writes and
+ * kdn_chunk_delta reads (must equal qkv_dtype for kdn_chunk_delta). */
+typedef struct {
+    int32_t B, H, T, d_k, d_v, chunk;
+    int32_t variant;    /* kdn_variant */
+    int32_t qkv_dtype;  /* kdn_dtype */
+    int32_t gate_dtype; /* kdn_dtype */
+    int32_t gain_dtype; /* kdn_dtype */
+} kdn_desc;
+
+/* Human-readable text of a status; never NULL. */
+const char *kdn_status_string(kdn_status s);
+
+/* Host-only check of a descriptor (no GPU call).  KDN_OK if every entry point
+ * that takes it supports it. */
+kdn_status kdn_validate(const kdn_desc *d);
+
+/* Bytes of device workspace kdn_forward needs for this descriptor (0 if the
+ * descriptor is invalid).  Host-only. */
+size_t kdn_forward_workspace_bytes(const kdn_desc *d);
+
+/* Full layer forward (predict, gain, projection, chunkwise memory write and
+ * read-out for all T tokens of all B*H heads).
+ *   lambda0: NULL -> all ones; S0: NULL -> zeros (the posterior at t = 0).
+ *   o: output [B,H,T,d_v] in qkv_dtype.
+ *   S_T, lambda_T: NULL or outputs; S_T may alias S0 and lambda_T may alias
+ *   lambda0 (read before written); o must not alias an input.
+ *   ws: device workspace of at least kdn_forward_workspace_bytes(d) bytes,
+ *   16-byte aligned; its contents on entry are ignored. */
+kdn_status kdn_forward(const kdn_desc *d, const void *q, const void *k, const void *v,
+                       const void *a, const void *qnoise, const void *r,
+                       const float *lambda0, const float *S0, void *o, float *S_T,
+                       float *lambda_T, void *ws, size_t ws_bytes, void *stream);
+
+/* kdn_forward with timing marks: events is NULL or an array of 5 hipEvent_t
+ * (entries may be NULL) created by the caller; event i is recorded on
+ * `stream` before kernel i (0 scan reduce, 1 scan carry, 2 chunk prep,
+ * 3 chunk state) and event 4 after the last one, so that a caller can time
+ * each kernel of the forward.  Otherwise identical to kdn_forward. */
+kdn_status kdn_forward_events(const kdn_desc *d, const void *q, const void *k, const void *v,
+                              const void *a, const void *qnoise, const void *r,
+                              const float *lambda0, const float *S0, void *o, float *S_T,
+                              float *lambda_T, void *ws, size_t ws_bytes, void *stream,
+                              void *const *events);
+
+/* Bytes of workspace kdn_mobius_scan needs (0 if invalid). */
+size_t kdn_mobius_scan_workspace_bytes(const kdn_desc *d);
+
+/* Precision recurrence alone: the associative scan of the per-token Moebius
+ * matrices (same pages: uncertainty recurrence as a Moebius map, associative
+ * scan of logarithmic depth).  Reads k, a, qnoise, r and lambda0 (NULL ->
+ * ones).  Writes, each optional (NULL skips it):
+ *   lambda_minus [B,H,T,d_k] (diagonal) or [B,H,T] (isotropic), float32:
+ *       the predictive precision of every token;
+ *   lambda_chunk [B,H,ceil(T/chunk)+1,d_k] (or [...,1]): the posterior
+ *       precision at every chunk boundary (index 0 = lambda0, last = lambda_T);
+ *   lambda_T [B,H,d_k] or [B,H]. */
+kdn_status kdn_mobius_scan(const kdn_desc *d, const void *k, const void *a,
+                           const void *qnoise, const void *r, const float *lambda0,
+                           float *lambda_minus, float *lambda_chunk, float *lambda_T,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Kalman gain of every token from given predictive precisions (same pages:
+ * the gain weights each residual write by accumulated evidence and
+ * observation reliability):  w = P^- k / (k^T P^- k + r),  P^- = 1/lambda^-.
+ *   lambda_minus: float32 [B,H,T,d_k] (diagonal) or [B,H,T] (isotropic).
+ *   w: output [B,H,T,d_k] in gain_dtype. */
+kdn_status kdn_gain(const kdn_desc *d, const void *k, const void *r,
+                    const float *lambda_minus, void *w, void *stream);
+
+/* Bytes of workspace kdn_chunk_delta needs (0 if invalid). */
+size_t kdn_chunk_delta_workspace_bytes(const kdn_desc *d);
+
+/* Memory write and read-out given the gain keys w (chunkwise form of
+ * S_t = a S_{t-1} + (v - a S_{t-1} k) w^T, o_t = S_t q_t; ai-feeds.com
+ * summary, section 方法 step 3: hardware-efficient chunkwise implementation).
+ * w [B,H,T,d_k] has qkv_dtype (gain_dtype must equal qkv_dtype); qnoise and r
+ * are not needed because w already carries them.
+ *   S0: NULL -> zeros.  o: [B,H,T,d_v] qkv_dtype.  S_T: NULL or output,
+ *   may alias S0.  ws: at least kdn_chunk_delta_workspace_bytes(d) bytes. */
+kdn_status kdn_chunk_delta(const kdn_desc *d, const void *q, const void *k, const void *v,
+                           const void *a, const void *w, const float *S0, void *o,
+                           float *S_T, void *ws, size_t ws_bytes, void *stream);
+
+/* One-token recurrent decode step, in place (same pages: constant-memory
+ * decoding).  d->B is the number of sequences N, d->T and d->chunk are
+ * ignored.  q, k [N,H,d_k]; v, o [N,H,d_v] (qkv_dtype); a, qnoise, r [N,H]
+ * (gate_dtype); S [N,H,d_v,d_k] and lambda [N,H,d_k] / [N,H] float32 are read
+ * and overwritten with the state after the token.  o must not alias S. */
+kdn_status kdn_decode_step(const kdn_desc *d, const void *q, const void *k, const void *v,
+                           const void *a, const void *qnoise, const void *r, float *S,
+                           float *lambda, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDN_H */

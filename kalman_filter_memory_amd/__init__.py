@@ -1,0 +1,302 @@
+"""Python binding of libkdn, the gfx950 KDN layer library (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels behind the C ABI of
+include/kdn.h; this module checks tensors, allocates outputs and workspaces
+with torch on the current device, and passes raw pointers and the current
+torch stream.  There is no fallback: if libkdn.so is missing or the tensors
+are not on a GPU, the calls raise.
+
+Functions (same names as the C entry points):
+  forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", chunk=64)
+      -> (o, S_T, lambda_T)
+  decode_step(q, k, v, a, qnoise, r, S, lam, variant="diagonal") -> o   (S, lam in place)
+  mobius_scan(k, a, qnoise, r, lambda0=None, variant=..., chunk=64) -> dict
+  gain(k, r, lambda_minus, variant=..., gain_dtype=None) -> w
+  chunk_delta(q, k, v, a, w, S0=None, chunk=64) -> (o, S_T)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkdn.so")
+
+DIAGONAL, ISOTROPIC = 0, 1
+F32, BF16 = 0, 1
+
+EXPORTS = (
+    "kdn_status_string", "kdn_validate", "kdn_forward_workspace_bytes", "kdn_forward",
+    "kdn_forward_events",
+    "kdn_mobius_scan_workspace_bytes", "kdn_mobius_scan", "kdn_gain",
+    "kdn_chunk_delta_workspace_bytes", "kdn_chunk_delta", "kdn_decode_step",
+)
+
+
+class KdnDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "B", "H", "T", "d_k", "d_v", "chunk", "variant", "qkv_dtype", "gate_dtype",
+        "gain_dtype")]
+
+
+class KdnError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkdn.so (built by kalman_filter_memory_amd.build) and declare its ABI."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise KdnError(f"{path} is not built; run `python -m kalman_filter_memory_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, S, D = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(KdnDesc)
+    I = ctypes.c_int
+    lib.kdn_status_string.argtypes = [I]
+    lib.kdn_status_string.restype = ctypes.c_char_p
+    lib.kdn_validate.argtypes = [D]
+    lib.kdn_validate.restype = I
+    for n in ("kdn_forward_workspace_bytes", "kdn_mobius_scan_workspace_bytes",
+              "kdn_chunk_delta_workspace_bytes"):
+        getattr(lib, n).argtypes = [D]
+        getattr(lib, n).restype = S
+    lib.kdn_forward.argtypes = [D] + [P] * 11 + [P, S, P]
+    lib.kdn_forward.restype = I
+    lib.kdn_forward_events.argtypes = [D] + [P] * 11 + [P, S, P, ctypes.POINTER(P)]
+    lib.kdn_forward_events.restype = I
+    lib.kdn_mobius_scan.argtypes = [D] + [P] * 8 + [P, S, P]
+    lib.kdn_mobius_scan.restype = I
+    lib.kdn_gain.argtypes = [D, P, P, P, P, P]
+    lib.kdn_gain.restype = I
+    lib.kdn_chunk_delta.argtypes = [D] + [P] * 8 + [P, S, P]
+    lib.kdn_chunk_delta.restype = I
+    lib.kdn_decode_step.argtypes = [D] + [P] * 9 + [P]
+    lib.kdn_decode_step.restype = I
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().kdn_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise KdnError(f"{what}: {status_string(code)} (kdn_status {code})")
+
+
+def _variant(v) -> int:
+    if v in (DIAGONAL, "diagonal", "diag"):
+        return DIAGONAL
+    if v in (ISOTROPIC, "isotropic", "iso"):
+        return ISOTROPIC
+    raise ValueError(f"unknown variant {v!r}")
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t}; use float32 or bfloat16")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == BF16 else torch.float32
+
+
+def _gpu(x: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not x.is_cuda:
+        raise KdnError(f"{name} must be on a GPU (no CPU path exists)")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return x
+
+
+def _ptr(x):
+    return None if x is None else x.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_desc(B, H, T, d_k, d_v, chunk, variant, qkv_dtype, gate_dtype, gain_dtype=None):
+    d = KdnDesc()
+    d.B, d.H, d.T, d.d_k, d.d_v, d.chunk = B, H, T, d_k, d_v, chunk
+    d.variant = _variant(variant)
+    d.qkv_dtype = qkv_dtype
+    d.gate_dtype = gate_dtype
+    d.gain_dtype = qkv_dtype if gain_dtype is None else gain_dtype
+    return d
+
+
+def validate(desc: KdnDesc) -> int:
+    return load_library().kdn_validate(ctypes.byref(desc))
+
+
+def forward_workspace_bytes(desc: KdnDesc) -> int:
+    return load_library().kdn_forward_workspace_bytes(ctypes.byref(desc))
+
+
+def _forward_desc(q, k, v, a, qnoise, r, variant, chunk):
+    for n, x in (("q", q), ("k", k), ("v", v), ("a", a), ("qnoise", qnoise), ("r", r)):
+        _gpu(x, n)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    if q.shape != k.shape or v.shape != (B, H, T, dv):
+        raise ValueError("q, k must be [B,H,T,d_k] and v [B,H,T,d_v]")
+    if a.shape != (B, H, T) or qnoise.shape != a.shape or r.shape != a.shape:
+        raise ValueError("a, qnoise, r must be [B,H,T]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if not (a.dtype == qnoise.dtype == r.dtype):
+        raise TypeError("a, qnoise, r must share one dtype")
+    return make_desc(B, H, T, dk, dv, chunk, variant, _dtype_code(q.dtype), _dtype_code(a.dtype))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", chunk=64,
+            workspace: torch.Tensor | None = None, out=None, events=None):
+    """KDN layer forward on the GPU.  Returns (o, S_T, lambda_T).
+
+    out: optional preallocated (o, S_T, lambda_T); events: optional list of 5
+    torch.cuda.Event (already recorded once) marking the kernel boundaries."""
+    lib = load_library()
+    d = _forward_desc(q, k, v, a, qnoise, r, variant, chunk)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    lam_shape = (B, H, dk) if d.variant == DIAGONAL else (B, H)
+    if lambda0 is not None:
+        _gpu(lambda0, "lambda0")
+        if lambda0.dtype != torch.float32 or tuple(lambda0.shape) != lam_shape:
+            raise ValueError(f"lambda0 must be float32 {lam_shape}")
+    if S0 is not None:
+        _gpu(S0, "S0")
+        if S0.dtype != torch.float32 or tuple(S0.shape) != (B, H, dv, dk):
+            raise ValueError("S0 must be float32 [B,H,d_v,d_k]")
+    dev = k.device
+    if out is not None:
+        o, S_T, lam_T = out
+    else:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        lam_T = torch.empty(lam_shape, dtype=torch.float32, device=dev)
+    need = lib.kdn_forward_workspace_bytes(ctypes.byref(d))
+    if need == 0:
+        _check(lib.kdn_validate(ctypes.byref(d)), "kdn_forward")
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    args = (ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(qnoise), _ptr(r),
+            _ptr(lambda0), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(lam_T), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream())
+    if events is None:
+        _check(lib.kdn_forward(*args), "kdn_forward")
+    else:
+        arr = (ctypes.c_void_p * 5)(*[None if e is None else e.cuda_event for e in events])
+        _check(lib.kdn_forward_events(*args, arr), "kdn_forward_events")
+    return o, S_T, lam_T
+
+
+def mobius_scan(k, a, qnoise, r, lambda0=None, variant="diagonal", chunk=64,
+                lambda_minus=True, lambda_chunk=False):
+    """Precision scan alone.  Returns dict with lambda_T and, if asked, lambda_minus
+    [B,H,T,d_k] / [B,H,T] and lambda_chunk [B,H,nc+1,d_k] / [B,H,nc+1]."""
+    lib = load_library()
+    for n, x in (("k", k), ("a", a), ("qnoise", qnoise), ("r", r)):
+        _gpu(x, n)
+    B, H, T, dk = k.shape
+    d = make_desc(B, H, T, dk, dk, chunk, variant, _dtype_code(k.dtype), _dtype_code(a.dtype))
+    diag = d.variant == DIAGONAL
+    dev = k.device
+    nc = (T + chunk - 1) // chunk
+    out = {"lambda_T": torch.empty((B, H, dk) if diag else (B, H), dtype=torch.float32,
+                                   device=dev)}
+    if lambda_minus:
+        out["lambda_minus"] = torch.empty((B, H, T, dk) if diag else (B, H, T),
+                                          dtype=torch.float32, device=dev)
+    if lambda_chunk:
+        out["lambda_chunk"] = torch.empty((B, H, nc + 1, dk) if diag else (B, H, nc + 1),
+                                          dtype=torch.float32, device=dev)
+    if lambda0 is not None:
+        _gpu(lambda0, "lambda0")
+    need = lib.kdn_mobius_scan_workspace_bytes(ctypes.byref(d))
+    if need == 0:
+        _check(3, "kdn_mobius_scan")
+    ws = _workspace(need, dev)
+    _check(lib.kdn_mobius_scan(ctypes.byref(d), _ptr(k), _ptr(a), _ptr(qnoise), _ptr(r),
+                               _ptr(lambda0), _ptr(out.get("lambda_minus")),
+                               _ptr(out.get("lambda_chunk")), _ptr(out["lambda_T"]), _ptr(ws),
+                               ws.numel(), _stream()), "kdn_mobius_scan")
+    return out
+
+
+def gain(k, r, lambda_minus, variant="diagonal", gain_dtype=None):
+    """Kalman gain keys w [B,H,T,d_k] from predictive precisions."""
+    lib = load_library()
+    _gpu(k, "k")
+    _gpu(r, "r")
+    _gpu(lambda_minus, "lambda_minus")
+    B, H, T, dk = k.shape
+    gdt = k.dtype if gain_dtype is None else gain_dtype
+    d = make_desc(B, H, T, dk, dk, 64, variant, _dtype_code(k.dtype), _dtype_code(r.dtype),
+                  _dtype_code(gdt))
+    w = torch.empty((B, H, T, dk), dtype=gdt, device=k.device)
+    _check(lib.kdn_gain(ctypes.byref(d), _ptr(k), _ptr(r), _ptr(lambda_minus), _ptr(w),
+                        _stream()), "kdn_gain")
+    return w
+
+
+def chunk_delta(q, k, v, a, w, S0=None, chunk=64):
+    """Chunkwise memory write / read-out with given gain keys w.  Returns (o, S_T)."""
+    lib = load_library()
+    for n, x in (("q", q), ("k", k), ("v", v), ("a", a), ("w", w)):
+        _gpu(x, n)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    d = make_desc(B, H, T, dk, dv, chunk, "diagonal", _dtype_code(q.dtype),
+                  _dtype_code(a.dtype), _dtype_code(w.dtype))
+    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=k.device)
+    S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=k.device)
+    need = lib.kdn_chunk_delta_workspace_bytes(ctypes.byref(d))
+    if need == 0:
+        _check(lib.kdn_validate(ctypes.byref(d)) or 3, "kdn_chunk_delta")
+    ws = _workspace(need, k.device)
+    if S0 is not None:
+        _gpu(S0, "S0")
+    _check(lib.kdn_chunk_delta(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(w),
+                               _ptr(S0), _ptr(o), _ptr(S_T), _ptr(ws), ws.numel(), _stream()),
+           "kdn_chunk_delta")
+    return o, S_T
+
+
+def decode_step(q, k, v, a, qnoise, r, S, lam, variant="diagonal", out=None):
+    """One in-place decode step on cached (S, lam).  q, k [N,H,d_k]; v [N,H,d_v];
+    a, qnoise, r [N,H]; S float32 [N,H,d_v,d_k]; lam float32 [N,H,d_k] or [N,H]."""
+    lib = load_library()
+    for n, x in (("q", q), ("k", k), ("v", v), ("a", a), ("qnoise", qnoise), ("r", r),
+                 ("S", S), ("lam", lam)):
+        _gpu(x, n)
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    if S.dtype != torch.float32 or tuple(S.shape) != (N, H, dv, dk):
+        raise ValueError("S must be float32 [N,H,d_v,d_k]")
+    d = make_desc(N, H, 1, dk, dv, 0, variant, _dtype_code(q.dtype), _dtype_code(a.dtype))
+    lam_shape = (N, H, dk) if d.variant == DIAGONAL else (N, H)
+    if lam.dtype != torch.float32 or tuple(lam.shape) != lam_shape:
+        raise ValueError(f"lam must be float32 {lam_shape}")
+    o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=k.device)
+    _check(lib.kdn_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                               _ptr(qnoise), _ptr(r), _ptr(S), _ptr(lam), _ptr(o), _stream()),
+           "kdn_decode_step")
+    return o

@@ -1,0 +1,246 @@
+// kdn_api.cpp -- the C ABI of libkdn (declared in include/kdn.h): descriptor
+// validation, workspace layout and the order in which the kernels run.
+//
+// kdn_forward runs four kernels on the caller's stream:
+//   1. scan reduce   per-chunk products of the 2x2 Moebius matrices
+//   2. scan carry    chunk-boundary precisions and lambda_T
+//   3. chunk prep    gain w of every token (from the boundary precision) and
+//                    T = (I + A)^{-1} of every chunk, all chunks in parallel
+//   4. chunk state   sequential pass per (head, d_v tile): innovations, memory
+//                    write and read-out on MFMA
+// Workspace (all offsets 256-byte aligned): Moebius aggregates, boundary
+// precisions, gain keys w, and the per-chunk T matrices.
+#include "kdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <climits>
+
+#include "kdn_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(int dtype) { return dtype == KDN_BF16 ? 2 : 4; }
+
+kdn_status check_common(const kdn_desc* d) {
+    if (!d) return KDN_ERR_NULL;
+    if (d->B < 0 || d->H < 0 || d->d_k < 0 || d->d_v < 0) return KDN_ERR_SHAPE;
+    if (d->variant != KDN_DIAGONAL && d->variant != KDN_ISOTROPIC) return KDN_ERR_UNSUPPORTED;
+    for (int t : {d->qkv_dtype, d->gate_dtype, d->gain_dtype})
+        if (t != KDN_F32 && t != KDN_BF16) return KDN_ERR_UNSUPPORTED;
+    if (!dim_ok(d->d_k) || !dim_ok(d->d_v)) return KDN_ERR_UNSUPPORTED;
+    if ((int64_t)d->B * d->H > INT32_MAX) return KDN_ERR_UNSUPPORTED;
+    return KDN_OK;
+}
+
+kdn_status check_chunked(const kdn_desc* d) {
+    kdn_status s = check_common(d);
+    if (s != KDN_OK) return s;
+    if (d->T < 0 || d->chunk < 0) return KDN_ERR_SHAPE;
+    if (d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return KDN_ERR_UNSUPPORTED;
+    if ((int64_t)d->B * d->H > 65535) return KDN_ERR_UNSUPPORTED;  // heads index grid.y
+    return KDN_OK;
+}
+
+kdn::Shape make_shape(const kdn_desc* d) {
+    kdn::Shape s;
+    s.BH = d->B * d->H;
+    s.T = d->T > 0 ? d->T : 0;
+    s.dk = d->d_k;
+    s.dv = d->d_v;
+    s.chunk = d->chunk > 0 ? d->chunk : 1;
+    s.nc = (d->T + s.chunk - 1) / s.chunk;
+    s.diag = d->variant == KDN_DIAGONAL;
+    s.qkv_bf16 = d->qkv_dtype == KDN_BF16;
+    s.gate_bf16 = d->gate_dtype == KDN_BF16;
+    s.gain_bf16 = d->gain_dtype == KDN_BF16;
+    return s;
+}
+
+struct ForwardWs {
+    size_t agg, lam_chunk, w, tm, total;
+};
+
+ForwardWs forward_ws(const kdn_desc* d) {
+    const kdn::Shape s = make_shape(d);
+    const size_t nl = s.diag ? s.dk : 1;
+    ForwardWs w;
+    w.agg = 0;
+    w.lam_chunk = w.agg + round_up((size_t)s.BH * s.nc * nl * 16);
+    w.w = w.lam_chunk + round_up((size_t)s.BH * (s.nc + 1) * nl * 4);
+    w.tm = w.w + round_up((size_t)s.BH * s.T * s.dk * esize(d->qkv_dtype));
+    w.total = w.tm + round_up((size_t)s.BH * s.nc * s.chunk * s.chunk * esize(d->qkv_dtype));
+    return w;
+}
+
+kdn_status hip_status(hipError_t e) { return e == hipSuccess ? KDN_OK : KDN_ERR_HIP; }
+
+char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kdn_status_string(kdn_status s) {
+    switch (s) {
+        case KDN_OK: return "ok";
+        case KDN_ERR_NULL: return "a required pointer is NULL";
+        case KDN_ERR_SHAPE: return "negative or inconsistent sizes";
+        case KDN_ERR_UNSUPPORTED: return "unsupported size, dtype, variant or chunk";
+        case KDN_ERR_WORKSPACE: return "workspace too small";
+        case KDN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case KDN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    }
+    return "unknown kdn_status";
+}
+
+kdn_status kdn_validate(const kdn_desc* d) {
+    kdn_status s = check_chunked(d);
+    if (s != KDN_OK) return s;
+    if (!kdn::chunk_supported(make_shape(d))) return KDN_ERR_UNSUPPORTED;
+    return KDN_OK;
+}
+
+size_t kdn_forward_workspace_bytes(const kdn_desc* d) {
+    if (kdn_validate(d) != KDN_OK) return 0;
+    return forward_ws(d).total;
+}
+
+size_t kdn_mobius_scan_workspace_bytes(const kdn_desc* d) {
+    if (check_chunked(d) != KDN_OK) return 0;
+    const ForwardWs w = forward_ws(d);
+    return w.w;  // aggregates + boundary precisions
+}
+
+kdn_status kdn_forward_events(const kdn_desc* d, const void* q, const void* k, const void* v,
+                              const void* a, const void* qnoise, const void* r,
+                              const float* lambda0, const float* S0, void* o, float* S_T,
+                              float* lambda_T, void* ws, size_t ws_bytes, void* stream,
+                              void* const* events) {
+    kdn_status st = kdn_validate(d);
+    if (st != KDN_OK) return st;
+    const kdn::Shape s = make_shape(d);
+    const ForwardWs w = forward_ws(d);
+    if (s.BH == 0) return KDN_OK;
+    if (s.T > 0 && (!q || !k || !v || !a || !qnoise || !r || !o)) return KDN_ERR_NULL;
+    if (!ws) return KDN_ERR_NULL;
+    if (ws_bytes < w.total) return KDN_ERR_WORKSPACE;
+    for (const void* p : {q, k, v, (const void*)o, (const void*)S0, (const void*)S_T, (const void*)ws})
+        if (p && !aligned16(p)) return KDN_ERR_ALIGN;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    float* agg = reinterpret_cast<float*>(at(ws, w.agg));
+    float* lc = reinterpret_cast<float*>(at(ws, w.lam_chunk));
+    void* wk = at(ws, w.w);
+    void* tm = at(ws, w.tm);
+    auto mark = [&](int i) {
+        if (events && events[i]) hipEventRecord(static_cast<hipEvent_t>(events[i]), hs);
+    };
+    mark(0);
+    hipError_t e = kdn::launch_scan_reduce(s, k, a, qnoise, r, agg, hs);
+    mark(1);
+    if (e == hipSuccess) e = kdn::launch_scan_carry(s, agg, lambda0, lc, lambda_T, hs);
+    mark(2);
+    kdn::Shape sw = s;
+    sw.gain_bf16 = s.qkv_bf16;
+    if (e == hipSuccess) e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, hs);
+    mark(3);
+    if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, a, wk, tm, S0, o, S_T, hs);
+    mark(4);
+    return hip_status(e);
+}
+
+kdn_status kdn_forward(const kdn_desc* d, const void* q, const void* k, const void* v,
+                       const void* a, const void* qnoise, const void* r, const float* lambda0,
+                       const float* S0, void* o, float* S_T, float* lambda_T, void* ws,
+                       size_t ws_bytes, void* stream) {
+    return kdn_forward_events(d, q, k, v, a, qnoise, r, lambda0, S0, o, S_T, lambda_T, ws,
+                              ws_bytes, stream, nullptr);
+}
+
+kdn_status kdn_mobius_scan(const kdn_desc* d, const void* k, const void* a, const void* qnoise,
+                           const void* r, const float* lambda0, float* lambda_minus,
+                           float* lambda_chunk, float* lambda_T, void* ws, size_t ws_bytes,
+                           void* stream) {
+    kdn_status st = check_chunked(d);
+    if (st != KDN_OK) return st;
+    const kdn::Shape s = make_shape(d);
+    const ForwardWs w = forward_ws(d);
+    if (s.BH == 0) return KDN_OK;
+    if (s.T > 0 && (!k || !a || !qnoise || !r)) return KDN_ERR_NULL;
+    if (!ws) return KDN_ERR_NULL;
+    if (ws_bytes < w.w) return KDN_ERR_WORKSPACE;
+    if (!aligned16(ws) || (k && !aligned16(k))) return KDN_ERR_ALIGN;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    float* agg = reinterpret_cast<float*>(at(ws, w.agg));
+    float* lc = lambda_chunk ? lambda_chunk : reinterpret_cast<float*>(at(ws, w.lam_chunk));
+    hipError_t e = kdn::launch_scan_reduce(s, k, a, qnoise, r, agg, hs);
+    if (e == hipSuccess) e = kdn::launch_scan_carry(s, agg, lambda0, lc, lambda_T, hs);
+    if (e == hipSuccess && lambda_minus)
+        e = kdn::launch_scan_emit(s, k, a, qnoise, r, lc, lambda_minus, hs);
+    return hip_status(e);
+}
+
+kdn_status kdn_gain(const kdn_desc* d, const void* k, const void* r, const float* lambda_minus,
+                    void* w, void* stream) {
+    kdn_status st = check_common(d);
+    if (st != KDN_OK) return st;
+    if (d->T < 0) return KDN_ERR_SHAPE;
+    const kdn::Shape s = make_shape(d);
+    if ((size_t)s.BH * s.T == 0) return KDN_OK;
+    if (!k || !r || !lambda_minus || !w) return KDN_ERR_NULL;
+    return hip_status(kdn::launch_gain(s, k, r, lambda_minus, w, static_cast<hipStream_t>(stream)));
+}
+
+size_t kdn_chunk_delta_workspace_bytes(const kdn_desc* d) {
+    if (kdn_validate(d) != KDN_OK) return 0;
+    const ForwardWs w = forward_ws(d);
+    return w.total - w.tm;
+}
+
+kdn_status kdn_chunk_delta(const kdn_desc* d, const void* q, const void* k, const void* v,
+                           const void* a, const void* w, const float* S0, void* o, float* S_T,
+                           void* ws, size_t ws_bytes, void* stream) {
+    kdn_status st = kdn_validate(d);
+    if (st != KDN_OK) return st;
+    if (d->gain_dtype != d->qkv_dtype) return KDN_ERR_UNSUPPORTED;
+    const kdn::Shape s = make_shape(d);
+    const ForwardWs fw = forward_ws(d);
+    if (s.BH == 0) return KDN_OK;
+    if (s.T > 0 && (!q || !k || !v || !a || !w || !o)) return KDN_ERR_NULL;
+    if (!ws) return KDN_ERR_NULL;
+    if (ws_bytes < fw.total - fw.tm) return KDN_ERR_WORKSPACE;
+    for (const void* p : {q, k, v, w, (const void*)o, (const void*)S0, (const void*)S_T, (const void*)ws})
+        if (p && !aligned16(p)) return KDN_ERR_ALIGN;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    void* wk = const_cast<void*>(w);  // read only when fuse_gain is false
+    hipError_t e = kdn::launch_chunk_prep(s, false, k, a, nullptr, nullptr, nullptr, wk, ws, hs);
+    if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, a, w, ws, S0, o, S_T, hs);
+    return hip_status(e);
+}
+
+kdn_status kdn_decode_step(const kdn_desc* d, const void* q, const void* k, const void* v,
+                           const void* a, const void* qnoise, const void* r, float* S,
+                           float* lambda, void* o, void* stream) {
+    kdn_status st = check_common(d);
+    if (st != KDN_OK) return st;
+    kdn::Shape s = make_shape(d);
+    s.T = 1;
+    s.nc = 1;
+    if (s.BH == 0) return KDN_OK;
+    if (!q || !k || !v || !a || !qnoise || !r || !S || !lambda || !o) return KDN_ERR_NULL;
+    if (!aligned16(S)) return KDN_ERR_ALIGN;
+    if (!kdn::decode_supported(s)) return KDN_ERR_UNSUPPORTED;
+    return hip_status(kdn::launch_decode(s, q, k, v, a, qnoise, r, S, lambda, o,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

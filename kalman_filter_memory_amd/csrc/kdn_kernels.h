@@ -1,0 +1,57 @@
+// kdn_kernels.h -- host-side launchers of the libkdn kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kdn {
+
+struct Shape {
+    int BH;  // B * H (heads, or sequences * heads for decode)
+    int T;   // tokens per head
+    int dk, dv, chunk;
+    int nc;  // ceil(T / chunk)
+    bool diag;
+    bool qkv_bf16, gate_bf16, gain_bf16;
+};
+
+// Each launcher returns hipSuccess or the launch error.  Pointers are device
+// pointers with the layouts documented in include/kdn.h.
+
+// Moebius scan, pass 1: per-chunk product of the 2x2 token matrices.
+// agg: [BH][nc][nl] float4 (nl = dk for diagonal, 1 for isotropic).
+hipError_t launch_scan_reduce(const Shape& s, const void* k, const void* a, const void* nu,
+                              const void* r, float* agg, hipStream_t st);
+// Moebius scan, pass 2: chunk-boundary precisions lam_chunk [BH][nc+1][nl] and
+// lambda_T [BH][nl] (either may be NULL) from lambda0 (NULL -> ones).
+hipError_t launch_scan_carry(const Shape& s, const float* agg, const float* lambda0,
+                             float* lam_chunk, float* lambda_T, hipStream_t st);
+// Moebius scan, pass 3: per-token predictive precision lambda_minus
+// [BH][T][nl] from the chunk-boundary values.
+hipError_t launch_scan_emit(const Shape& s, const void* k, const void* a, const void* nu,
+                            const void* r, const float* lam_chunk, float* lambda_minus,
+                            hipStream_t st);
+// Kalman gain from given predictive precisions; w [BH][T][dk] in gain dtype.
+hipError_t launch_gain(const Shape& s, const void* k, const void* r, const float* lambda_minus,
+                       void* w, hipStream_t st);
+// Per-chunk preparation: optionally the gain (from lam_chunk, written to w),
+// then A = strict_tril(K W^T * Gamma) and T = (I + A)^{-1} written to Tm
+// [BH][nc][chunk][chunk] in qkv dtype.  fuse_gain = false reads w instead.
+hipError_t launch_chunk_prep(const Shape& s, bool fuse_gain, const void* k, const void* a,
+                             const void* nu, const void* r, const float* lam_chunk, void* w,
+                             void* Tm, hipStream_t st);
+// Sequential chunk pass: memory write and read-out.
+hipError_t launch_chunk_state(const Shape& s, const void* q, const void* k, const void* v,
+                              const void* a, const void* w, const void* Tm, const float* S0,
+                              void* o, float* S_T, hipStream_t st);
+// One decode step in place.
+hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
+                         const void* a, const void* nu, const void* r, float* S, float* lam,
+                         void* o, hipStream_t st);
+
+// true if the chunk kernels are built for this (dtype, dk, dv, chunk)
+bool chunk_supported(const Shape& s);
+bool decode_supported(const Shape& s);
+
+}  // namespace kdn

@@ -1,0 +1,369 @@
+// kdn_scan.hip -- the precision (uncertainty) recurrence of the KDN layer as an
+// associative scan of 2x2 Moebius matrices, and the Kalman gain.
+//
+// Per token and per key dimension i (diagonal) or per head (isotropic), with
+// evidence b = k_i^2 / r (diagonal) or |k|^2 / (d_k r) (isotropic):
+//   lambda_t = (lambda^-_t + b),  lambda^-_t = lambda_{t-1} / (a^2 + nu lambda_{t-1})
+// which is the Moebius map of M_t = [[1 + b nu, b a^2], [nu, a^2]]
+// ("Kalman Delta Networks", English abstract: the uncertainty recurrences are
+// Moebius maps, enabling associative scans with logarithmic parallel depth).
+// A Moebius map does not change when its matrix is scaled, so products are
+// renormalised by exact powers of two to stay inside the float range.
+//
+// Three passes (reduce, carry, emit):
+//   reduce: one wave per chunk of `chunk` tokens forms the chunk's matrix
+//           product (diagonal: lane = key dimension, sequential over tokens;
+//           isotropic: lane = token, ordered wave-wide tree product);
+//   carry:  one thread per (head, key dim) applies the chunk products in order
+//           and writes the precision at every chunk boundary and lambda_T;
+//   emit:   one wave per chunk replays its tokens from the boundary value and
+//           writes every predictive precision lambda^-.
+// The gain kernel forms w = P^- k / (k^T P^- k + r) from given lambda^-.
+#include "kdn_device.h"
+#include "kdn_kernels.h"
+
+namespace kdn {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+struct M2 {
+    float a, b, c, d;  // [[a b] [c d]]
+};
+
+__device__ __forceinline__ M2 mul(const M2& x, const M2& y) {
+    return {x.a * y.a + x.b * y.c, x.a * y.b + x.b * y.d, x.c * y.a + x.d * y.c,
+            x.c * y.b + x.d * y.d};
+}
+
+// scale by the power of two that brings the largest entry into [0.5, 1)
+// (all entries are non-negative)
+__device__ __forceinline__ M2 renorm(const M2& m) {
+    const float mx = fmaxf(fmaxf(m.a, m.b), fmaxf(m.c, m.d));
+    int e;
+    frexpf(mx, &e);
+    return {ldexpf(m.a, -e), ldexpf(m.b, -e), ldexpf(m.c, -e), ldexpf(m.d, -e)};
+}
+
+__device__ __forceinline__ M2 shfl_down_m2(const M2& m, int off) {
+    return {__shfl_down(m.a, off, kWave), __shfl_down(m.b, off, kWave),
+            __shfl_down(m.c, off, kWave), __shfl_down(m.d, off, kWave)};
+}
+__device__ __forceinline__ M2 shfl_up_m2(const M2& m, int off) {
+    return {__shfl_up(m.a, off, kWave), __shfl_up(m.b, off, kWave), __shfl_up(m.c, off, kWave),
+            __shfl_up(m.d, off, kWave)};
+}
+
+__device__ __forceinline__ M2 token_matrix(float b, float a2, float nu) {
+    return {1.f + b * nu, b * a2, nu, a2};
+}
+
+__device__ __forceinline__ float apply(const M2& m, float x) {
+    return (m.a * x + m.b) / (m.c * x + m.d);
+}
+
+// key dimensions handled by one lane in the diagonal kernels
+template <int DK> struct Lanes {
+    static constexpr int IPL = DK >= 64 ? DK / 64 : 1;  // consecutive dims per lane
+    static constexpr int ACTIVE = DK / IPL;             // active lanes
+};
+
+template <typename E, int IPL>
+__device__ __forceinline__ void load_dims(const E* p, float (&x)[IPL]) {
+#pragma unroll
+    for (int j = 0; j < IPL; ++j) x[j] = to_f<E>(p[j]);
+}
+
+// ------------------------------------------------------------------ reduce
+template <typename E, int DK>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
+    const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
+    const void* __restrict__ r, bool gate_bf16, int T, int C, int NC,
+    float4* __restrict__ agg) {
+    using L = Lanes<DK>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = blockIdx.x * kWavesPerBlock + wave;
+    const size_t bh = blockIdx.y;
+    if (c >= NC || lane >= L::ACTIVE) return;
+    const int t0 = c * C, n = min(C, T - t0);
+    M2 P[L::IPL];
+#pragma unroll
+    for (int j = 0; j < L::IPL; ++j) P[j] = {1.f, 0.f, 0.f, 1.f};
+    for (int t = 0; t < n; ++t) {
+        const size_t tok = bh * T + t0 + t;
+        const float at = load_gate(a, tok, gate_bf16), nut = load_gate(nu, tok, gate_bf16);
+        const float ir = 1.f / load_gate(r, tok, gate_bf16);
+        float kv[L::IPL];
+        load_dims<E, L::IPL>(k + tok * DK + lane * L::IPL, kv);
+#pragma unroll
+        for (int j = 0; j < L::IPL; ++j) {
+            P[j] = mul(token_matrix(kv[j] * kv[j] * ir, at * at, nut), P[j]);
+            if ((t & 7) == 7) P[j] = renorm(P[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < L::IPL; ++j) {
+        const M2 m = renorm(P[j]);
+        agg[(bh * NC + c) * DK + lane * L::IPL + j] = make_float4(m.a, m.b, m.c, m.d);
+    }
+}
+
+template <typename E, int DK>
+__device__ __forceinline__ float row_sq(const E* p) {
+    float s = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < DK; ++i) {
+        const float x = to_f<E>(p[i]);
+        s += x * x;
+    }
+    return s;
+}
+
+template <typename E, int DK>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_iso_kernel(
+    const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
+    const void* __restrict__ r, bool gate_bf16, int T, int C, int NC,
+    float4* __restrict__ agg) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = blockIdx.x * kWavesPerBlock + wave;
+    const size_t bh = blockIdx.y;
+    if (c >= NC) return;
+    const int t0 = c * C, n = min(C, T - t0);
+    M2 P = {1.f, 0.f, 0.f, 1.f};
+    if (lane < n) {
+        const size_t tok = bh * T + t0 + lane;
+        const float at = load_gate(a, tok, gate_bf16), nut = load_gate(nu, tok, gate_bf16);
+        const float rt = load_gate(r, tok, gate_bf16);
+        const float b = row_sq<E, DK>(k + tok * DK) / (static_cast<float>(DK) * rt);
+        P = token_matrix(b, at * at, nut);
+    }
+    // ordered tree product: later tokens multiply on the left
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const M2 o = shfl_down_m2(P, off);
+        if ((lane & (2 * off - 1)) == 0) P = renorm(mul(o, P));
+    }
+    if (lane == 0) agg[bh * NC + c] = make_float4(P.a, P.b, P.c, P.d);
+}
+
+// ------------------------------------------------------------------- carry
+__global__ __launch_bounds__(256) void carry_kernel(const float4* __restrict__ agg,
+                                                    const float* __restrict__ lambda0, int BH,
+                                                    int NL, int NC, float* __restrict__ lam_chunk,
+                                                    float* __restrict__ lambda_T) {
+    const size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x;  // bh * NL + i
+    if (idx >= (size_t)BH * NL) return;
+    const size_t bh = idx / NL, i = idx % NL;
+    float lam = lambda0 ? lambda0[idx] : 1.f;
+    for (int c = 0; c < NC; ++c) {
+        if (lam_chunk) lam_chunk[(bh * (NC + 1) + c) * NL + i] = lam;
+        const float4 m = agg[(bh * NC + c) * NL + i];
+        lam = (m.x * lam + m.y) / (m.z * lam + m.w);
+    }
+    if (lam_chunk) lam_chunk[(bh * (NC + 1) + NC) * NL + i] = lam;
+    if (lambda_T) lambda_T[idx] = lam;
+}
+
+// -------------------------------------------------------------------- emit
+template <typename E, int DK>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void emit_diag_kernel(
+    const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
+    const void* __restrict__ r, bool gate_bf16, int T, int C, int NC,
+    const float* __restrict__ lam_chunk, float* __restrict__ lambda_minus) {
+    using L = Lanes<DK>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = blockIdx.x * kWavesPerBlock + wave;
+    const size_t bh = blockIdx.y;
+    if (c >= NC || lane >= L::ACTIVE) return;
+    const int t0 = c * C, n = min(C, T - t0);
+    float lam[L::IPL];
+#pragma unroll
+    for (int j = 0; j < L::IPL; ++j)
+        lam[j] = lam_chunk[(bh * (NC + 1) + c) * DK + lane * L::IPL + j];
+    for (int t = 0; t < n; ++t) {
+        const size_t tok = bh * T + t0 + t;
+        const float at = load_gate(a, tok, gate_bf16), nut = load_gate(nu, tok, gate_bf16);
+        const float ir = 1.f / load_gate(r, tok, gate_bf16);
+        float kv[L::IPL];
+        load_dims<E, L::IPL>(k + tok * DK + lane * L::IPL, kv);
+#pragma unroll
+        for (int j = 0; j < L::IPL; ++j) {
+            const float lm = lam[j] / (at * at + nut * lam[j]);
+            lambda_minus[tok * DK + lane * L::IPL + j] = lm;
+            lam[j] = lm + kv[j] * kv[j] * ir;
+        }
+    }
+}
+
+template <typename E, int DK>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void emit_iso_kernel(
+    const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
+    const void* __restrict__ r, bool gate_bf16, int T, int C, int NC,
+    const float* __restrict__ lam_chunk, float* __restrict__ lambda_minus) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = blockIdx.x * kWavesPerBlock + wave;
+    const size_t bh = blockIdx.y;
+    if (c >= NC) return;
+    const int t0 = c * C, n = min(C, T - t0);
+    const float lam0 = lam_chunk[bh * (NC + 1) + c];
+    M2 P = {1.f, 0.f, 0.f, 1.f};
+    float at = 1.f, nut = 0.f;
+    if (lane < n) {
+        const size_t tok = bh * T + t0 + lane;
+        at = load_gate(a, tok, gate_bf16);
+        nut = load_gate(nu, tok, gate_bf16);
+        const float rt = load_gate(r, tok, gate_bf16);
+        const float b = row_sq<E, DK>(k + tok * DK) / (static_cast<float>(DK) * rt);
+        P = token_matrix(b, at * at, nut);
+    }
+    // inclusive prefix product over the chunk's tokens (Hillis-Steele)
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const M2 o = shfl_up_m2(P, off);
+        if (lane >= off) P = renorm(mul(P, o));
+    }
+    const float lam_incl = apply(P, lam0);
+    float lam_prev = __shfl_up(lam_incl, 1, kWave);
+    if (lane == 0) lam_prev = lam0;
+    if (lane < n) lambda_minus[bh * T + t0 + lane] = lam_prev / (at * at + nut * lam_prev);
+}
+
+// -------------------------------------------------------------------- gain
+// One wave per 16 tokens; lanes over key dimensions.
+constexpr int kGainTokensPerWave = 16;
+
+template <typename E, typename W, int DK>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void gain_kernel(
+    const E* __restrict__ k, const void* __restrict__ r, bool gate_bf16, bool diag,
+    size_t n_tok, const float* __restrict__ lambda_minus, W* __restrict__ w) {
+    using L = Lanes<DK>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const size_t tok0 = (blockIdx.x * (size_t)kWavesPerBlock + wave) * kGainTokensPerWave;
+    for (int t = 0; t < kGainTokensPerWave; ++t) {
+        const size_t tok = tok0 + t;
+        if (tok >= n_tok) return;
+        const float rt = load_gate(r, tok, gate_bf16);
+        float kv[L::IPL], pk[L::IPL];
+        float part = 0.f;
+        if (lane < L::ACTIVE) {
+            load_dims<E, L::IPL>(k + tok * DK + lane * L::IPL, kv);
+#pragma unroll
+            for (int j = 0; j < L::IPL; ++j) {
+                const float lm = diag ? lambda_minus[tok * DK + lane * L::IPL + j]
+                                      : lambda_minus[tok];
+                pk[j] = kv[j] / lm;  // P^- k
+                part += kv[j] * pk[j];
+            }
+        }
+        const float den = wave_sum(part) + rt;
+        if (lane < L::ACTIVE) {
+#pragma unroll
+            for (int j = 0; j < L::IPL; ++j)
+                w[tok * DK + lane * L::IPL + j] = from_f<W>(pk[j] / den);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+template <typename E>
+hipError_t reduce_e(const Shape& s, const void* k, const void* a, const void* nu, const void* r,
+                    float* agg, hipStream_t st) {
+    const dim3 grid((s.nc + kWavesPerBlock - 1) / kWavesPerBlock, s.BH);
+    const dim3 block(64 * kWavesPerBlock);
+    float4* g = reinterpret_cast<float4*>(agg);
+    const E* kk = static_cast<const E*>(k);
+#define KDN_RED(DK_)                                                                         \
+    if (s.dk == DK_) {                                                                       \
+        if (s.diag)                                                                          \
+            hipLaunchKernelGGL((reduce_diag_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r, \
+                               s.gate_bf16, s.T, s.chunk, s.nc, g);                          \
+        else                                                                                 \
+            hipLaunchKernelGGL((reduce_iso_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r,  \
+                               s.gate_bf16, s.T, s.chunk, s.nc, g);                          \
+        return hipGetLastError();                                                            \
+    }
+    KDN_RED(32) KDN_RED(64) KDN_RED(128)
+#undef KDN_RED
+    return hipErrorInvalidValue;
+}
+
+template <typename E>
+hipError_t emit_e(const Shape& s, const void* k, const void* a, const void* nu, const void* r,
+                  const float* lam_chunk, float* lm, hipStream_t st) {
+    const dim3 grid((s.nc + kWavesPerBlock - 1) / kWavesPerBlock, s.BH);
+    const dim3 block(64 * kWavesPerBlock);
+    const E* kk = static_cast<const E*>(k);
+#define KDN_EMIT(DK_)                                                                        \
+    if (s.dk == DK_) {                                                                       \
+        if (s.diag)                                                                          \
+            hipLaunchKernelGGL((emit_diag_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r,   \
+                               s.gate_bf16, s.T, s.chunk, s.nc, lam_chunk, lm);              \
+        else                                                                                 \
+            hipLaunchKernelGGL((emit_iso_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r,    \
+                               s.gate_bf16, s.T, s.chunk, s.nc, lam_chunk, lm);              \
+        return hipGetLastError();                                                            \
+    }
+    KDN_EMIT(32) KDN_EMIT(64) KDN_EMIT(128)
+#undef KDN_EMIT
+    return hipErrorInvalidValue;
+}
+
+template <typename E, typename W>
+hipError_t gain_ew(const Shape& s, const void* k, const void* r, const float* lm, void* w,
+                   hipStream_t st) {
+    const size_t n_tok = (size_t)s.BH * s.T;
+    const size_t per_block = (size_t)kWavesPerBlock * kGainTokensPerWave;
+    const dim3 grid((unsigned)((n_tok + per_block - 1) / per_block));
+    const dim3 block(64 * kWavesPerBlock);
+    const E* kk = static_cast<const E*>(k);
+    W* ww = static_cast<W*>(w);
+#define KDN_GAIN(DK_)                                                                      \
+    if (s.dk == DK_) {                                                                     \
+        hipLaunchKernelGGL((gain_kernel<E, W, DK_>), grid, block, 0, st, kk, r, s.gate_bf16, \
+                           s.diag, n_tok, lm, ww);                                         \
+        return hipGetLastError();                                                          \
+    }
+    KDN_GAIN(32) KDN_GAIN(64) KDN_GAIN(128)
+#undef KDN_GAIN
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_scan_reduce(const Shape& s, const void* k, const void* a, const void* nu,
+                              const void* r, float* agg, hipStream_t st) {
+    if (s.BH == 0 || s.nc == 0) return hipSuccess;
+    return s.qkv_bf16 ? reduce_e<bf16_t>(s, k, a, nu, r, agg, st)
+                      : reduce_e<float>(s, k, a, nu, r, agg, st);
+}
+
+hipError_t launch_scan_carry(const Shape& s, const float* agg, const float* lambda0,
+                             float* lam_chunk, float* lambda_T, hipStream_t st) {
+    const int NL = s.diag ? s.dk : 1;
+    const size_t n = (size_t)s.BH * NL;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<const float4*>(agg), lambda0, s.BH, NL, s.nc, lam_chunk,
+                       lambda_T);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_emit(const Shape& s, const void* k, const void* a, const void* nu,
+                            const void* r, const float* lam_chunk, float* lambda_minus,
+                            hipStream_t st) {
+    if (s.BH == 0 || s.nc == 0) return hipSuccess;
+    return s.qkv_bf16 ? emit_e<bf16_t>(s, k, a, nu, r, lam_chunk, lambda_minus, st)
+                      : emit_e<float>(s, k, a, nu, r, lam_chunk, lambda_minus, st);
+}
+
+hipError_t launch_gain(const Shape& s, const void* k, const void* r, const float* lambda_minus,
+                       void* w, hipStream_t st) {
+    if (s.BH == 0 || s.T == 0) return hipSuccess;
+    if (s.qkv_bf16)
+        return s.gain_bf16 ? gain_ew<bf16_t, bf16_t>(s, k, r, lambda_minus, w, st)
+                           : gain_ew<bf16_t, float>(s, k, r, lambda_minus, w, st);
+    return s.gain_bf16 ? gain_ew<float, bf16_t>(s, k, r, lambda_minus, w, st)
+                       : gain_ew<float, float>(s, k, r, lambda_minus, w, st);
+}
+
+}  // namespace kdn

@@ -1,0 +1,125 @@
+"""Host-side checks of libkdn: the library loads, exports every function that
+include/kdn.h declares, and validates descriptors and arguments on the host
+before any GPU work (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kalman_filter_memory_amd as kdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "kdn.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kdn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kdn.LIB_PATH):
+        from kalman_filter_memory_amd import build
+        build.build()
+    return kdn.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(kdn.EXPORTS)
+
+
+def _desc(**kw):
+    base = dict(B=2, H=4, T=100, d_k=64, d_v=64, chunk=64, variant="diagonal",
+                qkv_dtype=kdn.BF16, gate_dtype=kdn.BF16)
+    base.update(kw)
+    return kdn.make_desc(base["B"], base["H"], base["T"], base["d_k"], base["d_v"],
+                         base["chunk"], base["variant"], base["qkv_dtype"], base["gate_dtype"])
+
+
+def test_validate_accepts_supported_and_rejects_the_rest(lib):
+    assert kdn.validate(_desc()) == 0
+    for dk in (32, 64, 128):
+        for dv in (32, 64, 128):
+            for c in (16, 32, 64):
+                assert kdn.validate(_desc(d_k=dk, d_v=dv, chunk=c)) == 0
+    assert kdn.validate(_desc(d_k=128, chunk=64, qkv_dtype=kdn.F32)) == 3  # LDS budget
+    assert kdn.validate(_desc(d_k=128, chunk=32, qkv_dtype=kdn.F32)) == 0
+    assert kdn.validate(_desc(d_k=48)) == 3
+    assert kdn.validate(_desc(chunk=128)) == 3
+    assert kdn.validate(_desc(chunk=24)) == 3
+    assert kdn.validate(_desc(T=-1)) == 2
+    assert kdn.validate(_desc(B=-2)) == 2
+    assert kdn.validate(_desc(B=300, H=300)) == 3  # heads index grid.y
+    d = _desc()
+    d.variant = 7
+    assert kdn.validate(d) == 3
+    d = _desc()
+    d.qkv_dtype = 5
+    assert kdn.validate(d) == 3
+    assert lib.kdn_validate(None) == 1
+
+
+def test_workspace_sizes(lib):
+    d = _desc(B=8, H=16, T=4096, d_k=128, d_v=128, chunk=64)
+    ws = kdn.forward_workspace_bytes(d)
+    bh, nc = 128, 64
+    expect = bh * nc * 128 * 16 + bh * (nc + 1) * 128 * 4 + bh * 4096 * 128 * 2 + bh * nc * 64 * 64 * 2
+    assert expect <= ws <= expect + 4 * 256
+    assert kdn.forward_workspace_bytes(_desc(d_k=48)) == 0
+    assert lib.kdn_mobius_scan_workspace_bytes(ctypes.byref(d)) < ws
+    assert lib.kdn_chunk_delta_workspace_bytes(ctypes.byref(d)) == bh * nc * 64 * 64 * 2
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = kdn.status_string(code)
+        assert isinstance(s, str) and s
+    assert "unknown" in kdn.status_string(99)
+
+
+def test_host_side_errors_return_before_any_launch(lib):
+    d = _desc()
+    fake = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x2000)
+    need = kdn.forward_workspace_bytes(d)
+    P = lambda: fake
+    # NULL descriptor
+    assert lib.kdn_forward(None, *([fake] * 11), ws, need, None) == 1
+    # missing input pointer
+    assert lib.kdn_forward(ctypes.byref(d), None, *([fake] * 10), ws, need, None) == 1
+    # workspace too small
+    assert lib.kdn_forward(ctypes.byref(d), *([fake] * 11), ws, need - 1, None) == 4
+    # misaligned q
+    assert lib.kdn_forward(ctypes.byref(d), ctypes.c_void_p(0x1002), *([fake] * 10), ws, need,
+                           None) == 5
+    # unsupported size
+    bad = _desc(d_k=40)
+    assert lib.kdn_forward(ctypes.byref(bad), *([fake] * 11), ws, need, None) == 3
+    # decode: NULL state
+    dd = _desc(T=1, chunk=0)
+    assert lib.kdn_decode_step(ctypes.byref(dd), *([fake] * 6), None, fake, fake, None) == 1
+    assert lib.kdn_decode_step(ctypes.byref(_desc(d_v=96)), *([fake] * 9), None) == 3
+    # chunk_delta needs gain dtype == qkv dtype
+    g = _desc()
+    g.gain_dtype = kdn.F32
+    assert lib.kdn_chunk_delta(ctypes.byref(g), *([fake] * 8), ws, 1 << 30, None) == 3
+    # empty problems are a no-op success without touching the GPU
+    e = _desc(B=0)
+    assert lib.kdn_forward(ctypes.byref(e), *([None] * 11), None, 0, None) == 0
+    assert lib.kdn_decode_step(ctypes.byref(_desc(B=0, T=1)), *([None] * 9), None) == 0
+    _ = P
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 4, 32)
+    g = torch.ones(1, 1, 4)
+    with pytest.raises(kdn.KdnError):
+        kdn.forward(x, x, x, g, g, g)
