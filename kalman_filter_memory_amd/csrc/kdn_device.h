@@ -45,8 +45,23 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// and meets the other waves, without waiting for outstanding global loads (a
+// full __syncthreads() also drains vmcnt, which would expose the latency of
+// loads issued early for the next chunk).
+__device__ __forceinline__ void sync_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // fast reciprocal (v_rcp_f32, about 1 ulp)
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+// hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32, about 1 ulp)
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+// value of lane `l` (uniform) of x, broadcast through a scalar register
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
 
 // ------------------------------------------------------------------- MFMA
 // 16x16 output tiles.  Operand fragments are read from row-major LDS arrays
@@ -57,6 +72,8 @@ template <typename E> struct Mma;
 
 template <> struct Mma<bf16_t> {
     static constexpr int KS = 32;  // contraction depth of one instruction
+    typedef bf16x8 frag_t;
+    typedef short4x frag16_t;
     // lane l reads 8 consecutive k at row (l % 16), k offset 8 * (l / 16)
     static __device__ __forceinline__ bf16x8 frag(const bf16_t* base, int ld, int row0, int k0,
                                                   int lane) {
@@ -66,22 +83,27 @@ template <> struct Mma<bf16_t> {
     static __device__ __forceinline__ floatx4 mma(bf16x8 a, bf16x8 b, floatx4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
-    // a 16-deep step (v_mfma_f32_16x16x16_bf16): lane l reads 4 consecutive k
-    // at row (l % 16), k offset 4 * (l / 16)
-    static __device__ __forceinline__ floatx4 mma16(const bf16_t* A, int lda, int m0,
-                                                    const bf16_t* B, int ldb, int n0, int k,
-                                                    int lane, floatx4 c) {
-        const short4x fa = *reinterpret_cast<const short4x*>(A + (m0 + (lane & 15)) * lda + k +
-                                                            4 * (lane >> 4));
-        const short4x fb = *reinterpret_cast<const short4x*>(B + (n0 + (lane & 15)) * ldb + k +
-                                                            4 * (lane >> 4));
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, fb, c, 0, 0, 0);
+    // 16-deep step (v_mfma_f32_16x16x16_bf16): lane l reads 4 consecutive k at
+    // row (l % 16), k offset 4 * (l / 16)
+    static __device__ __forceinline__ short4x frag16(const bf16_t* base, int ld, int row0,
+                                                     int k0, int lane) {
+        return *reinterpret_cast<const short4x*>(base + (row0 + (lane & 15)) * ld + k0 +
+                                                 4 * (lane >> 4));
     }
-    typedef bf16x8 frag_t;
+    static __device__ __forceinline__ floatx4 mma16(short4x a, short4x b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+    // the same fragments read from an array stored as X[k][m] (m contiguous)
+    static __device__ __forceinline__ bf16x8 fragT(const bf16_t* X, int ld, int m0, int k0,
+                                                    int lane);
+    static __device__ __forceinline__ short4x frag16T(const bf16_t* X, int ld, int m0, int k0,
+                                                       int lane);
 };
 
 template <> struct Mma<float> {
     static constexpr int KS = 4;
+    typedef float frag_t;
+    typedef float frag16_t;
     // lane l reads one k at row (l % 16), k offset (l / 16)
     static __device__ __forceinline__ float frag(const float* base, int ld, int row0, int k0,
                                                  int lane) {
@@ -90,25 +112,107 @@ template <> struct Mma<float> {
     static __device__ __forceinline__ floatx4 mma(float a, float b, floatx4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
-    typedef float frag_t;
+    static __device__ __forceinline__ float frag16(const float*, int, int, int, int) {
+        return 0.f;
+    }
+    static __device__ __forceinline__ floatx4 mma16(float, float, floatx4 c) { return c; }
+    // the same fragment read from an array stored as X[k][m] (m contiguous)
+    static __device__ __forceinline__ float fragT(const float* X, int ld, int m0, int k0,
+                                                   int lane) {
+        return X[(k0 + (lane >> 4)) * ld + m0 + (lane & 15)];
+    }
+    static __device__ __forceinline__ float frag16T(const float*, int, int, int, int) {
+        return 0.f;
+    }
 };
 
-// acc += A[m0:m0+16, k0:k1] * B[n0:n0+16, k0:k1]^T  (both row-major, k contiguous;
-// k1 - k0 a multiple of 16)
+// Fragments of an operand stored with the contraction index strided: the LDS
+// array holds X[k][m] (m contiguous) and the MFMA wants, for lane l, the values
+// X[k0 + 8 (l/16) + 0..7][m0 + l%16].  ds_read_b64_tr_b16 delivers, within each
+// group of 16 lanes, element (l % 4) of the 8-byte pieces addressed by lanes
+// 4 j + (l % 16) / 4 (j = 0..3); so lane 4 j + p of group g addresses
+// X[k0 + 8 g + j][m0 + 4 p .. 4 p + 3] and receives X[k0 + 8 g + j][m0 + l%16].
+typedef __attribute__((address_space(3))) short4x lds_short4x;
+typedef short short8x __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ short4x read_tr16(const bf16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4x*)(p));
+}
+
+__device__ __forceinline__ bf16x8 Mma<bf16_t>::fragT(const bf16_t* X, int ld, int m0, int k0,
+                                                     int lane) {
+    const int g = lane >> 4, j = (lane & 15) >> 2, p = lane & 3;
+    const bf16_t* p0 = X + (k0 + 8 * g + j) * ld + m0 + 4 * p;
+    const short4x lo = read_tr16(p0);
+    const short4x hi = read_tr16(p0 + 4 * ld);
+    const short8x v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// 16-deep version: lane l gets X[k0 + 4 (l/16) + 0..3][m0 + l%16]
+__device__ __forceinline__ short4x Mma<bf16_t>::frag16T(const bf16_t* X, int ld, int m0,
+                                                        int k0, int lane) {
+    const int g = lane >> 4, j = (lane & 15) >> 2, p = lane & 3;
+    return read_tr16(X + (k0 + 4 * g + j) * ld + m0 + 4 * p);
+}
+
+// acc[bm][bn] += A[m0+16bm : +16, k0:k1] * B[n0+16bn : +16, k0:k1]^T for a BM x BN
+// block of 16x16 tiles; both operands row-major with k contiguous, k1 - k0 a
+// multiple of 16.  Each fragment read from LDS feeds BN (or BM) instructions.
+// AT / BT: the A (B) operand is stored k-major (X[k][m]) and read with
+// transposing LDS reads instead of as row-major [m][k].
+template <typename E, int BM, int BN, bool AT = false, bool BT = false>
+__device__ __forceinline__ void mma_block(floatx4 (&acc)[BM][BN], const E* A, int lda, int m0,
+                                          const E* B, int ldb, int n0, int k0, int k1,
+                                          int lane) {
+    using M = Mma<E>;
+    int k = k0;
+    for (; k + M::KS <= k1; k += M::KS) {
+        typename M::frag_t fa[BM], fb[BN];
+#pragma unroll
+        for (int i = 0; i < BM; ++i) {
+            if constexpr (AT) fa[i] = M::fragT(A, lda, m0 + 16 * i, k, lane);
+            else fa[i] = M::frag(A, lda, m0 + 16 * i, k, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < BN; ++j) {
+            if constexpr (BT) fb[j] = M::fragT(B, ldb, n0 + 16 * j, k, lane);
+            else fb[j] = M::frag(B, ldb, n0 + 16 * j, k, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < BM; ++i)
+#pragma unroll
+            for (int j = 0; j < BN; ++j) acc[i][j] = M::mma(fa[i], fb[j], acc[i][j]);
+    }
+    if constexpr (M::KS > 16) {
+        if (k < k1) {
+            typename M::frag16_t fa[BM], fb[BN];
+#pragma unroll
+            for (int i = 0; i < BM; ++i) {
+                if constexpr (AT) fa[i] = M::frag16T(A, lda, m0 + 16 * i, k, lane);
+                else fa[i] = M::frag16(A, lda, m0 + 16 * i, k, lane);
+            }
+#pragma unroll
+            for (int j = 0; j < BN; ++j) {
+                if constexpr (BT) fb[j] = M::frag16T(B, ldb, n0 + 16 * j, k, lane);
+                else fb[j] = M::frag16(B, ldb, n0 + 16 * j, k, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < BM; ++i)
+#pragma unroll
+                for (int j = 0; j < BN; ++j) acc[i][j] = M::mma16(fa[i], fb[j], acc[i][j]);
+        }
+    }
+}
+
+// acc += A[m0:m0+16, k0:k1] * B[n0:n0+16, k0:k1]^T  (a single tile)
 template <typename E>
 __device__ __forceinline__ floatx4 mma_tile(floatx4 acc, const E* A, int lda, int m0,
                                             const E* B, int ldb, int n0, int k0, int k1,
                                             int lane) {
-    int k = k0;
-    for (; k + Mma<E>::KS <= k1; k += Mma<E>::KS) {
-        auto fa = Mma<E>::frag(A, lda, m0, k, lane);
-        auto fb = Mma<E>::frag(B, ldb, n0, k, lane);
-        acc = Mma<E>::mma(fa, fb, acc);
-    }
-    if constexpr (Mma<E>::KS > 16) {
-        if (k < k1) acc = Mma<E>::mma16(A, lda, m0, B, ldb, n0, k, lane, acc);
-    }
-    return acc;
+    floatx4 a[1][1] = {{acc}};
+    mma_block<E, 1, 1>(a, A, lda, m0, B, ldb, n0, k0, k1, lane);
+    return a[0][0];
 }
 
 // element e of a 16x16 C tile held by `lane`: row / column inside the tile

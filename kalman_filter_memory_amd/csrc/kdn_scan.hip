@@ -70,41 +70,83 @@ template <int DK> struct Lanes {
 
 template <typename E, int IPL>
 __device__ __forceinline__ void load_dims(const E* p, float (&x)[IPL]) {
+    if constexpr (IPL == 2 && sizeof(E) == 2) {  // one 4-byte load for a bf16 pair
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+        x[0] = __uint_as_float(u << 16);
+        x[1] = __uint_as_float(u & 0xFFFF0000u);
+    } else {
 #pragma unroll
-    for (int j = 0; j < IPL; ++j) x[j] = to_f<E>(p[j]);
+        for (int j = 0; j < IPL; ++j) x[j] = to_f<E>(p[j]);
+    }
 }
 
 // ------------------------------------------------------------------ reduce
-template <typename E, int DK>
+// One token's matrix factors as M = U_b P with P = [[1, 0], [nu, a^2]] and
+// U_b = [[1, b], [0, 1]], so  M X = [[x11 + b y1, x12 + b y2], [y1, y2]]  with
+// (y1, y2) = nu (x11, x12) + a^2 (x21, x22): six multiply-adds per step.
+__device__ __forceinline__ M2 step(const M2& x, float b, float a2, float nu) {
+    const float y1 = fmaf(nu, x.a, a2 * x.c);
+    const float y2 = fmaf(nu, x.b, a2 * x.d);
+    return {fmaf(b, y1, x.a), fmaf(b, y2, x.b), y1, y2};
+}
+
+// one chunk per wave, lanes over key dims; per-token scalars are computed once
+// by lane t and broadcast through scalar registers
+template <typename E, int DK, int C>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
     const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
-    const void* __restrict__ r, bool gate_bf16, int T, int C, int NC,
-    float4* __restrict__ agg) {
+    const void* __restrict__ r, bool gate_bf16, int T, int NC, float4* __restrict__ agg) {
     using L = Lanes<DK>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = blockIdx.x * kWavesPerBlock + wave;
     const size_t bh = blockIdx.y;
-    if (c >= NC || lane >= L::ACTIVE) return;
+    if (c >= NC) return;
     const int t0 = c * C, n = min(C, T - t0);
+    // lane t: gates of token t (padding: the identity, a = 1, nu = 0, 1/r = 0)
+    float ga2 = 1.f, gnu = 0.f, gir = 0.f;
+    {
+        const size_t tok = bh * T + t0 + min(lane, n - 1);
+        const float at = load_gate(a, tok, gate_bf16);
+        const float nut = load_gate(nu, tok, gate_bf16);
+        const float rt = load_gate(r, tok, gate_bf16);
+        if (lane < n) {
+            ga2 = at * at;
+            gnu = nut;
+            gir = 1.f / rt;
+        }
+    }
+    // keys of up to 32 tokens for this lane's dims are loaded before their products
+    constexpr int TB = C < 32 ? C : 32;
+    const bool act = lane < L::ACTIVE;
     M2 P[L::IPL];
 #pragma unroll
     for (int j = 0; j < L::IPL; ++j) P[j] = {1.f, 0.f, 0.f, 1.f};
-    for (int t = 0; t < n; ++t) {
-        const size_t tok = bh * T + t0 + t;
-        const float at = load_gate(a, tok, gate_bf16), nut = load_gate(nu, tok, gate_bf16);
-        const float ir = 1.f / load_gate(r, tok, gate_bf16);
-        float kv[L::IPL];
-        load_dims<E, L::IPL>(k + tok * DK + lane * L::IPL, kv);
+#pragma unroll 1
+    for (int tb = 0; tb < C; tb += TB) {
+        float kv[TB][L::IPL];
 #pragma unroll
-        for (int j = 0; j < L::IPL; ++j) {
-            P[j] = mul(token_matrix(kv[j] * kv[j] * ir, at * at, nut), P[j]);
-            if ((t & 7) == 7) P[j] = renorm(P[j]);
+        for (int u = 0; u < TB; ++u) {
+            const size_t tok = bh * T + t0 + min(tb + u, n - 1);
+            if (act) load_dims<E, L::IPL>(k + tok * DK + lane * L::IPL, kv[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            const int t = tb + u;
+            const float a2 = lane_value(ga2, t), nut = lane_value(gnu, t), ir = lane_value(gir, t);
+#pragma unroll
+            for (int j = 0; j < L::IPL; ++j)
+                P[j] = step(P[j], kv[u][j] * kv[u][j] * ir, a2, nut);
+            if ((t & 7) == 7)
+#pragma unroll
+                for (int j = 0; j < L::IPL; ++j) P[j] = renorm(P[j]);
         }
     }
+    if (act) {
 #pragma unroll
-    for (int j = 0; j < L::IPL; ++j) {
-        const M2 m = renorm(P[j]);
-        agg[(bh * NC + c) * DK + lane * L::IPL + j] = make_float4(m.a, m.b, m.c, m.d);
+        for (int j = 0; j < L::IPL; ++j) {
+            const M2 m = renorm(P[j]);
+            agg[(bh * NC + c) * DK + lane * L::IPL + j] = make_float4(m.a, m.b, m.c, m.d);
+        }
     }
 }
 
@@ -155,10 +197,19 @@ __global__ __launch_bounds__(256) void carry_kernel(const float4* __restrict__ a
     if (idx >= (size_t)BH * NL) return;
     const size_t bh = idx / NL, i = idx % NL;
     float lam = lambda0 ? lambda0[idx] : 1.f;
-    for (int c = 0; c < NC; ++c) {
-        if (lam_chunk) lam_chunk[(bh * (NC + 1) + c) * NL + i] = lam;
-        const float4 m = agg[(bh * NC + c) * NL + i];
-        lam = (m.x * lam + m.y) / (m.z * lam + m.w);
+    // chunk products are loaded 16 at a time ahead of the dependent applications
+    for (int cg = 0; cg < NC; cg += 16) {
+        float4 m[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            m[u] = (cg + u < NC) ? agg[(bh * NC + cg + u) * NL + i] : make_float4(1.f, 0.f, 0.f, 1.f);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if (cg + u < NC) {
+                if (lam_chunk) lam_chunk[(bh * (NC + 1) + cg + u) * NL + i] = lam;
+                lam = (m[u].x * lam + m[u].y) / (m[u].z * lam + m[u].w);
+            }
+        }
     }
     if (lam_chunk) lam_chunk[(bh * (NC + 1) + NC) * NL + i] = lam;
     if (lambda_T) lambda_T[idx] = lam;
@@ -272,18 +323,24 @@ hipError_t reduce_e(const Shape& s, const void* k, const void* a, const void* nu
     const dim3 block(64 * kWavesPerBlock);
     float4* g = reinterpret_cast<float4*>(agg);
     const E* kk = static_cast<const E*>(k);
-#define KDN_RED(DK_)                                                                         \
-    if (s.dk == DK_) {                                                                       \
-        if (s.diag)                                                                          \
-            hipLaunchKernelGGL((reduce_diag_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r, \
-                               s.gate_bf16, s.T, s.chunk, s.nc, g);                          \
-        else                                                                                 \
-            hipLaunchKernelGGL((reduce_iso_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r,  \
-                               s.gate_bf16, s.T, s.chunk, s.nc, g);                          \
-        return hipGetLastError();                                                            \
+#define KDN_RED_D(DK_, C_)                                                                    \
+    if (s.diag && s.dk == DK_ && s.chunk == C_) {                                             \
+        hipLaunchKernelGGL((reduce_diag_kernel<E, DK_, C_>), grid, block, 0, st, kk, a, nu, r,  \
+                           s.gate_bf16, s.T, s.nc, g);                                        \
+        return hipGetLastError();                                                             \
     }
-    KDN_RED(32) KDN_RED(64) KDN_RED(128)
-#undef KDN_RED
+#define KDN_RED_I(DK_)                                                                        \
+    if (!s.diag && s.dk == DK_) {                                                             \
+        hipLaunchKernelGGL((reduce_iso_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r,       \
+                           s.gate_bf16, s.T, s.chunk, s.nc, g);                               \
+        return hipGetLastError();                                                             \
+    }
+#define KDN_RED_DC(DK_) KDN_RED_D(DK_, 16) KDN_RED_D(DK_, 32) KDN_RED_D(DK_, 64)
+    KDN_RED_DC(32) KDN_RED_DC(64) KDN_RED_DC(128)
+    KDN_RED_I(32) KDN_RED_I(64) KDN_RED_I(128)
+#undef KDN_RED_DC
+#undef KDN_RED_I
+#undef KDN_RED_D
     return hipErrorInvalidValue;
 }
 
