@@ -89,6 +89,15 @@ def run(args):
         kdn.forward(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], lam0, S0, "diagonal", C,
                     workspace=ws, out=out, events=events)
 
+    if args.copy_calibration_mb:
+        nb = args.copy_calibration_mb << 20
+        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {nb} bytes read and written")
+        del src, dst
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -221,6 +230,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size "
+                         "kernel that HBM byte counters can be scaled against)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

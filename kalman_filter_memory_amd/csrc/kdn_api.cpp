@@ -9,7 +9,8 @@
 //   4. chunk state   sequential pass per (head, d_v tile): innovations, memory
 //                    write and read-out on MFMA
 // Workspace (all offsets 256-byte aligned): Moebius aggregates, boundary
-// precisions, gain keys w, and the per-chunk T matrices.
+// precisions, gain keys w, the per-chunk T matrices and the chunk-local
+// cumulative log2 decays.
 #include "kdn.h"
 
 #include <hip/hip_runtime.h>
@@ -67,9 +68,10 @@ kdn::Shape make_shape(const kdn_desc* d) {
 }
 
 struct ForwardWs {
-    size_t agg, lam_chunk, w, tm, total;
+    size_t agg, lam_chunk, w, tm, g, total;
 };
 
+// workspace offsets: [agg | lam_chunk | w | T | g]; kdn_chunk_delta uses [T | g]
 ForwardWs forward_ws(const kdn_desc* d) {
     const kdn::Shape s = make_shape(d);
     const size_t nl = s.diag ? s.dk : 1;
@@ -78,7 +80,8 @@ ForwardWs forward_ws(const kdn_desc* d) {
     w.lam_chunk = w.agg + round_up((size_t)s.BH * s.nc * nl * 16);
     w.w = w.lam_chunk + round_up((size_t)s.BH * (s.nc + 1) * nl * 4);
     w.tm = w.w + round_up((size_t)s.BH * s.T * s.dk * esize(d->qkv_dtype));
-    w.total = w.tm + round_up((size_t)s.BH * s.nc * s.chunk * s.chunk * esize(d->qkv_dtype));
+    w.g = w.tm + round_up((size_t)s.BH * s.nc * s.chunk * s.chunk * esize(d->qkv_dtype));
+    w.total = w.g + round_up((size_t)s.BH * s.nc * s.chunk * 4);
     return w;
 }
 
@@ -141,6 +144,7 @@ kdn_status kdn_forward_events(const kdn_desc* d, const void* q, const void* k, c
     float* lc = reinterpret_cast<float*>(at(ws, w.lam_chunk));
     void* wk = at(ws, w.w);
     void* tm = at(ws, w.tm);
+    float* g = reinterpret_cast<float*>(at(ws, w.g));
     auto mark = [&](int i) {
         if (events && events[i]) hipEventRecord(static_cast<hipEvent_t>(events[i]), hs);
     };
@@ -151,9 +155,9 @@ kdn_status kdn_forward_events(const kdn_desc* d, const void* q, const void* k, c
     mark(2);
     kdn::Shape sw = s;
     sw.gain_bf16 = s.qkv_bf16;
-    if (e == hipSuccess) e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, hs);
+    if (e == hipSuccess) e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, g, hs);
     mark(3);
-    if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, a, wk, tm, S0, o, S_T, hs);
+    if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs);
     mark(4);
     return hip_status(e);
 }
@@ -203,7 +207,7 @@ kdn_status kdn_gain(const kdn_desc* d, const void* k, const void* r, const float
 size_t kdn_chunk_delta_workspace_bytes(const kdn_desc* d) {
     if (kdn_validate(d) != KDN_OK) return 0;
     const ForwardWs w = forward_ws(d);
-    return w.total - w.tm;
+    return w.total - w.tm;  // T and g
 }
 
 kdn_status kdn_chunk_delta(const kdn_desc* d, const void* q, const void* k, const void* v,
@@ -222,8 +226,10 @@ kdn_status kdn_chunk_delta(const kdn_desc* d, const void* q, const void* k, cons
         if (p && !aligned16(p)) return KDN_ERR_ALIGN;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     void* wk = const_cast<void*>(w);  // read only when fuse_gain is false
-    hipError_t e = kdn::launch_chunk_prep(s, false, k, a, nullptr, nullptr, nullptr, wk, ws, hs);
-    if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, a, w, ws, S0, o, S_T, hs);
+    float* g = reinterpret_cast<float*>(at(ws, fw.g - fw.tm));
+    hipError_t e =
+        kdn::launch_chunk_prep(s, false, k, a, nullptr, nullptr, nullptr, wk, ws, g, hs);
+    if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, g, w, ws, S0, o, S_T, hs);
     return hip_status(e);
 }
 

@@ -51,10 +51,7 @@ __device__ __forceinline__ void store4<float>(float* p, float x0, float x1, floa
 template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float x0, float x1, float x2,
                                                float x3) {
-    uint2 u;
-    u.x = static_cast<uint32_t>(f2bf(x0)) | (static_cast<uint32_t>(f2bf(x1)) << 16);
-    u.y = static_cast<uint32_t>(f2bf(x2)) | (static_cast<uint32_t>(f2bf(x3)) << 16);
-    *reinterpret_cast<uint2*>(p) = u;
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16(x0, x1), pack_bf16(x2, x3));
 }
 
 template <typename E> __device__ __forceinline__ void load4(const E* p, float (&x)[4]);
@@ -110,39 +107,64 @@ __device__ __forceinline__ void stage_rows(E* dst, int sld, const E* src, size_t
 
 template <typename E, int DK, int C> struct PrepLds {
     static constexpr int PAD = Vec16<E>::N;
-    static constexpr int LDK = DK + PAD, LDA = C + 4, LDP = DK + 4;
+    static constexpr int LDK = DK + PAD, LDA = C + 4;
     static constexpr int NT = C / 16;
-    static constexpr int FSZ = (C * LDP > 2 * C * LDA) ? C * LDP : 2 * C * LDA;
-    static constexpr int ZSZ = (NT > 1 ? NT - 1 : 1) * 256;
+    static constexpr int NWALK = DK >= 64 ? DK / 64 : 1;  // waves of the precision walk
     static constexpr int BYTES =
-        2 * C * LDK * (int)sizeof(E) + (FSZ + 2 * C + ZSZ) * (int)sizeof(float);
+        2 * C * LDK * (int)sizeof(E) + (C * LDA + NWALK * C + 2 * C) * (int)sizeof(float);
+    // block-row scratch of the solve lives in the K buffer once A is formed
+    static_assert((NT > 1 ? NT - 1 : 1) * 256 * 4 <= C * LDK * (int)sizeof(E), "scratch");
 };
+
+// Sum over the 64 lanes of v[t] for every t: a transposing butterfly; on return
+// lane l holds the total of v[l].  63 exchanges instead of 64 full reductions.
+template <int H>
+__device__ __forceinline__ void transpose_sum_step(float (&v)[64], int lane) {
+    const bool upper = (lane & H) != 0;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+        const float keep = upper ? v[j + H] : v[j];
+        const float send = upper ? v[j] : v[j + H];
+        v[j] = keep + __shfl_xor(send, H, kWave);
+    }
+}
+__device__ __forceinline__ float transpose_sum64(float (&v)[64], int lane) {
+    transpose_sum_step<32>(v, lane);
+    transpose_sum_step<16>(v, lane);
+    transpose_sum_step<8>(v, lane);
+    transpose_sum_step<4>(v, lane);
+    transpose_sum_step<2>(v, lane);
+    transpose_sum_step<1>(v, lane);
+    return v[0];
+}
 
 // ------------------------------------------------------------ prep kernel
 // One workgroup (4 waves) per chunk.
-//   gain (fuse_gain): from the chunk-boundary precision, the predictive
-//     precision of every (token, key dim) by the step recurrence (diagonal:
-//     one lane per key dim, token scalars broadcast from the lane that loaded
-//     them; isotropic: one scalar chain), P^- k into LDS, the per-token
-//     denominator k^T P^- k + r (four lanes per token, a quarter of the key
-//     dims each), then w = P^- k / (k^T P^- k + r).
-//   A = strict_tril(K W^T * Gamma) on MFMA, T = (I + A)^{-1} in fp32:
-//     16x16 diagonal blocks by forward substitution (one lane per column),
-//     then block rows T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj with fp32 MFMA.
+//   gain (fuse_gain), diagonal: from the chunk-boundary precision each lane of
+//     the walk waves follows one key dimension through the chunk (predictive
+//     precision by the step recurrence, token scalars broadcast from the lane
+//     that loaded them), keeping P^- k of every token in registers; the
+//     per-token denominators k^T P^- k + r come from a transposing butterfly
+//     across lanes; then w = P^- k / (k^T P^- k + r).  Isotropic: |k|^2 per
+//     token, one scalar chain, w = k / (|k|^2 + r lambda^-).
+//   A = strict_tril(K W^T * Gamma) on MFMA and T = (I + A)^{-1} in fp32, in
+//     place: 16x16 diagonal blocks by forward substitution (one lane per
+//     column), then block rows T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA.
 template <typename E, int DK, int C>
 __global__ __launch_bounds__(kThreads) void prep_kernel(
     const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
     const void* __restrict__ r, bool gate_bf16, bool diag, bool fuse_gain,
-    const float* __restrict__ lam_chunk, E* __restrict__ w, E* __restrict__ Tm, int T, int NC) {
+    const float* __restrict__ lam_chunk, E* __restrict__ w, E* __restrict__ Tm,
+    float* __restrict__ gout, int T, int NC) {
     using L = PrepLds<E, DK, C>;
-    constexpr int LDK = L::LDK, LDA = L::LDA, LDP = L::LDP, NT = L::NT;
+    constexpr int LDK = L::LDK, LDA = L::LDA, NT = L::NT, NWALK = L::NWALK;
     constexpr int V = Vec16<E>::N, VPR = DK / V;
     __shared__ __align__(16) E sK[C * LDK];
     __shared__ __align__(16) E sW[C * LDK];
-    __shared__ __align__(16) float sF[L::FSZ];  // P^- k [C][LDP], later A and T [C][LDA]
+    __shared__ __align__(16) float sAT[C * LDA];  // A, overwritten in place by T
+    __shared__ __align__(16) float spart[NWALK * C];
     __shared__ __align__(16) float sden[C];
     __shared__ __align__(16) float sg[C];
-    __shared__ __align__(16) float sZ[L::ZSZ];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh = blockIdx.y;
@@ -174,44 +196,46 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
 
     if (fuse_gain) {
         if (diag) {
-            // predictive precision, sequential in t, one lane per key dim;
-            // stores P^- k = k (a^2 + nu lambda) / lambda
-            if (tid < DK) {
-                float lam = lam_chunk[(bh * (NC + 1) + c) * DK + tid];
-#pragma unroll 8
+            const int i = 64 * wave + lane;
+            const bool walker = wave < NWALK && i < DK;
+            float P[C];
+            if (wave < NWALK) {
+                float lam = walker ? lam_chunk[(bh * (NC + 1) + c) * DK + i] : 1.f;
+#pragma unroll
                 for (int t = 0; t < C; ++t) {
                     const float a2 = lane_value(ga2, t), nut = lane_value(gnu, t);
                     const float ir = lane_value(gir, t);
-                    const float kv = to_f<E>(sK[t * LDK + tid]);
+                    const float kv = walker ? to_f<E>(sK[t * LDK + i]) : 0.f;
                     const float d = fmaf(nut, lam, a2);
-                    sF[t * LDP + tid] = kv * d * rcp(lam);
+                    P[t] = kv * d * rcp(lam);  // P^- k
                     const float lm = lam * rcp(d);
                     lam = fmaf(kv * kv, ir, lm);
                 }
-            }
-            sync_lds();
-            // denominators: four lanes per token, a quarter of the key dims each
-            {
-                constexpr int Q = DK / 4;
-                const int t = wave * 16 + (lane >> 2), qd = lane & 3;
-                float part = 0.f;
-                if (t < C) {
+                float v[64];
 #pragma unroll
-                    for (int m = 0; m < Q; m += 4) {
-                        const float4 pv = *reinterpret_cast<const float4*>(sF + t * LDP + qd * Q + m);
-                        float kv[4];
-                        load4<E>(sK + t * LDK + qd * Q + m, kv);
-                        part += kv[0] * pv.x + kv[1] * pv.y + kv[2] * pv.z + kv[3] * pv.w;
-                    }
-                }
-                part += __shfl_xor(part, 1, kWave);
-                part += __shfl_xor(part, 2, kWave);
-                if (t < C && qd == 0) sden[t] = part;
+                for (int t = 0; t < 64; ++t)
+                    v[t] = (t < C && walker) ? to_f<E>(sK[t * LDK + i]) * P[t] : 0.f;
+                const float part = transpose_sum64(v, lane);
+                if (lane < C) spart[wave * C + lane] = part;
             }
             sync_lds();
-            if (tid < C) sden[tid] = 1.f / (sden[tid] + gr);  // wave 0: lane t holds r_t
+            if (tid < C) {  // wave 0: lane t holds r_t
+                float sum = gr;
+#pragma unroll
+                for (int wv = 0; wv < NWALK; ++wv) sum += spart[wv * C + tid];
+                sden[tid] = 1.f / sum;
+            }
+            sync_lds();
+            if (walker) {
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    const E wt = from_f<E>(P[t] * sden[t]);
+                    sW[t * LDK + i] = wt;
+                    if (t < n) w[(row0 + t) * DK + i] = wt;
+                }
+            }
         } else {
-            // |k|^2 per token, then one scalar chain: w = k / (|k|^2 + r lambda^-)
+            // |k|^2 per token (four lanes per token), then one scalar chain
             {
                 constexpr int Q = DK / 4;
                 const int t = wave * 16 + (lane >> 2), qd = lane & 3;
@@ -241,31 +265,29 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
                 }
                 if (lane < C) sden[lane] = den_l;
             }
-        }
-        sync_lds();
-        for (int e = tid; e < C * VPR; e += kThreads) {
-            const int t = e / VPR, i0 = (e % VPR) * V;
-            E out[V];
-            const float dn = sden[t];
+            sync_lds();
+            for (int e = tid; e < C * VPR; e += kThreads) {
+                const int t = e / VPR, i0 = (e % VPR) * V;
+                E out[V];
+                const float dn = sden[t];
 #pragma unroll
-            for (int j = 0; j < V; ++j) {
-                const float pk = diag ? sF[t * LDP + i0 + j] : to_f<E>(sK[t * LDK + i0 + j]);
-                out[j] = from_f<E>(pk * dn);
+                for (int j = 0; j < V; ++j) out[j] = from_f<E>(to_f<E>(sK[t * LDK + i0 + j]) * dn);
+                const uint4 u = *reinterpret_cast<const uint4*>(out);
+                *reinterpret_cast<uint4*>(sW + t * LDK + i0) = u;
+                if (t < n) *reinterpret_cast<uint4*>(w + (row0 + t) * DK + i0) = u;
             }
-            const uint4 u = *reinterpret_cast<const uint4*>(out);
-            *reinterpret_cast<uint4*>(sW + t * LDK + i0) = u;
-            if (t < n) *reinterpret_cast<uint4*>(w + (row0 + t) * DK + i0) = u;
         }
     }
     if (wave == 0) {
         const float g = wave_incl_sum(lane < C ? log2_hw(ga) : 0.f);
-        if (lane < C) sg[lane] = g;
+        if (lane < C) {
+            sg[lane] = g;
+            gout[(bh * NC + c) * C + lane] = g;  // for the state pass
+        }
     }
     sync_lds();
 
-    // A = strict_tril(K W^T * Gamma) in fp32; T zero-initialised
-    float* sA = sF;
-    float* sT = sF + C * LDA;
+    // A = strict_tril(K W^T * Gamma) in fp32 (zero on and above the diagonal)
     for (int id = wave; id < NT * NT; id += 4) {
         const int tb = id / NT, sb = id % NT;
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -273,13 +295,13 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = 16 * tb + c_row(lane, e), s = 16 * sb + c_col(lane);
-            sA[t * LDA + s] = (s < t) ? exp2_hw(sg[t] - sg[s]) * acc[e] : 0.f;
+            sAT[t * LDA + s] = (s < t) ? exp2_hw(sg[t] - sg[s]) * acc[e] : 0.f;
         }
     }
-    for (int e = tid; e < C * LDA; e += kThreads) sT[e] = 0.f;
     sync_lds();
 
-    // diagonal 16x16 blocks: forward substitution, one lane per column
+    // diagonal 16x16 blocks, in place: forward substitution, one lane per column
+    // (row t of A is read before row t of T is written)
     if (wave < NT && lane < 16) {
         const int b0 = 16 * wave;
         float x[16];
@@ -287,20 +309,21 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
         for (int t = 0; t < 16; ++t) {
             float acc = (t == lane) ? 1.f : 0.f;
 #pragma unroll
-            for (int s = 0; s < t; ++s) acc -= sA[(b0 + t) * LDA + b0 + s] * x[s];
+            for (int s = 0; s < t; ++s) acc -= sAT[(b0 + t) * LDA + b0 + s] * x[s];
             x[t] = acc;
-            sT[(b0 + t) * LDA + b0 + lane] = acc;
+            sAT[(b0 + t) * LDA + b0 + lane] = acc;
         }
     }
     sync_lds();
-    // block row i: Z_j = sum_{m=j}^{i-1} A_im T_mj, then T_ij = -T_ii Z_j
-    // (16x16x16 products on fp32 MFMA; T is read k-major as the B operand)
+    // block row i: Z_j = sum_{m=j}^{i-1} A_im T_mj, then T_ij = -T_ii Z_j over A_ij
+    // (16x16x16 products on fp32 MFMA; T read k-major as the B operand)
+    float* sZ = reinterpret_cast<float*>(sK);  // K is no longer needed
     for (int i = 1; i < NT; ++i) {
         for (int j = wave; j < i; j += 4) {
             floatx4 z[1][1] = {{floatx4{0.f, 0.f, 0.f, 0.f}}};
             for (int m = j; m < i; ++m)
-                mma_block<float, 1, 1, false, true>(z, sA + 16 * m, LDA, 16 * i,
-                                                    sT + 16 * m * LDA, LDA, 16 * j, 0, 16, lane);
+                mma_block<float, 1, 1, false, true>(z, sAT + 16 * m, LDA, 16 * i,
+                                                    sAT + 16 * m * LDA, LDA, 16 * j, 0, 16, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 sZ[(j << 8) + (c_row(lane, e) << 4) + c_col(lane)] = z[0][0][e];
@@ -308,11 +331,11 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
         sync_lds();
         for (int j = wave; j < i; j += 4) {
             floatx4 tij[1][1] = {{floatx4{0.f, 0.f, 0.f, 0.f}}};
-            mma_block<float, 1, 1, false, true>(tij, sT + 16 * i, LDA, 16 * i, sZ + (j << 8), 16,
+            mma_block<float, 1, 1, false, true>(tij, sAT + 16 * i, LDA, 16 * i, sZ + (j << 8), 16,
                                                 0, 0, 16, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                sT[(16 * i + c_row(lane, e)) * LDA + 16 * j + c_col(lane)] = -tij[0][0][e];
+                sAT[(16 * i + c_row(lane, e)) * LDA + 16 * j + c_col(lane)] = -tij[0][0][e];
         }
         sync_lds();
     }
@@ -321,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
         const int t = e / (C / V), s0 = (e % (C / V)) * V;
         E out[V];
 #pragma unroll
-        for (int j = 0; j < V; ++j) out[j] = from_f<E>(sT[t * LDA + s0 + j]);
+        for (int j = 0; j < V; ++j) out[j] = from_f<E>(sAT[t * LDA + s0 + j]);
         *reinterpret_cast<uint4*>(Tout + t * C + s0) = *reinterpret_cast<const uint4*>(out);
     }
 }
@@ -336,17 +359,20 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
 //   phase B  waves 0-3: U = T R (stored as U^T, and as U^T scaled by
 //            gamma_C / gamma_t); waves 4-7: M = tril(Q W^T) * Gamma
 //   phase C  every wave: O^T += U^T M^T for its block, written out; and one
-//            block of the state update S^T <- gamma_C S^T + W^T diag(gamma_C/gamma_t) U
-//   phase D  the next chunk's K, W, Q, V, T, a (loaded from HBM into registers
-//            at the start of this chunk) are written to LDS together with its
-//            decay tables; the new state is written to LDS as the next operand.
+//            block of the state update S^T <- gamma_C S^T + W^T diag(gamma_C/gamma_t) U;
+//            then the next chunk's K, W, Q, V, T, g (loaded from HBM into
+//            registers at the start of this chunk) are written to LDS with its decay
+//            tables (W into the other of two buffers, since the state update
+//            reads the current one), and the new state as the next operand.
 // Operands stored with the contraction index strided (token-major R and W) are
 // read with transposing LDS reads (ds_read_b64_tr_b16).  Barriers are LDS-only
 // (sync_lds) so that the next chunk's global loads stay in flight across them.
 // Decays use base-2 logarithms: g_t = sum_{s<=t} log2 a_s, Gamma_ts = 2^(g_t-g_s).
 template <typename E, int DK, int DVT, int C> struct StateCfg {
     static constexpr int NW = 8, THREADS = 64 * NW;
-    static constexpr int PAD = Vec16<E>::N, VEC = Vec16<E>::N;
+    // rows padded by 32 bytes: a row stride of 8 (mod 16) dwords lets the MFMA
+    // fragment reads (16 rows x 4 column groups) run at full LDS bandwidth
+    static constexpr int PAD = 32 / (int)sizeof(E), VEC = Vec16<E>::N;
     static constexpr int LDK = DK + PAD, LDC = C + PAD, LDV = DVT + PAD;
     static constexpr int NT = C / 16, NK = DK / 16, NV = DVT / 16;
     // phase A / O blocks: BVA j-tiles x 1 t-tile
@@ -366,120 +392,367 @@ template <typename E, int DK, int DVT, int C> struct StateCfg {
     static constexpr int PV = (NVV + THREADS - 1) / THREADS;
     static constexpr int PT = (NVT + THREADS - 1) / THREADS;
     static constexpr int BYTES =
-        (3 * C * LDK + DVT * LDK + C * LDV + 2 * DVT * LDC + 2 * C * LDC + C * LDV) *
+        (4 * C * LDK + DVT * LDK + C * LDV + 2 * DVT * LDC + 2 * C * LDC + C * LDV) *
             (int)sizeof(E) +
         3 * C * (int)sizeof(float);
 };
 
+// Loads of one chunk into registers (issued at the start of the previous chunk)
+// and their staging into LDS.  The loads never branch on their results, so
+// that the waits for them can be counted exactly and placed at the staging: a
+// chunk past the end reloads the last one and rows past the end of the
+// sequence load the last valid row (those rows only reach outputs that are
+// never stored, except through W, whose padded rows are stored as zeros).
 template <typename E, int DK, int DVT, int C>
-__global__ __launch_bounds__(512) void state_kernel(
+__device__ __forceinline__ void state_prefetch(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const void* __restrict__ a, bool gate_bf16, const E* __restrict__ w,
-    const E* __restrict__ Tm, const float* S0, E* __restrict__ o, float* S_T, int T, int DV,
-    int NC) {
+    const E* __restrict__ w, const E* __restrict__ Tm, const float* __restrict__ gin,
+    size_t bh, int j0, int T, int DV, int NC, int cc, int tid, int lane,
+    u32x4 (&pk)[StateCfg<E, DK, DVT, C>::PK], u32x4 (&pq)[StateCfg<E, DK, DVT, C>::PK],
+    u32x4 (&pw)[StateCfg<E, DK, DVT, C>::PK], u32x4 (&pv)[StateCfg<E, DK, DVT, C>::PV],
+    u32x4 (&pt)[StateCfg<E, DK, DVT, C>::PT], float& pg) {
     using G = StateCfg<E, DK, DVT, C>;
-    constexpr int LDK = G::LDK, LDC = G::LDC, LDV = G::LDV, VEC = G::VEC;
+    constexpr int VEC = G::VEC;
+    const int c = min(cc, NC - 1);
+    const int t0 = c * C, n = min(C, T - t0);
+    const size_t row0 = bh * T + t0;
+#pragma unroll
+    for (int x = 0; x < G::PK; ++x) {
+        const int e = tid + G::THREADS * x;
+        if (G::NVK % G::THREADS == 0 || e < G::NVK) {
+            const int t = e / (DK / VEC), c0 = (e % (DK / VEC)) * VEC;
+            const size_t off = (row0 + min(t, n - 1)) * DK + c0;
+            pk[x] = *reinterpret_cast<const u32x4*>(k + off);
+            pq[x] = *reinterpret_cast<const u32x4*>(q + off);
+            pw[x] = *reinterpret_cast<const u32x4*>(w + off);
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < G::PV; ++x) {
+        const int e = tid + G::THREADS * x;
+        if (G::NVV % G::THREADS == 0 || e < G::NVV) {
+            const int t = e / (DVT / VEC), c0 = (e % (DVT / VEC)) * VEC;
+            pv[x] = *reinterpret_cast<const u32x4*>(v + (row0 + min(t, n - 1)) * DV + j0 + c0);
+        }
+    }
+    const E* Tc = Tm + (bh * NC + c) * (size_t)(C * C);
+#pragma unroll
+    for (int x = 0; x < G::PT; ++x) {
+        const int e = tid + G::THREADS * x;
+        if (G::NVT % G::THREADS == 0 || e < G::NVT)
+            pt[x] = *reinterpret_cast<const u32x4*>(Tc + e * VEC);
+    }
+    // chunk-local cumulative log2 decay (padding rows repeat the last value)
+    pg = gin[(bh * NC + c) * C + min(lane, C - 1)];
+}
+
+template <typename E, int DK, int DVT, int C>
+__device__ __forceinline__ void state_stage(
+    E* sK, E* sQ, E* sWc, E* sV, E* sT, float* sg, float* sgam, float* sdel, int n, int tid,
+    int lane, int wave, const u32x4 (&pk)[StateCfg<E, DK, DVT, C>::PK],
+    const u32x4 (&pq)[StateCfg<E, DK, DVT, C>::PK], const u32x4 (&pw)[StateCfg<E, DK, DVT, C>::PK],
+    const u32x4 (&pv)[StateCfg<E, DK, DVT, C>::PV], const u32x4 (&pt)[StateCfg<E, DK, DVT, C>::PT],
+    float pg) {
+    using G = StateCfg<E, DK, DVT, C>;
+    constexpr int VEC = G::VEC, LDK = G::LDK, LDC = G::LDC, LDV = G::LDV;
+#pragma unroll
+    for (int x = 0; x < G::PK; ++x) {
+        const int e = tid + G::THREADS * x;
+        if (G::NVK % G::THREADS == 0 || e < G::NVK) {
+            const int t = e / (DK / VEC), c0 = (e % (DK / VEC)) * VEC;
+            *reinterpret_cast<u32x4*>(sK + t * LDK + c0) = pk[x];
+            *reinterpret_cast<u32x4*>(sQ + t * LDK + c0) = pq[x];
+            // padded rows of W are zero (a select at staging time, when the
+            // loaded row has to have arrived anyway)
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(sWc + t * LDK + c0) = (t < n) ? pw[x] : zero;
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < G::PV; ++x) {
+        const int e = tid + G::THREADS * x;
+        if (G::NVV % G::THREADS == 0 || e < G::NVV) {
+            const int t = e / (DVT / VEC), c0 = (e % (DVT / VEC)) * VEC;
+            *reinterpret_cast<u32x4*>(sV + t * LDV + c0) = pv[x];
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < G::PT; ++x) {
+        const int e = tid + G::THREADS * x;
+        if (G::NVT % G::THREADS == 0 || e < G::NVT) {
+            const int t = e / (C / VEC), c0 = (e % (C / VEC)) * VEC;
+            *reinterpret_cast<u32x4*>(sT + t * LDC + c0) = pt[x];
+        }
+    }
+    if (wave == 0) {
+        const float glast = lane_value(pg, C - 1);
+        if (lane < C) {
+            sg[lane] = pg;
+            sgam[lane] = exp2_hw(pg);
+            sdel[lane] = exp2_hw(glast - pg);
+        }
+    }
+}
+
+// LDS of the state kernel
+template <typename E, int DK, int DVT, int C> struct StateLds {
+    using G = StateCfg<E, DK, DVT, C>;
+    E K[C * G::LDK];
+    E W[2][C * G::LDK];  // double-buffered: read by the state update
+    E Q[C * G::LDK];
+    E S[DVT * G::LDK];   // state tile S[j][i] as an operand
+    E R[C * G::LDV];     // R [t][j]
+    E U[DVT * G::LDC];   // U^T [j][t]
+    E Us[DVT * G::LDC];  // U^T scaled by gamma_C / gamma_t
+    E Tt[C * G::LDC];    // (I + A)^{-1}  [t][s]
+    E M[C * G::LDC];     // tril(Q W^T) * Gamma  [t][s]
+    E V[C * G::LDV];
+    float g[C];          // g_t (base 2)
+    float gam[C];        // gamma_t = 2^g_t
+    float del[C];        // gamma_C / gamma_t
+};
+
+// what every wave of a state workgroup knows about its problem
+template <typename E> struct StateArgs {
+    const E *q, *k, *v, *w, *Tm;
+    const float* gin;
+    E* o;
+    size_t bh;
+    int j0, T, DV, NC, tid, lane, wave;
+};
+
+// the wave's share of the state, S^T blocks (BI x BV tiles); element e <->
+// i = 16 ti + 4 (lane/16) + e, j = 16 tj + lane % 16
+template <typename E, int DK, int DVT, int C>
+using StateAcc = floatx4[StateCfg<E, DK, DVT, C>::SPW][StateCfg<E, DK, DVT, C>::BI]
+                        [StateCfg<E, DK, DVT, C>::BV];
+
+// S^T blocks of the state -> LDS operand S[j][i] in qkv dtype
+template <typename E, int DK, int DVT, int C>
+__device__ __forceinline__ void state_write(const StateAcc<E, DK, DVT, C>& accS, E* sS, int wave,
+                                            int lane) {
+    using G = StateCfg<E, DK, DVT, C>;
+#pragma unroll
+    for (int x = 0; x < G::SPW; ++x) {
+        const int job = wave + G::NW * x;
+        if (job < G::NSJ) {
+            const int ib = (job / G::NVB) * G::BI, jb = (job % G::NVB) * G::BV;
+#pragma unroll
+            for (int bi = 0; bi < G::BI; ++bi)
+#pragma unroll
+                for (int bv = 0; bv < G::BV; ++bv) {
+                    const int i = 16 * (ib + bi) + 4 * (lane >> 4);
+                    const int j = 16 * (jb + bv) + (lane & 15);
+                    const floatx4 sv = accS[x][bi][bv];
+                    store4<E>(sS + j * G::LDK + i, sv[0], sv[1], sv[2], sv[3]);
+                }
+        }
+    }
+}
+
+// One chunk c of the state pass.  LDS holds chunk c on entry.  The register
+// set (lk..lg) has been staged already and now receives chunk c + 2 from HBM;
+// the set (nk..ng) holds chunk c + 1 and is staged into LDS in phase C.
+template <typename E, int DK, int DVT, int C>
+__device__ __forceinline__ void state_chunk(
+    const StateArgs<E>& A, StateLds<E, DK, DVT, C>& L, StateAcc<E, DK, DVT, C>& accS, int c,
+    u32x4 (&lk)[StateCfg<E, DK, DVT, C>::PK], u32x4 (&lq)[StateCfg<E, DK, DVT, C>::PK],
+    u32x4 (&lw)[StateCfg<E, DK, DVT, C>::PK], u32x4 (&lv)[StateCfg<E, DK, DVT, C>::PV],
+    u32x4 (&lt)[StateCfg<E, DK, DVT, C>::PT], float& lg,
+    const u32x4 (&nk)[StateCfg<E, DK, DVT, C>::PK], const u32x4 (&nq)[StateCfg<E, DK, DVT, C>::PK],
+    const u32x4 (&nw)[StateCfg<E, DK, DVT, C>::PK], const u32x4 (&nv)[StateCfg<E, DK, DVT, C>::PV],
+    const u32x4 (&nt)[StateCfg<E, DK, DVT, C>::PT], float ng) {
+    using G = StateCfg<E, DK, DVT, C>;
+    constexpr int LDK = G::LDK, LDC = G::LDC, LDV = G::LDV;
     constexpr int BT = G::BT, BV = G::BV, BI = G::BI, BVA = G::BVA;
-    constexpr int NTB = G::NTB, NVB = G::NVB, NT = G::NT;
-    __shared__ __align__(16) E sK[C * LDK];
-    __shared__ __align__(16) E sW[C * LDK];
-    __shared__ __align__(16) E sQ[C * LDK];
-    __shared__ __align__(16) E sS[DVT * LDK];  // state tile S[j][i] as an operand
-    __shared__ __align__(16) E sR[C * LDV];    // R [t][j]
-    __shared__ __align__(16) E sU[DVT * LDC];  // U^T [j][t]
-    __shared__ __align__(16) E sUs[DVT * LDC]; // U^T scaled by gamma_C / gamma_t
-    __shared__ __align__(16) E sT[C * LDC];    // (I + A)^{-1}  [t][s]
-    __shared__ __align__(16) E sM[C * LDC];    // tril(Q W^T) * Gamma  [t][s]
-    __shared__ __align__(16) E sV[C * LDV];
-    __shared__ __align__(16) float sg[C];      // g_t (base 2)
-    __shared__ __align__(16) float sgam[C];    // gamma_t = 2^g_t
-    __shared__ __align__(16) float sdel[C];    // gamma_C / gamma_t
+    constexpr int NVB = G::NVB, NT = G::NT;
+    const int lane = A.lane, wave = A.wave;
+    const int t0 = c * C, n = min(C, A.T - t0);
+    const size_t row0 = A.bh * A.T + t0;
+    E* sWc = L.W[c & 1];
+    state_prefetch<E, DK, DVT, C>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.bh, A.j0, A.T, A.DV, A.NC,
+                                  c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t bh = blockIdx.y;
-    const int j0 = blockIdx.x * DVT;
+    // ---------------- phase A: X^T = S K^T -> R ;  Y = S Q^T
+    // block (jb: BVA j-tiles, tb: one t-tile); C-layout element e <->
+    // j = 16 (jb + bv) + 4 (lane/16) + e, t = 16 tb + lane % 16
+    floatx4 accY[G::APW][BVA][1];
+#pragma unroll
+    for (int x = 0; x < G::APW; ++x) {
+        const int job = wave + G::NW * x;
+        const int jb = (job / NT) * BVA, tb = job % NT;
+        floatx4 xt[BVA][1];
+#pragma unroll
+        for (int bv = 0; bv < BVA; ++bv) {
+            xt[bv][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+            accY[x][bv][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (job < G::NAJ) {
+            using M = Mma<E>;
+#pragma unroll
+            for (int kk = 0; kk < DK; kk += M::KS) {
+                typename M::frag_t fs[BVA];
+#pragma unroll
+                for (int bv = 0; bv < BVA; ++bv)
+                    fs[bv] = M::frag(L.S, LDK, 16 * (jb + bv), kk, lane);
+                const auto fk = M::frag(L.K, LDK, 16 * tb, kk, lane);
+                const auto fq = M::frag(L.Q, LDK, 16 * tb, kk, lane);
+#pragma unroll
+                for (int bv = 0; bv < BVA; ++bv) {
+                    xt[bv][0] = M::mma(fs[bv], fk, xt[bv][0]);
+                    accY[x][bv][0] = M::mma(fs[bv], fq, accY[x][bv][0]);
+                }
+            }
+            const int t = 16 * tb + (lane & 15);
+            const float gt = L.gam[t];
+#pragma unroll
+            for (int bv = 0; bv < BVA; ++bv) {
+                const int j = 16 * (jb + bv) + 4 * (lane >> 4);
+                float vv[4];
+                load4<E>(L.V + t * LDV + j, vv);
+                const floatx4 xv = xt[bv][0];
+                store4<E>(L.R + t * LDV + j, vv[0] - gt * xv[0], vv[1] - gt * xv[1],
+                          vv[2] - gt * xv[2], vv[3] - gt * xv[3]);
+                accY[x][bv][0] = accY[x][bv][0] * gt;
+            }
+        }
+    }
+    sync_lds();
 
-    // ---- registers holding the next chunk while the current one is computed
-    uint4 pk[G::PK], pw[G::PK], pq[G::PK], pv[G::PV], pt[G::PT];
-    float pa = 1.f;
-    auto prefetch = [&](int c) {
-        // rows past the end of the sequence load the last valid row and are
-        // then zeroed, so that every load is unconditional
-        const int t0 = c * C, n = min(C, T - t0);
-        const size_t row0 = bh * T + t0;
+    // ---------------- phase B
+    const float gC = L.gam[C - 1];  // read before phase C restages the tables
+    if (wave < 4) {
+        // U = T R (T lower triangular: contract only up to the block's last row)
 #pragma unroll
-        for (int x = 0; x < G::PK; ++x) {
-            const int e = tid + G::THREADS * x;
-            if (e < G::NVK) {
-                const int t = e / (DK / VEC), c0 = (e % (DK / VEC)) * VEC;
-                const size_t off = (row0 + min(t, n - 1)) * DK + c0;
-                pk[x] = *reinterpret_cast<const uint4*>(k + off);
-                pq[x] = *reinterpret_cast<const uint4*>(q + off);
-                pw[x] = *reinterpret_cast<const uint4*>(w + off);
-                if (t >= n) pk[x] = pq[x] = pw[x] = make_uint4(0, 0, 0, 0);
+        for (int x = 0; x < G::UPW; ++x) {
+            const int job = wave + 4 * x;
+            if (job < G::NUJ) {
+                const int tb = (job / NVB) * BT, jb = (job % NVB) * BV;
+                floatx4 u[BT][BV];
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt)
+#pragma unroll
+                    for (int bv = 0; bv < BV; ++bv) u[bt][bv] = floatx4{0.f, 0.f, 0.f, 0.f};
+                mma_block<E, BT, BV, false, true>(u, L.Tt, LDC, 16 * tb, L.R, LDV, 16 * jb, 0,
+                                                  16 * (tb + BT), lane);
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt) {
+                    const int t = 16 * (tb + bt) + 4 * (lane >> 4);
+                    const float4 d4 = *reinterpret_cast<const float4*>(L.del + t);
+#pragma unroll
+                    for (int bv = 0; bv < BV; ++bv) {
+                        const int j = 16 * (jb + bv) + (lane & 15);
+                        const floatx4 uv = u[bt][bv];
+                        store4<E>(L.U + j * LDC + t, uv[0], uv[1], uv[2], uv[3]);
+                        store4<E>(L.Us + j * LDC + t, d4.x * uv[0], d4.y * uv[1], d4.z * uv[2],
+                                  d4.w * uv[3]);
+                    }
+                }
             }
         }
+    } else {
+        // M^T = W Q^T on the lower block triangle, stored as M[t][s]
 #pragma unroll
-        for (int x = 0; x < G::PV; ++x) {
-            const int e = tid + G::THREADS * x;
-            if (e < G::NVV) {
-                const int t = e / (DVT / VEC), c0 = (e % (DVT / VEC)) * VEC;
-                pv[x] = *reinterpret_cast<const uint4*>(v + (row0 + min(t, n - 1)) * DV + j0 + c0);
-                if (t >= n) pv[x] = make_uint4(0, 0, 0, 0);
+        for (int x = 0; x < G::MPW; ++x) {
+            const int job = (wave - 4) + 4 * x;
+            if (job < G::NMJ) {
+                int tbb = 0, sbb = job;
+                while (sbb > tbb) {
+                    sbb -= tbb + 1;
+                    ++tbb;
+                }
+                floatx4 m[BT][BT];
+#pragma unroll
+                for (int i = 0; i < BT; ++i)
+#pragma unroll
+                    for (int j = 0; j < BT; ++j) m[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+                mma_block<E, BT, BT>(m, sWc, LDK, 16 * sbb * BT, L.Q, LDK, 16 * tbb * BT, 0, DK,
+                                     lane);
+#pragma unroll
+                for (int bs = 0; bs < BT; ++bs)
+#pragma unroll
+                    for (int bt = 0; bt < BT; ++bt) {
+                        const int s0 = 16 * (sbb * BT + bs) + 4 * (lane >> 4);
+                        const int t = 16 * (tbb * BT + bt) + (lane & 15);
+                        const float gt = L.g[t];
+                        const float4 gs = *reinterpret_cast<const float4*>(L.g + s0);
+                        const floatx4 mv = m[bs][bt];
+                        store4<E>(L.M + t * LDC + s0,
+                                  (s0 + 0 <= t) ? exp2_hw(gt - gs.x) * mv[0] : 0.f,
+                                  (s0 + 1 <= t) ? exp2_hw(gt - gs.y) * mv[1] : 0.f,
+                                  (s0 + 2 <= t) ? exp2_hw(gt - gs.z) * mv[2] : 0.f,
+                                  (s0 + 3 <= t) ? exp2_hw(gt - gs.w) * mv[3] : 0.f);
+                    }
             }
         }
-        const E* Tc = Tm + (bh * NC + c) * (size_t)(C * C);
-#pragma unroll
-        for (int x = 0; x < G::PT; ++x) {
-            const int e = tid + G::THREADS * x;
-            if (e < G::NVT) pt[x] = *reinterpret_cast<const uint4*>(Tc + e * VEC);
-        }
-        if (wave == 0) {
-            pa = load_gate(a, row0 + min(lane, n - 1), gate_bf16);
-            if (lane >= n) pa = 1.f;
-        }
-    };
-    auto stage = [&]() {
-#pragma unroll
-        for (int x = 0; x < G::PK; ++x) {
-            const int e = tid + G::THREADS * x;
-            if (e < G::NVK) {
-                const int t = e / (DK / VEC), c0 = (e % (DK / VEC)) * VEC;
-                *reinterpret_cast<uint4*>(sK + t * LDK + c0) = pk[x];
-                *reinterpret_cast<uint4*>(sQ + t * LDK + c0) = pq[x];
-                *reinterpret_cast<uint4*>(sW + t * LDK + c0) = pw[x];
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < G::PV; ++x) {
-            const int e = tid + G::THREADS * x;
-            if (e < G::NVV) {
-                const int t = e / (DVT / VEC), c0 = (e % (DVT / VEC)) * VEC;
-                *reinterpret_cast<uint4*>(sV + t * LDV + c0) = pv[x];
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < G::PT; ++x) {
-            const int e = tid + G::THREADS * x;
-            if (e < G::NVT) {
-                const int t = e / (C / VEC), c0 = (e % (C / VEC)) * VEC;
-                *reinterpret_cast<uint4*>(sT + t * LDC + c0) = pt[x];
-            }
-        }
-        if (wave == 0) {
-            const float g = wave_incl_sum(lane < C ? log2_hw(pa) : 0.f);
-            const float glast = lane_value(g, C - 1);
-            if (lane < C) {
-                sg[lane] = g;
-                sgam[lane] = exp2_hw(g);
-                sdel[lane] = exp2_hw(glast - g);
-            }
-        }
-    };
+    }
+    sync_lds();
 
-    // ---- state: S^T blocks (BI x BV tiles), element e <-> i = 16 ti + 4 (lane/16) + e,
-    //      j = 16 tj + lane % 16
-    floatx4 accS[G::SPW][BI][BV];
+    // ---------------- phase C: O^T += U^T M^T ; state update ; stage chunk c + 1
+#pragma unroll
+    for (int x = 0; x < G::APW; ++x) {
+        const int job = wave + G::NW * x;
+        if (job < G::NAJ) {
+            const int jb = (job / NT) * BVA, tb = job % NT;
+            mma_block<E, BVA, 1>(accY[x], L.U, LDC, 16 * jb, L.M, LDC, 16 * tb, 0, 16 * (tb + 1),
+                                 lane);
+            const int t = 16 * tb + (lane & 15);
+            if (t < n) {
+#pragma unroll
+                for (int bv = 0; bv < BVA; ++bv) {
+                    const int j = 16 * (jb + bv) + 4 * (lane >> 4);
+                    const floatx4 ov = accY[x][bv][0];
+                    store4<E>(A.o + (row0 + t) * A.DV + A.j0 + j, ov[0], ov[1], ov[2], ov[3]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < G::SPW; ++x) {
+        const int job = wave + G::NW * x;
+        if (job < G::NSJ) {
+            const int ib = (job / NVB) * BI, jb = (job % NVB) * BV;
+#pragma unroll
+            for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                for (int bv = 0; bv < BV; ++bv) accS[x][bi][bv] = accS[x][bi][bv] * gC;
+            // W^T fragments straight from the token-major W
+            mma_block<E, BI, BV, true>(accS[x], sWc, LDK, 16 * ib, L.Us, LDC, 16 * jb, 0, C,
+                                       lane);
+        }
+    }
+    // nothing staged here is read in phase C (W goes to the other buffer)
+    if (c + 1 < A.NC)
+        state_stage<E, DK, DVT, C>(L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g, L.gam, L.del,
+                                   min(C, A.T - (c + 1) * C), A.tid, lane, wave, nk, nq, nw, nv,
+                                   nt, ng);
+    state_write<E, DK, DVT, C>(accS, L.S, wave, lane);
+    sync_lds();
+}
+
+// One workgroup per CU (its LDS footprint) = two waves per SIMD: give each wave
+// the full 256-register budget instead of spilling to reach more waves.
+template <typename E, int DK, int DVT, int C>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void state_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ gin, const E* __restrict__ w, const E* __restrict__ Tm,
+    const float* S0, E* __restrict__ o, float* S_T, int T, int DV, int NC) {
+    using G = StateCfg<E, DK, DVT, C>;
+    constexpr int BI = G::BI, BV = G::BV, NVB = G::NVB;
+    __shared__ __align__(16) StateLds<E, DK, DVT, C> L;
+    const int tid = threadIdx.x;
+    const StateArgs<E> A{q,  k,  v,      w,   Tm,  gin,      o,         blockIdx.y,
+                         (int)blockIdx.x * DVT, T, DV, NC, tid, tid & 63, tid >> 6};
+    const int lane = A.lane, wave = A.wave;
+    const size_t bh = A.bh;
+    const int j0 = A.j0;
+
+    // two register sets receive chunks from HBM two chunks ahead of their use
+    u32x4 pkA[G::PK], pqA[G::PK], pwA[G::PK], pvA[G::PV], ptA[G::PT];
+    u32x4 pkB[G::PK], pqB[G::PK], pwB[G::PK], pvB[G::PV], ptB[G::PT];
+    float pgA = 0.f, pgB = 0.f;
+
+    StateAcc<E, DK, DVT, C> accS;
 #pragma unroll
     for (int x = 0; x < G::SPW; ++x) {
         const int job = wave + G::NW * x;
@@ -498,190 +771,25 @@ __global__ __launch_bounds__(512) void state_kernel(
                 }
             }
     }
-    auto write_state = [&]() {
-#pragma unroll
-        for (int x = 0; x < G::SPW; ++x) {
-            const int job = wave + G::NW * x;
-            if (job < G::NSJ) {
-                const int ib = (job / NVB) * BI, jb = (job % NVB) * BV;
-#pragma unroll
-                for (int bi = 0; bi < BI; ++bi)
-#pragma unroll
-                    for (int bv = 0; bv < BV; ++bv) {
-                        const int i = 16 * (ib + bi) + 4 * (lane >> 4);
-                        const int j = 16 * (jb + bv) + (lane & 15);
-                        const floatx4 sv = accS[x][bi][bv];
-                        store4<E>(sS + j * LDK + i, sv[0], sv[1], sv[2], sv[3]);
-                    }
-            }
-        }
-    };
 
     if (NC > 0) {
-        prefetch(0);
-        stage();
+        state_prefetch<E, DK, DVT, C>(q, k, v, w, Tm, gin, bh, j0, T, DV, NC, 0, tid, lane, pkA,
+                                      pqA, pwA, pvA, ptA, pgA);
+        state_prefetch<E, DK, DVT, C>(q, k, v, w, Tm, gin, bh, j0, T, DV, NC, 1, tid, lane, pkB,
+                                      pqB, pwB, pvB, ptB, pgB);
+        state_stage<E, DK, DVT, C>(L.K, L.Q, L.W[0], L.V, L.Tt, L.g, L.gam, L.del, min(C, T), tid,
+                                   lane, wave, pkA, pqA, pwA, pvA, ptA, pgA);
     }
-    write_state();
+    state_write<E, DK, DVT, C>(accS, L.S, wave, lane);
     sync_lds();
 
-    for (int c = 0; c < NC; ++c) {
-        const int t0 = c * C, n = min(C, T - t0);
-        const size_t row0 = bh * T + t0;
-        if (c + 1 < NC) prefetch(c + 1);
-
-        // ---------------- phase A: X^T = S K^T -> R ;  Y = S Q^T
-        // block (jb: BVA j-tiles, tb: one t-tile); C-layout element e <->
-        // j = 16 (jb + bv) + 4 (lane/16) + e, t = 16 tb + lane % 16
-        floatx4 accY[G::APW][BVA][1];
-#pragma unroll
-        for (int x = 0; x < G::APW; ++x) {
-            const int job = wave + G::NW * x;
-            const int jb = (job / NT) * BVA, tb = job % NT;
-            floatx4 xt[BVA][1];
-#pragma unroll
-            for (int bv = 0; bv < BVA; ++bv) {
-                xt[bv][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-                accY[x][bv][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-            }
-            if (job < G::NAJ) {
-                using M = Mma<E>;
-                for (int kk = 0; kk < DK; kk += M::KS) {
-                    typename M::frag_t fs[BVA];
-#pragma unroll
-                    for (int bv = 0; bv < BVA; ++bv)
-                        fs[bv] = M::frag(sS, LDK, 16 * (jb + bv), kk, lane);
-                    const auto fk = M::frag(sK, LDK, 16 * tb, kk, lane);
-                    const auto fq = M::frag(sQ, LDK, 16 * tb, kk, lane);
-#pragma unroll
-                    for (int bv = 0; bv < BVA; ++bv) {
-                        xt[bv][0] = M::mma(fs[bv], fk, xt[bv][0]);
-                        accY[x][bv][0] = M::mma(fs[bv], fq, accY[x][bv][0]);
-                    }
-                }
-                const int t = 16 * tb + (lane & 15);
-                const float gt = sgam[t];
-#pragma unroll
-                for (int bv = 0; bv < BVA; ++bv) {
-                    const int j = 16 * (jb + bv) + 4 * (lane >> 4);
-                    float vv[4];
-                    load4<E>(sV + t * LDV + j, vv);
-                    const floatx4 xv = xt[bv][0];
-                    store4<E>(sR + t * LDV + j, vv[0] - gt * xv[0], vv[1] - gt * xv[1],
-                              vv[2] - gt * xv[2], vv[3] - gt * xv[3]);
-                    accY[x][bv][0] = accY[x][bv][0] * gt;
-                }
-            }
-        }
-        sync_lds();
-
-        // ---------------- phase B
-        if (wave < 4) {
-            // U = T R (T lower triangular: contract only up to the block's last row)
-#pragma unroll
-            for (int x = 0; x < G::UPW; ++x) {
-                const int job = wave + 4 * x;
-                if (job < G::NUJ) {
-                    const int tb = (job / NVB) * BT, jb = (job % NVB) * BV;
-                    floatx4 u[BT][BV];
-#pragma unroll
-                    for (int bt = 0; bt < BT; ++bt)
-#pragma unroll
-                        for (int bv = 0; bv < BV; ++bv) u[bt][bv] = floatx4{0.f, 0.f, 0.f, 0.f};
-                    mma_block<E, BT, BV, false, true>(u, sT, LDC, 16 * tb, sR, LDV, 16 * jb, 0,
-                                                      16 * (tb + BT), lane);
-#pragma unroll
-                    for (int bt = 0; bt < BT; ++bt) {
-                        const int t = 16 * (tb + bt) + 4 * (lane >> 4);
-                        const float4 d4 = *reinterpret_cast<const float4*>(sdel + t);
-#pragma unroll
-                        for (int bv = 0; bv < BV; ++bv) {
-                            const int j = 16 * (jb + bv) + (lane & 15);
-                            const floatx4 uv = u[bt][bv];
-                            store4<E>(sU + j * LDC + t, uv[0], uv[1], uv[2], uv[3]);
-                            store4<E>(sUs + j * LDC + t, d4.x * uv[0], d4.y * uv[1],
-                                      d4.z * uv[2], d4.w * uv[3]);
-                        }
-                    }
-                }
-            }
-        } else {
-            // M^T = W Q^T on the lower block triangle, stored as M[t][s]
-#pragma unroll
-            for (int x = 0; x < G::MPW; ++x) {
-                const int job = (wave - 4) + 4 * x;
-                if (job < G::NMJ) {
-                    int tbb = 0, sbb = job;
-                    while (sbb > tbb) {
-                        sbb -= tbb + 1;
-                        ++tbb;
-                    }
-                    floatx4 m[BT][BT];
-#pragma unroll
-                    for (int i = 0; i < BT; ++i)
-#pragma unroll
-                        for (int j = 0; j < BT; ++j) m[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-                    mma_block<E, BT, BT>(m, sW, LDK, 16 * sbb * BT, sQ, LDK, 16 * tbb * BT, 0,
-                                         DK, lane);
-#pragma unroll
-                    for (int bs = 0; bs < BT; ++bs)
-#pragma unroll
-                        for (int bt = 0; bt < BT; ++bt) {
-                            const int s0 = 16 * (sbb * BT + bs) + 4 * (lane >> 4);
-                            const int t = 16 * (tbb * BT + bt) + (lane & 15);
-                            const float gt = sg[t];
-                            const float4 gs = *reinterpret_cast<const float4*>(sg + s0);
-                            const floatx4 mv = m[bs][bt];
-                            store4<E>(sM + t * LDC + s0,
-                                      (s0 + 0 <= t) ? exp2_hw(gt - gs.x) * mv[0] : 0.f,
-                                      (s0 + 1 <= t) ? exp2_hw(gt - gs.y) * mv[1] : 0.f,
-                                      (s0 + 2 <= t) ? exp2_hw(gt - gs.z) * mv[2] : 0.f,
-                                      (s0 + 3 <= t) ? exp2_hw(gt - gs.w) * mv[3] : 0.f);
-                        }
-                }
-            }
-        }
-        sync_lds();
-
-        // ---------------- phase C: O^T += U^T M^T ;  state update
-#pragma unroll
-        for (int x = 0; x < G::APW; ++x) {
-            const int job = wave + G::NW * x;
-            if (job < G::NAJ) {
-                const int jb = (job / NT) * BVA, tb = job % NT;
-                mma_block<E, BVA, 1>(accY[x], sU, LDC, 16 * jb, sM, LDC, 16 * tb, 0,
-                                     16 * (tb + 1), lane);
-                const int t = 16 * tb + (lane & 15);
-                if (t < n) {
-#pragma unroll
-                    for (int bv = 0; bv < BVA; ++bv) {
-                        const int j = 16 * (jb + bv) + 4 * (lane >> 4);
-                        const floatx4 ov = accY[x][bv][0];
-                        store4<E>(o + (row0 + t) * DV + j0 + j, ov[0], ov[1], ov[2], ov[3]);
-                    }
-                }
-            }
-        }
-        const float gC = sgam[C - 1];
-#pragma unroll
-        for (int x = 0; x < G::SPW; ++x) {
-            const int job = wave + G::NW * x;
-            if (job < G::NSJ) {
-                const int ib = (job / NVB) * BI, jb = (job % NVB) * BV;
-#pragma unroll
-                for (int bi = 0; bi < BI; ++bi)
-#pragma unroll
-                    for (int bv = 0; bv < BV; ++bv) accS[x][bi][bv] = accS[x][bi][bv] * gC;
-                // W^T fragments straight from the token-major W
-                mma_block<E, BI, BV, true>(accS[x], sW, LDK, 16 * ib, sUs, LDC, 16 * jb, 0, C,
-                                           lane);
-            }
-        }
-        sync_lds();
-
-        // ---------------- phase D
-        if (c + 1 < NC) stage();
-        write_state();
-        sync_lds();
+    // the two sets alternate roles from chunk to chunk
+    for (int c = 0; c < NC; c += 2) {
+        state_chunk<E, DK, DVT, C>(A, L, accS, c, pkA, pqA, pwA, pvA, ptA, pgA, pkB, pqB, pwB,
+                                   pvB, ptB, pgB);
+        if (c + 1 < NC)
+            state_chunk<E, DK, DVT, C>(A, L, accS, c + 1, pkB, pqB, pwB, pvB, ptB, pgB, pkA, pqA,
+                                       pwA, pvA, ptA, pgA);
     }
     if (S_T) {
 #pragma unroll
@@ -736,23 +844,23 @@ int dv_tile(const Shape& s) {
 
 template <typename E, int DK, int C>
 hipError_t prep_t(const Shape& s, bool fuse, const void* k, const void* a, const void* nu,
-                  const void* r, const float* lc, void* w, void* Tm, hipStream_t st) {
+                  const void* r, const float* lc, void* w, void* Tm, float* g, hipStream_t st) {
     static_assert(PrepLds<E, DK, C>::BYTES <= kLdsLimit, "prep LDS");
     hipLaunchKernelGGL((prep_kernel<E, DK, C>), dim3(s.nc, s.BH), dim3(kThreads), 0, st,
                        static_cast<const E*>(k), a, nu, r, s.gate_bf16, s.diag, fuse, lc,
-                       static_cast<E*>(w), static_cast<E*>(Tm), s.T, s.nc);
+                       static_cast<E*>(w), static_cast<E*>(Tm), g, s.T, s.nc);
     return hipGetLastError();
 }
 
 template <typename E, int DK, int DVT, int C>
-hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, const void* a,
+hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, const float* g,
                    const void* w, const void* Tm, const float* S0, void* o, float* S_T,
                    hipStream_t st) {
     if constexpr (state_fits<E, DK, DVT, C>()) {
         hipLaunchKernelGGL((state_kernel<E, DK, DVT, C>), dim3(s.dv / DVT, s.BH),
                            dim3(StateCfg<E, DK, DVT, C>::THREADS), 0, st,
                            static_cast<const E*>(q), static_cast<const E*>(k),
-                           static_cast<const E*>(v), a, s.gate_bf16, static_cast<const E*>(w),
+                           static_cast<const E*>(v), g, static_cast<const E*>(w),
                            static_cast<const E*>(Tm), S0, static_cast<E*>(o), S_T, s.T, s.dv,
                            s.nc);
         return hipGetLastError();
@@ -763,9 +871,10 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
 
 template <typename E>
 hipError_t prep_e(const Shape& s, bool fuse, const void* k, const void* a, const void* nu,
-                  const void* r, const float* lc, void* w, void* Tm, hipStream_t st) {
+                  const void* r, const float* lc, void* w, void* Tm, float* g, hipStream_t st) {
 #define KDN_PREP(DK_, C_) \
-    if (s.dk == DK_ && s.chunk == C_) return prep_t<E, DK_, C_>(s, fuse, k, a, nu, r, lc, w, Tm, st);
+    if (s.dk == DK_ && s.chunk == C_)   \
+        return prep_t<E, DK_, C_>(s, fuse, k, a, nu, r, lc, w, Tm, g, st);
 #define KDN_PREP_C(DK_) KDN_PREP(DK_, 16) KDN_PREP(DK_, 32) KDN_PREP(DK_, 64)
     KDN_PREP_C(32) KDN_PREP_C(64) KDN_PREP_C(128)
 #undef KDN_PREP_C
@@ -774,13 +883,13 @@ hipError_t prep_e(const Shape& s, bool fuse, const void* k, const void* a, const
 }
 
 template <typename E>
-hipError_t state_e(const Shape& s, const void* q, const void* k, const void* v, const void* a,
+hipError_t state_e(const Shape& s, const void* q, const void* k, const void* v, const float* g,
                    const void* w, const void* Tm, const float* S0, void* o, float* S_T,
                    hipStream_t st) {
     const int dvt = dv_tile(s);
 #define KDN_ST(DK_, DVT_, C_)                                                             \
     if (s.dk == DK_ && dvt == DVT_ && s.chunk == C_)                                      \
-        return state_t<E, DK_, DVT_, C_>(s, q, k, v, a, w, Tm, S0, o, S_T, st);
+        return state_t<E, DK_, DVT_, C_>(s, q, k, v, g, w, Tm, S0, o, S_T, st);
 #define KDN_ST_C(DK_, DVT_) KDN_ST(DK_, DVT_, 16) KDN_ST(DK_, DVT_, 32) KDN_ST(DK_, DVT_, 64)
     KDN_ST_C(32, 32) KDN_ST_C(32, 64) KDN_ST_C(64, 32) KDN_ST_C(64, 64)
     KDN_ST_C(128, 32) KDN_ST_C(128, 64)
@@ -800,18 +909,18 @@ bool chunk_supported(const Shape& s) {
 
 hipError_t launch_chunk_prep(const Shape& s, bool fuse_gain, const void* k, const void* a,
                              const void* nu, const void* r, const float* lam_chunk, void* w,
-                             void* Tm, hipStream_t st) {
+                             void* Tm, float* g, hipStream_t st) {
     if (s.BH == 0 || s.nc == 0) return hipSuccess;
-    return s.qkv_bf16 ? prep_e<bf16_t>(s, fuse_gain, k, a, nu, r, lam_chunk, w, Tm, st)
-                      : prep_e<float>(s, fuse_gain, k, a, nu, r, lam_chunk, w, Tm, st);
+    return s.qkv_bf16 ? prep_e<bf16_t>(s, fuse_gain, k, a, nu, r, lam_chunk, w, Tm, g, st)
+                      : prep_e<float>(s, fuse_gain, k, a, nu, r, lam_chunk, w, Tm, g, st);
 }
 
 hipError_t launch_chunk_state(const Shape& s, const void* q, const void* k, const void* v,
-                              const void* a, const void* w, const void* Tm, const float* S0,
+                              const float* g, const void* w, const void* Tm, const float* S0,
                               void* o, float* S_T, hipStream_t st) {
     if (s.BH == 0) return hipSuccess;
-    return s.qkv_bf16 ? state_e<bf16_t>(s, q, k, v, a, w, Tm, S0, o, S_T, st)
-                      : state_e<float>(s, q, k, v, a, w, Tm, S0, o, S_T, st);
+    return s.qkv_bf16 ? state_e<bf16_t>(s, q, k, v, g, w, Tm, S0, o, S_T, st)
+                      : state_e<float>(s, q, k, v, g, w, Tm, S0, o, S_T, st);
 }
 
 }  // namespace kdn

@@ -8,6 +8,10 @@ namespace kdn {
 
 typedef uint16_t bf16_t;  // bfloat16 storage
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+// 16-byte register payload of a vector load; a native vector type (not the HIP
+// uint4 struct, whose copies become memcpys that can pin arrays of them to
+// scratch memory)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef short short4x __attribute__((ext_vector_type(4)));
 
@@ -18,11 +22,16 @@ __device__ __forceinline__ float bf2f(bf16_t x) {
     return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
 
-// float -> bfloat16, round to nearest even (inputs are finite).
+// float -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ bf16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+// two floats -> two bfloat16 packed in one word (x in the low half)
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float float2_t __attribute__((ext_vector_type(2)));
+    const float2_t v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 template <typename E> __device__ __forceinline__ float to_f(E x);

@@ -37,13 +37,14 @@ hipError_t launch_gain(const Shape& s, const void* k, const void* r, const float
                        void* w, hipStream_t st);
 // Per-chunk preparation: optionally the gain (from lam_chunk, written to w),
 // then A = strict_tril(K W^T * Gamma) and T = (I + A)^{-1} written to Tm
-// [BH][nc][chunk][chunk] in qkv dtype.  fuse_gain = false reads w instead.
+// [BH][nc][chunk][chunk] in qkv dtype, and the chunk-local cumulative log2
+// decay g [BH][nc][chunk] (float32).  fuse_gain = false reads w instead.
 hipError_t launch_chunk_prep(const Shape& s, bool fuse_gain, const void* k, const void* a,
                              const void* nu, const void* r, const float* lam_chunk, void* w,
-                             void* Tm, hipStream_t st);
-// Sequential chunk pass: memory write and read-out.
+                             void* Tm, float* g, hipStream_t st);
+// Sequential chunk pass: memory write and read-out (g from the prep pass).
 hipError_t launch_chunk_state(const Shape& s, const void* q, const void* k, const void* v,
-                              const void* a, const void* w, const void* Tm, const float* S0,
+                              const float* g, const void* w, const void* Tm, const float* S0,
                               void* o, float* S_T, hipStream_t st);
 // One decode step in place.
 hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
