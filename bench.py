@@ -33,7 +33,11 @@ def log(msg):
 
 
 def algorithmic(B, H, T, dk, dv, C):
-    """Algorithmic bytes and flops of each forward kernel (bf16 inputs)."""
+    """Algorithmic bytes and flops of each forward kernel (bf16 inputs).
+
+    Bytes count every tensor a kernel must read or write once; flops count
+    2 per multiply-add of the products the kernel performs, triangular ones at
+    their triangular size."""
     n = B * H * T           # token-heads
     nc = -(-T // C)
     bh = B * H
@@ -44,22 +48,49 @@ def algorithmic(B, H, T, dk, dv, C):
         "scan_reduce": n * (dk * e + g) + bh * nc * dk * 16,
         # read the chunk products, write chunk-boundary precisions
         "scan_carry": bh * nc * dk * 16 + bh * (nc + 1) * dk * 4 + bh * dk * 4 * 2,
-        # read k, gates, boundary precisions; write w and T
-        "chunk_prep": n * (dk * e + g) + bh * nc * dk * 4 + n * dk * e + bh * nc * C * C * e,
-        # read q, k, v, w, a, T, S0; write o, S_T
-        "chunk_state": n * (3 * dk + dv) * e + n * e + bh * nc * C * C * e + n * dv * e
+        # read k, gates, boundary precisions; write w, T and the log2 decays
+        "chunk_prep": n * (dk * e + g) + bh * nc * dk * 4 + n * dk * e + bh * nc * C * C * e
+        + n * 4,
+        # read q, k, v, w, T, log2 decays, S0; write o, S_T
+        "chunk_state": n * (3 * dk + dv) * e + n * 4 + bh * nc * C * C * e + n * dv * e
         + 2 * bh * dv * dk * 4,
     }
     fl = {
+        # six multiply-adds per (token, key dim) for the factorized Moebius step
         "scan_reduce": n * dk * 12,
         "scan_carry": bh * nc * dk * 5,
-        # gain (~8 dk), A = tril(K W^T) (C dk), T solve (~C^2/3)
+        # gain (~8 per key dim), strict lower triangle of K W^T (C dk), triangular
+        # inverse (~C^2/3)
         "chunk_prep": n * (8 * dk + C * dk + C * C // 3),
-        # K S^T, S Q^T, S update (2 dk dv each), tril(Q W^T) (C dk),
-        # U = T R and tril(M) U (C dv each)
+        # K S^T, Q S^T and the state update (2 dk dv each), lower triangle of
+        # Q W^T (C dk), U = T R and the masked M U (C dv each)
         "chunk_state": n * (6 * dk * dv + C * dk + 2 * C * dv),
     }
     return by, fl
+
+
+def chunk_flops_full(n, dk, dv, C):
+    """Flops of the chunkwise form counted on full (not triangular) products:
+    6 dk dv + C (6 dk + 4 dv) + C^2/3 per token-head (181,589 at d=128, C=64)."""
+    return n * (6 * dk * dv + C * (6 * dk + 4 * dv) + C * C / 3)
+
+
+# HBM bytes per launch of the state kernel from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE passes, scaled by the same counters on a plain device copy of
+# 512 MiB (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0), with the SHA-256 of the
+# kernel source they were taken on: reported only while the source is unchanged.
+TRAFFIC = {"kernel": "chunk_state", "src_sha256": None, "fetch_bytes": None,
+           "write_bytes": None}
+
+
+def _traffic():
+    import hashlib
+    path = os.path.join(ROOT, "kalman_filter_memory_amd", "csrc", "kdn_chunk.hip")
+    with open(path, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if TRAFFIC["src_sha256"] != sha or TRAFFIC["fetch_bytes"] is None:
+        return None, sha
+    return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"], sha
 
 
 def run(args):
@@ -130,10 +161,25 @@ def run(args):
     dom = max(KERNELS, key=lambda k: kern_ms[k])
     s_dom = kern_ms[dom] * 1e-3
     ach_gbs = by[dom] / s_dom / 1e9
+    traffic, sha = _traffic() if dom == TRAFFIC["kernel"] else (None, None)
     roofline = {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": dom,
-                "mfma_frac_bf16": round(fl[dom] / s_dom / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                "unit": "GB/s", "frac": round(ach_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "kernel": dom, "bytes_per_launch": by[dom],
+                "us_per_launch": round(kern_ms[dom] * 1e3, 2)}
+    # the chunk kernels (prep + state) against the bf16 MFMA peak
+    n = B * H * T
+    chunk_s = (kern_ms["chunk_prep"] + kern_ms["chunk_state"]) * 1e-3
+    mfma = {"kernels": "chunk_prep+chunk_state", "us": round(chunk_s * 1e6, 2),
+            "flops_full": chunk_flops_full(n, dk, dv, C),
+            "frac_full": round(chunk_flops_full(n, dk, dv, C) / chunk_s / 1e12
+                               / PEAK_BF16_TFLOPS, 4),
+            "flops_performed": fl["chunk_prep"] + fl["chunk_state"],
+            "frac_performed": round((fl["chunk_prep"] + fl["chunk_state"]) / chunk_s / 1e12
+                                    / PEAK_BF16_TFLOPS, 4),
+            "flops_recurrent": n * 6 * dk * dv,
+            "peak_TFLOP/s": PEAK_BF16_TFLOPS}
+    scan_s = (kern_ms["scan_reduce"] + kern_ms["scan_carry"]) * 1e-3
+    scan_by = by["scan_reduce"] + by["scan_carry"]
 
     res = {
         "metric": "KDN fwd tokens/s (B8 T4096 H16 d128); % MFMA peak; decode GB/s",
@@ -147,8 +193,14 @@ def run(args):
                    "B": B, "H": H, "T": T, "d_k": dk, "d_v": dv, "chunk": C,
                    "state_dtype": "f32"},
         "roofline": roofline,
+        "mfma_chunk": mfma,
+        "scan_hbm": {"kernels": "scan_reduce+scan_carry", "us": round(scan_s * 1e6, 2),
+                     "GB/s": round(scan_by / scan_s / 1e9, 1),
+                     "frac": round(scan_by / scan_s / 1e9 / PEAK_HBM_GBS, 4)},
         "kernels": kernels,
     }
+    if traffic is not None:
+        res["roofline"]["traffic_src_sha256"] = sha
     del t, ws, out
     torch.cuda.empty_cache()
     if not args.no_decode:
@@ -200,26 +252,30 @@ def bench_decode(args):
 
 
 def cpu_baseline(inp, args):
-    """The fp64 oracle on a bounded sample of heads of the same workload."""
+    """The fp64 oracle, as it is, on the same workload: all heads and tokens,
+    repeated until at least --cpu-seconds of wall time have passed."""
     import numpy as np
 
     import oracle
 
     threads = oracle.default_threads()
-    heads = max(1, args.cpu_heads)
-    sel = [(i % WL["B"], (i * 5) % WL["H"]) for i in range(heads)]
-    sub = {n: np.stack([inp[n][b, h] for b, h in sel])[:, None] for n in
-           ("q", "k", "v", "a", "nu", "r", "lambda0", "S0")}
-    log(f"cpu baseline: oracle on {heads} heads x T={WL['T']} with {threads} threads")
-    t0 = time.perf_counter()
-    oracle.forward(sub["q"], sub["k"], sub["v"], sub["a"], sub["nu"], sub["r"], sub["lambda0"],
-                   sub["S0"], "diagonal", threads=threads)
-    sec = time.perf_counter() - t0
-    tokens = heads * WL["T"] / WL["H"]  # a token carries all H heads
+    heads = WL["B"] * WL["H"]
+    sub = {n: inp[n] for n in ("q", "k", "v", "a", "nu", "r", "lambda0", "S0")}
+    log(f"cpu baseline: oracle on the whole workload ({heads} heads x T={WL['T']}) "
+        f"with {threads} threads, for at least {args.cpu_seconds} s")
+    reps, sec = 0, 0.0
+    while reps == 0 or sec < args.cpu_seconds:
+        t0 = time.perf_counter()
+        oracle.forward(sub["q"], sub["k"], sub["v"], sub["a"], sub["nu"], sub["r"],
+                       sub["lambda0"], sub["S0"], "diagonal", threads=threads)
+        sec += time.perf_counter() - t0
+        reps += 1
+    tokens = reps * WL["B"] * WL["T"]
     return {"value": round(tokens / sec, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{heads} of {WL['B'] * WL['H']} heads, all {WL['T']} tokens each "
-                      f"({sec:.1f} s); tokens/s counts H={WL['H']} heads as one token"}
+            "sample": f"the whole workload (B={WL['B']}, H={WL['H']}, T={WL['T']}, d=128, fp64 "
+                      f"token-by-token recurrence over the same bf16-rounded inputs) run {reps} "
+                      f"times in {sec:.1f} s; a token carries all {WL['H']} heads"}
 
 
 def main():
@@ -227,7 +283,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum wall time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,

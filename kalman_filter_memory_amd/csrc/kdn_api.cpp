@@ -146,7 +146,8 @@ kdn_status kdn_forward_events(const kdn_desc* d, const void* q, const void* k, c
     void* tm = at(ws, w.tm);
     float* g = reinterpret_cast<float*>(at(ws, w.g));
     auto mark = [&](int i) {
-        if (events && events[i]) hipEventRecord(static_cast<hipEvent_t>(events[i]), hs);
+        // a failed record only loses a timing mark; the kernels' status is what is returned
+        if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), hs);
     };
     mark(0);
     hipError_t e = kdn::launch_scan_reduce(s, k, a, qnoise, r, agg, hs);

@@ -38,6 +38,9 @@ constexpr int kThreads = 256;
 constexpr int kLdsLimit = 160 * 1024;
 
 // ---------------------------------------------------------------- helpers
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
+constexpr int cmin(int x, int y) { return x < y ? x : y; }
+
 template <typename E> struct Vec16 {
     static constexpr int N = 16 / sizeof(E);
 };
@@ -105,21 +108,41 @@ __device__ __forceinline__ void stage_rows(E* dst, int sld, const E* src, size_t
     }
 }
 
+// LDS of the prep kernel: two regions reused as the chunk proceeds.
+//   region 1: K [C][LDK] (input dtype), then A / T [C][LDA] (fp32)
+//   region 2: P^- k [C][LDP] (fp32, diagonal gain), then W [C][LDK] (input
+//             dtype), then the block-row scratch of the solve (fp32)
 template <typename E, int DK, int C> struct PrepLds {
-    static constexpr int PAD = Vec16<E>::N;
+    // rows padded by 32 bytes (a stride of 8 mod 16 dwords: conflict-free MFMA
+    // fragment reads)
+    static constexpr int PAD = 32 / (int)sizeof(E);
     static constexpr int LDK = DK + PAD, LDA = C + 4;
-    static constexpr int NT = C / 16;
-    static constexpr int NWALK = DK >= 64 ? DK / 64 : 1;  // waves of the precision walk
-    static constexpr int BYTES =
-        2 * C * LDK * (int)sizeof(E) + (C * LDA + NWALK * C + 2 * C) * (int)sizeof(float);
-    // block-row scratch of the solve lives in the K buffer once A is formed
-    static_assert((NT > 1 ? NT - 1 : 1) * 256 * 4 <= C * LDK * (int)sizeof(E), "scratch");
+    static constexpr int NT = C / 16;  // 16-token sub-blocks = waves of the gain pass
+    static constexpr int NPL = DK >= 64 ? DK / 64 : 1;  // key dims per lane (gain pass)
+    static constexpr int R1 = cmax(C * LDK * (int)sizeof(E), C * LDA * 4);
+    static constexpr int R2 = cmax(cmax(C * LDK * (int)sizeof(E), (NT > 1 ? NT - 1 : 1) * 256 * 4),
+                                   (NT > 1 ? NT - 1 : 1) * DK * 16);
+    static constexpr int BYTES = R1 + R2 + 2 * C * (int)sizeof(float);
 };
 
-// Sum over the 64 lanes of v[t] for every t: a transposing butterfly; on return
-// lane l holds the total of v[l].  63 exchanges instead of 64 full reductions.
+// ------------------------------------------------------------ prep kernel
+// One workgroup (4 waves) per chunk.
+//   gain (fuse_gain), diagonal: wave w takes the 16-token sub-block w and each
+//     lane NPL key dimensions.  (1) Each wave composes the Moebius maps of its
+//     sub-block; (2) wave w carries the chunk-boundary precision through the
+//     maps of sub-blocks 0..w-1 to its own start; (3) it walks its 16 tokens
+//     (predictive precision, P^- k); (4) the per-token sums k^T P^- k come from a
+//     transposing butterfly inside 16-lane groups and two cross-group
+//     exchanges; (5) w = P^- k / (k^T P^- k + r) is written by rows.
+//     Isotropic: |k|^2 per token, one scalar chain, w = k / (|k|^2 + r lambda^-).
+//   A = strict_tril(K W^T * Gamma) on MFMA and T = (I + A)^{-1} in fp32, in
+//     place: 16x16 diagonal blocks by forward substitution (one lane per
+//     column), then block rows T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA.
+
+// v[j] summed over the 16 lanes of each 16-lane group: on return lane l holds
+// in v[0] the group total of v[l % 16] (15 exchanges instead of 16 reductions)
 template <int H>
-__device__ __forceinline__ void transpose_sum_step(float (&v)[64], int lane) {
+__device__ __forceinline__ void transpose_sum_step(float (&v)[16], int lane) {
     const bool upper = (lane & H) != 0;
 #pragma unroll
     for (int j = 0; j < H; ++j) {
@@ -128,9 +151,7 @@ __device__ __forceinline__ void transpose_sum_step(float (&v)[64], int lane) {
         v[j] = keep + __shfl_xor(send, H, kWave);
     }
 }
-__device__ __forceinline__ float transpose_sum64(float (&v)[64], int lane) {
-    transpose_sum_step<32>(v, lane);
-    transpose_sum_step<16>(v, lane);
+__device__ __forceinline__ float transpose_sum16(float (&v)[16], int lane) {
     transpose_sum_step<8>(v, lane);
     transpose_sum_step<4>(v, lane);
     transpose_sum_step<2>(v, lane);
@@ -138,18 +159,6 @@ __device__ __forceinline__ float transpose_sum64(float (&v)[64], int lane) {
     return v[0];
 }
 
-// ------------------------------------------------------------ prep kernel
-// One workgroup (4 waves) per chunk.
-//   gain (fuse_gain), diagonal: from the chunk-boundary precision each lane of
-//     the walk waves follows one key dimension through the chunk (predictive
-//     precision by the step recurrence, token scalars broadcast from the lane
-//     that loaded them), keeping P^- k of every token in registers; the
-//     per-token denominators k^T P^- k + r come from a transposing butterfly
-//     across lanes; then w = P^- k / (k^T P^- k + r).  Isotropic: |k|^2 per
-//     token, one scalar chain, w = k / (|k|^2 + r lambda^-).
-//   A = strict_tril(K W^T * Gamma) on MFMA and T = (I + A)^{-1} in fp32, in
-//     place: 16x16 diagonal blocks by forward substitution (one lane per
-//     column), then block rows T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA.
 template <typename E, int DK, int C>
 __global__ __launch_bounds__(kThreads) void prep_kernel(
     const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
@@ -157,14 +166,16 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const float* __restrict__ lam_chunk, E* __restrict__ w, E* __restrict__ Tm,
     float* __restrict__ gout, int T, int NC) {
     using L = PrepLds<E, DK, C>;
-    constexpr int LDK = L::LDK, LDA = L::LDA, NT = L::NT, NWALK = L::NWALK;
-    constexpr int V = Vec16<E>::N, VPR = DK / V;
-    __shared__ __align__(16) E sK[C * LDK];
-    __shared__ __align__(16) E sW[C * LDK];
-    __shared__ __align__(16) float sAT[C * LDA];  // A, overwritten in place by T
-    __shared__ __align__(16) float spart[NWALK * C];
+    constexpr int LDK = L::LDK, LDA = L::LDA, NT = L::NT;
+    constexpr int V = Vec16<E>::N;
+    __shared__ __align__(16) unsigned char smem[L::R1 + L::R2];
     __shared__ __align__(16) float sden[C];
     __shared__ __align__(16) float sg[C];
+    E* sK = reinterpret_cast<E*>(smem);
+    float* sAT = reinterpret_cast<float*>(smem);  // after A is formed
+    float* sP = reinterpret_cast<float*>(smem + L::R1);
+    E* sW = reinterpret_cast<E*>(smem + L::R1);
+    float* sZ = reinterpret_cast<float*>(smem + L::R1);  // after A is formed
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh = blockIdx.y;
@@ -192,46 +203,95 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
             gir = 1.f / rt;
         }
     }
+    if (wave == 0) {
+        const float g = wave_incl_sum(lane < C ? log2_hw(ga) : 0.f);
+        if (lane < C) {
+            sg[lane] = g;
+            gout[(bh * NC + c) * C + lane] = g;  // for the state pass
+        }
+    }
     sync_lds();
 
     if (fuse_gain) {
         if (diag) {
-            const int i = 64 * wave + lane;
-            const bool walker = wave < NWALK && i < DK;
-            float P[C];
-            if (wave < NWALK) {
-                float lam = walker ? lam_chunk[(bh * (NC + 1) + c) * DK + i] : 1.f;
+            constexpr int NPL = L::NPL;
+            const int i0 = lane * NPL, tb0 = 16 * wave;
+            const bool act = wave < NT && i0 < DK;
+            float4* sprod = reinterpret_cast<float4*>(smem + L::R1);  // [NT-1][DK] maps
+            float kc[16][NPL];
+            M2 m[NPL];
+            if (act) {
+                // (1) the sub-block's 16 token maps composed, renormalised every 8
 #pragma unroll
-                for (int t = 0; t < C; ++t) {
-                    const float a2 = lane_value(ga2, t), nut = lane_value(gnu, t);
-                    const float ir = lane_value(gir, t);
-                    const float kv = walker ? to_f<E>(sK[t * LDK + i]) : 0.f;
-                    const float d = fmaf(nut, lam, a2);
-                    P[t] = kv * d * rcp(lam);  // P^- k
-                    const float lm = lam * rcp(d);
-                    lam = fmaf(kv * kv, ir, lm);
+                for (int j = 0; j < 16; ++j) load_dims<E, NPL>(sK + (tb0 + j) * LDK + i0, kc[j]);
+#pragma unroll
+                for (int d = 0; d < NPL; ++d) m[d] = M2{1.f, 0.f, 0.f, 1.f};
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float a2 = lane_value(ga2, tb0 + j), nut = lane_value(gnu, tb0 + j);
+                    const float ir = lane_value(gir, tb0 + j);
+#pragma unroll
+                    for (int d = 0; d < NPL; ++d) {
+                        m[d] = mob_step(m[d], kc[j][d] * kc[j][d] * ir, a2, nut);
+                        if ((j & 7) == 7) m[d] = mob_renorm(m[d]);
+                    }
                 }
-                float v[64];
+                if (wave < NT - 1) {
 #pragma unroll
-                for (int t = 0; t < 64; ++t)
-                    v[t] = (t < C && walker) ? to_f<E>(sK[t * LDK + i]) * P[t] : 0.f;
-                const float part = transpose_sum64(v, lane);
-                if (lane < C) spart[wave * C + lane] = part;
+                    for (int d = 0; d < NPL; ++d)
+                        sprod[wave * DK + i0 + d] = make_float4(m[d].a, m[d].b, m[d].c, m[d].d);
+                }
             }
             sync_lds();
-            if (tid < C) {  // wave 0: lane t holds r_t
-                float sum = gr;
+            float pk[16][NPL];
+            float den = 0.f;
+            if (act) {
+                // (2) precision at the sub-block start
+                float lam[NPL];
 #pragma unroll
-                for (int wv = 0; wv < NWALK; ++wv) sum += spart[wv * C + tid];
-                sden[tid] = 1.f / sum;
+                for (int d = 0; d < NPL; ++d) lam[d] = lam_chunk[(bh * (NC + 1) + c) * DK + i0 + d];
+                for (int sb = 0; sb < wave; ++sb) {
+#pragma unroll
+                    for (int d = 0; d < NPL; ++d) {
+                        const float4 q4 = sprod[sb * DK + i0 + d];
+                        lam[d] = mob_apply(M2{q4.x, q4.y, q4.z, q4.w}, lam[d]);
+                    }
+                }
+                // (3) walk: P^- k per token and dimension
+                float v[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float a2 = lane_value(ga2, tb0 + j), nut = lane_value(gnu, tb0 + j);
+                    const float ir = lane_value(gir, tb0 + j);
+                    v[j] = 0.f;
+#pragma unroll
+                    for (int d = 0; d < NPL; ++d) {
+                        const float kv = kc[j][d];
+                        const float dd = fmaf(nut, lam[d], a2);
+                        pk[j][d] = kv * dd * rcp(lam[d]);
+                        v[j] = fmaf(kv, pk[j][d], v[j]);
+                        lam[d] = fmaf(kv * kv, ir, lam[d] * rcp(dd));
+                    }
+                }
+                // (4) k^T P^- k of token tb0 + (lane % 16), summed over all lanes
+                den = transpose_sum16(v, lane);
             }
-            sync_lds();
-            if (walker) {
+            den += __shfl_xor(den, 16, kWave);
+            den += __shfl_xor(den, 32, kWave);
+            sync_lds();  // W overwrites the sub-block maps
+            if (act) {
+                // lane l: token tb0 + l % 16 (r gathered from the lane that loaded it)
+                const float rden = 1.f / (den + __shfl(gr, tb0 + (lane & 15), kWave));
+                // (5) w rows
 #pragma unroll
-                for (int t = 0; t < C; ++t) {
-                    const E wt = from_f<E>(P[t] * sden[t]);
-                    sW[t * LDK + i] = wt;
-                    if (t < n) w[(row0 + t) * DK + i] = wt;
+                for (int j = 0; j < 16; ++j) {
+                    const float rd = lane_value(rden, j);
+                    E out[NPL];
+#pragma unroll
+                    for (int d = 0; d < NPL; ++d) out[d] = from_f<E>(pk[j][d] * rd);
+                    const int t = tb0 + j;
+                    store_dims<E, NPL>(sW + t * LDK + i0, out);
+                    if (t < n) store_dims<E, NPL>(w + (row0 + t) * DK + i0, out);
                 }
             }
         } else {
@@ -266,6 +326,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
                 if (lane < C) sden[lane] = den_l;
             }
             sync_lds();
+            constexpr int VPR = DK / V;
             for (int e = tid; e < C * VPR; e += kThreads) {
                 const int t = e / VPR, i0 = (e % VPR) * V;
                 E out[V];
@@ -278,24 +339,44 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
             }
         }
     }
-    if (wave == 0) {
-        const float g = wave_incl_sum(lane < C ? log2_hw(ga) : 0.f);
-        if (lane < C) {
-            sg[lane] = g;
-            gout[(bh * NC + c) * C + lane] = g;  // for the state pass
-        }
-    }
     sync_lds();
 
-    // A = strict_tril(K W^T * Gamma) in fp32 (zero on and above the diagonal)
-    for (int id = wave; id < NT * NT; id += 4) {
-        const int tb = id / NT, sb = id % NT;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (sb <= tb) acc = mma_tile<E>(acc, sK, LDK, 16 * tb, sW, LDK, 16 * sb, 0, DK, lane);
+    // A = strict_tril(K W^T * Gamma) in fp32 (zero on and above the diagonal):
+    // the NT (NT + 1) / 2 lower tiles dealt round-robin to the waves, computed
+    // into registers, written over K after a barrier
+    constexpr int NTILE = NT * (NT + 1) / 2, TPW = (NTILE + 3) / 4;
+    floatx4 at[TPW];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 16 * tb + c_row(lane, e), s = 16 * sb + c_col(lane);
-            sAT[t * LDA + s] = (s < t) ? exp2_hw(sg[t] - sg[s]) * acc[e] : 0.f;
+    for (int x = 0; x < TPW; ++x) {
+        const int id = wave + 4 * x;
+        int tb = 0, sb = id;
+        while (sb > tb) {
+            sb -= tb + 1;
+            ++tb;
+        }
+        at[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (id < NTILE) at[x] = mma_tile<E>(at[x], sK, LDK, 16 * tb, sW, LDK, 16 * sb, 0, DK, lane);
+    }
+    sync_lds();
+    for (int e = tid; e < C * C / 4; e += kThreads) {  // zero the upper part first
+        const int t = e / (C / 4), s0 = (e % (C / 4)) * 4;
+        if ((s0 >> 4) > (t >> 4))
+            *reinterpret_cast<float4*>(sAT + t * LDA + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
+        const int id = wave + 4 * x;
+        if (id < NTILE) {
+            int tb = 0, sb = id;
+            while (sb > tb) {
+                sb -= tb + 1;
+                ++tb;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * tb + c_row(lane, e), s = 16 * sb + c_col(lane);
+                sAT[t * LDA + s] = (s < t) ? exp2_hw(sg[t] - sg[s]) * at[x][e] : 0.f;
+            }
         }
     }
     sync_lds();
@@ -317,7 +398,6 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     sync_lds();
     // block row i: Z_j = sum_{m=j}^{i-1} A_im T_mj, then T_ij = -T_ii Z_j over A_ij
     // (16x16x16 products on fp32 MFMA; T read k-major as the B operand)
-    float* sZ = reinterpret_cast<float*>(sK);  // K is no longer needed
     for (int i = 1; i < NT; ++i) {
         for (int j = wave; j < i; j += 4) {
             floatx4 z[1][1] = {{floatx4{0.f, 0.f, 0.f, 0.f}}};
@@ -736,13 +816,18 @@ template <typename E, int DK, int DVT, int C>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void state_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ gin, const E* __restrict__ w, const E* __restrict__ Tm,
-    const float* S0, E* __restrict__ o, float* S_T, int T, int DV, int NC) {
+    const float* S0, E* __restrict__ o, float* S_T, int BH, int T, int DV, int NC) {
     using G = StateCfg<E, DK, DVT, C>;
     constexpr int BI = G::BI, BV = G::BV, NVB = G::NVB;
     __shared__ __align__(16) StateLds<E, DK, DVT, C> L;
     const int tid = threadIdx.x;
-    const StateArgs<E> A{q,  k,  v,      w,   Tm,  gin,      o,         blockIdx.y,
-                         (int)blockIdx.x * DVT, T, DV, NC, tid, tid & 63, tid >> 6};
+    // Workgroups go to the 8 XCDs round-robin by linear id: the d_v tiles of one
+    // head get ids equal mod 8, so they share one XCD's L2 for K, Q, W and T.
+    const int ntile = DV / DVT, L_ = blockIdx.x, per = 8 * ntile;
+    const int head = (L_ / per) * 8 + (L_ % 8);
+    if (head >= BH) return;
+    const StateArgs<E> A{q,  k,  v,  w,  Tm, gin, o,  (size_t)head, ((L_ % per) / 8) * DVT,
+                         T,  DV, NC, tid, tid & 63, tid >> 6};
     const int lane = A.lane, wave = A.wave;
     const size_t bh = A.bh;
     const int j0 = A.j0;
@@ -857,12 +942,13 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
                    const void* w, const void* Tm, const float* S0, void* o, float* S_T,
                    hipStream_t st) {
     if constexpr (state_fits<E, DK, DVT, C>()) {
-        hipLaunchKernelGGL((state_kernel<E, DK, DVT, C>), dim3(s.dv / DVT, s.BH),
+        const int groups = (s.BH + 7) / 8;
+        hipLaunchKernelGGL((state_kernel<E, DK, DVT, C>), dim3(groups * 8 * (s.dv / DVT)),
                            dim3(StateCfg<E, DK, DVT, C>::THREADS), 0, st,
                            static_cast<const E*>(q), static_cast<const E*>(k),
                            static_cast<const E*>(v), g, static_cast<const E*>(w),
-                           static_cast<const E*>(Tm), S0, static_cast<E*>(o), S_T, s.T, s.dv,
-                           s.nc);
+                           static_cast<const E*>(Tm), S0, static_cast<E*>(o), S_T, s.BH, s.T,
+                           s.dv, s.nc);
         return hipGetLastError();
     } else {
         return hipErrorInvalidValue;

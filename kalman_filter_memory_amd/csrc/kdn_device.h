@@ -228,4 +228,64 @@ __device__ __forceinline__ floatx4 mma_tile(floatx4 acc, const E* A, int lda, in
 __device__ __forceinline__ int c_row(int lane, int e) { return 4 * (lane >> 4) + e; }
 __device__ __forceinline__ int c_col(int lane) { return lane & 15; }
 
+
+
+// N consecutive elements <-> floats (one 4-byte access for a bf16 pair)
+template <typename E, int N>
+__device__ __forceinline__ void load_dims(const E* p, float (&x)[N]) {
+    if constexpr (N == 2 && sizeof(E) == 2) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+        x[0] = __uint_as_float(u << 16);
+        x[1] = __uint_as_float(u & 0xFFFF0000u);
+    } else {
+#pragma unroll
+        for (int j = 0; j < N; ++j) x[j] = to_f<E>(p[j]);
+    }
+}
+template <typename E, int N> __device__ __forceinline__ void store_dims(E* p, const E (&x)[N]) {
+    if constexpr (N * sizeof(E) == 4) {
+        *reinterpret_cast<uint32_t*>(p) = __builtin_bit_cast(uint32_t, x);
+    } else if constexpr (N * sizeof(E) == 8) {
+        *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, x);
+    } else {
+#pragma unroll
+        for (int j = 0; j < N; ++j) p[j] = x[j];
+    }
+}
+
+// ------------------------------------------------------------ Moebius maps
+// The precision recurrence lambda_t = M_t<lambda_{t-1}> with M<x> = (m11 x +
+// m12) / (m21 x + m22) and the token matrix M_t = [[1 + b nu, b a^2], [nu, a^2]]
+// ("Kalman Delta Networks" summary, Moebius-transformation structure of the
+// precision update); maps compose by matrix product.  Entries are non-negative.
+struct M2 {
+    float a, b, c, d;  // [[a b] [c d]]
+};
+
+__device__ __forceinline__ M2 mob_mul(const M2& x, const M2& y) {
+    return {x.a * y.a + x.b * y.c, x.a * y.b + x.b * y.d, x.c * y.a + x.d * y.c,
+            x.c * y.b + x.d * y.d};
+}
+
+// scale by the power of two that brings the largest entry into [0.5, 1)
+__device__ __forceinline__ M2 mob_renorm(const M2& m) {
+    const float mx = fmaxf(fmaxf(m.a, m.b), fmaxf(m.c, m.d));
+    int e;
+    frexpf(mx, &e);
+    return {ldexpf(m.a, -e), ldexpf(m.b, -e), ldexpf(m.c, -e), ldexpf(m.d, -e)};
+}
+
+__device__ __forceinline__ float mob_apply(const M2& m, float x) {
+    return (m.a * x + m.b) / (m.c * x + m.d);
+}
+
+// M_t X for one token: M = U_b P with P = [[1, 0], [nu, a^2]] and U_b = [[1, b],
+// [0, 1]], so M X = [[x11 + b y1, x12 + b y2], [y1, y2]] with (y1, y2) =
+// nu (x11, x12) + a^2 (x21, x22): six multiply-adds.
+__device__ __forceinline__ M2 mob_step(const M2& x, float b, float a2, float nu) {
+    const float y1 = fmaf(nu, x.a, a2 * x.c);
+    const float y2 = fmaf(nu, x.b, a2 * x.d);
+    return {fmaf(b, y1, x.a), fmaf(b, y2, x.b), y1, y2};
+}
+
 }  // namespace kdn

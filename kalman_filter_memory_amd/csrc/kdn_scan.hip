@@ -27,24 +27,6 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
-struct M2 {
-    float a, b, c, d;  // [[a b] [c d]]
-};
-
-__device__ __forceinline__ M2 mul(const M2& x, const M2& y) {
-    return {x.a * y.a + x.b * y.c, x.a * y.b + x.b * y.d, x.c * y.a + x.d * y.c,
-            x.c * y.b + x.d * y.d};
-}
-
-// scale by the power of two that brings the largest entry into [0.5, 1)
-// (all entries are non-negative)
-__device__ __forceinline__ M2 renorm(const M2& m) {
-    const float mx = fmaxf(fmaxf(m.a, m.b), fmaxf(m.c, m.d));
-    int e;
-    frexpf(mx, &e);
-    return {ldexpf(m.a, -e), ldexpf(m.b, -e), ldexpf(m.c, -e), ldexpf(m.d, -e)};
-}
-
 __device__ __forceinline__ M2 shfl_down_m2(const M2& m, int off) {
     return {__shfl_down(m.a, off, kWave), __shfl_down(m.b, off, kWave),
             __shfl_down(m.c, off, kWave), __shfl_down(m.d, off, kWave)};
@@ -58,38 +40,14 @@ __device__ __forceinline__ M2 token_matrix(float b, float a2, float nu) {
     return {1.f + b * nu, b * a2, nu, a2};
 }
 
-__device__ __forceinline__ float apply(const M2& m, float x) {
-    return (m.a * x + m.b) / (m.c * x + m.d);
-}
-
 // key dimensions handled by one lane in the diagonal kernels
 template <int DK> struct Lanes {
     static constexpr int IPL = DK >= 64 ? DK / 64 : 1;  // consecutive dims per lane
     static constexpr int ACTIVE = DK / IPL;             // active lanes
 };
 
-template <typename E, int IPL>
-__device__ __forceinline__ void load_dims(const E* p, float (&x)[IPL]) {
-    if constexpr (IPL == 2 && sizeof(E) == 2) {  // one 4-byte load for a bf16 pair
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-        x[0] = __uint_as_float(u << 16);
-        x[1] = __uint_as_float(u & 0xFFFF0000u);
-    } else {
-#pragma unroll
-        for (int j = 0; j < IPL; ++j) x[j] = to_f<E>(p[j]);
-    }
-}
 
 // ------------------------------------------------------------------ reduce
-// One token's matrix factors as M = U_b P with P = [[1, 0], [nu, a^2]] and
-// U_b = [[1, b], [0, 1]], so  M X = [[x11 + b y1, x12 + b y2], [y1, y2]]  with
-// (y1, y2) = nu (x11, x12) + a^2 (x21, x22): six multiply-adds per step.
-__device__ __forceinline__ M2 step(const M2& x, float b, float a2, float nu) {
-    const float y1 = fmaf(nu, x.a, a2 * x.c);
-    const float y2 = fmaf(nu, x.b, a2 * x.d);
-    return {fmaf(b, y1, x.a), fmaf(b, y2, x.b), y1, y2};
-}
-
 // one chunk per wave, lanes over key dims; per-token scalars are computed once
 // by lane t and broadcast through scalar registers
 template <typename E, int DK, int C>
@@ -135,16 +93,16 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
             const float a2 = lane_value(ga2, t), nut = lane_value(gnu, t), ir = lane_value(gir, t);
 #pragma unroll
             for (int j = 0; j < L::IPL; ++j)
-                P[j] = step(P[j], kv[u][j] * kv[u][j] * ir, a2, nut);
+                P[j] = mob_step(P[j], kv[u][j] * kv[u][j] * ir, a2, nut);
             if ((t & 7) == 7)
 #pragma unroll
-                for (int j = 0; j < L::IPL; ++j) P[j] = renorm(P[j]);
+                for (int j = 0; j < L::IPL; ++j) P[j] = mob_renorm(P[j]);
         }
     }
     if (act) {
 #pragma unroll
         for (int j = 0; j < L::IPL; ++j) {
-            const M2 m = renorm(P[j]);
+            const M2 m = mob_renorm(P[j]);
             agg[(bh * NC + c) * DK + lane * L::IPL + j] = make_float4(m.a, m.b, m.c, m.d);
         }
     }
@@ -183,7 +141,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_iso_kernel(
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const M2 o = shfl_down_m2(P, off);
-        if ((lane & (2 * off - 1)) == 0) P = renorm(mul(o, P));
+        if ((lane & (2 * off - 1)) == 0) P = mob_renorm(mob_mul(o, P));
     }
     if (lane == 0) agg[bh * NC + c] = make_float4(P.a, P.b, P.c, P.d);
 }
@@ -271,9 +229,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void emit_iso_kernel(
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const M2 o = shfl_up_m2(P, off);
-        if (lane >= off) P = renorm(mul(P, o));
+        if (lane >= off) P = mob_renorm(mob_mul(P, o));
     }
-    const float lam_incl = apply(P, lam0);
+    const float lam_incl = mob_apply(P, lam0);
     float lam_prev = __shfl_up(lam_incl, 1, kWave);
     if (lane == 0) lam_prev = lam0;
     if (lane < n) lambda_minus[bh * T + t0 + lane] = lam_prev / (at * at + nut * lam_prev);
