@@ -440,10 +440,12 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
 //            gamma_C / gamma_t); waves 4-7: M = tril(Q W^T) * Gamma
 //   phase C  every wave: O^T += U^T M^T for its block, written out; and one
 //            block of the state update S^T <- gamma_C S^T + W^T diag(gamma_C/gamma_t) U;
-//            then the next chunk's K, W, Q, V, T, g (loaded from HBM into
-//            registers at the start of this chunk) are written to LDS with its decay
-//            tables (W into the other of two buffers, since the state update
-//            reads the current one), and the new state as the next operand.
+//            then the next chunk's K, W, Q, V, T, g (loaded from HBM into one of
+//            two register sets during the previous chunk) are written to LDS with
+//            its decay tables (W into the other of two buffers, since the state
+//            update reads the current one), and the new state as the next operand.
+//            The chunk after next is loaded into the other register set meanwhile,
+//            in three parts at the starts of the three phases.
 // Operands stored with the contraction index strided (token-major R and W) are
 // read with transposing LDS reads (ds_read_b64_tr_b16).  Barriers are LDS-only
 // (sync_lds) so that the next chunk's global loads stay in flight across them.
@@ -477,13 +479,16 @@ template <typename E, int DK, int DVT, int C> struct StateCfg {
         3 * C * (int)sizeof(float);
 };
 
-// Loads of one chunk into registers (issued at the start of the previous chunk)
-// and their staging into LDS.  The loads never branch on their results, so
-// that the waits for them can be counted exactly and placed at the staging: a
-// chunk past the end reloads the last one and rows past the end of the
-// sequence load the last valid row (those rows only reach outputs that are
-// never stored, except through W, whose padded rows are stored as zeros).
-template <typename E, int DK, int DVT, int C>
+// Loads of one chunk into registers, two chunks before its use, and their
+// staging into LDS.  The loads never branch on their results, so that the waits
+// for them can be counted exactly and placed at the staging: a chunk past the
+// end reloads the last one and rows past the end of the sequence load the last
+// valid row (those rows only reach outputs that are never stored, except
+// through W, whose padded rows are stored as zeros).  The loads come in three
+// parts issued at the starts of the three phases of a chunk: a burst of every
+// wave's loads at once would stall the waves on the vector-memory issue queue.
+enum { kLoadKQ = 0, kLoadW = 1, kLoadVTG = 2, kLoadAll = 3 };
+template <typename E, int DK, int DVT, int C, int PART>
 __device__ __forceinline__ void state_prefetch(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ w, const E* __restrict__ Tm, const float* __restrict__ gin,
@@ -496,34 +501,40 @@ __device__ __forceinline__ void state_prefetch(
     const int c = min(cc, NC - 1);
     const int t0 = c * C, n = min(C, T - t0);
     const size_t row0 = bh * T + t0;
+    if constexpr (PART == kLoadKQ || PART == kLoadW || PART == kLoadAll) {
 #pragma unroll
-    for (int x = 0; x < G::PK; ++x) {
-        const int e = tid + G::THREADS * x;
-        if (G::NVK % G::THREADS == 0 || e < G::NVK) {
-            const int t = e / (DK / VEC), c0 = (e % (DK / VEC)) * VEC;
-            const size_t off = (row0 + min(t, n - 1)) * DK + c0;
-            pk[x] = *reinterpret_cast<const u32x4*>(k + off);
-            pq[x] = *reinterpret_cast<const u32x4*>(q + off);
-            pw[x] = *reinterpret_cast<const u32x4*>(w + off);
+        for (int x = 0; x < G::PK; ++x) {
+            const int e = tid + G::THREADS * x;
+            if (G::NVK % G::THREADS == 0 || e < G::NVK) {
+                const int t = e / (DK / VEC), c0 = (e % (DK / VEC)) * VEC;
+                const size_t off = (row0 + min(t, n - 1)) * DK + c0;
+                if constexpr (PART != kLoadW) {
+                    pk[x] = *reinterpret_cast<const u32x4*>(k + off);
+                    pq[x] = *reinterpret_cast<const u32x4*>(q + off);
+                }
+                if constexpr (PART != kLoadKQ) pw[x] = *reinterpret_cast<const u32x4*>(w + off);
+            }
         }
     }
+    if constexpr (PART == kLoadVTG || PART == kLoadAll) {
 #pragma unroll
-    for (int x = 0; x < G::PV; ++x) {
-        const int e = tid + G::THREADS * x;
-        if (G::NVV % G::THREADS == 0 || e < G::NVV) {
-            const int t = e / (DVT / VEC), c0 = (e % (DVT / VEC)) * VEC;
-            pv[x] = *reinterpret_cast<const u32x4*>(v + (row0 + min(t, n - 1)) * DV + j0 + c0);
+        for (int x = 0; x < G::PV; ++x) {
+            const int e = tid + G::THREADS * x;
+            if (G::NVV % G::THREADS == 0 || e < G::NVV) {
+                const int t = e / (DVT / VEC), c0 = (e % (DVT / VEC)) * VEC;
+                pv[x] = *reinterpret_cast<const u32x4*>(v + (row0 + min(t, n - 1)) * DV + j0 + c0);
+            }
         }
-    }
-    const E* Tc = Tm + (bh * NC + c) * (size_t)(C * C);
+        const E* Tc = Tm + (bh * NC + c) * (size_t)(C * C);
 #pragma unroll
-    for (int x = 0; x < G::PT; ++x) {
-        const int e = tid + G::THREADS * x;
-        if (G::NVT % G::THREADS == 0 || e < G::NVT)
-            pt[x] = *reinterpret_cast<const u32x4*>(Tc + e * VEC);
+        for (int x = 0; x < G::PT; ++x) {
+            const int e = tid + G::THREADS * x;
+            if (G::NVT % G::THREADS == 0 || e < G::NVT)
+                pt[x] = *reinterpret_cast<const u32x4*>(Tc + e * VEC);
+        }
+        // chunk-local cumulative log2 decay (padding rows repeat the last value)
+        pg = gin[(bh * NC + c) * C + min(lane, C - 1)];
     }
-    // chunk-local cumulative log2 decay (padding rows repeat the last value)
-    pg = gin[(bh * NC + c) * C + min(lane, C - 1)];
 }
 
 template <typename E, int DK, int DVT, int C>
@@ -650,8 +661,10 @@ __device__ __forceinline__ void state_chunk(
     const int t0 = c * C, n = min(C, A.T - t0);
     const size_t row0 = A.bh * A.T + t0;
     E* sWc = L.W[c & 1];
-    state_prefetch<E, DK, DVT, C>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.bh, A.j0, A.T, A.DV, A.NC,
-                                  c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
+    __builtin_amdgcn_sched_barrier(0);
+    state_prefetch<E, DK, DVT, C, kLoadKQ>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.bh, A.j0, A.T, A.DV,
+                                           A.NC, c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
+    __builtin_amdgcn_sched_barrier(0);  // keep the three load bursts apart
 
     // ---------------- phase A: X^T = S K^T -> R ;  Y = S Q^T
     // block (jb: BVA j-tiles, tb: one t-tile); C-layout element e <->
@@ -698,6 +711,9 @@ __device__ __forceinline__ void state_chunk(
         }
     }
     sync_lds();
+    state_prefetch<E, DK, DVT, C, kLoadW>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.bh, A.j0, A.T, A.DV,
+                                          A.NC, c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
+    __builtin_amdgcn_sched_barrier(0);  // keep the three load bursts apart
 
     // ---------------- phase B
     const float gC = L.gam[C - 1];  // read before phase C restages the tables
@@ -767,6 +783,9 @@ __device__ __forceinline__ void state_chunk(
         }
     }
     sync_lds();
+    state_prefetch<E, DK, DVT, C, kLoadVTG>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.bh, A.j0, A.T,
+                                            A.DV, A.NC, c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
+    __builtin_amdgcn_sched_barrier(0);  // keep the three load bursts apart
 
     // ---------------- phase C: O^T += U^T M^T ; state update ; stage chunk c + 1
 #pragma unroll
@@ -858,10 +877,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
 
     if (NC > 0) {
-        state_prefetch<E, DK, DVT, C>(q, k, v, w, Tm, gin, bh, j0, T, DV, NC, 0, tid, lane, pkA,
-                                      pqA, pwA, pvA, ptA, pgA);
-        state_prefetch<E, DK, DVT, C>(q, k, v, w, Tm, gin, bh, j0, T, DV, NC, 1, tid, lane, pkB,
-                                      pqB, pwB, pvB, ptB, pgB);
+        state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, v, w, Tm, gin, bh, j0, T, DV, NC, 0, tid,
+                                                lane, pkA, pqA, pwA, pvA, ptA, pgA);
+        state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, v, w, Tm, gin, bh, j0, T, DV, NC, 1, tid,
+                                                lane, pkB, pqB, pwB, pvB, ptB, pgB);
         state_stage<E, DK, DVT, C>(L.K, L.Q, L.W[0], L.V, L.Tt, L.g, L.gam, L.del, min(C, T), tid,
                                    lane, wave, pkA, pqA, pwA, pvA, ptA, pgA);
     }
