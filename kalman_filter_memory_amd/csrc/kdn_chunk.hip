@@ -14,10 +14,10 @@
 // Everything except the S0 terms is local to the chunk.
 //
 // Two kernels:
-//   prep_kernel   one workgroup per chunk, all chunks in parallel: optionally
+//   prep_kernel   two chunks per workgroup, all chunks in parallel: optionally
 //                 the gain w from the chunk-boundary precision, then A and the
 //                 unit-lower-triangular inverse T (16x16 diagonal blocks by
-//                 forward substitution, off-diagonal blocks by block rows),
+//                 forward substitution, off-diagonal blocks by block columns),
 //                 all in fp32; T is stored in the input dtype.
 //   state_kernel  one workgroup per (head, d_v tile), sequential over chunks:
 //                 the S0-dependent products on MFMA (bf16 inputs: 16x16x32
@@ -108,10 +108,16 @@ __device__ __forceinline__ void stage_rows(E* dst, int sld, const E* src, size_t
     }
 }
 
+// index of the off-diagonal block (i, j), i > j, in a packed strictly lower
+// block triangle
+__device__ __forceinline__ int tri_index(int i, int j) { return i * (i - 1) / 2 + j; }
+
 // LDS of the prep kernel: two regions reused as the chunk proceeds.
-//   region 1: K [C][LDK] (input dtype), then A / T [C][LDA] (fp32)
-//   region 2: P^- k [C][LDP] (fp32, diagonal gain), then W [C][LDK] (input
-//             dtype), then the block-row scratch of the solve (fp32)
+//   region 1: K [C][LDK] (input dtype), then A with the diagonal blocks of T
+//             [C][LDA] (fp32)
+//   region 2: the sub-block Moebius maps of the gain pass, then W [C][LDK]
+//             (input dtype), then the off-diagonal blocks of T and the
+//             per-wave scratch of the solve (fp32)
 template <typename E, int DK, int C> struct PrepLds {
     // rows padded by 32 bytes (a stride of 8 mod 16 dwords: conflict-free MFMA
     // fragment reads)
@@ -120,9 +126,14 @@ template <typename E, int DK, int C> struct PrepLds {
     static constexpr int NT = C / 16;  // 16-token sub-blocks = waves of the gain pass
     static constexpr int NPL = DK >= 64 ? DK / 64 : 1;  // key dims per lane (gain pass)
     static constexpr int R1 = cmax(C * LDK * (int)sizeof(E), C * LDA * 4);
-    static constexpr int R2 = cmax(cmax(C * LDK * (int)sizeof(E), (NT > 1 ? NT - 1 : 1) * 256 * 4),
+    // region 2 also holds the off-diagonal blocks of T and one 16x16 fp32
+    // scratch block per wave while T is formed
+    static constexpr int R2 = cmax(cmax(C * LDK * (int)sizeof(E), (NT * (NT - 1) / 2 + 4) * 1024),
                                    (NT > 1 ? NT - 1 : 1) * DK * 16);
     static constexpr int BYTES = R1 + R2 + 2 * C * (int)sizeof(float);
+    // 16-byte pieces of one chunk's K per thread
+    static constexpr int NV = C * DK / Vec16<E>::N;
+    static constexpr int IT = (NV + kThreads - 1) / kThreads;
 };
 
 // ------------------------------------------------------------ prep kernel
@@ -135,9 +146,10 @@ template <typename E, int DK, int C> struct PrepLds {
 //     transposing butterfly inside 16-lane groups and two cross-group
 //     exchanges; (5) w = P^- k / (k^T P^- k + r) is written by rows.
 //     Isotropic: |k|^2 per token, one scalar chain, w = k / (|k|^2 + r lambda^-).
-//   A = strict_tril(K W^T * Gamma) on MFMA and T = (I + A)^{-1} in fp32, in
-//     place: 16x16 diagonal blocks by forward substitution (one lane per
-//     column), then block rows T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA.
+//   A = strict_tril(K W^T * Gamma) on MFMA and T = (I + A)^{-1} in fp32:
+//     16x16 diagonal blocks in place by forward substitution (one lane per
+//     column, all blocks in one wave), then block columns T_ij = -T_ii
+//     sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA, one wave per block column.
 
 // v[j] summed over the 16 lanes of each 16-lane group: on return lane l holds
 // in v[0] the group total of v[l % 16] (15 exchanges instead of 16 reductions)
@@ -159,49 +171,96 @@ __device__ __forceinline__ float transpose_sum16(float (&v)[16], int lane) {
     return v[0];
 }
 
-template <typename E, int DK, int C>
-__global__ __launch_bounds__(kThreads) void prep_kernel(
-    const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
-    const void* __restrict__ r, bool gate_bf16, bool diag, bool fuse_gain,
-    const float* __restrict__ lam_chunk, E* __restrict__ w, E* __restrict__ Tm,
-    float* __restrict__ gout, int T, int NC) {
+// One chunk's inputs, loaded into registers ahead of their use: K rows, the
+// gates of token `lane` (in their storage type G, widened only when used, so
+// that no wait for the load is forced early) and the chunk-boundary precision
+// of the lane's key dimensions.  Rows past the end of the sequence load the
+// last valid row and are zeroed when staged.
+template <typename E, typename G, int DK, int C> struct PrepIn {
+    u32x4 k[PrepLds<E, DK, C>::IT];
+    G a, nu, r;
+    float lam[PrepLds<E, DK, C>::NPL];
+};
+
+template <typename E, typename G, int DK, int C, bool FUSE>
+__device__ __forceinline__ void prep_fetch(const E* __restrict__ k, const G* __restrict__ a,
+                                           const G* __restrict__ nu, const G* __restrict__ r,
+                                           bool diag, const float* __restrict__ lam_chunk,
+                                           size_t bh, int c, int T, int NC, int tid,
+                                           PrepIn<E, G, DK, C>& in) {
     using L = PrepLds<E, DK, C>;
-    constexpr int LDK = L::LDK, LDA = L::LDA, NT = L::NT;
-    constexpr int V = Vec16<E>::N;
-    __shared__ __align__(16) unsigned char smem[L::R1 + L::R2];
-    __shared__ __align__(16) float sden[C];
-    __shared__ __align__(16) float sg[C];
+    constexpr int V = Vec16<E>::N, VPR = DK / V, NPL = L::NPL;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int t0 = c * C, n = min(C, T - t0);
+    const size_t row0 = bh * T + t0;
+#pragma unroll
+    for (int x = 0; x < L::IT; ++x) {
+        const int e = tid + kThreads * x;
+        if (L::NV % kThreads == 0 || e < L::NV) {
+            const int t = e / VPR, c0 = (e % VPR) * V;
+            in.k[x] = *reinterpret_cast<const u32x4*>(k + (row0 + min(t, n - 1)) * DK + c0);
+        }
+    }
+    const size_t tok = row0 + min(lane, n - 1);
+    in.a = a[tok];
+    in.nu = from_f<G>(0.f);
+    in.r = from_f<G>(1.f);
+#pragma unroll
+    for (int d = 0; d < NPL; ++d) in.lam[d] = 1.f;
+    if constexpr (FUSE) {
+        in.nu = nu[tok];
+        in.r = r[tok];
+        if (diag) {
+            const int i0 = lane * NPL;
+            if (wave < L::NT && i0 < DK) {
+#pragma unroll
+                for (int d = 0; d < NPL; ++d)
+                    in.lam[d] = lam_chunk[(bh * (NC + 1) + c) * DK + i0 + d];
+            }
+        } else if (wave == 0) {
+            in.lam[0] = lam_chunk[bh * (NC + 1) + c];
+        }
+    }
+}
+
+// The work of one chunk; LDS as in PrepLds, inputs already in registers.
+template <typename E, typename G, int DK, int C, bool FUSE>
+__device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
+                                           E* __restrict__ Tm, float* __restrict__ gout, int T,
+                                           int NC, size_t bh, int c, const PrepIn<E, G, DK, C>& in,
+                                           unsigned char* smem, float* sden, float* sg) {
+    using L = PrepLds<E, DK, C>;
+    constexpr int LDK = L::LDK, LDA = L::LDA, NT = L::NT, NPL = L::NPL;
+    constexpr int V = Vec16<E>::N, VPR = DK / V;
     E* sK = reinterpret_cast<E*>(smem);
     float* sAT = reinterpret_cast<float*>(smem);  // after A is formed
-    float* sP = reinterpret_cast<float*>(smem + L::R1);
     E* sW = reinterpret_cast<E*>(smem + L::R1);
     float* sZ = reinterpret_cast<float*>(smem + L::R1);  // after A is formed
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t bh = blockIdx.y;
-    const int c = blockIdx.x;
     const int t0 = c * C, n = min(C, T - t0);
     const size_t row0 = bh * T + t0;
 
-    stage_rows<E, C, DK>(sK, LDK, k + row0 * DK, DK, n);
-    if (!fuse_gain) stage_rows<E, C, DK>(sW, LDK, w + row0 * DK, DK, n);
+    // stage K; rows past the end of the sequence are zero.  A given W (no fused
+    // gain: a stage call, not the forward) is read here directly.
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int x = 0; x < L::IT; ++x) {
+        const int e = tid + kThreads * x;
+        if (L::NV % kThreads == 0 || e < L::NV) {
+            const int t = e / VPR, c0 = (e % VPR) * V;
+            *reinterpret_cast<u32x4*>(sK + t * LDK + c0) = (t < n) ? in.k[x] : zero;
+        }
+    }
+    if constexpr (!FUSE) stage_rows<E, C, DK>(sW, LDK, w_in + row0 * DK, DK, n);
     // lane t of every wave: the gates of token t (padding: a = 1, nu = 0, r = 1)
     float ga = 1.f, ga2 = 1.f, gnu = 0.f, gr = 1.f, gir = 1.f;
-    {
-        const size_t tok = row0 + min(lane, n - 1);
-        const float at = load_gate(a, tok, gate_bf16);
-        float rt = 1.f, nut = 0.f;
-        if (fuse_gain) {
-            rt = load_gate(r, tok, gate_bf16);
-            nut = load_gate(nu, tok, gate_bf16);
-        }
-        if (lane < n) {
-            ga = at;
-            ga2 = at * at;
-            gnu = nut;
-            gr = rt;
-            gir = 1.f / rt;
-        }
+    if (lane < n) {
+        ga = to_f<G>(in.a);
+        ga2 = ga * ga;
+        gnu = to_f<G>(in.nu);
+        gr = to_f<G>(in.r);
+        gir = 1.f / gr;
     }
     if (wave == 0) {
         const float g = wave_incl_sum(lane < C ? log2_hw(ga) : 0.f);
@@ -212,9 +271,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     }
     sync_lds();
 
-    if (fuse_gain) {
+    if constexpr (FUSE) {
         if (diag) {
-            constexpr int NPL = L::NPL;
             const int i0 = lane * NPL, tb0 = 16 * wave;
             const bool act = wave < NT && i0 < DK;
             float4* sprod = reinterpret_cast<float4*>(smem + L::R1);  // [NT-1][DK] maps
@@ -249,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
                 // (2) precision at the sub-block start
                 float lam[NPL];
 #pragma unroll
-                for (int d = 0; d < NPL; ++d) lam[d] = lam_chunk[(bh * (NC + 1) + c) * DK + i0 + d];
+                for (int d = 0; d < NPL; ++d) lam[d] = in.lam[d];
                 for (int sb = 0; sb < wave; ++sb) {
 #pragma unroll
                     for (int d = 0; d < NPL; ++d) {
@@ -257,7 +315,11 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
                         lam[d] = mob_apply(M2{q4.x, q4.y, q4.z, q4.w}, lam[d]);
                     }
                 }
-                // (3) walk: P^- k per token and dimension
+                // (3) walk in variance form, P = 1 / lambda: P^- = a^2 P + nu, then
+                // P = P^- / (1 + b P^-) (one reciprocal per token); P^- k per token
+                float pv[NPL];
+#pragma unroll
+                for (int d = 0; d < NPL; ++d) pv[d] = rcp(lam[d]);
                 float v[16];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
@@ -267,10 +329,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
 #pragma unroll
                     for (int d = 0; d < NPL; ++d) {
                         const float kv = kc[j][d];
-                        const float dd = fmaf(nut, lam[d], a2);
-                        pk[j][d] = kv * dd * rcp(lam[d]);
+                        const float pm = fmaf(a2, pv[d], nut);
+                        pk[j][d] = kv * pm;
                         v[j] = fmaf(kv, pk[j][d], v[j]);
-                        lam[d] = fmaf(kv * kv, ir, lam[d] * rcp(dd));
+                        pv[d] = pm * rcp(fmaf(pm, kv * kv * ir, 1.f));
                     }
                 }
                 // (4) k^T P^- k of token tb0 + (lane % 16), summed over all lanes
@@ -315,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
             sync_lds();
             if (wave == 0) {
                 const float kk_l = lane < C ? sden[lane] : 0.f;
-                float lam = lam_chunk[bh * (NC + 1) + c];
+                float lam = in.lam[0];
                 float den_l = 1.f;
                 for (int t = 0; t < C; ++t) {
                     const float kk = lane_value(kk_l, t);
@@ -381,51 +443,95 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     }
     sync_lds();
 
-    // diagonal 16x16 blocks, in place: forward substitution, one lane per column
-    // (row t of A is read before row t of T is written)
-    if (wave < NT && lane < 16) {
-        const int b0 = 16 * wave;
+    // diagonal 16x16 blocks, in place, all in one wave: forward substitution with
+    // lane 16 b + j on column j of block b (row t of A is read before row t of T
+    // is written)
+    if (wave == 0 && (lane >> 4) < NT) {
+        const int b0 = 16 * (lane >> 4), col = lane & 15;
         float x[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            float acc = (t == lane) ? 1.f : 0.f;
+            float acc = (t == col) ? 1.f : 0.f;
 #pragma unroll
             for (int s = 0; s < t; ++s) acc -= sAT[(b0 + t) * LDA + b0 + s] * x[s];
             x[t] = acc;
-            sAT[(b0 + t) * LDA + b0 + lane] = acc;
+            sAT[(b0 + t) * LDA + b0 + col] = acc;
         }
     }
     sync_lds();
-    // block row i: Z_j = sum_{m=j}^{i-1} A_im T_mj, then T_ij = -T_ii Z_j over A_ij
-    // (16x16x16 products on fp32 MFMA; T read k-major as the B operand)
-    for (int i = 1; i < NT; ++i) {
-        for (int j = wave; j < i; j += 4) {
+    // off-diagonal blocks by block columns: wave j forms T_ij for i = j+1, j+2, ...
+    // in order, T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, on 16x16x16 fp32 MFMA
+    // products.  A stays in place (the other waves still read it); T_ij goes to
+    // its own block of sTo, and Z passes through a wave-private scratch block, so
+    // a wave depends only on its own earlier blocks: no barrier between steps.
+    float* sTo = sZ;                               // [NT (NT - 1) / 2][16][16]
+    float* sZw = sZ + 256 * (NT * (NT - 1) / 2) + 256 * wave;  // [16][16] per wave
+    if (wave < NT - 1) {
+        const int j = wave;
+        for (int i = j + 1; i < NT; ++i) {
             floatx4 z[1][1] = {{floatx4{0.f, 0.f, 0.f, 0.f}}};
-            for (int m = j; m < i; ++m)
+            // m = j: A_ij T_jj (T_jj in place)
+            mma_block<float, 1, 1, false, true>(z, sAT + 16 * j, LDA, 16 * i, sAT + 16 * j * LDA,
+                                                LDA, 16 * j, 0, 16, lane);
+            for (int m = j + 1; m < i; ++m)
                 mma_block<float, 1, 1, false, true>(z, sAT + 16 * m, LDA, 16 * i,
-                                                    sAT + 16 * m * LDA, LDA, 16 * j, 0, 16, lane);
+                                                    sTo + 256 * tri_index(m, j), 16, 0, 0, 16,
+                                                    lane);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sZ[(j << 8) + (c_row(lane, e) << 4) + c_col(lane)] = z[0][0][e];
-        }
-        sync_lds();
-        for (int j = wave; j < i; j += 4) {
+            for (int e = 0; e < 4; ++e) sZw[(c_row(lane, e) << 4) + c_col(lane)] = z[0][0][e];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // Z is read back below
             floatx4 tij[1][1] = {{floatx4{0.f, 0.f, 0.f, 0.f}}};
-            mma_block<float, 1, 1, false, true>(tij, sAT + 16 * i, LDA, 16 * i, sZ + (j << 8), 16,
-                                                0, 0, 16, lane);
+            mma_block<float, 1, 1, false, true>(tij, sAT + 16 * i, LDA, 16 * i, sZw, 16, 0, 0, 16,
+                                                lane);
+            float* dst = sTo + 256 * tri_index(i, j);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sAT[(16 * i + c_row(lane, e)) * LDA + 16 * j + c_col(lane)] = -tij[0][0][e];
+            for (int e = 0; e < 4; ++e) dst[(c_row(lane, e) << 4) + c_col(lane)] = -tij[0][0][e];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // T_ij is read in the next step
         }
-        sync_lds();
     }
+    sync_lds();
     E* Tout = Tm + (bh * NC + c) * (size_t)(C * C);
     for (int e = tid; e < C * C / V; e += kThreads) {
         const int t = e / (C / V), s0 = (e % (C / V)) * V;
+        const int tb = t >> 4, sb = s0 >> 4;
         E out[V];
+        if (sb == tb) {
 #pragma unroll
-        for (int j = 0; j < V; ++j) out[j] = from_f<E>(sAT[t * LDA + s0 + j]);
+            for (int j = 0; j < V; ++j) out[j] = from_f<E>(sAT[t * LDA + s0 + j]);
+        } else if (sb < tb) {
+            const float* src = sTo + 256 * tri_index(tb, sb) + ((t & 15) << 4) + (s0 & 15);
+#pragma unroll
+            for (int j = 0; j < V; ++j) out[j] = from_f<E>(src[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < V; ++j) out[j] = from_f<E>(0.f);
+        }
         *reinterpret_cast<uint4*>(Tout + t * C + s0) = *reinterpret_cast<const uint4*>(out);
+    }
+}
+
+// Two chunks per workgroup (2 blockIdx.x and the next): the second chunk's
+// inputs are loaded at the start and arrive while the first is processed.
+template <typename E, typename G, int DK, int C, bool FUSE>
+__global__ __launch_bounds__(kThreads) void prep_kernel(
+    const E* __restrict__ k, const G* __restrict__ a, const G* __restrict__ nu,
+    const G* __restrict__ r, bool diag, const float* __restrict__ lam_chunk, E* __restrict__ w,
+    E* __restrict__ Tm, float* __restrict__ gout, int T, int NC) {
+    using L = PrepLds<E, DK, C>;
+    __shared__ __align__(16) unsigned char smem[L::R1 + L::R2];
+    __shared__ __align__(16) float sden[C];
+    __shared__ __align__(16) float sg[C];
+    const int tid = threadIdx.x;
+    const size_t bh = blockIdx.y;
+    const int c0 = 2 * blockIdx.x, c1 = c0 + 1;
+    PrepIn<E, G, DK, C> in0, in1;
+    prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, bh, c0, T, NC, tid, in0);
+    prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, bh, min(c1, NC - 1), T, NC, tid,
+                                  in1);
+    prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, T, NC, bh, c0, in0, smem, sden, sg);
+    if (c1 < NC) {
+        sync_lds();  // the second chunk's staging overwrites K / A / T
+        prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, T, NC, bh, c1, in1, smem, sden, sg);
     }
 }
 
@@ -946,13 +1052,21 @@ int dv_tile(const Shape& s) {
                       : dv_tile_e<float>(s.dk, s.dv, s.chunk);
 }
 
-template <typename E, int DK, int C>
+template <typename E, typename G, int DK, int C>
 hipError_t prep_t(const Shape& s, bool fuse, const void* k, const void* a, const void* nu,
                   const void* r, const float* lc, void* w, void* Tm, float* g, hipStream_t st) {
     static_assert(PrepLds<E, DK, C>::BYTES <= kLdsLimit, "prep LDS");
-    hipLaunchKernelGGL((prep_kernel<E, DK, C>), dim3(s.nc, s.BH), dim3(kThreads), 0, st,
-                       static_cast<const E*>(k), a, nu, r, s.gate_bf16, s.diag, fuse, lc,
-                       static_cast<E*>(w), static_cast<E*>(Tm), g, s.T, s.nc);
+    const dim3 grid((s.nc + 1) / 2, s.BH);
+    if (fuse)
+        hipLaunchKernelGGL((prep_kernel<E, G, DK, C, true>), grid, dim3(kThreads), 0, st,
+                           static_cast<const E*>(k), static_cast<const G*>(a),
+                           static_cast<const G*>(nu), static_cast<const G*>(r), s.diag, lc,
+                           static_cast<E*>(w), static_cast<E*>(Tm), g, s.T, s.nc);
+    else
+        hipLaunchKernelGGL((prep_kernel<E, G, DK, C, false>), grid, dim3(kThreads), 0, st,
+                           static_cast<const E*>(k), static_cast<const G*>(a),
+                           static_cast<const G*>(nu), static_cast<const G*>(r), s.diag, lc,
+                           static_cast<E*>(w), static_cast<E*>(Tm), g, s.T, s.nc);
     return hipGetLastError();
 }
 
@@ -977,9 +1091,10 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
 template <typename E>
 hipError_t prep_e(const Shape& s, bool fuse, const void* k, const void* a, const void* nu,
                   const void* r, const float* lc, void* w, void* Tm, float* g, hipStream_t st) {
-#define KDN_PREP(DK_, C_) \
-    if (s.dk == DK_ && s.chunk == C_)   \
-        return prep_t<E, DK_, C_>(s, fuse, k, a, nu, r, lc, w, Tm, g, st);
+#define KDN_PREP(DK_, C_)                                                                 \
+    if (s.dk == DK_ && s.chunk == C_)                                                     \
+        return s.gate_bf16 ? prep_t<E, bf16_t, DK_, C_>(s, fuse, k, a, nu, r, lc, w, Tm, g, st) \
+                           : prep_t<E, float, DK_, C_>(s, fuse, k, a, nu, r, lc, w, Tm, g, st);
 #define KDN_PREP_C(DK_) KDN_PREP(DK_, 16) KDN_PREP(DK_, 32) KDN_PREP(DK_, 64)
     KDN_PREP_C(32) KDN_PREP_C(64) KDN_PREP_C(128)
 #undef KDN_PREP_C
