@@ -112,6 +112,31 @@ __device__ __forceinline__ void stage_rows(E* dst, int sld, const E* src, size_t
 // block triangle
 __device__ __forceinline__ int tri_index(int i, int j) { return i * (i - 1) / 2 + j; }
 
+// 16x16 fp32 blocks of the solve, stored [n][k] with a padded row
+constexpr int kBld = 20, kBlk = 16 * kBld;
+
+// acc += A Bt^T for 16x16 blocks: A row-major [m][k] (row stride lda), Bt
+// stored [n][k] (row stride kBld).  Each lane reads one 16-byte piece of each;
+// the four 16x16x4 fp32 MFMA steps take the contraction in the order
+// k = 4 (lane / 16) + step on both operands, which covers every k once.
+__device__ __forceinline__ floatx4 mma16_f32(floatx4 acc, const float* A, int lda,
+                                             const float* Bt, int lane) {
+    const float4 a4 = *reinterpret_cast<const float4*>(A + (lane & 15) * lda + 4 * (lane >> 4));
+    const float4 b4 = *reinterpret_cast<const float4*>(Bt + (lane & 15) * kBld + 4 * (lane >> 4));
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, b4.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, b4.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, b4.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, b4.w, acc, 0, 0, 0);
+    return acc;
+}
+
+// a 16x16 MFMA result (lane l: rows 4 (l / 16) + e, column l % 16) stored
+// transposed, [n][m], one 16-byte store per lane
+__device__ __forceinline__ void store_ct(float* dst, floatx4 v, int lane) {
+    *reinterpret_cast<float4*>(dst + (lane & 15) * kBld + 4 * (lane >> 4)) =
+        make_float4(v[0], v[1], v[2], v[3]);
+}
+
 // LDS of the prep kernel: two regions reused as the chunk proceeds.
 //   region 1: K [C][LDK] (input dtype), then A with the diagonal blocks of T
 //             [C][LDA] (fp32)
@@ -122,14 +147,15 @@ template <typename E, int DK, int C> struct PrepLds {
     // rows padded by 32 bytes (a stride of 8 mod 16 dwords: conflict-free MFMA
     // fragment reads)
     static constexpr int PAD = 32 / (int)sizeof(E);
-    static constexpr int LDK = DK + PAD, LDA = C + 4;
+    static constexpr int LDK = DK + PAD, LDA = C + 8;
     static constexpr int NT = C / 16;  // 16-token sub-blocks = waves of the gain pass
     static constexpr int NPL = DK >= 64 ? DK / 64 : 1;  // key dims per lane (gain pass)
     static constexpr int R1 = cmax(C * LDK * (int)sizeof(E), C * LDA * 4);
     // region 2 also holds the off-diagonal blocks of T and one 16x16 fp32
     // scratch block per wave while T is formed
-    static constexpr int R2 = cmax(cmax(C * LDK * (int)sizeof(E), (NT * (NT - 1) / 2 + 4) * 1024),
-                                   (NT > 1 ? NT - 1 : 1) * DK * 16);
+    static constexpr int R2 =
+        cmax(cmax(C * LDK * (int)sizeof(E), (NT * (NT - 1) / 2 + NT + 4) * kBlk * 4),
+             (NT > 1 ? NT - 1 : 1) * DK * 16);
     static constexpr int BYTES = R1 + R2 + 2 * C * (int)sizeof(float);
     // 16-byte pieces of one chunk's K per thread
     static constexpr int NV = C * DK / Vec16<E>::N;
@@ -416,8 +442,10 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
             sb -= tb + 1;
             ++tb;
         }
+        // the transposed tile W K^T: lane l holds 4 consecutive columns of row
+        // 16 tb + l % 16 of A, written with one 16-byte store
         at[x] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (id < NTILE) at[x] = mma_tile<E>(at[x], sK, LDK, 16 * tb, sW, LDK, 16 * sb, 0, DK, lane);
+        if (id < NTILE) at[x] = mma_tile<E>(at[x], sW, LDK, 16 * sb, sK, LDK, 16 * tb, 0, DK, lane);
     }
     sync_lds();
     for (int e = tid; e < C * C / 4; e += kThreads) {  // zero the upper part first
@@ -434,11 +462,15 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
                 sb -= tb + 1;
                 ++tb;
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * tb + c_row(lane, e), s = 16 * sb + c_col(lane);
-                sAT[t * LDA + s] = (s < t) ? exp2_hw(sg[t] - sg[s]) * at[x][e] : 0.f;
-            }
+            const int t = 16 * tb + c_col(lane), s0 = 16 * sb + c_row(lane, 0);
+            const float gt = sg[t];
+            const float4 gs = *reinterpret_cast<const float4*>(sg + s0);
+            const floatx4 v = at[x];
+            *reinterpret_cast<float4*>(sAT + t * LDA + s0) =
+                make_float4((s0 + 0 < t) ? exp2_hw(gt - gs.x) * v[0] : 0.f,
+                            (s0 + 1 < t) ? exp2_hw(gt - gs.y) * v[1] : 0.f,
+                            (s0 + 2 < t) ? exp2_hw(gt - gs.z) * v[2] : 0.f,
+                            (s0 + 3 < t) ? exp2_hw(gt - gs.w) * v[3] : 0.f);
         }
     }
     sync_lds();
@@ -446,47 +478,57 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
     // diagonal 16x16 blocks, in place, all in one wave: forward substitution with
     // lane 16 b + j on column j of block b (row t of A is read before row t of T
     // is written)
+    float* sTo = sZ;                                      // [NT (NT - 1) / 2] blocks
+    float* sTd = sZ + kBlk * (NT * (NT - 1) / 2);          // [NT] blocks
+    float* sZw = sTd + kBlk * NT + kBlk * wave;            // per-wave scratch block
     if (wave == 0 && (lane >> 4) < NT) {
         const int b0 = 16 * (lane >> 4), col = lane & 15;
         float x[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
+            float arow[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 a4 = *reinterpret_cast<const float4*>(sAT + (b0 + t) * LDA + b0 + 4 * q);
+                arow[4 * q] = a4.x;
+                arow[4 * q + 1] = a4.y;
+                arow[4 * q + 2] = a4.z;
+                arow[4 * q + 3] = a4.w;
+            }
             float acc = (t == col) ? 1.f : 0.f;
 #pragma unroll
-            for (int s = 0; s < t; ++s) acc -= sAT[(b0 + t) * LDA + b0 + s] * x[s];
+            for (int s = 0; s < t; ++s) acc -= arow[s] * x[s];
             x[t] = acc;
             sAT[(b0 + t) * LDA + b0 + col] = acc;
         }
+        // T_bb^T (column col of T_bb as a row), the operand layout of the solve
+        float* dst = sTd + kBlk * (lane >> 4) + col * kBld;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(dst + 4 * q) =
+                make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
     }
     sync_lds();
     // off-diagonal blocks by block columns: wave j forms T_ij for i = j+1, j+2, ...
-    // in order, T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, on 16x16x16 fp32 MFMA
-    // products.  A stays in place (the other waves still read it); T_ij goes to
-    // its own block of sTo, and Z passes through a wave-private scratch block, so
-    // a wave depends only on its own earlier blocks: no barrier between steps.
-    float* sTo = sZ;                               // [NT (NT - 1) / 2][16][16]
-    float* sZw = sZ + 256 * (NT * (NT - 1) / 2) + 256 * wave;  // [16][16] per wave
+    // in order, T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, on fp32 MFMA.  A stays in
+    // place (the other waves still read it); the T_ij (and Z) are kept
+    // transposed, [n][k], in blocks of their own, so every operand fragment is
+    // one 16-byte read and a wave depends only on its own earlier blocks: no
+    // barrier between steps.
     if (wave < NT - 1) {
         const int j = wave;
         for (int i = j + 1; i < NT; ++i) {
-            floatx4 z[1][1] = {{floatx4{0.f, 0.f, 0.f, 0.f}}};
-            // m = j: A_ij T_jj (T_jj in place)
-            mma_block<float, 1, 1, false, true>(z, sAT + 16 * j, LDA, 16 * i, sAT + 16 * j * LDA,
-                                                LDA, 16 * j, 0, 16, lane);
+            floatx4 z = {0.f, 0.f, 0.f, 0.f};
+            z = mma16_f32(z, sAT + 16 * i * LDA + 16 * j, LDA, sTd + kBlk * j, lane);
             for (int m = j + 1; m < i; ++m)
-                mma_block<float, 1, 1, false, true>(z, sAT + 16 * m, LDA, 16 * i,
-                                                    sTo + 256 * tri_index(m, j), 16, 0, 0, 16,
-                                                    lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sZw[(c_row(lane, e) << 4) + c_col(lane)] = z[0][0][e];
+                z = mma16_f32(z, sAT + 16 * i * LDA + 16 * m, LDA, sTo + kBlk * tri_index(m, j),
+                              lane);
+            store_ct(sZw, z, lane);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // Z is read back below
-            floatx4 tij[1][1] = {{floatx4{0.f, 0.f, 0.f, 0.f}}};
-            mma_block<float, 1, 1, false, true>(tij, sAT + 16 * i, LDA, 16 * i, sZw, 16, 0, 0, 16,
-                                                lane);
-            float* dst = sTo + 256 * tri_index(i, j);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[(c_row(lane, e) << 4) + c_col(lane)] = -tij[0][0][e];
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // T_ij is read in the next step
+            floatx4 tij = {0.f, 0.f, 0.f, 0.f};
+            tij = mma16_f32(tij, sAT + 16 * i * LDA + 16 * i, LDA, sZw, lane);
+            store_ct(sTo + kBlk * tri_index(i, j), -tij, lane);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read in the next step
         }
     }
     sync_lds();
@@ -498,10 +540,10 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
         if (sb == tb) {
 #pragma unroll
             for (int j = 0; j < V; ++j) out[j] = from_f<E>(sAT[t * LDA + s0 + j]);
-        } else if (sb < tb) {
-            const float* src = sTo + 256 * tri_index(tb, sb) + ((t & 15) << 4) + (s0 & 15);
+        } else if (sb < tb) {  // stored transposed
+            const float* src = sTo + kBlk * tri_index(tb, sb) + (s0 & 15) * kBld + (t & 15);
 #pragma unroll
-            for (int j = 0; j < V; ++j) out[j] = from_f<E>(src[j]);
+            for (int j = 0; j < V; ++j) out[j] = from_f<E>(src[j * kBld]);
         } else {
 #pragma unroll
             for (int j = 0; j < V; ++j) out[j] = from_f<E>(0.f);
