@@ -73,6 +73,33 @@ template <> __device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float
     x[3] = __uint_as_float(u.y & 0xFFFF0000u);
 }
 
+// Two 16x16 MFMA result tiles that neighbour along their 4-consecutive
+// dimension (lane l holds elements 4 (l / 16) .. +3 of line l % 16 in each),
+// written as 16-byte stores: the lanes of each pair of 16-lane rows swap halves
+// (v_permlane16_swap), after which lanes of even rows hold 8 consecutive
+// elements of tile 0 and lanes of odd rows 8 of tile 1.  p0 / p1: the start of
+// the lane's line in tile 0 / tile 1.
+template <typename E>
+__device__ __forceinline__ void store8x2(E* p0, E* p1, floatx4 a, floatx4 b, int lane);
+template <>
+__device__ __forceinline__ void store8x2<float>(float* p0, float* p1, floatx4 a, floatx4 b,
+                                                int lane) {
+    store4<float>(p0 + 4 * (lane >> 4), a[0], a[1], a[2], a[3]);
+    store4<float>(p1 + 4 * (lane >> 4), b[0], b[1], b[2], b[3]);
+}
+template <>
+__device__ __forceinline__ void store8x2<bf16_t>(bf16_t* p0, bf16_t* p1, floatx4 a, floatx4 b,
+                                                 int lane) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 s0 = __builtin_amdgcn_permlane16_swap(pack_bf16(a[0], a[1]),
+                                                      pack_bf16(b[0], b[1]), false, false);
+    const u32x2 s1 = __builtin_amdgcn_permlane16_swap(pack_bf16(a[2], a[3]),
+                                                      pack_bf16(b[2], b[3]), false, false);
+    const int g = lane >> 4;
+    bf16_t* dst = ((g & 1) ? p1 : p0) + 8 * (g >> 1);
+    *reinterpret_cast<u32x4*>(dst) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+}
+
 // inclusive prefix sum over the 64 lanes of a wave
 __device__ __forceinline__ float wave_incl_sum(float x) {
     const int lane = threadIdx.x & 63;
@@ -776,15 +803,12 @@ __device__ __forceinline__ void state_write(const StateAcc<E, DK, DVT, C>& accS,
         const int job = wave + G::NW * x;
         if (job < G::NSJ) {
             const int ib = (job / G::NVB) * G::BI, jb = (job % G::NVB) * G::BV;
+            static_assert(G::BI == 2, "state tiles pair along i");
 #pragma unroll
-            for (int bi = 0; bi < G::BI; ++bi)
-#pragma unroll
-                for (int bv = 0; bv < G::BV; ++bv) {
-                    const int i = 16 * (ib + bi) + 4 * (lane >> 4);
-                    const int j = 16 * (jb + bv) + (lane & 15);
-                    const floatx4 sv = accS[x][bi][bv];
-                    store4<E>(sS + j * G::LDK + i, sv[0], sv[1], sv[2], sv[3]);
-                }
+            for (int bv = 0; bv < G::BV; ++bv) {
+                E* row = sS + (16 * (jb + bv) + (lane & 15)) * G::LDK + 16 * ib;
+                store8x2<E>(row, row + 16, accS[x][0][bv], accS[x][1][bv], lane);
+            }
         }
     }
 }
@@ -846,16 +870,20 @@ __device__ __forceinline__ void state_chunk(
             }
             const int t = 16 * tb + (lane & 15);
             const float gt = L.gam[t];
+            floatx4 rv[BVA];
 #pragma unroll
             for (int bv = 0; bv < BVA; ++bv) {
                 const int j = 16 * (jb + bv) + 4 * (lane >> 4);
                 float vv[4];
                 load4<E>(L.V + t * LDV + j, vv);
                 const floatx4 xv = xt[bv][0];
-                store4<E>(L.R + t * LDV + j, vv[0] - gt * xv[0], vv[1] - gt * xv[1],
-                          vv[2] - gt * xv[2], vv[3] - gt * xv[3]);
+                rv[bv] = floatx4{vv[0] - gt * xv[0], vv[1] - gt * xv[1], vv[2] - gt * xv[2],
+                                 vv[3] - gt * xv[3]};
                 accY[x][bv][0] = accY[x][bv][0] * gt;
             }
+            static_assert(BVA == 2, "R tiles pair along j");
+            E* row = L.R + t * LDV + 16 * jb;
+            store8x2<E>(row, row + 16, rv[0], rv[1], lane);
         }
     }
     sync_lds();
@@ -879,17 +907,30 @@ __device__ __forceinline__ void state_chunk(
                     for (int bv = 0; bv < BV; ++bv) u[bt][bv] = floatx4{0.f, 0.f, 0.f, 0.f};
                 mma_block<E, BT, BV, false, true>(u, L.Tt, LDC, 16 * tb, L.R, LDV, 16 * jb, 0,
                                                   16 * (tb + BT), lane);
+                floatx4 us[BT][BV];
 #pragma unroll
                 for (int bt = 0; bt < BT; ++bt) {
                     const int t = 16 * (tb + bt) + 4 * (lane >> 4);
                     const float4 d4 = *reinterpret_cast<const float4*>(L.del + t);
 #pragma unroll
                     for (int bv = 0; bv < BV; ++bv) {
-                        const int j = 16 * (jb + bv) + (lane & 15);
                         const floatx4 uv = u[bt][bv];
+                        us[bt][bv] = floatx4{d4.x * uv[0], d4.y * uv[1], d4.z * uv[2], d4.w * uv[3]};
+                    }
+                }
+#pragma unroll
+                for (int bv = 0; bv < BV; ++bv) {
+                    const int j = 16 * (jb + bv) + (lane & 15);
+                    if constexpr (BT == 2) {
+                        store8x2<E>(L.U + j * LDC + 16 * tb, L.U + j * LDC + 16 * tb + 16,
+                                    u[0][bv], u[1][bv], lane);
+                        store8x2<E>(L.Us + j * LDC + 16 * tb, L.Us + j * LDC + 16 * tb + 16,
+                                    us[0][bv], us[1][bv], lane);
+                    } else {
+                        const int t = 16 * tb + 4 * (lane >> 4);
+                        const floatx4 uv = u[0][bv], sv = us[0][bv];
                         store4<E>(L.U + j * LDC + t, uv[0], uv[1], uv[2], uv[3]);
-                        store4<E>(L.Us + j * LDC + t, d4.x * uv[0], d4.y * uv[1], d4.z * uv[2],
-                                  d4.w * uv[3]);
+                        store4<E>(L.Us + j * LDC + t, sv[0], sv[1], sv[2], sv[3]);
                     }
                 }
             }
@@ -913,20 +954,28 @@ __device__ __forceinline__ void state_chunk(
                 mma_block<E, BT, BT>(m, sWc, LDK, 16 * sbb * BT, L.Q, LDK, 16 * tbb * BT, 0, DK,
                                      lane);
 #pragma unroll
-                for (int bs = 0; bs < BT; ++bs)
+                for (int bt = 0; bt < BT; ++bt) {
+                    const int t = 16 * (tbb * BT + bt) + (lane & 15);
+                    const float gt = L.g[t];
+                    floatx4 mm[BT];
 #pragma unroll
-                    for (int bt = 0; bt < BT; ++bt) {
+                    for (int bs = 0; bs < BT; ++bs) {
                         const int s0 = 16 * (sbb * BT + bs) + 4 * (lane >> 4);
-                        const int t = 16 * (tbb * BT + bt) + (lane & 15);
-                        const float gt = L.g[t];
                         const float4 gs = *reinterpret_cast<const float4*>(L.g + s0);
                         const floatx4 mv = m[bs][bt];
-                        store4<E>(L.M + t * LDC + s0,
-                                  (s0 + 0 <= t) ? exp2_hw(gt - gs.x) * mv[0] : 0.f,
-                                  (s0 + 1 <= t) ? exp2_hw(gt - gs.y) * mv[1] : 0.f,
-                                  (s0 + 2 <= t) ? exp2_hw(gt - gs.z) * mv[2] : 0.f,
-                                  (s0 + 3 <= t) ? exp2_hw(gt - gs.w) * mv[3] : 0.f);
+                        mm[bs] = floatx4{(s0 + 0 <= t) ? exp2_hw(gt - gs.x) * mv[0] : 0.f,
+                                         (s0 + 1 <= t) ? exp2_hw(gt - gs.y) * mv[1] : 0.f,
+                                         (s0 + 2 <= t) ? exp2_hw(gt - gs.z) * mv[2] : 0.f,
+                                         (s0 + 3 <= t) ? exp2_hw(gt - gs.w) * mv[3] : 0.f};
                     }
+                    E* row = L.M + t * LDC + 16 * sbb * BT;
+                    if constexpr (BT == 2) {
+                        store8x2<E>(row, row + 16, mm[0], mm[1], lane);
+                    } else {
+                        const floatx4 v = mm[0];
+                        store4<E>(row + 4 * (lane >> 4), v[0], v[1], v[2], v[3]);
+                    }
+                }
             }
         }
     }
