@@ -100,6 +100,59 @@ __device__ __forceinline__ void store8x2<bf16_t>(bf16_t* p0, bf16_t* p1, floatx4
     *reinterpret_cast<u32x4*>(dst) = u32x4{s0[0], s1[0], s0[1], s1[1]};
 }
 
+// the same, with the store predicated per lane (the swap involves every lane;
+// a lane stores the line it held before the swap, so its predicate is its own)
+template <typename E>
+__device__ __forceinline__ void store8x2_if(bool pred, E* p0, E* p1, floatx4 a, floatx4 b,
+                                            int lane);
+template <>
+__device__ __forceinline__ void store8x2_if<float>(bool pred, float* p0, float* p1, floatx4 a,
+                                                   floatx4 b, int lane) {
+    if (pred) store8x2<float>(p0, p1, a, b, lane);
+}
+template <>
+__device__ __forceinline__ void store8x2_if<bf16_t>(bool pred, bf16_t* p0, bf16_t* p1, floatx4 a,
+                                                    floatx4 b, int lane) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 s0 = __builtin_amdgcn_permlane16_swap(pack_bf16(a[0], a[1]),
+                                                      pack_bf16(b[0], b[1]), false, false);
+    const u32x2 s1 = __builtin_amdgcn_permlane16_swap(pack_bf16(a[2], a[3]),
+                                                      pack_bf16(b[2], b[3]), false, false);
+    const int g = lane >> 4;
+    bf16_t* dst = ((g & 1) ? p1 : p0) + 8 * (g >> 1);
+    if (pred) *reinterpret_cast<u32x4*>(dst) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+}
+
+// The inverse of store8x2: two neighbouring tiles read with 16-byte loads and
+// returned in the MFMA result layout (lane l: elements 4 (l / 16) .. +3 of its
+// line in each tile); the swap is its own inverse.
+template <typename E>
+__device__ __forceinline__ void load8x2(const E* p0, const E* p1, float (&a)[4], float (&b)[4],
+                                        int lane);
+template <>
+__device__ __forceinline__ void load8x2<float>(const float* p0, const float* p1, float (&a)[4],
+                                               float (&b)[4], int lane) {
+    load4<float>(p0 + 4 * (lane >> 4), a);
+    load4<float>(p1 + 4 * (lane >> 4), b);
+}
+template <>
+__device__ __forceinline__ void load8x2<bf16_t>(const bf16_t* p0, const bf16_t* p1,
+                                                float (&a)[4], float (&b)[4], int lane) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const int g = lane >> 4;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(((g & 1) ? p1 : p0) + 8 * (g >> 1));
+    const u32x2 s0 = __builtin_amdgcn_permlane16_swap(v[0], v[2], false, false);
+    const u32x2 s1 = __builtin_amdgcn_permlane16_swap(v[1], v[3], false, false);
+    a[0] = __uint_as_float(s0[0] << 16);
+    a[1] = __uint_as_float(s0[0] & 0xFFFF0000u);
+    a[2] = __uint_as_float(s1[0] << 16);
+    a[3] = __uint_as_float(s1[0] & 0xFFFF0000u);
+    b[0] = __uint_as_float(s0[1] << 16);
+    b[1] = __uint_as_float(s0[1] & 0xFFFF0000u);
+    b[2] = __uint_as_float(s1[1] << 16);
+    b[3] = __uint_as_float(s1[1] & 0xFFFF0000u);
+}
+
 // inclusive prefix sum over the 64 lanes of a wave
 __device__ __forceinline__ float wave_incl_sum(float x) {
     const int lane = threadIdx.x & 63;
@@ -870,18 +923,18 @@ __device__ __forceinline__ void state_chunk(
             }
             const int t = 16 * tb + (lane & 15);
             const float gt = L.gam[t];
+            static_assert(BVA == 2, "R and V tiles pair along j");
+            float vt[BVA][4];
+            load8x2<E>(L.V + t * LDV + 16 * jb, L.V + t * LDV + 16 * jb + 16, vt[0], vt[1], lane);
             floatx4 rv[BVA];
 #pragma unroll
             for (int bv = 0; bv < BVA; ++bv) {
-                const int j = 16 * (jb + bv) + 4 * (lane >> 4);
-                float vv[4];
-                load4<E>(L.V + t * LDV + j, vv);
+                const float* vv = vt[bv];
                 const floatx4 xv = xt[bv][0];
                 rv[bv] = floatx4{vv[0] - gt * xv[0], vv[1] - gt * xv[1], vv[2] - gt * xv[2],
                                  vv[3] - gt * xv[3]};
                 accY[x][bv][0] = accY[x][bv][0] * gt;
             }
-            static_assert(BVA == 2, "R tiles pair along j");
             E* row = L.R + t * LDV + 16 * jb;
             store8x2<E>(row, row + 16, rv[0], rv[1], lane);
         }
@@ -993,14 +1046,8 @@ __device__ __forceinline__ void state_chunk(
             mma_block<E, BVA, 1>(accY[x], L.U, LDC, 16 * jb, L.M, LDC, 16 * tb, 0, 16 * (tb + 1),
                                  lane);
             const int t = 16 * tb + (lane & 15);
-            if (t < n) {
-#pragma unroll
-                for (int bv = 0; bv < BVA; ++bv) {
-                    const int j = 16 * (jb + bv) + 4 * (lane >> 4);
-                    const floatx4 ov = accY[x][bv][0];
-                    store4<E>(A.o + (row0 + t) * A.DV + A.j0 + j, ov[0], ov[1], ov[2], ov[3]);
-                }
-            }
+            E* orow = A.o + (row0 + t) * A.DV + A.j0 + 16 * jb;
+            store8x2_if<E>(t < n, orow, orow + 16, accY[x][0][0], accY[x][1][0], lane);
         }
     }
 #pragma unroll
