@@ -678,6 +678,13 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
 // read with transposing LDS reads (ds_read_b64_tr_b16).  Barriers are LDS-only
 // (sync_lds) so that the next chunk's global loads stay in flight across them.
 // Decays use base-2 logarithms: g_t = sum_{s<=t} log2 a_s, Gamma_ts = 2^(g_t-g_s).
+// t-tile of a phase-A / output job: odd groups of NT jobs run the t-tiles in
+// reverse, so that the two waves sharing a SIMD (w and w + 4) get output
+// contractions of complementary depth
+template <int NT> __device__ __forceinline__ int a_tile(int job) {
+    return ((job / NT) & 1) ? NT - 1 - job % NT : job % NT;
+}
+
 template <typename E, int DK, int DVT, int C> struct StateCfg {
     static constexpr int NW = 8, THREADS = 64 * NW;
     // rows padded by 32 bytes: a row stride of 8 (mod 16) dwords lets the MFMA
@@ -898,7 +905,7 @@ __device__ __forceinline__ void state_chunk(
 #pragma unroll
     for (int x = 0; x < G::APW; ++x) {
         const int job = wave + G::NW * x;
-        const int jb = (job / NT) * BVA, tb = job % NT;
+        const int jb = (job / NT) * BVA, tb = a_tile<NT>(job);
         floatx4 xt[BVA][1];
 #pragma unroll
         for (int bv = 0; bv < BVA; ++bv) {
@@ -946,6 +953,37 @@ __device__ __forceinline__ void state_chunk(
 
     // ---------------- phase B
     const float gC = L.gam[C - 1];  // read before phase C restages the tables
+    // one 16x16 tile of M^T = W Q^T (full depth), masked and scaled, stored as
+    // M[t][s] (element e <-> s = 16 ss + 4 (lane/16) + e, t = 16 tt + lane % 16)
+    auto m_store = [&](int ss, int tt, floatx4 mv) __attribute__((always_inline)) {
+        const int s0 = 16 * ss + 4 * (lane >> 4);
+        const int t = 16 * tt + (lane & 15);
+        const float gt = L.g[t];
+        const float4 gs = *reinterpret_cast<const float4*>(L.g + s0);
+        store4<E>(L.M + t * LDC + s0, (s0 + 0 <= t) ? exp2_hw(gt - gs.x) * mv[0] : 0.f,
+                  (s0 + 1 <= t) ? exp2_hw(gt - gs.y) * mv[1] : 0.f,
+                  (s0 + 2 <= t) ? exp2_hw(gt - gs.z) * mv[2] : 0.f,
+                  (s0 + 3 <= t) ? exp2_hw(gt - gs.w) * mv[3] : 0.f);
+    };
+    constexpr bool kBalancedB = NT == 4 && G::NV == 4 && BT == 2 && BV == 2 && G::NW == 8;
+    if constexpr (kBalancedB) {
+        // 64 MFMAs per chunk, 8 per wave (2 waves per SIMD: 16 per SIMD).  Waves
+        // 0-3: the U blocks (as below); waves 0 and 1, whose U blocks are the
+        // shallow ones, also one M tile each; waves 4-7: two M tiles each that
+        // share their W fragments.
+        if (wave < 2) {
+            const int ss = wave == 0 ? 1 : 3;
+            m_store(ss, 3, mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, sWc, LDK, 16 * ss, L.Q, LDK,
+                                       48, 0, DK, lane));
+        } else if (wave >= 4) {
+            const int ss = wave < 6 ? 0 : wave - 5;             // 0, 0, 1, 2
+            const int tt = wave == 4 ? 0 : wave == 5 ? 2 : ss;  // pairs (tt, tt + 1)
+            floatx4 m[1][2] = {{floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}}};
+            mma_block<E, 1, 2>(m, sWc, LDK, 16 * ss, L.Q, LDK, 16 * tt, 0, DK, lane);
+            m_store(ss, tt, m[0][0]);
+            m_store(ss, tt + 1, m[0][1]);
+        }
+    }
     if (wave < 4) {
         // U = T R (T lower triangular: contract only up to the block's last row)
 #pragma unroll
@@ -988,7 +1026,7 @@ __device__ __forceinline__ void state_chunk(
                 }
             }
         }
-    } else {
+    } else if (!kBalancedB) {
         // M^T = W Q^T on the lower block triangle, stored as M[t][s]
 #pragma unroll
         for (int x = 0; x < G::MPW; ++x) {
@@ -1042,7 +1080,7 @@ __device__ __forceinline__ void state_chunk(
     for (int x = 0; x < G::APW; ++x) {
         const int job = wave + G::NW * x;
         if (job < G::NAJ) {
-            const int jb = (job / NT) * BVA, tb = job % NT;
+            const int jb = (job / NT) * BVA, tb = a_tile<NT>(job);
             mma_block<E, BVA, 1>(accY[x], L.U, LDC, 16 * jb, L.M, LDC, 16 * tb, 0, 16 * (tb + 1),
                                  lane);
             const int t = 16 * tb + (lane & 15);
