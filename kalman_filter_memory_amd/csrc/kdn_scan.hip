@@ -50,54 +50,83 @@ template <int DK> struct Lanes {
 // ------------------------------------------------------------------ reduce
 // one chunk per wave, lanes over key dims; per-token scalars are computed once
 // by lane t and broadcast through scalar registers
-template <typename E, int DK, int C>
+// The IPL consecutive key elements of one lane as loaded (widened when used,
+// so that every load of a chunk can be in flight before the first is needed).
+template <typename E, int IPL> struct KeyRaw;
+template <> struct KeyRaw<bf16_t, 2> {
+    typedef uint32_t type;
+    static __device__ __forceinline__ type load(const bf16_t* p) {
+        return *reinterpret_cast<const uint32_t*>(p);
+    }
+    static __device__ __forceinline__ void widen(type u, float (&x)[2]) {
+        x[0] = __uint_as_float(u << 16);
+        x[1] = __uint_as_float(u & 0xFFFF0000u);
+    }
+};
+template <> struct KeyRaw<bf16_t, 1> {
+    typedef bf16_t type;
+    static __device__ __forceinline__ type load(const bf16_t* p) { return *p; }
+    static __device__ __forceinline__ void widen(type u, float (&x)[1]) { x[0] = bf2f(u); }
+};
+template <> struct KeyRaw<float, 2> {
+    typedef float2 type;
+    static __device__ __forceinline__ type load(const float* p) {
+        return *reinterpret_cast<const float2*>(p);
+    }
+    static __device__ __forceinline__ void widen(type u, float (&x)[2]) {
+        x[0] = u.x;
+        x[1] = u.y;
+    }
+};
+template <> struct KeyRaw<float, 1> {
+    typedef float type;
+    static __device__ __forceinline__ type load(const float* p) { return *p; }
+    static __device__ __forceinline__ void widen(type u, float (&x)[1]) { x[0] = u; }
+};
+
+template <typename E, typename G, int DK, int C>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
-    const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
-    const void* __restrict__ r, bool gate_bf16, int T, int NC, float4* __restrict__ agg) {
+    const E* __restrict__ k, const G* __restrict__ a, const G* __restrict__ nu,
+    const G* __restrict__ r, int T, int NC, float4* __restrict__ agg) {
     using L = Lanes<DK>;
+    using KR = KeyRaw<E, L::IPL>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = blockIdx.x * kWavesPerBlock + wave;
     const size_t bh = blockIdx.y;
     if (c >= NC) return;
     const int t0 = c * C, n = min(C, T - t0);
+    const bool act = lane < L::ACTIVE;
+    // every load of the chunk first: the gates of token `lane` and the keys of
+    // all C tokens for this lane's dims (rows past the end repeat the last one)
+    const size_t tok_l = bh * T + t0 + min(lane, n - 1);
+    const G ra = a[tok_l], rnu = nu[tok_l], rr = r[tok_l];
+    typename KR::type kr[C];
+#pragma unroll
+    for (int u = 0; u < C; ++u) {
+        const size_t tok = bh * T + t0 + min(u, n - 1);
+        kr[u] = KR::load(k + tok * DK + (act ? lane : 0) * L::IPL);
+    }
     // lane t: gates of token t (padding: the identity, a = 1, nu = 0, 1/r = 0)
     float ga2 = 1.f, gnu = 0.f, gir = 0.f;
-    {
-        const size_t tok = bh * T + t0 + min(lane, n - 1);
-        const float at = load_gate(a, tok, gate_bf16);
-        const float nut = load_gate(nu, tok, gate_bf16);
-        const float rt = load_gate(r, tok, gate_bf16);
-        if (lane < n) {
-            ga2 = at * at;
-            gnu = nut;
-            gir = 1.f / rt;
-        }
+    if (lane < n) {
+        const float at = to_f<G>(ra);
+        ga2 = at * at;
+        gnu = to_f<G>(rnu);
+        gir = 1.f / to_f<G>(rr);
     }
-    // keys of up to 32 tokens for this lane's dims are loaded before their products
-    constexpr int TB = C < 32 ? C : 32;
-    const bool act = lane < L::ACTIVE;
     M2 P[L::IPL];
 #pragma unroll
     for (int j = 0; j < L::IPL; ++j) P[j] = {1.f, 0.f, 0.f, 1.f};
-#pragma unroll 1
-    for (int tb = 0; tb < C; tb += TB) {
-        float kv[TB][L::IPL];
 #pragma unroll
-        for (int u = 0; u < TB; ++u) {
-            const size_t tok = bh * T + t0 + min(tb + u, n - 1);
-            if (act) load_dims<E, L::IPL>(k + tok * DK + lane * L::IPL, kv[u]);
-        }
+    for (int t = 0; t < C; ++t) {
+        float kv[L::IPL];
+        KR::widen(kr[t], kv);
+        const float a2 = lane_value(ga2, t), nut = lane_value(gnu, t), ir = lane_value(gir, t);
 #pragma unroll
-        for (int u = 0; u < TB; ++u) {
-            const int t = tb + u;
-            const float a2 = lane_value(ga2, t), nut = lane_value(gnu, t), ir = lane_value(gir, t);
+        for (int j = 0; j < L::IPL; ++j) P[j] = mob_step(P[j], kv[j] * kv[j] * ir, a2, nut);
+        if ((t & 7) == 7)
 #pragma unroll
-            for (int j = 0; j < L::IPL; ++j)
-                P[j] = mob_step(P[j], kv[u][j] * kv[u][j] * ir, a2, nut);
-            if ((t & 7) == 7)
-#pragma unroll
-                for (int j = 0; j < L::IPL; ++j) P[j] = mob_renorm(P[j]);
-        }
+            for (int j = 0; j < L::IPL; ++j) P[j] = mob_renorm(P[j]);
     }
     if (act) {
 #pragma unroll
@@ -147,27 +176,36 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_iso_kernel(
 }
 
 // ------------------------------------------------------------------- carry
-__global__ __launch_bounds__(256) void carry_kernel(const float4* __restrict__ agg,
-                                                    const float* __restrict__ lambda0, int BH,
-                                                    int NL, int NC, float* __restrict__ lam_chunk,
-                                                    float* __restrict__ lambda_T) {
+// One wave per 64 (head, key dim) scans; the chunk products are loaded in
+// groups of 16, the next group in flight while the current one is applied.
+constexpr int kCarryGroup = 16;
+__global__ __launch_bounds__(64) void carry_kernel(const float4* __restrict__ agg,
+                                                   const float* __restrict__ lambda0, int BH,
+                                                   int NL, int NC, float* __restrict__ lam_chunk,
+                                                   float* __restrict__ lambda_T) {
     const size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x;  // bh * NL + i
     if (idx >= (size_t)BH * NL) return;
     const size_t bh = idx / NL, i = idx % NL;
+    const float4* src = agg + bh * NC * NL + i;
     float lam = lambda0 ? lambda0[idx] : 1.f;
-    // chunk products are loaded 16 at a time ahead of the dependent applications
-    for (int cg = 0; cg < NC; cg += 16) {
-        float4 m[16];
+    float4 cur[kCarryGroup], nxt[kCarryGroup];
+    auto fetch = [&](float4(&m)[kCarryGroup], int cg) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-            m[u] = (cg + u < NC) ? agg[(bh * NC + cg + u) * NL + i] : make_float4(1.f, 0.f, 0.f, 1.f);
+        for (int u = 0; u < kCarryGroup; ++u)
+            m[u] = src[(size_t)min(cg + u, NC - 1) * NL];  // past the end: reloaded, unused
+    };
+    fetch(cur, 0);
+    for (int cg = 0; cg < NC; cg += kCarryGroup) {
+        fetch(nxt, min(cg + kCarryGroup, NC - 1));
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < kCarryGroup; ++u) {
             if (cg + u < NC) {
                 if (lam_chunk) lam_chunk[(bh * (NC + 1) + cg + u) * NL + i] = lam;
-                lam = (m[u].x * lam + m[u].y) / (m[u].z * lam + m[u].w);
+                lam = fmaf(cur[u].x, lam, cur[u].y) * __builtin_amdgcn_rcpf(fmaf(cur[u].z, lam, cur[u].w));
             }
         }
+#pragma unroll
+        for (int u = 0; u < kCarryGroup; ++u) cur[u] = nxt[u];
     }
     if (lam_chunk) lam_chunk[(bh * (NC + 1) + NC) * NL + i] = lam;
     if (lambda_T) lambda_T[idx] = lam;
@@ -283,8 +321,15 @@ hipError_t reduce_e(const Shape& s, const void* k, const void* a, const void* nu
     const E* kk = static_cast<const E*>(k);
 #define KDN_RED_D(DK_, C_)                                                                    \
     if (s.diag && s.dk == DK_ && s.chunk == C_) {                                             \
-        hipLaunchKernelGGL((reduce_diag_kernel<E, DK_, C_>), grid, block, 0, st, kk, a, nu, r,  \
-                           s.gate_bf16, s.T, s.nc, g);                                        \
+        if (s.gate_bf16)                                                                      \
+            hipLaunchKernelGGL((reduce_diag_kernel<E, bf16_t, DK_, C_>), grid, block, 0, st,  \
+                               kk, static_cast<const bf16_t*>(a),                             \
+                               static_cast<const bf16_t*>(nu), static_cast<const bf16_t*>(r), \
+                               s.T, s.nc, g);                                                 \
+        else                                                                                  \
+            hipLaunchKernelGGL((reduce_diag_kernel<E, float, DK_, C_>), grid, block, 0, st,   \
+                               kk, static_cast<const float*>(a), static_cast<const float*>(nu), \
+                               static_cast<const float*>(r), s.T, s.nc, g);                   \
         return hipGetLastError();                                                             \
     }
 #define KDN_RED_I(DK_)                                                                        \
@@ -357,7 +402,7 @@ hipError_t launch_scan_carry(const Shape& s, const float* agg, const float* lamb
     const int NL = s.diag ? s.dk : 1;
     const size_t n = (size_t)s.BH * NL;
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, st,
                        reinterpret_cast<const float4*>(agg), lambda0, s.BH, NL, s.nc, lam_chunk,
                        lambda_T);
     return hipGetLastError();
