@@ -80,8 +80,8 @@ def chunk_flops_full(n, dk, dv, C):
 # 512 MiB (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0), with the SHA-256 of the
 # kernel source they were taken on: reported only while the source is unchanged.
 TRAFFIC = {"kernel": "chunk_state",
-           "src_sha256": "954a0acf5f7886a4fef2f5449ab92f22f52c6e7d534fca4092cf642b8e18539d",
-           "fetch_bytes": 614602153, "write_bytes": 142606336}
+           "src_sha256": "6440bdc9ea6622e15342cede916ced10b9c4c67b892ad59d018bbbcd966d5060",
+           "fetch_bytes": 614595600, "write_bytes": 142606336}
 
 
 def _traffic():
@@ -150,7 +150,16 @@ def run(args):
     for row in evs:
         step(events=row)
     torch.cuda.synchronize()
-    kern_ms = {k: float(np.mean([row[i].elapsed_time(row[i + 1]) for row in evs]))
+    # the interval between two events recorded back to back with no work between
+    # them (the marks' own cost), subtracted from every kernel's interval
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for e0, e1 in pairs:
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    mark_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pairs]))
+    kern_ms = {k: float(np.mean([row[i].elapsed_time(row[i + 1]) for row in evs])) - mark_ms
                for i, k in enumerate(KERNELS)}
     by, fl = algorithmic(B, H, T, dk, dv, C)
     kernels = {}
@@ -199,6 +208,7 @@ def run(args):
                      "GB/s": round(scan_by / scan_s / 1e9, 1),
                      "frac": round(scan_by / scan_s / 1e9 / PEAK_HBM_GBS, 4)},
         "kernels": kernels,
+        "event_mark_us": round(mark_ms * 1e3, 2),
     }
     if traffic is not None:
         res["roofline"]["traffic_src_sha256"] = sha
