@@ -154,7 +154,8 @@ kdn_status kdn_chunk_delta(const kdn_desc *d, const void *q, const void *k, cons
  * decoding).  d->B is the number of sequences N, d->T and d->chunk are
  * ignored.  q, k [N,H,d_k]; v, o [N,H,d_v] (qkv_dtype); a, qnoise, r [N,H]
  * (gate_dtype); S [N,H,d_v,d_k] and lambda [N,H,d_k] / [N,H] float32 are read
- * and overwritten with the state after the token.  o must not alias S. */
+ * and overwritten with the state after the token.  o must not alias S.
+ * q, k, S and lambda must be 16-byte aligned (KDN_ERR_ALIGN otherwise). */
 kdn_status kdn_decode_step(const kdn_desc *d, const void *q, const void *k, const void *v,
                            const void *a, const void *qnoise, const void *r, float *S,
                            float *lambda, void *o, void *stream);

@@ -244,7 +244,8 @@ kdn_status kdn_decode_step(const kdn_desc* d, const void* q, const void* k, cons
     s.nc = 1;
     if (s.BH == 0) return KDN_OK;
     if (!q || !k || !v || !a || !qnoise || !r || !S || !lambda || !o) return KDN_ERR_NULL;
-    if (!aligned16(S)) return KDN_ERR_ALIGN;
+    for (const void* p : {q, k, (const void*)S, (const void*)lambda})
+        if (!aligned16(p)) return KDN_ERR_ALIGN;
     if (!kdn::decode_supported(s)) return KDN_ERR_UNSUPPORTED;
     return hip_status(kdn::launch_decode(s, q, k, v, a, qnoise, r, S, lambda, o,
                                          static_cast<hipStream_t>(stream)));

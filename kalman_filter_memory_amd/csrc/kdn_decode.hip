@@ -9,123 +9,168 @@
 // The last line is o = S_t q expanded so that S is read once and written once.
 //
 // The step is bound by HBM traffic: 2 * d_v * d_k * 4 bytes of state per
-// (sequence, head) against 6 d_k d_v flops.  One workgroup (4 waves) owns one
-// state; each lane streams float4 pieces of S rows (d_k / 4 lanes per row), so
-// a wave's load covers whole contiguous rows.
+// (sequence, head) against 6 d_k d_v flops.  One workgroup owns one state;
+// each lane streams float4 pieces of S rows (d_k / 4 lanes per row), so a
+// wave's load covers whole contiguous rows.  The group of d_k / 4 lanes that
+// shares a row holds every key dimension, so each group computes the gain in
+// full with shuffles: no LDS, and the only barrier orders the reads of lambda
+// before its in-place update.  The gain inputs are loaded before the state
+// rows, so waiting for them leaves the rows in flight.
 #include "kdn_device.h"
 #include "kdn_kernels.h"
 
 namespace kdn {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kMaxWaves = 8;
 
-__device__ __forceinline__ float block_sum(float x, float* red) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    x = wave_sum(x);
-    __syncthreads();  // red may still be read by a previous block_sum
-    if (lane == 0) red[wave] = x;
-    __syncthreads();
-    return red[0] + red[1] + red[2] + red[3];
+template <int DK, int DV> struct DecCfg {
+    static constexpr int LPR = DK / 4;         // lanes per S row (one float4 each)
+    static constexpr int RPS = kWave / LPR;    // rows covered by one wave-wide load
+    static constexpr int NW = DV / RPS < kMaxWaves ? DV / RPS : kMaxWaves;
+    static constexpr int RPW = DV / NW;        // rows per wave
+    static constexpr int SLOTS = RPW / RPS;    // wave-wide loads per wave
+    static_assert(SLOTS >= 1 && RPW % RPS == 0 && DV % NW == 0, "unsupported tile");
+};
+
+// four consecutive elements as floats (one 8-byte access for bf16)
+template <typename E> __device__ __forceinline__ float4 load4f(const E* p);
+template <> __device__ __forceinline__ float4 load4f<float>(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+template <> __device__ __forceinline__ float4 load4f<bf16_t>(const bf16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
 }
 
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void decode_kernel(
-    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const void* __restrict__ a, const void* __restrict__ nu, const void* __restrict__ r,
-    bool gate_bf16, bool diag, float* __restrict__ S, float* __restrict__ lam,
-    E* __restrict__ o) {
-    constexpr int LPR = DK / 4;            // lanes per S row (one float4 each)
-    constexpr int RPS = kWave / LPR;       // rows covered by one wave-wide load
-    constexpr int ROWS_PER_WAVE = DV / 4;  // 4 waves share the d_v rows
-    constexpr int SLOTS = ROWS_PER_WAVE / RPS;
-    static_assert(SLOTS >= 1 && ROWS_PER_WAVE % RPS == 0, "unsupported tile");
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-    __shared__ float sk[DK], sq[DK], sw[DK];
-    __shared__ float red[4];
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// sum over the LPR aligned lanes of a row group, returned to every lane of it:
+// quad_perm xor 1 and xor 2, then row_half_mirror (other quad of 8 lanes),
+// row_mirror (other 8 of 16) and, for 32 lanes, v_permlane16_swap of x with
+// itself, whose two results add up to x + x of the lane 16 away.
+template <int LPR> __device__ __forceinline__ float group_sum(float x) {
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "unsupported group");
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    if constexpr (LPR >= 16) x += dpp<0x140>(x);
+    if constexpr (LPR >= 32) {
+        const u32x2 s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                         false, false);
+        x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    }
+    return x;
+}
+
+__device__ __forceinline__ float dot4(const float4& x, const float4& y) {
+    return x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+}
+
+template <typename E, typename G, int DK, int DV, bool DIAG>
+__global__ __launch_bounds__((DecCfg<DK, DV>::NW * kWave)) void decode_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const G* __restrict__ a, const G* __restrict__ nu, const G* __restrict__ r,
+    float* __restrict__ S, float* __restrict__ lam, E* __restrict__ o) {
+    using Cfg = DecCfg<DK, DV>;
+    constexpr int LPR = Cfg::LPR, RPS = Cfg::RPS, RPW = Cfg::RPW, SLOTS = Cfg::SLOTS;
 
     const size_t st = blockIdx.x;  // (sequence, head) index
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float at = load_gate(a, st, gate_bf16);
-    const float nut = load_gate(nu, st, gate_bf16);
-    const float rt = load_gate(r, st, gate_bf16);
-    const float a2 = at * at;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = 4 * (lane % LPR), rsub = lane / LPR;
 
-    // ---- predict, gain and projection (d_k lanes) ----
-    float ki = 0.f, qi = 0.f, li = 0.f;
-    if (tid < DK) {
-        ki = to_f<E>(k[st * DK + tid]);
-        qi = to_f<E>(q[st * DK + tid]);
-        li = diag ? lam[st * DK + tid] : lam[st];
-    }
-    float wi = 0.f;
-    if (diag) {
-        float lmi = 1.f, pi = 0.f;
-        if (tid < DK) {
-            lmi = li / (a2 + nut * li);
-            pi = 1.f / lmi;
-        }
-        const float den = rt + block_sum(ki * ki * pi, red);
-        if (tid < DK) {
-            wi = pi * ki / den;
-            lam[st * DK + tid] = lmi + ki * ki / rt;
-        }
-    } else {
-        const float kk = block_sum(ki * ki, red);
-        const float lm = li / (a2 + nut * li);
-        wi = ki / (kk + rt * lm);
-        if (tid == 0) lam[st] = lm + kk / (static_cast<float>(DK) * rt);
-    }
-    const float wq = block_sum(wi * qi, red);
-    if (tid < DK) {
-        sk[tid] = ki;
-        sq[tid] = qi;
-        sw[tid] = wi;
-    }
-    __syncthreads();
+    // ---- gain inputs and values, then the state rows ----
+    const float at = to_f<G>(a[st]), nut = to_f<G>(nu[st]), rt = to_f<G>(r[st]);
+    const float4 k4 = load4f<E>(k + st * DK + col);
+    const float4 q4 = load4f<E>(q + st * DK + col);
+    float4 l4;
+    if constexpr (DIAG) l4 = *reinterpret_cast<const float4*>(lam + st * DK + col);
+    else l4.x = lam[st];
 
-    // ---- one pass over the rows of S ----
-    const int col = 4 * (lane % LPR);
-    const float4 k4 = make_float4(sk[col], sk[col + 1], sk[col + 2], sk[col + 3]);
-    const float4 q4 = make_float4(sq[col], sq[col + 1], sq[col + 2], sq[col + 3]);
-    const float4 w4 = make_float4(sw[col], sw[col + 1], sw[col + 2], sw[col + 3]);
     float* Sst = S + st * (size_t)(DV * DK);
     float4 srow[SLOTS];
+    float vj[SLOTS];
+#pragma unroll
+    for (int m = 0; m < SLOTS; ++m) vj[m] = to_f<E>(v[st * DV + wave * RPW + m * RPS + rsub]);
 #pragma unroll
     for (int m = 0; m < SLOTS; ++m) {
-        const int row = wave * ROWS_PER_WAVE + m * RPS + lane / LPR;
+        const int row = wave * RPW + m * RPS + rsub;
         srow[m] = *reinterpret_cast<const float4*>(Sst + row * DK + col);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the row loads ahead of the gain arithmetic
+
+    // ---- predict, gain and projection ----
+    const float a2 = at * at;
+    float4 w4, ln4;
+    if constexpr (DIAG) {
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, kv[4] = {k4.x, k4.y, k4.z, k4.w};
+        float lm[4], pk[4], part = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float dn = a2 + nut * lv[i];
+            lm[i] = lv[i] / dn;
+            pk[i] = dn / lv[i] * kv[i];  // P^- k
+            part += kv[i] * pk[i];
+        }
+        const float iden = 1.f / (rt + group_sum<LPR>(part)), ir = 1.f / rt;
+        w4 = make_float4(pk[0] * iden, pk[1] * iden, pk[2] * iden, pk[3] * iden);
+        ln4 = make_float4(lm[0] + kv[0] * kv[0] * ir, lm[1] + kv[1] * kv[1] * ir,
+                          lm[2] + kv[2] * kv[2] * ir, lm[3] + kv[3] * kv[3] * ir);
+    } else {
+        const float kk = group_sum<LPR>(dot4(k4, k4));
+        const float lm = l4.x / (a2 + nut * l4.x);
+        const float g = 1.f / (kk + rt * lm);
+        w4 = make_float4(k4.x * g, k4.y * g, k4.z * g, k4.w * g);
+        ln4.x = lm + kk / (static_cast<float>(DK) * rt);
+    }
+    const float wq = group_sum<LPR>(dot4(w4, q4));
+    __syncthreads();  // every wave has read lambda before it is overwritten
+    if (wave == 0 && rsub == 0) {
+        if constexpr (DIAG) *reinterpret_cast<float4*>(lam + st * DK + col) = ln4;
+        else if (col == 0) lam[st] = ln4.x;
+    }
+
+    // ---- one pass over the rows of S ----
 #pragma unroll
     for (int m = 0; m < SLOTS; ++m) {
-        const int row = wave * ROWS_PER_WAVE + m * RPS + lane / LPR;
-        float pk = srow[m].x * k4.x + srow[m].y * k4.y + srow[m].z * k4.z + srow[m].w * k4.w;
-        float pq = srow[m].x * q4.x + srow[m].y * q4.y + srow[m].z * q4.z + srow[m].w * q4.w;
-#pragma unroll
-        for (int off = LPR / 2; off >= 1; off >>= 1) {
-            pk += __shfl_xor(pk, off, kWave);
-            pq += __shfl_xor(pq, off, kWave);
-        }
-        const float vj = to_f<E>(v[st * DV + row]);
-        const float u = vj - at * pk;
+        const int row = wave * RPW + m * RPS + rsub;
+        const float pk = group_sum<LPR>(dot4(srow[m], k4));
+        const float pq = group_sum<LPR>(dot4(srow[m], q4));
+        const float u = vj[m] - at * pk;
         float4 ns;
         ns.x = at * srow[m].x + u * w4.x;
         ns.y = at * srow[m].y + u * w4.y;
         ns.z = at * srow[m].z + u * w4.z;
         ns.w = at * srow[m].w + u * w4.w;
         *reinterpret_cast<float4*>(Sst + row * DK + col) = ns;
-        if ((lane % LPR) == 0) o[st * DV + row] = from_f<E>(at * pq + u * wq);
+        if (col == 0) o[st * DV + row] = from_f<E>(at * pq + u * wq);
     }
 }
 
-template <typename E, int DK, int DV>
+template <typename E, typename G, int DK, int DV>
 hipError_t launch_t(const Shape& s, const void* q, const void* k, const void* v, const void* a,
                     const void* nu, const void* r, float* S, float* lam, void* o,
                     hipStream_t st) {
-    hipLaunchKernelGGL((decode_kernel<E, DK, DV>), dim3(s.BH), dim3(kThreads), 0, st,
-                       static_cast<const E*>(q), static_cast<const E*>(k),
-                       static_cast<const E*>(v), a, nu, r, s.gate_bf16, s.diag, S, lam,
-                       static_cast<E*>(o));
+    const dim3 grid(s.BH), block(DecCfg<DK, DV>::NW * kWave);
+    const E* qe = static_cast<const E*>(q);
+    const E* ke = static_cast<const E*>(k);
+    const E* ve = static_cast<const E*>(v);
+    const G* ag = static_cast<const G*>(a);
+    const G* ng = static_cast<const G*>(nu);
+    const G* rg = static_cast<const G*>(r);
+    E* oe = static_cast<E*>(o);
+    if (s.diag)
+        hipLaunchKernelGGL((decode_kernel<E, G, DK, DV, true>), grid, block, 0, st, qe, ke, ve,
+                           ag, ng, rg, S, lam, oe);
+    else
+        hipLaunchKernelGGL((decode_kernel<E, G, DK, DV, false>), grid, block, 0, st, qe, ke, ve,
+                           ag, ng, rg, S, lam, oe);
     return hipGetLastError();
 }
 
@@ -133,9 +178,11 @@ template <typename E>
 hipError_t launch_e(const Shape& s, const void* q, const void* k, const void* v, const void* a,
                     const void* nu, const void* r, float* S, float* lam, void* o,
                     hipStream_t st) {
-#define KDN_DEC_CASE(DK_, DV_)                                                   \
-    if (s.dk == DK_ && s.dv == DV_)                                              \
-        return launch_t<E, DK_, DV_>(s, q, k, v, a, nu, r, S, lam, o, st);
+#define KDN_DEC_CASE(DK_, DV_)                                                        \
+    if (s.dk == DK_ && s.dv == DV_)                                                   \
+        return s.gate_bf16                                                            \
+                   ? launch_t<E, bf16_t, DK_, DV_>(s, q, k, v, a, nu, r, S, lam, o, st) \
+                   : launch_t<E, float, DK_, DV_>(s, q, k, v, a, nu, r, S, lam, o, st);
     KDN_DEC_CASE(32, 32) KDN_DEC_CASE(32, 64) KDN_DEC_CASE(32, 128)
     KDN_DEC_CASE(64, 32) KDN_DEC_CASE(64, 64) KDN_DEC_CASE(64, 128)
     KDN_DEC_CASE(128, 32) KDN_DEC_CASE(128, 64) KDN_DEC_CASE(128, 128)

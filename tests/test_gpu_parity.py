@@ -253,6 +253,42 @@ def test_decode_steps_equal_forward(variant):
     assert elementwise(host(lam), host(l_f)) < 1e-5
 
 
+DECODE_SHAPES = [(dk, dv) for dk in (32, 64, 128) for dv in (32, 64, 128)]
+
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+@pytest.mark.parametrize("dk,dv", DECODE_SHAPES)
+def test_decode_shapes_match_oracle(dk, dv, variant):
+    """Every built (d_k, d_v) of the decode step (each has its own workgroup
+    shape), alternating q/k/v and gate dtypes, three steps against the oracle."""
+    i = DECODE_SHAPES.index((dk, dv))
+    qkv = "bf16" if i % 2 else "f32"
+    gate = "bf16" if (i // 2) % 2 else "f32"
+    N, H, steps = 3, 5, 3
+    d = decode_inputs(N, H, dk, dv, steps, variant=variant, seed=40 + i, qkv_dtype=qkv,
+                      gate_dtype=gate)
+    tdt = lambda name: torch.bfloat16 if (gate if name in ("a", "nu", "r") else qkv) == "bf16" \
+        else torch.float32
+    dev = {n: torch.from_numpy(d[n]).cuda().to(tdt(n)) for n in ("q", "k", "v", "a", "nu", "r")}
+    S = torch.from_numpy(d["S0"]).cuda()
+    lam = torch.from_numpy(d["lambda0"]).cuda()
+    Sr = d["S0"].astype(np.float64)
+    lr = d["lambda0"].astype(np.float64)
+    say(f"[gpu] decode d_k={dk} d_v={dv} {variant} qkv {qkv} gates {gate}")
+    tol = _tol(qkv)
+    for s in range(steps):
+        o = kdn.decode_step(dev["q"][s], dev["k"][s], dev["v"][s], dev["a"][s], dev["nu"][s],
+                            dev["r"][s], S, lam, variant)
+        o_ref = oracle.decode_step(*(d[n][s] for n in ("q", "k", "v", "a", "nu", "r")), Sr, lr,
+                                   variant)
+        e_o = normwise(host(o), o_ref)
+        assert e_o <= tol, (s, e_o)
+    torch.cuda.synchronize()
+    e_s, e_l = normwise(host(S), Sr), elementwise(host(lam), lr)
+    say(f"    err S {e_s:.2e}  lambda {e_l:.2e}")
+    assert e_s <= tol and e_l <= TOL_LAMBDA
+
+
 def test_forward_is_bitwise_deterministic():
     inp = forward_inputs(2, 2, 300, 128, 128, variant="diagonal", dtype="bf16", seed=27)
     a = _gpu_forward(inp, 64)
