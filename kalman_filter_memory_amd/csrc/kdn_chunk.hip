@@ -296,7 +296,7 @@ __device__ __forceinline__ void prep_fetch(const E* __restrict__ k, const G* __r
                                            PrepIn<E, G, DK, C>& in) {
     using L = PrepLds<E, DK, C>;
     constexpr int V = Vec16<E>::N, VPR = DK / V, NPL = L::NPL;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = wave_id();
     const int t0 = c * C, n = min(C, T - t0);
     const size_t row0 = bh * T + t0;
 #pragma unroll
@@ -343,7 +343,7 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
     E* sW = reinterpret_cast<E*>(smem + L::R1);
     float* sZ = reinterpret_cast<float*>(smem + L::R1);  // after A is formed
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int t0 = c * C, n = min(C, T - t0);
     const size_t row0 = bh * T + t0;
 
@@ -1128,7 +1128,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const int head = (L_ / per) * 8 + (L_ % 8);
     if (head >= BH) return;
     const StateArgs<E> A{q,  k,  v,  w,  Tm, gin, o,  (size_t)head, ((L_ % per) / 8) * DVT,
-                         T,  DV, NC, tid, tid & 63, tid >> 6};
+                         T,  DV, NC, tid, tid & 63, wave_id()};
     const int lane = A.lane, wave = A.wave;
     const size_t bh = A.bh;
     const int j0 = A.j0;

@@ -82,7 +82,7 @@ __global__ __launch_bounds__((DecCfg<DK, DV>::NW * kWave)) void decode_kernel(
     constexpr int LPR = Cfg::LPR, RPS = Cfg::RPS, RPW = Cfg::RPW, SLOTS = Cfg::SLOTS;
 
     const size_t st = blockIdx.x;  // (sequence, head) index
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int col = 4 * (lane % LPR), rsub = lane / LPR;
 
     // ---- gain inputs and values, then the state rows ----

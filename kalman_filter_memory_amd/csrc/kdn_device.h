@@ -68,6 +68,23 @@ __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x);
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 // value of lane `l` (uniform) of x, broadcast through a scalar register
+// index of the calling wave in its workgroup, in a scalar register: the
+// compiler's divergence analysis cannot see that threadIdx.x / 64 is uniform
+// across a wave, and would otherwise keep everything derived from it (tile
+// choices, row offsets, addresses) in vector registers
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
+// Raw buffer resource over `bytes` bytes at p (descriptor word 3 of the gfx9
+// family: 32-bit data format, no swizzle).  Buffer loads take a per-lane
+// offset in a vector register and a uniform one in a scalar register, so rows
+// chosen uniformly cost no vector address arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
 __device__ __forceinline__ float lane_value(float x, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }

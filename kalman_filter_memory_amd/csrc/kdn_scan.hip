@@ -55,8 +55,9 @@ template <int DK> struct Lanes {
 template <typename E, int IPL> struct KeyRaw;
 template <> struct KeyRaw<bf16_t, 2> {
     typedef uint32_t type;
-    static __device__ __forceinline__ type load(const bf16_t* p) {
-        return *reinterpret_cast<const uint32_t*>(p);
+    static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t rs, unsigned voff,
+                                                unsigned soff) {
+        return __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
     }
     static __device__ __forceinline__ void widen(type u, float (&x)[2]) {
         x[0] = __uint_as_float(u << 16);
@@ -64,24 +65,46 @@ template <> struct KeyRaw<bf16_t, 2> {
     }
 };
 template <> struct KeyRaw<bf16_t, 1> {
-    typedef bf16_t type;
-    static __device__ __forceinline__ type load(const bf16_t* p) { return *p; }
+    typedef uint16_t type;
+    static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t rs, unsigned voff,
+                                                unsigned soff) {
+        return __builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0);
+    }
     static __device__ __forceinline__ void widen(type u, float (&x)[1]) { x[0] = bf2f(u); }
 };
 template <> struct KeyRaw<float, 2> {
-    typedef float2 type;
-    static __device__ __forceinline__ type load(const float* p) {
-        return *reinterpret_cast<const float2*>(p);
+    typedef unsigned int type __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t rs, unsigned voff,
+                                                unsigned soff) {
+        return __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
     }
     static __device__ __forceinline__ void widen(type u, float (&x)[2]) {
-        x[0] = u.x;
-        x[1] = u.y;
+        x[0] = __uint_as_float(u[0]);
+        x[1] = __uint_as_float(u[1]);
     }
 };
 template <> struct KeyRaw<float, 1> {
-    typedef float type;
-    static __device__ __forceinline__ type load(const float* p) { return *p; }
-    static __device__ __forceinline__ void widen(type u, float (&x)[1]) { x[0] = u; }
+    typedef uint32_t type;
+    static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t rs, unsigned voff,
+                                                unsigned soff) {
+        return __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+    }
+    static __device__ __forceinline__ void widen(type u, float (&x)[1]) {
+        x[0] = __uint_as_float(u);
+    }
+};
+
+// one gate value through a buffer resource
+template <typename G> struct GateRaw;
+template <> struct GateRaw<bf16_t> {
+    static __device__ __forceinline__ bf16_t load(__amdgpu_buffer_rsrc_t rs, unsigned off) {
+        return __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+    }
+};
+template <> struct GateRaw<float> {
+    static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t rs, unsigned off) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+    }
 };
 
 template <typename E, typename G, int DK, int C>
@@ -90,30 +113,39 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
     const G* __restrict__ r, int T, int NC, float4* __restrict__ agg) {
     using L = Lanes<DK>;
     using KR = KeyRaw<E, L::IPL>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ float4 sgate[kWavesPerBlock][C];  // per token of the wave's chunk: a^2, nu, 1/r
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int c = blockIdx.x * kWavesPerBlock + wave;
     const size_t bh = blockIdx.y;
     if (c >= NC) return;
     const int t0 = c * C, n = min(C, T - t0);
     const bool act = lane < L::ACTIVE;
-    // every load of the chunk first: the gates of token `lane` and the keys of
-    // all C tokens for this lane's dims (rows past the end repeat the last one)
-    const size_t tok_l = bh * T + t0 + min(lane, n - 1);
-    const G ra = a[tok_l], rnu = nu[tok_l], rr = r[tok_l];
+    // every load of the chunk first: the gates of token `lane`, then the keys
+    // of all C tokens for this lane's dims (rows past the end repeat the last
+    // one); row offsets are uniform, only the lane's column varies
+    const size_t row0 = bh * T + t0;
+    const unsigned gbytes = static_cast<unsigned>(n * sizeof(G));
+    const unsigned goff = static_cast<unsigned>(min(lane, n - 1) * sizeof(G));
+    const G ra = GateRaw<G>::load(buffer_rsrc(a + row0, gbytes), goff);
+    const G rnu = GateRaw<G>::load(buffer_rsrc(nu + row0, gbytes), goff);
+    const G rr = GateRaw<G>::load(buffer_rsrc(r + row0, gbytes), goff);
+    const __amdgpu_buffer_rsrc_t kc =
+        buffer_rsrc(k + row0 * DK, static_cast<unsigned>(n * DK * sizeof(E)));
+    const unsigned col = (act ? lane : 0) * L::IPL * sizeof(E);
     typename KR::type kr[C];
 #pragma unroll
-    for (int u = 0; u < C; ++u) {
-        const size_t tok = bh * T + t0 + min(u, n - 1);
-        kr[u] = KR::load(k + tok * DK + (act ? lane : 0) * L::IPL);
+    for (int u = 0; u < C; ++u) kr[u] = KR::load(kc, col, min(u, n - 1) * DK * sizeof(E));
+    // lane t: gates of token t (padding: the identity, a = 1, nu = 0, 1/r = 0),
+    // handed to every lane through LDS (one broadcast read per token)
+    // (padding by arithmetic, not a select, which would be compiled to a branch
+    // around the gate loads, placing them after the keys)
+    {
+        const float at = to_f<G>(ra), m = lane < n ? 1.f : 0.f;
+        const float4 g = make_float4(fmaf(at * at, m, 1.f - m), to_f<G>(rnu) * m,
+                                     __builtin_amdgcn_rcpf(to_f<G>(rr)) * m, 0.f);
+        if (lane < C) sgate[wave][lane] = g;
     }
-    // lane t: gates of token t (padding: the identity, a = 1, nu = 0, 1/r = 0)
-    float ga2 = 1.f, gnu = 0.f, gir = 0.f;
-    if (lane < n) {
-        const float at = to_f<G>(ra);
-        ga2 = at * at;
-        gnu = to_f<G>(rnu);
-        gir = 1.f / to_f<G>(rr);
-    }
+    __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in order
     M2 P[L::IPL];
 #pragma unroll
     for (int j = 0; j < L::IPL; ++j) P[j] = {1.f, 0.f, 0.f, 1.f};
@@ -121,9 +153,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
     for (int t = 0; t < C; ++t) {
         float kv[L::IPL];
         KR::widen(kr[t], kv);
-        const float a2 = lane_value(ga2, t), nut = lane_value(gnu, t), ir = lane_value(gir, t);
+        const float4 g = sgate[wave][t];
 #pragma unroll
-        for (int j = 0; j < L::IPL; ++j) P[j] = mob_step(P[j], kv[j] * kv[j] * ir, a2, nut);
+        for (int j = 0; j < L::IPL; ++j) P[j] = mob_step(P[j], kv[j] * kv[j] * g.z, g.x, g.y);
         if ((t & 7) == 7)
 #pragma unroll
             for (int j = 0; j < L::IPL; ++j) P[j] = mob_renorm(P[j]);
@@ -153,7 +185,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_iso_kernel(
     const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
     const void* __restrict__ r, bool gate_bf16, int T, int C, int NC,
     float4* __restrict__ agg) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int c = blockIdx.x * kWavesPerBlock + wave;
     const size_t bh = blockIdx.y;
     if (c >= NC) return;
@@ -176,39 +208,83 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_iso_kernel(
 }
 
 // ------------------------------------------------------------------- carry
-// One wave per 64 (head, key dim) scans; the chunk products are loaded in
-// groups of 16, the next group in flight while the current one is applied.
-constexpr int kCarryGroup = 16;
-__global__ __launch_bounds__(64) void carry_kernel(const float4* __restrict__ agg,
-                                                   const float* __restrict__ lambda0, int BH,
-                                                   int NL, int NC, float* __restrict__ lam_chunk,
-                                                   float* __restrict__ lambda_T) {
-    const size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x;  // bh * NL + i
-    if (idx >= (size_t)BH * NL) return;
-    const size_t bh = idx / NL, i = idx % NL;
+// Each scan (one per (head, key dim) or per head) runs over the chunk maps in
+// order.  A wave takes 16 scans and cuts each into kCarrySeg segments of
+// consecutive chunks, one lane per (segment, scan): rows of 16 lanes are
+// segments.  A lane composes its segment's maps, takes the products of the
+// segments before its own from the lanes of its scan, carries the starting
+// precision through them, and walks its segment writing the precision at each
+// chunk start.  Segments of up to kCarryGroup chunks stay in registers between
+// the two passes; longer ones are read twice, kCarryGroup maps at a time.
+constexpr int kCarrySeg = 4, kCarryScans = kWave / kCarrySeg, kCarryGroup = 16;
+
+__device__ __forceinline__ M2 as_m2(const float4& v) { return {v.x, v.y, v.z, v.w}; }
+
+__device__ __forceinline__ float mob_apply_fast(const float4& m, float x) {
+    return fmaf(m.x, x, m.y) * __builtin_amdgcn_rcpf(fmaf(m.z, x, m.w));
+}
+
+template <bool ONE_GROUP>
+__global__ __launch_bounds__(kWave) void carry_kernel(const float4* __restrict__ agg,
+                                                      const float* __restrict__ lambda0, int BH,
+                                                      int NL, int NC,
+                                                      float* __restrict__ lam_chunk,
+                                                      float* __restrict__ lambda_T) {
+    const int lane = threadIdx.x, seg = lane / kCarryScans, sl = lane % kCarryScans;
+    const size_t n_scan = (size_t)BH * NL;
+    const size_t idx = blockIdx.x * (size_t)kCarryScans + sl;  // bh * NL + i
+    const bool valid = idx < n_scan;
+    const size_t id = valid ? idx : n_scan - 1;  // loads of lanes past the end stay in range
+    const size_t bh = id / NL, i = id % NL;
     const float4* src = agg + bh * NC * NL + i;
-    float lam = lambda0 ? lambda0[idx] : 1.f;
-    float4 cur[kCarryGroup], nxt[kCarryGroup];
-    auto fetch = [&](float4(&m)[kCarryGroup], int cg) __attribute__((always_inline)) {
+    const int SL = (NC + kCarrySeg - 1) / kCarrySeg;
+    const int c0 = min(seg * SL, NC), c1 = min(c0 + SL, NC);  // this lane's chunks [c0, c1)
+    auto map_at = [&](int c) { return src[(size_t)min(c, NC - 1) * NL]; };
+
+    // (1) the segment's product, later chunks on the left
+    float4 buf[kCarryGroup];
+    M2 P = {1.f, 0.f, 0.f, 1.f};
+    for (int g = c0; g < c1; g += kCarryGroup) {
 #pragma unroll
-        for (int u = 0; u < kCarryGroup; ++u)
-            m[u] = src[(size_t)min(cg + u, NC - 1) * NL];  // past the end: reloaded, unused
-    };
-    fetch(cur, 0);
-    for (int cg = 0; cg < NC; cg += kCarryGroup) {
-        fetch(nxt, min(cg + kCarryGroup, NC - 1));
+        for (int u = 0; u < kCarryGroup; ++u) buf[u] = map_at(g + u);
 #pragma unroll
         for (int u = 0; u < kCarryGroup; ++u) {
-            if (cg + u < NC) {
-                if (lam_chunk) lam_chunk[(bh * (NC + 1) + cg + u) * NL + i] = lam;
-                lam = fmaf(cur[u].x, lam, cur[u].y) * __builtin_amdgcn_rcpf(fmaf(cur[u].z, lam, cur[u].w));
-            }
+            if (g + u < c1) P = mob_mul(as_m2(buf[u]), P);
+            if ((u & 7) == 7) P = mob_renorm(P);
+        }
+        if (ONE_GROUP) break;
+    }
+    P = mob_renorm(P);
+    // (2) precision at the segment start: the starting one carried through the
+    // products of the earlier segments of the same scan
+    float lam = lambda0 ? lambda0[id] : 1.f;
+#pragma unroll
+    for (int j = 0; j < kCarrySeg - 1; ++j) {
+        const int from = j * kCarryScans + sl;
+        const float4 q = make_float4(__shfl(P.a, from, kWave), __shfl(P.b, from, kWave),
+                                     __shfl(P.c, from, kWave), __shfl(P.d, from, kWave));
+        if (j < seg) lam = mob_apply_fast(q, lam);
+    }
+    // (3) walk the segment
+    float* out = lam_chunk ? lam_chunk + bh * (size_t)(NC + 1) * NL + i : nullptr;
+    for (int g = c0; g < c1; g += kCarryGroup) {
+        if (!ONE_GROUP) {
+#pragma unroll
+            for (int u = 0; u < kCarryGroup; ++u) buf[u] = map_at(g + u);
         }
 #pragma unroll
-        for (int u = 0; u < kCarryGroup; ++u) cur[u] = nxt[u];
+        for (int u = 0; u < kCarryGroup; ++u) {
+            if (g + u < c1) {
+                if (out && valid) out[(size_t)(g + u) * NL] = lam;
+                lam = mob_apply_fast(buf[u], lam);
+            }
+        }
+        if (ONE_GROUP) break;
     }
-    if (lam_chunk) lam_chunk[(bh * (NC + 1) + NC) * NL + i] = lam;
-    if (lambda_T) lambda_T[idx] = lam;
+    if (seg == kCarrySeg - 1 && valid) {  // the last segment ends at chunk NC
+        if (out) out[(size_t)NC * NL] = lam;
+        if (lambda_T) lambda_T[id] = lam;
+    }
 }
 
 // -------------------------------------------------------------------- emit
@@ -218,7 +294,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void emit_diag_kernel(
     const void* __restrict__ r, bool gate_bf16, int T, int C, int NC,
     const float* __restrict__ lam_chunk, float* __restrict__ lambda_minus) {
     using L = Lanes<DK>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int c = blockIdx.x * kWavesPerBlock + wave;
     const size_t bh = blockIdx.y;
     if (c >= NC || lane >= L::ACTIVE) return;
@@ -247,7 +323,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void emit_iso_kernel(
     const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
     const void* __restrict__ r, bool gate_bf16, int T, int C, int NC,
     const float* __restrict__ lam_chunk, float* __restrict__ lambda_minus) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int c = blockIdx.x * kWavesPerBlock + wave;
     const size_t bh = blockIdx.y;
     if (c >= NC) return;
@@ -284,7 +360,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gain_kernel(
     const E* __restrict__ k, const void* __restrict__ r, bool gate_bf16, bool diag,
     size_t n_tok, const float* __restrict__ lambda_minus, W* __restrict__ w) {
     using L = Lanes<DK>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const size_t tok0 = (blockIdx.x * (size_t)kWavesPerBlock + wave) * kGainTokensPerWave;
     for (int t = 0; t < kGainTokensPerWave; ++t) {
         const size_t tok = tok0 + t;
@@ -402,9 +478,14 @@ hipError_t launch_scan_carry(const Shape& s, const float* agg, const float* lamb
     const int NL = s.diag ? s.dk : 1;
     const size_t n = (size_t)s.BH * NL;
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, st,
-                       reinterpret_cast<const float4*>(agg), lambda0, s.BH, NL, s.nc, lam_chunk,
-                       lambda_T);
+    const dim3 grid((unsigned)((n + kCarryScans - 1) / kCarryScans)), block(kWave);
+    const float4* a4 = reinterpret_cast<const float4*>(agg);
+    if (s.nc <= kCarrySeg * kCarryGroup)
+        hipLaunchKernelGGL(carry_kernel<true>, grid, block, 0, st, a4, lambda0, s.BH, NL, s.nc,
+                           lam_chunk, lambda_T);
+    else
+        hipLaunchKernelGGL(carry_kernel<false>, grid, block, 0, st, a4, lambda0, s.BH, NL, s.nc,
+                           lam_chunk, lambda_T);
     return hipGetLastError();
 }
 
