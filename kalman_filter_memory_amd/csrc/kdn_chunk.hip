@@ -334,7 +334,8 @@ template <typename E, typename G, int DK, int C, bool FUSE>
 __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
                                            E* __restrict__ Tm, float* __restrict__ gout, int T,
                                            int NC, size_t bh, int c, const PrepIn<E, G, DK, C>& in,
-                                           unsigned char* smem, float* sden, float* sg) {
+                                           unsigned char* smem, float* sden, float* sg,
+                                           float4* sgt) {
     using L = PrepLds<E, DK, C>;
     constexpr int LDK = L::LDK, LDA = L::LDA, NT = L::NT, NPL = L::NPL;
     constexpr int V = Vec16<E>::N, VPR = DK / V;
@@ -372,6 +373,7 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
         const float g = wave_incl_sum(lane < C ? log2_hw(ga) : 0.f);
         if (lane < C) {
             sg[lane] = g;
+            sgt[lane] = make_float4(ga2, gnu, gir, gr);  // read by every lane, token by token
             gout[(bh * NC + c) * C + lane] = g;  // for the state pass
         }
     }
@@ -392,8 +394,8 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
                 for (int d = 0; d < NPL; ++d) m[d] = M2{1.f, 0.f, 0.f, 1.f};
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const float a2 = lane_value(ga2, tb0 + j), nut = lane_value(gnu, tb0 + j);
-                    const float ir = lane_value(gir, tb0 + j);
+                    const float4 gv = sgt[tb0 + j];
+                    const float a2 = gv.x, nut = gv.y, ir = gv.z;
 #pragma unroll
                     for (int d = 0; d < NPL; ++d) {
                         m[d] = mob_step(m[d], kc[j][d] * kc[j][d] * ir, a2, nut);
@@ -429,8 +431,8 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
                 float v[16];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const float a2 = lane_value(ga2, tb0 + j), nut = lane_value(gnu, tb0 + j);
-                    const float ir = lane_value(gir, tb0 + j);
+                    const float4 gv = sgt[tb0 + j];
+                    const float a2 = gv.x, nut = gv.y, ir = gv.z;
                     v[j] = 0.f;
 #pragma unroll
                     for (int d = 0; d < NPL; ++d) {
@@ -635,7 +637,7 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
 // Two chunks per workgroup (2 blockIdx.x and the next): the second chunk's
 // inputs are loaded at the start and arrive while the first is processed.
 template <typename E, typename G, int DK, int C, bool FUSE>
-__global__ __launch_bounds__(kThreads) void prep_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void prep_kernel(
     const E* __restrict__ k, const G* __restrict__ a, const G* __restrict__ nu,
     const G* __restrict__ r, bool diag, const float* __restrict__ lam_chunk, E* __restrict__ w,
     E* __restrict__ Tm, float* __restrict__ gout, int T, int NC) {
@@ -643,6 +645,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     __shared__ __align__(16) unsigned char smem[L::R1 + L::R2];
     __shared__ __align__(16) float sden[C];
     __shared__ __align__(16) float sg[C];
+    __shared__ float4 sgt[C];  // per token: a^2, nu, 1/r, r
     const int tid = threadIdx.x;
     const size_t bh = blockIdx.y;
     const int c0 = 2 * blockIdx.x, c1 = c0 + 1;
@@ -650,10 +653,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, bh, c0, T, NC, tid, in0);
     prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, bh, min(c1, NC - 1), T, NC, tid,
                                   in1);
-    prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, T, NC, bh, c0, in0, smem, sden, sg);
+    prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, T, NC, bh, c0, in0, smem, sden, sg, sgt);
     if (c1 < NC) {
         sync_lds();  // the second chunk's staging overwrites K / A / T
-        prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, T, NC, bh, c1, in1, smem, sden, sg);
+        prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, T, NC, bh, c1, in1, smem, sden, sg, sgt);
     }
 }
 
