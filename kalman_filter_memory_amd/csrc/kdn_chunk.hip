@@ -901,6 +901,23 @@ __device__ __forceinline__ void state_chunk(
                                            A.NC, c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
     __builtin_amdgcn_sched_barrier(0);  // keep the three load bursts apart
 
+    // one 16x16 tile of M^T = W Q^T (full depth), masked and scaled, stored as
+    // M[t][s] (element e <-> s = 16 ss + 4 (lane/16) + e, t = 16 tt + lane % 16)
+    auto m_store = [&](int ss, int tt, floatx4 mv) __attribute__((always_inline)) {
+        const int s0 = 16 * ss + 4 * (lane >> 4);
+        const int t = 16 * tt + (lane & 15);
+        const float gt = L.g[t];
+        const float4 gs = *reinterpret_cast<const float4*>(L.g + s0);
+        store4<E>(L.M + t * LDC + s0, (s0 + 0 <= t) ? exp2_hw(gt - gs.x) * mv[0] : 0.f,
+                  (s0 + 1 <= t) ? exp2_hw(gt - gs.y) * mv[1] : 0.f,
+                  (s0 + 2 <= t) ? exp2_hw(gt - gs.z) * mv[2] : 0.f,
+                  (s0 + 3 <= t) ? exp2_hw(gt - gs.w) * mv[3] : 0.f);
+    };
+    // the layer shape (four t-tiles, four j-tiles, eight waves): M is formed in
+    // phase A, where the first wave of each SIMD has slack, and U = T R takes all
+    // eight waves in phase B
+    constexpr bool kMInA = NT == 4 && G::NV == 4 && BT == 2 && BV == 2 && G::NW == 8;
+
     // ---------------- phase A: X^T = S K^T -> R ;  Y = S Q^T
     // block (jb: BVA j-tiles, tb: one t-tile); C-layout element e <->
     // j = 16 (jb + bv) + 4 (lane/16) + e, t = 16 tb + lane % 16
@@ -949,6 +966,22 @@ __device__ __forceinline__ void state_chunk(
             store8x2<E>(row, row + 16, rv[0], rv[1], lane);
         }
     }
+    if constexpr (kMInA) {
+        // the ten lower tiles of M: waves 0-3 two tiles that share their W
+        // fragments, (0,0)+(0,1), (0,2)+(0,3), (1,1)+(1,2), (2,2)+(2,3); waves 4
+        // and 5 one tile, (1,3) and (3,3)
+        if (wave < 4) {
+            const int ss = wave < 2 ? 0 : wave - 1, tt = wave == 1 ? 2 : ss;
+            floatx4 m[1][2] = {{floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}}};
+            mma_block<E, 1, 2>(m, sWc, LDK, 16 * ss, L.Q, LDK, 16 * tt, 0, DK, lane);
+            m_store(ss, tt, m[0][0]);
+            m_store(ss, tt + 1, m[0][1]);
+        } else if (wave < 6) {
+            const int ss = wave == 4 ? 1 : 3;
+            m_store(ss, 3, mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, sWc, LDK, 16 * ss, L.Q, LDK,
+                                       48, 0, DK, lane));
+        }
+    }
     sync_lds();
     state_prefetch<E, DK, DVT, C, kLoadW>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.bh, A.j0, A.T, A.DV,
                                           A.NC, c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
@@ -956,38 +989,26 @@ __device__ __forceinline__ void state_chunk(
 
     // ---------------- phase B
     const float gC = L.gam[C - 1];  // read before phase C restages the tables
-    // one 16x16 tile of M^T = W Q^T (full depth), masked and scaled, stored as
-    // M[t][s] (element e <-> s = 16 ss + 4 (lane/16) + e, t = 16 tt + lane % 16)
-    auto m_store = [&](int ss, int tt, floatx4 mv) __attribute__((always_inline)) {
-        const int s0 = 16 * ss + 4 * (lane >> 4);
-        const int t = 16 * tt + (lane & 15);
-        const float gt = L.g[t];
-        const float4 gs = *reinterpret_cast<const float4*>(L.g + s0);
-        store4<E>(L.M + t * LDC + s0, (s0 + 0 <= t) ? exp2_hw(gt - gs.x) * mv[0] : 0.f,
-                  (s0 + 1 <= t) ? exp2_hw(gt - gs.y) * mv[1] : 0.f,
-                  (s0 + 2 <= t) ? exp2_hw(gt - gs.z) * mv[2] : 0.f,
-                  (s0 + 3 <= t) ? exp2_hw(gt - gs.w) * mv[3] : 0.f);
-    };
-    constexpr bool kBalancedB = NT == 4 && G::NV == 4 && BT == 2 && BV == 2 && G::NW == 8;
-    if constexpr (kBalancedB) {
-        // 64 MFMAs per chunk, 8 per wave (2 waves per SIMD: 16 per SIMD).  Waves
-        // 0-3: the U blocks (as below); waves 0 and 1, whose U blocks are the
-        // shallow ones, also one M tile each; waves 4-7: two M tiles each that
-        // share their W fragments.
-        if (wave < 2) {
-            const int ss = wave == 0 ? 1 : 3;
-            m_store(ss, 3, mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, sWc, LDK, 16 * ss, L.Q, LDK,
-                                       48, 0, DK, lane));
-        } else if (wave >= 4) {
-            const int ss = wave < 6 ? 0 : wave - 5;             // 0, 0, 1, 2
-            const int tt = wave == 4 ? 0 : wave == 5 ? 2 : ss;  // pairs (tt, tt + 1)
-            floatx4 m[1][2] = {{floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}}};
-            mma_block<E, 1, 2>(m, sWc, LDK, 16 * ss, L.Q, LDK, 16 * tt, 0, DK, lane);
-            m_store(ss, tt, m[0][0]);
-            m_store(ss, tt + 1, m[0][1]);
+    if constexpr (kMInA) {
+        // U = T R (T lower triangular: contract only up to the block's last row):
+        // a pair of t-tiles x one j-tile per wave, the deep pair on the first
+        // wave of each SIMD; stored as U^T and as U^T scaled by gamma_C / gamma_t
+        const int tb = wave < 4 ? 2 : 0, jv = wave & 3;
+        floatx4 u[2][1] = {{floatx4{0.f, 0.f, 0.f, 0.f}}, {floatx4{0.f, 0.f, 0.f, 0.f}}};
+        mma_block<E, 2, 1, false, true>(u, L.Tt, LDC, 16 * tb, L.R, LDV, 16 * jv, 0,
+                                        16 * (tb + 2), lane);
+        floatx4 us[2];
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt) {
+            const int t = 16 * (tb + bt) + 4 * (lane >> 4);
+            const float4 d4 = *reinterpret_cast<const float4*>(L.del + t);
+            const floatx4 uv = u[bt][0];
+            us[bt] = floatx4{d4.x * uv[0], d4.y * uv[1], d4.z * uv[2], d4.w * uv[3]};
         }
-    }
-    if (wave < 4) {
+        const int j = 16 * jv + (lane & 15);
+        store8x2<E>(L.U + j * LDC + 16 * tb, L.U + j * LDC + 16 * tb + 16, u[0][0], u[1][0], lane);
+        store8x2<E>(L.Us + j * LDC + 16 * tb, L.Us + j * LDC + 16 * tb + 16, us[0], us[1], lane);
+    } else if (wave < 4) {
         // U = T R (T lower triangular: contract only up to the block's last row)
 #pragma unroll
         for (int x = 0; x < G::UPW; ++x) {
@@ -1029,7 +1050,8 @@ __device__ __forceinline__ void state_chunk(
                 }
             }
         }
-    } else if (!kBalancedB) {
+    }
+    if (!kMInA && wave >= 4) {
         // M^T = W Q^T on the lower block triangle, stored as M[t][s]
 #pragma unroll
         for (int x = 0; x < G::MPW; ++x) {
