@@ -666,17 +666,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 //   phase A  every wave, one (2 j-tiles x 1 t-tile) block:
 //              X^T = S K^T  ->  R = V - diag(gamma) X   (stored token-major)
 //              Y   = diag(gamma) Q S^T, kept as the O^T accumulator
-//            (both products share the S fragments)
-//   phase B  waves 0-3: U = T R (stored as U^T, and as U^T scaled by
-//            gamma_C / gamma_t); waves 4-7: M = tril(Q W^T) * Gamma
+//            (both products share the S fragments); in the layer shape (four
+//            t-tiles and j-tiles, eight waves) also M = tril(Q W^T) * Gamma
+//   phase B  U = T R (stored as U^T, and as U^T scaled by gamma_C / gamma_t);
+//            in the layer shape on all waves, which then stage the next
+//            chunk's K, Q, V and W (the first three were last read in phase A,
+//            W goes to the other of two buffers); otherwise U on waves 0-3 and
+//            M on waves 4-7
 //   phase C  every wave: O^T += U^T M^T for its block, written out; and one
 //            block of the state update S^T <- gamma_C S^T + W^T diag(gamma_C/gamma_t) U;
-//            then the next chunk's K, W, Q, V, T, g (loaded from HBM into one of
-//            two register sets during the previous chunk) are written to LDS with
-//            its decay tables (W into the other of two buffers, since the state
-//            update reads the current one), and the new state as the next operand.
-//            The chunk after next is loaded into the other register set meanwhile,
-//            in three parts at the starts of the three phases.
+//            then the rest of the next chunk (loaded from HBM into one of two
+//            register sets during the previous chunk) is written to LDS with its
+//            decay tables, and the new state as the next operand.  The chunk
+//            after next is loaded into the other register set meanwhile, in
+//            three parts at the starts of the three phases.
 // Operands stored with the contraction index strided (token-major R and W) are
 // read with transposing LDS reads (ds_read_b64_tr_b16).  Barriers are LDS-only
 // (sync_lds) so that the next chunk's global loads stay in flight across them.
@@ -775,7 +778,10 @@ __device__ __forceinline__ void state_prefetch(
     }
 }
 
-template <typename E, int DK, int DVT, int C>
+// parts of a chunk staged from registers into LDS: K, Q, W and V; T and the
+// decay tables
+enum { kStageKQWV = 1, kStageT = 2, kStageAll = 3 };
+template <typename E, int DK, int DVT, int C, int PARTS>
 __device__ __forceinline__ void state_stage(
     E* sK, E* sQ, E* sWc, E* sV, E* sT, float* sg, float* sgam, float* sdel, int n, int tid,
     int lane, int wave, const u32x4 (&pk)[StateCfg<E, DK, DVT, C>::PK],
@@ -784,41 +790,45 @@ __device__ __forceinline__ void state_stage(
     float pg) {
     using G = StateCfg<E, DK, DVT, C>;
     constexpr int VEC = G::VEC, LDK = G::LDK, LDC = G::LDC, LDV = G::LDV;
+    if constexpr ((PARTS & kStageKQWV) != 0) {
 #pragma unroll
-    for (int x = 0; x < G::PK; ++x) {
-        const int e = tid + G::THREADS * x;
-        if (G::NVK % G::THREADS == 0 || e < G::NVK) {
-            const int t = e / (DK / VEC), c0 = (e % (DK / VEC)) * VEC;
-            *reinterpret_cast<u32x4*>(sK + t * LDK + c0) = pk[x];
-            *reinterpret_cast<u32x4*>(sQ + t * LDK + c0) = pq[x];
-            // padded rows of W are zero (a select at staging time, when the
-            // loaded row has to have arrived anyway)
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(sWc + t * LDK + c0) = (t < n) ? pw[x] : zero;
+        for (int x = 0; x < G::PK; ++x) {
+            const int e = tid + G::THREADS * x;
+            if (G::NVK % G::THREADS == 0 || e < G::NVK) {
+                const int t = e / (DK / VEC), c0 = (e % (DK / VEC)) * VEC;
+                *reinterpret_cast<u32x4*>(sK + t * LDK + c0) = pk[x];
+                *reinterpret_cast<u32x4*>(sQ + t * LDK + c0) = pq[x];
+                // padded rows of W are zero (a select at staging time, when the
+                // loaded row has to have arrived anyway)
+                const u32x4 zero = {0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4*>(sWc + t * LDK + c0) = (t < n) ? pw[x] : zero;
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < G::PV; ++x) {
+            const int e = tid + G::THREADS * x;
+            if (G::NVV % G::THREADS == 0 || e < G::NVV) {
+                const int t = e / (DVT / VEC), c0 = (e % (DVT / VEC)) * VEC;
+                *reinterpret_cast<u32x4*>(sV + t * LDV + c0) = pv[x];
+            }
         }
     }
+    if constexpr ((PARTS & kStageT) != 0) {
 #pragma unroll
-    for (int x = 0; x < G::PV; ++x) {
-        const int e = tid + G::THREADS * x;
-        if (G::NVV % G::THREADS == 0 || e < G::NVV) {
-            const int t = e / (DVT / VEC), c0 = (e % (DVT / VEC)) * VEC;
-            *reinterpret_cast<u32x4*>(sV + t * LDV + c0) = pv[x];
+        for (int x = 0; x < G::PT; ++x) {
+            const int e = tid + G::THREADS * x;
+            if (G::NVT % G::THREADS == 0 || e < G::NVT) {
+                const int t = e / (C / VEC), c0 = (e % (C / VEC)) * VEC;
+                *reinterpret_cast<u32x4*>(sT + t * LDC + c0) = pt[x];
+            }
         }
-    }
-#pragma unroll
-    for (int x = 0; x < G::PT; ++x) {
-        const int e = tid + G::THREADS * x;
-        if (G::NVT % G::THREADS == 0 || e < G::NVT) {
-            const int t = e / (C / VEC), c0 = (e % (C / VEC)) * VEC;
-            *reinterpret_cast<u32x4*>(sT + t * LDC + c0) = pt[x];
-        }
-    }
-    if (wave == 0) {
-        const float glast = lane_value(pg, C - 1);
-        if (lane < C) {
-            sg[lane] = pg;
-            sgam[lane] = exp2_hw(pg);
-            sdel[lane] = exp2_hw(glast - pg);
+        if (wave == 0) {
+            const float glast = lane_value(pg, C - 1);
+            if (lane < C) {
+                sg[lane] = pg;
+                sgam[lane] = exp2_hw(pg);
+                sdel[lane] = exp2_hw(glast - pg);
+            }
         }
     }
 }
@@ -1008,6 +1018,12 @@ __device__ __forceinline__ void state_chunk(
         const int j = 16 * jv + (lane & 15);
         store8x2<E>(L.U + j * LDC + 16 * tb, L.U + j * LDC + 16 * tb + 16, u[0][0], u[1][0], lane);
         store8x2<E>(L.Us + j * LDC + 16 * tb, L.Us + j * LDC + 16 * tb + 16, us[0], us[1], lane);
+        // K, Q, V and W of chunk c + 1 (the first three were last read in phase A;
+        // W goes to the other buffer): staged here, where the waves have slack
+        if (c + 1 < A.NC)
+            state_stage<E, DK, DVT, C, kStageKQWV>(
+                L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g, L.gam, L.del,
+                min(C, A.T - (c + 1) * C), A.tid, lane, wave, nk, nq, nw, nv, nt, ng);
     } else if (wave < 4) {
         // U = T R (T lower triangular: contract only up to the block's last row)
 #pragma unroll
@@ -1129,9 +1145,9 @@ __device__ __forceinline__ void state_chunk(
     }
     // nothing staged here is read in phase C (W goes to the other buffer)
     if (c + 1 < A.NC)
-        state_stage<E, DK, DVT, C>(L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g, L.gam, L.del,
-                                   min(C, A.T - (c + 1) * C), A.tid, lane, wave, nk, nq, nw, nv,
-                                   nt, ng);
+        state_stage<E, DK, DVT, C, kMInA ? kStageT : kStageAll>(
+            L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g, L.gam, L.del, min(C, A.T - (c + 1) * C),
+            A.tid, lane, wave, nk, nq, nw, nv, nt, ng);
     state_write<E, DK, DVT, C>(accS, L.S, wave, lane);
     sync_lds();
 }
@@ -1188,7 +1204,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                                                 lane, pkA, pqA, pwA, pvA, ptA, pgA);
         state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, v, w, Tm, gin, bh, j0, T, DV, NC, 1, tid,
                                                 lane, pkB, pqB, pwB, pvB, ptB, pgB);
-        state_stage<E, DK, DVT, C>(L.K, L.Q, L.W[0], L.V, L.Tt, L.g, L.gam, L.del, min(C, T), tid,
+        state_stage<E, DK, DVT, C, kStageAll>(L.K, L.Q, L.W[0], L.V, L.Tt, L.g, L.gam, L.del, min(C, T), tid,
                                    lane, wave, pkA, pqA, pwA, pvA, ptA, pgA);
     }
     state_write<E, DK, DVT, C>(accS, L.S, wave, lane);
