@@ -141,8 +141,10 @@ def run(args):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # per-kernel durations: events recorded between the kernels on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # per-kernel durations: start and stop events recorded by each kernel's own
+    # dispatch on the launch stream (no marker packets between the kernels)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(KERNELS))]
+           for _ in range(args.steps)]
     for row in evs:
         for e in row:
             e.record()
@@ -150,16 +152,7 @@ def run(args):
     for row in evs:
         step(events=row)
     torch.cuda.synchronize()
-    # the interval between two events recorded back to back with no work between
-    # them (the marks' own cost), subtracted from every kernel's interval
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(args.steps)]
-    for e0, e1 in pairs:
-        e0.record()
-        e1.record()
-    torch.cuda.synchronize()
-    mark_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pairs]))
-    kern_ms = {k: float(np.mean([row[i].elapsed_time(row[i + 1]) for row in evs])) - mark_ms
+    kern_ms = {k: float(np.mean([row[2 * i].elapsed_time(row[2 * i + 1]) for row in evs]))
                for i, k in enumerate(KERNELS)}
     by, fl = algorithmic(B, H, T, dk, dv, C)
     kernels = {}
@@ -208,7 +201,6 @@ def run(args):
                      "GB/s": round(scan_by / scan_s / 1e9, 1),
                      "frac": round(scan_by / scan_s / 1e9 / PEAK_HBM_GBS, 4)},
         "kernels": kernels,
-        "event_mark_us": round(mark_ms * 1e3, 2),
     }
     if traffic is not None:
         res["roofline"]["traffic_src_sha256"] = sha

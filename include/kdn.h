@@ -100,11 +100,12 @@ kdn_status kdn_forward(const kdn_desc *d, const void *q, const void *k, const vo
                        const float *lambda0, const float *S0, void *o, float *S_T,
                        float *lambda_T, void *ws, size_t ws_bytes, void *stream);
 
-/* kdn_forward with timing marks: events is NULL or an array of 5 hipEvent_t
- * (entries may be NULL) created by the caller; event i is recorded on
- * `stream` before kernel i (0 scan reduce, 1 scan carry, 2 chunk prep,
- * 3 chunk state) and event 4 after the last one, so that a caller can time
- * each kernel of the forward.  Otherwise identical to kdn_forward. */
+/* kdn_forward with timing: events is NULL or an array of 8 hipEvent_t
+ * (entries may be NULL) created by the caller; events 2i and 2i + 1 are the
+ * start and stop of kernel i (0 scan reduce, 1 scan carry, 2 chunk prep,
+ * 3 chunk state), recorded by the kernel dispatches themselves on `stream`
+ * (no extra packets between the kernels), so that a caller can time each
+ * kernel of the forward.  Otherwise identical to kdn_forward. */
 kdn_status kdn_forward_events(const kdn_desc *d, const void *q, const void *k, const void *v,
                               const void *a, const void *qnoise, const void *r,
                               const float *lambda0, const float *S0, void *o, float *S_T,

@@ -171,8 +171,9 @@ def forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", ch
             workspace: torch.Tensor | None = None, out=None, events=None):
     """KDN layer forward on the GPU.  Returns (o, S_T, lambda_T).
 
-    out: optional preallocated (o, S_T, lambda_T); events: optional list of 5
-    torch.cuda.Event (already recorded once) marking the kernel boundaries."""
+    out: optional preallocated (o, S_T, lambda_T); events: optional list of 8
+    torch.cuda.Event (already recorded once): the start and stop of each of the
+    four kernels, recorded by the kernel dispatches."""
     lib = load_library()
     d = _forward_desc(q, k, v, a, qnoise, r, variant, chunk)
     B, H, T, dk = k.shape
@@ -203,7 +204,9 @@ def forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", ch
     if events is None:
         _check(lib.kdn_forward(*args), "kdn_forward")
     else:
-        arr = (ctypes.c_void_p * 5)(*[None if e is None else e.cuda_event for e in events])
+        if len(events) != 8:
+            raise ValueError("events: 8 entries (start and stop of four kernels)")
+        arr = (ctypes.c_void_p * 8)(*[None if e is None else e.cuda_event for e in events])
         _check(lib.kdn_forward_events(*args, arr), "kdn_forward_events")
     return o, S_T, lam_T
 

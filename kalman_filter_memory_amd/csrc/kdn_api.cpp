@@ -20,6 +20,13 @@
 
 #include "kdn_kernels.h"
 
+namespace kdn {
+LaunchTiming& launch_timing() {
+    static thread_local LaunchTiming t;
+    return t;
+}
+}  // namespace kdn
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -145,21 +152,27 @@ kdn_status kdn_forward_events(const kdn_desc* d, const void* q, const void* k, c
     void* wk = at(ws, w.w);
     void* tm = at(ws, w.tm);
     float* g = reinterpret_cast<float*>(at(ws, w.g));
-    auto mark = [&](int i) {
-        // a failed record only loses a timing mark; the kernels' status is what is returned
-        if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), hs);
+    // timing: the dispatches themselves record the start and stop events of
+    // each kernel (entries may be NULL)
+    auto timed = [&](int i) {
+        kdn::LaunchTiming t;
+        if (events) {
+            t.start = static_cast<hipEvent_t>(events[2 * i]);
+            t.stop = static_cast<hipEvent_t>(events[2 * i + 1]);
+        }
+        kdn::launch_timing() = t;
     };
-    mark(0);
+    timed(0);
     hipError_t e = kdn::launch_scan_reduce(s, k, a, qnoise, r, agg, hs);
-    mark(1);
+    timed(1);
     if (e == hipSuccess) e = kdn::launch_scan_carry(s, agg, lambda0, lc, lambda_T, hs);
-    mark(2);
     kdn::Shape sw = s;
     sw.gain_bf16 = s.qkv_bf16;
+    timed(2);
     if (e == hipSuccess) e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, g, hs);
-    mark(3);
+    timed(3);
     if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs);
-    mark(4);
+    kdn::launch_timing() = kdn::LaunchTiming{};
     return hip_status(e);
 }
 

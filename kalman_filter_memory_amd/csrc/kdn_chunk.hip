@@ -1275,12 +1275,12 @@ hipError_t prep_t(const Shape& s, bool fuse, const void* k, const void* a, const
     static_assert(PrepLds<E, DK, C>::BYTES <= kLdsLimit, "prep LDS");
     const dim3 grid((s.nc + 1) / 2, s.BH);
     if (fuse)
-        hipLaunchKernelGGL((prep_kernel<E, G, DK, C, true>), grid, dim3(kThreads), 0, st,
+        launch_k((prep_kernel<E, G, DK, C, true>), grid, dim3(kThreads), 0, st,
                            static_cast<const E*>(k), static_cast<const G*>(a),
                            static_cast<const G*>(nu), static_cast<const G*>(r), s.diag, lc,
                            static_cast<E*>(w), static_cast<E*>(Tm), g, s.T, s.nc);
     else
-        hipLaunchKernelGGL((prep_kernel<E, G, DK, C, false>), grid, dim3(kThreads), 0, st,
+        launch_k((prep_kernel<E, G, DK, C, false>), grid, dim3(kThreads), 0, st,
                            static_cast<const E*>(k), static_cast<const G*>(a),
                            static_cast<const G*>(nu), static_cast<const G*>(r), s.diag, lc,
                            static_cast<E*>(w), static_cast<E*>(Tm), g, s.T, s.nc);
@@ -1293,7 +1293,7 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
                    hipStream_t st) {
     if constexpr (state_fits<E, DK, DVT, C>()) {
         const int groups = (s.BH + 7) / 8;
-        hipLaunchKernelGGL((state_kernel<E, DK, DVT, C>), dim3(groups * 8 * (s.dv / DVT)),
+        launch_k((state_kernel<E, DK, DVT, C>), dim3(groups * 8 * (s.dv / DVT)),
                            dim3(StateCfg<E, DK, DVT, C>::THREADS), 0, st,
                            static_cast<const E*>(q), static_cast<const E*>(k),
                            static_cast<const E*>(v), g, static_cast<const E*>(w),

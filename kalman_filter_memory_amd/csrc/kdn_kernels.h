@@ -1,11 +1,29 @@
 // kdn_kernels.h -- host-side launchers of the libkdn kernels (internal).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace kdn {
+
+// Optional timing of the next kernel launched through launch_k: the dispatch
+// itself records the start and stop events (hipExtLaunchKernel), so that no
+// marker packet sits between the kernels.  Per host thread; consumed by that
+// one launch.
+struct LaunchTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchTiming& launch_timing();
+
+template <typename F, typename... Args>
+inline void launch_k(F kernel, dim3 grid, dim3 block, unsigned shmem, hipStream_t st,
+                     Args... args) {
+    LaunchTiming& t = launch_timing();
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, t.start, t.stop, 0u, args...);
+    t = LaunchTiming{};
+}
 
 struct Shape {
     int BH;  // B * H (heads, or sequences * heads for decode)

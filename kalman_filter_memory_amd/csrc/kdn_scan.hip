@@ -398,19 +398,19 @@ hipError_t reduce_e(const Shape& s, const void* k, const void* a, const void* nu
 #define KDN_RED_D(DK_, C_)                                                                    \
     if (s.diag && s.dk == DK_ && s.chunk == C_) {                                             \
         if (s.gate_bf16)                                                                      \
-            hipLaunchKernelGGL((reduce_diag_kernel<E, bf16_t, DK_, C_>), grid, block, 0, st,  \
+            launch_k((reduce_diag_kernel<E, bf16_t, DK_, C_>), grid, block, 0, st,  \
                                kk, static_cast<const bf16_t*>(a),                             \
                                static_cast<const bf16_t*>(nu), static_cast<const bf16_t*>(r), \
                                s.T, s.nc, g);                                                 \
         else                                                                                  \
-            hipLaunchKernelGGL((reduce_diag_kernel<E, float, DK_, C_>), grid, block, 0, st,   \
+            launch_k((reduce_diag_kernel<E, float, DK_, C_>), grid, block, 0, st,   \
                                kk, static_cast<const float*>(a), static_cast<const float*>(nu), \
                                static_cast<const float*>(r), s.T, s.nc, g);                   \
         return hipGetLastError();                                                             \
     }
 #define KDN_RED_I(DK_)                                                                        \
     if (!s.diag && s.dk == DK_) {                                                             \
-        hipLaunchKernelGGL((reduce_iso_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r,       \
+        launch_k((reduce_iso_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r,       \
                            s.gate_bf16, s.T, s.chunk, s.nc, g);                               \
         return hipGetLastError();                                                             \
     }
@@ -432,10 +432,10 @@ hipError_t emit_e(const Shape& s, const void* k, const void* a, const void* nu, 
 #define KDN_EMIT(DK_)                                                                        \
     if (s.dk == DK_) {                                                                       \
         if (s.diag)                                                                          \
-            hipLaunchKernelGGL((emit_diag_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r,   \
+            launch_k((emit_diag_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r,   \
                                s.gate_bf16, s.T, s.chunk, s.nc, lam_chunk, lm);              \
         else                                                                                 \
-            hipLaunchKernelGGL((emit_iso_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r,    \
+            launch_k((emit_iso_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r,    \
                                s.gate_bf16, s.T, s.chunk, s.nc, lam_chunk, lm);              \
         return hipGetLastError();                                                            \
     }
@@ -455,7 +455,7 @@ hipError_t gain_ew(const Shape& s, const void* k, const void* r, const float* lm
     W* ww = static_cast<W*>(w);
 #define KDN_GAIN(DK_)                                                                      \
     if (s.dk == DK_) {                                                                     \
-        hipLaunchKernelGGL((gain_kernel<E, W, DK_>), grid, block, 0, st, kk, r, s.gate_bf16, \
+        launch_k((gain_kernel<E, W, DK_>), grid, block, 0, st, kk, r, s.gate_bf16, \
                            s.diag, n_tok, lm, ww);                                         \
         return hipGetLastError();                                                          \
     }
@@ -481,10 +481,10 @@ hipError_t launch_scan_carry(const Shape& s, const float* agg, const float* lamb
     const dim3 grid((unsigned)((n + kCarryScans - 1) / kCarryScans)), block(kWave);
     const float4* a4 = reinterpret_cast<const float4*>(agg);
     if (s.nc <= kCarrySeg * kCarryGroup)
-        hipLaunchKernelGGL(carry_kernel<true>, grid, block, 0, st, a4, lambda0, s.BH, NL, s.nc,
+        launch_k(carry_kernel<true>, grid, block, 0, st, a4, lambda0, s.BH, NL, s.nc,
                            lam_chunk, lambda_T);
     else
-        hipLaunchKernelGGL(carry_kernel<false>, grid, block, 0, st, a4, lambda0, s.BH, NL, s.nc,
+        launch_k(carry_kernel<false>, grid, block, 0, st, a4, lambda0, s.BH, NL, s.nc,
                            lam_chunk, lambda_T);
     return hipGetLastError();
 }
