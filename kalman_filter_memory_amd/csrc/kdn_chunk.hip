@@ -387,9 +387,12 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
             float kc[16][NPL];
             M2 m[NPL];
             if (act) {
-                // (1) the sub-block's 16 token maps composed, renormalised every 8
 #pragma unroll
                 for (int j = 0; j < 16; ++j) load_dims<E, NPL>(sK + (tb0 + j) * LDK + i0, kc[j]);
+            }
+            if (act && wave < NT - 1) {
+                // (1) the sub-block's 16 token maps composed, renormalised every 8 (the
+                // last sub-block's product is not needed)
 #pragma unroll
                 for (int d = 0; d < NPL; ++d) m[d] = M2{1.f, 0.f, 0.f, 1.f};
 #pragma unroll
@@ -402,11 +405,9 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
                         if ((j & 7) == 7) m[d] = mob_renorm(m[d]);
                     }
                 }
-                if (wave < NT - 1) {
 #pragma unroll
-                    for (int d = 0; d < NPL; ++d)
-                        sprod[wave * DK + i0 + d] = make_float4(m[d].a, m[d].b, m[d].c, m[d].d);
-                }
+                for (int d = 0; d < NPL; ++d)
+                    sprod[wave * DK + i0 + d] = make_float4(m[d].a, m[d].b, m[d].c, m[d].d);
             }
             sync_lds();
             float pk[16][NPL];
@@ -420,7 +421,7 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
 #pragma unroll
                     for (int d = 0; d < NPL; ++d) {
                         const float4 q4 = sprod[sb * DK + i0 + d];
-                        lam[d] = mob_apply(M2{q4.x, q4.y, q4.z, q4.w}, lam[d]);
+                        lam[d] = fmaf(q4.x, lam[d], q4.y) * rcp(fmaf(q4.z, lam[d], q4.w));
                     }
                 }
                 // (3) walk in variance form, P = 1 / lambda: P^- = a^2 P + nu, then
