@@ -7,6 +7,9 @@ Prints ONE JSON line with tokens/s (tokens = B*T positions, all 16 heads),
 the roofline of the dominant kernel timed with HIP events on the stream the
 kernels run on, the per-kernel breakdown, the decode step's bandwidth, and
 the fp64 CPU oracle timed on a bounded sample of the same workload.
+Before the W warmup steps the forward runs untimed for --ramp-ms of wall time
+(default 0.2 s), so that the K timed steps see the clocks of a GPU that is
+running continuously rather than one just out of idle.
 """
 from __future__ import annotations
 
@@ -130,6 +133,7 @@ def run(args):
         torch.cuda.synchronize()
         log(f"copy calibration: {nb} bytes read and written")
         del src, dst
+    ramp(step, args.ramp_ms)
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -188,7 +192,7 @@ def run(args):
         "metric": "KDN fwd tokens/s (B8 T4096 H16 d128); % MFMA peak; decode GB/s",
         "value": round(B * T / (ms * 1e-3), 1),
         "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ramp_ms": args.ramp_ms,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
@@ -211,6 +215,24 @@ def run(args):
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args)
     print(json.dumps(res), flush=True)
+
+
+def ramp(fn, ms):
+    """Run fn back to back for about `ms` milliseconds of wall time, untimed.
+
+    An idle GPU runs its first tens of milliseconds of work at lower clocks
+    (measured on MI355X: 20 back-to-back forward steps after a pause take
+    ~350 us each, the same steps after ~50 ms of work ~297 us), so the timed
+    steps start from the state a continuously running layer is in."""
+    import torch
+
+    if ms <= 0:
+        return
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
 
 
 def bench_decode(args):
@@ -236,6 +258,7 @@ def bench_decode(args):
         kdn.decode_step(x["q"][s], x["k"][s], x["v"][s], x["a"][s], x["nu"][s], x["r"][s], S,
                         lam, "diagonal", out=o)
 
+    ramp(lambda: one(0), args.ramp_ms / 2)
     for s in range(4):
         one(s)
     torch.cuda.synchronize()
@@ -284,8 +307,11 @@ def cpu_baseline(inp, args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--ramp-ms", type=float, default=200.0,
+                    help="untimed back-to-back steps for this long before the warmup steps, "
+                         "so that the GPU is out of its idle clock state (0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
