@@ -107,50 +107,66 @@ template <> struct GateRaw<float> {
     }
 };
 
+// A chunk of 64 tokens is split over two waves of a workgroup (32 keys in
+// registers each, eight waves per SIMD); the second wave multiplies the first
+// one's product in through LDS.
+template <int C> struct RedSplit {
+    static constexpr int SPLIT = C >= 64 ? 2 : 1;       // waves per chunk
+    static constexpr int TPW = C / SPLIT;               // tokens per wave
+    static constexpr int CPB = kWavesPerBlock / SPLIT;  // chunks per workgroup
+};
+
 template <typename E, typename G, int DK, int C>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
     const E* __restrict__ k, const G* __restrict__ a, const G* __restrict__ nu,
     const G* __restrict__ r, int T, int NC, float4* __restrict__ agg) {
     using L = Lanes<DK>;
     using KR = KeyRaw<E, L::IPL>;
-    __shared__ float4 sgate[kWavesPerBlock][C];  // per token of the wave's chunk: a^2, nu, 1/r
+    using RS = RedSplit<C>;
+    constexpr int TPW = RS::TPW;
+    __shared__ float4 sgate[kWavesPerBlock][TPW];  // per token of the wave: a^2, nu, 1/r
+    __shared__ float4 spart[RS::SPLIT > 1 ? RS::CPB : 1][RS::SPLIT > 1 ? DK : 1];
     const int lane = threadIdx.x & 63, wave = wave_id();
-    const int c = blockIdx.x * kWavesPerBlock + wave;
+    const int part = wave % RS::SPLIT, cb = wave / RS::SPLIT;
+    const int c_raw = blockIdx.x * RS::CPB + cb;
+    const bool live = c_raw < NC;  // no early exit: the halves of a chunk meet at a barrier
+    const int c = live ? c_raw : NC - 1;
     const size_t bh = blockIdx.y;
-    if (c >= NC) return;
     const int t0 = c * C, n = min(C, T - t0);
+    const int tb = part * TPW;  // first token of this wave in the chunk
     const bool act = lane < L::ACTIVE;
-    // every load of the chunk first: the gates of token `lane`, then the keys
-    // of all C tokens for this lane's dims (rows past the end repeat the last
+    // every load first: the gates of token tb + lane, then the keys of the
+    // wave's tokens for this lane's dims (rows past the end repeat the last
     // one); row offsets are uniform, only the lane's column varies
     const size_t row0 = bh * T + t0;
     const unsigned gbytes = static_cast<unsigned>(n * sizeof(G));
-    const unsigned goff = static_cast<unsigned>(min(lane, n - 1) * sizeof(G));
+    const unsigned goff = static_cast<unsigned>(min(tb + lane, n - 1) * sizeof(G));
     const G ra = GateRaw<G>::load(buffer_rsrc(a + row0, gbytes), goff);
     const G rnu = GateRaw<G>::load(buffer_rsrc(nu + row0, gbytes), goff);
     const G rr = GateRaw<G>::load(buffer_rsrc(r + row0, gbytes), goff);
     const __amdgpu_buffer_rsrc_t kc =
         buffer_rsrc(k + row0 * DK, static_cast<unsigned>(n * DK * sizeof(E)));
     const unsigned col = (act ? lane : 0) * L::IPL * sizeof(E);
-    typename KR::type kr[C];
+    typename KR::type kr[TPW];
 #pragma unroll
-    for (int u = 0; u < C; ++u) kr[u] = KR::load(kc, col, min(u, n - 1) * DK * sizeof(E));
-    // lane t: gates of token t (padding: the identity, a = 1, nu = 0, 1/r = 0),
-    // handed to every lane through LDS (one broadcast read per token)
-    // (padding by arithmetic, not a select, which would be compiled to a branch
-    // around the gate loads, placing them after the keys)
+    for (int u = 0; u < TPW; ++u)
+        kr[u] = KR::load(kc, col, min(tb + u, n - 1) * DK * sizeof(E));
+    // lane t: gates of token tb + t (padding: the identity, a = 1, nu = 0,
+    // 1/r = 0), handed to every lane of the wave through LDS (one broadcast read
+    // per token).  Padding by arithmetic, not a select, which would be compiled
+    // to a branch around the gate loads, placing them after the keys.
     {
-        const float at = to_f<G>(ra), m = lane < n ? 1.f : 0.f;
+        const float at = to_f<G>(ra), m = tb + lane < n ? 1.f : 0.f;
         const float4 g = make_float4(fmaf(at * at, m, 1.f - m), to_f<G>(rnu) * m,
                                      __builtin_amdgcn_rcpf(to_f<G>(rr)) * m, 0.f);
-        if (lane < C) sgate[wave][lane] = g;
+        if (lane < TPW) sgate[wave][lane] = g;
     }
     __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in order
     M2 P[L::IPL];
 #pragma unroll
     for (int j = 0; j < L::IPL; ++j) P[j] = {1.f, 0.f, 0.f, 1.f};
 #pragma unroll
-    for (int t = 0; t < C; ++t) {
+    for (int t = 0; t < TPW; ++t) {
         float kv[L::IPL];
         KR::widen(kr[t], kv);
         const float4 g = sgate[wave][t];
@@ -160,7 +176,24 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
 #pragma unroll
             for (int j = 0; j < L::IPL; ++j) P[j] = mob_renorm(P[j]);
     }
-    if (act) {
+    if constexpr (RS::SPLIT > 1) {
+        static_assert(RS::SPLIT == 2, "two waves per chunk");
+        if (part == 0 && act) {
+#pragma unroll
+            for (int j = 0; j < L::IPL; ++j)
+                spart[cb][lane * L::IPL + j] = make_float4(P[j].a, P[j].b, P[j].c, P[j].d);
+        }
+        __syncthreads();
+        if (part == 0) return;
+        if (act) {
+#pragma unroll
+            for (int j = 0; j < L::IPL; ++j) {
+                const float4 f = spart[cb][lane * L::IPL + j];
+                P[j] = mob_mul(P[j], M2{f.x, f.y, f.z, f.w});
+            }
+        }
+    }
+    if (act && live) {
 #pragma unroll
         for (int j = 0; j < L::IPL; ++j) {
             const M2 m = mob_renorm(P[j]);
@@ -397,13 +430,15 @@ hipError_t reduce_e(const Shape& s, const void* k, const void* a, const void* nu
     const E* kk = static_cast<const E*>(k);
 #define KDN_RED_D(DK_, C_)                                                                    \
     if (s.diag && s.dk == DK_ && s.chunk == C_) {                                             \
+        constexpr int cpb = RedSplit<C_>::CPB;                                                \
+        const dim3 gridd((s.nc + cpb - 1) / cpb, s.BH);                                       \
         if (s.gate_bf16)                                                                      \
-            launch_k((reduce_diag_kernel<E, bf16_t, DK_, C_>), grid, block, 0, st,  \
+            launch_k((reduce_diag_kernel<E, bf16_t, DK_, C_>), gridd, block, 0, st,  \
                                kk, static_cast<const bf16_t*>(a),                             \
                                static_cast<const bf16_t*>(nu), static_cast<const bf16_t*>(r), \
                                s.T, s.nc, g);                                                 \
         else                                                                                  \
-            launch_k((reduce_diag_kernel<E, float, DK_, C_>), grid, block, 0, st,   \
+            launch_k((reduce_diag_kernel<E, float, DK_, C_>), gridd, block, 0, st,  \
                                kk, static_cast<const float*>(a), static_cast<const float*>(nu), \
                                static_cast<const float*>(r), s.T, s.nc, g);                   \
         return hipGetLastError();                                                             \
