@@ -87,6 +87,25 @@ def forward_inputs(B, H, T, dk, dv, *, variant=DIAGONAL, dtype="f32", gate_dtype
     return out
 
 
+def backward_cotangents(B, H, T, dk, dv, *, variant=DIAGONAL, dtype="f32", seed=0,
+                        state_cotangents=True) -> dict:
+    """Cotangents of one backward call: dO [B,H,T,dv] ~ N(0, 1) in the input
+    dtype; dS_T [B,H,dv,dk] ~ N(0, variance 0.1) and dlambda_T ([B,H,dk] or
+    [B,H]) ~ N(0, variance 0.01) as float32, or None with
+    state_cotangents=False.  Drawn from their own PCG64 stream (seed + 7919),
+    so the forward inputs of the same seed are unchanged."""
+    rng = np.random.default_rng(seed + 7919)
+    out = {"dO": _round(rng.standard_normal((B, H, T, dv)), dtype)}
+    lam_shape = (B, H, dk) if variant == DIAGONAL else (B, H)
+    if state_cotangents:
+        out["dS_T"] = rng.normal(0.0, math.sqrt(0.1), (B, H, dv, dk)).astype(np.float32)
+        out["dlambda_T"] = rng.normal(0.0, 0.1, lam_shape).astype(np.float32)
+    else:
+        out["dS_T"] = None
+        out["dlambda_T"] = None
+    return out
+
+
 def decode_inputs(N, H, dk, dv, steps, *, variant=DIAGONAL, seed=0, qkv_dtype="bf16",
                   gate_dtype="f32", a_mu=2.0) -> dict:
     """Cached state plus per-step inputs of `steps` decode steps.

@@ -50,6 +50,8 @@ def _load():
         lib.kdn_oracle_forward.restype = I
         lib.kdn_oracle_decode_step.argtypes = [I, I, I, I, I] + [P] * 9 + [I]
         lib.kdn_oracle_decode_step.restype = I
+        lib.kdn_oracle_backward.argtypes = [I, I, I, I, I, I] + [P] * 19 + [I]
+        lib.kdn_oracle_backward.restype = I
         _lib = lib
     return _lib
 
@@ -141,3 +143,46 @@ def decode_step(q, k, v, a, nu, r, S, lam, variant="diagonal", threads: int | No
     if rc != 0:
         raise ValueError(f"kdn_oracle_decode_step rejected its arguments (code {rc})")
     return o
+
+
+def backward(q, k, v, a, nu, r, dO, lambda0=None, S0=None, dS_T=None, dlambda_T=None,
+             variant="diagonal", threads: int | None = None) -> dict:
+    """fp64 gradient of L = <dO, o> + <dS_T, S_T> + <dlambda_T, lambda_T> (the
+    last two taken as zero when None) with respect to every input of
+    ``forward``: returns float64 arrays dq, dk, dv, da, dnu, dr, dlambda0, dS0
+    shaped like the inputs (dlambda0 and dS0 also when lambda0 / S0 were None,
+    the defaults ones / zeros being the point of evaluation)."""
+    lib = _load()
+    var = _variant(variant)
+    q, k, v, a, nu, r, dO = (_f32(x) for x in (q, k, v, a, nu, r, dO))
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    assert q.shape == k.shape and v.shape == (B, H, T, dv) and dO.shape == v.shape
+    assert a.shape == (B, H, T) and nu.shape == a.shape and r.shape == a.shape
+    lam_shape = (B, H, dk) if var == DIAGONAL else (B, H)
+    if lambda0 is not None:
+        lambda0 = _f32(lambda0)
+        assert lambda0.shape == lam_shape
+    if S0 is not None:
+        S0 = _f32(S0)
+        assert S0.shape == (B, H, dv, dk)
+    if dS_T is not None:
+        dS_T = _f32(dS_T)
+        assert dS_T.shape == (B, H, dv, dk)
+    if dlambda_T is not None:
+        dlambda_T = _f32(dlambda_T)
+        assert dlambda_T.shape == lam_shape
+    out = {
+        "dq": np.empty((B, H, T, dk)), "dk": np.empty((B, H, T, dk)),
+        "dv": np.empty((B, H, T, dv)), "da": np.empty((B, H, T)),
+        "dnu": np.empty((B, H, T)), "dr": np.empty((B, H, T)),
+        "dlambda0": np.empty(lam_shape), "dS0": np.empty((B, H, dv, dk)),
+    }
+    rc = lib.kdn_oracle_backward(
+        B, H, T, dk, dv, var, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(nu), _ptr(r),
+        _ptr(lambda0), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(dlambda_T),
+        *(_ptr(out[n]) for n in ("dq", "dk", "dv", "da", "dnu", "dr", "dlambda0", "dS0")),
+        threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"kdn_oracle_backward rejected its arguments (code {rc})")
+    return out

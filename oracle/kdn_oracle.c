@@ -261,3 +261,233 @@ int kdn_oracle_decode_step(int N, int H, int dk, int dv, int variant, const floa
     free(jobs);
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Reverse-mode derivative of kdn_oracle_forward (a vector-Jacobian product).
+ *
+ * Given the cotangents dO [B,H,T,d_v], dS_T [B,H,d_v,d_k] (NULL: zero) and
+ * dlambda_T (NULL: zero), it returns the gradient of
+ *     L = <dO, o> + <dS_T, S_T> + <dlambda_T, lambda_T>
+ * with respect to every input: dq, dk [B,H,T,d_k], dv [B,H,T,d_v],
+ * da, dnu, dr [B,H,T], dlambda0 (like lambda0) and dS0 (like S0).  Training
+ * the layer needs exactly these ("Kalman Delta Networks", English abstract:
+ * the variants are pretrained inside language models of 750M and 1.3B
+ * parameters).
+ *
+ * It differentiates the per-token steps of kdn_token above, in the reverse of
+ * their order, by the chain rule written out; nothing is re-associated.  The
+ * rows of S evolve independently given the gains, so the mean part runs row
+ * by row; the precision recursion (which does not see S) runs per head.
+ *
+ * Mean, for one row s of S (u = v_j - a s_{t-1}.k, s_t = a s_{t-1} + u w,
+ * o_j = s_t.q), with sigma the adjoint of s_t:
+ *     sigma += do_j q;  dq += do_j s_t;  du = sigma.w;  dw += u sigma;
+ *     dv_j = du;  dk -= du a s_{t-1};  da += sigma.s_{t-1} - du (s_{t-1}.k);
+ *     sigma <- a sigma - a du k.
+ * Precision, per token in reverse with Lambda the adjoint of lambda_t:
+ *     lambda_t = lambda^- + (k.k)/r   (isotropic: + |k|^2/(d_k r))
+ *     w = P^- k / D,  D = r + sum_i k_i^2 P^-_i   (isotropic: D = P^- |k|^2 + r)
+ *     lambda^- = lambda_{t-1} / (a^2 + nu lambda_{t-1}),  P^- = 1/lambda^-.
+ * Inputs are single precision as in the forward; every operation is double.
+ * Return value as kdn_oracle_forward.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int T, dk, dv, variant;
+    const float *q, *k, *v, *a, *nu, *r, *lambda0, *S0, *dO, *dS_T, *dlam_T;
+    double *dq, *dk_, *dv_, *da, *dnu, *dr, *dlam0, *dS0;
+    int n_heads, n_threads, tid;
+} bjob_t;
+
+static void *run_heads_backward(void *arg)
+{
+    const bjob_t *J = (const bjob_t *)arg;
+    const int T = J->T, dk = J->dk, dv = J->dv;
+    const int diag = J->variant == KDN_ORACLE_DIAGONAL;
+    const int nl = diag ? dk : 1;
+    double *lamprev = (double *)malloc(sizeof(double) * ((size_t)T * nl + 1));
+    double *lmh = (double *)malloc(sizeof(double) * ((size_t)T * nl + 1));
+    double *wh = (double *)malloc(sizeof(double) * ((size_t)T * dk + 1));
+    double *Dh = (double *)malloc(sizeof(double) * ((size_t)T + 1));
+    double *hist = (double *)malloc(sizeof(double) * ((size_t)(T + 1) * dk));
+    double *dw = (double *)malloc(sizeof(double) * ((size_t)T * dk + 1));
+    double *lam = (double *)malloc(sizeof(double) * (size_t)nl);
+    double *Lam = (double *)malloc(sizeof(double) * (size_t)nl);
+    double *sig = (double *)malloc(sizeof(double) * (size_t)dk);
+    int bh, t, i, j;
+    for (bh = J->tid; bh < J->n_heads; bh += J->n_threads) {
+        const size_t tok0 = (size_t)bh * T;
+        double *dq = J->dq + tok0 * dk, *dkk = J->dk_ + tok0 * dk, *dvv = J->dv_ + tok0 * dv;
+        double *da = J->da + tok0, *dnu = J->dnu + tok0, *dr = J->dr + tok0;
+        /* precision recursion forward: lambda_{t-1}, lambda^-_t, w_t, D_t */
+        for (i = 0; i < nl; ++i)
+            lam[i] = J->lambda0 ? (double)J->lambda0[(size_t)bh * nl + i] : 1.0;
+        for (t = 0; t < T; ++t) {
+            const float *kt = J->k + (tok0 + t) * dk;
+            const double a = J->a[tok0 + t], nu = J->nu[tok0 + t], r = J->r[tok0 + t];
+            double D;
+            for (i = 0; i < nl; ++i) {
+                lamprev[(size_t)t * nl + i] = lam[i];
+                lmh[(size_t)t * nl + i] = lam[i] / (a * a + nu * lam[i]);
+            }
+            if (diag) {
+                D = r;
+                for (i = 0; i < dk; ++i) D += (double)kt[i] * (double)kt[i] / lmh[(size_t)t * dk + i];
+                for (i = 0; i < dk; ++i) {
+                    wh[(size_t)t * dk + i] = ((double)kt[i] / lmh[(size_t)t * dk + i]) / D;
+                    lam[i] = lmh[(size_t)t * dk + i] + (double)kt[i] * (double)kt[i] / r;
+                }
+            } else {
+                double kk = 0.0, p = 1.0 / lmh[t];
+                for (i = 0; i < dk; ++i) kk += (double)kt[i] * (double)kt[i];
+                D = p * kk + r;
+                for (i = 0; i < dk; ++i) wh[(size_t)t * dk + i] = p * (double)kt[i] / D;
+                lam[0] = lmh[t] + kk / ((double)dk * r);
+            }
+            Dh[t] = D;
+        }
+        for (i = 0; i < T * dk; ++i) { dq[i] = 0.0; dkk[i] = 0.0; dw[i] = 0.0; }
+        for (t = 0; t < T; ++t) { da[t] = 0.0; dnu[t] = 0.0; dr[t] = 0.0; }
+        /* mean: one row of S at a time, forward (keeping every s_t) then reverse */
+        for (j = 0; j < dv; ++j) {
+            for (i = 0; i < dk; ++i)
+                hist[i] = J->S0 ? (double)J->S0[((size_t)bh * dv + j) * dk + i] : 0.0;
+            for (t = 0; t < T; ++t) {
+                const float *kt = J->k + (tok0 + t) * dk;
+                const double a = J->a[tok0 + t];
+                const double *sp = hist + (size_t)t * dk;
+                double *sn = hist + (size_t)(t + 1) * dk;
+                double sk = 0.0, u;
+                for (i = 0; i < dk; ++i) sk += a * sp[i] * (double)kt[i];
+                u = (double)J->v[(tok0 + t) * dv + j] - sk;
+                for (i = 0; i < dk; ++i) sn[i] = a * sp[i] + u * wh[(size_t)t * dk + i];
+            }
+            for (i = 0; i < dk; ++i)
+                sig[i] = J->dS_T ? (double)J->dS_T[((size_t)bh * dv + j) * dk + i] : 0.0;
+            for (t = T - 1; t >= 0; --t) {
+                const float *kt = J->k + (tok0 + t) * dk, *qt = J->q + (tok0 + t) * dk;
+                const double a = J->a[tok0 + t];
+                const double doj = J->dO[(tok0 + t) * dv + j];
+                const double *sp = hist + (size_t)t * dk, *sn = hist + (size_t)(t + 1) * dk;
+                const double *wt = wh + (size_t)t * dk;
+                double sk = 0.0, du = 0.0, ss = 0.0, u;
+                for (i = 0; i < dk; ++i) {
+                    sig[i] += doj * (double)qt[i];
+                    dq[(size_t)t * dk + i] += doj * sn[i];
+                    sk += sp[i] * (double)kt[i];
+                }
+                u = (double)J->v[(tok0 + t) * dv + j] - a * sk;
+                for (i = 0; i < dk; ++i) {
+                    du += sig[i] * wt[i];
+                    dw[(size_t)t * dk + i] += u * sig[i];
+                    ss += sig[i] * sp[i];
+                }
+                dvv[(size_t)t * dv + j] = du;
+                da[t] += ss - du * sk;
+                for (i = 0; i < dk; ++i) {
+                    dkk[(size_t)t * dk + i] -= du * a * sp[i];
+                    sig[i] = a * sig[i] - a * du * (double)kt[i];
+                }
+            }
+            if (J->dS0)
+                for (i = 0; i < dk; ++i) J->dS0[((size_t)bh * dv + j) * dk + i] = sig[i];
+        }
+        /* precision recursion in reverse */
+        for (i = 0; i < nl; ++i) Lam[i] = J->dlam_T ? (double)J->dlam_T[(size_t)bh * nl + i] : 0.0;
+        for (t = T - 1; t >= 0; --t) {
+            const float *kt = J->k + (tok0 + t) * dk;
+            const double a = J->a[tok0 + t], nu = J->nu[tok0 + t], r = J->r[tok0 + t];
+            const double D = Dh[t];
+            const double *wt = wh + (size_t)t * dk, *dwt = dw + (size_t)t * dk;
+            double s = 0.0;
+            for (i = 0; i < dk; ++i) s += dwt[i] * wt[i];
+            dr[t] += -s / D;
+            if (diag) {
+                for (i = 0; i < dk; ++i) {
+                    const double ki = kt[i], lm = lmh[(size_t)t * dk + i], p = 1.0 / lm;
+                    const double lp = lamprev[(size_t)t * dk + i], e = a * a + nu * lp;
+                    double dlm = Lam[i], dp;
+                    /* lambda_t = lambda^- + k^2 / r */
+                    dkk[(size_t)t * dk + i] += Lam[i] * 2.0 * ki / r;
+                    dr[t] += -Lam[i] * ki * ki / (r * r);
+                    /* w = P^- k / D */
+                    dp = (ki / D) * (dwt[i] - ki * s);
+                    dkk[(size_t)t * dk + i] += (p / D) * (dwt[i] - 2.0 * ki * s);
+                    dlm += -dp * p * p;
+                    /* lambda^- = lambda_{t-1} / (a^2 + nu lambda_{t-1}) */
+                    Lam[i] = dlm * a * a / (e * e);
+                    da[t] += dlm * (-2.0 * a * lp) / (e * e);
+                    dnu[t] += dlm * (-lp * lp) / (e * e);
+                }
+            } else {
+                double kk = 0.0, z = 0.0, dkap, dp, dlm;
+                const double lm = lmh[t], p = 1.0 / lm, lp = lamprev[t], e = a * a + nu * lp;
+                for (i = 0; i < dk; ++i) {
+                    kk += (double)kt[i] * (double)kt[i];
+                    z += dwt[i] * (double)kt[i];
+                }
+                /* lambda_t = lambda^- + |k|^2 / (d_k r) */
+                dlm = Lam[0];
+                dkap = Lam[0] / ((double)dk * r);
+                dr[t] += -Lam[0] * kk / ((double)dk * r * r);
+                /* w = P^- k / (P^- |k|^2 + r) */
+                dp = z / D - s * kk / D;
+                dkap += -p * s / D;
+                for (i = 0; i < dk; ++i)
+                    dkk[(size_t)t * dk + i] += dwt[i] * p / D + dkap * 2.0 * (double)kt[i];
+                dlm += -dp * p * p;
+                Lam[0] = dlm * a * a / (e * e);
+                da[t] += dlm * (-2.0 * a * lp) / (e * e);
+                dnu[t] += dlm * (-lp * lp) / (e * e);
+            }
+        }
+        if (J->dlam0)
+            for (i = 0; i < nl; ++i) J->dlam0[(size_t)bh * nl + i] = Lam[i];
+    }
+    free(lamprev); free(lmh); free(wh); free(Dh); free(hist); free(dw);
+    free(lam); free(Lam); free(sig);
+    return NULL;
+}
+
+int kdn_oracle_backward(int B, int H, int T, int dk, int dv, int variant, const float *q,
+                        const float *k, const float *v, const float *a, const float *nu,
+                        const float *r, const float *lambda0, const float *S0, const float *dO,
+                        const float *dS_T, const float *dlambda_T, double *dq, double *dk_,
+                        double *dv_, double *da, double *dnu, double *dr, double *dlambda0,
+                        double *dS0, int n_threads)
+{
+    bjob_t base, *jobs;
+    pthread_t *th;
+    int i, rc, n_heads = B * H;
+    size_t nl;
+    if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1) return -1;
+    if (variant != KDN_ORACLE_DIAGONAL && variant != KDN_ORACLE_ISOTROPIC) return -1;
+    if (T > 0 && (!q || !k || !v || !a || !nu || !r || !dO || !dq || !dk_ || !dv_ || !da ||
+                  !dnu || !dr))
+        return -2;
+    nl = (variant == KDN_ORACLE_DIAGONAL) ? (size_t)dk : 1;
+    rc = check_values((size_t)B * H * T, (size_t)B * H * nl, a, nu, r, lambda0);
+    if (rc) return rc;
+    if (n_heads == 0) return 0;
+    base.T = T; base.dk = dk; base.dv = dv; base.variant = variant;
+    base.q = q; base.k = k; base.v = v; base.a = a; base.nu = nu; base.r = r;
+    base.lambda0 = lambda0; base.S0 = S0; base.dO = dO; base.dS_T = dS_T;
+    base.dlam_T = dlambda_T;
+    base.dq = dq; base.dk_ = dk_; base.dv_ = dv_; base.da = da; base.dnu = dnu; base.dr = dr;
+    base.dlam0 = dlambda0; base.dS0 = dS0;
+    base.n_heads = n_heads;
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > n_heads) n_threads = n_heads;
+    th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+    jobs = (bjob_t *)malloc(sizeof(bjob_t) * (size_t)n_threads);
+    for (i = 0; i < n_threads; ++i) {
+        jobs[i] = base;
+        jobs[i].tid = i;
+        jobs[i].n_threads = n_threads;
+    }
+    for (i = 1; i < n_threads; ++i) pthread_create(&th[i], NULL, run_heads_backward, &jobs[i]);
+    run_heads_backward(&jobs[0]);
+    for (i = 1; i < n_threads; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+    return 0;
+}
