@@ -323,10 +323,13 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
             }
             den += __shfl_xor(den, 16, kWave);
             den += __shfl_xor(den, 32, kWave);
+            // lane l: r of token tb0 + l % 16, gathered from the lane that loaded it
+            // with every lane active (with d_k < 64 the lanes past d_k are off
+            // inside the branch below, and a shuffle reads nothing from them)
+            const float rt = __shfl(gr, tb0 + (lane & 15), kWave);
             sync_lds();  // W overwrites the sub-block maps
             if (act) {
-                // lane l: token tb0 + l % 16 (r gathered from the lane that loaded it)
-                const float rden = 1.f / (den + __shfl(gr, tb0 + (lane & 15), kWave));
+                const float rden = 1.f / (den + rt);
                 // (5) w rows
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {

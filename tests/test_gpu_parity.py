@@ -63,6 +63,9 @@ SMALL = [
     (2, 2, 65, 128, 32, 64, "diagonal", "bf16"),
     (1, 3, 64, 32, 128, 64, "isotropic", "f32"),
     (3, 1, 300, 128, 128, 16, "diagonal", "bf16"),
+    # d_k < 64 with four 16-token sub-blocks: the gain's lanes past d_k are idle
+    (1, 3, 64, 32, 128, 64, "diagonal", "f32"),
+    (1, 3, 130, 32, 64, 64, "diagonal", "bf16"),
 ]
 
 
