@@ -161,6 +161,48 @@ kdn_status kdn_decode_step(const kdn_desc *d, const void *q, const void *k, cons
                            const void *a, const void *qnoise, const void *r, float *S,
                            float *lambda, void *o, void *stream);
 
+/* Bytes of workspace kdn_backward needs (0 if the descriptor is invalid or
+ * the backward does not support it).  Host-only. */
+size_t kdn_backward_workspace_bytes(const kdn_desc *d);
+
+/* Backward pass of kdn_forward (diagonal variant): the gradient of
+ *     L = <dO, o> + <dS_T, S_T> + <dlambda_T, lambda_T>
+ * with respect to every input, as training the layer needs ("Kalman Delta
+ * Networks", English abstract: the variants are pretrained inside language
+ * models of 750M and 1.3B parameters).  The forward's intermediates are
+ * recomputed from the inputs (nothing is kept between the two calls).
+ *   Inputs as kdn_forward (same descriptor, same q, k, v, a, qnoise, r,
+ *   lambda0, S0); dO [B,H,T,d_v] in qkv_dtype; dS_T [B,H,d_v,d_k] and
+ *   dlambda_T [B,H,d_k] float32 or NULL (zero).
+ *   Outputs, float32 whatever the input dtypes: dq, dk [B,H,T,d_k];
+ *   dv [B,H,T,d_v]; da, dqnoise, dr [B,H,T]; dlambda0 [B,H,d_k] and
+ *   dS0 [B,H,d_v,d_k] (either may be NULL to skip it; they are the gradient
+ *   at the given lambda0 / S0, or at ones / zeros when those are NULL).
+ *   No output may alias an input.  ws: at least
+ *   kdn_backward_workspace_bytes(d) bytes, 16-byte aligned, contents ignored.
+ * Returns KDN_ERR_UNSUPPORTED for the isotropic variant and for shapes the
+ * chunk kernels do not take (kdn_backward_workspace_bytes returns 0). */
+kdn_status kdn_backward(const kdn_desc *d, const void *q, const void *k, const void *v,
+                        const void *a, const void *qnoise, const void *r,
+                        const float *lambda0, const float *S0, const void *dO,
+                        const float *dS_T, const float *dlambda_T, float *dq, float *dk,
+                        float *dv, float *da, float *dqnoise, float *dr, float *dlambda0,
+                        float *dS0, void *ws, size_t ws_bytes, void *stream);
+
+/* kdn_backward with timing: events is NULL or an array of 14 hipEvent_t
+ * (entries may be NULL); events 2i and 2i + 1 are recorded by the dispatches
+ * that start and end stage i: 0 scan reduce, 1 scan carry, 2 chunk prep,
+ * 3 chunk state (the forward recompute), 4 reverse state pass, 5 per-chunk
+ * gradients, 6 gain and precision recursion (three kernels).  Otherwise
+ * identical to kdn_backward. */
+kdn_status kdn_backward_events(const kdn_desc *d, const void *q, const void *k, const void *v,
+                               const void *a, const void *qnoise, const void *r,
+                               const float *lambda0, const float *S0, const void *dO,
+                               const float *dS_T, const float *dlambda_T, float *dq,
+                               float *dk, float *dv, float *da, float *dqnoise, float *dr,
+                               float *dlambda0, float *dS0, void *ws, size_t ws_bytes,
+                               void *stream, void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

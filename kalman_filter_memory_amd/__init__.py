@@ -13,6 +13,9 @@ Functions (same names as the C entry points):
   mobius_scan(k, a, qnoise, r, lambda0=None, variant=..., chunk=64) -> dict
   gain(k, r, lambda_minus, variant=..., gain_dtype=None) -> w
   chunk_delta(q, k, v, a, w, S0=None, chunk=64) -> (o, S_T)
+  backward(q, k, v, a, qnoise, r, dO, lambda0=None, S0=None, dS_T=None, dlambda_T=None,
+           chunk=64) -> dict of float32 gradients (dq, dk, dv, da, dqnoise, dr,
+           dlambda0, dS0)
 """
 from __future__ import annotations
 
@@ -32,6 +35,7 @@ EXPORTS = (
     "kdn_forward_events",
     "kdn_mobius_scan_workspace_bytes", "kdn_mobius_scan", "kdn_gain",
     "kdn_chunk_delta_workspace_bytes", "kdn_chunk_delta", "kdn_decode_step",
+    "kdn_backward_workspace_bytes", "kdn_backward", "kdn_backward_events",
 )
 
 
@@ -77,6 +81,8 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_chunk_delta.argtypes = [D] + [P] * 8 + [P, S, P]
     lib.kdn_chunk_delta.restype = I
     lib.kdn_decode_step.argtypes = [D] + [P] * 9 + [P]
+    lib.kdn_backward.argtypes = [D] + [P] * 19 + [P, S, P]
+    lib.kdn_backward_events.argtypes = [D] + [P] * 19 + [P, S, P, ctypes.POINTER(P)]
     lib.kdn_decode_step.restype = I
     _lib = lib
     return lib
@@ -209,6 +215,57 @@ def forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", ch
         arr = (ctypes.c_void_p * 8)(*[None if e is None else e.cuda_event for e in events])
         _check(lib.kdn_forward_events(*args, arr), "kdn_forward_events")
     return o, S_T, lam_T
+
+
+def backward_workspace_bytes(desc: KdnDesc) -> int:
+    return load_library().kdn_backward_workspace_bytes(ctypes.byref(desc))
+
+
+def backward(q, k, v, a, qnoise, r, dO, lambda0=None, S0=None, dS_T=None, dlambda_T=None,
+             chunk=64, workspace: torch.Tensor | None = None, out=None, events=None) -> dict:
+    """Gradients of <dO, o> + <dS_T, S_T> + <dlambda_T, lambda_T> (diagonal
+    variant) with respect to q, k, v, a, qnoise, r, lambda0 and S0, as float32
+    tensors in a dict (keys dq, dk, dv, da, dqnoise, dr, dlambda0, dS0).
+
+    out: optional dict of preallocated outputs with those keys; events:
+    optional list of 14 torch.cuda.Event (already recorded once), start and
+    stop of the seven stages."""
+    lib = load_library()
+    d = _forward_desc(q, k, v, a, qnoise, r, "diagonal", chunk)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    _gpu(dO, "dO")
+    if dO.dtype != q.dtype or tuple(dO.shape) != (B, H, T, dv):
+        raise ValueError("dO must be [B,H,T,d_v] in the dtype of q, k, v")
+    for name, x, shape in (("lambda0", lambda0, (B, H, dk)), ("S0", S0, (B, H, dv, dk)),
+                           ("dS_T", dS_T, (B, H, dv, dk)), ("dlambda_T", dlambda_T, (B, H, dk))):
+        if x is not None:
+            _gpu(x, name)
+            if x.dtype != torch.float32 or tuple(x.shape) != shape:
+                raise ValueError(f"{name} must be float32 {shape}")
+    dev = k.device
+    shapes = {"dq": (B, H, T, dk), "dk": (B, H, T, dk), "dv": (B, H, T, dv),
+              "da": (B, H, T), "dqnoise": (B, H, T), "dr": (B, H, T),
+              "dlambda0": (B, H, dk), "dS0": (B, H, dv, dk)}
+    g = out if out is not None else {
+        n: torch.empty(sh, dtype=torch.float32, device=dev) for n, sh in shapes.items()}
+    need = lib.kdn_backward_workspace_bytes(ctypes.byref(d))
+    if need == 0:
+        _check(lib.kdn_validate(ctypes.byref(d)), "kdn_backward")
+        raise KdnError("kdn_backward: shape not supported by the backward kernels")
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    args = (ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(qnoise), _ptr(r),
+            _ptr(lambda0), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(dlambda_T),
+            *(_ptr(g[n]) for n in ("dq", "dk", "dv", "da", "dqnoise", "dr", "dlambda0", "dS0")),
+            _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    if events is None:
+        _check(lib.kdn_backward(*args), "kdn_backward")
+    else:
+        if len(events) != 14:
+            raise ValueError("events: 14 entries (start and stop of seven stages)")
+        arr = (ctypes.c_void_p * 14)(*[None if e is None else e.cuda_event for e in events])
+        _check(lib.kdn_backward_events(*args, arr), "kdn_backward_events")
+    return g
 
 
 def mobius_scan(k, a, qnoise, r, lambda0=None, variant="diagonal", chunk=64,

@@ -92,6 +92,32 @@ ForwardWs forward_ws(const kdn_desc* d) {
     return w;
 }
 
+// backward workspace: the forward's, then [1/D | chunk-start states |
+// chunk-end adjoints | dW | s | d(ln a) | chunk maps (float2) | G at chunk ends]
+struct BackwardWs {
+    ForwardWs f;
+    size_t dinv, Sc, dSe, dW, sdot, dlna, ab, Gout, total;
+};
+
+BackwardWs backward_ws(const kdn_desc* d) {
+    const kdn::Shape s = make_shape(d);
+    BackwardWs b;
+    b.f = forward_ws(d);
+    const size_t n = (size_t)s.BH * s.T;
+    const size_t states = (size_t)s.BH * s.nc * s.dv * s.dk * esize(d->qkv_dtype);
+    const size_t per_dim = (size_t)s.BH * s.nc * s.dk;
+    b.dinv = b.f.total;
+    b.Sc = b.dinv + round_up(n * 4);
+    b.dSe = b.Sc + round_up(states);
+    b.dW = b.dSe + round_up(states);
+    b.sdot = b.dW + round_up(n * s.dk * 4);
+    b.dlna = b.sdot + round_up(n * 4);
+    b.ab = b.dlna + round_up(n * 4);
+    b.Gout = b.ab + round_up(per_dim * 8);
+    b.total = b.Gout + round_up(per_dim * 4);
+    return b;
+}
+
 kdn_status hip_status(hipError_t e) { return e == hipSuccess ? KDN_OK : KDN_ERR_HIP; }
 
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
@@ -174,6 +200,97 @@ kdn_status kdn_forward_events(const kdn_desc* d, const void* q, const void* k, c
     if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs);
     kdn::launch_timing() = kdn::LaunchTiming{};
     return hip_status(e);
+}
+
+size_t kdn_backward_workspace_bytes(const kdn_desc* d) {
+    if (check_chunked(d) != KDN_OK || d->variant != KDN_DIAGONAL) return 0;
+    if (!kdn::backward_supported(make_shape(d))) return 0;
+    return backward_ws(d).total;
+}
+
+kdn_status kdn_backward_events(const kdn_desc* d, const void* q, const void* k, const void* v,
+                               const void* a, const void* qnoise, const void* r,
+                               const float* lambda0, const float* S0, const void* dO,
+                               const float* dS_T, const float* dlambda_T, float* dq, float* dk,
+                               float* dv, float* da, float* dqnoise, float* dr, float* dlambda0,
+                               float* dS0, void* ws, size_t ws_bytes, void* stream,
+                               void* const* events) {
+    kdn_status st = check_chunked(d);
+    if (st != KDN_OK) return st;
+    if (d->variant != KDN_DIAGONAL) return KDN_ERR_UNSUPPORTED;
+    const kdn::Shape s = make_shape(d);
+    if (!kdn::backward_supported(s)) return KDN_ERR_UNSUPPORTED;
+    const BackwardWs w = backward_ws(d);
+    if (s.BH == 0) return KDN_OK;
+    if (s.T > 0 && (!q || !k || !v || !a || !qnoise || !r || !dO || !dq || !dk || !dv || !da ||
+                    !dqnoise || !dr))
+        return KDN_ERR_NULL;
+    if (!ws) return KDN_ERR_NULL;
+    if (ws_bytes < w.total) return KDN_ERR_WORKSPACE;
+    for (const void* p : {q, k, v, dO, (const void*)S0, (const void*)dS_T, (const void*)dq,
+                          (const void*)dk, (const void*)dv, (const void*)dS0, (const void*)ws})
+        if (p && !aligned16(p)) return KDN_ERR_ALIGN;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    float* agg = reinterpret_cast<float*>(at(ws, w.f.agg));
+    float* lc = reinterpret_cast<float*>(at(ws, w.f.lam_chunk));
+    void* wk = at(ws, w.f.w);
+    void* tm = at(ws, w.f.tm);
+    float* g = reinterpret_cast<float*>(at(ws, w.f.g));
+    float* dinv = reinterpret_cast<float*>(at(ws, w.dinv));
+    kdn::BwdArgs b;
+    b.q = q; b.k = k; b.v = v; b.a = a; b.nu = qnoise; b.r = r;
+    b.dO = dO; b.dS_T = dS_T; b.dlambda_T = dlambda_T;
+    b.w = wk; b.Tm = tm; b.g = g; b.lam_chunk = lc; b.dinv = dinv;
+    b.Sc = at(ws, w.Sc);
+    b.dSe = at(ws, w.dSe);
+    b.dW = reinterpret_cast<float*>(at(ws, w.dW));
+    b.sdot = reinterpret_cast<float*>(at(ws, w.sdot));
+    b.dlna = reinterpret_cast<float*>(at(ws, w.dlna));
+    b.ab = reinterpret_cast<float*>(at(ws, w.ab));
+    b.Gout = reinterpret_cast<float*>(at(ws, w.Gout));
+    b.dq = dq; b.dk = dk; b.dv = dv; b.da = da; b.dnu = dqnoise; b.dr = dr;
+    b.dlambda0 = dlambda0; b.dS0 = dS0;
+    auto timed = [&](int i) {
+        kdn::LaunchTiming t;
+        if (events) {
+            t.start = static_cast<hipEvent_t>(events[2 * i]);
+            t.stop = static_cast<hipEvent_t>(events[2 * i + 1]);
+        }
+        kdn::launch_timing() = t;
+    };
+    // forward recompute, keeping 1/D of every token and the chunk-start states;
+    // its read-out goes to dv, which the reverse pass overwrites
+    timed(0);
+    hipError_t e = kdn::launch_scan_reduce(s, k, a, qnoise, r, agg, hs);
+    timed(1);
+    if (e == hipSuccess) e = kdn::launch_scan_carry(s, agg, lambda0, lc, nullptr, hs);
+    kdn::Shape sw = s;
+    sw.gain_bf16 = s.qkv_bf16;
+    timed(2);
+    if (e == hipSuccess)
+        e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, g, hs, dinv);
+    timed(3);
+    if (e == hipSuccess)
+        e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, dv, nullptr, hs, at(ws, w.Sc));
+    timed(4);
+    if (e == hipSuccess) e = kdn::launch_bwd_state(s, b, hs);
+    timed(5);
+    if (e == hipSuccess) e = kdn::launch_bwd_grad(s, b, hs);
+    timed(6);
+    if (e == hipSuccess) e = kdn::launch_bwd_gain(s, b, hs);
+    kdn::launch_timing() = kdn::LaunchTiming{};
+    return hip_status(e);
+}
+
+kdn_status kdn_backward(const kdn_desc* d, const void* q, const void* k, const void* v,
+                        const void* a, const void* qnoise, const void* r, const float* lambda0,
+                        const float* S0, const void* dO, const float* dS_T,
+                        const float* dlambda_T, float* dq, float* dk, float* dv, float* da,
+                        float* dqnoise, float* dr, float* dlambda0, float* dS0, void* ws,
+                        size_t ws_bytes, void* stream) {
+    return kdn_backward_events(d, q, k, v, a, qnoise, r, lambda0, S0, dO, dS_T, dlambda_T, dq,
+                               dk, dv, da, dqnoise, dr, dlambda0, dS0, ws, ws_bytes, stream,
+                               nullptr);
 }
 
 kdn_status kdn_forward(const kdn_desc* d, const void* q, const void* k, const void* v,

@@ -1,0 +1,950 @@
+// kdn_bwd.hip -- backward pass of the chunkwise KDN layer (diagonal variant).
+//
+// Gradients of L = <dO, o> + <dS_T, S_T> + <dlambda_T, lambda_T> with respect
+// to q, k, v, a, nu, r, lambda0 and S0: what training the layer needs ("Kalman
+// Delta Networks", English abstract: the variants are pretrained inside
+// language models).  Reverse-mode differentiation of the chunkwise forward of
+// kdn_chunk.hip (ai-feeds.com summary, section 方法 step 3), in its notation:
+// within a chunk with start state S, gamma_t = 2^(g_t), Gamma_ts = 2^(g_t - g_s),
+// D_s = gamma_C / gamma_s,
+//   A = strict_tril(K W^T * Gamma), T = (I + A)^{-1}, R = V - diag(gamma) K S^T,
+//   U = T R, M = tril(Q W^T * Gamma), O = diag(gamma) Q S^T + M U,
+//   S' = gamma_C S + U^T diag(D) W.
+// With dS' the adjoint of the chunk-end state:
+//   dU = diag(D) W dS'^T + M^T dO,      dR = T^T dU   (= dV)
+//   dS = gamma_C dS' + dO^T diag(gamma) Q - dR^T diag(gamma) K
+//   dM = tril(dO U^T),                   dA = -strict_tril(dR U^T)
+//   dQ = diag(gamma) dO S + (dM * Gamma) W
+//   dK = -diag(gamma) dR S + (dA * Gamma) W          (+ the gain's part)
+//   dW = diag(D) U dS' + (dM * Gamma)^T Q + (dA * Gamma)^T K
+// The decay enters through gamma, Gamma and D; its derivative is collected per
+// token with respect to g_t (ln 2 cancels against the base-2 logarithm of a)
+// and summed over the later tokens of the chunk to give d(ln a_t).
+// The gain and the precision recursion ("Kalman Delta Networks", English
+// abstract: Diagonal KDN, a Moebius-map uncertainty recurrence) are
+// differentiated in variance form, per key dimension i:
+//   P^- = a^2 P + nu,  P = P^- / (1 + b P^-),  b = k_i^2 / r,
+//   w_i = P^-_i k_i / D,  D = r + sum_j k_j^2 P^-_j.
+// With G the adjoint of P after a token and s = sum_i dW_i w_i:
+//   H  = (k_i / D)(dW_i - k_i s) + G (P / P^-)^2      (adjoint of P^-)
+//   dk_i += (P^-_i / D)(dW_i - 2 k_i s) - G P^2 2 k_i / r
+//   dnu += H,  da += 2 a P_prev H,  dr += -s / D + G P^2 b / r,  G <- a^2 H.
+// G's recursion is affine, so it runs chunk-parallel: each chunk's map
+// G_in = alpha G_out + beta, a carry over the chunks, then the outputs.
+//
+// Kernels, after a forward recompute that also keeps the state at every chunk
+// start and 1/D of every token:
+//   bstate_kernel  one workgroup per (head, d_v tile), chunks in reverse: dU,
+//                  dR, the state adjoint (kept at every chunk end), dS0
+//   bgrad_kernel   one workgroup per chunk, all chunks in parallel, over d_v
+//                  slices: dQ, the memory part of dK, dW, s and d(ln a)
+//   bgain_kernel   one workgroup per chunk: the precision recursion walked
+//                  forward, then backward (alpha, beta; or, given G_out, the
+//                  outputs); bgain_carry between the two
+// All products on MFMA with fp32 accumulation; operands in the input dtype.
+#include "kdn_device.h"
+#include "kdn_kernels.h"
+#include "kdn_tiles.h"
+
+namespace kdn {
+namespace {
+
+constexpr int kLdsCap = 160 * 1024;
+constexpr int kBThreads = 512;
+
+// lower-triangular tile pair (tt >= ss) of triangle index j (row by row)
+__device__ __forceinline__ void tri_pair(int j, int& tt, int& ss) {
+    tt = 0;
+    while ((tt + 1) * (tt + 2) / 2 <= j) ++tt;
+    ss = j - tt * (tt + 1) / 2;
+}
+
+// ROWS x COLS of E from global rows of stride gld into LDS rows of stride sld
+// with 16-byte vectors; rows >= n are zero (their loads repeat row n - 1)
+template <typename E, int ROWS, int COLS>
+__device__ __forceinline__ void stage_tile(E* dst, int sld, const E* src, size_t gld, int n,
+                                           int tid) {
+    constexpr int V = Vec16<E>::N, VPR = COLS / V, NV = ROWS * VPR;
+    constexpr int IT = (NV + kBThreads - 1) / kBThreads;
+    u32x4 val[IT];
+#pragma unroll
+    for (int x = 0; x < IT; ++x) {
+        const int e = tid + kBThreads * x;
+        if (NV % kBThreads == 0 || e < NV) {
+            const int t = e / VPR, c0 = (e % VPR) * V;
+            val[x] = *reinterpret_cast<const u32x4*>(src + min(t, n - 1) * gld + c0);
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < IT; ++x) {
+        const int e = tid + kBThreads * x;
+        if (NV % kBThreads == 0 || e < NV) {
+            const int t = e / VPR, c0 = (e % VPR) * V;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(dst + t * sld + c0) = t < n ? val[x] : z;
+        }
+    }
+}
+
+// the same from fp32 global rows, converted to E
+template <typename E, int ROWS, int COLS>
+__device__ __forceinline__ void stage_tile_f32(E* dst, int sld, const float* src, size_t gld,
+                                               int n, int tid) {
+    constexpr int VPR = COLS / 4, NV = ROWS * VPR;
+    constexpr int IT = (NV + kBThreads - 1) / kBThreads;
+    float4 val[IT];
+#pragma unroll
+    for (int x = 0; x < IT; ++x) {
+        const int e = tid + kBThreads * x;
+        if (NV % kBThreads == 0 || e < NV) {
+            const int t = e / VPR, c0 = (e % VPR) * 4;
+            val[x] = *reinterpret_cast<const float4*>(src + min(t, n - 1) * gld + c0);
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < IT; ++x) {
+        const int e = tid + kBThreads * x;
+        if (NV % kBThreads == 0 || e < NV) {
+            const int t = e / VPR, c0 = (e % VPR) * 4;
+            const float4 v = t < n ? val[x] : make_float4(0.f, 0.f, 0.f, 0.f);
+            store4<E>(dst + t * sld + c0, v.x, v.y, v.z, v.w);
+        }
+    }
+}
+
+// sum over the 16 lanes of each 16-lane group (lanes sharing the rows of an
+// MFMA result tile)
+__device__ __forceinline__ float group16_sum(float x) {
+    x += __shfl_xor(x, 1, kWave);
+    x += __shfl_xor(x, 2, kWave);
+    x += __shfl_xor(x, 4, kWave);
+    x += __shfl_xor(x, 8, kWave);
+    return x;
+}
+
+// ======================================================= reverse state pass
+template <typename E, int DK, int DVT, int C> struct BStateLds {
+    using G = StateCfg<E, DK, DVT, C>;
+    E K[C * G::LDK];
+    E Q[C * G::LDK];
+    E W[C * G::LDK];
+    E dO[C * G::LDV];     // [t][j]; rows past the end are zero
+    E Tt[C * G::LDC];     // T [t][s]
+    E M[C * G::LDC];      // tril(Q W^T) * Gamma [t][s]
+    E dUt[DVT * G::LDC];  // dU^T [j][s]
+    E dOg[DVT * G::LDC];  // gamma_t dO[t][j] as [j][t]
+    E dRg[DVT * G::LDC];  // -gamma_s dR[s][j] as [j][s]
+    E S[DVT * G::LDK];    // the state adjoint as an operand [j][i]
+    float g[C], gam[C], del[C];
+};
+
+template <typename E, int DK, int DVT, int C>
+constexpr bool bstate_fits() {
+    return sizeof(BStateLds<E, DK, DVT, C>) <= kLdsCap;
+}
+
+// One workgroup of 8 waves per (head, d_v tile), chunks from last to first.
+// The state adjoint dS (S^T blocks, as the forward keeps S) lives in MFMA
+// accumulators; per chunk:
+//   1  dU = diag(D) W dS^T  (per wave: one s-tile x BVU j-tiles);  M tiles;
+//      gamma-scaled transposed dO
+//   2  dU += M^T dO, stored transposed
+//   3  dR = T^T dU -> dv (fp32) and -gamma dR (transposed) for the update
+//   4  dS <- gamma_C dS + Q^T (gamma dO) - K^T (gamma dR)
+// The next chunk's operands are loaded into registers at the start of a chunk
+// and staged at its end; the adjoint entering each chunk is stored (dSe).
+template <typename E, int DK, int DVT, int C>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void bstate_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ dO,
+    const float* __restrict__ gin, const E* __restrict__ w, const E* __restrict__ Tm,
+    const float* __restrict__ dS_T, float* __restrict__ dv_out, E* __restrict__ dSe,
+    float* __restrict__ dS0, int BH, int T, int DV, int NC) {
+    using G = StateCfg<E, DK, DVT, C>;
+    constexpr int LDK = G::LDK, LDC = G::LDC, LDV = G::LDV, NT = G::NT, NV = G::NV;
+    constexpr int BI = G::BI, BV = G::BV, NVB = G::NVB, VEC = G::VEC;
+    constexpr int BVU = NV >= 2 ? 2 : 1, NUB = NV / BVU, NUJ = NT * NUB, UPW = (NUJ + 7) / 8;
+    constexpr int NMT = NT * (NT + 1) / 2, MPW = (NMT + 7) / 8;
+    __shared__ __align__(16) BStateLds<E, DK, DVT, C> L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    // the d_v tiles of one head share an XCD (workgroups go to XCDs round-robin)
+    const int ntile = DV / DVT, L_ = blockIdx.x, per = 8 * ntile;
+    const int head = (L_ / per) * 8 + (L_ % 8);
+    if (head >= BH) return;
+    const size_t bh = head;
+    const int j0 = ((L_ % per) / 8) * DVT;
+
+    StateAcc<E, DK, DVT, C> acc;
+#pragma unroll
+    for (int x = 0; x < G::SPW; ++x) {
+        const int job = wave + G::NW * x;
+        const int ib = (job / NVB) * BI, jb = (job % NVB) * BV;
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+            for (int bv = 0; bv < BV; ++bv) {
+                acc[x][bi][bv] = floatx4{0.f, 0.f, 0.f, 0.f};
+                if (job < G::NSJ && dS_T) {
+                    const int i = 16 * (ib + bi) + 4 * (lane >> 4);
+                    const int j = 16 * (jb + bv) + (lane & 15);
+                    const float4 s4 =
+                        *reinterpret_cast<const float4*>(dS_T + (bh * DV + j0 + j) * DK + i);
+                    acc[x][bi][bv] = floatx4{s4.x, s4.y, s4.z, s4.w};
+                }
+            }
+    }
+
+    u32x4 pk[G::PK], pq[G::PK], pw[G::PK], pv[G::PV], pt[G::PT];
+    float pg = 0.f;
+    // stage chunk cc from the registers; dO rows past the end are zeroed first
+    auto stage = [&](int cc) {
+        const int n = min(C, T - cc * C);
+#pragma unroll
+        for (int x = 0; x < G::PV; ++x) {
+            const int e = tid + G::THREADS * x;
+            if ((G::NVV % G::THREADS == 0 || e < G::NVV) && e / (DVT / VEC) >= n)
+                pv[x] = u32x4{0u, 0u, 0u, 0u};
+        }
+        state_stage<E, DK, DVT, C, kStageAll>(L.K, L.Q, L.W, L.dO, L.Tt, L.g, L.gam, L.del, n,
+                                              tid, lane, wave, pk, pq, pw, pv, pt, pg);
+    };
+    if (NC > 0) {
+        state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, dO, w, Tm, gin, bh, j0, T, DV, NC, NC - 1,
+                                                tid, lane, pk, pq, pw, pv, pt, pg);
+        stage(NC - 1);
+    }
+    state_write<E, DK, DVT, C>(acc, L.S, wave, lane);
+    sync_lds();
+
+    for (int c = NC - 1; c >= 0; --c) {
+        const int n = min(C, T - c * C);
+        const size_t row0 = bh * T + (size_t)c * C;
+        state_save<E, DK, DVT, C>(acc, dSe + ((bh * NC + c) * DV + j0) * DK, wave, lane);
+        if (c > 0)
+            state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, dO, w, Tm, gin, bh, j0, T, DV, NC,
+                                                    c - 1, tid, lane, pk, pq, pw, pv, pt, pg);
+        // 1: dU = diag(D) W dS^T; M; gamma dO transposed
+        floatx4 au[UPW][1][BVU];
+#pragma unroll
+        for (int x = 0; x < UPW; ++x) {
+            const int job = wave + 8 * x;
+#pragma unroll
+            for (int bv = 0; bv < BVU; ++bv) au[x][0][bv] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (job < NUJ) {
+                const int st = job / NUB, jb = (job % NUB) * BVU;
+                mma_block<E, 1, BVU>(au[x], L.W, LDK, 16 * st, L.S, LDK, 16 * jb, 0, DK, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float d = L.del[16 * st + 4 * (lane >> 4) + e];
+#pragma unroll
+                    for (int bv = 0; bv < BVU; ++bv) au[x][0][bv][e] *= d;
+                }
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < MPW; ++x) {
+            const int job = wave + 8 * x;
+            if (job < NMT) {
+                int tt, ss;
+                tri_pair(job, tt, ss);
+                const floatx4 m = mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, L.Q, LDK, 16 * tt, L.W,
+                                              LDK, 16 * ss, 0, DK, lane);
+                const int s = 16 * ss + (lane & 15);
+                const float gs = L.g[s];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * tt + 4 * (lane >> 4) + e;
+                    const float val = s <= t ? m[e] * exp2_hw(L.g[t] - gs) : 0.f;
+                    L.M[t * LDC + s] = from_f<E>(val);
+                }
+            }
+        }
+        for (int e = tid; e < C * DVT; e += kBThreads) {
+            const int t = e / DVT, j = e % DVT;
+            L.dOg[j * LDC + t] = from_f<E>(L.gam[t] * to_f<E>(L.dO[t * LDV + j]));
+        }
+        sync_lds();
+        // 2: dU += M^T dO  (M[t][s] = 0 for t < s)
+#pragma unroll
+        for (int x = 0; x < UPW; ++x) {
+            const int job = wave + 8 * x;
+            if (job < NUJ) {
+                const int st = job / NUB, jb = (job % NUB) * BVU;
+                mma_block<E, 1, BVU, true, true>(au[x], L.M, LDC, 16 * st, L.dO, LDV, 16 * jb,
+                                                 16 * st, C, lane);
+#pragma unroll
+                for (int bv = 0; bv < BVU; ++bv) {
+                    const int j = 16 * (jb + bv) + (lane & 15);
+                    const floatx4 u = au[x][0][bv];
+                    store4<E>(L.dUt + j * LDC + 16 * st + 4 * (lane >> 4), u[0], u[1], u[2], u[3]);
+                }
+            }
+        }
+        sync_lds();
+        // 3: dR = T^T dU  (T[t][s] = 0 for t < s)
+#pragma unroll
+        for (int x = 0; x < UPW; ++x) {
+            const int job = wave + 8 * x;
+            if (job < NUJ) {
+                const int st = job / NUB, jb = (job % NUB) * BVU;
+                floatx4 ar[1][BVU];
+#pragma unroll
+                for (int bv = 0; bv < BVU; ++bv) ar[0][bv] = floatx4{0.f, 0.f, 0.f, 0.f};
+                mma_block<E, 1, BVU, true>(ar, L.Tt, LDC, 16 * st, L.dUt, LDC, 16 * jb, 16 * st,
+                                           C, lane);
+                const int s0 = 16 * st + 4 * (lane >> 4);
+#pragma unroll
+                for (int bv = 0; bv < BVU; ++bv) {
+                    const int j = 16 * (jb + bv) + (lane & 15);
+                    const floatx4 r4 = ar[0][bv];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (s0 + e < n) dv_out[(row0 + s0 + e) * DV + j0 + j] = r4[e];
+                    store4<E>(L.dRg + j * LDC + s0, -L.gam[s0] * r4[0], -L.gam[s0 + 1] * r4[1],
+                              -L.gam[s0 + 2] * r4[2], -L.gam[s0 + 3] * r4[3]);
+                }
+            }
+        }
+        sync_lds();
+        // 4: dS <- gamma_C dS + Q^T (gamma dO) - K^T (gamma dR)
+        const float gC = L.gam[C - 1];
+#pragma unroll
+        for (int x = 0; x < G::SPW; ++x) {
+            const int job = wave + G::NW * x;
+            if (job < G::NSJ) {
+                const int ib = (job / NVB) * BI, jb = (job % NVB) * BV;
+#pragma unroll
+                for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                    for (int bv = 0; bv < BV; ++bv) acc[x][bi][bv] = acc[x][bi][bv] * gC;
+                mma_block<E, BI, BV, true>(acc[x], L.Q, LDK, 16 * ib, L.dOg, LDC, 16 * jb, 0, C,
+                                           lane);
+                mma_block<E, BI, BV, true>(acc[x], L.K, LDK, 16 * ib, L.dRg, LDC, 16 * jb, 0, C,
+                                           lane);
+            }
+        }
+        sync_lds();
+        if (c > 0) stage(c - 1);
+        state_write<E, DK, DVT, C>(acc, L.S, wave, lane);
+        sync_lds();
+    }
+    if (dS0) {
+#pragma unroll
+        for (int x = 0; x < G::SPW; ++x) {
+            const int job = wave + G::NW * x;
+            if (job < G::NSJ) {
+                const int ib = (job / NVB) * BI, jb = (job % NVB) * BV;
+#pragma unroll
+                for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                    for (int bv = 0; bv < BV; ++bv) {
+                        const int i = 16 * (ib + bi) + 4 * (lane >> 4);
+                        const int j = 16 * (jb + bv) + (lane & 15);
+                        const floatx4 sv = acc[x][bi][bv];
+                        *reinterpret_cast<float4*>(dS0 + (bh * DV + j0 + j) * DK + i) =
+                            make_float4(sv[0], sv[1], sv[2], sv[3]);
+                    }
+            }
+        }
+    }
+}
+
+// ===================================================== per-chunk gradients
+template <typename E, int DK, int C, int JT> struct BGradLds {
+    static constexpr int PAD = 32 / (int)sizeof(E);
+    static constexpr int LDK = DK + PAD, LDC = C + PAD, LDJ = JT + PAD;
+    E K[C * LDK];
+    E Q[C * LDK];
+    E W[C * LDK];
+    E Tt[C * LDC];    // T; after the slices dM * Gamma  [t][s]
+    E dAG[C * LDC];   // dA * Gamma [t][s]
+    E Sj[JT * LDK];   // chunk-start state rows of the slice [j][i]
+    E dSj[JT * LDK];  // chunk-end adjoint rows of the slice [j][i]
+    E R[C * LDJ];     // V, then R = V - diag(gamma) K S^T  [t][j]
+    E U[C * LDJ];     // [t][j]
+    E dO[C * LDJ];    // [t][j]
+    E dR[C * LDJ];    // [t][j]
+    float g[C], gam[C], del[C], dlg[C], sdot[C], misc[2];
+};
+
+template <typename E, int DK, int C, int JT>
+constexpr bool bgrad_fits() {
+    return sizeof(BGradLds<E, DK, C, JT>) <= kLdsCap;
+}
+
+// One workgroup of 8 waves per chunk.  Over d_v slices of JT: R, U (recomputed
+// from the chunk-start state), and the accumulation of dM, dA (lower-triangle
+// tiles) and of gamma^-1 dQ1 = dO S, dR S and D^-1 dW1 = U dS' (per wave one
+// t-tile x BKI i-tiles).  Then the decay derivative of every token, dM * Gamma
+// and dA * Gamma, and the finished dQ, dK (memory part) and dW.
+template <typename E, int DK, int C, int JT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void bgrad_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const E* __restrict__ dO, const float* __restrict__ dR, const E* __restrict__ w,
+    const E* __restrict__ Tm, const float* __restrict__ gin, const E* __restrict__ Sc,
+    const E* __restrict__ dSe, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dW, float* __restrict__ sdot_out, float* __restrict__ dlna, int T, int DV,
+    int NC) {
+    using LL = BGradLds<E, DK, C, JT>;
+    constexpr int LDK = LL::LDK, LDC = LL::LDC, LDJ = LL::LDJ;
+    constexpr int NT = C / 16, NK = DK / 16, NJ = JT / 16;
+    constexpr int BKI = NK >= 4 ? 4 : NK, NKB = NK / BKI, NQJ = NT * NKB, QPW = (NQJ + 7) / 8;
+    constexpr int NMT = NT * (NT + 1) / 2, MPW = (NMT + 7) / 8;
+    constexpr int BJX = NJ >= 2 ? 2 : 1, NXB = NJ / BJX, NXJ = NT * NXB, XPW = (NXJ + 7) / 8;
+    __shared__ __align__(16) LL L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int c = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int n = min(C, T - c * C);
+    const size_t row0 = bh * T + (size_t)c * C;
+    const size_t cidx = bh * NC + c;
+
+    stage_tile<E, C, DK>(L.K, LDK, k + row0 * DK, DK, n, tid);
+    stage_tile<E, C, DK>(L.Q, LDK, q + row0 * DK, DK, n, tid);
+    stage_tile<E, C, DK>(L.W, LDK, w + row0 * DK, DK, n, tid);
+    stage_tile<E, C, C>(L.Tt, LDC, Tm + cidx * C * C, C, C, tid);
+    if (tid < C) {
+        const float gv = gin[cidx * C + tid], gC = gin[cidx * C + C - 1];
+        L.g[tid] = gv;
+        L.gam[tid] = exp2_hw(gv);
+        L.del[tid] = exp2_hw(gC - gv);
+        L.dlg[tid] = 0.f;
+        L.sdot[tid] = 0.f;
+        if (tid < 2) L.misc[tid] = 0.f;
+    }
+
+    floatx4 aq[QPW][1][BKI], ak[QPW][1][BKI], aw[QPW][1][BKI];
+#pragma unroll
+    for (int x = 0; x < QPW; ++x)
+#pragma unroll
+        for (int b = 0; b < BKI; ++b) {
+            aq[x][0][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+            ak[x][0][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+            aw[x][0][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+    floatx4 am[MPW], aa[MPW];
+#pragma unroll
+    for (int x = 0; x < MPW; ++x) {
+        am[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+        aa[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    float xc = 0.f;
+
+    for (int j0 = 0; j0 < DV; j0 += JT) {
+        stage_tile<E, JT, DK>(L.Sj, LDK, Sc + (cidx * DV + j0) * DK, DK, JT, tid);
+        stage_tile<E, JT, DK>(L.dSj, LDK, dSe + (cidx * DV + j0) * DK, DK, JT, tid);
+        stage_tile<E, C, JT>(L.R, LDJ, v + row0 * DV + j0, DV, n, tid);
+        stage_tile<E, C, JT>(L.dO, LDJ, dO + row0 * DV + j0, DV, n, tid);
+        stage_tile_f32<E, C, JT>(L.dR, LDJ, dR + row0 * DV + j0, DV, n, tid);
+        sync_lds();
+        // R = V - diag(gamma) K S^T, in place
+#pragma unroll
+        for (int x = 0; x < XPW; ++x) {
+            const int job = wave + 8 * x;
+            if (job < NXJ) {
+                const int tt = job / NXB, jb = (job % NXB) * BJX;
+                floatx4 ax[1][BJX];
+#pragma unroll
+                for (int b = 0; b < BJX; ++b) ax[0][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+                mma_block<E, 1, BJX>(ax, L.K, LDK, 16 * tt, L.Sj, LDK, 16 * jb, 0, DK, lane);
+#pragma unroll
+                for (int b = 0; b < BJX; ++b)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * tt + 4 * (lane >> 4) + e;
+                        E* p = L.R + t * LDJ + 16 * (jb + b) + (lane & 15);
+                        *p = from_f<E>(to_f<E>(*p) - L.gam[t] * ax[0][b][e]);
+                    }
+            }
+        }
+        sync_lds();
+        // U = T R  (T[t][s] = 0 for s > t)
+#pragma unroll
+        for (int x = 0; x < XPW; ++x) {
+            const int job = wave + 8 * x;
+            if (job < NXJ) {
+                const int tt = job / NXB, jb = (job % NXB) * BJX;
+                floatx4 au[1][BJX];
+#pragma unroll
+                for (int b = 0; b < BJX; ++b) au[0][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+                mma_block<E, 1, BJX, false, true>(au, L.Tt, LDC, 16 * tt, L.R, LDJ, 16 * jb, 0,
+                                                  16 * (tt + 1), lane);
+#pragma unroll
+                for (int b = 0; b < BJX; ++b)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * tt + 4 * (lane >> 4) + e;
+                        L.U[t * LDJ + 16 * (jb + b) + (lane & 15)] = from_f<E>(au[0][b][e]);
+                    }
+            }
+        }
+        for (int e = tid; e < JT * DK; e += kBThreads) {
+            const int jr = e / DK, i = e % DK;
+            xc += to_f<E>(L.dSj[jr * LDK + i]) * to_f<E>(L.Sj[jr * LDK + i]);
+        }
+        sync_lds();
+        // dM += dO U^T, dA' += dR U^T (negated later); dO S, dR S, U dS'
+#pragma unroll
+        for (int x = 0; x < MPW; ++x) {
+            const int job = wave + 8 * x;
+            if (job < NMT) {
+                int tt, ss;
+                tri_pair(job, tt, ss);
+                am[x] = mma_tile<E>(am[x], L.dO, LDJ, 16 * tt, L.U, LDJ, 16 * ss, 0, JT, lane);
+                aa[x] = mma_tile<E>(aa[x], L.dR, LDJ, 16 * tt, L.U, LDJ, 16 * ss, 0, JT, lane);
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < QPW; ++x) {
+            const int job = wave + 8 * x;
+            if (job < NQJ) {
+                const int tt = job / NKB, ib = (job % NKB) * BKI;
+                mma_block<E, 1, BKI, false, true>(aq[x], L.dO, LDJ, 16 * tt, L.Sj, LDK, 16 * ib,
+                                                  0, JT, lane);
+                mma_block<E, 1, BKI, false, true>(ak[x], L.dR, LDJ, 16 * tt, L.Sj, LDK, 16 * ib,
+                                                  0, JT, lane);
+                mma_block<E, 1, BKI, false, true>(aw[x], L.U, LDJ, 16 * tt, L.dSj, LDK, 16 * ib,
+                                                  0, JT, lane);
+            }
+        }
+        sync_lds();
+    }
+
+    // xc: <dS', S> over the whole chunk state
+    {
+        float xs = wave_sum(xc);
+        if (lane == 0) atomicAdd(&L.misc[1], xs);
+    }
+    // dQ1 = diag(gamma) dO S, dK1 = -diag(gamma) dR S, dW1 = diag(D) U dS';
+    // decay derivative: + q_t.dQ1_t + k_t.dK1_t - w_t.dW1_t, and sum_s w_s.dW1_s
+    // for the last token
+#pragma unroll
+    for (int x = 0; x < QPW; ++x) {
+        const int job = wave + 8 * x;
+        if (job < NQJ) {
+            const int tt = job / NKB, ib = (job % NKB) * BKI;
+            float wsum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * tt + 4 * (lane >> 4) + e;
+                const float gt = L.gam[t], dt = L.del[t];
+                float row = 0.f, roww = 0.f;
+#pragma unroll
+                for (int b = 0; b < BKI; ++b) {
+                    const int i = 16 * (ib + b) + (lane & 15);
+                    aq[x][0][b][e] *= gt;
+                    ak[x][0][b][e] *= -gt;
+                    aw[x][0][b][e] *= dt;
+                    row += to_f<E>(L.Q[t * LDK + i]) * aq[x][0][b][e] +
+                           to_f<E>(L.K[t * LDK + i]) * ak[x][0][b][e];
+                    roww += to_f<E>(L.W[t * LDK + i]) * aw[x][0][b][e];
+                }
+                row = group16_sum(row - roww);
+                roww = group16_sum(roww);
+                if ((lane & 15) == 0) atomicAdd(&L.dlg[t], row);
+                wsum += roww;
+            }
+            if ((lane & 15) == 0) atomicAdd(&L.misc[0], wsum);
+        }
+    }
+    // M and A tiles; dM * Gamma and dA * Gamma; decay derivative: for each pair
+    // (t, s) of M (and A), z = dM_ts M_ts adds to token t and subtracts from s
+#pragma unroll
+    for (int x = 0; x < MPW; ++x) {
+        const int job = wave + 8 * x;
+        if (job < NMT) {
+            int tt, ss;
+            tri_pair(job, tt, ss);
+            const floatx4 mq = mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, L.Q, LDK, 16 * tt, L.W,
+                                           LDK, 16 * ss, 0, DK, lane);
+            const floatx4 mk = mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, L.K, LDK, 16 * tt, L.W,
+                                           LDK, 16 * ss, 0, DK, lane);
+            const int s = 16 * ss + (lane & 15);
+            const float gs = L.g[s];
+            float col = 0.f, rowz[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * tt + 4 * (lane >> 4) + e;
+                const float gm = s <= t ? exp2_hw(L.g[t] - gs) : 0.f;
+                const float ga = s < t ? gm : 0.f;
+                const float dm = am[x][e], dA = -aa[x][e];
+                const float z = dm * mq[e] * gm + dA * mk[e] * ga;
+                rowz[e] = z;
+                col += z;
+                L.Tt[t * LDC + s] = from_f<E>(dm * gm);
+                L.dAG[t * LDC + s] = from_f<E>(dA * ga);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float zr = group16_sum(rowz[e]);
+                if ((lane & 15) == 0) atomicAdd(&L.dlg[16 * tt + 4 * (lane >> 4) + e], zr);
+            }
+            col += __shfl_xor(col, 16, kWave);
+            col += __shfl_xor(col, 32, kWave);
+            if (lane < 16) atomicAdd(&L.dlg[s], -col);
+        }
+    }
+    sync_lds();
+    // dQ = dQ1 + (dM Gamma) W; dK = dK1 + (dA Gamma) W;
+    // dW = dW1 + (dM Gamma)^T Q + (dA Gamma)^T K; s_t = dW_t . w_t
+#pragma unroll
+    for (int x = 0; x < QPW; ++x) {
+        const int job = wave + 8 * x;
+        if (job < NQJ) {
+            const int tt = job / NKB, ib = (job % NKB) * BKI;
+            mma_block<E, 1, BKI, false, true>(aq[x], L.Tt, LDC, 16 * tt, L.W, LDK, 16 * ib, 0,
+                                              16 * (tt + 1), lane);
+            mma_block<E, 1, BKI, false, true>(ak[x], L.dAG, LDC, 16 * tt, L.W, LDK, 16 * ib, 0,
+                                              16 * (tt + 1), lane);
+            mma_block<E, 1, BKI, true, true>(aw[x], L.Tt, LDC, 16 * tt, L.Q, LDK, 16 * ib,
+                                             16 * tt, C, lane);
+            mma_block<E, 1, BKI, true, true>(aw[x], L.dAG, LDC, 16 * tt, L.K, LDK, 16 * ib,
+                                             16 * tt, C, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * tt + 4 * (lane >> 4) + e;
+                float sd = 0.f;
+#pragma unroll
+                for (int b = 0; b < BKI; ++b) {
+                    const int i = 16 * (ib + b) + (lane & 15);
+                    sd += aw[x][0][b][e] * to_f<E>(L.W[t * LDK + i]);
+                    if (t < n) {
+                        const size_t o = (row0 + t) * DK + i;
+                        dq[o] = aq[x][0][b][e];
+                        dk[o] = ak[x][0][b][e];
+                        dW[o] = aw[x][0][b][e];
+                    }
+                }
+                sd = group16_sum(sd);
+                if ((lane & 15) == 0) atomicAdd(&L.sdot[t], sd);
+            }
+        }
+    }
+    sync_lds();
+    // d(ln a_t) = sum over the chunk's tokens u >= t of the derivative w.r.t. g_u;
+    // the state carried to the next chunk adds gamma_C <dS', S> and
+    // sum_s w_s.dW1_s to the last token
+    if (wave == 0) {
+        float x = lane < n ? L.dlg[lane] : 0.f;
+        if (lane == n - 1) x += L.misc[0] + L.gam[C - 1] * L.misc[1];
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float y = __shfl_down(x, off, kWave);
+            if (lane + off < kWave) x += y;
+        }
+        if (lane < n) {
+            dlna[row0 + lane] = x;
+            sdot_out[row0 + lane] = L.sdot[lane];
+        }
+    }
+}
+
+// ============================================== gain and precision recursion
+// One workgroup per chunk, lane i = key dimension.  The precision is walked
+// forward from the chunk-boundary value (P^- kept in LDS), then backward:
+//   APPLY = false: the chunk's affine map G_in = alpha G_out + beta (float2)
+//   APPLY = true:  with G_out given, dk += the gain's part, and per token
+//                  da = d(ln a)/a + sum_i 2 a P_prev H, dnu = sum_i H,
+//                  dr = -s/D + sum_i G P^2 b / r.
+template <typename E, typename G, int DK, int C, bool APPLY>
+__global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
+    const E* __restrict__ k, const G* __restrict__ a, const G* __restrict__ nu,
+    const G* __restrict__ r, const float* __restrict__ lam_chunk, const float* __restrict__ dinv,
+    const float* __restrict__ sdot, const float* __restrict__ dW, const float* __restrict__ dlna,
+    const float* __restrict__ Gout, float2* __restrict__ ab, float* __restrict__ dk,
+    float* __restrict__ da, float* __restrict__ dnu, float* __restrict__ dr, int T, int NC) {
+    constexpr int NTH = DK < 64 ? 64 : DK;
+    __shared__ float pm_s[C * NTH];  // P^-, then the gain's part of dk
+    __shared__ float k_s[C * NTH];   // the lane's key component of every token
+    __shared__ float red[3][C];      // per token: sum_i H, sum_i 2 a P_prev H, sum_i G P^2 b/r
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int c = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int n = min(C, T - c * C);
+    const size_t row0 = bh * T + (size_t)c * C;
+    const int i = tid;
+    const bool act = i < DK;
+    const int ic = act ? i : 0;
+    if (APPLY && tid < C) {
+        red[0][tid] = 0.f;
+        red[1][tid] = 0.f;
+        red[2][tid] = 0.f;
+    }
+    // token scalars in lane t (broadcast with readlane)
+    const size_t tk = row0 + min(lane, n - 1);
+    const float ta = to_f<G>(a[tk]), tnu = to_f<G>(nu[tk]), tr = to_f<G>(r[tk]);
+    const float tir = 1.f / tr, tdi = dinv[tk], tsd = sdot[tk];
+    // forward: P^- of every token from the chunk-boundary precision
+    float P = 1.f / lam_chunk[(bh * (NC + 1) + c) * DK + ic];
+    for (int g0 = 0; g0 < C; g0 += 16) {
+        float kg[16];
+#pragma unroll
+        for (int h = 0; h < 16; ++h) kg[h] = to_f<E>(k[(row0 + min(g0 + h, n - 1)) * DK + ic]);
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+            const int t = g0 + h;
+            k_s[t * NTH + tid] = kg[h];
+            if (t < n) {
+                const float at = lane_value(ta, t), nut = lane_value(tnu, t);
+                const float irt = lane_value(tir, t);
+                const float pm = fmaf(at * at, P, nut);
+                pm_s[t * NTH + tid] = pm;
+                P = pm * rcp(fmaf(kg[h] * kg[h] * irt, pm, 1.f));
+            }
+        }
+    }
+    // backward over the tokens, 16 at a time
+    float al = 1.f, be = 0.f, Gv = 0.f;
+    if constexpr (APPLY) Gv = act ? Gout[(bh * NC + c) * DK + i] : 0.f;
+    for (int g0 = C - 16; g0 >= 0; g0 -= 16) {
+        float dwg[16], hv[16], ha[16], hr[16];
+#pragma unroll
+        for (int h = 0; h < 16; ++h) dwg[h] = dW[(row0 + min(g0 + h, n - 1)) * DK + ic];
+#pragma unroll
+        for (int h = 15; h >= 0; --h) {
+            const int t = g0 + h;
+            hv[h] = 0.f;
+            ha[h] = 0.f;
+            hr[h] = 0.f;
+            if (t < n) {
+                const float at = lane_value(ta, t), nut = lane_value(tnu, t);
+                const float irt = lane_value(tir, t), dit = lane_value(tdi, t);
+                const float sdt = lane_value(tsd, t);
+                const float kv = k_s[t * NTH + tid], pm = pm_s[t * NTH + tid];
+                const float b = kv * kv * irt;
+                const float Pt = pm * rcp(fmaf(b, pm, 1.f));
+                const float rat = Pt * rcp(pm), c2 = rat * rat;
+                const float gainP = kv * dit * (dwg[h] - kv * sdt);
+                if constexpr (APPLY) {
+                    const float H = fmaf(c2, Gv, gainP);
+                    const float db = -Gv * Pt * Pt;
+                    pm_s[t * NTH + tid] =
+                        pm * dit * (dwg[h] - 2.f * kv * sdt) + db * 2.f * kv * irt;
+                    if (act) {
+                        hv[h] = H;
+                        ha[h] = 2.f * (pm - nut) * H / at;
+                        hr[h] = -db * b * irt;
+                    }
+                    Gv = at * at * H;
+                } else {
+                    al = at * at * c2 * al;
+                    be = at * at * fmaf(c2, be, gainP);
+                }
+            }
+        }
+        if constexpr (APPLY) {
+            // per-token sums over the key dimensions of these 16 tokens
+            float sv = transpose_sum16(hv, lane), sa = transpose_sum16(ha, lane),
+                  sr = transpose_sum16(hr, lane);
+            sv += __shfl_xor(sv, 16, kWave);
+            sv += __shfl_xor(sv, 32, kWave);
+            sa += __shfl_xor(sa, 16, kWave);
+            sa += __shfl_xor(sa, 32, kWave);
+            sr += __shfl_xor(sr, 16, kWave);
+            sr += __shfl_xor(sr, 32, kWave);
+            if (lane < 16 && g0 + lane < n) {
+                atomicAdd(&red[0][g0 + lane], sv);
+                atomicAdd(&red[1][g0 + lane], sa);
+                atomicAdd(&red[2][g0 + lane], sr);
+            }
+        }
+    }
+    if constexpr (!APPLY) {
+        if (act) ab[(bh * NC + c) * DK + i] = make_float2(al, be);
+    } else {
+        if (act)
+            for (int t = 0; t < n; ++t) dk[(row0 + t) * DK + i] += pm_s[t * NTH + tid];
+        __syncthreads();
+        if (tid < n) {
+            const size_t o = row0 + tid;
+            da[o] = dlna[o] / ta + red[1][tid];
+            dnu[o] = red[0][tid];
+            dr[o] = -tsd * tdi + red[2][tid];
+        }
+    }
+}
+
+// G_out of every chunk from the chunk maps, last chunk first; dlambda0 at the end
+__global__ void bgain_carry_kernel(const float2* __restrict__ ab,
+                                   const float* __restrict__ lam_chunk,
+                                   const float* __restrict__ dlambda_T, float* __restrict__ Gout,
+                                   float* __restrict__ dlambda0, int BH, int DK, int NC) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= BH * DK) return;
+    const size_t bh = idx / DK;
+    const int i = idx % DK;
+    const float lT = lam_chunk[(bh * (NC + 1) + NC) * DK + i];
+    float G = dlambda_T ? -dlambda_T[idx] * lT * lT : 0.f;
+    for (int c = NC - 1; c >= 0; --c) {
+        const size_t o = (bh * NC + c) * DK + i;
+        Gout[o] = G;
+        const float2 m = ab[o];
+        G = fmaf(m.x, G, m.y);
+    }
+    if (dlambda0) {
+        const float l0 = lam_chunk[bh * (NC + 1) * DK + i];
+        // no tokens: lambda_T is lambda0 and its cotangent passes through as is
+        dlambda0[idx] = NC == 0 ? (dlambda_T ? dlambda_T[idx] : 0.f) : -G / (l0 * l0);
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+template <typename E, int DK, int DVT, int C>
+hipError_t bstate_t(const Shape& s, const BwdArgs& b, hipStream_t st) {
+    if constexpr (bstate_fits<E, DK, DVT, C>()) {
+        const int groups = (s.BH + 7) / 8;
+        launch_k((bstate_kernel<E, DK, DVT, C>), dim3(groups * 8 * (s.dv / DVT)), dim3(512), 0,
+                 st, static_cast<const E*>(b.q), static_cast<const E*>(b.k),
+                 static_cast<const E*>(b.dO), b.g, static_cast<const E*>(b.w),
+                 static_cast<const E*>(b.Tm), b.dS_T, b.dv, static_cast<E*>(b.dSe), b.dS0, s.BH,
+                 s.T, s.dv, s.nc);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
+template <typename E, int DK, int C>
+int bstate_tile(int dv) {
+    if (dv >= 64 && bstate_fits<E, DK, 64, C>()) return 64;
+    if (bstate_fits<E, DK, 32, C>()) return 32;
+    return 0;
+}
+
+template <typename E, int DK, int C, int JT>
+hipError_t bgrad_t(const Shape& s, const BwdArgs& b, hipStream_t st) {
+    if constexpr (bgrad_fits<E, DK, C, JT>()) {
+        launch_k((bgrad_kernel<E, DK, C, JT>), dim3(s.nc, s.BH), dim3(512), 0, st,
+                 static_cast<const E*>(b.q), static_cast<const E*>(b.k),
+                 static_cast<const E*>(b.v), static_cast<const E*>(b.dO), b.dv,
+                 static_cast<const E*>(b.w), static_cast<const E*>(b.Tm), b.g,
+                 static_cast<const E*>(b.Sc), static_cast<const E*>(b.dSe), b.dq, b.dk, b.dW,
+                 b.sdot, b.dlna, s.T, s.dv, s.nc);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
+template <typename E, int DK, int C>
+int bgrad_slice(int dv) {
+    if (dv >= 64 && bgrad_fits<E, DK, C, 64>()) return 64;
+    if (dv >= 32 && bgrad_fits<E, DK, C, 32>()) return 32;
+    if (bgrad_fits<E, DK, C, 16>()) return 16;
+    return 0;
+}
+
+template <typename E, typename G, int DK, int C>
+hipError_t bgain_t(const Shape& s, const BwdArgs& b, hipStream_t st) {
+    constexpr int NTH = DK < 64 ? 64 : DK;
+    const dim3 grid(s.nc, s.BH);
+    // a timing request covers the three launches: start at the first, stop at the last
+    const LaunchTiming tm = launch_timing();
+    launch_timing() = LaunchTiming{tm.start, nullptr};
+    launch_k((bgain_kernel<E, G, DK, C, false>), grid, dim3(NTH), 0, st,
+             static_cast<const E*>(b.k), static_cast<const G*>(b.a), static_cast<const G*>(b.nu),
+             static_cast<const G*>(b.r), b.lam_chunk, b.dinv, b.sdot, b.dW, b.dlna, b.Gout,
+             reinterpret_cast<float2*>(b.ab), b.dk, b.da, b.dnu, b.dr, s.T, s.nc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n = s.BH * s.dk;
+    hipLaunchKernelGGL(bgain_carry_kernel, dim3((n + 255) / 256), dim3(256), 0, st,
+                       reinterpret_cast<const float2*>(b.ab), b.lam_chunk, b.dlambda_T, b.Gout,
+                       b.dlambda0, s.BH, s.dk, s.nc);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch_timing() = LaunchTiming{nullptr, tm.stop};
+    launch_k((bgain_kernel<E, G, DK, C, true>), grid, dim3(NTH), 0, st,
+             static_cast<const E*>(b.k), static_cast<const G*>(b.a), static_cast<const G*>(b.nu),
+             static_cast<const G*>(b.r), b.lam_chunk, b.dinv, b.sdot, b.dW, b.dlna, b.Gout,
+             reinterpret_cast<float2*>(b.ab), b.dk, b.da, b.dnu, b.dr, s.T, s.nc);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t bwd_state_e(const Shape& s, const BwdArgs& b, hipStream_t st) {
+#define KDN_BS(DK_, DVT_, C_)                                                          \
+    if (s.dk == DK_ && C_ == s.chunk && bstate_tile<E, DK_, C_>(s.dv) == DVT_ &&       \
+        s.dv % DVT_ == 0)                                                              \
+        return bstate_t<E, DK_, DVT_, C_>(s, b, st);
+#define KDN_BS_C(DK_, DVT_) KDN_BS(DK_, DVT_, 16) KDN_BS(DK_, DVT_, 32) KDN_BS(DK_, DVT_, 64)
+    KDN_BS_C(32, 32) KDN_BS_C(32, 64) KDN_BS_C(64, 32) KDN_BS_C(64, 64)
+    KDN_BS_C(128, 32) KDN_BS_C(128, 64)
+#undef KDN_BS_C
+#undef KDN_BS
+    return hipErrorInvalidValue;
+}
+
+template <typename E>
+hipError_t bwd_grad_e(const Shape& s, const BwdArgs& b, hipStream_t st) {
+#define KDN_BG(DK_, C_, JT_)                                                           \
+    if (s.dk == DK_ && C_ == s.chunk && bgrad_slice<E, DK_, C_>(s.dv) == JT_)          \
+        return bgrad_t<E, DK_, C_, JT_>(s, b, st);
+#define KDN_BG_C(DK_, C_) KDN_BG(DK_, C_, 16) KDN_BG(DK_, C_, 32) KDN_BG(DK_, C_, 64)
+#define KDN_BG_K(DK_) KDN_BG_C(DK_, 16) KDN_BG_C(DK_, 32) KDN_BG_C(DK_, 64)
+    KDN_BG_K(32) KDN_BG_K(64) KDN_BG_K(128)
+#undef KDN_BG_K
+#undef KDN_BG_C
+#undef KDN_BG
+    return hipErrorInvalidValue;
+}
+
+template <typename E>
+hipError_t bwd_gain_e(const Shape& s, const BwdArgs& b, hipStream_t st) {
+#define KDN_BN(DK_, C_)                                                                \
+    if (s.dk == DK_ && s.chunk == C_)                                                  \
+        return s.gate_bf16 ? bgain_t<E, bf16_t, DK_, C_>(s, b, st)                     \
+                           : bgain_t<E, float, DK_, C_>(s, b, st);
+#define KDN_BN_C(DK_) KDN_BN(DK_, 16) KDN_BN(DK_, 32) KDN_BN(DK_, 64)
+    KDN_BN_C(32) KDN_BN_C(64) KDN_BN_C(128)
+#undef KDN_BN_C
+#undef KDN_BN
+    return hipErrorInvalidValue;
+}
+
+template <typename E>
+bool bwd_supported_e(const Shape& s) {
+    bool st = false, gr = false;
+#define KDN_SUP(DK_, C_)                                                               \
+    if (s.dk == DK_ && s.chunk == C_) {                                                \
+        const int t = bstate_tile<E, DK_, C_>(s.dv);                                   \
+        st = t > 0 && s.dv % t == 0;                                                   \
+        gr = bgrad_slice<E, DK_, C_>(s.dv) > 0;                                        \
+    }
+#define KDN_SUP_C(DK_) KDN_SUP(DK_, 16) KDN_SUP(DK_, 32) KDN_SUP(DK_, 64)
+    KDN_SUP_C(32) KDN_SUP_C(64) KDN_SUP_C(128)
+#undef KDN_SUP_C
+#undef KDN_SUP
+    return st && gr;
+}
+
+}  // namespace
+
+bool backward_supported(const Shape& s) {
+    if (!s.diag || !chunk_supported(s)) return false;
+    return s.qkv_bf16 ? bwd_supported_e<bf16_t>(s) : bwd_supported_e<float>(s);
+}
+
+hipError_t launch_bwd_state(const Shape& s, const BwdArgs& b, hipStream_t st) {
+    if (s.BH == 0) return hipSuccess;
+    return s.qkv_bf16 ? bwd_state_e<bf16_t>(s, b, st) : bwd_state_e<float>(s, b, st);
+}
+
+hipError_t launch_bwd_grad(const Shape& s, const BwdArgs& b, hipStream_t st) {
+    if (s.BH == 0 || s.nc == 0) return hipSuccess;
+    return s.qkv_bf16 ? bwd_grad_e<bf16_t>(s, b, st) : bwd_grad_e<float>(s, b, st);
+}
+
+hipError_t launch_bwd_gain(const Shape& s, const BwdArgs& b, hipStream_t st) {
+    if (s.BH == 0) return hipSuccess;
+    if (s.nc == 0) {
+        // no tokens: dlambda0 = dlambda_T (the carry over zero chunks)
+        const int n = s.BH * s.dk;
+        hipLaunchKernelGGL(bgain_carry_kernel, dim3((n + 255) / 256), dim3(256), 0, st,
+                           reinterpret_cast<const float2*>(b.ab), b.lam_chunk, b.dlambda_T,
+                           b.Gout, b.dlambda0, s.BH, s.dk, 0);
+        return hipGetLastError();
+    }
+    return s.qkv_bf16 ? bwd_gain_e<bf16_t>(s, b, st) : bwd_gain_e<float>(s, b, st);
+}
+
+}  // namespace kdn

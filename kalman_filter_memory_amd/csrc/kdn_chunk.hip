@@ -131,26 +131,6 @@ template <typename E, int DK, int C> struct PrepLds {
 //     column, all blocks in one wave), then block columns T_ij = -T_ii
 //     sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA, one wave per block column.
 
-// v[j] summed over the 16 lanes of each 16-lane group: on return lane l holds
-// in v[0] the group total of v[l % 16] (15 exchanges instead of 16 reductions)
-template <int H>
-__device__ __forceinline__ void transpose_sum_step(float (&v)[16], int lane) {
-    const bool upper = (lane & H) != 0;
-#pragma unroll
-    for (int j = 0; j < H; ++j) {
-        const float keep = upper ? v[j + H] : v[j];
-        const float send = upper ? v[j] : v[j + H];
-        v[j] = keep + __shfl_xor(send, H, kWave);
-    }
-}
-__device__ __forceinline__ float transpose_sum16(float (&v)[16], int lane) {
-    transpose_sum_step<8>(v, lane);
-    transpose_sum_step<4>(v, lane);
-    transpose_sum_step<2>(v, lane);
-    transpose_sum_step<1>(v, lane);
-    return v[0];
-}
-
 // One chunk's inputs, loaded into registers ahead of their use: K rows, the
 // gates of token `lane` (in their storage type G, widened only when used, so
 // that no wait for the load is forced early) and the chunk-boundary precision
@@ -206,8 +186,9 @@ __device__ __forceinline__ void prep_fetch(const E* __restrict__ k, const G* __r
 // The work of one chunk; LDS as in PrepLds, inputs already in registers.
 template <typename E, typename G, int DK, int C, bool FUSE>
 __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
-                                           E* __restrict__ Tm, float* __restrict__ gout, int T,
-                                           int NC, size_t bh, int c, const PrepIn<E, G, DK, C>& in,
+                                           E* __restrict__ Tm, float* __restrict__ gout,
+                                           float* __restrict__ dinv, int T, int NC, size_t bh,
+                                           int c, const PrepIn<E, G, DK, C>& in,
                                            unsigned char* smem, float* sden, float* sg,
                                            float4* sgt) {
     using L = PrepLds<E, DK, C>;
@@ -330,6 +311,7 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
             sync_lds();  // W overwrites the sub-block maps
             if (act) {
                 const float rden = 1.f / (den + rt);
+                if (dinv && lane < 16 && tb0 + lane < n) dinv[row0 + tb0 + lane] = rden;
                 // (5) w rows
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
@@ -518,7 +500,7 @@ template <typename E, typename G, int DK, int C, bool FUSE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void prep_kernel(
     const E* __restrict__ k, const G* __restrict__ a, const G* __restrict__ nu,
     const G* __restrict__ r, bool diag, const float* __restrict__ lam_chunk, E* __restrict__ w,
-    E* __restrict__ Tm, float* __restrict__ gout, int T, int NC) {
+    E* __restrict__ Tm, float* __restrict__ gout, float* __restrict__ dinv, int T, int NC) {
     using L = PrepLds<E, DK, C>;
     __shared__ __align__(16) unsigned char smem[L::R1 + L::R2];
     __shared__ __align__(16) float sden[C];
@@ -531,10 +513,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, bh, c0, T, NC, tid, in0);
     prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, bh, min(c1, NC - 1), T, NC, tid,
                                   in1);
-    prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, T, NC, bh, c0, in0, smem, sden, sg, sgt);
+    prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, dinv, T, NC, bh, c0, in0, smem, sden, sg,
+                                  sgt);
     if (c1 < NC) {
         sync_lds();  // the second chunk's staging overwrites K / A / T
-        prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, T, NC, bh, c1, in1, smem, sden, sg, sgt);
+        prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, dinv, T, NC, bh, c1, in1, smem, sden,
+                                      sg, sgt);
     }
 }
 
@@ -868,7 +852,8 @@ template <typename E, int DK, int DVT, int C>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void state_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ gin, const E* __restrict__ w, const E* __restrict__ Tm,
-    const float* S0, E* __restrict__ o, float* S_T, int BH, int T, int DV, int NC) {
+    const float* S0, E* __restrict__ o, float* S_T, E* __restrict__ Sc, int BH, int T, int DV,
+    int NC) {
     using G = StateCfg<E, DK, DVT, C>;
     constexpr int BI = G::BI, BV = G::BV, NVB = G::NVB;
     __shared__ __align__(16) StateLds<E, DK, DVT, C> L;
@@ -921,12 +906,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     sync_lds();
 
     // the two sets alternate roles from chunk to chunk
+    // (Sc: the state at every chunk start, kept for the backward pass)
     for (int c = 0; c < NC; c += 2) {
+        if (Sc) state_save<E, DK, DVT, C>(accS, Sc + ((bh * NC + c) * DV + j0) * DK, wave, lane);
         state_chunk<E, DK, DVT, C>(A, L, accS, c, pkA, pqA, pwA, pvA, ptA, pgA, pkB, pqB, pwB,
                                    pvB, ptB, pgB);
-        if (c + 1 < NC)
+        if (c + 1 < NC) {
+            if (Sc)
+                state_save<E, DK, DVT, C>(accS, Sc + ((bh * NC + c + 1) * DV + j0) * DK, wave,
+                                          lane);
             state_chunk<E, DK, DVT, C>(A, L, accS, c + 1, pkB, pqB, pwB, pvB, ptB, pgB, pkA, pqA,
                                        pwA, pvA, ptA, pgA);
+        }
     }
     if (S_T) {
 #pragma unroll
@@ -981,25 +972,26 @@ int dv_tile(const Shape& s) {
 
 template <typename E, typename G, int DK, int C>
 hipError_t prep_t(const Shape& s, bool fuse, const void* k, const void* a, const void* nu,
-                  const void* r, const float* lc, void* w, void* Tm, float* g, hipStream_t st) {
+                  const void* r, const float* lc, void* w, void* Tm, float* g, float* dinv,
+                  hipStream_t st) {
     static_assert(PrepLds<E, DK, C>::BYTES <= kLdsLimit, "prep LDS");
     const dim3 grid((s.nc + 1) / 2, s.BH);
     if (fuse)
         launch_k((prep_kernel<E, G, DK, C, true>), grid, dim3(kThreads), 0, st,
                            static_cast<const E*>(k), static_cast<const G*>(a),
                            static_cast<const G*>(nu), static_cast<const G*>(r), s.diag, lc,
-                           static_cast<E*>(w), static_cast<E*>(Tm), g, s.T, s.nc);
+                           static_cast<E*>(w), static_cast<E*>(Tm), g, dinv, s.T, s.nc);
     else
         launch_k((prep_kernel<E, G, DK, C, false>), grid, dim3(kThreads), 0, st,
                            static_cast<const E*>(k), static_cast<const G*>(a),
                            static_cast<const G*>(nu), static_cast<const G*>(r), s.diag, lc,
-                           static_cast<E*>(w), static_cast<E*>(Tm), g, s.T, s.nc);
+                           static_cast<E*>(w), static_cast<E*>(Tm), g, dinv, s.T, s.nc);
     return hipGetLastError();
 }
 
 template <typename E, int DK, int DVT, int C>
 hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, const float* g,
-                   const void* w, const void* Tm, const float* S0, void* o, float* S_T,
+                   const void* w, const void* Tm, const float* S0, void* o, float* S_T, void* Sc,
                    hipStream_t st) {
     if constexpr (state_fits<E, DK, DVT, C>()) {
         const int groups = (s.BH + 7) / 8;
@@ -1007,8 +999,8 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
                            dim3(StateCfg<E, DK, DVT, C>::THREADS), 0, st,
                            static_cast<const E*>(q), static_cast<const E*>(k),
                            static_cast<const E*>(v), g, static_cast<const E*>(w),
-                           static_cast<const E*>(Tm), S0, static_cast<E*>(o), S_T, s.BH, s.T,
-                           s.dv, s.nc);
+                           static_cast<const E*>(Tm), S0, static_cast<E*>(o), S_T,
+                           static_cast<E*>(Sc), s.BH, s.T, s.dv, s.nc);
         return hipGetLastError();
     } else {
         return hipErrorInvalidValue;
@@ -1017,11 +1009,13 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
 
 template <typename E>
 hipError_t prep_e(const Shape& s, bool fuse, const void* k, const void* a, const void* nu,
-                  const void* r, const float* lc, void* w, void* Tm, float* g, hipStream_t st) {
-#define KDN_PREP(DK_, C_)                                                                 \
-    if (s.dk == DK_ && s.chunk == C_)                                                     \
-        return s.gate_bf16 ? prep_t<E, bf16_t, DK_, C_>(s, fuse, k, a, nu, r, lc, w, Tm, g, st) \
-                           : prep_t<E, float, DK_, C_>(s, fuse, k, a, nu, r, lc, w, Tm, g, st);
+                  const void* r, const float* lc, void* w, void* Tm, float* g, float* dinv,
+                  hipStream_t st) {
+#define KDN_PREP(DK_, C_)                                                                   \
+    if (s.dk == DK_ && s.chunk == C_)                                                       \
+        return s.gate_bf16                                                                  \
+                   ? prep_t<E, bf16_t, DK_, C_>(s, fuse, k, a, nu, r, lc, w, Tm, g, dinv, st) \
+                   : prep_t<E, float, DK_, C_>(s, fuse, k, a, nu, r, lc, w, Tm, g, dinv, st);
 #define KDN_PREP_C(DK_) KDN_PREP(DK_, 16) KDN_PREP(DK_, 32) KDN_PREP(DK_, 64)
     KDN_PREP_C(32) KDN_PREP_C(64) KDN_PREP_C(128)
 #undef KDN_PREP_C
@@ -1031,12 +1025,12 @@ hipError_t prep_e(const Shape& s, bool fuse, const void* k, const void* a, const
 
 template <typename E>
 hipError_t state_e(const Shape& s, const void* q, const void* k, const void* v, const float* g,
-                   const void* w, const void* Tm, const float* S0, void* o, float* S_T,
+                   const void* w, const void* Tm, const float* S0, void* o, float* S_T, void* Sc,
                    hipStream_t st) {
     const int dvt = dv_tile(s);
 #define KDN_ST(DK_, DVT_, C_)                                                             \
     if (s.dk == DK_ && dvt == DVT_ && s.chunk == C_)                                      \
-        return state_t<E, DK_, DVT_, C_>(s, q, k, v, g, w, Tm, S0, o, S_T, st);
+        return state_t<E, DK_, DVT_, C_>(s, q, k, v, g, w, Tm, S0, o, S_T, Sc, st);
 #define KDN_ST_C(DK_, DVT_) KDN_ST(DK_, DVT_, 16) KDN_ST(DK_, DVT_, 32) KDN_ST(DK_, DVT_, 64)
     KDN_ST_C(32, 32) KDN_ST_C(32, 64) KDN_ST_C(64, 32) KDN_ST_C(64, 64)
     KDN_ST_C(128, 32) KDN_ST_C(128, 64)
@@ -1056,18 +1050,18 @@ bool chunk_supported(const Shape& s) {
 
 hipError_t launch_chunk_prep(const Shape& s, bool fuse_gain, const void* k, const void* a,
                              const void* nu, const void* r, const float* lam_chunk, void* w,
-                             void* Tm, float* g, hipStream_t st) {
+                             void* Tm, float* g, hipStream_t st, float* dinv) {
     if (s.BH == 0 || s.nc == 0) return hipSuccess;
-    return s.qkv_bf16 ? prep_e<bf16_t>(s, fuse_gain, k, a, nu, r, lam_chunk, w, Tm, g, st)
-                      : prep_e<float>(s, fuse_gain, k, a, nu, r, lam_chunk, w, Tm, g, st);
+    return s.qkv_bf16 ? prep_e<bf16_t>(s, fuse_gain, k, a, nu, r, lam_chunk, w, Tm, g, dinv, st)
+                      : prep_e<float>(s, fuse_gain, k, a, nu, r, lam_chunk, w, Tm, g, dinv, st);
 }
 
 hipError_t launch_chunk_state(const Shape& s, const void* q, const void* k, const void* v,
                               const float* g, const void* w, const void* Tm, const float* S0,
-                              void* o, float* S_T, hipStream_t st) {
+                              void* o, float* S_T, hipStream_t st, void* Sc) {
     if (s.BH == 0) return hipSuccess;
-    return s.qkv_bf16 ? state_e<bf16_t>(s, q, k, v, g, w, Tm, S0, o, S_T, st)
-                      : state_e<float>(s, q, k, v, g, w, Tm, S0, o, S_T, st);
+    return s.qkv_bf16 ? state_e<bf16_t>(s, q, k, v, g, w, Tm, S0, o, S_T, Sc, st)
+                      : state_e<float>(s, q, k, v, g, w, Tm, S0, o, S_T, Sc, st);
 }
 
 }  // namespace kdn

@@ -57,17 +57,44 @@ hipError_t launch_gain(const Shape& s, const void* k, const void* r, const float
 // then A = strict_tril(K W^T * Gamma) and T = (I + A)^{-1} written to Tm
 // [BH][nc][chunk][chunk] in qkv dtype, and the chunk-local cumulative log2
 // decay g [BH][nc][chunk] (float32).  fuse_gain = false reads w instead.
+// dinv (diagonal, fused gain; may be NULL): 1 / (k^T P^- k + r) per token
+// [BH][T] (float32), kept for the backward pass.
 hipError_t launch_chunk_prep(const Shape& s, bool fuse_gain, const void* k, const void* a,
                              const void* nu, const void* r, const float* lam_chunk, void* w,
-                             void* Tm, float* g, hipStream_t st);
+                             void* Tm, float* g, hipStream_t st, float* dinv = nullptr);
 // Sequential chunk pass: memory write and read-out (g from the prep pass).
+// Sc (may be NULL): the state at every chunk start, [BH][nc][dv][dk] in qkv
+// dtype, kept for the backward pass.
 hipError_t launch_chunk_state(const Shape& s, const void* q, const void* k, const void* v,
                               const float* g, const void* w, const void* Tm, const float* S0,
-                              void* o, float* S_T, hipStream_t st);
+                              void* o, float* S_T, hipStream_t st, void* Sc = nullptr);
 // One decode step in place.
 hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
                          const void* a, const void* nu, const void* r, float* S, float* lam,
                          void* o, hipStream_t st);
+
+// Backward pass (diagonal variant).  Device pointers; per-token arrays are
+// [BH][T], per-(token, dim) arrays [BH][T][d], per-chunk states [BH][nc][dv][dk].
+struct BwdArgs {
+    const void *q, *k, *v, *a, *nu, *r;  // the forward's inputs
+    const void* dO;                      // [BH][T][dv], qkv dtype
+    const float *dS_T, *dlambda_T;       // may be NULL (zero)
+    const void *w, *Tm;                  // the forward's gain keys and T matrices
+    const float *g, *lam_chunk, *dinv;   // log2 decays, boundary precisions, 1/D
+    const void* Sc;                      // state at every chunk start (qkv dtype)
+    void* dSe;                           // state adjoint at every chunk end (qkv dtype)
+    float *dW, *sdot, *dlna;             // dW [BH][T][dk]; s_t and d(ln a_t) [BH][T]
+    float *ab, *Gout;                    // per (chunk, dim): float2 map, G at the chunk end
+    float *dq, *dk, *dv, *da, *dnu, *dr;  // outputs
+    float *dlambda0, *dS0;               // outputs, may be NULL
+};
+// reverse state pass: dv, dSe, dS0
+hipError_t launch_bwd_state(const Shape& s, const BwdArgs& b, hipStream_t st);
+// per-chunk gradients: dq, dk (memory part), dW, sdot, dlna
+hipError_t launch_bwd_grad(const Shape& s, const BwdArgs& b, hipStream_t st);
+// gain and precision recursion: dk (+= gain part), da, dnu, dr, dlambda0
+hipError_t launch_bwd_gain(const Shape& s, const BwdArgs& b, hipStream_t st);
+bool backward_supported(const Shape& s);
 
 // true if the chunk kernels are built for this (dtype, dk, dv, chunk)
 bool chunk_supported(const Shape& s);

@@ -303,5 +303,49 @@ __device__ __forceinline__ void state_write(const StateAcc<E, DK, DVT, C>& accS,
     }
 }
 
+// v[j] summed over the 16 lanes of each 16-lane group: on return lane l holds
+// in v[0] the group total of v[l % 16] (15 exchanges instead of 16 reductions)
+template <int H>
+__device__ __forceinline__ void transpose_sum_step(float (&v)[16], int lane) {
+    const bool upper = (lane & H) != 0;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+        const float keep = upper ? v[j + H] : v[j];
+        const float send = upper ? v[j] : v[j + H];
+        v[j] = keep + __shfl_xor(send, H, kWave);
+    }
+}
+__device__ __forceinline__ float transpose_sum16(float (&v)[16], int lane) {
+    transpose_sum_step<8>(v, lane);
+    transpose_sum_step<4>(v, lane);
+    transpose_sum_step<2>(v, lane);
+    transpose_sum_step<1>(v, lane);
+    return v[0];
+}
+
+// S^T blocks of the state -> global rows S[j][i] (row stride DK) in the input
+// dtype, from dst = the tile's first row
+template <typename E, int DK, int DVT, int C>
+__device__ __forceinline__ void state_save(const StateAcc<E, DK, DVT, C>& accS, E* dst, int wave,
+                                           int lane) {
+    using G = StateCfg<E, DK, DVT, C>;
+#pragma unroll
+    for (int x = 0; x < G::SPW; ++x) {
+        const int job = wave + G::NW * x;
+        if (job < G::NSJ) {
+            const int ib = (job / G::NVB) * G::BI, jb = (job % G::NVB) * G::BV;
+#pragma unroll
+            for (int bi = 0; bi < G::BI; ++bi)
+#pragma unroll
+                for (int bv = 0; bv < G::BV; ++bv) {
+                    const int i = 16 * (ib + bi) + 4 * (lane >> 4);
+                    const int j = 16 * (jb + bv) + (lane & 15);
+                    const floatx4 sv = accS[x][bi][bv];
+                    store4<E>(dst + j * DK + i, sv[0], sv[1], sv[2], sv[3]);
+                }
+        }
+    }
+}
+
 }  // namespace
 }  // namespace kdn

@@ -118,6 +118,31 @@ def test_host_side_errors_return_before_any_launch(lib):
     _ = P
 
 
+def test_backward_host_side_checks(lib):
+    """kdn_backward: workspace query and argument errors, all before any launch."""
+    fake = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x2000)
+    d = _desc(B=8, H=16, T=4096, d_k=128, d_v=128, chunk=64)
+    need = kdn.backward_workspace_bytes(d)
+    bh, nc, n = 128, 64, 8 * 16 * 4096
+    # forward workspace, then 1/D, chunk-start states and chunk-end adjoints
+    # (bf16), dW, s, d(ln a), chunk maps and G
+    states = bh * nc * 128 * 128 * 2
+    expect = (kdn.forward_workspace_bytes(d) + n * 4 + 2 * states + n * 128 * 4 + 2 * n * 4
+              + bh * nc * 128 * 12)
+    assert expect <= need <= expect + 9 * 256
+    iso = _desc(B=1, H=1, T=16, d_k=32, d_v=32, chunk=16)
+    iso.variant = kdn.ISOTROPIC
+    assert kdn.backward_workspace_bytes(iso) == 0
+    args = [fake] * 19
+    assert lib.kdn_backward(ctypes.byref(iso), *args, ws, 1 << 40, None) == 3
+    assert lib.kdn_backward(ctypes.byref(d), None, *args[1:], ws, need, None) == 1
+    assert lib.kdn_backward(ctypes.byref(d), *args, ws, need - 1, None) == 4
+    assert lib.kdn_backward(ctypes.byref(d), *args[:9], ctypes.c_void_p(0x1004), *args[10:],
+                            ws, need, None) == 5
+    assert lib.kdn_backward(ctypes.byref(_desc(B=0)), *([None] * 19), None, 0, None) == 0
+
+
 def test_python_binding_refuses_cpu_tensors(lib):
     import torch
     x = torch.zeros(1, 1, 4, 32)

@@ -1,0 +1,136 @@
+"""GPU parity of the backward pass (kdn_backward, diagonal variant) against the
+fp64 oracle's vector-Jacobian product, through the C ABI.
+
+Every gradient is compared per (b, h) slice with the normwise metric of the
+forward tests (max|x - ref| / max|ref| over the slice).  Bars: TOL_BWD_F32 for
+float32 inputs (the forward's float32 bar) and TOL_BWD_BF16 for bfloat16 inputs
+(the MFMA operands -- the states, U, dU, dR -- are rounded to bfloat16, 2^-9
+relative each, as in the forward; every gradient, dlambda0 included, is fed by
+dW and so by those products).  The full-size workloads run in the launch
+configuration of the benchmark; the oracle checks sampled heads (heads are
+independent, so a sampled head is the full-size computation for it).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import kalman_filter_memory_amd as kdn
+import oracle
+from gpu_util import forward_tensors, head_slice, host, normwise, say, to_dev, tdtype
+from kdn_inputs import backward_cotangents, config_inputs, forward_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_BWD_F32 = 1e-4
+TOL_BWD_BF16 = 3e-2
+GRADS = ("dq", "dk", "dv", "da", "dnu", "dr", "dlambda0", "dS0")
+KEYMAP = {"dnu": "dqnoise"}
+
+
+def _gpu_backward(inp, cot, chunk):
+    t = forward_tensors(inp)
+    dO = to_dev(cot["dO"], tdtype(inp["dtype"]))
+    dS_T = None if cot["dS_T"] is None else to_dev(cot["dS_T"], torch.float32)
+    dl_T = None if cot["dlambda_T"] is None else to_dev(cot["dlambda_T"], torch.float32)
+    g = kdn.backward(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], dO, t["lambda0"],
+                     t["S0"], dS_T, dl_T, chunk=chunk)
+    torch.cuda.synchronize()
+    return {n: host(g[KEYMAP.get(n, n)]) for n in GRADS}
+
+
+def _oracle_backward(inp, cot):
+    return oracle.backward(inp["q"], inp["k"], inp["v"], inp["a"], inp["nu"], inp["r"],
+                           cot["dO"], inp["lambda0"], inp["S0"], cot["dS_T"], cot["dlambda_T"],
+                           variant="diagonal")
+
+
+def _errors(got, ref, heads=None):
+    err = {}
+    for n in GRADS:
+        x = got[n]
+        if heads is not None:
+            x = x[tuple(np.array(heads).T)][:, None]
+        err[n] = normwise(x, ref[n])
+    return err
+
+
+def _assert(err, dtype):
+    tol = TOL_BWD_BF16 if dtype == "bf16" else TOL_BWD_F32
+    say("    " + "  ".join(f"{n} {e:.1e}" for n, e in err.items()) + f"  (tol {tol:g})")
+    for n, e in err.items():
+        assert e <= tol, (n, e)
+
+
+SMALL = [
+    # B, H, T, dk, dv, chunk, dtype
+    (1, 1, 1, 32, 32, 16, "f32"),
+    (1, 2, 37, 32, 64, 16, "f32"),
+    (1, 2, 100, 64, 32, 32, "bf16"),
+    (1, 2, 200, 64, 128, 64, "f32"),
+    (1, 1, 97, 128, 64, 32, "f32"),
+    (2, 2, 65, 128, 32, 64, "bf16"),
+    (2, 1, 130, 128, 128, 64, "bf16"),
+    (3, 1, 300, 128, 128, 16, "bf16"),
+    (1, 3, 64, 32, 128, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SMALL)),
+                         ids=["B{}H{}T{}k{}v{}C{}_{}".format(*c) for c in SMALL])
+def test_backward_small_shapes(idx):
+    B, H, T, dk, dv, C, dtype = SMALL[idx]
+    inp = forward_inputs(B, H, T, dk, dv, dtype=dtype, seed=300 + idx)
+    cot = backward_cotangents(B, H, T, dk, dv, dtype=dtype, seed=300 + idx)
+    say(f"[gpu] backward B{B} H{H} T{T} dk{dk} dv{dv} C{C} {dtype}")
+    got = _gpu_backward(inp, cot, C)
+    for n, x in got.items():
+        assert np.all(np.isfinite(x)), n
+    _assert(_errors(got, _oracle_backward(inp, cot)), dtype)
+
+
+def test_backward_without_state_cotangents():
+    inp = forward_inputs(1, 2, 150, 64, 64, dtype="bf16", seed=41)
+    cot = backward_cotangents(1, 2, 150, 64, 64, dtype="bf16", seed=41, state_cotangents=False)
+    say("[gpu] backward, read-out cotangent only")
+    _assert(_errors(_gpu_backward(inp, cot, 64), _oracle_backward(inp, cot)), "bf16")
+
+
+def test_backward_empty_sequence_passes_state_cotangents_through():
+    inp = forward_inputs(1, 2, 0, 64, 64, seed=42)
+    cot = backward_cotangents(1, 2, 0, 64, 64, seed=42)
+    say("[gpu] backward T=0")
+    got = _gpu_backward(inp, cot, 64)
+    np.testing.assert_array_equal(got["dS0"], cot["dS_T"])
+    np.testing.assert_array_equal(got["dlambda0"], cot["dlambda_T"])
+    assert got["dq"].size == 0 and got["da"].size == 0
+
+
+def test_workload_diag_f32_B2_H4_T2048_d64_backward():
+    inp = config_inputs(1)
+    cot = backward_cotangents(2, 4, 2048, 64, 64, dtype="f32", seed=1001)
+    say("[gpu] backward diag f32 [2,4,2048,64]")
+    _assert(_errors(_gpu_backward(inp, cot, 64), _oracle_backward(inp, cot)), "f32")
+
+
+def _sampled(index, heads, B, H, T, d):
+    say(f"[gpu] generating workload {index}")
+    inp = config_inputs(index)
+    cot = backward_cotangents(B, H, T, d, d, dtype="bf16", seed=1000 + index)
+    say(f"[gpu] backward full size {inp['q'].shape}")
+    got = _gpu_backward(inp, cot, 64)
+    for n, x in got.items():
+        assert np.all(np.isfinite(x)), n
+    sub = head_slice(inp, heads)
+    csub = {n: np.stack([cot[n][b, h] for b, h in heads])[:, None] for n in cot}
+    say(f"[cpu] oracle backward on heads {heads}")
+    _assert(_errors(got, _oracle_backward(sub, csub), heads), "bf16")
+
+
+def test_workload_diag_bf16_B8_H16_T4096_d128_backward_sampled_heads():
+    _sampled(2, [(0, 0), (3, 7), (7, 15)], 8, 16, 4096, 128)
+
+
+def test_workload_long_bf16_B1_H16_T65536_d128_backward_sampled_head():
+    _sampled(3, [(0, 11)], 1, 16, 65536, 128)
