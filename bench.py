@@ -210,11 +210,138 @@ def run(args):
         res["roofline"]["traffic_src_sha256"] = sha
     del t, ws, out
     torch.cuda.empty_cache()
+    if not args.no_backward:
+        res["backward"] = bench_backward(args, inp)
     if not args.no_decode:
         res["decode"] = bench_decode(args)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args)
     print(json.dumps(res), flush=True)
+
+
+BWD_STAGES = ("scan_reduce", "scan_carry", "chunk_prep", "chunk_state", "bwd_state",
+              "bwd_grad", "bwd_gain")
+
+
+def algorithmic_backward(B, H, T, dk, dv, C):
+    """Algorithmic bytes and MFMA flops of each backward stage (bf16 inputs,
+    float32 gradients).  The first four stages are the forward recompute
+    (as in the forward, plus 1/D per token from the prep pass and the bf16
+    state at every chunk start from the state pass)."""
+    n = B * H * T
+    nc = -(-T // C)
+    bh = B * H
+    e = 2
+    g = 3 * e
+    states = bh * nc * dv * dk * e
+    fby, ffl = algorithmic(B, H, T, dk, dv, C)
+    by = {
+        "scan_reduce": fby["scan_reduce"],
+        "scan_carry": fby["scan_carry"] - bh * dk * 4,  # no lambda_T
+        "chunk_prep": fby["chunk_prep"] + n * 4,
+        "chunk_state": fby["chunk_state"] + states,
+        # read q, k, w, dO, T, g, dS_T; write dv (= dR, f32), the chunk-end
+        # adjoints (bf16) and dS0
+        "bwd_state": n * (3 * dk + dv) * e + bh * nc * C * C * e + n * 4 + bh * dv * dk * 4
+        + n * dv * 4 + states + bh * dv * dk * 4,
+        # read q, k, w, v, dO, dR, T, g and both chunk states; write dq, dk, dW
+        # (f32), s and d(ln a)
+        "bwd_grad": n * (3 * dk + 2 * dv) * e + n * dv * 4 + bh * nc * C * C * e + n * 4
+        + 2 * states + 3 * n * dk * 4 + 2 * n * 4,
+        # map pass: k, dW, gates, 1/D, s, boundary precisions -> chunk maps;
+        # carry; apply pass: the same plus d(ln a), G, dk read and written,
+        # da, dnu, dr
+        "bwd_gain": (n * dk * (e + 4) + n * (g + 8) + bh * nc * dk * (4 + 8))
+        + bh * nc * dk * (8 + 4)
+        + (n * dk * (e + 4) + n * (g + 12) + bh * nc * dk * 8 + 2 * n * dk * 4 + 3 * n * 4),
+    }
+    fl = {
+        "scan_reduce": ffl["scan_reduce"], "scan_carry": ffl["scan_carry"],
+        "chunk_prep": ffl["chunk_prep"], "chunk_state": ffl["chunk_state"],
+        # M (lower half), D W dS^T, M^T dO, T^T dU, the adjoint update (two products)
+        "bwd_state": n * (6 * dk * dv + C * dk + 2 * C * dv),
+        # X = K S^T, U = T R (half), dM and dA (halves), dO S, dR S, U dS', M and A
+        # (halves), (dM G) W, (dA G) W and their transposed products with Q, K (halves)
+        "bwd_grad": n * (8 * dk * dv + 3 * C * dv + 4 * C * dk),
+        "bwd_gain": 0,
+    }
+    return by, fl
+
+
+def bench_backward(args, inp):
+    """Backward pass (kdn_backward) on the same workload: recompute plus the
+    gradient kernels, per-stage times from dispatch-recorded events."""
+    import numpy as np
+    import torch
+
+    import kalman_filter_memory_amd as kdn
+    from kdn_inputs import backward_cotangents
+
+    dev = torch.device("cuda:0")
+    B, H, T, dk, dv, C = (WL[x] for x in ("B", "H", "T", "dk", "dv", "chunk"))
+    bf = torch.bfloat16
+    t = {n: torch.from_numpy(inp[n]).to(dev, bf) for n in ("q", "k", "v", "a", "nu", "r")}
+    lam0 = torch.from_numpy(inp["lambda0"]).to(dev)
+    S0 = torch.from_numpy(inp["S0"]).to(dev)
+    log("generating backward cotangents")
+    cot = backward_cotangents(B, H, T, dk, dv, dtype="bf16", seed=1002)
+    dO = torch.from_numpy(cot["dO"]).to(dev, bf)
+    dS_T = torch.from_numpy(cot["dS_T"]).to(dev)
+    dl_T = torch.from_numpy(cot["dlambda_T"]).to(dev)
+    d = kdn.make_desc(B, H, T, dk, dv, C, "diagonal", kdn.BF16, kdn.BF16)
+    ws = torch.empty(kdn.backward_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    shapes = {"dq": (B, H, T, dk), "dk": (B, H, T, dk), "dv": (B, H, T, dv),
+              "da": (B, H, T), "dqnoise": (B, H, T), "dr": (B, H, T),
+              "dlambda0": (B, H, dk), "dS0": (B, H, dv, dk)}
+    out = {n: torch.empty(sh, dtype=torch.float32, device=dev) for n, sh in shapes.items()}
+
+    def step(events=None):
+        kdn.backward(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], dO, lam0, S0, dS_T, dl_T,
+                     chunk=C, workspace=ws, out=out, events=events)
+
+    steps = max(1, args.backward_steps)
+    ramp(step, args.ramp_ms)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {steps} backward steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(BWD_STAGES))]
+           for _ in range(steps)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for row in evs:
+        step(events=row)
+    torch.cuda.synchronize()
+    st_ms = {k: float(np.mean([row[2 * i].elapsed_time(row[2 * i + 1]) for row in evs]))
+             for i, k in enumerate(BWD_STAGES)}
+    by, fl = algorithmic_backward(B, H, T, dk, dv, C)
+    stages = {}
+    for k in BWD_STAGES:
+        sec = st_ms[k] * 1e-3
+        stages[k] = {"us": round(st_ms[k] * 1e3, 2), "GB/s": round(by[k] / sec / 1e9, 1)}
+        if fl[k]:
+            stages[k]["TFLOP/s"] = round(fl[k] / sec / 1e12, 2)
+    grad_stages = ("bwd_state", "bwd_grad", "bwd_gain")
+    dom = max(grad_stages, key=lambda k: st_ms[k])
+    ach = by[dom] / (st_ms[dom] * 1e-3) / 1e9
+    del t, ws, out, dO
+    torch.cuda.empty_cache()
+    return {"workload": "diag_bf16_B8_H16_T4096_d128", "steps": steps,
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "includes": "forward recompute (scan, prep, state keeping chunk states) "
+                        "and the three gradient stages",
+            "stages": stages,
+            "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(ach / PEAK_HBM_GBS, 4), "bytes_per_launch": by[dom],
+                         "us_per_launch": round(st_ms[dom] * 1e3, 2), "traffic": None}}
 
 
 def ramp(fn, ms):
@@ -316,13 +443,15 @@ def main():
                     help="minimum wall time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "kernel that HBM byte counters can be scaled against)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer shards over heads with no communication; see DESIGN.md)",
+              "(the layer shards over heads with no communication)",
               file=sys.stderr)
         sys.exit(2)
     run(args)

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     for (int c = NC - 1; c >= 0; --c) {
         const int n = min(C, T - c * C);
         const size_t row0 = bh * T + (size_t)c * C;
-        state_save<E, DK, DVT, C>(acc, dSe + ((bh * NC + c) * DV + j0) * DK, wave, lane);
+        state_copy_out<E, DK, DVT, C>(L.S, dSe + ((bh * NC + c) * DV + j0) * DK, tid);
         if (c > 0)
             state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, dO, w, Tm, gin, bh, j0, T, DV, NC,
                                                     c - 1, tid, lane, pk, pq, pw, pv, pt, pg);
@@ -652,10 +652,7 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
     const float* __restrict__ sdot, const float* __restrict__ dW, const float* __restrict__ dlna,
     const float* __restrict__ Gout, float2* __restrict__ ab, float* __restrict__ dk,
     float* __restrict__ da, float* __restrict__ dnu, float* __restrict__ dr, int T, int NC) {
-    constexpr int NTH = DK < 64 ? 64 : DK;
-    __shared__ float pm_s[C * NTH];  // P^-, then the gain's part of dk
-    __shared__ float k_s[C * NTH];   // the lane's key component of every token
-    __shared__ float red[3][C];      // per token: sum_i H, sum_i 2 a P_prev H, sum_i G P^2 b/r
+    __shared__ float red[3][C];  // per token: sum_i H, sum_i 2 a P_prev H, sum_i G P^2 b/r
     const int tid = threadIdx.x, lane = tid & 63;
     const int c = blockIdx.x;
     const size_t bh = blockIdx.y;
@@ -675,6 +672,8 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
     const float tir = 1.f / tr, tdi = dinv[tk], tsd = sdot[tk];
     // forward: P^- of every token from the chunk-boundary precision
     float P = 1.f / lam_chunk[(bh * (NC + 1) + c) * DK + ic];
+    float pms[C];  // P^- of every token (both walks fully unrolled: static indices)
+#pragma unroll
     for (int g0 = 0; g0 < C; g0 += 16) {
         float kg[16];
 #pragma unroll
@@ -682,23 +681,29 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
 #pragma unroll
         for (int h = 0; h < 16; ++h) {
             const int t = g0 + h;
-            k_s[t * NTH + tid] = kg[h];
             if (t < n) {
                 const float at = lane_value(ta, t), nut = lane_value(tnu, t);
                 const float irt = lane_value(tir, t);
                 const float pm = fmaf(at * at, P, nut);
-                pm_s[t * NTH + tid] = pm;
+                pms[t] = pm;
                 P = pm * rcp(fmaf(kg[h] * kg[h] * irt, pm, 1.f));
             }
         }
     }
-    // backward over the tokens, 16 at a time
+    // backward over the tokens, 16 at a time (every load of a group issued at
+    // its start; the gain's part of dk added to the memory part in registers)
     float al = 1.f, be = 0.f, Gv = 0.f;
     if constexpr (APPLY) Gv = act ? Gout[(bh * NC + c) * DK + i] : 0.f;
-    for (int g0 = C - 16; g0 >= 0; g0 -= 16) {
-        float dwg[16], hv[16], ha[16], hr[16];
 #pragma unroll
-        for (int h = 0; h < 16; ++h) dwg[h] = dW[(row0 + min(g0 + h, n - 1)) * DK + ic];
+    for (int g0 = C - 16; g0 >= 0; g0 -= 16) {
+        float kg[16], dwg[16], dkg[16], hv[16], ha[16], hr[16];
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+            const size_t o = (row0 + min(g0 + h, n - 1)) * DK + ic;
+            kg[h] = to_f<E>(k[o]);
+            dwg[h] = dW[o];
+            if constexpr (APPLY) dkg[h] = dk[o];
+        }
 #pragma unroll
         for (int h = 15; h >= 0; --h) {
             const int t = g0 + h;
@@ -709,7 +714,7 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
                 const float at = lane_value(ta, t), nut = lane_value(tnu, t);
                 const float irt = lane_value(tir, t), dit = lane_value(tdi, t);
                 const float sdt = lane_value(tsd, t);
-                const float kv = k_s[t * NTH + tid], pm = pm_s[t * NTH + tid];
+                const float kv = kg[h], pm = pms[t];
                 const float b = kv * kv * irt;
                 const float Pt = pm * rcp(fmaf(b, pm, 1.f));
                 const float rat = Pt * rcp(pm), c2 = rat * rat;
@@ -717,8 +722,7 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
                 if constexpr (APPLY) {
                     const float H = fmaf(c2, Gv, gainP);
                     const float db = -Gv * Pt * Pt;
-                    pm_s[t * NTH + tid] =
-                        pm * dit * (dwg[h] - 2.f * kv * sdt) + db * 2.f * kv * irt;
+                    dkg[h] += pm * dit * (dwg[h] - 2.f * kv * sdt) + db * 2.f * kv * irt;
                     if (act) {
                         hv[h] = H;
                         ha[h] = 2.f * (pm - nut) * H / at;
@@ -732,6 +736,11 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
             }
         }
         if constexpr (APPLY) {
+            if (act) {
+#pragma unroll
+                for (int h = 0; h < 16; ++h)
+                    if (g0 + h < n) dk[(row0 + g0 + h) * DK + i] = dkg[h];
+            }
             // per-token sums over the key dimensions of these 16 tokens
             float sv = transpose_sum16(hv, lane), sa = transpose_sum16(ha, lane),
                   sr = transpose_sum16(hr, lane);
@@ -751,8 +760,6 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
     if constexpr (!APPLY) {
         if (act) ab[(bh * NC + c) * DK + i] = make_float2(al, be);
     } else {
-        if (act)
-            for (int t = 0; t < n; ++t) dk[(row0 + t) * DK + i] += pm_s[t * NTH + tid];
         __syncthreads();
         if (tid < n) {
             const size_t o = row0 + tid;

@@ -908,13 +908,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     // the two sets alternate roles from chunk to chunk
     // (Sc: the state at every chunk start, kept for the backward pass)
     for (int c = 0; c < NC; c += 2) {
-        if (Sc) state_save<E, DK, DVT, C>(accS, Sc + ((bh * NC + c) * DV + j0) * DK, wave, lane);
+        if (Sc) state_copy_out<E, DK, DVT, C>(L.S, Sc + ((bh * NC + c) * DV + j0) * DK, tid);
         state_chunk<E, DK, DVT, C>(A, L, accS, c, pkA, pqA, pwA, pvA, ptA, pgA, pkB, pqB, pwB,
                                    pvB, ptB, pgB);
         if (c + 1 < NC) {
             if (Sc)
-                state_save<E, DK, DVT, C>(accS, Sc + ((bh * NC + c + 1) * DV + j0) * DK, wave,
-                                          lane);
+                state_copy_out<E, DK, DVT, C>(L.S, Sc + ((bh * NC + c + 1) * DV + j0) * DK, tid);
             state_chunk<E, DK, DVT, C>(A, L, accS, c + 1, pkB, pqB, pwB, pvB, ptB, pgB, pkA, pqA,
                                        pwA, pvA, ptA, pgA);
         }

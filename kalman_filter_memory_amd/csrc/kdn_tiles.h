@@ -323,26 +323,19 @@ __device__ __forceinline__ float transpose_sum16(float (&v)[16], int lane) {
     return v[0];
 }
 
-// S^T blocks of the state -> global rows S[j][i] (row stride DK) in the input
-// dtype, from dst = the tile's first row
+// The LDS operand copy of the state, S[j][i] (DVT rows of stride LDK), to
+// global rows of stride DK with 16-byte stores (whole rows per 16-lane group)
 template <typename E, int DK, int DVT, int C>
-__device__ __forceinline__ void state_save(const StateAcc<E, DK, DVT, C>& accS, E* dst, int wave,
-                                           int lane) {
+__device__ __forceinline__ void state_copy_out(const E* sS, E* dst, int tid) {
     using G = StateCfg<E, DK, DVT, C>;
+    constexpr int VPR = DK / G::VEC, NV = DVT * VPR;
 #pragma unroll
-    for (int x = 0; x < G::SPW; ++x) {
-        const int job = wave + G::NW * x;
-        if (job < G::NSJ) {
-            const int ib = (job / G::NVB) * G::BI, jb = (job % G::NVB) * G::BV;
-#pragma unroll
-            for (int bi = 0; bi < G::BI; ++bi)
-#pragma unroll
-                for (int bv = 0; bv < G::BV; ++bv) {
-                    const int i = 16 * (ib + bi) + 4 * (lane >> 4);
-                    const int j = 16 * (jb + bv) + (lane & 15);
-                    const floatx4 sv = accS[x][bi][bv];
-                    store4<E>(dst + j * DK + i, sv[0], sv[1], sv[2], sv[3]);
-                }
+    for (int x = 0; x < (NV + G::THREADS - 1) / G::THREADS; ++x) {
+        const int e = tid + G::THREADS * x;
+        if (NV % G::THREADS == 0 || e < NV) {
+            const int j = e / VPR, c0 = (e % VPR) * G::VEC;
+            *reinterpret_cast<u32x4*>(dst + j * DK + c0) =
+                *reinterpret_cast<const u32x4*>(sS + j * G::LDK + c0);
         }
     }
 }
