@@ -60,53 +60,69 @@ __device__ __forceinline__ void tri_pair(int j, int& tt, int& ss) {
 }
 
 // ROWS x COLS of E from global rows of stride gld into LDS rows of stride sld
-// with 16-byte vectors; rows >= n are zero (their loads repeat row n - 1)
+// with 16-byte vectors, in two steps through registers: the loads (rows >= n
+// repeat row n - 1) issued ahead of the work they overlap, the stores (rows
+// >= n zero) when the LDS buffer is free again.
+template <typename E, int ROWS, int COLS> struct RegTile {
+    static constexpr int V = Vec16<E>::N, VPR = COLS / V, NV = ROWS * VPR;
+    static constexpr int IT = (NV + kBThreads - 1) / kBThreads;
+};
+template <typename E, int ROWS, int COLS> using TileRegs = u32x4[RegTile<E, ROWS, COLS>::IT];
 template <typename E, int ROWS, int COLS>
-__device__ __forceinline__ void stage_tile(E* dst, int sld, const E* src, size_t gld, int n,
-                                           int tid) {
-    constexpr int V = Vec16<E>::N, VPR = COLS / V, NV = ROWS * VPR;
-    constexpr int IT = (NV + kBThreads - 1) / kBThreads;
-    u32x4 val[IT];
+__device__ __forceinline__ void tile_load(TileRegs<E, ROWS, COLS>& r, const E* src,
+                                          size_t gld, int n, int tid) {
+    using TT = RegTile<E, ROWS, COLS>;
 #pragma unroll
-    for (int x = 0; x < IT; ++x) {
+    for (int x = 0; x < TT::IT; ++x) {
         const int e = tid + kBThreads * x;
-        if (NV % kBThreads == 0 || e < NV) {
-            const int t = e / VPR, c0 = (e % VPR) * V;
-            val[x] = *reinterpret_cast<const u32x4*>(src + min(t, n - 1) * gld + c0);
-        }
-    }
-#pragma unroll
-    for (int x = 0; x < IT; ++x) {
-        const int e = tid + kBThreads * x;
-        if (NV % kBThreads == 0 || e < NV) {
-            const int t = e / VPR, c0 = (e % VPR) * V;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(dst + t * sld + c0) = t < n ? val[x] : z;
+        if (TT::NV % kBThreads == 0 || e < TT::NV) {
+            const int t = e / TT::VPR, c0 = (e % TT::VPR) * TT::V;
+            r[x] = *reinterpret_cast<const u32x4*>(src + min(t, n - 1) * gld + c0);
         }
     }
 }
-
-// the same from fp32 global rows, converted to E
 template <typename E, int ROWS, int COLS>
-__device__ __forceinline__ void stage_tile_f32(E* dst, int sld, const float* src, size_t gld,
-                                               int n, int tid) {
-    constexpr int VPR = COLS / 4, NV = ROWS * VPR;
-    constexpr int IT = (NV + kBThreads - 1) / kBThreads;
-    float4 val[IT];
+__device__ __forceinline__ void tile_store(E* dst, int sld, const TileRegs<E, ROWS, COLS>& r,
+                                           int n, int tid) {
+    using TT = RegTile<E, ROWS, COLS>;
 #pragma unroll
-    for (int x = 0; x < IT; ++x) {
+    for (int x = 0; x < TT::IT; ++x) {
         const int e = tid + kBThreads * x;
-        if (NV % kBThreads == 0 || e < NV) {
-            const int t = e / VPR, c0 = (e % VPR) * 4;
-            val[x] = *reinterpret_cast<const float4*>(src + min(t, n - 1) * gld + c0);
+        if (TT::NV % kBThreads == 0 || e < TT::NV) {
+            const int t = e / TT::VPR, c0 = (e % TT::VPR) * TT::V;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(dst + t * sld + c0) = t < n ? r[x] : z;
         }
     }
+}
+template <int ROWS, int COLS> struct RegFTile {
+    static constexpr int VPR = COLS / 4, NV = ROWS * VPR;
+    static constexpr int IT = (NV + kBThreads - 1) / kBThreads;
+};
+template <int ROWS, int COLS> using FTileRegs = float4[RegFTile<ROWS, COLS>::IT];
+template <int ROWS, int COLS>
+__device__ __forceinline__ void ftile_load(FTileRegs<ROWS, COLS>& r, const float* src,
+                                           size_t gld, int n, int tid) {
+    using TT = RegFTile<ROWS, COLS>;
 #pragma unroll
-    for (int x = 0; x < IT; ++x) {
+    for (int x = 0; x < TT::IT; ++x) {
         const int e = tid + kBThreads * x;
-        if (NV % kBThreads == 0 || e < NV) {
-            const int t = e / VPR, c0 = (e % VPR) * 4;
-            const float4 v = t < n ? val[x] : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (TT::NV % kBThreads == 0 || e < TT::NV) {
+            const int t = e / TT::VPR, c0 = (e % TT::VPR) * 4;
+            r[x] = *reinterpret_cast<const float4*>(src + min(t, n - 1) * gld + c0);
+        }
+    }
+}
+template <typename E, int ROWS, int COLS>
+__device__ __forceinline__ void ftile_store(E* dst, int sld, const FTileRegs<ROWS, COLS>& r,
+                                            int n, int tid) {
+    using TT = RegFTile<ROWS, COLS>;
+#pragma unroll
+    for (int x = 0; x < TT::IT; ++x) {
+        const int e = tid + kBThreads * x;
+        if (TT::NV % kBThreads == 0 || e < TT::NV) {
+            const int t = e / TT::VPR, c0 = (e % TT::VPR) * 4;
+            const float4 v = t < n ? r[x] : make_float4(0.f, 0.f, 0.f, 0.f);
             store4<E>(dst + t * sld + c0, v.x, v.y, v.z, v.w);
         }
     }
@@ -398,10 +414,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const size_t row0 = bh * T + (size_t)c * C;
     const size_t cidx = bh * NC + c;
 
-    stage_tile<E, C, DK>(L.K, LDK, k + row0 * DK, DK, n, tid);
-    stage_tile<E, C, DK>(L.Q, LDK, q + row0 * DK, DK, n, tid);
-    stage_tile<E, C, DK>(L.W, LDK, w + row0 * DK, DK, n, tid);
-    stage_tile<E, C, C>(L.Tt, LDC, Tm + cidx * C * C, C, C, tid);
+    // every load of the chunk operands and of the first slice at once; the next
+    // slice is loaded while the current one is worked on
+    u32x4 rs[RegTile<E, JT, DK>::IT], rds[RegTile<E, JT, DK>::IT], rv[RegTile<E, C, JT>::IT],
+        ro[RegTile<E, C, JT>::IT];
+    float4 rr[RegFTile<C, JT>::IT];
+    auto load_slice = [&](int j0) {
+        tile_load<E, JT, DK>(rs, Sc + (cidx * DV + j0) * DK, DK, JT, tid);
+        tile_load<E, JT, DK>(rds, dSe + (cidx * DV + j0) * DK, DK, JT, tid);
+        tile_load<E, C, JT>(rv, v + row0 * DV + j0, DV, n, tid);
+        tile_load<E, C, JT>(ro, dO + row0 * DV + j0, DV, n, tid);
+        ftile_load<C, JT>(rr, dR + row0 * DV + j0, DV, n, tid);
+    };
+    auto store_slice = [&]() {
+        tile_store<E, JT, DK>(L.Sj, LDK, rs, JT, tid);
+        tile_store<E, JT, DK>(L.dSj, LDK, rds, JT, tid);
+        tile_store<E, C, JT>(L.R, LDJ, rv, n, tid);
+        tile_store<E, C, JT>(L.dO, LDJ, ro, n, tid);
+        ftile_store<E, C, JT>(L.dR, LDJ, rr, n, tid);
+    };
+    {
+        u32x4 rk[RegTile<E, C, DK>::IT], rq[RegTile<E, C, DK>::IT], rw[RegTile<E, C, DK>::IT],
+            rt[RegTile<E, C, C>::IT];
+        tile_load<E, C, DK>(rk, k + row0 * DK, DK, n, tid);
+        tile_load<E, C, DK>(rq, q + row0 * DK, DK, n, tid);
+        tile_load<E, C, DK>(rw, w + row0 * DK, DK, n, tid);
+        tile_load<E, C, C>(rt, Tm + cidx * C * C, C, C, tid);
+        load_slice(0);
+        tile_store<E, C, DK>(L.K, LDK, rk, n, tid);
+        tile_store<E, C, DK>(L.Q, LDK, rq, n, tid);
+        tile_store<E, C, DK>(L.W, LDK, rw, n, tid);
+        tile_store<E, C, C>(L.Tt, LDC, rt, C, tid);
+    }
+    store_slice();
     if (tid < C) {
         const float gv = gin[cidx * C + tid], gC = gin[cidx * C + C - 1];
         L.g[tid] = gv;
@@ -429,13 +474,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
     float xc = 0.f;
 
+    sync_lds();
     for (int j0 = 0; j0 < DV; j0 += JT) {
-        stage_tile<E, JT, DK>(L.Sj, LDK, Sc + (cidx * DV + j0) * DK, DK, JT, tid);
-        stage_tile<E, JT, DK>(L.dSj, LDK, dSe + (cidx * DV + j0) * DK, DK, JT, tid);
-        stage_tile<E, C, JT>(L.R, LDJ, v + row0 * DV + j0, DV, n, tid);
-        stage_tile<E, C, JT>(L.dO, LDJ, dO + row0 * DV + j0, DV, n, tid);
-        stage_tile_f32<E, C, JT>(L.dR, LDJ, dR + row0 * DV + j0, DV, n, tid);
-        sync_lds();
+        const bool more = j0 + JT < DV;
+        if (more) load_slice(j0 + JT);
         // R = V - diag(gamma) K S^T, in place
 #pragma unroll
         for (int x = 0; x < XPW; ++x) {
@@ -507,6 +549,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             }
         }
         sync_lds();
+        if (more) {
+            store_slice();
+            sync_lds();
+        }
     }
 
     // xc: <dS', S> over the whole chunk state
@@ -781,11 +827,18 @@ __global__ void bgain_carry_kernel(const float2* __restrict__ ab,
     const int i = idx % DK;
     const float lT = lam_chunk[(bh * (NC + 1) + NC) * DK + i];
     float G = dlambda_T ? -dlambda_T[idx] * lT * lT : 0.f;
-    for (int c = NC - 1; c >= 0; --c) {
-        const size_t o = (bh * NC + c) * DK + i;
-        Gout[o] = G;
-        const float2 m = ab[o];
-        G = fmaf(m.x, G, m.y);
+    // eight chunk maps loaded at a time, so the chain waits once per eight
+    for (int c8 = NC - 1; c8 >= 0; c8 -= 8) {
+        float2 m[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m[u] = ab[(bh * NC + max(c8 - u, 0)) * DK + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (c8 - u >= 0) {
+                Gout[(bh * NC + c8 - u) * DK + i] = G;
+                G = fmaf(m[u].x, G, m[u].y);
+            }
+        }
     }
     if (dlambda0) {
         const float l0 = lam_chunk[bh * (NC + 1) * DK + i];
