@@ -239,21 +239,21 @@ def algorithmic_backward(B, H, T, dk, dv, C):
         "scan_reduce": fby["scan_reduce"],
         "scan_carry": fby["scan_carry"] - bh * dk * 4,  # no lambda_T
         "chunk_prep": fby["chunk_prep"] + n * 4,
-        "chunk_state": fby["chunk_state"] + states,
+        "chunk_state": fby["chunk_state"] + states - n * dv * e,  # no read-out
         # read q, k, w, dO, T, g, dS_T; write dv (= dR, f32), the chunk-end
         # adjoints (bf16) and dS0
         "bwd_state": n * (3 * dk + dv) * e + bh * nc * C * C * e + n * 4 + bh * dv * dk * 4
         + n * dv * 4 + states + bh * dv * dk * 4,
-        # read q, k, w, v, dO, dR, T, g and both chunk states; write dq, dk, dW
-        # (f32), s and d(ln a)
+        # read q, k, w, v, dO, dR, T, g and both chunk states; write dq, dk
+        # (f32), dW (bf16), s and d(ln a)
         "bwd_grad": n * (3 * dk + 2 * dv) * e + n * dv * 4 + bh * nc * C * C * e + n * 4
-        + 2 * states + 3 * n * dk * 4 + 2 * n * 4,
+        + 2 * states + 2 * n * dk * 4 + n * dk * e + 2 * n * 4,
         # map pass: k, dW, gates, 1/D, s, boundary precisions -> chunk maps;
         # carry; apply pass: the same plus d(ln a), G, dk read and written,
         # da, dnu, dr
-        "bwd_gain": (n * dk * (e + 4) + n * (g + 8) + bh * nc * dk * (4 + 8))
+        "bwd_gain": (n * dk * 2 * e + n * (g + 8) + bh * nc * dk * (4 + 8))
         + bh * nc * dk * (8 + 4)
-        + (n * dk * (e + 4) + n * (g + 12) + bh * nc * dk * 8 + 2 * n * dk * 4 + 3 * n * 4),
+        + (n * dk * 2 * e + n * (g + 12) + bh * nc * dk * 8 + 2 * n * dk * 4 + 3 * n * 4),
     }
     fl = {
         "scan_reduce": ffl["scan_reduce"], "scan_carry": ffl["scan_carry"],

@@ -93,7 +93,8 @@ ForwardWs forward_ws(const kdn_desc* d) {
 }
 
 // backward workspace: the forward's, then [1/D | chunk-start states |
-// chunk-end adjoints | dW | s | d(ln a) | chunk maps (float2) | G at chunk ends]
+// chunk-end adjoints | dW (qkv dtype) | s | d(ln a) | chunk maps (float2) |
+// G at chunk ends]
 struct BackwardWs {
     ForwardWs f;
     size_t dinv, Sc, dSe, dW, sdot, dlna, ab, Gout, total;
@@ -110,7 +111,7 @@ BackwardWs backward_ws(const kdn_desc* d) {
     b.Sc = b.dinv + round_up(n * 4);
     b.dSe = b.Sc + round_up(states);
     b.dW = b.dSe + round_up(states);
-    b.sdot = b.dW + round_up(n * s.dk * 4);
+    b.sdot = b.dW + round_up(n * s.dk * esize(d->qkv_dtype));
     b.dlna = b.sdot + round_up(n * 4);
     b.ab = b.dlna + round_up(n * 4);
     b.Gout = b.ab + round_up(per_dim * 8);
@@ -243,7 +244,7 @@ kdn_status kdn_backward_events(const kdn_desc* d, const void* q, const void* k, 
     b.w = wk; b.Tm = tm; b.g = g; b.lam_chunk = lc; b.dinv = dinv;
     b.Sc = at(ws, w.Sc);
     b.dSe = at(ws, w.dSe);
-    b.dW = reinterpret_cast<float*>(at(ws, w.dW));
+    b.dW = at(ws, w.dW);
     b.sdot = reinterpret_cast<float*>(at(ws, w.sdot));
     b.dlna = reinterpret_cast<float*>(at(ws, w.dlna));
     b.ab = reinterpret_cast<float*>(at(ws, w.ab));
@@ -258,8 +259,8 @@ kdn_status kdn_backward_events(const kdn_desc* d, const void* q, const void* k, 
         }
         kdn::launch_timing() = t;
     };
-    // forward recompute, keeping 1/D of every token and the chunk-start states;
-    // its read-out goes to dv, which the reverse pass overwrites
+    // forward recompute, keeping 1/D of every token and the chunk-start states
+    // (no read-out)
     timed(0);
     hipError_t e = kdn::launch_scan_reduce(s, k, a, qnoise, r, agg, hs);
     timed(1);
@@ -271,7 +272,7 @@ kdn_status kdn_backward_events(const kdn_desc* d, const void* q, const void* k, 
         e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, g, hs, dinv);
     timed(3);
     if (e == hipSuccess)
-        e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, dv, nullptr, hs, at(ws, w.Sc));
+        e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, nullptr, nullptr, hs, at(ws, w.Sc));
     timed(4);
     if (e == hipSuccess) e = kdn::launch_bwd_state(s, b, hs);
     timed(5);

@@ -128,6 +128,24 @@ __device__ __forceinline__ void ftile_store(E* dst, int sld, const FTileRegs<ROW
     }
 }
 
+// dot product of two 16-byte vectors of E
+template <typename E> __device__ __forceinline__ float dot16(u32x4 x, u32x4 y);
+template <> __device__ __forceinline__ float dot16<float>(u32x4 x, u32x4 y) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = fmaf(__uint_as_float(x[j]), __uint_as_float(y[j]), s);
+    return s;
+}
+template <> __device__ __forceinline__ float dot16<bf16_t>(u32x4 x, u32x4 y) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        s = fmaf(__uint_as_float(x[j] << 16), __uint_as_float(y[j] << 16), s);
+        s = fmaf(__uint_as_float(x[j] & 0xFFFF0000u), __uint_as_float(y[j] & 0xFFFF0000u), s);
+    }
+    return s;
+}
+
 // sum over the 16 lanes of each 16-lane group (lanes sharing the rows of an
 // MFMA result tile)
 __device__ __forceinline__ float group16_sum(float x) {
@@ -398,7 +416,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const E* __restrict__ dO, const float* __restrict__ dR, const E* __restrict__ w,
     const E* __restrict__ Tm, const float* __restrict__ gin, const E* __restrict__ Sc,
     const E* __restrict__ dSe, float* __restrict__ dq, float* __restrict__ dk,
-    float* __restrict__ dW, float* __restrict__ sdot_out, float* __restrict__ dlna, int T, int DV,
+    E* __restrict__ dW, float* __restrict__ sdot_out, float* __restrict__ dlna, int T, int DV,
     int NC) {
     using LL = BGradLds<E, DK, C, JT>;
     constexpr int LDK = LL::LDK, LDC = LL::LDC, LDJ = LL::LDJ;
@@ -426,7 +444,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         tile_load<E, C, JT>(ro, dO + row0 * DV + j0, DV, n, tid);
         ftile_load<C, JT>(rr, dR + row0 * DV + j0, DV, n, tid);
     };
+    float xc = 0.f;  // <dS', S> over the chunk state, from the staged registers
     auto store_slice = [&]() {
+#pragma unroll
+        for (int x = 0; x < RegTile<E, JT, DK>::IT; ++x) {
+            const int e = tid + kBThreads * x;
+            if (RegTile<E, JT, DK>::NV % kBThreads == 0 || e < RegTile<E, JT, DK>::NV)
+                xc += dot16<E>(rs[x], rds[x]);
+        }
         tile_store<E, JT, DK>(L.Sj, LDK, rs, JT, tid);
         tile_store<E, JT, DK>(L.dSj, LDK, rds, JT, tid);
         tile_store<E, C, JT>(L.R, LDJ, rv, n, tid);
@@ -472,7 +497,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         am[x] = floatx4{0.f, 0.f, 0.f, 0.f};
         aa[x] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    float xc = 0.f;
 
     sync_lds();
     for (int j0 = 0; j0 < DV; j0 += JT) {
@@ -518,10 +542,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                         L.U[t * LDJ + 16 * (jb + b) + (lane & 15)] = from_f<E>(au[0][b][e]);
                     }
             }
-        }
-        for (int e = tid; e < JT * DK; e += kBThreads) {
-            const int jr = e / DK, i = e % DK;
-            xc += to_f<E>(L.dSj[jr * LDK + i]) * to_f<E>(L.Sj[jr * LDK + i]);
         }
         sync_lds();
         // dM += dO U^T, dA' += dR U^T (negated later); dO S, dR S, U dS'
@@ -652,12 +672,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
                 for (int b = 0; b < BKI; ++b) {
                     const int i = 16 * (ib + b) + (lane & 15);
-                    sd += aw[x][0][b][e] * to_f<E>(L.W[t * LDK + i]);
+                    // s_t from dW as the gain pass will read it (input dtype)
+                    const E dw = from_f<E>(aw[x][0][b][e]);
+                    sd += to_f<E>(dw) * to_f<E>(L.W[t * LDK + i]);
                     if (t < n) {
                         const size_t o = (row0 + t) * DK + i;
                         dq[o] = aq[x][0][b][e];
                         dk[o] = ak[x][0][b][e];
-                        dW[o] = aw[x][0][b][e];
+                        dW[o] = dw;
                     }
                 }
                 sd = group16_sum(sd);
@@ -695,7 +717,7 @@ template <typename E, typename G, int DK, int C, bool APPLY>
 __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
     const E* __restrict__ k, const G* __restrict__ a, const G* __restrict__ nu,
     const G* __restrict__ r, const float* __restrict__ lam_chunk, const float* __restrict__ dinv,
-    const float* __restrict__ sdot, const float* __restrict__ dW, const float* __restrict__ dlna,
+    const float* __restrict__ sdot, const E* __restrict__ dW, const float* __restrict__ dlna,
     const float* __restrict__ Gout, float2* __restrict__ ab, float* __restrict__ dk,
     float* __restrict__ da, float* __restrict__ dnu, float* __restrict__ dr, int T, int NC) {
     __shared__ float red[3][C];  // per token: sum_i H, sum_i 2 a P_prev H, sum_i G P^2 b/r
@@ -747,7 +769,7 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
         for (int h = 0; h < 16; ++h) {
             const size_t o = (row0 + min(g0 + h, n - 1)) * DK + ic;
             kg[h] = to_f<E>(k[o]);
-            dwg[h] = dW[o];
+            dwg[h] = to_f<E>(dW[o]);
             if constexpr (APPLY) dkg[h] = dk[o];
         }
 #pragma unroll
@@ -877,8 +899,8 @@ hipError_t bgrad_t(const Shape& s, const BwdArgs& b, hipStream_t st) {
                  static_cast<const E*>(b.q), static_cast<const E*>(b.k),
                  static_cast<const E*>(b.v), static_cast<const E*>(b.dO), b.dv,
                  static_cast<const E*>(b.w), static_cast<const E*>(b.Tm), b.g,
-                 static_cast<const E*>(b.Sc), static_cast<const E*>(b.dSe), b.dq, b.dk, b.dW,
-                 b.sdot, b.dlna, s.T, s.dv, s.nc);
+                 static_cast<const E*>(b.Sc), static_cast<const E*>(b.dSe), b.dq, b.dk,
+                 static_cast<E*>(b.dW), b.sdot, b.dlna, s.T, s.dv, s.nc);
         return hipGetLastError();
     } else {
         return hipErrorInvalidValue;
@@ -902,7 +924,8 @@ hipError_t bgain_t(const Shape& s, const BwdArgs& b, hipStream_t st) {
     launch_timing() = LaunchTiming{tm.start, nullptr};
     launch_k((bgain_kernel<E, G, DK, C, false>), grid, dim3(NTH), 0, st,
              static_cast<const E*>(b.k), static_cast<const G*>(b.a), static_cast<const G*>(b.nu),
-             static_cast<const G*>(b.r), b.lam_chunk, b.dinv, b.sdot, b.dW, b.dlna, b.Gout,
+             static_cast<const G*>(b.r), b.lam_chunk, b.dinv, b.sdot,
+             static_cast<const E*>(b.dW), b.dlna, b.Gout,
              reinterpret_cast<float2*>(b.ab), b.dk, b.da, b.dnu, b.dr, s.T, s.nc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -915,7 +938,8 @@ hipError_t bgain_t(const Shape& s, const BwdArgs& b, hipStream_t st) {
     launch_timing() = LaunchTiming{nullptr, tm.stop};
     launch_k((bgain_kernel<E, G, DK, C, true>), grid, dim3(NTH), 0, st,
              static_cast<const E*>(b.k), static_cast<const G*>(b.a), static_cast<const G*>(b.nu),
-             static_cast<const G*>(b.r), b.lam_chunk, b.dinv, b.sdot, b.dW, b.dlna, b.Gout,
+             static_cast<const G*>(b.r), b.lam_chunk, b.dinv, b.sdot,
+             static_cast<const E*>(b.dW), b.dlna, b.Gout,
              reinterpret_cast<float2*>(b.ab), b.dk, b.da, b.dnu, b.dr, s.T, s.nc);
     return hipGetLastError();
 }

@@ -820,7 +820,8 @@ __device__ __forceinline__ void state_chunk(
                                  lane);
             const int t = 16 * tb + (lane & 15);
             E* orow = A.o + (row0 + t) * A.DV + A.j0 + 16 * jb;
-            store8x2_if<E>(t < n, orow, orow + 16, accY[x][0][0], accY[x][1][0], lane);
+            // (o is NULL when the backward recomputes the forward for its states)
+            store8x2_if<E>(t < n && A.o, orow, orow + 16, accY[x][0][0], accY[x][1][0], lane);
         }
     }
 #pragma unroll

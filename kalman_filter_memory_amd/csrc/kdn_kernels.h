@@ -65,6 +65,7 @@ hipError_t launch_chunk_prep(const Shape& s, bool fuse_gain, const void* k, cons
 // Sequential chunk pass: memory write and read-out (g from the prep pass).
 // Sc (may be NULL): the state at every chunk start, [BH][nc][dv][dk] in qkv
 // dtype, kept for the backward pass.
+// o may be NULL (not written) when only Sc is wanted.
 hipError_t launch_chunk_state(const Shape& s, const void* q, const void* k, const void* v,
                               const float* g, const void* w, const void* Tm, const float* S0,
                               void* o, float* S_T, hipStream_t st, void* Sc = nullptr);
@@ -83,7 +84,8 @@ struct BwdArgs {
     const float *g, *lam_chunk, *dinv;   // log2 decays, boundary precisions, 1/D
     const void* Sc;                      // state at every chunk start (qkv dtype)
     void* dSe;                           // state adjoint at every chunk end (qkv dtype)
-    float *dW, *sdot, *dlna;             // dW [BH][T][dk]; s_t and d(ln a_t) [BH][T]
+    void* dW;                            // dW [BH][T][dk], qkv dtype
+    float *sdot, *dlna;                  // s_t and d(ln a_t) [BH][T]
     float *ab, *Gout;                    // per (chunk, dim): float2 map, G at the chunk end
     float *dq, *dk, *dv, *da, *dnu, *dr;  // outputs
     float *dlambda0, *dS0;               // outputs, may be NULL

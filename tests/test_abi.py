@@ -126,9 +126,9 @@ def test_backward_host_side_checks(lib):
     need = kdn.backward_workspace_bytes(d)
     bh, nc, n = 128, 64, 8 * 16 * 4096
     # forward workspace, then 1/D, chunk-start states and chunk-end adjoints
-    # (bf16), dW, s, d(ln a), chunk maps and G
+    # (bf16), dW (bf16), s, d(ln a), chunk maps and G
     states = bh * nc * 128 * 128 * 2
-    expect = (kdn.forward_workspace_bytes(d) + n * 4 + 2 * states + n * 128 * 4 + 2 * n * 4
+    expect = (kdn.forward_workspace_bytes(d) + n * 4 + 2 * states + n * 128 * 2 + 2 * n * 4
               + bh * nc * 128 * 12)
     assert expect <= need <= expect + 9 * 256
     iso = _desc(B=1, H=1, T=16, d_k=32, d_v=32, chunk=16)
