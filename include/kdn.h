@@ -165,7 +165,7 @@ kdn_status kdn_decode_step(const kdn_desc *d, const void *q, const void *k, cons
  * the backward does not support it).  Host-only. */
 size_t kdn_backward_workspace_bytes(const kdn_desc *d);
 
-/* Backward pass of kdn_forward (diagonal variant): the gradient of
+/* Backward pass of kdn_forward (both variants): the gradient of
  *     L = <dO, o> + <dS_T, S_T> + <dlambda_T, lambda_T>
  * with respect to every input, as training the layer needs ("Kalman Delta
  * Networks", English abstract: the variants are pretrained inside language
@@ -173,15 +173,15 @@ size_t kdn_backward_workspace_bytes(const kdn_desc *d);
  * recomputed from the inputs (nothing is kept between the two calls).
  *   Inputs as kdn_forward (same descriptor, same q, k, v, a, qnoise, r,
  *   lambda0, S0); dO [B,H,T,d_v] in qkv_dtype; dS_T [B,H,d_v,d_k] and
- *   dlambda_T [B,H,d_k] float32 or NULL (zero).
+ *   dlambda_T (shaped like lambda0) float32 or NULL (zero).
  *   Outputs, float32 whatever the input dtypes: dq, dk [B,H,T,d_k];
- *   dv [B,H,T,d_v]; da, dqnoise, dr [B,H,T]; dlambda0 [B,H,d_k] and
+ *   dv [B,H,T,d_v]; da, dqnoise, dr [B,H,T]; dlambda0 (like lambda0) and
  *   dS0 [B,H,d_v,d_k] (either may be NULL to skip it; they are the gradient
  *   at the given lambda0 / S0, or at ones / zeros when those are NULL).
  *   No output may alias an input.  ws: at least
  *   kdn_backward_workspace_bytes(d) bytes, 16-byte aligned, contents ignored.
- * Returns KDN_ERR_UNSUPPORTED for the isotropic variant and for shapes the
- * chunk kernels do not take (kdn_backward_workspace_bytes returns 0). */
+ * Returns KDN_ERR_UNSUPPORTED for shapes the chunk kernels do not take
+ * (kdn_backward_workspace_bytes returns 0 for them). */
 kdn_status kdn_backward(const kdn_desc *d, const void *q, const void *k, const void *v,
                         const void *a, const void *qnoise, const void *r,
                         const float *lambda0, const float *S0, const void *dO,

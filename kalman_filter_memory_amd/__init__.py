@@ -14,7 +14,7 @@ Functions (same names as the C entry points):
   gain(k, r, lambda_minus, variant=..., gain_dtype=None) -> w
   chunk_delta(q, k, v, a, w, S0=None, chunk=64) -> (o, S_T)
   backward(q, k, v, a, qnoise, r, dO, lambda0=None, S0=None, dS_T=None, dlambda_T=None,
-           chunk=64) -> dict of float32 gradients (dq, dk, dv, da, dqnoise, dr,
+           variant="diagonal", chunk=64) -> dict of float32 gradients (dq, dk, dv, da, dqnoise, dr,
            dlambda0, dS0)
 """
 from __future__ import annotations
@@ -222,23 +222,25 @@ def backward_workspace_bytes(desc: KdnDesc) -> int:
 
 
 def backward(q, k, v, a, qnoise, r, dO, lambda0=None, S0=None, dS_T=None, dlambda_T=None,
-             chunk=64, workspace: torch.Tensor | None = None, out=None, events=None) -> dict:
-    """Gradients of <dO, o> + <dS_T, S_T> + <dlambda_T, lambda_T> (diagonal
-    variant) with respect to q, k, v, a, qnoise, r, lambda0 and S0, as float32
-    tensors in a dict (keys dq, dk, dv, da, dqnoise, dr, dlambda0, dS0).
+             variant="diagonal", chunk=64, workspace: torch.Tensor | None = None, out=None,
+             events=None) -> dict:
+    """Gradients of <dO, o> + <dS_T, S_T> + <dlambda_T, lambda_T> with respect
+    to q, k, v, a, qnoise, r, lambda0 and S0, as float32 tensors in a dict
+    (keys dq, dk, dv, da, dqnoise, dr, dlambda0, dS0).
 
     out: optional dict of preallocated outputs with those keys; events:
     optional list of 14 torch.cuda.Event (already recorded once), start and
     stop of the seven stages."""
     lib = load_library()
-    d = _forward_desc(q, k, v, a, qnoise, r, "diagonal", chunk)
+    d = _forward_desc(q, k, v, a, qnoise, r, variant, chunk)
     B, H, T, dk = k.shape
     dv = v.shape[-1]
+    lam_shape = (B, H, dk) if d.variant == DIAGONAL else (B, H)
     _gpu(dO, "dO")
     if dO.dtype != q.dtype or tuple(dO.shape) != (B, H, T, dv):
         raise ValueError("dO must be [B,H,T,d_v] in the dtype of q, k, v")
-    for name, x, shape in (("lambda0", lambda0, (B, H, dk)), ("S0", S0, (B, H, dv, dk)),
-                           ("dS_T", dS_T, (B, H, dv, dk)), ("dlambda_T", dlambda_T, (B, H, dk))):
+    for name, x, shape in (("lambda0", lambda0, lam_shape), ("S0", S0, (B, H, dv, dk)),
+                           ("dS_T", dS_T, (B, H, dv, dk)), ("dlambda_T", dlambda_T, lam_shape)):
         if x is not None:
             _gpu(x, name)
             if x.dtype != torch.float32 or tuple(x.shape) != shape:
@@ -246,7 +248,7 @@ def backward(q, k, v, a, qnoise, r, dO, lambda0=None, S0=None, dS_T=None, dlambd
     dev = k.device
     shapes = {"dq": (B, H, T, dk), "dk": (B, H, T, dk), "dv": (B, H, T, dv),
               "da": (B, H, T), "dqnoise": (B, H, T), "dr": (B, H, T),
-              "dlambda0": (B, H, dk), "dS0": (B, H, dv, dk)}
+              "dlambda0": lam_shape, "dS0": (B, H, dv, dk)}
     g = out if out is not None else {
         n: torch.empty(sh, dtype=torch.float32, device=dev) for n, sh in shapes.items()}
     need = lib.kdn_backward_workspace_bytes(ctypes.byref(d))

@@ -106,7 +106,7 @@ BackwardWs backward_ws(const kdn_desc* d) {
     b.f = forward_ws(d);
     const size_t n = (size_t)s.BH * s.T;
     const size_t states = (size_t)s.BH * s.nc * s.dv * s.dk * esize(d->qkv_dtype);
-    const size_t per_dim = (size_t)s.BH * s.nc * s.dk;
+    const size_t per_dim = (size_t)s.BH * s.nc * (s.diag ? s.dk : 1);
     b.dinv = b.f.total;
     b.Sc = b.dinv + round_up(n * 4);
     b.dSe = b.Sc + round_up(states);
@@ -204,7 +204,7 @@ kdn_status kdn_forward_events(const kdn_desc* d, const void* q, const void* k, c
 }
 
 size_t kdn_backward_workspace_bytes(const kdn_desc* d) {
-    if (check_chunked(d) != KDN_OK || d->variant != KDN_DIAGONAL) return 0;
+    if (check_chunked(d) != KDN_OK) return 0;
     if (!kdn::backward_supported(make_shape(d))) return 0;
     return backward_ws(d).total;
 }
@@ -218,7 +218,6 @@ kdn_status kdn_backward_events(const kdn_desc* d, const void* q, const void* k, 
                                void* const* events) {
     kdn_status st = check_chunked(d);
     if (st != KDN_OK) return st;
-    if (d->variant != KDN_DIAGONAL) return KDN_ERR_UNSUPPORTED;
     const kdn::Shape s = make_shape(d);
     if (!kdn::backward_supported(s)) return KDN_ERR_UNSUPPORTED;
     const BackwardWs w = backward_ws(d);

@@ -1,4 +1,4 @@
-// kdn_bwd.hip -- backward pass of the chunkwise KDN layer (diagonal variant).
+// kdn_bwd.hip -- backward pass of the chunkwise KDN layer.
 //
 // Gradients of L = <dO, o> + <dS_T, S_T> + <dlambda_T, lambda_T> with respect
 // to q, k, v, a, nu, r, lambda0 and S0: what training the layer needs ("Kalman
@@ -22,7 +22,8 @@
 // and summed over the later tokens of the chunk to give d(ln a_t).
 // The gain and the precision recursion ("Kalman Delta Networks", English
 // abstract: Diagonal KDN, a Moebius-map uncertainty recurrence) are
-// differentiated in variance form, per key dimension i:
+// differentiated in variance form, per key dimension i (the isotropic
+// variant's single chain is described at bgain_iso_kernel):
 //   P^- = a^2 P + nu,  P = P^- / (1 + b P^-),  b = k_i^2 / r,
 //   w_i = P^-_i k_i / D,  D = r + sum_j k_j^2 P^-_j.
 // With G the adjoint of P after a token and s = sum_i dW_i w_i:
@@ -838,6 +839,116 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
     }
 }
 
+// Isotropic variant: one precision per head, so the recursion is one scalar
+// chain and every per-token quantity is a scalar; with kappa = |k|^2,
+// b = kappa / (d_k r), D = P^- kappa + r, w = P^- k / D and s = dW . w:
+//   H = s r / (P^- D) + G (P / P^-)^2,  dkappa = -P^- s / D - G P^2 / (d_k r),
+//   dk += dW P^- / D + 2 dkappa k,  dr = -s / D + G P^2 b / r,
+//   dnu = H,  da = d(ln a)/a + 2 a P_prev H,  G <- a^2 H.
+// One workgroup of 4 waves per chunk: kappa by all threads, the chain on wave 0
+// (lane t keeps token t), the dk update by all threads in 16-byte pieces.
+template <typename E, typename G, int DK, int C, bool APPLY>
+__global__ __launch_bounds__(256) void bgain_iso_kernel(
+    const E* __restrict__ k, const G* __restrict__ a, const G* __restrict__ nu,
+    const G* __restrict__ r, const float* __restrict__ lam_chunk, const float* __restrict__ sdot,
+    const E* __restrict__ dW, const float* __restrict__ dlna, const float* __restrict__ Gout,
+    float2* __restrict__ ab, float* __restrict__ dk, float* __restrict__ da,
+    float* __restrict__ dnu, float* __restrict__ dr, int T, int NC) {
+    __shared__ float skk[C], scA[C], scB[C];
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int c = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int n = min(C, T - c * C);
+    const size_t row0 = bh * T + (size_t)c * C;
+    // kappa_t, four threads per token
+    {
+        constexpr int V = Vec16<E>::N, PER = DK / 4;
+        const int t = tid >> 2, part = tid & 3;
+        float acc = 0.f;
+        if (t < C) {
+            const E* row = k + (row0 + min(t, n - 1)) * DK + part * PER;
+#pragma unroll
+            for (int j = 0; j < PER; j += V) {
+                const u32x4 x = *reinterpret_cast<const u32x4*>(row + j);
+                acc += dot16<E>(x, x);
+            }
+        }
+        acc += __shfl_xor(acc, 1, kWave);
+        acc += __shfl_xor(acc, 2, kWave);
+        if (t < C && part == 0) skk[t] = acc;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const size_t tk = row0 + min(lane, n - 1);
+        const float ta = to_f<G>(a[tk]), tnu = to_f<G>(nu[tk]), tr = to_f<G>(r[tk]);
+        const float tir = 1.f / tr, tsd = sdot[tk], tkk = skk[min(lane, C - 1)];
+        const float tb = tkk * tir * (1.f / static_cast<float>(DK));
+        // forward walk (the same on every lane); lane t keeps P^- of token t
+        float P = 1.f / lam_chunk[bh * (NC + 1) + c], pml = 1.f;
+#pragma unroll
+        for (int t = 0; t < C; ++t) {
+            if (t < n) {
+                const float at = lane_value(ta, t), pm = fmaf(at * at, P, lane_value(tnu, t));
+                if (lane == t) pml = pm;
+                P = pm * rcp(fmaf(lane_value(tb, t), pm, 1.f));
+            }
+        }
+        const float iD = 1.f / fmaf(pml, tkk, tr);
+        const float Pt = pml * rcp(fmaf(tb, pml, 1.f));
+        const float rat = Pt * rcp(pml), c2 = rat * rat;
+        const float gainP = tsd * tr * iD * rcp(pml);
+        if constexpr (!APPLY) {
+            float al = 1.f, be = 0.f;
+#pragma unroll
+            for (int t = C - 1; t >= 0; --t) {
+                if (t < n) {
+                    const float at = lane_value(ta, t), a2 = at * at;
+                    al = a2 * lane_value(c2, t) * al;
+                    be = a2 * fmaf(lane_value(c2, t), be, lane_value(gainP, t));
+                }
+            }
+            if (lane == 0) ab[bh * NC + c] = make_float2(al, be);
+        } else {
+            float Gv = Gout[bh * NC + c], Gl = 0.f;
+#pragma unroll
+            for (int t = C - 1; t >= 0; --t) {
+                if (t < n) {
+                    if (lane == t) Gl = Gv;
+                    const float at = lane_value(ta, t);
+                    Gv = at * at * fmaf(lane_value(c2, t), Gv, lane_value(gainP, t));
+                }
+            }
+            const float H = fmaf(c2, Gl, gainP), db = -Gl * Pt * Pt;
+            const float dkap = -pml * tsd * iD + db * tir * (1.f / static_cast<float>(DK));
+            if (lane < n) {
+                da[tk] = dlna[tk] / ta + 2.f * (pml - tnu) * H / ta;
+                dnu[tk] = H;
+                dr[tk] = -tsd * iD - db * tb * tir;
+                scA[lane] = pml * iD;
+                scB[lane] = 2.f * dkap;
+            }
+        }
+    }
+    if constexpr (APPLY) {
+        __syncthreads();
+        // dk += dW P^- / D + 2 dkappa k, four components at a time
+        for (int e = tid; e < n * (DK / 4); e += 256) {
+            const int t = e / (DK / 4), i0 = (e % (DK / 4)) * 4;
+            const size_t o = (row0 + t) * DK + i0;
+            float kv[4], wv[4];
+            load4<E>(k + o, kv);
+            load4<E>(dW + o, wv);
+            float4 d4 = *reinterpret_cast<const float4*>(dk + o);
+            const float A = scA[t], B = scB[t];
+            d4.x += fmaf(wv[0], A, B * kv[0]);
+            d4.y += fmaf(wv[1], A, B * kv[1]);
+            d4.z += fmaf(wv[2], A, B * kv[2]);
+            d4.w += fmaf(wv[3], A, B * kv[3]);
+            *reinterpret_cast<float4*>(dk + o) = d4;
+        }
+    }
+}
+
 // G_out of every chunk from the chunk maps, last chunk first; dlambda0 at the end
 __global__ void bgain_carry_kernel(const float2* __restrict__ ab,
                                    const float* __restrict__ lam_chunk,
@@ -944,6 +1055,30 @@ hipError_t bgain_t(const Shape& s, const BwdArgs& b, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <typename E, typename G, int DK, int C>
+hipError_t bgain_iso_t(const Shape& s, const BwdArgs& b, hipStream_t st) {
+    const dim3 grid(s.nc, s.BH);
+    const LaunchTiming tm = launch_timing();
+    launch_timing() = LaunchTiming{tm.start, nullptr};
+    launch_k((bgain_iso_kernel<E, G, DK, C, false>), grid, dim3(256), 0, st,
+             static_cast<const E*>(b.k), static_cast<const G*>(b.a), static_cast<const G*>(b.nu),
+             static_cast<const G*>(b.r), b.lam_chunk, b.sdot, static_cast<const E*>(b.dW),
+             b.dlna, b.Gout, reinterpret_cast<float2*>(b.ab), b.dk, b.da, b.dnu, b.dr, s.T, s.nc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bgain_carry_kernel, dim3((s.BH + 255) / 256), dim3(256), 0, st,
+                       reinterpret_cast<const float2*>(b.ab), b.lam_chunk, b.dlambda_T, b.Gout,
+                       b.dlambda0, s.BH, 1, s.nc);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch_timing() = LaunchTiming{nullptr, tm.stop};
+    launch_k((bgain_iso_kernel<E, G, DK, C, true>), grid, dim3(256), 0, st,
+             static_cast<const E*>(b.k), static_cast<const G*>(b.a), static_cast<const G*>(b.nu),
+             static_cast<const G*>(b.r), b.lam_chunk, b.sdot, static_cast<const E*>(b.dW),
+             b.dlna, b.Gout, reinterpret_cast<float2*>(b.ab), b.dk, b.da, b.dnu, b.dr, s.T, s.nc);
+    return hipGetLastError();
+}
+
 template <typename E>
 hipError_t bwd_state_e(const Shape& s, const BwdArgs& b, hipStream_t st) {
 #define KDN_BS(DK_, DVT_, C_)                                                          \
@@ -975,9 +1110,13 @@ hipError_t bwd_grad_e(const Shape& s, const BwdArgs& b, hipStream_t st) {
 template <typename E>
 hipError_t bwd_gain_e(const Shape& s, const BwdArgs& b, hipStream_t st) {
 #define KDN_BN(DK_, C_)                                                                \
-    if (s.dk == DK_ && s.chunk == C_)                                                  \
+    if (s.dk == DK_ && s.chunk == C_) {                                                \
+        if (!s.diag)                                                                   \
+            return s.gate_bf16 ? bgain_iso_t<E, bf16_t, DK_, C_>(s, b, st)             \
+                               : bgain_iso_t<E, float, DK_, C_>(s, b, st);             \
         return s.gate_bf16 ? bgain_t<E, bf16_t, DK_, C_>(s, b, st)                     \
-                           : bgain_t<E, float, DK_, C_>(s, b, st);
+                           : bgain_t<E, float, DK_, C_>(s, b, st);                     \
+    }
 #define KDN_BN_C(DK_) KDN_BN(DK_, 16) KDN_BN(DK_, 32) KDN_BN(DK_, 64)
     KDN_BN_C(32) KDN_BN_C(64) KDN_BN_C(128)
 #undef KDN_BN_C
@@ -1004,7 +1143,7 @@ bool bwd_supported_e(const Shape& s) {
 }  // namespace
 
 bool backward_supported(const Shape& s) {
-    if (!s.diag || !chunk_supported(s)) return false;
+    if (!chunk_supported(s)) return false;
     return s.qkv_bf16 ? bwd_supported_e<bf16_t>(s) : bwd_supported_e<float>(s);
 }
 
@@ -1022,10 +1161,10 @@ hipError_t launch_bwd_gain(const Shape& s, const BwdArgs& b, hipStream_t st) {
     if (s.BH == 0) return hipSuccess;
     if (s.nc == 0) {
         // no tokens: dlambda0 = dlambda_T (the carry over zero chunks)
-        const int n = s.BH * s.dk;
+        const int nl = s.diag ? s.dk : 1, n = s.BH * nl;
         hipLaunchKernelGGL(bgain_carry_kernel, dim3((n + 255) / 256), dim3(256), 0, st,
                            reinterpret_cast<const float2*>(b.ab), b.lam_chunk, b.dlambda_T,
-                           b.Gout, b.dlambda0, s.BH, s.dk, 0);
+                           b.Gout, b.dlambda0, s.BH, nl, 0);
         return hipGetLastError();
     }
     return s.qkv_bf16 ? bwd_gain_e<bf16_t>(s, b, st) : bwd_gain_e<float>(s, b, st);

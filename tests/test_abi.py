@@ -133,9 +133,11 @@ def test_backward_host_side_checks(lib):
     assert expect <= need <= expect + 9 * 256
     iso = _desc(B=1, H=1, T=16, d_k=32, d_v=32, chunk=16)
     iso.variant = kdn.ISOTROPIC
-    assert kdn.backward_workspace_bytes(iso) == 0
+    assert kdn.backward_workspace_bytes(iso) > 0
+    bad = _desc(d_k=48)
+    assert kdn.backward_workspace_bytes(bad) == 0
     args = [fake] * 19
-    assert lib.kdn_backward(ctypes.byref(iso), *args, ws, 1 << 40, None) == 3
+    assert lib.kdn_backward(ctypes.byref(bad), *args, ws, 1 << 40, None) == 3
     assert lib.kdn_backward(ctypes.byref(d), None, *args[1:], ws, need, None) == 1
     assert lib.kdn_backward(ctypes.byref(d), *args, ws, need - 1, None) == 4
     assert lib.kdn_backward(ctypes.byref(d), *args[:9], ctypes.c_void_p(0x1004), *args[10:],

@@ -1,4 +1,4 @@
-"""GPU parity of the backward pass (kdn_backward, diagonal variant) against the
+"""GPU parity of the backward pass (kdn_backward, both variants) against the
 fp64 oracle's vector-Jacobian product, through the C ABI.
 
 Every gradient is compared per (b, h) slice with the normwise metric of the
@@ -35,7 +35,7 @@ def _gpu_backward(inp, cot, chunk):
     dS_T = None if cot["dS_T"] is None else to_dev(cot["dS_T"], torch.float32)
     dl_T = None if cot["dlambda_T"] is None else to_dev(cot["dlambda_T"], torch.float32)
     g = kdn.backward(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], dO, t["lambda0"],
-                     t["S0"], dS_T, dl_T, chunk=chunk)
+                     t["S0"], dS_T, dl_T, variant=inp["variant"], chunk=chunk)
     torch.cuda.synchronize()
     return {n: host(g[KEYMAP.get(n, n)]) for n in GRADS}
 
@@ -43,7 +43,7 @@ def _gpu_backward(inp, cot, chunk):
 def _oracle_backward(inp, cot):
     return oracle.backward(inp["q"], inp["k"], inp["v"], inp["a"], inp["nu"], inp["r"],
                            cot["dO"], inp["lambda0"], inp["S0"], cot["dS_T"], cot["dlambda_T"],
-                           variant="diagonal")
+                           variant=inp["variant"])
 
 
 def _errors(got, ref, heads=None):
@@ -90,6 +90,36 @@ def test_backward_small_shapes(idx):
     _assert(_errors(got, _oracle_backward(inp, cot)), dtype)
 
 
+SMALL_ISO = [
+    # B, H, T, dk, dv, chunk, dtype
+    (1, 1, 1, 32, 32, 16, "f32"),
+    (2, 3, 37, 32, 64, 16, "f32"),
+    (2, 1, 130, 128, 128, 64, "bf16"),
+    (1, 3, 64, 32, 128, 64, "f32"),
+    (1, 2, 100, 64, 32, 32, "bf16"),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SMALL_ISO)),
+                         ids=["iso_B{}H{}T{}k{}v{}C{}_{}".format(*c) for c in SMALL_ISO])
+def test_backward_isotropic_small_shapes(idx):
+    B, H, T, dk, dv, C, dtype = SMALL_ISO[idx]
+    inp = forward_inputs(B, H, T, dk, dv, variant="isotropic", dtype=dtype, seed=350 + idx)
+    cot = backward_cotangents(B, H, T, dk, dv, variant="isotropic", dtype=dtype, seed=350 + idx)
+    say(f"[gpu] backward isotropic B{B} H{H} T{T} dk{dk} dv{dv} C{C} {dtype}")
+    got = _gpu_backward(inp, cot, C)
+    for n, x in got.items():
+        assert np.all(np.isfinite(x)), n
+    _assert(_errors(got, _oracle_backward(inp, cot)), dtype)
+
+
+def test_workload_iso_f32_B1_H2_T256_d32_backward():
+    inp = config_inputs(0)
+    cot = backward_cotangents(1, 2, 256, 32, 32, variant="isotropic", dtype="f32", seed=1000)
+    say("[gpu] backward iso f32 [1,2,256,32]")
+    _assert(_errors(_gpu_backward(inp, cot, 32), _oracle_backward(inp, cot)), "f32")
+
+
 def test_backward_without_state_cotangents():
     inp = forward_inputs(1, 2, 150, 64, 64, dtype="bf16", seed=41)
     cot = backward_cotangents(1, 2, 150, 64, 64, dtype="bf16", seed=41, state_cotangents=False)
@@ -114,10 +144,11 @@ def test_workload_diag_f32_B2_H4_T2048_d64_backward():
     _assert(_errors(_gpu_backward(inp, cot, 64), _oracle_backward(inp, cot)), "f32")
 
 
-def _sampled(index, heads, B, H, T, d):
+def _sampled(index, heads, B, H, T, d, variant=None):
     say(f"[gpu] generating workload {index}")
-    inp = config_inputs(index)
-    cot = backward_cotangents(B, H, T, d, d, dtype="bf16", seed=1000 + index)
+    inp = config_inputs(index, variant=variant)
+    cot = backward_cotangents(B, H, T, d, d, variant=inp["variant"], dtype="bf16",
+                              seed=1000 + index)
     say(f"[gpu] backward full size {inp['q'].shape}")
     got = _gpu_backward(inp, cot, 64)
     for n, x in got.items():
@@ -132,5 +163,6 @@ def test_workload_diag_bf16_B8_H16_T4096_d128_backward_sampled_heads():
     _sampled(2, [(0, 0), (3, 7), (7, 15)], 8, 16, 4096, 128)
 
 
-def test_workload_long_bf16_B1_H16_T65536_d128_backward_sampled_head():
-    _sampled(3, [(0, 11)], 1, 16, 65536, 128)
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+def test_workload_long_bf16_B1_H16_T65536_d128_backward_sampled_head(variant):
+    _sampled(3, [(0, 11)], 1, 16, 65536, 128, variant)
