@@ -331,12 +331,47 @@ def bench_backward(args, inp):
     grad_stages = ("bwd_state", "bwd_grad", "bwd_gain")
     dom = max(grad_stages, key=lambda k: st_ms[k])
     ach = by[dom] / (st_ms[dom] * 1e-3) / 1e9
-    del t, ws, out, dO
+
+    # training step: the forward keeping its intermediates, then the backward
+    # without its recompute
+    o = torch.empty((B, H, T, dv), dtype=bf, device=dev)
+    S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    lam_T = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+
+    def fwd_keep():
+        kdn.forward(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], lam0, S0, "diagonal", C,
+                    out=(o, S_T, lam_T), keep=ws)
+
+    def bwd_kept():
+        kdn.backward(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], dO, lam0, S0, dS_T, dl_T,
+                     chunk=C, out=out, kept=ws)
+
+    def timed_ms(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t1) * 1e3 / steps
+
+    ramp(lambda: (fwd_keep(), bwd_kept()), args.ramp_ms)
+    train_ms = timed_ms(lambda: (fwd_keep(), bwd_kept()))
+    fk_ms = timed_ms(fwd_keep)
+    bk_ms = timed_ms(lambda: (fwd_keep(), bwd_kept())) - fk_ms
+    train = {"ms_per_step": round(train_ms, 4),
+             "tokens_per_s": round(B * T / (train_ms * 1e-3), 1),
+             "forward_keep_ms": round(fk_ms, 4), "backward_kept_ms": round(bk_ms, 4),
+             "what": "kdn_forward_keep (the forward, keeping what the backward needs) then "
+                     "kdn_backward_kept (no recompute), back to back"}
+    del t, ws, out, dO, o, S_T, lam_T
     torch.cuda.empty_cache()
     return {"workload": "diag_bf16_B8_H16_T4096_d128", "steps": steps,
             "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "includes": "forward recompute (scan, prep, state keeping chunk states) "
                         "and the three gradient stages",
+            "train_step": train,
             "stages": stages,
             "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -203,6 +203,34 @@ kdn_status kdn_backward_events(const kdn_desc *d, const void *q, const void *k, 
                                float *dlambda0, float *dS0, void *ws, size_t ws_bytes,
                                void *stream, void *const *events);
 
+/* A training step without the backward's recompute: kdn_forward_keep runs the
+ * forward (same arguments and outputs as kdn_forward) into a workspace of
+ * kdn_backward_workspace_bytes(d) bytes and leaves in it everything the
+ * backward needs (the gain keys, T matrices, decays, boundary precisions,
+ * 1/D of every token and the state at every chunk start).  kdn_backward_kept
+ * then takes the arguments of kdn_backward and skips the recompute; it must
+ * get the same descriptor, inputs and workspace, unchanged since the
+ * kdn_forward_keep call (nothing checks this).  The gradients are the ones
+ * kdn_backward returns.  kdn_backward_kept_events: events as for
+ * kdn_backward_events; stages 0-3 are not run and their events not recorded. */
+kdn_status kdn_forward_keep(const kdn_desc *d, const void *q, const void *k, const void *v,
+                            const void *a, const void *qnoise, const void *r,
+                            const float *lambda0, const float *S0, void *o, float *S_T,
+                            float *lambda_T, void *ws, size_t ws_bytes, void *stream);
+kdn_status kdn_backward_kept(const kdn_desc *d, const void *q, const void *k, const void *v,
+                             const void *a, const void *qnoise, const void *r,
+                             const float *lambda0, const float *S0, const void *dO,
+                             const float *dS_T, const float *dlambda_T, float *dq, float *dk,
+                             float *dv, float *da, float *dqnoise, float *dr, float *dlambda0,
+                             float *dS0, void *ws, size_t ws_bytes, void *stream);
+kdn_status kdn_backward_kept_events(const kdn_desc *d, const void *q, const void *k,
+                                    const void *v, const void *a, const void *qnoise,
+                                    const void *r, const float *lambda0, const float *S0,
+                                    const void *dO, const float *dS_T, const float *dlambda_T,
+                                    float *dq, float *dk, float *dv, float *da, float *dqnoise,
+                                    float *dr, float *dlambda0, float *dS0, void *ws,
+                                    size_t ws_bytes, void *stream, void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,7 @@ EXPORTS = (
     "kdn_mobius_scan_workspace_bytes", "kdn_mobius_scan", "kdn_gain",
     "kdn_chunk_delta_workspace_bytes", "kdn_chunk_delta", "kdn_decode_step",
     "kdn_backward_workspace_bytes", "kdn_backward", "kdn_backward_events",
+    "kdn_forward_keep", "kdn_backward_kept", "kdn_backward_kept_events",
 )
 
 
@@ -83,6 +84,9 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_decode_step.argtypes = [D] + [P] * 9 + [P]
     lib.kdn_backward.argtypes = [D] + [P] * 19 + [P, S, P]
     lib.kdn_backward_events.argtypes = [D] + [P] * 19 + [P, S, P, ctypes.POINTER(P)]
+    lib.kdn_forward_keep.argtypes = [D] + [P] * 11 + [P, S, P]
+    lib.kdn_backward_kept.argtypes = [D] + [P] * 19 + [P, S, P]
+    lib.kdn_backward_kept_events.argtypes = [D] + [P] * 19 + [P, S, P, ctypes.POINTER(P)]
     lib.kdn_decode_step.restype = I
     _lib = lib
     return lib
@@ -174,12 +178,15 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", chunk=64,
-            workspace: torch.Tensor | None = None, out=None, events=None):
+            workspace: torch.Tensor | None = None, out=None, events=None,
+            keep: torch.Tensor | None = None):
     """KDN layer forward on the GPU.  Returns (o, S_T, lambda_T).
 
     out: optional preallocated (o, S_T, lambda_T); events: optional list of 8
     torch.cuda.Event (already recorded once): the start and stop of each of the
-    four kernels, recorded by the kernel dispatches."""
+    four kernels, recorded by the kernel dispatches.  keep: a uint8 tensor of
+    backward_workspace_bytes: the forward keeps in it what backward(...,
+    kept=keep) needs (kdn_forward_keep)."""
     lib = load_library()
     d = _forward_desc(q, k, v, a, qnoise, r, variant, chunk)
     B, H, T, dk = k.shape
@@ -200,6 +207,12 @@ def forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", ch
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
         S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
         lam_T = torch.empty(lam_shape, dtype=torch.float32, device=dev)
+    if keep is not None:
+        args = (ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(qnoise), _ptr(r),
+                _ptr(lambda0), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(lam_T), _ptr(keep),
+                keep.numel() * keep.element_size(), _stream())
+        _check(lib.kdn_forward_keep(*args), "kdn_forward_keep")
+        return o, S_T, lam_T
     need = lib.kdn_forward_workspace_bytes(ctypes.byref(d))
     if need == 0:
         _check(lib.kdn_validate(ctypes.byref(d)), "kdn_forward")
@@ -223,14 +236,16 @@ def backward_workspace_bytes(desc: KdnDesc) -> int:
 
 def backward(q, k, v, a, qnoise, r, dO, lambda0=None, S0=None, dS_T=None, dlambda_T=None,
              variant="diagonal", chunk=64, workspace: torch.Tensor | None = None, out=None,
-             events=None) -> dict:
+             events=None, kept: torch.Tensor | None = None) -> dict:
     """Gradients of <dO, o> + <dS_T, S_T> + <dlambda_T, lambda_T> with respect
     to q, k, v, a, qnoise, r, lambda0 and S0, as float32 tensors in a dict
     (keys dq, dk, dv, da, dqnoise, dr, dlambda0, dS0).
 
     out: optional dict of preallocated outputs with those keys; events:
     optional list of 14 torch.cuda.Event (already recorded once), start and
-    stop of the seven stages."""
+    stop of the seven stages.  kept: the workspace that forward(..., keep=)
+    filled for these same inputs; the backward then skips its recompute
+    (kdn_backward_kept)."""
     lib = load_library()
     d = _forward_desc(q, k, v, a, qnoise, r, variant, chunk)
     B, H, T, dk = k.shape
@@ -255,18 +270,20 @@ def backward(q, k, v, a, qnoise, r, dO, lambda0=None, S0=None, dS_T=None, dlambd
     if need == 0:
         _check(lib.kdn_validate(ctypes.byref(d)), "kdn_backward")
         raise KdnError("kdn_backward: shape not supported by the backward kernels")
-    ws = workspace if workspace is not None else _workspace(need, dev)
+    ws = kept if kept is not None else (workspace if workspace is not None
+                                         else _workspace(need, dev))
     args = (ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(qnoise), _ptr(r),
             _ptr(lambda0), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(dlambda_T),
             *(_ptr(g[n]) for n in ("dq", "dk", "dv", "da", "dqnoise", "dr", "dlambda0", "dS0")),
             _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    name = "kdn_backward_kept" if kept is not None else "kdn_backward"
     if events is None:
-        _check(lib.kdn_backward(*args), "kdn_backward")
+        _check(getattr(lib, name)(*args), name)
     else:
         if len(events) != 14:
             raise ValueError("events: 14 entries (start and stop of seven stages)")
         arr = (ctypes.c_void_p * 14)(*[None if e is None else e.cuda_event for e in events])
-        _check(lib.kdn_backward_events(*args, arr), "kdn_backward_events")
+        _check(getattr(lib, name + "_events")(*args, arr), name + "_events")
     return g
 
 

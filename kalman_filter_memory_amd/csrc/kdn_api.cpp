@@ -209,26 +209,37 @@ size_t kdn_backward_workspace_bytes(const kdn_desc* d) {
     return backward_ws(d).total;
 }
 
-kdn_status kdn_backward_events(const kdn_desc* d, const void* q, const void* k, const void* v,
-                               const void* a, const void* qnoise, const void* r,
-                               const float* lambda0, const float* S0, const void* dO,
-                               const float* dS_T, const float* dlambda_T, float* dq, float* dk,
-                               float* dv, float* da, float* dqnoise, float* dr, float* dlambda0,
-                               float* dS0, void* ws, size_t ws_bytes, void* stream,
-                               void* const* events) {
+}  // extern "C"
+
+namespace {
+
+// The backward, with (recompute) or without (the intermediates kept in ws by
+// kdn_forward_keep) its forward recompute.  With keep_o, only the forward
+// runs, writing o, S_T and lambda_T as well.
+kdn_status backward_impl(const kdn_desc* d, const void* q, const void* k, const void* v,
+                         const void* a, const void* qnoise, const void* r, const float* lambda0,
+                         const float* S0, const void* dO, const float* dS_T,
+                         const float* dlambda_T, float* dq, float* dk, float* dv, float* da,
+                         float* dqnoise, float* dr, float* dlambda0, float* dS0, void* ws,
+                         size_t ws_bytes, void* stream, void* const* events, bool recompute,
+                         void* o, float* S_T, float* lambda_T) {
+    const bool fwd_only = o != nullptr;
     kdn_status st = check_chunked(d);
     if (st != KDN_OK) return st;
     const kdn::Shape s = make_shape(d);
     if (!kdn::backward_supported(s)) return KDN_ERR_UNSUPPORTED;
     const BackwardWs w = backward_ws(d);
     if (s.BH == 0) return KDN_OK;
-    if (s.T > 0 && (!q || !k || !v || !a || !qnoise || !r || !dO || !dq || !dk || !dv || !da ||
-                    !dqnoise || !dr))
+    if (s.T > 0 && (!q || !k || !v || !a || !qnoise || !r))
+        return KDN_ERR_NULL;
+    if (s.T > 0 && !fwd_only && (!dO || !dq || !dk || !dv || !da || !dqnoise || !dr))
         return KDN_ERR_NULL;
     if (!ws) return KDN_ERR_NULL;
     if (ws_bytes < w.total) return KDN_ERR_WORKSPACE;
     for (const void* p : {q, k, v, dO, (const void*)S0, (const void*)dS_T, (const void*)dq,
-                          (const void*)dk, (const void*)dv, (const void*)dS0, (const void*)ws})
+                          (const void*)dk, (const void*)dv, (const void*)dS0, (const void*)ws,
+                          (const void*)o,
+                          (const void*)S_T})
         if (p && !aligned16(p)) return KDN_ERR_ALIGN;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     float* agg = reinterpret_cast<float*>(at(ws, w.f.agg));
@@ -258,20 +269,27 @@ kdn_status kdn_backward_events(const kdn_desc* d, const void* q, const void* k, 
         }
         kdn::launch_timing() = t;
     };
-    // forward recompute, keeping 1/D of every token and the chunk-start states
-    // (no read-out)
-    timed(0);
-    hipError_t e = kdn::launch_scan_reduce(s, k, a, qnoise, r, agg, hs);
-    timed(1);
-    if (e == hipSuccess) e = kdn::launch_scan_carry(s, agg, lambda0, lc, nullptr, hs);
-    kdn::Shape sw = s;
-    sw.gain_bf16 = s.qkv_bf16;
-    timed(2);
-    if (e == hipSuccess)
-        e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, g, hs, dinv);
-    timed(3);
-    if (e == hipSuccess)
-        e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, nullptr, nullptr, hs, at(ws, w.Sc));
+    hipError_t e = hipSuccess;
+    if (recompute) {
+        // the forward, keeping 1/D of every token and the chunk-start states
+        // (the read-out only when asked for)
+        timed(0);
+        e = kdn::launch_scan_reduce(s, k, a, qnoise, r, agg, hs);
+        timed(1);
+        if (e == hipSuccess) e = kdn::launch_scan_carry(s, agg, lambda0, lc, lambda_T, hs);
+        kdn::Shape sw = s;
+        sw.gain_bf16 = s.qkv_bf16;
+        timed(2);
+        if (e == hipSuccess)
+            e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, g, hs, dinv);
+        timed(3);
+        if (e == hipSuccess)
+            e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs, at(ws, w.Sc));
+        if (fwd_only) {
+            kdn::launch_timing() = kdn::LaunchTiming{};
+            return hip_status(e);
+        }
+    }
     timed(4);
     if (e == hipSuccess) e = kdn::launch_bwd_state(s, b, hs);
     timed(5);
@@ -280,6 +298,60 @@ kdn_status kdn_backward_events(const kdn_desc* d, const void* q, const void* k, 
     if (e == hipSuccess) e = kdn::launch_bwd_gain(s, b, hs);
     kdn::launch_timing() = kdn::LaunchTiming{};
     return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+kdn_status kdn_backward_events(const kdn_desc* d, const void* q, const void* k, const void* v,
+                               const void* a, const void* qnoise, const void* r,
+                               const float* lambda0, const float* S0, const void* dO,
+                               const float* dS_T, const float* dlambda_T, float* dq, float* dk,
+                               float* dv, float* da, float* dqnoise, float* dr, float* dlambda0,
+                               float* dS0, void* ws, size_t ws_bytes, void* stream,
+                               void* const* events) {
+    return backward_impl(d, q, k, v, a, qnoise, r, lambda0, S0, dO, dS_T, dlambda_T, dq, dk, dv,
+                         da, dqnoise, dr, dlambda0, dS0, ws, ws_bytes, stream, events, true,
+                         nullptr, nullptr, nullptr);
+}
+
+kdn_status kdn_forward_keep(const kdn_desc* d, const void* q, const void* k, const void* v,
+                            const void* a, const void* qnoise, const void* r,
+                            const float* lambda0, const float* S0, void* o, float* S_T,
+                            float* lambda_T, void* ws, size_t ws_bytes, void* stream) {
+    if (d && d->T > 0 && !o) return KDN_ERR_NULL;
+    if (d && d->T == 0) {
+        // nothing to keep: the plain forward copies the state through
+        return kdn_forward(d, q, k, v, a, qnoise, r, lambda0, S0, o, S_T, lambda_T, ws,
+                           ws_bytes, stream);
+    }
+    return backward_impl(d, q, k, v, a, qnoise, r, lambda0, S0, nullptr, nullptr, nullptr,
+                         nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                         ws, ws_bytes, stream, nullptr, true, o, S_T, lambda_T);
+}
+
+kdn_status kdn_backward_kept_events(const kdn_desc* d, const void* q, const void* k,
+                                    const void* v, const void* a, const void* qnoise,
+                                    const void* r, const float* lambda0, const float* S0,
+                                    const void* dO, const float* dS_T, const float* dlambda_T,
+                                    float* dq, float* dk, float* dv, float* da, float* dqnoise,
+                                    float* dr, float* dlambda0, float* dS0, void* ws,
+                                    size_t ws_bytes, void* stream, void* const* events) {
+    return backward_impl(d, q, k, v, a, qnoise, r, lambda0, S0, dO, dS_T, dlambda_T, dq, dk, dv,
+                         da, dqnoise, dr, dlambda0, dS0, ws, ws_bytes, stream, events, false,
+                         nullptr, nullptr, nullptr);
+}
+
+kdn_status kdn_backward_kept(const kdn_desc* d, const void* q, const void* k, const void* v,
+                             const void* a, const void* qnoise, const void* r,
+                             const float* lambda0, const float* S0, const void* dO,
+                             const float* dS_T, const float* dlambda_T, float* dq, float* dk,
+                             float* dv, float* da, float* dqnoise, float* dr, float* dlambda0,
+                             float* dS0, void* ws, size_t ws_bytes, void* stream) {
+    return kdn_backward_kept_events(d, q, k, v, a, qnoise, r, lambda0, S0, dO, dS_T, dlambda_T,
+                                    dq, dk, dv, da, dqnoise, dr, dlambda0, dS0, ws, ws_bytes,
+                                    stream, nullptr);
 }
 
 kdn_status kdn_backward(const kdn_desc* d, const void* q, const void* k, const void* v,

@@ -398,7 +398,10 @@ template <typename E, int DK, int C, int JT> struct BGradLds {
     E U[C * LDJ];     // [t][j]
     E dO[C * LDJ];    // [t][j]
     E dR[C * LDJ];    // [t][j]
-    float g[C], gam[C], del[C], dlg[C], sdot[C], misc[2];
+    float g[C], gam[C], del[C];
+    // per-wave partial sums, added in a fixed order at the end (no atomics:
+    // the gradients are bitwise reproducible)
+    float dlg[8][C], sdot[8][C], misc[8][2];
 };
 
 template <typename E, int DK, int C, int JT>
@@ -478,9 +481,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         L.g[tid] = gv;
         L.gam[tid] = exp2_hw(gv);
         L.del[tid] = exp2_hw(gC - gv);
-        L.dlg[tid] = 0.f;
-        L.sdot[tid] = 0.f;
-        if (tid < 2) L.misc[tid] = 0.f;
+#pragma unroll
+        for (int w8 = 0; w8 < 8; ++w8) {
+            L.dlg[w8][tid] = 0.f;
+            L.sdot[w8][tid] = 0.f;
+        }
+        if (tid < 16) L.misc[tid >> 1][tid & 1] = 0.f;
     }
 
     floatx4 aq[QPW][1][BKI], ak[QPW][1][BKI], aw[QPW][1][BKI];
@@ -579,7 +585,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     // xc: <dS', S> over the whole chunk state
     {
         float xs = wave_sum(xc);
-        if (lane == 0) atomicAdd(&L.misc[1], xs);
+        if (lane == 0) L.misc[wave][1] = xs;
     }
     // dQ1 = diag(gamma) dO S, dK1 = -diag(gamma) dR S, dW1 = diag(D) U dS';
     // decay derivative: + q_t.dQ1_t + k_t.dK1_t - w_t.dW1_t, and sum_s w_s.dW1_s
@@ -607,10 +613,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                 }
                 row = group16_sum(row - roww);
                 roww = group16_sum(roww);
-                if ((lane & 15) == 0) atomicAdd(&L.dlg[t], row);
+                if ((lane & 15) == 0) L.dlg[wave][t] += row;
                 wsum += roww;
             }
-            if ((lane & 15) == 0) atomicAdd(&L.misc[0], wsum);
+            wsum += __shfl_xor(wsum, 16, kWave);
+            wsum += __shfl_xor(wsum, 32, kWave);
+            if (lane == 0) L.misc[wave][0] += wsum;
         }
     }
     // M and A tiles; dM * Gamma and dA * Gamma; decay derivative: for each pair
@@ -643,11 +651,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float zr = group16_sum(rowz[e]);
-                if ((lane & 15) == 0) atomicAdd(&L.dlg[16 * tt + 4 * (lane >> 4) + e], zr);
+                if ((lane & 15) == 0) L.dlg[wave][16 * tt + 4 * (lane >> 4) + e] += zr;
             }
             col += __shfl_xor(col, 16, kWave);
             col += __shfl_xor(col, 32, kWave);
-            if (lane < 16) atomicAdd(&L.dlg[s], -col);
+            if (lane < 16) L.dlg[wave][s] -= col;
         }
     }
     sync_lds();
@@ -684,7 +692,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                     }
                 }
                 sd = group16_sum(sd);
-                if ((lane & 15) == 0) atomicAdd(&L.sdot[t], sd);
+                if ((lane & 15) == 0) L.sdot[wave][t] += sd;
             }
         }
     }
@@ -693,8 +701,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     // the state carried to the next chunk adds gamma_C <dS', S> and
     // sum_s w_s.dW1_s to the last token
     if (wave == 0) {
-        float x = lane < n ? L.dlg[lane] : 0.f;
-        if (lane == n - 1) x += L.misc[0] + L.gam[C - 1] * L.misc[1];
+        float x = 0.f, sd = 0.f, m0 = 0.f, m1 = 0.f;
+        const int tl = min(lane, C - 1);
+#pragma unroll
+        for (int w8 = 0; w8 < 8; ++w8) {
+            x += L.dlg[w8][tl];
+            sd += L.sdot[w8][tl];
+            m0 += L.misc[w8][0];
+            m1 += L.misc[w8][1];
+        }
+        if (lane >= n) x = 0.f;
+        if (lane == n - 1) x += m0 + L.gam[C - 1] * m1;
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
             const float y = __shfl_down(x, off, kWave);
@@ -702,7 +719,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         }
         if (lane < n) {
             dlna[row0 + lane] = x;
-            sdot_out[row0 + lane] = L.sdot[lane];
+            sdot_out[row0 + lane] = sd;
         }
     }
 }
@@ -721,8 +738,11 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
     const float* __restrict__ sdot, const E* __restrict__ dW, const float* __restrict__ dlna,
     const float* __restrict__ Gout, float2* __restrict__ ab, float* __restrict__ dk,
     float* __restrict__ da, float* __restrict__ dnu, float* __restrict__ dr, int T, int NC) {
-    __shared__ float red[3][C];  // per token: sum_i H, sum_i 2 a P_prev H, sum_i G P^2 b/r
-    const int tid = threadIdx.x, lane = tid & 63;
+    constexpr int NW = (DK < 64 ? 64 : DK) / 64;
+    // per token and wave: sum_i H, sum_i 2 a P_prev H, sum_i G P^2 b/r (summed
+    // over the waves in a fixed order at the end)
+    __shared__ float red[NW][3][C];
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int c = blockIdx.x;
     const size_t bh = blockIdx.y;
     const int n = min(C, T - c * C);
@@ -730,11 +750,6 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
     const int i = tid;
     const bool act = i < DK;
     const int ic = act ? i : 0;
-    if (APPLY && tid < C) {
-        red[0][tid] = 0.f;
-        red[1][tid] = 0.f;
-        red[2][tid] = 0.f;
-    }
     // token scalars in lane t (broadcast with readlane)
     const size_t tk = row0 + min(lane, n - 1);
     const float ta = to_f<G>(a[tk]), tnu = to_f<G>(nu[tk]), tr = to_f<G>(r[tk]);
@@ -819,10 +834,10 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
             sa += __shfl_xor(sa, 32, kWave);
             sr += __shfl_xor(sr, 16, kWave);
             sr += __shfl_xor(sr, 32, kWave);
-            if (lane < 16 && g0 + lane < n) {
-                atomicAdd(&red[0][g0 + lane], sv);
-                atomicAdd(&red[1][g0 + lane], sa);
-                atomicAdd(&red[2][g0 + lane], sr);
+            if (lane < 16) {
+                red[wave][0][g0 + lane] = sv;
+                red[wave][1][g0 + lane] = sa;
+                red[wave][2][g0 + lane] = sr;
             }
         }
     }
@@ -832,9 +847,16 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
         __syncthreads();
         if (tid < n) {
             const size_t o = row0 + tid;
-            da[o] = dlna[o] / ta + red[1][tid];
-            dnu[o] = red[0][tid];
-            dr[o] = -tsd * tdi + red[2][tid];
+            float sv = 0.f, sa = 0.f, sr = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                sv += red[w][0][tid];
+                sa += red[w][1][tid];
+                sr += red[w][2][tid];
+            }
+            da[o] = dlna[o] / ta + sa;
+            dnu[o] = sv;
+            dr[o] = -tsd * tdi + sr;
         }
     }
 }

@@ -166,3 +166,44 @@ def test_workload_diag_bf16_B8_H16_T4096_d128_backward_sampled_heads():
 @pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
 def test_workload_long_bf16_B1_H16_T65536_d128_backward_sampled_head(variant):
     _sampled(3, [(0, 11)], 1, 16, 65536, 128, variant)
+
+
+@pytest.mark.parametrize("variant,dtype", [("diagonal", "bf16"), ("isotropic", "f32")])
+def test_forward_keep_then_backward_kept_matches_the_plain_calls(variant, dtype):
+    """kdn_forward_keep returns what kdn_forward returns and kdn_backward_kept
+    what kdn_backward returns (the same kernels on the same inputs: bitwise)."""
+    B, H, T, dk, dv, C = 2, 2, 150, 64, 64, 64
+    inp = forward_inputs(B, H, T, dk, dv, variant=variant, dtype=dtype, seed=61)
+    cot = backward_cotangents(B, H, T, dk, dv, variant=variant, dtype=dtype, seed=61)
+    say(f"[gpu] forward_keep + backward_kept {variant} {dtype}")
+    t = forward_tensors(inp)
+    dO = to_dev(cot["dO"], tdtype(dtype))
+    dS_T = to_dev(cot["dS_T"], torch.float32)
+    dl_T = to_dev(cot["dlambda_T"], torch.float32)
+    args = (t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"])
+    o, S_T, lam = kdn.forward(*args, t["lambda0"], t["S0"], variant=variant, chunk=C)
+    desc = kdn.make_desc(B, H, T, dk, dv, C, variant, kdn._dtype_code(t["q"].dtype),
+                         kdn._dtype_code(t["a"].dtype))
+    keep = torch.empty(kdn.backward_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    o2, S_T2, lam2 = kdn.forward(*args, t["lambda0"], t["S0"], variant=variant, chunk=C,
+                                 keep=keep)
+    g_kept = kdn.backward(*args, dO, t["lambda0"], t["S0"], dS_T, dl_T, variant=variant,
+                          chunk=C, kept=keep)
+    g = kdn.backward(*args, dO, t["lambda0"], t["S0"], dS_T, dl_T, variant=variant, chunk=C)
+    torch.cuda.synchronize()
+    for x, y in ((o, o2), (S_T, S_T2), (lam, lam2)):
+        assert torch.equal(x, y)
+    for n in g:
+        assert torch.equal(g[n], g_kept[n]), n
+
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+def test_backward_is_bitwise_reproducible(variant):
+    """No atomics in the gradient reductions: two calls give identical bits."""
+    inp = forward_inputs(2, 3, 200, 128, 128, variant=variant, dtype="bf16", seed=71)
+    cot = backward_cotangents(2, 3, 200, 128, 128, variant=variant, dtype="bf16", seed=71)
+    say(f"[gpu] backward twice, {variant}")
+    a = _gpu_backward(inp, cot, 64)
+    b = _gpu_backward(inp, cot, 64)
+    for n in GRADS:
+        np.testing.assert_array_equal(a[n], b[n], err_msg=n)
