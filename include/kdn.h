@@ -161,6 +161,21 @@ kdn_status kdn_decode_step(const kdn_desc *d, const void *q, const void *k, cons
                            const void *a, const void *qnoise, const void *r, float *S,
                            float *lambda, void *o, void *stream);
 
+/* Continuous-batching decode step (SURVEY's serving path; same pages:
+ * constant-memory decoding): kdn_decode_step for d->B active sequences whose
+ * states live in a cache of n_slots entries.  S_cache [n_slots,H,d_v,d_k] and
+ * lambda_cache [n_slots,H,d_k] (or [n_slots,H]) float32 are read and updated in
+ * place at the slots slot[0..B-1] (device int32); q, k, v, a, qnoise, r and o
+ * are indexed by the active sequence as in kdn_decode_step.  A slot outside
+ * [0, n_slots) marks an idle sequence: its state and its o row are not
+ * touched.  Slots of active sequences must be distinct (two sequences on one
+ * slot race); the call does not check this.  q, k, S_cache and lambda_cache
+ * must be 16-byte aligned. */
+kdn_status kdn_decode_step_indexed(const kdn_desc *d, const void *q, const void *k,
+                                   const void *v, const void *a, const void *qnoise,
+                                   const void *r, float *S_cache, float *lambda_cache,
+                                   const int32_t *slot, int32_t n_slots, void *o, void *stream);
+
 /* Bytes of workspace kdn_backward needs (0 if the descriptor is invalid or
  * the backward does not support it).  Host-only. */
 size_t kdn_backward_workspace_bytes(const kdn_desc *d);

@@ -10,6 +10,7 @@ Functions (same names as the C entry points):
   forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", chunk=64)
       -> (o, S_T, lambda_T)
   decode_step(q, k, v, a, qnoise, r, S, lam, variant="diagonal") -> o   (S, lam in place)
+  decode_step_indexed(q, k, v, a, qnoise, r, S_cache, lam_cache, slot, variant=...) -> o
   mobius_scan(k, a, qnoise, r, lambda0=None, variant=..., chunk=64) -> dict
   gain(k, r, lambda_minus, variant=..., gain_dtype=None) -> w
   chunk_delta(q, k, v, a, w, S0=None, chunk=64) -> (o, S_T)
@@ -37,6 +38,7 @@ EXPORTS = (
     "kdn_chunk_delta_workspace_bytes", "kdn_chunk_delta", "kdn_decode_step",
     "kdn_backward_workspace_bytes", "kdn_backward", "kdn_backward_events",
     "kdn_forward_keep", "kdn_backward_kept", "kdn_backward_kept_events",
+    "kdn_decode_step_indexed",
 )
 
 
@@ -85,6 +87,7 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_backward.argtypes = [D] + [P] * 19 + [P, S, P]
     lib.kdn_backward_events.argtypes = [D] + [P] * 19 + [P, S, P, ctypes.POINTER(P)]
     lib.kdn_forward_keep.argtypes = [D] + [P] * 11 + [P, S, P]
+    lib.kdn_decode_step_indexed.argtypes = [D] + [P] * 9 + [ctypes.c_int32, P, P]
     lib.kdn_backward_kept.argtypes = [D] + [P] * 19 + [P, S, P]
     lib.kdn_backward_kept_events.argtypes = [D] + [P] * 19 + [P, S, P, ctypes.POINTER(P)]
     lib.kdn_decode_step.restype = I
@@ -378,4 +381,35 @@ def decode_step(q, k, v, a, qnoise, r, S, lam, variant="diagonal", out=None):
     _check(lib.kdn_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                _ptr(qnoise), _ptr(r), _ptr(S), _ptr(lam), _ptr(o), _stream()),
            "kdn_decode_step")
+    return o
+
+
+def decode_step_indexed(q, k, v, a, qnoise, r, S_cache, lam_cache, slot, variant="diagonal",
+                        out=None):
+    """Continuous-batching decode step: sequence n of the active batch (q, k
+    [N,H,d_k]; v [N,H,d_v]; a, qnoise, r [N,H]) reads and updates its state at
+    cache slot slot[n] (int32 [N] on the GPU; outside [0, n_slots): idle) of
+    S_cache float32 [n_slots,H,d_v,d_k] and lam_cache [n_slots,H,d_k] or
+    [n_slots,H].  Returns o [N,H,d_v] (rows of idle sequences are left as they
+    were in `out`, or uninitialised)."""
+    lib = load_library()
+    for n, x in (("q", q), ("k", k), ("v", v), ("a", a), ("qnoise", qnoise), ("r", r),
+                 ("S_cache", S_cache), ("lam_cache", lam_cache), ("slot", slot)):
+        _gpu(x, n)
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    n_slots = S_cache.shape[0]
+    if S_cache.dtype != torch.float32 or tuple(S_cache.shape) != (n_slots, H, dv, dk):
+        raise ValueError("S_cache must be float32 [n_slots,H,d_v,d_k]")
+    if slot.dtype != torch.int32 or tuple(slot.shape) != (N,):
+        raise ValueError("slot must be int32 [N]")
+    d = make_desc(N, H, 1, dk, dv, 0, variant, _dtype_code(q.dtype), _dtype_code(a.dtype))
+    lam_shape = (n_slots, H, dk) if d.variant == DIAGONAL else (n_slots, H)
+    if lam_cache.dtype != torch.float32 or tuple(lam_cache.shape) != lam_shape:
+        raise ValueError(f"lam_cache must be float32 {lam_shape}")
+    o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=k.device)
+    _check(lib.kdn_decode_step_indexed(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                       _ptr(qnoise), _ptr(r), _ptr(S_cache), _ptr(lam_cache),
+                                       _ptr(slot), n_slots, _ptr(o), _stream()),
+           "kdn_decode_step_indexed")
     return o

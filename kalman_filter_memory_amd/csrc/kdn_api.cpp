@@ -453,4 +453,25 @@ kdn_status kdn_decode_step(const kdn_desc* d, const void* q, const void* k, cons
                                          static_cast<hipStream_t>(stream)));
 }
 
+kdn_status kdn_decode_step_indexed(const kdn_desc* d, const void* q, const void* k,
+                                   const void* v, const void* a, const void* qnoise,
+                                   const void* r, float* S_cache, float* lambda_cache,
+                                   const int32_t* slot, int32_t n_slots, void* o, void* stream) {
+    kdn_status st = check_common(d);
+    if (st != KDN_OK) return st;
+    if (n_slots < 0) return KDN_ERR_SHAPE;
+    kdn::Shape s = make_shape(d);
+    s.T = 1;
+    s.nc = 1;
+    if (s.BH == 0) return KDN_OK;
+    if (!q || !k || !v || !a || !qnoise || !r || !S_cache || !lambda_cache || !slot || !o)
+        return KDN_ERR_NULL;
+    for (const void* p : {q, k, (const void*)S_cache, (const void*)lambda_cache})
+        if (!aligned16(p)) return KDN_ERR_ALIGN;
+    if (!kdn::decode_supported(s)) return KDN_ERR_UNSUPPORTED;
+    return hip_status(kdn::launch_decode(s, q, k, v, a, qnoise, r, S_cache, lambda_cache, o,
+                                         static_cast<hipStream_t>(stream), slot, d->H,
+                                         n_slots));
+}
+
 }  // extern "C"

@@ -73,15 +73,25 @@ __device__ __forceinline__ float dot4(const float4& x, const float4& y) {
     return x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
 }
 
-template <typename E, typename G, int DK, int DV, bool DIAG>
+// INDEXED (continuous batching): the state of active sequence n lives at cache
+// slot slot[n] (S and lam then hold n_slots x H states); a slot outside
+// [0, n_slots) marks an idle row, whose workgroup returns at once.
+template <typename E, typename G, int DK, int DV, bool DIAG, bool INDEXED>
 __global__ __launch_bounds__((DecCfg<DK, DV>::NW * kWave)) void decode_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const G* __restrict__ a, const G* __restrict__ nu, const G* __restrict__ r,
-    float* __restrict__ S, float* __restrict__ lam, E* __restrict__ o) {
+    float* __restrict__ S, float* __restrict__ lam, E* __restrict__ o,
+    const int32_t* __restrict__ slot, int H, int n_slots) {
     using Cfg = DecCfg<DK, DV>;
     constexpr int LPR = Cfg::LPR, RPS = Cfg::RPS, RPW = Cfg::RPW, SLOTS = Cfg::SLOTS;
 
-    const size_t st = blockIdx.x;  // (sequence, head) index
+    const size_t st = blockIdx.x;  // (sequence, head) index of the active batch
+    size_t sc = st;                // index of its state
+    if constexpr (INDEXED) {
+        const int sl = slot[st / H];
+        if (sl < 0 || sl >= n_slots) return;  // idle row (the whole workgroup)
+        sc = (size_t)sl * H + st % H;
+    }
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int col = 4 * (lane % LPR), rsub = lane / LPR;
 
@@ -90,10 +100,10 @@ __global__ __launch_bounds__((DecCfg<DK, DV>::NW * kWave)) void decode_kernel(
     const float4 k4 = load4f<E>(k + st * DK + col);
     const float4 q4 = load4f<E>(q + st * DK + col);
     float4 l4;
-    if constexpr (DIAG) l4 = *reinterpret_cast<const float4*>(lam + st * DK + col);
-    else l4.x = lam[st];
+    if constexpr (DIAG) l4 = *reinterpret_cast<const float4*>(lam + sc * DK + col);
+    else l4.x = lam[sc];
 
-    float* Sst = S + st * (size_t)(DV * DK);
+    float* Sst = S + sc * (size_t)(DV * DK);
     float4 srow[SLOTS];
     float vj[SLOTS];
 #pragma unroll
@@ -132,8 +142,8 @@ __global__ __launch_bounds__((DecCfg<DK, DV>::NW * kWave)) void decode_kernel(
     const float wq = group_sum<LPR>(dot4(w4, q4));
     __syncthreads();  // every wave has read lambda before it is overwritten
     if (wave == 0 && rsub == 0) {
-        if constexpr (DIAG) *reinterpret_cast<float4*>(lam + st * DK + col) = ln4;
-        else if (col == 0) lam[st] = ln4.x;
+        if constexpr (DIAG) *reinterpret_cast<float4*>(lam + sc * DK + col) = ln4;
+        else if (col == 0) lam[sc] = ln4.x;
     }
 
     // ---- one pass over the rows of S ----
@@ -156,7 +166,7 @@ __global__ __launch_bounds__((DecCfg<DK, DV>::NW * kWave)) void decode_kernel(
 template <typename E, typename G, int DK, int DV>
 hipError_t launch_t(const Shape& s, const void* q, const void* k, const void* v, const void* a,
                     const void* nu, const void* r, float* S, float* lam, void* o,
-                    hipStream_t st) {
+                    const int32_t* slot, int H, int n_slots, hipStream_t st) {
     const dim3 grid(s.BH), block(DecCfg<DK, DV>::NW * kWave);
     const E* qe = static_cast<const E*>(q);
     const E* ke = static_cast<const E*>(k);
@@ -165,24 +175,30 @@ hipError_t launch_t(const Shape& s, const void* q, const void* k, const void* v,
     const G* ng = static_cast<const G*>(nu);
     const G* rg = static_cast<const G*>(r);
     E* oe = static_cast<E*>(o);
-    if (s.diag)
-        hipLaunchKernelGGL((decode_kernel<E, G, DK, DV, true>), grid, block, 0, st, qe, ke, ve,
-                           ag, ng, rg, S, lam, oe);
-    else
-        hipLaunchKernelGGL((decode_kernel<E, G, DK, DV, false>), grid, block, 0, st, qe, ke, ve,
-                           ag, ng, rg, S, lam, oe);
+#define KDN_DEC_L(DIAG_, IDX_)                                                             \
+    hipLaunchKernelGGL((decode_kernel<E, G, DK, DV, DIAG_, IDX_>), grid, block, 0, st, qe, ke, \
+                       ve, ag, ng, rg, S, lam, oe, slot, H, n_slots)
+    if (slot) {
+        if (s.diag) KDN_DEC_L(true, true);
+        else KDN_DEC_L(false, true);
+    } else {
+        if (s.diag) KDN_DEC_L(true, false);
+        else KDN_DEC_L(false, false);
+    }
+#undef KDN_DEC_L
     return hipGetLastError();
 }
 
 template <typename E>
 hipError_t launch_e(const Shape& s, const void* q, const void* k, const void* v, const void* a,
                     const void* nu, const void* r, float* S, float* lam, void* o,
-                    hipStream_t st) {
-#define KDN_DEC_CASE(DK_, DV_)                                                        \
-    if (s.dk == DK_ && s.dv == DV_)                                                   \
-        return s.gate_bf16                                                            \
-                   ? launch_t<E, bf16_t, DK_, DV_>(s, q, k, v, a, nu, r, S, lam, o, st) \
-                   : launch_t<E, float, DK_, DV_>(s, q, k, v, a, nu, r, S, lam, o, st);
+                    const int32_t* slot, int H, int n_slots, hipStream_t st) {
+#define KDN_DEC_CASE(DK_, DV_)                                                                \
+    if (s.dk == DK_ && s.dv == DV_)                                                           \
+        return s.gate_bf16 ? launch_t<E, bf16_t, DK_, DV_>(s, q, k, v, a, nu, r, S, lam, o,   \
+                                                           slot, H, n_slots, st)              \
+                           : launch_t<E, float, DK_, DV_>(s, q, k, v, a, nu, r, S, lam, o,    \
+                                                          slot, H, n_slots, st);
     KDN_DEC_CASE(32, 32) KDN_DEC_CASE(32, 64) KDN_DEC_CASE(32, 128)
     KDN_DEC_CASE(64, 32) KDN_DEC_CASE(64, 64) KDN_DEC_CASE(64, 128)
     KDN_DEC_CASE(128, 32) KDN_DEC_CASE(128, 64) KDN_DEC_CASE(128, 128)
@@ -199,10 +215,10 @@ bool decode_supported(const Shape& s) {
 
 hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
                          const void* a, const void* nu, const void* r, float* S, float* lam,
-                         void* o, hipStream_t st) {
+                         void* o, hipStream_t st, const int32_t* slot, int H, int n_slots) {
     if (s.BH == 0) return hipSuccess;
-    return s.qkv_bf16 ? launch_e<bf16_t>(s, q, k, v, a, nu, r, S, lam, o, st)
-                      : launch_e<float>(s, q, k, v, a, nu, r, S, lam, o, st);
+    return s.qkv_bf16 ? launch_e<bf16_t>(s, q, k, v, a, nu, r, S, lam, o, slot, H, n_slots, st)
+                      : launch_e<float>(s, q, k, v, a, nu, r, S, lam, o, slot, H, n_slots, st);
 }
 
 }  // namespace kdn

@@ -69,10 +69,13 @@ hipError_t launch_chunk_prep(const Shape& s, bool fuse_gain, const void* k, cons
 hipError_t launch_chunk_state(const Shape& s, const void* q, const void* k, const void* v,
                               const float* g, const void* w, const void* Tm, const float* S0,
                               void* o, float* S_T, hipStream_t st, void* Sc = nullptr);
-// One decode step in place.
+// One decode step in place.  slot (may be NULL): per active sequence, the
+// cache slot of its state among n_slots (H heads each); outside [0, n_slots):
+// idle, nothing read or written for that sequence.
 hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
                          const void* a, const void* nu, const void* r, float* S, float* lam,
-                         void* o, hipStream_t st);
+                         void* o, hipStream_t st, const int32_t* slot = nullptr, int H = 1,
+                         int n_slots = 0);
 
 // Backward pass (diagonal variant).  Device pointers; per-token arrays are
 // [BH][T], per-(token, dim) arrays [BH][T][d], per-chunk states [BH][nc][dv][dk].

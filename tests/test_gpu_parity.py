@@ -317,3 +317,44 @@ def test_axis_aligned_keys_follow_the_dense_kalman_filter():
     assert normwise(o, o_ref[None, None]) <= TOL_F32
     assert normwise(S_T, M[None, None]) <= TOL_F32
     assert elementwise(lam[0, 0], 1.0 / np.diag(Sig)) <= TOL_LAMBDA
+
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+def test_decode_indexed_cache_matches_oracle(variant):
+    """Continuous batching: 24 active sequences on a cache of 40 slots, slots in
+    a shuffled order, one sequence idle (slot -1) and one past the cache; the
+    touched slots match the oracle's step, every other slot and the idle rows'
+    outputs are left bit for bit as they were."""
+    N, H, dk, dv, n_slots = 24, 4, 64, 128, 40
+    rng = np.random.default_rng(7)
+    cache = decode_inputs(n_slots, H, dk, dv, 1, variant=variant, seed=81)
+    step = decode_inputs(N, H, dk, dv, 1, variant=variant, seed=82)
+    slots = rng.permutation(n_slots)[:N].astype(np.int32)
+    slots[3] = -1
+    slots[10] = n_slots + 5
+    say(f"[gpu] decode_step_indexed {variant}: N={N} slots={n_slots}")
+    S = torch.from_numpy(cache["S0"]).cuda()
+    lam = torch.from_numpy(cache["lambda0"]).cuda()
+    x = {n: torch.from_numpy(step[n][0]).cuda().to(torch.bfloat16 if n in ("q", "k", "v")
+                                                     else torch.float32)
+         for n in ("q", "k", "v", "a", "nu", "r")}
+    o = torch.full((N, H, dv), 7.0, dtype=torch.bfloat16, device="cuda")
+    kdn.decode_step_indexed(x["q"], x["k"], x["v"], x["a"], x["nu"], x["r"], S, lam,
+                            torch.from_numpy(slots).cuda(), variant, out=o)
+    torch.cuda.synchronize()
+    active = [n for n in range(N) if 0 <= slots[n] < n_slots]
+    Sr = cache["S0"][slots[active]].astype(np.float64).copy()
+    lr = cache["lambda0"][slots[active]].astype(np.float64).copy()
+    sub = {n: step[n][0][active] for n in ("q", "k", "v", "a", "nu", "r")}
+    o_ref = oracle.decode_step(sub["q"], sub["k"], sub["v"], sub["a"], sub["nu"], sub["r"],
+                               Sr, lr, variant)
+    o_h, S_h, l_h = host(o), host(S), host(lam)
+    e_o = normwise(o_h[active], o_ref)
+    e_s = normwise(S_h[slots[active]], Sr)
+    e_l = elementwise(l_h[slots[active]], lr)
+    say(f"    err o {e_o:.2e}  S {e_s:.2e}  lambda {e_l:.2e}")
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16 and e_l <= TOL_LAMBDA
+    untouched = sorted(set(range(n_slots)) - set(slots[active].tolist()))
+    np.testing.assert_array_equal(S_h[untouched], cache["S0"][untouched])
+    np.testing.assert_array_equal(l_h[untouched], cache["lambda0"][untouched])
+    assert np.all(o_h[[3, 10]] == 7.0)
