@@ -161,6 +161,29 @@ kdn_status kdn_decode_step(const kdn_desc *d, const void *q, const void *k, cons
                            const void *a, const void *qnoise, const void *r, float *S,
                            float *lambda, void *o, void *stream);
 
+/* Bytes of workspace kdn_forward_varlen needs (0 if invalid); sized from d
+ * alone (d->B sequences, d->T tokens per head in all). */
+size_t kdn_forward_varlen_workspace_bytes(const kdn_desc *d);
+
+/* Forward of a packed batch of d->B variable-length sequences (SURVEY's
+ * serving path: prefill of many prompts in one call).  Every head's rows hold
+ * the sequences one after another: q, k [H, T, d_k]; v, o [H, T, d_v]; a,
+ * qnoise, r [H, T], with T = d->T the total token count; sequence s has rows
+ * cu_seqlens[s] .. cu_seqlens[s+1] (device int32 [B+1], non-decreasing, from 0
+ * to T).  Each sequence starts from its own lambda0 / S0 ([B,H,d_k] or [B,H];
+ * [B,H,d_v,d_k]; NULL: ones / zeros) and ends in its own lambda_T / S_T (same
+ * shapes, required).  max_seqlen (host) must be at least the longest
+ * sequence: it sizes the grids.  Offsets outside [0, T] or decreasing are
+ * clamped (no memory outside the buffers is touched), but then the results
+ * are not those of the sequences meant; the same holds for a max_seqlen that
+ * is too small.  The result for each sequence is kdn_forward's for that
+ * sequence alone. */
+kdn_status kdn_forward_varlen(const kdn_desc *d, const int32_t *cu_seqlens, int32_t max_seqlen,
+                              const void *q, const void *k, const void *v, const void *a,
+                              const void *qnoise, const void *r, const float *lambda0,
+                              const float *S0, void *o, float *S_T, float *lambda_T, void *ws,
+                              size_t ws_bytes, void *stream);
+
 /* Continuous-batching decode step (SURVEY's serving path; same pages:
  * constant-memory decoding): kdn_decode_step for d->B active sequences whose
  * states live in a cache of n_slots entries.  S_cache [n_slots,H,d_v,d_k] and

@@ -11,6 +11,8 @@ Functions (same names as the C entry points):
       -> (o, S_T, lambda_T)
   decode_step(q, k, v, a, qnoise, r, S, lam, variant="diagonal") -> o   (S, lam in place)
   decode_step_indexed(q, k, v, a, qnoise, r, S_cache, lam_cache, slot, variant=...) -> o
+  forward_varlen(q, k, v, a, qnoise, r, cu_seqlens, max_seqlen, lambda0=None, S0=None,
+                 variant=..., chunk=64) -> (o, S_T, lambda_T)   (a packed batch)
   mobius_scan(k, a, qnoise, r, lambda0=None, variant=..., chunk=64) -> dict
   gain(k, r, lambda_minus, variant=..., gain_dtype=None) -> w
   chunk_delta(q, k, v, a, w, S0=None, chunk=64) -> (o, S_T)
@@ -38,7 +40,7 @@ EXPORTS = (
     "kdn_chunk_delta_workspace_bytes", "kdn_chunk_delta", "kdn_decode_step",
     "kdn_backward_workspace_bytes", "kdn_backward", "kdn_backward_events",
     "kdn_forward_keep", "kdn_backward_kept", "kdn_backward_kept_events",
-    "kdn_decode_step_indexed",
+    "kdn_decode_step_indexed", "kdn_forward_varlen_workspace_bytes", "kdn_forward_varlen",
 )
 
 
@@ -88,6 +90,9 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_backward_events.argtypes = [D] + [P] * 19 + [P, S, P, ctypes.POINTER(P)]
     lib.kdn_forward_keep.argtypes = [D] + [P] * 11 + [P, S, P]
     lib.kdn_decode_step_indexed.argtypes = [D] + [P] * 9 + [ctypes.c_int32, P, P]
+    lib.kdn_forward_varlen_workspace_bytes.argtypes = [D]
+    lib.kdn_forward_varlen_workspace_bytes.restype = S
+    lib.kdn_forward_varlen.argtypes = [D, P, ctypes.c_int32] + [P] * 12 + [S, P]
     lib.kdn_backward_kept.argtypes = [D] + [P] * 19 + [P, S, P]
     lib.kdn_backward_kept_events.argtypes = [D] + [P] * 19 + [P, S, P, ctypes.POINTER(P)]
     lib.kdn_decode_step.restype = I
@@ -230,6 +235,46 @@ def forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", ch
             raise ValueError("events: 8 entries (start and stop of four kernels)")
         arr = (ctypes.c_void_p * 8)(*[None if e is None else e.cuda_event for e in events])
         _check(lib.kdn_forward_events(*args, arr), "kdn_forward_events")
+    return o, S_T, lam_T
+
+
+def forward_varlen(q, k, v, a, qnoise, r, cu_seqlens, max_seqlen, lambda0=None, S0=None,
+                   variant="diagonal", chunk=64, workspace: torch.Tensor | None = None):
+    """Forward of a packed batch: q, k [H,T,d_k]; v [H,T,d_v]; a, qnoise, r [H,T]
+    with N sequences laid end to end along T (cu_seqlens: int32 [N+1] on the
+    GPU; max_seqlen: an int at least the longest length).  Returns (o [H,T,d_v],
+    S_T [N,H,d_v,d_k], lambda_T [N,H,d_k] or [N,H])."""
+    lib = load_library()
+    for n, x in (("q", q), ("k", k), ("v", v), ("a", a), ("qnoise", qnoise), ("r", r),
+                 ("cu_seqlens", cu_seqlens)):
+        _gpu(x, n)
+    H, T, dk = k.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.shape[0] - 1
+    if q.shape != k.shape or v.shape != (H, T, dv) or a.shape != (H, T):
+        raise ValueError("q, k [H,T,d_k]; v [H,T,d_v]; a, qnoise, r [H,T]")
+    if cu_seqlens.dtype != torch.int32 or N < 0:
+        raise ValueError("cu_seqlens must be int32 [N+1]")
+    d = make_desc(N, H, T, dk, dv, chunk, variant, _dtype_code(q.dtype), _dtype_code(a.dtype))
+    lam_shape = (N, H, dk) if d.variant == DIAGONAL else (N, H)
+    for name, x, shape in (("lambda0", lambda0, lam_shape), ("S0", S0, (N, H, dv, dk))):
+        if x is not None:
+            _gpu(x, name)
+            if x.dtype != torch.float32 or tuple(x.shape) != shape:
+                raise ValueError(f"{name} must be float32 {shape}")
+    dev = k.device
+    o = torch.empty((H, T, dv), dtype=q.dtype, device=dev)
+    S_T = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    lam_T = torch.empty(lam_shape, dtype=torch.float32, device=dev)
+    need = lib.kdn_forward_varlen_workspace_bytes(ctypes.byref(d))
+    if need == 0:
+        _check(lib.kdn_validate(ctypes.byref(d)), "kdn_forward_varlen")
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    _check(lib.kdn_forward_varlen(ctypes.byref(d), _ptr(cu_seqlens), int(max_seqlen), _ptr(q),
+                                  _ptr(k), _ptr(v), _ptr(a), _ptr(qnoise), _ptr(r),
+                                  _ptr(lambda0), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(lam_T),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream()),
+           "kdn_forward_varlen")
     return o, S_T, lam_T
 
 

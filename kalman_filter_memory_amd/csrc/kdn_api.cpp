@@ -15,6 +15,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <climits>
 
@@ -117,6 +118,32 @@ BackwardWs backward_ws(const kdn_desc* d) {
     b.Gout = b.ab + round_up(per_dim * 8);
     b.total = b.Gout + round_up(per_dim * 4);
     return b;
+}
+
+// Packed batches: d->B sequences, d->T tokens per head in all.  The chunk
+// count is bounded by sum ceil(L / C) <= (T + B (C - 1)) / C whatever the
+// lengths, which sizes the per-chunk arrays.  Layout: [cu | cc | agg |
+// lam_chunk | w | T | g].
+struct PackedWs {
+    size_t cu, cc, agg, lam_chunk, w, tm, g, total;
+    int nc_bound;
+};
+
+PackedWs packed_ws(const kdn_desc* d) {
+    const kdn::Shape s = make_shape(d);
+    const size_t N = d->B > 0 ? d->B : 0, H = d->H, nl = s.diag ? s.dk : 1;
+    const size_t ncb = (s.T + N * (s.chunk - 1)) / s.chunk;
+    PackedWs w;
+    w.nc_bound = static_cast<int>(ncb);
+    w.cu = 0;
+    w.cc = round_up((N + 1) * 4);
+    w.agg = w.cc + round_up((N + 1) * 4);
+    w.lam_chunk = w.agg + round_up(H * ncb * nl * 16);
+    w.w = w.lam_chunk + round_up(H * (ncb + N) * nl * 4);
+    w.tm = w.w + round_up(H * s.T * s.dk * esize(d->qkv_dtype));
+    w.g = w.tm + round_up(H * ncb * s.chunk * s.chunk * esize(d->qkv_dtype));
+    w.total = w.g + round_up(H * ncb * s.chunk * 4);
+    return w;
 }
 
 kdn_status hip_status(hipError_t e) { return e == hipSuccess ? KDN_OK : KDN_ERR_HIP; }
@@ -451,6 +478,59 @@ kdn_status kdn_decode_step(const kdn_desc* d, const void* q, const void* k, cons
     if (!kdn::decode_supported(s)) return KDN_ERR_UNSUPPORTED;
     return hip_status(kdn::launch_decode(s, q, k, v, a, qnoise, r, S, lambda, o,
                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t kdn_forward_varlen_workspace_bytes(const kdn_desc* d) {
+    if (check_chunked(d) != KDN_OK) return 0;
+    if (!kdn::chunk_supported(make_shape(d))) return 0;
+    return packed_ws(d).total;
+}
+
+kdn_status kdn_forward_varlen(const kdn_desc* d, const int32_t* cu_seqlens, int32_t max_seqlen,
+                              const void* q, const void* k, const void* v, const void* a,
+                              const void* qnoise, const void* r, const float* lambda0,
+                              const float* S0, void* o, float* S_T, float* lambda_T, void* ws,
+                              size_t ws_bytes, void* stream) {
+    kdn_status st = check_chunked(d);
+    if (st != KDN_OK) return st;
+    if (max_seqlen < 0) return KDN_ERR_SHAPE;
+    if ((int64_t)d->B * d->H > 65535) return KDN_ERR_UNSUPPORTED;
+    kdn::Shape s = make_shape(d);
+    if (!kdn::chunk_supported(s)) return KDN_ERR_UNSUPPORTED;
+    const PackedWs w = packed_ws(d);
+    const int N = d->B;
+    if (N == 0 || d->H == 0) return KDN_OK;
+    if (!cu_seqlens || !ws || !S_T || !lambda_T) return KDN_ERR_NULL;
+    if (s.T > 0 && (!q || !k || !v || !a || !qnoise || !r || !o)) return KDN_ERR_NULL;
+    if (ws_bytes < w.total) return KDN_ERR_WORKSPACE;
+    for (const void* p : {q, k, v, (const void*)o, (const void*)S0, (const void*)S_T,
+                          (const void*)ws})
+        if (p && !aligned16(p)) return KDN_ERR_ALIGN;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int32_t* cu = reinterpret_cast<int32_t*>(at(ws, w.cu));
+    int32_t* cc = reinterpret_cast<int32_t*>(at(ws, w.cc));
+    // the packed batch: N * H slabs; nc is the longest sequence's chunk count
+    s.varlen = true;
+    s.BH = N * d->H;
+    s.nc = (std::min<int32_t>(max_seqlen, s.T) + s.chunk - 1) / s.chunk;
+    s.pk.cu = cu;
+    s.pk.cc = cc;
+    s.pk.H = d->H;
+    s.pk.Ttot = s.T;
+    float* agg = reinterpret_cast<float*>(at(ws, w.agg));
+    float* lc = reinterpret_cast<float*>(at(ws, w.lam_chunk));
+    void* wk = at(ws, w.w);
+    void* tm = at(ws, w.tm);
+    float* g = reinterpret_cast<float*>(at(ws, w.g));
+    hipError_t e = kdn::launch_packed_table(cu_seqlens, N, s.T, s.chunk, cu, cc, hs);
+    if (e == hipSuccess && s.nc > 0) e = kdn::launch_scan_reduce(s, k, a, qnoise, r, agg, hs);
+    if (e == hipSuccess) e = kdn::launch_scan_carry(s, agg, lambda0, lc, lambda_T, hs);
+    kdn::Shape sw = s;
+    sw.gain_bf16 = s.qkv_bf16;
+    if (e == hipSuccess && s.nc > 0)
+        e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, g, hs);
+    if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs);
+    return hip_status(e);
 }
 
 kdn_status kdn_decode_step_indexed(const kdn_desc* d, const void* q, const void* k,

@@ -242,9 +242,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         state_stage<E, DK, DVT, C, kStageAll>(L.K, L.Q, L.W, L.dO, L.Tt, L.g, L.gam, L.del, n,
                                               tid, lane, wave, pk, pq, pw, pv, pt, pg);
     };
+    const Slab sl = slab_of<false>(bh, T, NC, Packed{});
     if (NC > 0) {
-        state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, dO, w, Tm, gin, bh, j0, T, DV, NC, NC - 1,
-                                                tid, lane, pk, pq, pw, pv, pt, pg);
+        state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, dO, w, Tm, gin, sl, j0, DV, NC - 1, tid,
+                                                lane, pk, pq, pw, pv, pt, pg);
         stage(NC - 1);
     }
     state_write<E, DK, DVT, C>(acc, L.S, wave, lane);
@@ -255,8 +256,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         const size_t row0 = bh * T + (size_t)c * C;
         state_copy_out<E, DK, DVT, C>(L.S, dSe + ((bh * NC + c) * DV + j0) * DK, tid);
         if (c > 0)
-            state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, dO, w, Tm, gin, bh, j0, T, DV, NC,
-                                                    c - 1, tid, lane, pk, pq, pw, pv, pt, pg);
+            state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, dO, w, Tm, gin, sl, j0, DV, c - 1, tid,
+                                                    lane, pk, pq, pw, pv, pt, pg);
         // 1: dU = diag(D) W dS^T; M; gamma dO transposed
         floatx4 au[UPW][1][BVU];
 #pragma unroll

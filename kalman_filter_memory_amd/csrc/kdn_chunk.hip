@@ -146,13 +146,13 @@ template <typename E, typename G, int DK, int C, bool FUSE>
 __device__ __forceinline__ void prep_fetch(const E* __restrict__ k, const G* __restrict__ a,
                                            const G* __restrict__ nu, const G* __restrict__ r,
                                            bool diag, const float* __restrict__ lam_chunk,
-                                           size_t bh, int c, int T, int NC, int tid,
+                                           const Slab& sl, int c, int tid,
                                            PrepIn<E, G, DK, C>& in) {
     using L = PrepLds<E, DK, C>;
     constexpr int V = Vec16<E>::N, VPR = DK / V, NPL = L::NPL;
     const int lane = tid & 63, wave = wave_id();
-    const int t0 = c * C, n = min(C, T - t0);
-    const size_t row0 = bh * T + t0;
+    const int t0 = c * C, n = min(C, sl.T - t0);
+    const size_t row0 = sl.row0 + t0;
 #pragma unroll
     for (int x = 0; x < L::IT; ++x) {
         const int e = tid + kThreads * x;
@@ -175,10 +175,10 @@ __device__ __forceinline__ void prep_fetch(const E* __restrict__ k, const G* __r
             if (wave < L::NT && i0 < DK) {
 #pragma unroll
                 for (int d = 0; d < NPL; ++d)
-                    in.lam[d] = lam_chunk[(bh * (NC + 1) + c) * DK + i0 + d];
+                    in.lam[d] = lam_chunk[(sl.l0 + c) * DK + i0 + d];
             }
         } else if (wave == 0) {
-            in.lam[0] = lam_chunk[bh * (NC + 1) + c];
+            in.lam[0] = lam_chunk[sl.l0 + c];
         }
     }
 }
@@ -187,8 +187,8 @@ __device__ __forceinline__ void prep_fetch(const E* __restrict__ k, const G* __r
 template <typename E, typename G, int DK, int C, bool FUSE>
 __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
                                            E* __restrict__ Tm, float* __restrict__ gout,
-                                           float* __restrict__ dinv, int T, int NC, size_t bh,
-                                           int c, const PrepIn<E, G, DK, C>& in,
+                                           float* __restrict__ dinv, const Slab& sl, int c,
+                                           const PrepIn<E, G, DK, C>& in,
                                            unsigned char* smem, float* sden, float* sg,
                                            float4* sgt) {
     using L = PrepLds<E, DK, C>;
@@ -200,8 +200,8 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
     float* sZ = reinterpret_cast<float*>(smem + L::R1);  // after A is formed
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const int t0 = c * C, n = min(C, T - t0);
-    const size_t row0 = bh * T + t0;
+    const int t0 = c * C, n = min(C, sl.T - t0);
+    const size_t row0 = sl.row0 + t0;
 
     // stage K; rows past the end of the sequence are zero.  A given W (no fused
     // gain: a stage call, not the forward) is read here directly.
@@ -229,7 +229,7 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
         if (lane < C) {
             sg[lane] = g;
             sgt[lane] = make_float4(ga2, gnu, gir, gr);  // read by every lane, token by token
-            gout[(bh * NC + c) * C + lane] = g;  // for the state pass
+            gout[(sl.c0 + c) * C + lane] = g;  // for the state pass
         }
     }
     sync_lds();
@@ -474,7 +474,7 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
         }
     }
     sync_lds();
-    E* Tout = Tm + (bh * NC + c) * (size_t)(C * C);
+    E* Tout = Tm + (sl.c0 + c) * (size_t)(C * C);
     for (int e = tid; e < C * C / V; e += kThreads) {
         const int t = e / (C / V), s0 = (e % (C / V)) * V;
         const int tb = t >> 4, sb = s0 >> 4;
@@ -496,29 +496,31 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
 
 // Two chunks per workgroup (2 blockIdx.x and the next): the second chunk's
 // inputs are loaded at the start and arrive while the first is processed.
-template <typename E, typename G, int DK, int C, bool FUSE>
+// VL: a packed batch (blockIdx.y = sequence * H + head); workgroups past the
+// sequence's chunks return at once.
+template <typename E, typename G, int DK, int C, bool FUSE, bool VL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void prep_kernel(
     const E* __restrict__ k, const G* __restrict__ a, const G* __restrict__ nu,
     const G* __restrict__ r, bool diag, const float* __restrict__ lam_chunk, E* __restrict__ w,
-    E* __restrict__ Tm, float* __restrict__ gout, float* __restrict__ dinv, int T, int NC) {
+    E* __restrict__ Tm, float* __restrict__ gout, float* __restrict__ dinv, int T, int NC,
+    Packed pk) {
     using L = PrepLds<E, DK, C>;
     __shared__ __align__(16) unsigned char smem[L::R1 + L::R2];
     __shared__ __align__(16) float sden[C];
     __shared__ __align__(16) float sg[C];
     __shared__ float4 sgt[C];  // per token: a^2, nu, 1/r, r
     const int tid = threadIdx.x;
-    const size_t bh = blockIdx.y;
+    const Slab sl = slab_of<VL>(blockIdx.y, T, NC, pk);
     const int c0 = 2 * blockIdx.x, c1 = c0 + 1;
+    if (VL && c0 >= sl.nc) return;
     PrepIn<E, G, DK, C> in0, in1;
-    prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, bh, c0, T, NC, tid, in0);
-    prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, bh, min(c1, NC - 1), T, NC, tid,
-                                  in1);
-    prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, dinv, T, NC, bh, c0, in0, smem, sden, sg,
-                                  sgt);
-    if (c1 < NC) {
+    prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, sl, c0, tid, in0);
+    prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, sl, min(c1, sl.nc - 1), tid, in1);
+    prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, dinv, sl, c0, in0, smem, sden, sg, sgt);
+    if (c1 < sl.nc) {
         sync_lds();  // the second chunk's staging overwrites K / A / T
-        prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, dinv, T, NC, bh, c1, in1, smem, sden,
-                                      sg, sgt);
+        prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, dinv, sl, c1, in1, smem, sden, sg,
+                                      sgt);
     }
 }
 
@@ -576,8 +578,8 @@ template <typename E> struct StateArgs {
     const E *q, *k, *v, *w, *Tm;
     const float* gin;
     E* o;
-    size_t bh;
-    int j0, T, DV, NC, tid, lane, wave;
+    Slab sl;  // the head's rows and chunks
+    int j0, DV, tid, lane, wave;
 };
 
 // One chunk c of the state pass.  LDS holds chunk c on entry.  The register
@@ -597,12 +599,12 @@ __device__ __forceinline__ void state_chunk(
     constexpr int BT = G::BT, BV = G::BV, BI = G::BI, BVA = G::BVA;
     constexpr int NVB = G::NVB, NT = G::NT;
     const int lane = A.lane, wave = A.wave;
-    const int t0 = c * C, n = min(C, A.T - t0);
-    const size_t row0 = A.bh * A.T + t0;
+    const int t0 = c * C, n = min(C, A.sl.T - t0);
+    const size_t row0 = A.sl.row0 + t0;
     E* sWc = L.W[c & 1];
     __builtin_amdgcn_sched_barrier(0);
-    state_prefetch<E, DK, DVT, C, kLoadKQ>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.bh, A.j0, A.T, A.DV,
-                                           A.NC, c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
+    state_prefetch<E, DK, DVT, C, kLoadKQ>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.sl, A.j0, A.DV,
+                                           c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
     __builtin_amdgcn_sched_barrier(0);  // keep the three load bursts apart
 
     // one 16x16 tile of M^T = W Q^T (full depth), masked and scaled, stored as
@@ -687,8 +689,8 @@ __device__ __forceinline__ void state_chunk(
         }
     }
     sync_lds();
-    state_prefetch<E, DK, DVT, C, kLoadW>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.bh, A.j0, A.T, A.DV,
-                                          A.NC, c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
+    state_prefetch<E, DK, DVT, C, kLoadW>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.sl, A.j0, A.DV,
+                                          c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
     __builtin_amdgcn_sched_barrier(0);  // keep the three load bursts apart
 
     // ---------------- phase B
@@ -714,10 +716,10 @@ __device__ __forceinline__ void state_chunk(
         store8x2<E>(L.Us + j * LDC + 16 * tb, L.Us + j * LDC + 16 * tb + 16, us[0], us[1], lane);
         // K, Q, V and W of chunk c + 1 (the first three were last read in phase A;
         // W goes to the other buffer): staged here, where the waves have slack
-        if (c + 1 < A.NC)
+        if (c + 1 < A.sl.nc)
             state_stage<E, DK, DVT, C, kStageKQWV>(
                 L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g, L.gam, L.del,
-                min(C, A.T - (c + 1) * C), A.tid, lane, wave, nk, nq, nw, nv, nt, ng);
+                min(C, A.sl.T - (c + 1) * C), A.tid, lane, wave, nk, nq, nw, nv, nt, ng);
     } else if (wave < 4) {
         // U = T R (T lower triangular: contract only up to the block's last row)
 #pragma unroll
@@ -806,8 +808,8 @@ __device__ __forceinline__ void state_chunk(
         }
     }
     sync_lds();
-    state_prefetch<E, DK, DVT, C, kLoadVTG>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.bh, A.j0, A.T,
-                                            A.DV, A.NC, c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
+    state_prefetch<E, DK, DVT, C, kLoadVTG>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.sl, A.j0, A.DV,
+                                            c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
     __builtin_amdgcn_sched_barrier(0);  // keep the three load bursts apart
 
     // ---------------- phase C: O^T += U^T M^T ; state update ; stage chunk c + 1
@@ -839,9 +841,9 @@ __device__ __forceinline__ void state_chunk(
         }
     }
     // nothing staged here is read in phase C (W goes to the other buffer)
-    if (c + 1 < A.NC)
+    if (c + 1 < A.sl.nc)
         state_stage<E, DK, DVT, C, kMInA ? kStageT : kStageAll>(
-            L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g, L.gam, L.del, min(C, A.T - (c + 1) * C),
+            L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g, L.gam, L.del, min(C, A.sl.T - (c + 1) * C),
             A.tid, lane, wave, nk, nq, nw, nv, nt, ng);
     state_write<E, DK, DVT, C>(accS, L.S, wave, lane);
     sync_lds();
@@ -849,12 +851,13 @@ __device__ __forceinline__ void state_chunk(
 
 // One workgroup per CU (its LDS footprint) = two waves per SIMD: give each wave
 // the full 256-register budget instead of spilling to reach more waves.
-template <typename E, int DK, int DVT, int C>
+// VL: a packed batch, head = sequence * H + head within the sequence.
+template <typename E, int DK, int DVT, int C, bool VL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void state_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ gin, const E* __restrict__ w, const E* __restrict__ Tm,
     const float* S0, E* __restrict__ o, float* S_T, E* __restrict__ Sc, int BH, int T, int DV,
-    int NC) {
+    int NC, Packed pk) {
     using G = StateCfg<E, DK, DVT, C>;
     constexpr int BI = G::BI, BV = G::BV, NVB = G::NVB;
     __shared__ __align__(16) StateLds<E, DK, DVT, C> L;
@@ -864,11 +867,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const int ntile = DV / DVT, L_ = blockIdx.x, per = 8 * ntile;
     const int head = (L_ / per) * 8 + (L_ % 8);
     if (head >= BH) return;
-    const StateArgs<E> A{q,  k,  v,  w,  Tm, gin, o,  (size_t)head, ((L_ % per) / 8) * DVT,
-                         T,  DV, NC, tid, tid & 63, wave_id()};
+    const StateArgs<E> A{q,  k,  v,      w,   Tm,       gin,      o, slab_of<VL>(head, T, NC, pk),
+                         ((L_ % per) / 8) * DVT, DV, tid, tid & 63, wave_id()};
     const int lane = A.lane, wave = A.wave;
-    const size_t bh = A.bh;
+    const size_t bh = head;
     const int j0 = A.j0;
+    const Slab& sl = A.sl;
 
     // two register sets receive chunks from HBM two chunks ahead of their use
     u32x4 pkA[G::PK], pqA[G::PK], pwA[G::PK], pvA[G::PV], ptA[G::PT];
@@ -895,26 +899,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             }
     }
 
-    if (NC > 0) {
-        state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, v, w, Tm, gin, bh, j0, T, DV, NC, 0, tid,
-                                                lane, pkA, pqA, pwA, pvA, ptA, pgA);
-        state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, v, w, Tm, gin, bh, j0, T, DV, NC, 1, tid,
-                                                lane, pkB, pqB, pwB, pvB, ptB, pgB);
-        state_stage<E, DK, DVT, C, kStageAll>(L.K, L.Q, L.W[0], L.V, L.Tt, L.g, L.gam, L.del, min(C, T), tid,
-                                   lane, wave, pkA, pqA, pwA, pvA, ptA, pgA);
+    if (sl.nc > 0) {
+        state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, v, w, Tm, gin, sl, j0, DV, 0, tid, lane,
+                                                pkA, pqA, pwA, pvA, ptA, pgA);
+        state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, v, w, Tm, gin, sl, j0, DV, 1, tid, lane,
+                                                pkB, pqB, pwB, pvB, ptB, pgB);
+        state_stage<E, DK, DVT, C, kStageAll>(L.K, L.Q, L.W[0], L.V, L.Tt, L.g, L.gam, L.del,
+                                              min(C, sl.T), tid, lane, wave, pkA, pqA, pwA, pvA,
+                                              ptA, pgA);
     }
     state_write<E, DK, DVT, C>(accS, L.S, wave, lane);
     sync_lds();
 
     // the two sets alternate roles from chunk to chunk
     // (Sc: the state at every chunk start, kept for the backward pass)
-    for (int c = 0; c < NC; c += 2) {
-        if (Sc) state_copy_out<E, DK, DVT, C>(L.S, Sc + ((bh * NC + c) * DV + j0) * DK, tid);
+    for (int c = 0; c < sl.nc; c += 2) {
+        if (Sc) state_copy_out<E, DK, DVT, C>(L.S, Sc + ((sl.c0 + c) * DV + j0) * DK, tid);
         state_chunk<E, DK, DVT, C>(A, L, accS, c, pkA, pqA, pwA, pvA, ptA, pgA, pkB, pqB, pwB,
                                    pvB, ptB, pgB);
-        if (c + 1 < NC) {
+        if (c + 1 < sl.nc) {
             if (Sc)
-                state_copy_out<E, DK, DVT, C>(L.S, Sc + ((bh * NC + c + 1) * DV + j0) * DK, tid);
+                state_copy_out<E, DK, DVT, C>(L.S, Sc + ((sl.c0 + c + 1) * DV + j0) * DK, tid);
             state_chunk<E, DK, DVT, C>(A, L, accS, c + 1, pkB, pqB, pwB, pvB, ptB, pgB, pkA, pqA,
                                        pwA, pvA, ptA, pgA);
         }
@@ -976,16 +981,20 @@ hipError_t prep_t(const Shape& s, bool fuse, const void* k, const void* a, const
                   hipStream_t st) {
     static_assert(PrepLds<E, DK, C>::BYTES <= kLdsLimit, "prep LDS");
     const dim3 grid((s.nc + 1) / 2, s.BH);
-    if (fuse)
-        launch_k((prep_kernel<E, G, DK, C, true>), grid, dim3(kThreads), 0, st,
-                           static_cast<const E*>(k), static_cast<const G*>(a),
-                           static_cast<const G*>(nu), static_cast<const G*>(r), s.diag, lc,
-                           static_cast<E*>(w), static_cast<E*>(Tm), g, dinv, s.T, s.nc);
-    else
-        launch_k((prep_kernel<E, G, DK, C, false>), grid, dim3(kThreads), 0, st,
-                           static_cast<const E*>(k), static_cast<const G*>(a),
-                           static_cast<const G*>(nu), static_cast<const G*>(r), s.diag, lc,
-                           static_cast<E*>(w), static_cast<E*>(Tm), g, dinv, s.T, s.nc);
+#define KDN_PREP_L(FUSE_, VL_)                                                                \
+    launch_k((prep_kernel<E, G, DK, C, FUSE_, VL_>), grid, dim3(kThreads), 0, st,            \
+             static_cast<const E*>(k), static_cast<const G*>(a), static_cast<const G*>(nu),  \
+             static_cast<const G*>(r), s.diag, lc, static_cast<E*>(w), static_cast<E*>(Tm), g, \
+             dinv, s.T, s.nc, s.pk)
+    if (s.varlen) {
+        if (!fuse) return hipErrorInvalidValue;  // packed batches: the forward only
+        KDN_PREP_L(true, true);
+    } else if (fuse) {
+        KDN_PREP_L(true, false);
+    } else {
+        KDN_PREP_L(false, false);
+    }
+#undef KDN_PREP_L
     return hipGetLastError();
 }
 
@@ -995,12 +1004,15 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
                    hipStream_t st) {
     if constexpr (state_fits<E, DK, DVT, C>()) {
         const int groups = (s.BH + 7) / 8;
-        launch_k((state_kernel<E, DK, DVT, C>), dim3(groups * 8 * (s.dv / DVT)),
-                           dim3(StateCfg<E, DK, DVT, C>::THREADS), 0, st,
-                           static_cast<const E*>(q), static_cast<const E*>(k),
-                           static_cast<const E*>(v), g, static_cast<const E*>(w),
-                           static_cast<const E*>(Tm), S0, static_cast<E*>(o), S_T,
-                           static_cast<E*>(Sc), s.BH, s.T, s.dv, s.nc);
+#define KDN_STATE_L(VL_)                                                                     \
+    launch_k((state_kernel<E, DK, DVT, C, VL_>), dim3(groups * 8 * (s.dv / DVT)),           \
+             dim3(StateCfg<E, DK, DVT, C>::THREADS), 0, st, static_cast<const E*>(q),       \
+             static_cast<const E*>(k), static_cast<const E*>(v), g, static_cast<const E*>(w), \
+             static_cast<const E*>(Tm), S0, static_cast<E*>(o), S_T, static_cast<E*>(Sc),   \
+             s.BH, s.T, s.dv, s.nc, s.pk)
+        if (s.varlen) KDN_STATE_L(true);
+        else KDN_STATE_L(false);
+#undef KDN_STATE_L
         return hipGetLastError();
     } else {
         return hipErrorInvalidValue;

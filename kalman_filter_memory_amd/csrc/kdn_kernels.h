@@ -25,14 +25,49 @@ inline void launch_k(F kernel, dim3 grid, dim3 block, unsigned shmem, hipStream_
     t = LaunchTiming{};
 }
 
+// A packed batch of N variable-length sequences: every head's rows hold the
+// sequences one after another ([H][Ttot][d]); sequence s has rows
+// cu[s]..cu[s+1] and its chunks are numbered from cc[s] (cc[s] = sum over the
+// earlier sequences of ceil(length / chunk)).  Device pointers.
+struct Packed {
+    const int32_t* cu = nullptr;
+    const int32_t* cc = nullptr;
+    int H = 1;
+    int Ttot = 0;
+};
+
 struct Shape {
-    int BH;  // B * H (heads, or sequences * heads for decode)
-    int T;   // tokens per head
+    int BH;  // B * H (heads, or sequences * heads for decode and packed batches)
+    int T;   // tokens per head (packed: total tokens per head)
     int dk, dv, chunk;
-    int nc;  // ceil(T / chunk)
+    int nc;  // ceil(T / chunk) (packed: the longest sequence's chunk count)
     bool diag;
     bool qkv_bf16, gate_bf16, gain_bf16;
+    bool varlen = false;  // a packed batch (pk), BH = N * H
+    Packed pk;
 };
+
+// The token rows and chunks of one head (or, packed, one (sequence, head)):
+// first row, tokens, chunks, and its first entry in the per-chunk arrays (Moebius
+// products, T matrices, decays: nc each) and in the chunk-boundary precisions
+// (nc + 1 each).
+struct Slab {
+    size_t row0;
+    int T, nc;
+    size_t c0, l0;
+};
+template <bool VL>
+__device__ __forceinline__ Slab slab_of(size_t bh, int T, int NC, const Packed& pk) {
+    if constexpr (!VL) {
+        return Slab{bh * T, T, NC, bh * NC, bh * (size_t)(NC + 1)};
+    } else {
+        const int s = static_cast<int>(bh / pk.H), h = static_cast<int>(bh % pk.H);
+        const int b = pk.cu[s], e = pk.cu[s + 1], c0 = pk.cc[s], c1 = pk.cc[s + 1];
+        const int nc = c1 - c0;
+        return Slab{(size_t)h * pk.Ttot + b, e - b, nc, (size_t)pk.H * c0 + (size_t)h * nc,
+                    (size_t)pk.H * (c0 + s) + (size_t)h * (nc + 1)};
+    }
+}
 
 // Each launcher returns hipSuccess or the launch error.  Pointers are device
 // pointers with the layouts documented in include/kdn.h.
@@ -41,6 +76,10 @@ struct Shape {
 // agg: [BH][nc][nl] float4 (nl = dk for diagonal, 1 for isotropic).
 hipError_t launch_scan_reduce(const Shape& s, const void* k, const void* a, const void* nu,
                               const void* r, float* agg, hipStream_t st);
+// Offsets of a packed batch (cu_in: the caller's N + 1 sequence offsets):
+// a sanitised copy cu and the chunk offsets cc, both N + 1 int32.
+hipError_t launch_packed_table(const int32_t* cu_in, int N, int Ttot, int C, int32_t* cu,
+                               int32_t* cc, hipStream_t st);
 // Moebius scan, pass 2: chunk-boundary precisions lam_chunk [BH][nc+1][nl] and
 // lambda_T [BH][nl] (either may be NULL) from lambda0 (NULL -> ones).
 hipError_t launch_scan_carry(const Shape& s, const float* agg, const float* lambda0,

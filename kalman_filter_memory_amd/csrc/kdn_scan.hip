@@ -116,10 +116,10 @@ template <int C> struct RedSplit {
     static constexpr int CPB = kWavesPerBlock / SPLIT;  // chunks per workgroup
 };
 
-template <typename E, typename G, int DK, int C>
+template <typename E, typename G, int DK, int C, bool VL>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
     const E* __restrict__ k, const G* __restrict__ a, const G* __restrict__ nu,
-    const G* __restrict__ r, int T, int NC, float4* __restrict__ agg) {
+    const G* __restrict__ r, int T, int NC, float4* __restrict__ agg, Packed pk) {
     using L = Lanes<DK>;
     using KR = KeyRaw<E, L::IPL>;
     using RS = RedSplit<C>;
@@ -128,17 +128,19 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
     __shared__ float4 spart[RS::SPLIT > 1 ? RS::CPB : 1][RS::SPLIT > 1 ? DK : 1];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int part = wave % RS::SPLIT, cb = wave / RS::SPLIT;
+    const Slab sl = slab_of<VL>(blockIdx.y, T, NC, pk);
+    // (packed: a workgroup wholly past its sequence's chunks returns at once)
+    if (VL && (int)blockIdx.x * RS::CPB >= sl.nc) return;
     const int c_raw = blockIdx.x * RS::CPB + cb;
-    const bool live = c_raw < NC;  // no early exit: the halves of a chunk meet at a barrier
-    const int c = live ? c_raw : NC - 1;
-    const size_t bh = blockIdx.y;
-    const int t0 = c * C, n = min(C, T - t0);
+    const bool live = c_raw < sl.nc;  // no early exit: the halves of a chunk meet at a barrier
+    const int c = live ? c_raw : sl.nc - 1;
+    const int t0 = c * C, n = min(C, sl.T - t0);
     const int tb = part * TPW;  // first token of this wave in the chunk
     const bool act = lane < L::ACTIVE;
     // every load first: the gates of token tb + lane, then the keys of the
     // wave's tokens for this lane's dims (rows past the end repeat the last
     // one); row offsets are uniform, only the lane's column varies
-    const size_t row0 = bh * T + t0;
+    const size_t row0 = sl.row0 + t0;
     const unsigned gbytes = static_cast<unsigned>(n * sizeof(G));
     const unsigned goff = static_cast<unsigned>(min(tb + lane, n - 1) * sizeof(G));
     const G ra = GateRaw<G>::load(buffer_rsrc(a + row0, gbytes), goff);
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
 #pragma unroll
         for (int j = 0; j < L::IPL; ++j) {
             const M2 m = mob_renorm(P[j]);
-            agg[(bh * NC + c) * DK + lane * L::IPL + j] = make_float4(m.a, m.b, m.c, m.d);
+            agg[(sl.c0 + c) * DK + lane * L::IPL + j] = make_float4(m.a, m.b, m.c, m.d);
         }
     }
 }
@@ -213,19 +215,19 @@ __device__ __forceinline__ float row_sq(const E* p) {
     return s;
 }
 
-template <typename E, int DK>
+template <typename E, int DK, bool VL>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_iso_kernel(
     const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
     const void* __restrict__ r, bool gate_bf16, int T, int C, int NC,
-    float4* __restrict__ agg) {
+    float4* __restrict__ agg, Packed pk) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int c = blockIdx.x * kWavesPerBlock + wave;
-    const size_t bh = blockIdx.y;
-    if (c >= NC) return;
-    const int t0 = c * C, n = min(C, T - t0);
+    const Slab sl = slab_of<VL>(blockIdx.y, T, NC, pk);
+    if (c >= sl.nc) return;
+    const int t0 = c * C, n = min(C, sl.T - t0);
     M2 P = {1.f, 0.f, 0.f, 1.f};
     if (lane < n) {
-        const size_t tok = bh * T + t0 + lane;
+        const size_t tok = sl.row0 + t0 + lane;
         const float at = load_gate(a, tok, gate_bf16), nut = load_gate(nu, tok, gate_bf16);
         const float rt = load_gate(r, tok, gate_bf16);
         const float b = row_sq<E, DK>(k + tok * DK) / (static_cast<float>(DK) * rt);
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_iso_kernel(
         const M2 o = shfl_down_m2(P, off);
         if ((lane & (2 * off - 1)) == 0) P = mob_renorm(mob_mul(o, P));
     }
-    if (lane == 0) agg[bh * NC + c] = make_float4(P.a, P.b, P.c, P.d);
+    if (lane == 0) agg[sl.c0 + c] = make_float4(P.a, P.b, P.c, P.d);
 }
 
 // ------------------------------------------------------------------- carry
@@ -257,19 +259,21 @@ __device__ __forceinline__ float mob_apply_fast(const float4& m, float x) {
     return fmaf(m.x, x, m.y) * __builtin_amdgcn_rcpf(fmaf(m.z, x, m.w));
 }
 
-template <bool ONE_GROUP>
+template <bool ONE_GROUP, bool VL>
 __global__ __launch_bounds__(kWave) void carry_kernel(const float4* __restrict__ agg,
                                                       const float* __restrict__ lambda0, int BH,
-                                                      int NL, int NC,
+                                                      int NL, int T, int NC_all,
                                                       float* __restrict__ lam_chunk,
-                                                      float* __restrict__ lambda_T) {
+                                                      float* __restrict__ lambda_T, Packed pk) {
     const int lane = threadIdx.x, seg = lane / kCarryScans, sl = lane % kCarryScans;
     const size_t n_scan = (size_t)BH * NL;
     const size_t idx = blockIdx.x * (size_t)kCarryScans + sl;  // bh * NL + i
     const bool valid = idx < n_scan;
     const size_t id = valid ? idx : n_scan - 1;  // loads of lanes past the end stay in range
     const size_t bh = id / NL, i = id % NL;
-    const float4* src = agg + bh * NC * NL + i;
+    const Slab sb = slab_of<VL>(bh, T, NC_all, pk);
+    const int NC = sb.nc;
+    const float4* src = agg + sb.c0 * NL + i;
     const int SL = (NC + kCarrySeg - 1) / kCarrySeg;
     const int c0 = min(seg * SL, NC), c1 = min(c0 + SL, NC);  // this lane's chunks [c0, c1)
     auto map_at = [&](int c) { return src[(size_t)min(c, NC - 1) * NL]; };
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(kWave) void carry_kernel(const float4* __restrict__
         if (j < seg) lam = mob_apply_fast(q, lam);
     }
     // (3) walk the segment
-    float* out = lam_chunk ? lam_chunk + bh * (size_t)(NC + 1) * NL + i : nullptr;
+    float* out = lam_chunk ? lam_chunk + sb.l0 * NL + i : nullptr;
     for (int g = c0; g < c1; g += kCarryGroup) {
         if (!ONE_GROUP) {
 #pragma unroll
@@ -428,25 +432,31 @@ hipError_t reduce_e(const Shape& s, const void* k, const void* a, const void* nu
     const dim3 block(64 * kWavesPerBlock);
     float4* g = reinterpret_cast<float4*>(agg);
     const E* kk = static_cast<const E*>(k);
+#define KDN_RED_DL(G_, VL_, DK_, C_)                                                          \
+    launch_k((reduce_diag_kernel<E, G_, DK_, C_, VL_>), gridd, block, 0, st, kk,                \
+             static_cast<const G_*>(a), static_cast<const G_*>(nu), static_cast<const G_*>(r), \
+             s.T, s.nc, g, s.pk)
 #define KDN_RED_D(DK_, C_)                                                                    \
     if (s.diag && s.dk == DK_ && s.chunk == C_) {                                             \
         constexpr int cpb = RedSplit<C_>::CPB;                                                \
         const dim3 gridd((s.nc + cpb - 1) / cpb, s.BH);                                       \
-        if (s.gate_bf16)                                                                      \
-            launch_k((reduce_diag_kernel<E, bf16_t, DK_, C_>), gridd, block, 0, st,  \
-                               kk, static_cast<const bf16_t*>(a),                             \
-                               static_cast<const bf16_t*>(nu), static_cast<const bf16_t*>(r), \
-                               s.T, s.nc, g);                                                 \
-        else                                                                                  \
-            launch_k((reduce_diag_kernel<E, float, DK_, C_>), gridd, block, 0, st,  \
-                               kk, static_cast<const float*>(a), static_cast<const float*>(nu), \
-                               static_cast<const float*>(r), s.T, s.nc, g);                   \
+        if (s.gate_bf16) {                                                                    \
+            if (s.varlen) KDN_RED_DL(bf16_t, true, DK_, C_);                                  \
+            else KDN_RED_DL(bf16_t, false, DK_, C_);                                          \
+        } else {                                                                              \
+            if (s.varlen) KDN_RED_DL(float, true, DK_, C_);                                   \
+            else KDN_RED_DL(float, false, DK_, C_);                                           \
+        }                                                                                     \
         return hipGetLastError();                                                             \
     }
 #define KDN_RED_I(DK_)                                                                        \
     if (!s.diag && s.dk == DK_) {                                                             \
-        launch_k((reduce_iso_kernel<E, DK_>), grid, block, 0, st, kk, a, nu, r,       \
-                           s.gate_bf16, s.T, s.chunk, s.nc, g);                               \
+        if (s.varlen)                                                                         \
+            launch_k((reduce_iso_kernel<E, DK_, true>), grid, block, 0, st, kk, a, nu, r,     \
+                     s.gate_bf16, s.T, s.chunk, s.nc, g, s.pk);                               \
+        else                                                                                  \
+            launch_k((reduce_iso_kernel<E, DK_, false>), grid, block, 0, st, kk, a, nu, r,    \
+                     s.gate_bf16, s.T, s.chunk, s.nc, g, s.pk);                               \
         return hipGetLastError();                                                             \
     }
 #define KDN_RED_DC(DK_) KDN_RED_D(DK_, 16) KDN_RED_D(DK_, 32) KDN_RED_D(DK_, 64)
@@ -455,6 +465,7 @@ hipError_t reduce_e(const Shape& s, const void* k, const void* a, const void* nu
 #undef KDN_RED_DC
 #undef KDN_RED_I
 #undef KDN_RED_D
+#undef KDN_RED_DL
     return hipErrorInvalidValue;
 }
 
@@ -508,6 +519,30 @@ hipError_t launch_scan_reduce(const Shape& s, const void* k, const void* a, cons
                       : reduce_e<float>(s, k, a, nu, r, agg, st);
 }
 
+// Offsets of a packed batch: a sanitised copy of the caller's sequence
+// offsets (clamped to [0, Ttot] and made non-decreasing, so that every index
+// derived from them stays inside the buffers) and the chunk offsets cc.
+__global__ void packed_table_kernel(const int32_t* __restrict__ cu_in, int N, int Ttot, int C,
+                                    int32_t* __restrict__ cu, int32_t* __restrict__ cc) {
+    if (threadIdx.x != 0) return;
+    int prev = 0, chunks = 0;
+    cu[0] = 0;
+    cc[0] = 0;
+    for (int s = 0; s < N; ++s) {
+        const int e = min(max(cu_in[s + 1], prev), Ttot);
+        chunks += (e - prev + C - 1) / C;
+        cu[s + 1] = e;
+        cc[s + 1] = chunks;
+        prev = e;
+    }
+}
+
+hipError_t launch_packed_table(const int32_t* cu_in, int N, int Ttot, int C, int32_t* cu,
+                               int32_t* cc, hipStream_t st) {
+    hipLaunchKernelGGL(packed_table_kernel, dim3(1), dim3(64), 0, st, cu_in, N, Ttot, C, cu, cc);
+    return hipGetLastError();
+}
+
 hipError_t launch_scan_carry(const Shape& s, const float* agg, const float* lambda0,
                              float* lam_chunk, float* lambda_T, hipStream_t st) {
     const int NL = s.diag ? s.dk : 1;
@@ -515,12 +550,18 @@ hipError_t launch_scan_carry(const Shape& s, const float* agg, const float* lamb
     if (n == 0) return hipSuccess;
     const dim3 grid((unsigned)((n + kCarryScans - 1) / kCarryScans)), block(kWave);
     const float4* a4 = reinterpret_cast<const float4*>(agg);
-    if (s.nc <= kCarrySeg * kCarryGroup)
-        launch_k(carry_kernel<true>, grid, block, 0, st, a4, lambda0, s.BH, NL, s.nc,
-                           lam_chunk, lambda_T);
-    else
-        launch_k(carry_kernel<false>, grid, block, 0, st, a4, lambda0, s.BH, NL, s.nc,
-                           lam_chunk, lambda_T);
+#define KDN_CARRY_L(ONE_, VL_)                                                             \
+    launch_k(carry_kernel<ONE_, VL_>, grid, block, 0, st, a4, lambda0, s.BH, NL, s.T, s.nc, \
+             lam_chunk, lambda_T, s.pk)
+    const bool one = s.nc <= kCarrySeg * kCarryGroup;
+    if (s.varlen) {
+        if (one) KDN_CARRY_L(true, true);
+        else KDN_CARRY_L(false, true);
+    } else {
+        if (one) KDN_CARRY_L(true, false);
+        else KDN_CARRY_L(false, false);
+    }
+#undef KDN_CARRY_L
     return hipGetLastError();
 }
 

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "kdn_device.h"
+#include "kdn_kernels.h"
 
 namespace kdn {
 namespace {
@@ -177,15 +178,15 @@ template <typename E, int DK, int DVT, int C, int PART>
 __device__ __forceinline__ void state_prefetch(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ w, const E* __restrict__ Tm, const float* __restrict__ gin,
-    size_t bh, int j0, int T, int DV, int NC, int cc, int tid, int lane,
+    const Slab& sl, int j0, int DV, int cc, int tid, int lane,
     u32x4 (&pk)[StateCfg<E, DK, DVT, C>::PK], u32x4 (&pq)[StateCfg<E, DK, DVT, C>::PK],
     u32x4 (&pw)[StateCfg<E, DK, DVT, C>::PK], u32x4 (&pv)[StateCfg<E, DK, DVT, C>::PV],
     u32x4 (&pt)[StateCfg<E, DK, DVT, C>::PT], float& pg) {
     using G = StateCfg<E, DK, DVT, C>;
     constexpr int VEC = G::VEC;
-    const int c = min(cc, NC - 1);
-    const int t0 = c * C, n = min(C, T - t0);
-    const size_t row0 = bh * T + t0;
+    const int c = min(cc, sl.nc - 1);
+    const int t0 = c * C, n = min(C, sl.T - t0);
+    const size_t row0 = sl.row0 + t0;
     if constexpr (PART == kLoadKQ || PART == kLoadW || PART == kLoadAll) {
 #pragma unroll
         for (int x = 0; x < G::PK; ++x) {
@@ -210,7 +211,7 @@ __device__ __forceinline__ void state_prefetch(
                 pv[x] = *reinterpret_cast<const u32x4*>(v + (row0 + min(t, n - 1)) * DV + j0 + c0);
             }
         }
-        const E* Tc = Tm + (bh * NC + c) * (size_t)(C * C);
+        const E* Tc = Tm + (sl.c0 + c) * (size_t)(C * C);
 #pragma unroll
         for (int x = 0; x < G::PT; ++x) {
             const int e = tid + G::THREADS * x;
@@ -218,7 +219,7 @@ __device__ __forceinline__ void state_prefetch(
                 pt[x] = *reinterpret_cast<const u32x4*>(Tc + e * VEC);
         }
         // chunk-local cumulative log2 decay (padding rows repeat the last value)
-        pg = gin[(bh * NC + c) * C + min(lane, C - 1)];
+        pg = gin[(sl.c0 + c) * C + min(lane, C - 1)];
     }
 }
 

@@ -358,3 +358,42 @@ def test_decode_indexed_cache_matches_oracle(variant):
     np.testing.assert_array_equal(S_h[untouched], cache["S0"][untouched])
     np.testing.assert_array_equal(l_h[untouched], cache["lambda0"][untouched])
     assert np.all(o_h[[3, 10]] == 7.0)
+
+
+@pytest.mark.parametrize("variant,dtype,chunk", [("diagonal", "bf16", 64),
+                                                 ("isotropic", "f32", 32),
+                                                 ("diagonal", "f32", 16)])
+def test_forward_varlen_matches_oracle_per_sequence(variant, dtype, chunk):
+    """A packed batch of sequences of lengths 0, 1, ragged, exact chunk multiples
+    and several chunks: each sequence's o, S_T and lambda_T are the oracle's
+    for that sequence alone."""
+    lens = [37, 0, 64, 1, 200, 130, 65, 5]
+    H, dk, dv = 3, 64, 32
+    N, T = len(lens), sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    say(f"[gpu] forward_varlen {variant} {dtype} C={chunk} lens={lens}")
+    # one draw of a [1, H, T] batch, cut into the sequences
+    inp = forward_inputs(1, H, T, dk, dv, variant=variant, dtype=dtype, seed=91)
+    init = forward_inputs(N, H, 1, dk, dv, variant=variant, dtype=dtype, seed=92)
+    t = forward_tensors(inp)
+    lam0 = torch.from_numpy(init["lambda0"]).cuda()
+    S0 = torch.from_numpy(init["S0"]).cuda()
+    o, S_T, lam_T = kdn.forward_varlen(t["q"][0], t["k"][0], t["v"][0], t["a"][0], t["nu"][0],
+                                       t["r"][0], torch.from_numpy(cu).cuda(), max(lens),
+                                       lam0, S0, variant=variant, chunk=chunk)
+    torch.cuda.synchronize()
+    o_h, S_h, l_h = host(o), host(S_T), host(lam_T)
+    tol = _tol(dtype)
+    for s_, L in enumerate(lens):
+        sl = slice(cu[s_], cu[s_ + 1])
+        sub = {n: inp[n][:, :, sl] for n in ("q", "k", "v", "a", "nu", "r")}
+        ref = oracle.forward(sub["q"], sub["k"], sub["v"], sub["a"], sub["nu"], sub["r"],
+                             init["lambda0"][s_:s_ + 1], init["S0"][s_:s_ + 1], variant)
+        e_o = normwise(o_h[:, sl][None], ref["o"]) if L else 0.0
+        e_s = normwise(S_h[s_:s_ + 1], ref["S_T"])
+        e_l = elementwise(l_h[s_:s_ + 1], ref["lambda_T"])
+        say(f"    seq {s_} (L={L}): err o {e_o:.2e}  S_T {e_s:.2e}  lambda_T {e_l:.2e}")
+        assert e_o <= tol and e_s <= tol and e_l <= TOL_LAMBDA
+    # an empty sequence passes its state through unchanged
+    np.testing.assert_array_equal(S_h[1], init["S0"][1])
+    np.testing.assert_array_equal(l_h[1], init["lambda0"][1])
