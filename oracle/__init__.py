@@ -52,6 +52,8 @@ def _load():
         lib.kdn_oracle_decode_step.restype = I
         lib.kdn_oracle_backward.argtypes = [I, I, I, I, I, I] + [P] * 19 + [I]
         lib.kdn_oracle_backward.restype = I
+        lib.kdn_oracle_forward_dense.argtypes = [I, I, I, I, I] + [P] * 12 + [I]
+        lib.kdn_oracle_forward_dense.restype = I
         _lib = lib
     return _lib
 
@@ -185,4 +187,34 @@ def backward(q, k, v, a, nu, r, dO, lambda0=None, S0=None, dS_T=None, dlambda_T=
         threads or default_threads())
     if rc != 0:
         raise ValueError(f"kdn_oracle_backward rejected its arguments (code {rc})")
+    return out
+
+
+def forward_dense(q, k, v, a, nu, r, P0=None, S0=None, debug=False,
+                  threads: int | None = None) -> dict:
+    """Exact KDN (dense Riccati recursion, one d_k x d_k covariance per head),
+    fp64.  P0: [B,H,d_k,d_k] prior covariance or None (identity).  Returns o,
+    S_T, P_T and, with debug=True, the gains w [B,H,T,d_k]."""
+    lib = _load()
+    q, k, v, a, nu, r = (_f32(x) for x in (q, k, v, a, nu, r))
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    if P0 is not None:
+        P0 = _f32(P0)
+        assert P0.shape == (B, H, dk, dk)
+    if S0 is not None:
+        S0 = _f32(S0)
+        assert S0.shape == (B, H, dv, dk)
+    o = np.empty((B, H, T, dv))
+    S_T = np.empty((B, H, dv, dk))
+    P_T = np.empty((B, H, dk, dk))
+    w = np.empty((B, H, T, dk)) if debug else None
+    rc = lib.kdn_oracle_forward_dense(B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                      _ptr(nu), _ptr(r), _ptr(P0), _ptr(S0), _ptr(o), _ptr(S_T),
+                                      _ptr(P_T), _ptr(w), threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"kdn_oracle_forward_dense rejected its arguments (code {rc})")
+    out = {"o": o, "S_T": S_T, "P_T": P_T}
+    if debug:
+        out["w"] = w
     return out

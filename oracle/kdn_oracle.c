@@ -491,3 +491,115 @@ int kdn_oracle_backward(int B, int H, int T, int dk, int dv, int variant, const 
     free(jobs);
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Exact KDN: the dense Riccati recursion that the two approximations replace
+ * ("Kalman Delta Networks", English abstract: exact tracking entails a dense,
+ * state-dependent Riccati recursion).  One d_k x d_k covariance P per head,
+ * shared by the rows of S; per token, in the order of kdn_token:
+ *     predict:  P^- = a^2 P + nu I
+ *     gain:     w = P^- k / (k^T P^- k + r)
+ *     update:   P = P^- - (P^- k)(P^- k)^T / (k^T P^- k + r)
+ *     mean:     S <- a S;  u = v - S k;  S <- S + u w^T;  o = S q
+ * P0 [B,H,d_k,d_k] (NULL: identity) is the posterior covariance at t = 0.
+ * Outputs o, S_T as kdn_oracle_forward, P_T [B,H,d_k,d_k], and optionally the
+ * gains dbg_w [B,H,T,d_k].  Return value as kdn_oracle_forward (-3 also for a
+ * P0 with a non-positive diagonal).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int T, dk, dv;
+    const float *q, *k, *v, *a, *nu, *r, *P0, *S0;
+    double *o, *S_T, *P_T, *dbg_w;
+    int n_heads, n_threads, tid;
+} djob2_t;
+
+static void *run_heads_dense(void *arg)
+{
+    const djob2_t *J = (const djob2_t *)arg;
+    const int T = J->T, dk = J->dk, dv = J->dv;
+    double *pk = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *w = (double *)malloc(sizeof(double) * (size_t)dk);
+    int bh, t, i, j;
+    for (bh = J->tid; bh < J->n_heads; bh += J->n_threads) {
+        double *P = J->P_T + (size_t)bh * dk * dk;
+        double *S = J->S_T + (size_t)bh * dv * dk;
+        for (i = 0; i < dk * dk; ++i)
+            P[i] = J->P0 ? (double)J->P0[(size_t)bh * dk * dk + i] : (i % (dk + 1) == 0 ? 1.0 : 0.0);
+        for (i = 0; i < dv * dk; ++i) S[i] = J->S0 ? (double)J->S0[(size_t)bh * dv * dk + i] : 0.0;
+        for (t = 0; t < T; ++t) {
+            const size_t tok = (size_t)bh * T + t;
+            const float *kt = J->k + tok * dk, *qt = J->q + tok * dk, *vt = J->v + tok * dv;
+            const double a = J->a[tok], nu = J->nu[tok], r = J->r[tok];
+            double den = r;
+            for (i = 0; i < dk * dk; ++i) P[i] *= a * a;
+            for (i = 0; i < dk; ++i) P[(size_t)i * dk + i] += nu;
+            for (i = 0; i < dk; ++i) {
+                double s = 0.0;
+                for (j = 0; j < dk; ++j) s += P[(size_t)i * dk + j] * (double)kt[j];
+                pk[i] = s;
+            }
+            for (i = 0; i < dk; ++i) den += (double)kt[i] * pk[i];
+            for (i = 0; i < dk; ++i) w[i] = pk[i] / den;
+            for (i = 0; i < dk; ++i)
+                for (j = 0; j < dk; ++j) P[(size_t)i * dk + j] -= pk[i] * pk[j] / den;
+            if (J->dbg_w)
+                for (i = 0; i < dk; ++i) J->dbg_w[tok * dk + i] = w[i];
+            for (j = 0; j < dv; ++j) {
+                double *row = S + (size_t)j * dk;
+                double sk = 0.0, sq = 0.0, u;
+                for (i = 0; i < dk; ++i) {
+                    row[i] *= a;
+                    sk += row[i] * (double)kt[i];
+                }
+                u = (double)vt[j] - sk;
+                for (i = 0; i < dk; ++i) {
+                    row[i] += u * w[i];
+                    sq += row[i] * (double)qt[i];
+                }
+                J->o[tok * dv + j] = sq;
+            }
+        }
+    }
+    free(pk);
+    free(w);
+    return NULL;
+}
+
+int kdn_oracle_forward_dense(int B, int H, int T, int dk, int dv, const float *q, const float *k,
+                             const float *v, const float *a, const float *nu, const float *r,
+                             const float *P0, const float *S0, double *o, double *S_T,
+                             double *P_T, double *dbg_w, int n_threads)
+{
+    djob2_t base, *jobs;
+    pthread_t *th;
+    int i, n_heads = B * H;
+    size_t h;
+    if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1) return -1;
+    if (!S_T || !P_T) return -2;
+    if (T > 0 && (!q || !k || !v || !a || !nu || !r || !o)) return -2;
+    if (check_values((size_t)B * H * T, 0, a, nu, r, NULL)) return -3;
+    if (P0)
+        for (h = 0; h < (size_t)n_heads; ++h)
+            for (i = 0; i < dk; ++i)
+                if (!(P0[h * dk * dk + (size_t)i * dk + i] > 0.0f)) return -3;
+    if (n_heads == 0) return 0;
+    base.T = T; base.dk = dk; base.dv = dv;
+    base.q = q; base.k = k; base.v = v; base.a = a; base.nu = nu; base.r = r;
+    base.P0 = P0; base.S0 = S0; base.o = o; base.S_T = S_T; base.P_T = P_T; base.dbg_w = dbg_w;
+    base.n_heads = n_heads;
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > n_heads) n_threads = n_heads;
+    th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+    jobs = (djob2_t *)malloc(sizeof(djob2_t) * (size_t)n_threads);
+    for (i = 0; i < n_threads; ++i) {
+        jobs[i] = base;
+        jobs[i].tid = i;
+        jobs[i].n_threads = n_threads;
+    }
+    for (i = 1; i < n_threads; ++i) pthread_create(&th[i], NULL, run_heads_dense, &jobs[i]);
+    run_heads_dense(&jobs[0]);
+    for (i = 1; i < n_threads; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+    return 0;
+}
