@@ -161,6 +161,22 @@ kdn_status kdn_decode_step(const kdn_desc *d, const void *q, const void *k, cons
                            const void *a, const void *qnoise, const void *r, float *S,
                            float *lambda, void *o, void *stream);
 
+/* Exact KDN gain (SURVEY's next row f3; "Kalman Delta Networks", English
+ * abstract: exact tracking entails a dense, state-dependent Riccati recursion):
+ * per head one d_k x d_k covariance P, per token P^- = a^2 P + qnoise I,
+ * w = P^- k / (k^T P^- k + r), P = P^- - (P^- k)(P^- k)^T / (k^T P^- k + r).
+ * k [B,H,T,d_k] (qkv_dtype); a, qnoise, r [B,H,T]; P0 [B,H,d_k,d_k] float32
+ * (NULL: identity), the covariance at t = 0; w: output [B,H,T,d_k] (gain_dtype,
+ * which must equal qkv_dtype); P_T: NULL or output [B,H,d_k,d_k].  d_k is 32,
+ * 64 or 128 (KDN_ERR_UNSUPPORTED otherwise); d_v and chunk are not read; the
+ * variant field must hold either value and does not change the result.  k and
+ * w must be 16-byte aligned (KDN_ERR_ALIGN otherwise).  The memory write and
+ * read-out with these gains is
+ * kdn_chunk_delta.  One workgroup per head, sequential over T: meant for the
+ * small d_k and head counts where the exact filter is affordable. */
+kdn_status kdn_dense_gain(const kdn_desc *d, const void *k, const void *a, const void *qnoise,
+                          const void *r, const float *P0, void *w, float *P_T, void *stream);
+
 /* Bytes of workspace kdn_forward_varlen needs (0 if invalid); sized from d
  * alone (d->B sequences, d->T tokens per head in all). */
 size_t kdn_forward_varlen_workspace_bytes(const kdn_desc *d);

@@ -11,6 +11,7 @@ Functions (same names as the C entry points):
       -> (o, S_T, lambda_T)
   decode_step(q, k, v, a, qnoise, r, S, lam, variant="diagonal") -> o   (S, lam in place)
   decode_step_indexed(q, k, v, a, qnoise, r, S_cache, lam_cache, slot, variant=...) -> o
+  dense_gain(k, a, qnoise, r, P0=None) -> (w, P_T);  forward_dense(...) -> (o, S_T, P_T)
   forward_varlen(q, k, v, a, qnoise, r, cu_seqlens, max_seqlen, lambda0=None, S0=None,
                  variant=..., chunk=64) -> (o, S_T, lambda_T)   (a packed batch)
   mobius_scan(k, a, qnoise, r, lambda0=None, variant=..., chunk=64) -> dict
@@ -41,6 +42,7 @@ EXPORTS = (
     "kdn_backward_workspace_bytes", "kdn_backward", "kdn_backward_events",
     "kdn_forward_keep", "kdn_backward_kept", "kdn_backward_kept_events",
     "kdn_decode_step_indexed", "kdn_forward_varlen_workspace_bytes", "kdn_forward_varlen",
+    "kdn_dense_gain",
 )
 
 
@@ -90,6 +92,7 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_backward_events.argtypes = [D] + [P] * 19 + [P, S, P, ctypes.POINTER(P)]
     lib.kdn_forward_keep.argtypes = [D] + [P] * 11 + [P, S, P]
     lib.kdn_decode_step_indexed.argtypes = [D] + [P] * 9 + [ctypes.c_int32, P, P]
+    lib.kdn_dense_gain.argtypes = [D] + [P] * 8
     lib.kdn_forward_varlen_workspace_bytes.argtypes = [D]
     lib.kdn_forward_varlen_workspace_bytes.restype = S
     lib.kdn_forward_varlen.argtypes = [D, P, ctypes.c_int32] + [P] * 12 + [S, P]
@@ -236,6 +239,34 @@ def forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", ch
         arr = (ctypes.c_void_p * 8)(*[None if e is None else e.cuda_event for e in events])
         _check(lib.kdn_forward_events(*args, arr), "kdn_forward_events")
     return o, S_T, lam_T
+
+
+def dense_gain(k, a, qnoise, r, P0=None, want_P=True):
+    """Exact KDN gains (dense Riccati recursion): k [B,H,T,d_k]; a, qnoise, r
+    [B,H,T]; P0 float32 [B,H,d_k,d_k] or None (identity).  Returns (w in k's
+    dtype [B,H,T,d_k], P_T float32 [B,H,d_k,d_k] or None)."""
+    lib = load_library()
+    for n, x in (("k", k), ("a", a), ("qnoise", qnoise), ("r", r)):
+        _gpu(x, n)
+    B, H, T, dk = k.shape
+    d = make_desc(B, H, T, dk, dk, 0, "diagonal", _dtype_code(k.dtype), _dtype_code(a.dtype))
+    if P0 is not None:
+        _gpu(P0, "P0")
+        if P0.dtype != torch.float32 or tuple(P0.shape) != (B, H, dk, dk):
+            raise ValueError("P0 must be float32 [B,H,d_k,d_k]")
+    w = torch.empty_like(k)
+    P_T = torch.empty((B, H, dk, dk), dtype=torch.float32, device=k.device) if want_P else None
+    _check(lib.kdn_dense_gain(ctypes.byref(d), _ptr(k), _ptr(a), _ptr(qnoise), _ptr(r),
+                              _ptr(P0), _ptr(w), _ptr(P_T), _stream()), "kdn_dense_gain")
+    return w, P_T
+
+
+def forward_dense(q, k, v, a, qnoise, r, P0=None, S0=None, chunk=64):
+    """Exact KDN layer forward: kdn_dense_gain, then the memory write and
+    read-out with those gains (kdn_chunk_delta).  Returns (o, S_T, P_T)."""
+    w, P_T = dense_gain(k, a, qnoise, r, P0)
+    o, S_T = chunk_delta(q, k, v, a, w, S0, chunk=chunk)
+    return o, S_T, P_T
 
 
 def forward_varlen(q, k, v, a, qnoise, r, cu_seqlens, max_seqlen, lambda0=None, S0=None,

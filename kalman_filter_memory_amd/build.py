@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkdn.so")
-SOURCES = ["kdn_api.cpp", "kdn_scan.hip", "kdn_chunk.hip", "kdn_decode.hip", "kdn_bwd.hip"]
+SOURCES = ["kdn_api.cpp", "kdn_scan.hip", "kdn_chunk.hip", "kdn_decode.hip", "kdn_bwd.hip", "kdn_dense.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

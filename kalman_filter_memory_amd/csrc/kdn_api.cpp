@@ -446,6 +446,7 @@ kdn_status kdn_chunk_delta(const kdn_desc* d, const void* q, const void* k, cons
     kdn_status st = kdn_validate(d);
     if (st != KDN_OK) return st;
     if (d->gain_dtype != d->qkv_dtype) return KDN_ERR_UNSUPPORTED;
+    if (d->d_k != 32 && d->d_k != 64 && d->d_k != 128) return KDN_ERR_UNSUPPORTED;
     const kdn::Shape s = make_shape(d);
     const ForwardWs fw = forward_ws(d);
     if (s.BH == 0) return KDN_OK;
@@ -478,6 +479,21 @@ kdn_status kdn_decode_step(const kdn_desc* d, const void* q, const void* k, cons
     if (!kdn::decode_supported(s)) return KDN_ERR_UNSUPPORTED;
     return hip_status(kdn::launch_decode(s, q, k, v, a, qnoise, r, S, lambda, o,
                                          static_cast<hipStream_t>(stream)));
+}
+
+kdn_status kdn_dense_gain(const kdn_desc* d, const void* k, const void* a, const void* qnoise,
+                          const void* r, const float* P0, void* w, float* P_T, void* stream) {
+    kdn_status st = check_common(d);
+    if (st != KDN_OK) return st;
+    if (d->T < 0) return KDN_ERR_SHAPE;
+    if (d->gain_dtype != d->qkv_dtype) return KDN_ERR_UNSUPPORTED;
+    if (d->d_k != 32 && d->d_k != 64 && d->d_k != 128) return KDN_ERR_UNSUPPORTED;
+    const kdn::Shape s = make_shape(d);
+    if (s.BH == 0) return KDN_OK;
+    if (s.T > 0 && (!k || !a || !qnoise || !r || !w)) return KDN_ERR_NULL;
+    if (s.T > 0 && (!aligned16(k) || !aligned16(w))) return KDN_ERR_ALIGN;
+    return hip_status(kdn::launch_dense_gain(s, k, a, qnoise, r, P0, w, P_T,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 size_t kdn_forward_varlen_workspace_bytes(const kdn_desc* d) {

@@ -44,31 +44,6 @@ template <> __device__ __forceinline__ float4 load4f<bf16_t>(const bf16_t* p) {
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
 }
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-template <int CTRL> __device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(
-        __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// sum over the LPR aligned lanes of a row group, returned to every lane of it:
-// quad_perm xor 1 and xor 2, then row_half_mirror (other quad of 8 lanes),
-// row_mirror (other 8 of 16) and, for 32 lanes, v_permlane16_swap of x with
-// itself, whose two results add up to x + x of the lane 16 away.
-template <int LPR> __device__ __forceinline__ float group_sum(float x) {
-    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "unsupported group");
-    x += dpp<0xB1>(x);
-    x += dpp<0x4E>(x);
-    x += dpp<0x141>(x);
-    if constexpr (LPR >= 16) x += dpp<0x140>(x);
-    if constexpr (LPR >= 32) {
-        const u32x2 s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
-                                                         false, false);
-        x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
-    }
-    return x;
-}
-
 __device__ __forceinline__ float dot4(const float4& x, const float4& y) {
     return x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
 }

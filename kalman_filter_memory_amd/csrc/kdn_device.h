@@ -89,6 +89,33 @@ __device__ __forceinline__ float lane_value(float x, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
+// x of another lane of the same row of 16, chosen by a DPP control (quad_perm,
+// row_mirror, row_half_mirror ...), as a source modifier of one VALU move
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// sum over the LPR aligned lanes of a row group, returned to every lane of it,
+// without LDS: quad_perm xor 1 and xor 2, then row_half_mirror (other quad of 8
+// lanes), row_mirror (other 8 of 16) and, for 32 lanes, v_permlane16_swap of x
+// with itself, whose two results add up to x + x of the lane 16 away.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <int LPR> __device__ __forceinline__ float group_sum(float x) {
+    static_assert(LPR == 2 || LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32,
+                  "unsupported group");
+    x += dpp<0xB1>(x);
+    if constexpr (LPR >= 4) x += dpp<0x4E>(x);
+    if constexpr (LPR >= 8) x += dpp<0x141>(x);
+    if constexpr (LPR >= 16) x += dpp<0x140>(x);
+    if constexpr (LPR >= 32) {
+        const u32x2 s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                         false, false);
+        x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    }
+    return x;
+}
+
 // ------------------------------------------------------------------- MFMA
 // 16x16 output tiles.  Operand fragments are read from row-major LDS arrays
 // whose contraction index is contiguous:  A as [m][k], B as [n][k].

@@ -140,6 +140,12 @@ hipError_t launch_bwd_grad(const Shape& s, const BwdArgs& b, hipStream_t st);
 hipError_t launch_bwd_gain(const Shape& s, const BwdArgs& b, hipStream_t st);
 bool backward_supported(const Shape& s);
 
+// Exact KDN gain (dense Riccati recursion) per token; P0 [BH][dk][dk] or NULL
+// (identity); w [BH][T][dk] in qkv dtype; P_T [BH][dk][dk] or NULL.
+hipError_t launch_dense_gain(const Shape& s, const void* k, const void* a, const void* nu,
+                             const void* r, const float* P0, void* w, float* P_T,
+                             hipStream_t st);
+
 // true if the chunk kernels are built for this (dtype, dk, dv, chunk)
 bool chunk_supported(const Shape& s);
 bool decode_supported(const Shape& s);

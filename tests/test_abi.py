@@ -145,6 +145,21 @@ def test_backward_host_side_checks(lib):
     assert lib.kdn_backward(ctypes.byref(_desc(B=0)), *([None] * 19), None, 0, None) == 0
 
 
+def test_dense_gain_host_side_checks(lib):
+    """kdn_dense_gain: unsupported d_k and mixed gain dtype are refused before
+    any launch; no heads is a no-op."""
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake] * 4 + [None, fake, None]
+    assert lib.kdn_dense_gain(ctypes.byref(_desc(d_k=48)), *args, None) == 3
+    mixed = _desc(d_k=64)
+    mixed.gain_dtype = kdn.F32
+    assert lib.kdn_dense_gain(ctypes.byref(mixed), *args, None) == 3
+    assert lib.kdn_dense_gain(ctypes.byref(_desc(d_k=64)), None, *args[1:], None) == 1
+    odd = [ctypes.c_void_p(0x1002)] + args[1:]
+    assert lib.kdn_dense_gain(ctypes.byref(_desc(d_k=64)), *odd, None) == 5
+    assert lib.kdn_dense_gain(ctypes.byref(_desc(B=0, d_k=64)), *([None] * 7), None) == 0
+
+
 def test_python_binding_refuses_cpu_tensors(lib):
     import torch
     x = torch.zeros(1, 1, 4, 32)

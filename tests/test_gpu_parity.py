@@ -397,3 +397,46 @@ def test_forward_varlen_matches_oracle_per_sequence(variant, dtype, chunk):
     # an empty sequence passes its state through unchanged
     np.testing.assert_array_equal(S_h[1], init["S0"][1])
     np.testing.assert_array_equal(l_h[1], init["lambda0"][1])
+
+
+@pytest.mark.parametrize("dk,dtype,T,chunk", [(32, "f32", 300, 64), (64, "f32", 257, 64),
+                                              (64, "bf16", 200, 64), (128, "f32", 96, 32),
+                                              (128, "bf16", 150, 64), (32, "bf16", 5, 16)])
+def test_dense_exact_kdn_matches_oracle(dk, dtype, T, chunk):
+    """Exact KDN (dense Riccati gain, then the chunkwise write): gains, o, S_T
+    and P_T against the oracle's dense filter, from a random SPD P0."""
+    B, H, dv = 1, 3, 32
+    inp = forward_inputs(B, H, T, dk, dv, dtype=dtype, seed=95)
+    rng = np.random.default_rng(96)
+    X = rng.standard_normal((B, H, dk, dk)) / np.sqrt(dk)
+    P0 = (X @ np.swapaxes(X, -1, -2) + 0.5 * np.eye(dk)).astype(np.float32)
+    say(f"[gpu] exact KDN dk={dk} {dtype} T={T}")
+    t = forward_tensors(inp)
+    o, S_T, P_T = kdn.forward_dense(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"],
+                                    torch.from_numpy(P0).cuda(), t["S0"], chunk=chunk)
+    w, _ = kdn.dense_gain(t["k"], t["a"], t["nu"], t["r"], torch.from_numpy(P0).cuda(),
+                          want_P=False)
+    torch.cuda.synchronize()
+    ref = oracle.forward_dense(inp["q"], inp["k"], inp["v"], inp["a"], inp["nu"], inp["r"], P0,
+                               inp["S0"], debug=True)
+    e_w = normwise(host(w), ref["w"])
+    e_o = normwise(host(o), ref["o"])
+    e_s = normwise(host(S_T), ref["S_T"])
+    e_p = normwise(host(P_T), ref["P_T"])
+    say(f"    err w {e_w:.2e}  o {e_o:.2e}  S_T {e_s:.2e}  P_T {e_p:.2e}")
+    tol = _tol(dtype)
+    assert e_w <= tol and e_o <= tol and e_s <= tol and e_p <= 1e-4
+
+
+def test_dense_exact_kdn_empty_sequence_keeps_prior():
+    """T = 0: no gains, P_T equals P0 (identity when P0 is omitted)."""
+    say("[gpu] exact KDN T=0")
+    k = torch.empty((2, 2, 0, 64), device="cuda")
+    g = torch.empty((2, 2, 0), device="cuda")
+    P0 = torch.randn((2, 2, 64, 64), device="cuda")
+    w, P_T = kdn.dense_gain(k, g, g, g, P0)
+    _, P_I = kdn.dense_gain(k, g, g, g, None)
+    torch.cuda.synchronize()
+    assert w.numel() == 0
+    assert torch.equal(P_T, P0)
+    assert torch.equal(P_I, torch.eye(64, device="cuda").expand(2, 2, 64, 64))
