@@ -8,17 +8,24 @@
 // variants (kdn_chunk_delta).
 //
 // One workgroup of 256 threads per head, sequential over the tokens.  P lives
-// in registers: row i is held by 256 / d_k consecutive lanes, d_k^2 / 256
-// entries each.  Per token the row sums of P^- k come from DPP lane moves; the
-// sum k^T P^- k, taken over the lanes' partial row sums weighted by the key,
-// from DPP sums over rows of 16 lanes and four partials in LDS (the token's one
-// barrier, which waits for LDS traffic only); P^- k is shared through LDS for
-// the rank-one update.  Keys and gates arrive in blocks of NB tokens: the
-// next block is loaded into registers while the current one is worked on and
-// moved into the other LDS buffer at its end, so that no token waits for
-// global memory; the gains of a block collect in LDS and leave in 16-byte
-// stores.  Per-token LDS buffers alternate between tokens, so that one
-// barrier per token orders every access.
+// in registers as a 16 x 16 grid of (d_k/16)^2 blocks, one per lane; the 16
+// lanes of a DPP row (one row of blocks) sum their parts of P^- k with DPP
+// moves, so that each lane needs the key and P^- k only at its own d_k/16 rows
+// and columns.  k^T P^- k comes from the same lane partials, DPP sums and four
+// wave partials in LDS (the token's one barrier, which waits for LDS traffic
+// only); P^- k is shared through LDS for the rank-one update.
+//
+// P is kept as s * Ps with a running scale s: the prediction a^2 P + nu I
+// becomes s <- a^2 s and nu / s added to the diagonal of Ps, so that it costs
+// nothing per entry; the update P^- - (P^- k)(P^- k)^T / den becomes
+// Ps - c u u^T with u = Ps^- k and c = s / den, and the gain is c u.  When s
+// leaves [2^-32, 2^32] (or a is zero) it is folded into Ps.
+//
+// Keys and gates arrive in blocks of NB tokens: the next block is loaded into
+// registers while the current one is worked on and moved into the other LDS
+// buffer at its end, so that no token waits for global memory; the gains of a
+// block collect in LDS and leave in 16-byte stores.  Per-token LDS buffers
+// alternate between tokens, so that one barrier per token orders every access.
 #include "kdn_device.h"
 #include "kdn_kernels.h"
 
@@ -62,32 +69,35 @@ __global__ __launch_bounds__(256) void dense_gain_kernel(
     const G* __restrict__ r, const float* __restrict__ P0, E* __restrict__ w,
     float* __restrict__ P_T, int T) {
     constexpr int NB = kDenseNB;
-    constexpr int TPR = 256 / DK, CPT = DK / TPR;  // threads per row, columns per thread
+    constexpr int BS = DK / 16;  // block edge: lane holds P[BS*rb + i][BS*cb + j]
     using V = Vec16<E>;
     constexpr int NV = NB * DK / V::N;              // 16-byte vectors of keys per block
     constexpr int VPT = (NV + 255) / 256;           // per thread
     __shared__ float kb[2][NB * DK], wb[2][NB * DK], gb[2][3][NB];
-    __shared__ float pks[2][DK], denp[2][4];
+    __shared__ float us[2][DK], denp[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const int row = tid / TPR, cb = (tid % TPR) * CPT;
-    const bool lead = tid % TPR == 0;
+    const int rb = tid >> 4, cb = tid & 15;
+    const bool lead = cb == 0, diag = rb == cb;
     const size_t bh = blockIdx.x, tok0 = bh * T;
     const typename V::T* kv = reinterpret_cast<const typename V::T*>(k + tok0 * DK);
     typename V::T* wv = reinterpret_cast<typename V::T*>(w + tok0 * DK);
-    float P[CPT];
+    float P[BS][BS], sc = 1.f;  // P = sc * Ps
 #pragma unroll
-    for (int j = 0; j < CPT; ++j)
-        P[j] = P0 ? P0[(bh * DK + row) * DK + cb + j] : (row == cb + j ? 1.f : 0.f);
+    for (int i = 0; i < BS; ++i)
+#pragma unroll
+        for (int j = 0; j < BS; ++j)
+            P[i][j] = P0 ? P0[(bh * DK + BS * rb + i) * DK + BS * cb + j]
+                         : (diag && i == j ? 1.f : 0.f);
 
     // registers holding the block being fetched
-    typename V::T kr[VPT];
+    typename V::T kpre[VPT];
     G gr = G(0);
 #define KDN_DENSE_FETCH(base_)                                                          \
     {                                                                                  \
         const int nv_ = min(NB, T - (base_)) * (DK / V::N);                            \
         _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                              \
             const int v = tid + 256 * i;                                               \
-            if (v < nv_) kr[i] = kv[size_t(base_) * (DK / V::N) + v];                  \
+            if (v < nv_) kpre[i] = kv[size_t(base_) * (DK / V::N) + v];                \
         }                                                                              \
         if (tid < 3 * NB) {                                                            \
             const int g = tid / NB, t = (base_) + tid % NB;                            \
@@ -100,7 +110,7 @@ __global__ __launch_bounds__(256) void dense_gain_kernel(
         const int nv_ = min(NB, T - (base_)) * (DK / V::N);                            \
         _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                              \
             const int v = tid + 256 * i;                                               \
-            if (v < nv_) V::to_f(kr[i], &kb[buf_][v * V::N]);                          \
+            if (v < nv_) V::to_f(kpre[i], &kb[buf_][v * V::N]);                        \
         }                                                                              \
         if (tid < 3 * NB) gb[buf_][tid / NB][tid % NB] = to_f<G>(gr);                  \
     }
@@ -121,30 +131,63 @@ __global__ __launch_bounds__(256) void dense_gain_kernel(
         for (int tt = 0; tt < nt; ++tt) {
             const int b = tt & 1;
             const float* kt = kk + tt * DK;
-            // predict, and the lane's part of row `row` of P^- k
+            // predict: sc <- a^2 sc, nu / sc onto the diagonal of Ps
             const float at = gb[buf][0][tt], nut = gb[buf][1][tt];
-            const float a2 = at * at;
-            float pp[4] = {0.f, 0.f, 0.f, 0.f};  // four chains, for latency
+            const float sn = sc * (at * at);
+            if (!(sn >= 0x1p-32f && sn <= 0x1p32f)) {  // uniform: fold the scale into Ps
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                P[j] = fmaf(P[j], a2, row == cb + j ? nut : 0.f);
-                pp[j % 4] = fmaf(P[j], kt[cb + j], pp[j % 4]);
+                for (int i = 0; i < BS; ++i)
+#pragma unroll
+                    for (int j = 0; j < BS; ++j) P[i][j] *= sn;
+                sc = 1.f;
+            } else {
+                sc = sn;
             }
-            const float part = (pp[0] + pp[1]) + (pp[2] + pp[3]);
-            const float pk = group_sum<TPR>(part);
-            const float d16 = group_sum<16>(kt[row] * part);
-            const float d = lane_value(d16, 0) + lane_value(d16, 16) + lane_value(d16, 32) +
-                            lane_value(d16, 48);
-            if (lead) pks[b][row] = pk;
-            if (lane == 0) denp[b][wave] = d;
+            if (diag) {
+                const float add = nut / sc;
+#pragma unroll
+                for (int i = 0; i < BS; ++i) P[i][i] += add;
+            }
+            // u = Ps^- k at this lane's rows, from its columns; kr . u for k^T Ps^- k
+            float kc[BS], kr[BS], u[BS];
+#pragma unroll
+            for (int j = 0; j < BS; ++j) {
+                kc[j] = kt[BS * cb + j];
+                kr[j] = kt[BS * rb + j];
+            }
+            float dp = 0.f;
+#pragma unroll
+            for (int i = 0; i < BS; ++i) {
+                float x = 0.f;
+#pragma unroll
+                for (int j = 0; j < BS; ++j) x = fmaf(P[i][j], kc[j], x);
+                u[i] = x;
+                dp = fmaf(kr[i], x, dp);
+            }
+#pragma unroll
+            for (int i = 0; i < BS; ++i) u[i] = group_sum<16>(u[i]);
+            dp = group_sum<16>(dp);
+            const float dw = lane_value(dp, 0) + lane_value(dp, 16) + lane_value(dp, 32) +
+                             lane_value(dp, 48);
+            if (lead) {
+#pragma unroll
+                for (int i = 0; i < BS; ++i) us[b][BS * rb + i] = u[i];
+            }
+            if (lane == 0) denp[b][wave] = dw;
             sync_lds();
             const float rt = gb[buf][2][tt];
-            const float iden = 1.f / (rt + denp[b][0] + denp[b][1] + denp[b][2] + denp[b][3]);
-            // rank-one update and the gain row
-            const float pki = pk * iden;
+            const float c = sc / (rt + sc * (denp[b][0] + denp[b][1] + denp[b][2] + denp[b][3]));
+            // rank-one update of Ps and the gain rows c u
+            float ucol[BS];
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) P[j] = fmaf(-pki, pks[b][cb + j], P[j]);
-            if (lead) wb[buf][tt * DK + row] = pki;
+            for (int j = 0; j < BS; ++j) ucol[j] = us[b][BS * cb + j];
+#pragma unroll
+            for (int i = 0; i < BS; ++i) {
+                const float ci = c * u[i];
+#pragma unroll
+                for (int j = 0; j < BS; ++j) P[i][j] = fmaf(-ci, ucol[j], P[i][j]);
+                if (lead) wb[buf][tt * DK + BS * rb + i] = ci;
+            }
         }
         // the next block into the other buffers; this block's gains out
         if (jb + 1 < nblk) KDN_DENSE_STAGE(buf ^ 1, base + NB)
@@ -158,7 +201,10 @@ __global__ __launch_bounds__(256) void dense_gain_kernel(
     }
     if (P_T) {
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) P_T[(bh * DK + row) * DK + cb + j] = P[j];
+        for (int i = 0; i < BS; ++i)
+#pragma unroll
+            for (int j = 0; j < BS; ++j)
+                P_T[(bh * DK + BS * rb + i) * DK + BS * cb + j] = sc * P[i][j];
     }
 #undef KDN_DENSE_FETCH
 #undef KDN_DENSE_STAGE

@@ -440,3 +440,27 @@ def test_dense_exact_kdn_empty_sequence_keeps_prior():
     assert w.numel() == 0
     assert torch.equal(P_T, P0)
     assert torch.equal(P_I, torch.eye(64, device="cuda").expand(2, 2, 64, 64))
+
+
+@pytest.mark.parametrize("dk", [32, 128])
+def test_dense_exact_kdn_extreme_decays(dk):
+    """Decays of 1e-6 (the running scale of the covariance is folded back on
+    that token), 1e-3 and exactly one, against the oracle's dense filter."""
+    B, H, T, dv = 1, 2, 64, 32
+    inp = forward_inputs(B, H, T, dk, dv, dtype="f32", seed=97)
+    rng = np.random.default_rng(98)
+    a = rng.uniform(0.02, 1.0, (B, H, T)).astype(np.float32)
+    a[..., ::7] = 1e-6
+    a[..., 1::9] = 1e-3
+    a[..., 2::11] = 1.0
+    inp["a"] = a
+    say(f"[gpu] exact KDN extreme decays dk={dk}")
+    t = forward_tensors(inp)
+    o, S_T, P_T = kdn.forward_dense(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], None,
+                                    t["S0"], chunk=32)
+    torch.cuda.synchronize()
+    ref = oracle.forward_dense(inp["q"], inp["k"], inp["v"], inp["a"], inp["nu"], inp["r"], None,
+                               inp["S0"])
+    e_o, e_s, e_p = (normwise(host(x), ref[n]) for x, n in ((o, "o"), (S_T, "S_T"), (P_T, "P_T")))
+    say(f"    err o {e_o:.2e}  S_T {e_s:.2e}  P_T {e_p:.2e}")
+    assert e_o <= TOL_F32 and e_s <= TOL_F32 and e_p <= 1e-4
