@@ -83,8 +83,8 @@ def chunk_flops_full(n, dk, dv, C):
 # 512 MiB (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0), with the SHA-256 of the
 # kernel source they were taken on: reported only while the source is unchanged.
 TRAFFIC = {"kernel": "chunk_state",
-           "src_sha256": "d1135162ecab8b1c7471775f07f8b739c3504ad3eae59f4e6acad66e7a68c875",
-           "fetch_bytes": 614593684, "write_bytes": 142606669}
+           "src_sha256": "66ba408fa12b213600f6d921be9898e8585a6b08c7f75e255c4884ae5de413d9",
+           "fetch_bytes": 614605070, "write_bytes": 142606457}
 
 
 def _traffic():
@@ -212,6 +212,8 @@ def run(args):
     torch.cuda.empty_cache()
     if not args.no_backward:
         res["backward"] = bench_backward(args, inp)
+    if not args.no_dense:
+        res["dense"] = bench_dense(args, inp)
     if not args.no_decode:
         res["decode"] = bench_decode(args)
     if not args.no_cpu_baseline:
@@ -397,6 +399,53 @@ def ramp(fn, ms):
         torch.cuda.synchronize()
 
 
+def bench_dense(args, inp):
+    """Exact KDN (dense Riccati gain, then the chunkwise write) on the same
+    workload from P0 = I.  The gain kernel is a sequential recursion per head;
+    it is reported by its time per token and its arithmetic rate: the
+    algorithmic count per token and head is 5 d_k^2 flops (prediction d_k^2,
+    P^- k 2 d_k^2, rank-one update 2 d_k^2)."""
+    import torch
+
+    import kalman_filter_memory_amd as kdn
+
+    dev = torch.device("cuda:0")
+    B, H, T, dk, C = (WL[x] for x in ("B", "H", "T", "dk", "chunk"))
+    bf = torch.bfloat16
+    t = {n: torch.from_numpy(inp[n]).to(dev, bf) for n in ("q", "k", "v", "a", "nu", "r")}
+    S0 = torch.from_numpy(inp["S0"]).to(dev)
+
+    def fwd():
+        kdn.forward_dense(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], None, S0, chunk=C)
+
+    def gain():
+        kdn.dense_gain(t["k"], t["a"], t["nu"], t["r"], None, want_P=False)
+
+    steps = 10
+    for _ in range(2):
+        fwd()
+    torch.cuda.synchronize()
+    log(f"timing {steps} exact-KDN forward steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        gain()
+    e1.record()
+    torch.cuda.synchronize()
+    g_ms = e0.elapsed_time(e1) / steps
+    flops = 5.0 * B * H * T * dk * dk
+    tf = flops / (g_ms * 1e-3) / 1e12
+    return {"ms_per_step": round(ms, 4), "tokens/s": round(B * T / (ms * 1e-3), 1),
+            "gain_us": round(g_ms * 1e3, 1), "ns_per_token": round(g_ms * 1e6 / T, 1),
+            "gain_TFLOP/s": round(tf, 2), "frac_fp32": round(tf / PEAK_FP32_TFLOPS, 4),
+            "bound": "latency (sequential over tokens; one workgroup per head)"}
+
+
 def bench_decode(args):
     """Decode step at 256 sequences x 16 heads x d 128, 128 steps in place."""
     import numpy as np
@@ -479,6 +528,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
