@@ -214,6 +214,8 @@ def run(args):
         res["backward"] = bench_backward(args, inp)
     if not args.no_dense:
         res["dense"] = bench_dense(args, inp)
+    if not args.no_layer:
+        res["layer"] = bench_layer(args)
     if not args.no_decode:
         res["decode"] = bench_decode(args)
     if not args.no_cpu_baseline:
@@ -446,6 +448,75 @@ def bench_dense(args, inp):
             "bound": "latency (sequential over tokens; one workgroup per head)"}
 
 
+LAYER = dict(B=8, T=4096, H=16, D=2048, dk=128, dv=128, chunk=64)
+LAYER_STAGES = ("gemm_in", "norm_gates", "recurrence", "readout_rows", "gemm_out")
+
+
+def bench_layer(args):
+    """The KDN layer on random weights (kdn_layer_forward): input GEMM (rocBLAS),
+    normalisation and gates, the recurrence, the read-out to token rows, output
+    GEMM; per-stage times from events recorded between the stages."""
+    import numpy as np
+    import torch
+
+    import kalman_filter_memory_amd as kdn
+    from kdn_inputs import layer_inputs
+
+    dev = torch.device("cuda:0")
+    B, T, H, D, dk, dv, C = (LAYER[x] for x in ("B", "T", "H", "D", "dk", "dv", "chunk"))
+    log("generating layer inputs")
+    p = layer_inputs(B, T, H, D, dk, dv, dtype="bf16", seed=1003)
+    bf = torch.bfloat16
+    t = {n: torch.from_numpy(p[n]).to(dev, bf) for n in ("x", "W_in", "W_out")}
+    t.update({n: torch.from_numpy(p[n]).to(dev) for n in ("b_gate", "lambda0", "S0")})
+    d = kdn.make_layer_desc(B, T, H, D, dk, dv, C, "diagonal", kdn.BF16)
+    ws = torch.empty(kdn.layer_workspace_bytes(d), dtype=torch.uint8, device=dev)
+
+    def step(events=None):
+        kdn.layer_forward(t["x"], t["W_in"], t["b_gate"], t["W_out"], H, dk, dv, t["lambda0"],
+                          t["S0"], chunk=C, workspace=ws, events=events)
+
+    ramp(step, args.ramp_ms)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    steps = 20
+    log(f"timing {steps} layer steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(steps)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for row in evs:
+        step(events=row)
+    torch.cuda.synchronize()
+    st = {k: float(np.mean([row[2 * i].elapsed_time(row[2 * i + 1]) for row in evs]))
+          for i, k in enumerate(LAYER_STAGES)}
+    M, n_in = B * T, H * (2 * dk + dv) + 3 * H
+    flops = {"gemm_in": 2.0 * M * D * n_in, "gemm_out": 2.0 * M * H * dv * D}
+    nbytes = {"norm_gates": M * n_in * 2 + B * H * T * (2 * dk + dv + 3) * 2,
+              "readout_rows": 2 * B * H * T * dv * 2}
+    stages = {}
+    for k in LAYER_STAGES:
+        sec = st[k] * 1e-3
+        stages[k] = {"us": round(st[k] * 1e3, 1)}
+        if k in flops:
+            tf = flops[k] / sec / 1e12
+            stages[k].update({"TFLOP/s": round(tf, 1), "frac_bf16": round(tf / PEAK_BF16_TFLOPS, 4)})
+        if k in nbytes:
+            gbs = nbytes[k] / sec / 1e9
+            stages[k].update({"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+    return {"workload": f"layer_diag_bf16_B{B}_T{T}_H{H}_D{D}_d{dk}", "ms_per_step": round(ms, 4),
+            "tokens/s": round(M / (ms * 1e-3), 1), "stages": stages,
+            "gemm": "rocBLAS gemm_ex, bf16 in and out, fp32 accumulation",
+            "weights": "random (kdn_inputs.layer_inputs), no trained checkpoint"}
+
+
 def bench_decode(args):
     """Decode step at 256 sequences x 16 heads x d 128, 128 steps in place."""
     import numpy as np
@@ -529,6 +600,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "

@@ -177,6 +177,57 @@ kdn_status kdn_decode_step(const kdn_desc *d, const void *q, const void *k, cons
 kdn_status kdn_dense_gain(const kdn_desc *d, const void *k, const void *a, const void *qnoise,
                           const void *r, const float *P0, void *w, float *P_T, void *stream);
 
+/* ------------------------------------------------------------------ layer
+ * The KDN layer around the recurrence, on caller-given weights ("Kalman Delta
+ * Networks", English abstract: a drop-in replacement for linear attention;
+ * KDN summary, 关键模块: queries, keys, values and the gates a, nu, r):
+ *   Z = x W_in, with the columns of W_in [d_model, H(2 d_k + d_v) + 3H] in the
+ *       order q (head-major), k, v, then the logits of a, nu and r (H each);
+ *   q_h, k_h divided by max(|q_h|, 1e-6) and max(|k_h|, 1e-6);
+ *   a = sigmoid(z_a + b_a), nu = softplus(z_nu + b_nu), r = softplus(z_r + b_r),
+ *       b_gate [3H] float32 in the same order;
+ *   o = kdn_forward(q, k, v, a, nu, r, lambda0, S0) over B*H heads;
+ *   y = [o_1 .. o_H] W_out, W_out [H d_v, d_model].
+ * x [B, T, d_model] and y [B, T, d_model] are token rows.  Every tensor but
+ * b_gate, lambda0, S0, S_T and lambda_T is in `dtype`; the GEMMs accumulate in
+ * float32 and round their outputs to dtype.  The two GEMMs run in rocBLAS on a
+ * handle from kdn_blas_create; the rest in this library's kernels. */
+typedef struct {
+    int32_t B, T, H, d_model, d_k, d_v, chunk;
+    int32_t variant; /* kdn_variant of the recurrence */
+    int32_t dtype;   /* kdn_dtype of x, the weights, y and every activation */
+} kdn_layer_desc;
+
+/* A rocBLAS handle for kdn_layer_forward (atomics off, so that results do not
+ * depend on the run).  Creating it allocates (inside rocBLAS); the caller owns
+ * it, creates it once and frees it with kdn_blas_destroy.  A handle serves one
+ * call at a time; each call sets its stream. */
+kdn_status kdn_blas_create(void **handle);
+kdn_status kdn_blas_destroy(void *handle);
+
+/* Bytes of workspace kdn_layer_forward needs (0 if the descriptor is invalid:
+ * the recurrence's limits of kdn_validate, d_model a positive multiple of 8,
+ * 3H <= 256).  Host-only. */
+size_t kdn_layer_workspace_bytes(const kdn_layer_desc *d);
+
+/* The layer forward.  lambda0, S0 (NULL: ones, zeros), S_T, lambda_T (NULL:
+ * not written) as in kdn_forward; x, W_in, W_out, y and ws 16-byte aligned;
+ * ws of at least kdn_layer_workspace_bytes(d) bytes; y must not alias x. */
+kdn_status kdn_layer_forward(const kdn_layer_desc *d, void *blas, const void *x, const void *W_in,
+                             const float *b_gate, const void *W_out, const float *lambda0,
+                             const float *S0, void *y, float *S_T, float *lambda_T, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* kdn_layer_forward with timing: events is NULL or 10 hipEvent_t (entries may
+ * be NULL) recorded on `stream` around the five stages (0-1 input GEMM, 2-3
+ * normalisation and gates, 4-5 recurrence, 6-7 read-out to token rows, 8-9
+ * output GEMM). */
+kdn_status kdn_layer_forward_events(const kdn_layer_desc *d, void *blas, const void *x,
+                                    const void *W_in, const float *b_gate, const void *W_out,
+                                    const float *lambda0, const float *S0, void *y, float *S_T,
+                                    float *lambda_T, void *ws, size_t ws_bytes, void *stream,
+                                    void *const *events);
+
 /* Bytes of workspace kdn_forward_varlen needs (0 if invalid); sized from d
  * alone (d->B sequences, d->T tokens per head in all). */
 size_t kdn_forward_varlen_workspace_bytes(const kdn_desc *d);

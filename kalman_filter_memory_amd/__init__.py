@@ -12,6 +12,7 @@ Functions (same names as the C entry points):
   decode_step(q, k, v, a, qnoise, r, S, lam, variant="diagonal") -> o   (S, lam in place)
   decode_step_indexed(q, k, v, a, qnoise, r, S_cache, lam_cache, slot, variant=...) -> o
   dense_gain(k, a, qnoise, r, P0=None) -> (w, P_T);  forward_dense(...) -> (o, S_T, P_T)
+  layer_forward(x, W_in, b_gate, W_out, H, d_k, d_v, ...) -> (y, S_T, lambda_T)
   forward_varlen(q, k, v, a, qnoise, r, cu_seqlens, max_seqlen, lambda0=None, S0=None,
                  variant=..., chunk=64) -> (o, S_T, lambda_T)   (a packed batch)
   mobius_scan(k, a, qnoise, r, lambda0=None, variant=..., chunk=64) -> dict
@@ -23,6 +24,7 @@ Functions (same names as the C entry points):
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 
@@ -42,7 +44,8 @@ EXPORTS = (
     "kdn_backward_workspace_bytes", "kdn_backward", "kdn_backward_events",
     "kdn_forward_keep", "kdn_backward_kept", "kdn_backward_kept_events",
     "kdn_decode_step_indexed", "kdn_forward_varlen_workspace_bytes", "kdn_forward_varlen",
-    "kdn_dense_gain",
+    "kdn_dense_gain", "kdn_blas_create", "kdn_blas_destroy", "kdn_layer_workspace_bytes",
+    "kdn_layer_forward", "kdn_layer_forward_events",
 )
 
 
@@ -50,6 +53,11 @@ class KdnDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "B", "H", "T", "d_k", "d_v", "chunk", "variant", "qkv_dtype", "gate_dtype",
         "gain_dtype")]
+
+
+class KdnLayerDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "B", "T", "H", "d_model", "d_k", "d_v", "chunk", "variant", "dtype")]
 
 
 class KdnError(RuntimeError):
@@ -93,6 +101,13 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_forward_keep.argtypes = [D] + [P] * 11 + [P, S, P]
     lib.kdn_decode_step_indexed.argtypes = [D] + [P] * 9 + [ctypes.c_int32, P, P]
     lib.kdn_dense_gain.argtypes = [D] + [P] * 8
+    L = ctypes.POINTER(KdnLayerDesc)
+    lib.kdn_blas_create.argtypes = [ctypes.POINTER(P)]
+    lib.kdn_blas_destroy.argtypes = [P]
+    lib.kdn_layer_workspace_bytes.argtypes = [L]
+    lib.kdn_layer_workspace_bytes.restype = S
+    lib.kdn_layer_forward.argtypes = [L] + [P] * 11 + [S, P]
+    lib.kdn_layer_forward_events.argtypes = [L] + [P] * 11 + [S, P, ctypes.POINTER(P)]
     lib.kdn_forward_varlen_workspace_bytes.argtypes = [D]
     lib.kdn_forward_varlen_workspace_bytes.restype = S
     lib.kdn_forward_varlen.argtypes = [D, P, ctypes.c_int32] + [P] * 12 + [S, P]
@@ -267,6 +282,80 @@ def forward_dense(q, k, v, a, qnoise, r, P0=None, S0=None, chunk=64):
     w, P_T = dense_gain(k, a, qnoise, r, P0)
     o, S_T = chunk_delta(q, k, v, a, w, S0, chunk=chunk)
     return o, S_T, P_T
+
+
+_blas = None
+
+
+def blas_handle():
+    """This process's rocBLAS handle for the layer's GEMMs (created on first use,
+    freed at exit)."""
+    global _blas
+    if _blas is None:
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check(lib.kdn_blas_create(ctypes.byref(h)), "kdn_blas_create")
+        _blas = h
+        atexit.register(lambda: lib.kdn_blas_destroy(h))
+    return _blas
+
+
+def make_layer_desc(B, T, H, d_model, d_k, d_v, chunk, variant, dtype) -> KdnLayerDesc:
+    d = KdnLayerDesc()
+    d.B, d.T, d.H, d.d_model, d.d_k, d.d_v, d.chunk = B, T, H, d_model, d_k, d_v, chunk
+    d.variant = _variant(variant)
+    d.dtype = dtype
+    return d
+
+
+def layer_workspace_bytes(d: KdnLayerDesc) -> int:
+    return int(load_library().kdn_layer_workspace_bytes(ctypes.byref(d)))
+
+
+def layer_forward(x, W_in, b_gate, W_out, H, d_k, d_v, lambda0=None, S0=None,
+                  variant="diagonal", chunk=64, workspace=None, events=None):
+    """KDN layer on given weights (kdn_layer_forward): x [B,T,D] -> y [B,T,D].
+    W_in [D, H(2 d_k + d_v) + 3H], b_gate float32 [3H], W_out [H d_v, D], all
+    but b_gate in x's dtype.  Returns (y, S_T, lambda_T).  events: optional 10
+    torch.cuda.Event around the five stages."""
+    lib = load_library()
+    for n, t in (("x", x), ("W_in", W_in), ("b_gate", b_gate), ("W_out", W_out)):
+        _gpu(t, n)
+    B, T, D = x.shape
+    code = _dtype_code(x.dtype)
+    n_in = H * (2 * d_k + d_v) + 3 * H
+    if W_in.dtype != x.dtype or tuple(W_in.shape) != (D, n_in):
+        raise ValueError(f"W_in must be {x.dtype} [{D}, {n_in}]")
+    if W_out.dtype != x.dtype or tuple(W_out.shape) != (H * d_v, D):
+        raise ValueError(f"W_out must be {x.dtype} [{H * d_v}, {D}]")
+    if b_gate.dtype != torch.float32 or tuple(b_gate.shape) != (3 * H,):
+        raise ValueError(f"b_gate must be float32 [{3 * H}]")
+    d = make_layer_desc(B, T, H, D, d_k, d_v, chunk, variant, code)
+    lam_shape = (B, H, d_k) if d.variant == DIAGONAL else (B, H)
+    for n, t, sh in (("lambda0", lambda0, lam_shape), ("S0", S0, (B, H, d_v, d_k))):
+        if t is not None:
+            _gpu(t, n)
+            if t.dtype != torch.float32 or tuple(t.shape) != sh:
+                raise ValueError(f"{n} must be float32 {sh}")
+    need = layer_workspace_bytes(d)
+    if need == 0:
+        raise KdnError("kdn_layer_forward: unsupported layer shape")
+    dev = x.device
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    y = torch.empty((B, T, D), dtype=x.dtype, device=dev)
+    S_T = torch.empty((B, H, d_v, d_k), dtype=torch.float32, device=dev)
+    lam_T = torch.empty(lam_shape, dtype=torch.float32, device=dev)
+    args = (ctypes.byref(d), blas_handle(), _ptr(x), _ptr(W_in), _ptr(b_gate), _ptr(W_out),
+            _ptr(lambda0), _ptr(S0), _ptr(y), _ptr(S_T), _ptr(lam_T), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream())
+    if events is None:
+        _check(lib.kdn_layer_forward(*args), "kdn_layer_forward")
+    else:
+        if len(events) != 10:
+            raise ValueError("events: 10 entries (start and stop of five stages)")
+        arr = (ctypes.c_void_p * 10)(*[None if e is None else e.cuda_event for e in events])
+        _check(lib.kdn_layer_forward_events(*args, arr), "kdn_layer_forward_events")
+    return y, S_T, lam_T
 
 
 def forward_varlen(q, k, v, a, qnoise, r, cu_seqlens, max_seqlen, lambda0=None, S0=None,

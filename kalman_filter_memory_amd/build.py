@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkdn.so")
-SOURCES = ["kdn_api.cpp", "kdn_scan.hip", "kdn_chunk.hip", "kdn_decode.hip", "kdn_bwd.hip", "kdn_dense.hip"]
+SOURCES = ["kdn_api.cpp", "kdn_scan.hip", "kdn_chunk.hip", "kdn_decode.hip", "kdn_bwd.hip", "kdn_dense.hip",
+           "kdn_layer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -45,7 +46,8 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp,
+           "-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)

@@ -171,3 +171,30 @@ def config_inputs(index: int, variant: str | None = None, **overrides) -> dict:
                          variant=variant or cfg["variant"], seed=seed,
                          qkv_dtype=cfg["qkv_dtype"], gate_dtype=cfg["gate_dtype"],
                          a_mu=cfg["a_mu"])
+
+
+def layer_inputs(B, T, H, D, dk, dv, *, variant=DIAGONAL, dtype="f32", seed=0) -> dict:
+    """Inputs and random weights of one KDN layer call, as float32 numpy arrays
+    (bf16-exact if dtype='bf16').
+
+    x [B,T,D] standard normal; W_in [D, H(2dk+dv)+3H] and W_out [H*dv, D] with
+    entries N(0, 1/fan_in); b_gate [3H] float32 = (2, -3, 0) per gate, so that
+    with unit-variance logits the gates follow the layer workload's recipe
+    (decay logits N(2, 1), process-noise logits N(-3, 1), observation-noise
+    logits N(0, 1)); lambda0 and S0 as in forward_inputs.
+    """
+    rng = np.random.default_rng(seed)
+    n_in = H * (2 * dk + dv) + 3 * H
+    out = {
+        "x": _round(rng.standard_normal((B, T, D)), dtype),
+        "W_in": _round(rng.standard_normal((D, n_in)) / math.sqrt(D), dtype),
+        "W_out": _round(rng.standard_normal((H * dv, D)) / math.sqrt(H * dv), dtype),
+        "b_gate": np.concatenate([np.full(H, 2.0), np.full(H, -3.0), np.zeros(H)]).astype(
+            np.float32),
+    }
+    lam_shape = (B, H, dk) if variant == DIAGONAL else (B, H)
+    out["lambda0"] = rng.uniform(0.5, 2.0, lam_shape).astype(np.float32)
+    out["S0"] = rng.normal(0.0, math.sqrt(0.1), (B, H, dv, dk)).astype(np.float32)
+    out.update(variant=variant, dtype=dtype, H=H, dk=dk, dv=dv)
+    return out
+

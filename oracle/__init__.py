@@ -8,7 +8,9 @@ it with gcc and marshals numpy arrays through ctypes.
 
 Which passage each step follows is stated in the header of ``kdn_oracle.c``
 ("Kalman Delta Networks: Uncertainty-aware Associative Memory", English
-abstract; ai-feeds.com summary, section 方法, steps 1-3).
+abstract; ai-feeds.com summary, section 方法, steps 1-3).  The layer around
+the recurrence (projections, normalisation, gates) is ``oracle.layer``, in
+numpy float64.
 """
 from __future__ import annotations
 

@@ -160,6 +160,36 @@ def test_dense_gain_host_side_checks(lib):
     assert lib.kdn_dense_gain(ctypes.byref(_desc(B=0, d_k=64)), *([None] * 7), None) == 0
 
 
+def test_layer_host_side_checks(lib):
+    """kdn_layer_workspace_bytes: the documented layout at the layer workload;
+    0 for shapes the layer does not take; argument errors before any launch."""
+    d = kdn.make_layer_desc(8, 4096, 16, 2048, 128, 128, 64, "diagonal", kdn.BF16)
+    need = kdn.layer_workspace_bytes(d)
+    M, BH, T = 8 * 4096, 128, 4096
+    n_in = 16 * (2 * 128 + 128) + 48
+    ldz = (n_in + 15) // 16 * 16
+    core = kdn.forward_workspace_bytes(_desc(B=8, H=16, T=4096, d_k=128, d_v=128, chunk=64))
+    expect = (M * ldz * 2 + 2 * BH * T * 128 * 2 + BH * T * 128 * 2 + 3 * BH * T * 2
+              + BH * T * 128 * 2 + core)
+    assert expect <= need <= expect + 9 * 256
+    assert kdn.layer_workspace_bytes(
+        kdn.make_layer_desc(1, 16, 2, 100, 32, 32, 16, "diagonal", kdn.F32)) == 0
+    assert kdn.layer_workspace_bytes(
+        kdn.make_layer_desc(1, 16, 90, 64, 32, 32, 16, "diagonal", kdn.F32)) == 0
+    assert kdn.layer_workspace_bytes(
+        kdn.make_layer_desc(1, 16, 2, 64, 48, 32, 16, "diagonal", kdn.F32)) == 0
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake] * 4 + [None, None, fake, None, None, fake]
+    small = kdn.make_layer_desc(1, 16, 2, 64, 32, 32, 16, "diagonal", kdn.F32)
+    n = kdn.layer_workspace_bytes(small)
+    assert lib.kdn_layer_forward(ctypes.byref(small), None, *args, n, None) == 1
+    assert lib.kdn_layer_forward(ctypes.byref(small), fake, *args, n - 1, None) == 4
+    odd = [ctypes.c_void_p(0x1004)] + args[1:]
+    assert lib.kdn_layer_forward(ctypes.byref(small), fake, *odd, n, None) == 5
+    none = kdn.make_layer_desc(0, 16, 2, 64, 32, 32, 16, "diagonal", kdn.F32)
+    assert lib.kdn_layer_forward(ctypes.byref(none), None, *([None] * 10), 0, None) == 0
+
+
 def test_python_binding_refuses_cpu_tensors(lib):
     import torch
     x = torch.zeros(1, 1, 4, 32)
