@@ -207,7 +207,7 @@ kdn_status kdn_blas_destroy(void *handle);
 
 /* Bytes of workspace kdn_layer_forward needs (0 if the descriptor is invalid:
  * the recurrence's limits of kdn_validate, d_model a positive multiple of 8,
- * 3H <= 256).  Host-only. */
+ * 3H <= 256, B*T <= 2^31 - 1).  Host-only. */
 size_t kdn_layer_workspace_bytes(const kdn_layer_desc *d);
 
 /* The layer forward.  lambda0, S0 (NULL: ones, zeros), S_T, lambda_T (NULL:

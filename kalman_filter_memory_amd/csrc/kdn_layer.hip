@@ -243,6 +243,9 @@ kdn_status check_layer(const kdn_layer_desc* d) {
     // every row of the GEMM operands starts 16-byte aligned
     if (d->d_model % 8 != 0 || d->d_model == 0) return KDN_ERR_UNSUPPORTED;
     if (3 * d->H > 256) return KDN_ERR_UNSUPPORTED;  // gate threads of layer_in_kernel
+    // token rows index grid.x and rocBLAS's 32-bit sizes
+    if (int64_t(d->B) * d->T > INT32_MAX) return KDN_ERR_UNSUPPORTED;
+    if (int64_t(d->H) * (2 * d->d_k + d->d_v + 3) > INT32_MAX / 16) return KDN_ERR_UNSUPPORTED;
     const kdn_desc c = core_desc(d);
     return kdn_validate(&c);
 }

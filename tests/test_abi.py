@@ -178,6 +178,8 @@ def test_layer_host_side_checks(lib):
         kdn.make_layer_desc(1, 16, 90, 64, 32, 32, 16, "diagonal", kdn.F32)) == 0
     assert kdn.layer_workspace_bytes(
         kdn.make_layer_desc(1, 16, 2, 64, 48, 32, 16, "diagonal", kdn.F32)) == 0
+    assert kdn.layer_workspace_bytes(
+        kdn.make_layer_desc(1 << 16, 1 << 16, 2, 64, 32, 32, 16, "diagonal", kdn.F32)) == 0
     fake = ctypes.c_void_p(0x1000)
     args = [fake] * 4 + [None, None, fake, None, None, fake]
     small = kdn.make_layer_desc(1, 16, 2, 64, 32, 32, 16, "diagonal", kdn.F32)
