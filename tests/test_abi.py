@@ -192,6 +192,15 @@ def test_layer_host_side_checks(lib):
     assert lib.kdn_layer_forward(ctypes.byref(none), None, *([None] * 10), 0, None) == 0
 
 
+def test_smoke_cases_are_supported(lib):
+    """The smoke check's forward calls are shapes the library builds."""
+    import __graft_entry__ as g
+    for variant, dtype, _, chunk in g.SMOKE_CASES:
+        code = kdn.BF16 if dtype == "bf16" else kdn.F32
+        d = kdn.make_desc(2, 2, 150, 128, 64, chunk, variant, code, code)
+        assert kdn.validate(d) == 0, (variant, dtype, chunk)
+
+
 def test_python_binding_refuses_cpu_tensors(lib):
     import torch
     x = torch.zeros(1, 1, 4, 32)
