@@ -464,3 +464,29 @@ def test_dense_exact_kdn_extreme_decays(dk):
     e_o, e_s, e_p = (normwise(host(x), ref[n]) for x, n in ((o, "o"), (S_T, "S_T"), (P_T, "P_T")))
     say(f"    err o {e_o:.2e}  S_T {e_s:.2e}  P_T {e_p:.2e}")
     assert e_o <= TOL_F32 and e_s <= TOL_F32 and e_p <= 1e-4
+
+
+def test_dense_exact_kdn_workload_bf16_B8_H16_T4096_d128_sampled_heads():
+    """The exact forward at the layer workload's full size, in the launch
+    configuration the benchmark times (P0 = I, chunk 64); three sampled heads
+    against the oracle's dense filter."""
+    say("[gpu] generating workload 2 for the exact filter")
+    inp = config_inputs(2)
+    t = forward_tensors(inp)
+    say(f"[gpu] exact forward full size {inp['q'].shape}")
+    o, S_T, P_T = kdn.forward_dense(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], None,
+                                    t["S0"], chunk=64)
+    torch.cuda.synchronize()
+    o, S_T, P_T = host(o), host(S_T), host(P_T)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(P_T))
+    heads = [(0, 0), (3, 7), (7, 15)]
+    sub = head_slice(inp, heads)
+    say(f"[cpu] dense oracle on heads {heads}")
+    ref = oracle.forward_dense(sub["q"], sub["k"], sub["v"], sub["a"], sub["nu"], sub["r"],
+                               None, sub["S0"])
+    idx = tuple(np.array(heads).T)
+    e_o = normwise(o[idx][:, None], ref["o"])
+    e_s = normwise(S_T[idx][:, None], ref["S_T"])
+    e_p = normwise(P_T[idx][:, None], ref["P_T"])
+    say(f"    sampled heads: err o {e_o:.2e}  S_T {e_s:.2e}  P_T {e_p:.2e}")
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16 and e_p <= 1e-4
