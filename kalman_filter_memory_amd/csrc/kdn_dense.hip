@@ -19,7 +19,9 @@
 // becomes s <- a^2 s and nu / s added to the diagonal of Ps, so that it costs
 // nothing per entry; the update P^- - (P^- k)(P^- k)^T / den becomes
 // Ps - c u u^T with u = Ps^- k and c = s / den, and the gain is c u.  When s
-// leaves [2^-32, 2^32] (or a is zero) it is folded into Ps.
+// leaves [2^-32, 2^32] (or a is zero) it is folded into Ps.  The two
+// reciprocals per token are v_rcp_f32 (about 1 ulp), off the division's longer
+// instruction sequence on the token's critical path.
 //
 // Keys and gates arrive in blocks of NB tokens: the next block is loaded into
 // registers while the current one is worked on and moved into the other LDS
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(256) void dense_gain_kernel(
                 sc = sn;
             }
             if (diag) {
-                const float add = nut / sc;
+                const float add = nut * rcp(sc);
 #pragma unroll
                 for (int i = 0; i < BS; ++i) P[i][i] += add;
             }
@@ -176,7 +178,8 @@ __global__ __launch_bounds__(256) void dense_gain_kernel(
             if (lane == 0) denp[b][wave] = dw;
             sync_lds();
             const float rt = gb[buf][2][tt];
-            const float c = sc / (rt + sc * (denp[b][0] + denp[b][1] + denp[b][2] + denp[b][3]));
+            const float c =
+                sc * rcp(rt + sc * (denp[b][0] + denp[b][1] + denp[b][2] + denp[b][3]));
             // rank-one update of Ps and the gain rows c u
             float ucol[BS];
 #pragma unroll
