@@ -161,8 +161,8 @@ kdn_status kdn_decode_step(const kdn_desc *d, const void *q, const void *k, cons
                            const void *a, const void *qnoise, const void *r, float *S,
                            float *lambda, void *o, void *stream);
 
-/* Exact KDN gain (SURVEY's next row f3; "Kalman Delta Networks", English
- * abstract: exact tracking entails a dense, state-dependent Riccati recursion):
+/* Exact KDN gain ("Kalman Delta Networks", English abstract: exact tracking
+ * entails a dense, state-dependent Riccati recursion):
  * per head one d_k x d_k covariance P, per token P^- = a^2 P + qnoise I,
  * w = P^- k / (k^T P^- k + r), P = P^- - (P^- k)(P^- k)^T / (k^T P^- k + r).
  * k [B,H,T,d_k] (qkv_dtype); a, qnoise, r [B,H,T]; P0 [B,H,d_k,d_k] float32
@@ -232,8 +232,9 @@ kdn_status kdn_layer_forward_events(const kdn_layer_desc *d, void *blas, const v
  * alone (d->B sequences, d->T tokens per head in all). */
 size_t kdn_forward_varlen_workspace_bytes(const kdn_desc *d);
 
-/* Forward of a packed batch of d->B variable-length sequences (SURVEY's
- * serving path: prefill of many prompts in one call).  Every head's rows hold
+/* Forward of a packed batch of d->B variable-length sequences (serving: the
+ * prefill of many prompts in one call; "Kalman Delta Networks", English
+ * abstract: efficient long-context inference).  Every head's rows hold
  * the sequences one after another: q, k [H, T, d_k]; v, o [H, T, d_v]; a,
  * qnoise, r [H, T], with T = d->T the total token count; sequence s has rows
  * cu_seqlens[s] .. cu_seqlens[s+1] (device int32 [B+1], non-decreasing, from 0
@@ -251,8 +252,8 @@ kdn_status kdn_forward_varlen(const kdn_desc *d, const int32_t *cu_seqlens, int3
                               const float *S0, void *o, float *S_T, float *lambda_T, void *ws,
                               size_t ws_bytes, void *stream);
 
-/* Continuous-batching decode step (SURVEY's serving path; same pages:
- * constant-memory decoding): kdn_decode_step for d->B active sequences whose
+/* Continuous-batching decode step (serving; "Kalman Delta Networks", English
+ * abstract: constant-memory decoding): kdn_decode_step for d->B active sequences whose
  * states live in a cache of n_slots entries.  S_cache [n_slots,H,d_v,d_k] and
  * lambda_cache [n_slots,H,d_k] (or [n_slots,H]) float32 are read and updated in
  * place at the slots slot[0..B-1] (device int32); q, k, v, a, qnoise, r and o
