@@ -1,0 +1,45 @@
+"""Host-side checks of bench.py (no GPU): the refusal of several GPUs, and the
+algorithmic byte counts that the roofline's achieved rate divides by, at the
+layer workload (B8 H16 T4096, d 128, chunk 64, bf16)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_forward_algorithmic_bytes_at_the_layer_workload():
+    B, H, T, d, C = 8, 16, 4096, 128, 64
+    by, _ = bench.algorithmic(B, H, T, d, d, C)
+    n, bh, nc = B * H * T, B * H, T // C
+    # keys (bf16) and three bf16 gates in, one fp32 Moebius product (4 floats)
+    # per (head, chunk, key dim) out
+    assert by["scan_reduce"] == n * d * 2 + 3 * n * 2 + bh * nc * d * 16
+    # per token-head: k 256 + gates 6 + w 256 + T 128 + g 4 + boundary precision 8
+    assert by["chunk_prep"] == pytest.approx(n * (256 + 6 + 256 + 128 + 4 + 8), rel=1e-3)
+    # q, k, w, v 1024 + T 128 + g 4 + o 256 per token-head, plus S0 and S_T
+    assert by["chunk_state"] == pytest.approx(n * (1024 + 128 + 4 + 256)
+                                              + 2 * bh * d * d * 4, rel=1e-3)
+    assert round(by["chunk_state"] / 1e6, 1) == 757.1
+
+
+def test_backward_algorithmic_bytes_cover_every_stage():
+    by, fl = bench.algorithmic_backward(8, 16, 4096, 128, 128, 64)
+    assert set(by) == set(bench.BWD_STAGES)
+    assert all(v > 0 for v in by.values())
+    # the gradient stages move more than the forward's state pass
+    assert by["bwd_grad"] > by["bwd_state"] > bench.algorithmic(8, 16, 4096, 128, 128, 64)[0][
+        "chunk_state"]
