@@ -97,3 +97,25 @@ def test_layer_is_bitwise_deterministic():
     b = _gpu(p, t=t)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+def test_layer_with_stage_events_matches_and_times_every_stage():
+    """kdn_layer_forward_events (the benchmark's timing path): the same output,
+    bit for bit, and a positive time for each of the five stages."""
+    p = layer_inputs(2, 200, 4, 128, 32, 32, dtype="bf16", seed=35)
+    t = _tensors(p)
+    say("[gpu] layer with stage events")
+    plain = _gpu(p, t=t)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    y, S_T, lam_T = kdn.layer_forward(t["x"], t["W_in"], t["b_gate"], t["W_out"], p["H"], p["dk"],
+                                      p["dv"], t["lambda0"], t["S0"], variant=p["variant"],
+                                      events=evs)
+    torch.cuda.synchronize()
+    for a, b in zip(plain, (host(y), host(S_T), host(lam_T))):
+        np.testing.assert_array_equal(a, b)
+    times = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(5)]
+    say(f"    stage ms {['%.3f' % x for x in times]}")
+    assert all(x > 0 for x in times)
