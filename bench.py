@@ -210,6 +210,8 @@ def run(args):
         res["roofline"]["traffic_src_sha256"] = sha
     del t, ws, out
     torch.cuda.empty_cache()
+    if not args.no_isotropic:
+        res["isotropic"] = bench_isotropic(args)
     if not args.no_backward:
         res["backward"] = bench_backward(args, inp)
     if not args.no_dense:
@@ -448,6 +450,58 @@ def bench_dense(args, inp):
             "bound": "latency (sequential over tokens; one workgroup per head)"}
 
 
+def bench_isotropic(args):
+    """The isotropic variant's forward on the same workload (one scalar
+    precision per head; inputs of the same recipe with a per-head lambda0)."""
+    import numpy as np
+    import torch
+
+    import kalman_filter_memory_amd as kdn
+    from kdn_inputs import config_inputs
+
+    dev = torch.device("cuda:0")
+    B, H, T, dk, dv, C = (WL[x] for x in ("B", "H", "T", "dk", "dv", "chunk"))
+    inp = config_inputs(2, variant="isotropic")
+    bf = torch.bfloat16
+    t = {n: torch.from_numpy(inp[n]).to(dev, bf) for n in ("q", "k", "v", "a", "nu", "r")}
+    lam0 = torch.from_numpy(inp["lambda0"]).to(dev)
+    S0 = torch.from_numpy(inp["S0"]).to(dev)
+    d = kdn.make_desc(B, H, T, dk, dv, C, "isotropic", kdn.BF16, kdn.BF16)
+    ws = torch.empty(kdn.forward_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    out = (torch.empty((B, H, T, dv), dtype=bf, device=dev),
+           torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev),
+           torch.empty((B, H), dtype=torch.float32, device=dev))
+
+    def step(events=None):
+        kdn.forward(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], lam0, S0, "isotropic", C,
+                    workspace=ws, out=out, events=events)
+
+    ramp(step, args.ramp_ms)
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    steps = 50
+    log(f"timing {steps} isotropic forward steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(KERNELS))]
+           for _ in range(10)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for row in evs:
+        step(events=row)
+    torch.cuda.synchronize()
+    kern = {k: round(float(np.mean([row[2 * i].elapsed_time(row[2 * i + 1]) for row in evs]))
+                     * 1e3, 2) for i, k in enumerate(KERNELS)}
+    return {"workload": f"iso_bf16_B{B}_H{H}_T{T}_d{dk}", "ms_per_step": round(ms, 4),
+            "tokens/s": round(B * T / (ms * 1e-3), 1), "kernels_us": kern}
+
+
 LAYER = dict(B=8, T=4096, H=16, D=2048, dk=128, dv=128, chunk=64)
 LAYER_STAGES = ("gemm_in", "norm_gates", "recurrence", "readout_rows", "gemm_out")
 
@@ -600,6 +654,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-isotropic", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,

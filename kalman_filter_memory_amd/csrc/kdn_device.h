@@ -89,6 +89,39 @@ __device__ __forceinline__ float lane_value(float x, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
+// N contiguous elements of E at p as floats, in vector loads (p aligned to
+// N * sizeof(E) bytes, or to 16 when that is more; N * sizeof(E) a power of two
+// of at least 4 bytes)
+template <typename E, int N>
+__device__ __forceinline__ void load_vec(const E* p, float* f) {
+    constexpr int W = N * int(sizeof(E)) / 4;  // 32-bit words
+    uint32_t u[W];
+    if constexpr (W % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < W / 4; ++i) {
+            const u32x4 x = reinterpret_cast<const u32x4*>(p)[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) u[4 * i + j] = x[j];
+        }
+    } else if constexpr (W == 2) {
+        typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t x = *reinterpret_cast<const u32x2_t*>(p);
+        u[0] = x[0];
+        u[1] = x[1];
+    } else {
+        u[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+        if constexpr (sizeof(E) == 4) {
+            f[i] = __uint_as_float(u[i]);
+        } else {
+            f[2 * i] = __uint_as_float(u[i] << 16);
+            f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    }
+}
+
 // x of another lane of the same row of 16, chosen by a DPP control (quad_perm,
 // row_mirror, row_half_mirror ...), as a source modifier of one VALU move
 template <int CTRL> __device__ __forceinline__ float dpp(float x) {

@@ -215,6 +215,28 @@ __device__ __forceinline__ float row_sq(const E* p) {
     return s;
 }
 
+// |k_t|^2 of a chunk's tokens (n <= 64 rows from k0), token t's value
+// returned in lane t: 16 lanes read each key row in contiguous pieces (one
+// vector load of d_k/16 elements per lane), add them with DPP over their row
+// of 16 lanes, and hand the sum to the token's lane through the wave's LDS
+// slice `sq` (written and read by this wave only, in order).
+template <typename E, int DK>
+__device__ __forceinline__ float chunk_row_sq(const E* __restrict__ k0, int n, int lane,
+                                              float* sq) {
+    constexpr int EPL = DK / 16;
+    const int g = lane >> 4, l16 = lane & 15;
+    for (int t = g; t < n; t += 4) {  // uniform within each row of 16 lanes
+        float x[EPL];
+        load_vec<E, EPL>(k0 + size_t(t) * DK + l16 * EPL, x);
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) s = fmaf(x[i], x[i], s);
+        s = group_sum<16>(s);
+        if (l16 == 0) sq[t] = s;
+    }
+    return lane < n ? sq[lane] : 0.f;
+}
+
 template <typename E, int DK, bool VL>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_iso_kernel(
     const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
@@ -225,12 +247,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_iso_kernel(
     const Slab sl = slab_of<VL>(blockIdx.y, T, NC, pk);
     if (c >= sl.nc) return;
     const int t0 = c * C, n = min(C, sl.T - t0);
+    __shared__ float sq[kWavesPerBlock][kWave];
+    const float kk = chunk_row_sq<E, DK>(k + (sl.row0 + t0) * DK, n, lane, sq[wave]);
     M2 P = {1.f, 0.f, 0.f, 1.f};
     if (lane < n) {
         const size_t tok = sl.row0 + t0 + lane;
         const float at = load_gate(a, tok, gate_bf16), nut = load_gate(nu, tok, gate_bf16);
         const float rt = load_gate(r, tok, gate_bf16);
-        const float b = row_sq<E, DK>(k + tok * DK) / (static_cast<float>(DK) * rt);
+        const float b = kk / (static_cast<float>(DK) * rt);
         P = token_matrix(b, at * at, nut);
     }
     // ordered tree product: later tokens multiply on the left
