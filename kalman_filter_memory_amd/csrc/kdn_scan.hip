@@ -204,17 +204,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
     }
 }
 
-template <typename E, int DK>
-__device__ __forceinline__ float row_sq(const E* p) {
-    float s = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < DK; ++i) {
-        const float x = to_f<E>(p[i]);
-        s += x * x;
-    }
-    return s;
-}
-
 // |k_t|^2 of a chunk's tokens (n <= 64 rows from k0), token t's value
 // returned in lane t: 16 lanes read each key row in contiguous pieces (one
 // vector load of d_k/16 elements per lane), add them with DPP over their row
@@ -390,6 +379,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void emit_iso_kernel(
     if (c >= NC) return;
     const int t0 = c * C, n = min(C, T - t0);
     const float lam0 = lam_chunk[bh * (NC + 1) + c];
+    __shared__ float sq[kWavesPerBlock][kWave];
+    const float kk = chunk_row_sq<E, DK>(k + (bh * T + t0) * DK, n, lane, sq[wave]);
     M2 P = {1.f, 0.f, 0.f, 1.f};
     float at = 1.f, nut = 0.f;
     if (lane < n) {
@@ -397,7 +388,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void emit_iso_kernel(
         at = load_gate(a, tok, gate_bf16);
         nut = load_gate(nu, tok, gate_bf16);
         const float rt = load_gate(r, tok, gate_bf16);
-        const float b = row_sq<E, DK>(k + tok * DK) / (static_cast<float>(DK) * rt);
+        const float b = kk / (static_cast<float>(DK) * rt);
         P = token_matrix(b, at * at, nut);
     }
     // inclusive prefix product over the chunk's tokens (Hillis-Steele)
