@@ -344,16 +344,24 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
             }
             sync_lds();
             if (wave == 0) {
-                const float kk_l = lane < C ? sden[lane] : 0.f;
-                float lam = in.lam[0];
-                float den_l = 1.f;
-                for (int t = 0; t < C; ++t) {
-                    const float kk = lane_value(kk_l, t);
-                    const float lm = lam * rcp(fmaf(lane_value(gnu, t), lam, lane_value(ga2, t)));
-                    if (lane == t) den_l = 1.f / (kk + lane_value(gr, t) * lm);
-                    lam = fmaf(kk, lane_value(gir, t) * (1.f / static_cast<float>(DK)), lm);
+                // the chunk's precision walk as an inclusive prefix product of the
+                // tokens' Moebius maps (later tokens on the left; padded tokens are
+                // the identity), then each token's predictive precision from the
+                // posterior after the token before it
+                const float kk = lane < C ? sden[lane] : 0.f;
+                const float bt = kk * gir * (1.f / static_cast<float>(DK));
+                M2 P = {1.f + bt * gnu, bt * ga2, gnu, ga2};
+#pragma unroll
+                for (int off = 1; off < kWave; off <<= 1) {
+                    const M2 o = {__shfl_up(P.a, off, kWave), __shfl_up(P.b, off, kWave),
+                                  __shfl_up(P.c, off, kWave), __shfl_up(P.d, off, kWave)};
+                    if (lane >= off) P = mob_renorm(mob_mul(P, o));
                 }
-                if (lane < C) sden[lane] = den_l;
+                const float lam_incl = mob_apply(P, in.lam[0]);
+                float lam = __shfl_up(lam_incl, 1, kWave);
+                if (lane == 0) lam = in.lam[0];
+                const float lm = lam * rcp(fmaf(gnu, lam, ga2));
+                if (lane < C) sden[lane] = 1.f / (kk + gr * lm);
             }
             sync_lds();
             constexpr int VPR = DK / V;
