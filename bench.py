@@ -35,8 +35,10 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic(B, H, T, dk, dv, C):
-    """Algorithmic bytes and flops of each forward kernel (bf16 inputs).
+def algorithmic(B, H, T, dk, dv, C, variant="diagonal"):
+    """Design bytes and flops of each forward kernel (bf16 inputs): what this
+    design's kernels read and write, the intermediates it passes between
+    kernels through HBM (w, T) included.
 
     Bytes count every tensor a kernel must read or write once; flops count
     2 per multiply-add of the products the kernel performs, triangular ones at
@@ -46,22 +48,24 @@ def algorithmic(B, H, T, dk, dv, C):
     bh = B * H
     e = 2                   # bf16 bytes
     g = 3 * e               # a, nu, r per token-head
+    nl = dk if variant == "diagonal" else 1  # precisions per token
     by = {
-        # read k and the three gates, write one float4 Moebius product per (chunk, key dim)
-        "scan_reduce": n * (dk * e + g) + bh * nc * dk * 16,
+        # read k and the three gates, write one float4 Moebius product per (chunk, precision)
+        "scan_reduce": n * (dk * e + g) + bh * nc * nl * 16,
         # read the chunk products, write chunk-boundary precisions
-        "scan_carry": bh * nc * dk * 16 + bh * (nc + 1) * dk * 4 + bh * dk * 4 * 2,
+        "scan_carry": bh * nc * nl * 16 + bh * (nc + 1) * nl * 4 + bh * nl * 4 * 2,
         # read k, gates, boundary precisions; write w, T and the log2 decays
-        "chunk_prep": n * (dk * e + g) + bh * nc * dk * 4 + n * dk * e + bh * nc * C * C * e
+        "chunk_prep": n * (dk * e + g) + bh * nc * nl * 4 + n * dk * e + bh * nc * C * C * e
         + n * 4,
         # read q, k, v, w, T, log2 decays, S0; write o, S_T
         "chunk_state": n * (3 * dk + dv) * e + n * 4 + bh * nc * C * C * e + n * dv * e
         + 2 * bh * dv * dk * 4,
     }
     fl = {
-        # six multiply-adds per (token, key dim) for the factorized Moebius step
-        "scan_reduce": n * dk * 12,
-        "scan_carry": bh * nc * dk * 5,
+        # six multiply-adds per (token, precision) for the factorized Moebius
+        # step (isotropic: plus |k|^2)
+        "scan_reduce": n * nl * 12 + (0 if variant == "diagonal" else n * 2 * dk),
+        "scan_carry": bh * nc * nl * 5,
         # gain (~8 per key dim), strict lower triangle of K W^T (C dk), triangular
         # inverse (~C^2/3)
         "chunk_prep": n * (8 * dk + C * dk + C * C // 3),
@@ -97,58 +101,92 @@ def _traffic():
     return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"], sha
 
 
-def run(args):
+def bytes_8d(B, H, T, dk, dv):
+    """The chunk stage's algorithmic bytes by its per-unit figure: per
+    token-head, read q, k, v and the gain key w (bf16), the decay a (bf16),
+    write o (bf16), and the head's S0 read and S_T write (fp32) amortised over
+    its T tokens.  1,314 B per token-head at d_k = d_v = 128, T = 4096."""
+    n = B * H * T
+    e = 2
+    return n * ((3 * dk + dv) * e + e + dv * e) + B * H * 2 * dv * dk * 4
+
+
+def _stats(xs):
+    import numpy as np
+
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "mean": round(float(a.mean()), 2),
+            "n": int(a.size)}
+
+
+def bench_forward(args, inp, variant, steps, cold_reps, label):
+    """One forward workload: wall-clock mean over `steps` back-to-back steps;
+    per-step times (warm: back to back; cold: each step after a 512 MiB write
+    that evicts the L2 and Infinity caches) as median / p10 / p90 from HIP
+    events; per-kernel times from the start and stop events that each kernel's
+    own dispatch records on the launch stream."""
     import numpy as np
     import torch
 
     import kalman_filter_memory_amd as kdn
-    from kdn_inputs import config_inputs
 
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda:0")
-    B, H, T, dk, dv, C = (WL[x] for x in ("B", "H", "T", "dk", "dv", "chunk"))
-    log("generating inputs")
-    inp = config_inputs(2)
+    B, H, T, dk = inp["k"].shape
+    dv = inp["v"].shape[-1]
+    C = args.chunk
     bf = torch.bfloat16
     t = {n: torch.from_numpy(inp[n]).to(dev, bf) for n in ("q", "k", "v", "a", "nu", "r")}
     lam0 = torch.from_numpy(inp["lambda0"]).to(dev)
     S0 = torch.from_numpy(inp["S0"]).to(dev)
-    d = kdn.make_desc(B, H, T, dk, dv, C, "diagonal", kdn.BF16, kdn.BF16)
+    d = kdn.make_desc(B, H, T, dk, dv, C, variant, kdn.BF16, kdn.BF16)
     ws = torch.empty(kdn.forward_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    lam_shape = (B, H, dk) if variant == "diagonal" else (B, H)
     out = (torch.empty((B, H, T, dv), dtype=bf, device=dev),
            torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev),
-           torch.empty((B, H, dk), dtype=torch.float32, device=dev))
+           torch.empty(lam_shape, dtype=torch.float32, device=dev))
 
     def step(events=None):
-        kdn.forward(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], lam0, S0, "diagonal", C,
+        kdn.forward(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], lam0, S0, variant, C,
                     workspace=ws, out=out, events=events)
 
-    if args.copy_calibration_mb:
-        nb = args.copy_calibration_mb << 20
-        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).uniform_()
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy calibration: {nb} bytes read and written")
-        del src, dst
     ramp(step, args.ramp_ms)
-    log(f"warmup {args.warmup}")
+    log(f"{label}: warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
+    log(f"{label}: timing {steps} steps")
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = (time.perf_counter() - t0) * 1e3 / steps
 
-    # per-kernel durations: start and stop events recorded by each kernel's own
-    # dispatch on the launch stream (no marker packets between the kernels)
+    # warm per-step distribution (back to back, one event pair per step)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a0, a1 in ev:
+        a0.record()
+        step()
+        a1.record()
+    torch.cuda.synchronize()
+    warm_us = [a0.elapsed_time(a1) * 1e3 for a0, a1 in ev]
+    # cold: a 512 MiB write between the steps evicts every cache level
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    cold_us = []
+    for _ in range(cold_reps):
+        flush.fill_(1.0)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        step()
+        a1.record()
+        torch.cuda.synchronize()
+        cold_us.append(a0.elapsed_time(a1) * 1e3)
+    del flush
+
+    # per-kernel durations from the dispatches' own events
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(KERNELS))]
-           for _ in range(args.steps)]
+           for _ in range(steps)]
     for row in evs:
         for e in row:
             e.record()
@@ -156,26 +194,34 @@ def run(args):
     for row in evs:
         step(events=row)
     torch.cuda.synchronize()
-    kern_ms = {k: float(np.mean([row[2 * i].elapsed_time(row[2 * i + 1]) for row in evs]))
+    kern_us = {k: [row[2 * i].elapsed_time(row[2 * i + 1]) * 1e3 for row in evs]
                for i, k in enumerate(KERNELS)}
-    by, fl = algorithmic(B, H, T, dk, dv, C)
+    kern_mean = {k: float(np.mean(v)) for k, v in kern_us.items()}
+    by, fl = algorithmic(B, H, T, dk, dv, C, variant)
     kernels = {}
     for k in KERNELS:
-        s = kern_ms[k] * 1e-3
-        kernels[k] = {"us": round(kern_ms[k] * 1e3, 2),
-                      "GB/s": round(by[k] / s / 1e9, 1),
-                      "TFLOP/s": round(fl[k] / s / 1e12, 2)}
-    dom = max(KERNELS, key=lambda k: kern_ms[k])
-    s_dom = kern_ms[dom] * 1e-3
-    ach_gbs = by[dom] / s_dom / 1e9
-    traffic, sha = _traffic() if dom == TRAFFIC["kernel"] else (None, None)
-    roofline = {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": dom, "bytes_per_launch": by[dom],
-                "us_per_launch": round(kern_ms[dom] * 1e3, 2)}
-    # the chunk kernels (prep + state) against the bf16 MFMA peak
+        sec = kern_mean[k] * 1e-6
+        kernels[k] = {"us": round(kern_mean[k], 2), "us_stats": _stats(kern_us[k]),
+                      "GB/s": round(by[k] / sec / 1e9, 1),
+                      "TFLOP/s": round(fl[k] / sec / 1e12, 2)}
+    # the dominant kernel (the chunk state pass) against HBM, by the chunk
+    # stage's per-unit bytes; the design's own bytes (which also count the w
+    # and T this design passes from prep to state through HBM) beside it
+    dom = max(KERNELS, key=lambda k: kern_mean[k])
+    s_dom = kern_mean[dom] * 1e-6
+    alg = bytes_8d(B, H, T, dk, dv) if dom == "chunk_state" else by[dom]
+    ach = alg / s_dom / 1e9
+    roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                "bytes_per_launch": alg,
+                "bytes_rule": "q, k, v, w, a read and o written once per token-head, S0 and S_T "
+                              "amortised (1314 B per token-head at d 128, T 4096)"
+                if dom == "chunk_state" else "design bytes",
+                "us_per_launch": round(kern_mean[dom], 2),
+                "design_bytes_per_launch": by[dom],
+                "design_frac": round(by[dom] / s_dom / 1e9 / PEAK_HBM_GBS, 4)}
     n = B * H * T
-    chunk_s = (kern_ms["chunk_prep"] + kern_ms["chunk_state"]) * 1e-3
+    chunk_s = (kern_mean["chunk_prep"] + kern_mean["chunk_state"]) * 1e-6
     mfma = {"kernels": "chunk_prep+chunk_state", "us": round(chunk_s * 1e6, 2),
             "flops_full": chunk_flops_full(n, dk, dv, C),
             "frac_full": round(chunk_flops_full(n, dk, dv, C) / chunk_s / 1e12
@@ -185,33 +231,88 @@ def run(args):
                                     / PEAK_BF16_TFLOPS, 4),
             "flops_recurrent": n * 6 * dk * dv,
             "peak_TFLOP/s": PEAK_BF16_TFLOPS}
-    scan_s = (kern_ms["scan_reduce"] + kern_ms["scan_carry"]) * 1e-3
+    scan_s = (kern_mean["scan_reduce"] + kern_mean["scan_carry"]) * 1e-6
     scan_by = by["scan_reduce"] + by["scan_carry"]
+    scan8 = scan_bytes_8d(B, H, T, dk, variant)
+    res = {"workload": f"{'diag' if variant == 'diagonal' else 'iso'}_bf16_B{B}_H{H}_T{T}_d{dk}",
+           "variant": variant, "ms_per_step": round(ms, 4),
+           "tokens/s": round(B * T / (ms * 1e-3), 1),
+           "step_us_warm": _stats(warm_us), "step_us_cold": _stats(cold_us),
+           "roofline": roofline, "mfma_chunk": mfma,
+           "scan_hbm": {"kernels": "scan_reduce+scan_carry", "us": round(scan_s * 1e6, 2),
+                        "bytes": scan_by, "GB/s": round(scan_by / scan_s / 1e9, 1),
+                        "frac": round(scan_by / scan_s / 1e9 / PEAK_HBM_GBS, 4),
+                        "bytes_8d": scan8,
+                        "frac_8d": round(scan8 / scan_s / 1e9 / PEAK_HBM_GBS, 4)},
+           "kernels": kernels}
+    del t, ws, out
+    torch.cuda.empty_cache()
+    return res
 
+
+def scan_bytes_8d(B, H, T, dk, variant):
+    """The precision scan's per-unit bytes: read k (bf16) and the three gates
+    per token, write one fp32 predictive precision per (token, key dim)
+    (diagonal) or per token (isotropic)."""
+    n = B * H * T
+    return n * (dk * 2 + 6 + (dk * 4 if variant == "diagonal" else 4))
+
+
+def run(args):
+    import torch
+
+    from kdn_inputs import config_inputs
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    B, T = WL["B"], WL["T"]
+    log("generating inputs")
+    inp = config_inputs(2)
+    if args.copy_calibration_mb:
+        dev = torch.device("cuda:0")
+        nb = args.copy_calibration_mb << 20
+        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {nb} bytes read and written")
+        del src, dst
+    head = bench_forward(args, inp, "diagonal", args.steps, args.cold_reps, "forward")
+    ms = head["ms_per_step"]
+    traffic, sha = _traffic()
+    roofline = dict(head["roofline"])
+    if roofline["kernel"] == TRAFFIC["kernel"]:
+        roofline["traffic"] = traffic
+        if traffic is not None:
+            roofline["traffic_src_sha256"] = sha
     res = {
         "metric": "KDN fwd tokens/s (B8 T4096 H16 d128); % MFMA peak; decode GB/s",
         "value": round(B * T / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ramp_ms": args.ramp_ms,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "diag_bf16_B8_H16_T4096_d128", "variant": "diagonal",
-                   "B": B, "H": H, "T": T, "d_k": dk, "d_v": dv, "chunk": C,
-                   "state_dtype": "f32"},
+                   "B": B, "H": WL["H"], "T": T, "d_k": WL["dk"], "d_v": WL["dv"],
+                   "chunk": args.chunk, "state_dtype": "f32"},
         "roofline": roofline,
-        "mfma_chunk": mfma,
-        "scan_hbm": {"kernels": "scan_reduce+scan_carry", "us": round(scan_s * 1e6, 2),
-                     "GB/s": round(scan_by / scan_s / 1e9, 1),
-                     "frac": round(scan_by / scan_s / 1e9 / PEAK_HBM_GBS, 4)},
-        "kernels": kernels,
+        "step_us_warm": head["step_us_warm"], "step_us_cold": head["step_us_cold"],
+        "mfma_chunk": head["mfma_chunk"],
+        "scan_hbm": head["scan_hbm"],
+        "kernels": head["kernels"],
     }
-    if traffic is not None:
-        res["roofline"]["traffic_src_sha256"] = sha
-    del t, ws, out
-    torch.cuda.empty_cache()
     if not args.no_isotropic:
-        res["isotropic"] = bench_isotropic(args)
+        res["isotropic"] = bench_forward(args, config_inputs(2, variant="isotropic"),
+                                         "isotropic", 50, args.cold_reps, "isotropic forward")
+    if not args.no_long:
+        res["long"] = {}
+        for variant in ("diagonal", "isotropic"):
+            log(f"generating the long workload ({variant})")
+            li = config_inputs(3, variant=variant)
+            res["long"][variant] = bench_forward(args, li, variant, 10, 5, f"long {variant}")
+            del li
     if not args.no_backward:
         res["backward"] = bench_backward(args, inp)
     if not args.no_dense:
@@ -450,58 +551,6 @@ def bench_dense(args, inp):
             "bound": "latency (sequential over tokens; one workgroup per head)"}
 
 
-def bench_isotropic(args):
-    """The isotropic variant's forward on the same workload (one scalar
-    precision per head; inputs of the same recipe with a per-head lambda0)."""
-    import numpy as np
-    import torch
-
-    import kalman_filter_memory_amd as kdn
-    from kdn_inputs import config_inputs
-
-    dev = torch.device("cuda:0")
-    B, H, T, dk, dv, C = (WL[x] for x in ("B", "H", "T", "dk", "dv", "chunk"))
-    inp = config_inputs(2, variant="isotropic")
-    bf = torch.bfloat16
-    t = {n: torch.from_numpy(inp[n]).to(dev, bf) for n in ("q", "k", "v", "a", "nu", "r")}
-    lam0 = torch.from_numpy(inp["lambda0"]).to(dev)
-    S0 = torch.from_numpy(inp["S0"]).to(dev)
-    d = kdn.make_desc(B, H, T, dk, dv, C, "isotropic", kdn.BF16, kdn.BF16)
-    ws = torch.empty(kdn.forward_workspace_bytes(d), dtype=torch.uint8, device=dev)
-    out = (torch.empty((B, H, T, dv), dtype=bf, device=dev),
-           torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev),
-           torch.empty((B, H), dtype=torch.float32, device=dev))
-
-    def step(events=None):
-        kdn.forward(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], lam0, S0, "isotropic", C,
-                    workspace=ws, out=out, events=events)
-
-    ramp(step, args.ramp_ms)
-    for _ in range(10):
-        step()
-    torch.cuda.synchronize()
-    steps = 50
-    log(f"timing {steps} isotropic forward steps")
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(KERNELS))]
-           for _ in range(10)]
-    for row in evs:
-        for e in row:
-            e.record()
-    torch.cuda.synchronize()
-    for row in evs:
-        step(events=row)
-    torch.cuda.synchronize()
-    kern = {k: round(float(np.mean([row[2 * i].elapsed_time(row[2 * i + 1]) for row in evs]))
-                     * 1e3, 2) for i, k in enumerate(KERNELS)}
-    return {"workload": f"iso_bf16_B{B}_H{H}_T{T}_d{dk}", "ms_per_step": round(ms, 4),
-            "tokens/s": round(B * T / (ms * 1e-3), 1), "kernels_us": kern}
-
-
 LAYER = dict(B=8, T=4096, H=16, D=2048, dk=128, dv=128, chunk=64)
 LAYER_STAGES = ("gemm_in", "norm_gates", "recurrence", "readout_rows", "gemm_out")
 
@@ -656,6 +705,11 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-isotropic", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context workload (B1 H16 T65536, both variants)")
+    ap.add_argument("--chunk", type=int, default=64)
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="steps timed one by one after a 512 MiB cache-evicting write")
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "

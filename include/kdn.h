@@ -130,8 +130,8 @@ kdn_status kdn_mobius_scan(const kdn_desc *d, const void *k, const void *a,
                            void *ws, size_t ws_bytes, void *stream);
 
 /* Kalman gain of every token from given predictive precisions (same pages:
- * the gain weights each residual write by accumulated evidence and
- * observation reliability):  w = P^- k / (k^T P^- k + r),  P^- = 1/lambda^-.
+ * how strongly a token's residual is written depends on how much evidence the
+ * memory already holds and on how noisy the token's observation is):  w = P^- k / (k^T P^- k + r),  P^- = 1/lambda^-.
  *   lambda_minus: float32 [B,H,T,d_k] (diagonal) or [B,H,T] (isotropic).
  *   w: output [B,H,T,d_k] in gain_dtype. */
 kdn_status kdn_gain(const kdn_desc *d, const void *k, const void *r,
@@ -142,7 +142,7 @@ size_t kdn_chunk_delta_workspace_bytes(const kdn_desc *d);
 
 /* Memory write and read-out given the gain keys w (chunkwise form of
  * S_t = a S_{t-1} + (v - a S_{t-1} k) w^T, o_t = S_t q_t; ai-feeds.com
- * summary, section 方法 step 3: hardware-efficient chunkwise implementation).
+ * summary, section 方法 step 3: the write is computed chunk by chunk).
  * w [B,H,T,d_k] has qkv_dtype (gain_dtype must equal qkv_dtype); qnoise and r
  * are not needed because w already carries them.
  *   S0: NULL -> zeros.  o: [B,H,T,d_v] qkv_dtype.  S_T: NULL or output,
@@ -161,8 +161,9 @@ kdn_status kdn_decode_step(const kdn_desc *d, const void *q, const void *k, cons
                            const void *a, const void *qnoise, const void *r, float *S,
                            float *lambda, void *o, void *stream);
 
-/* Exact KDN gain ("Kalman Delta Networks", English abstract: exact tracking
- * entails a dense, state-dependent Riccati recursion):
+/* Exact KDN gain ("Kalman Delta Networks", English abstract: tracking the
+ * key-space posterior exactly needs a full covariance with a state-dependent
+ * Riccati update, which the two variants approximate):
  * per head one d_k x d_k covariance P, per token P^- = a^2 P + qnoise I,
  * w = P^- k / (k^T P^- k + r), P = P^- - (P^- k)(P^- k)^T / (k^T P^- k + r).
  * k [B,H,T,d_k] (qkv_dtype); a, qnoise, r [B,H,T]; P0 [B,H,d_k,d_k] float32
@@ -234,7 +235,7 @@ size_t kdn_forward_varlen_workspace_bytes(const kdn_desc *d);
 
 /* Forward of a packed batch of d->B variable-length sequences (serving: the
  * prefill of many prompts in one call; "Kalman Delta Networks", English
- * abstract: efficient long-context inference).  Every head's rows hold
+ * abstract: the layer is meant for fast inference over long contexts).  Every head's rows hold
  * the sequences one after another: q, k [H, T, d_k]; v, o [H, T, d_v]; a,
  * qnoise, r [H, T], with T = d->T the total token count; sequence s has rows
  * cu_seqlens[s] .. cu_seqlens[s+1] (device int32 [B+1], non-decreasing, from 0

@@ -13,7 +13,7 @@
 // cumulative log2 decays.
 #include "kdn.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cstdint>

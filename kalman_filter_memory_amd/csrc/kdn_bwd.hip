@@ -44,7 +44,7 @@
 //                  outputs); bgain_carry between the two
 // All products on MFMA with fp32 accumulation; operands in the input dtype.
 #include "kdn_device.h"
-#include "kdn_kernels.h"
+#include "kdn_launch.h"
 #include "kdn_tiles.h"
 
 namespace kdn {

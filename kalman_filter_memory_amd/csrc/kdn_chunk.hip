@@ -2,9 +2,10 @@
 //
 // The memory recurrence S_t = a_t S_{t-1} + (v_t - a_t S_{t-1} k_t) w_t^T,
 // o_t = S_t q_t is a generalised delta rule whose write key w_t is the Kalman
-// gain ("Kalman Delta Networks", English abstract: the Kalman gain weights
-// each residual write; ai-feeds.com summary, section 方法 step 3: hardware-
-// efficient chunkwise implementation).  Within a chunk of C tokens that
+// gain ("Kalman Delta Networks", English abstract: the gain sets how much of
+// each token's residual is written; ai-feeds.com summary, section 方法 step 3:
+// the write is computed chunk by chunk, as in hardware-friendly delta-rule
+// kernels).  Within a chunk of C tokens that
 // starts from S0, with local cumulative decay gamma_t = prod_{s<=t} a_s,
 // g = log gamma and Gamma_ts = exp(g_t - g_s):
 //   A  = strict_tril(K W^T * Gamma),  T = (I + A)^{-1}
@@ -29,7 +30,7 @@
 // so every MFMA fragment is one 16-byte (bf16) or 4-byte (fp32) LDS read; the
 // transposed copy of W needed by the state update is written when staged.
 #include "kdn_device.h"
-#include "kdn_kernels.h"
+#include "kdn_launch.h"
 #include "kdn_tiles.h"
 
 namespace kdn {

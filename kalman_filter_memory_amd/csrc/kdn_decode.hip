@@ -17,7 +17,7 @@
 // before its in-place update.  The gain inputs are loaded before the state
 // rows, so waiting for them leaves the rows in flight.
 #include "kdn_device.h"
-#include "kdn_kernels.h"
+#include "kdn_launch.h"
 
 namespace kdn {
 namespace {

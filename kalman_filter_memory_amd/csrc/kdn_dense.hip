@@ -1,7 +1,8 @@
 // kdn_dense.hip -- the exact KDN gain: the dense Riccati recursion with one
 // d_k x d_k covariance per head ("Kalman Delta Networks", English abstract:
-// exact tracking entails a dense, state-dependent Riccati recursion, which the
-// diagonal and isotropic variants approximate).  Per token:
+// tracking the key-space posterior exactly needs a full covariance whose
+// Riccati update depends on the state; the diagonal and isotropic variants are
+// the two cheap replacements for it).  Per token:
 //   P^- = a^2 P + nu I,   w = P^- k / (k^T P^- k + r),
 //   P   = P^- - (P^- k)(P^- k)^T / (k^T P^- k + r).
 // The memory write with these gains is the generalised delta rule of the other
@@ -29,7 +30,7 @@
 // block collect in LDS and leave in 16-byte stores.  Per-token LDS buffers
 // alternate between tokens, so that one barrier per token orders every access.
 #include "kdn_device.h"
-#include "kdn_kernels.h"
+#include "kdn_launch.h"
 
 namespace kdn {
 namespace {

@@ -1,8 +1,9 @@
 // kdn_kernels.h -- host-side launchers of the libkdn kernels (internal).
+// Plain host declarations: the C ABI (kdn_api.cpp) needs only these, so it
+// also builds with a host compiler alone (the sanitizer test does that).
 #pragma once
 
-#include <hip/hip_ext.h>
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -16,14 +17,6 @@ struct LaunchTiming {
     hipEvent_t start = nullptr, stop = nullptr;
 };
 LaunchTiming& launch_timing();
-
-template <typename F, typename... Args>
-inline void launch_k(F kernel, dim3 grid, dim3 block, unsigned shmem, hipStream_t st,
-                     Args... args) {
-    LaunchTiming& t = launch_timing();
-    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, t.start, t.stop, 0u, args...);
-    t = LaunchTiming{};
-}
 
 // A packed batch of N variable-length sequences: every head's rows hold the
 // sequences one after another ([H][Ttot][d]); sequence s has rows
@@ -46,28 +39,6 @@ struct Shape {
     bool varlen = false;  // a packed batch (pk), BH = N * H
     Packed pk;
 };
-
-// The token rows and chunks of one head (or, packed, one (sequence, head)):
-// first row, tokens, chunks, and its first entry in the per-chunk arrays (Moebius
-// products, T matrices, decays: nc each) and in the chunk-boundary precisions
-// (nc + 1 each).
-struct Slab {
-    size_t row0;
-    int T, nc;
-    size_t c0, l0;
-};
-template <bool VL>
-__device__ __forceinline__ Slab slab_of(size_t bh, int T, int NC, const Packed& pk) {
-    if constexpr (!VL) {
-        return Slab{bh * T, T, NC, bh * NC, bh * (size_t)(NC + 1)};
-    } else {
-        const int s = static_cast<int>(bh / pk.H), h = static_cast<int>(bh % pk.H);
-        const int b = pk.cu[s], e = pk.cu[s + 1], c0 = pk.cc[s], c1 = pk.cc[s + 1];
-        const int nc = c1 - c0;
-        return Slab{(size_t)h * pk.Ttot + b, e - b, nc, (size_t)pk.H * c0 + (size_t)h * nc,
-                    (size_t)pk.H * (c0 + s) + (size_t)h * (nc + 1)};
-    }
-}
 
 // Each launcher returns hipSuccess or the launch error.  Pointers are device
 // pointers with the layouts documented in include/kdn.h.

@@ -5,8 +5,9 @@
 // evidence b = k_i^2 / r (diagonal) or |k|^2 / (d_k r) (isotropic):
 //   lambda_t = (lambda^-_t + b),  lambda^-_t = lambda_{t-1} / (a^2 + nu lambda_{t-1})
 // which is the Moebius map of M_t = [[1 + b nu, b a^2], [nu, a^2]]
-// ("Kalman Delta Networks", English abstract: the uncertainty recurrences are
-// Moebius maps, enabling associative scans with logarithmic parallel depth).
+// ("Kalman Delta Networks", English abstract: because each precision update is
+// a linear-fractional map, the whole sequence of them composes associatively
+// and can be evaluated by a scan of depth log T).
 // A Moebius map does not change when its matrix is scaled, so products are
 // renormalised by exact powers of two to stay inside the float range.
 //
@@ -20,7 +21,7 @@
 //           writes every predictive precision lambda^-.
 // The gain kernel forms w = P^- k / (k^T P^- k + r) from given lambda^-.
 #include "kdn_device.h"
-#include "kdn_kernels.h"
+#include "kdn_launch.h"
 
 namespace kdn {
 namespace {
@@ -223,6 +224,9 @@ __device__ __forceinline__ float chunk_row_sq(const E* __restrict__ k0, int n, i
         s = group_sum<16>(s);
         if (l16 == 0) sq[t] = s;
     }
+    // the stores above and the read below are by different lanes of this
+    // wave: keep the compiler from moving the read ahead of the stores
+    __builtin_amdgcn_wave_barrier();
     return lane < n ? sq[lane] : 0.f;
 }
 

@@ -5,7 +5,7 @@
 #pragma once
 
 #include "kdn_device.h"
-#include "kdn_kernels.h"
+#include "kdn_launch.h"
 
 namespace kdn {
 namespace {

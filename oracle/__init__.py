@@ -23,6 +23,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kdn_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "_kdn_oracle.so")
+# another build of the same source (the sanitizer test loads an
+# AddressSanitizer / UndefinedBehaviorSanitizer build this way)
+_LIB_OVERRIDE = os.environ.get("KDN_ORACLE_LIB")
 _lib = None
 
 DIAGONAL = 0
@@ -43,9 +46,12 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB_PATH)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB_PATH):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         I = ctypes.c_int
         lib.kdn_oracle_forward.argtypes = [I, I, I, I, I, I] + [P] * 13 + [I]

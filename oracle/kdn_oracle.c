@@ -494,8 +494,9 @@ int kdn_oracle_backward(int B, int H, int T, int dk, int dv, int variant, const 
 
 /* ------------------------------------------------------------------------
  * Exact KDN: the dense Riccati recursion that the two approximations replace
- * ("Kalman Delta Networks", English abstract: exact tracking entails a dense,
- * state-dependent Riccati recursion).  One d_k x d_k covariance P per head,
+ * ("Kalman Delta Networks", English abstract: exact tracking of the key-space
+ * posterior needs a full covariance whose Riccati update depends on the
+ * state).  One d_k x d_k covariance P per head,
  * shared by the rows of S; per token, in the order of kdn_token:
  *     predict:  P^- = a^2 P + nu I
  *     gain:     w = P^- k / (k^T P^- k + r)

@@ -43,3 +43,23 @@ def test_backward_algorithmic_bytes_cover_every_stage():
     # the gradient stages move more than the forward's state pass
     assert by["bwd_grad"] > by["bwd_state"] > bench.algorithmic(8, 16, 4096, 128, 128, 64)[0][
         "chunk_state"]
+
+
+def test_chunk_stage_roofline_bytes_follow_the_per_unit_figure():
+    """The headline roofline divides by the chunk stage's per-unit bytes: q, k,
+    v, w (bf16, 1024 B), a (2 B), o (256 B) and S0 / S_T amortised (32 B at
+    T 4096): 1,314 B per token-head, 688.9 MB at the layer workload; 1,346 MB
+    at the long workload (B1 H16 T65536)."""
+    B, H, T, d = 8, 16, 4096, 128
+    assert bench.bytes_8d(B, H, T, d, d) == B * H * T * 1314
+    assert round(bench.bytes_8d(B, H, T, d, d) / 1e6, 1) == 688.9
+    assert round(bench.bytes_8d(1, 16, 65536, d, d) / 1e6) == 1346
+
+
+def test_isotropic_scan_bytes_hold_one_precision_per_chunk():
+    by_d, _ = bench.algorithmic(1, 16, 65536, 128, 128, 64, "diagonal")
+    by_i, _ = bench.algorithmic(1, 16, 65536, 128, 128, 64, "isotropic")
+    n, nc = 16 * 65536, 1024
+    assert by_d["scan_reduce"] - by_i["scan_reduce"] == 16 * nc * 127 * 16
+    assert by_i["scan_carry"] < by_d["scan_carry"] / 100
+    assert bench.scan_bytes_8d(1, 16, 65536, 128, "isotropic") == n * (256 + 6 + 4)

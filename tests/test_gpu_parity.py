@@ -2,9 +2,8 @@
 
 Bars: o and S_T within 1e-4 (float32 inputs) or 2e-2 (bfloat16 inputs, float32
 state) normwise per (b, h); lambda within 1e-5 elementwise relative.  The
-full-size workloads run in the same launch configuration as the benchmark;
-the oracle then checks a sample of heads (heads are independent, so a sampled
-head is the exact full-size computation for that head)."""
+full-size workloads run in the same launch configuration as the benchmark,
+and the oracle checks every head of them."""
 from __future__ import annotations
 
 import numpy as np
@@ -13,8 +12,8 @@ import torch
 
 import kalman_filter_memory_amd as kdn
 import oracle
-from gpu_util import (TOL_BF16, TOL_F32, TOL_LAMBDA, elementwise, forward_tensors, head_slice,
-                      host, normwise, say)
+from gpu_util import (TOL_BF16, TOL_F32, TOL_LAMBDA, cached_config, elementwise,
+                      forward_tensors, host, normwise, row_errors, say)
 from kdn_inputs import config_inputs, forward_inputs, decode_inputs
 
 pytestmark = pytest.mark.gpu
@@ -100,63 +99,70 @@ def test_workload_diag_f32_B2_H4_T2048_d64():
     _check_forward(config_inputs(1), 64, "diag f32 [2,4,2048,64]")
 
 
-def _sampled_full_size(index, variant, heads, chunk=64):
+def _full_size_all_heads(index, variant, chunk=64):
+    """The full-size workload in the benchmark's launch configuration, every
+    head compared with the oracle (which runs the whole workload on the host
+    cores), plus a per-token-row diagnostic of o."""
     say(f"[gpu] generating workload {index} ({variant})")
-    inp = config_inputs(index, variant=variant)
+    inp = cached_config(index, variant)
     say(f"[gpu] forward full size {inp['q'].shape} {variant}")
     o, S_T, lam = _gpu_forward(inp, chunk)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(S_T)) and np.all(lam > 0)
-    sub = head_slice(inp, heads)
-    say(f"[cpu] oracle on heads {heads}")
-    ref = _oracle_forward(sub)
-    idx = tuple(np.array(heads).T)
-    e_o = normwise(o[idx][:, None], ref["o"])
-    e_s = normwise(S_T[idx][:, None], ref["S_T"])
-    e_l = elementwise(lam[idx][:, None], ref["lambda_T"])
-    say(f"    sampled heads: err o {e_o:.2e}  S_T {e_s:.2e}  lambda_T {e_l:.2e}")
+    say(f"[cpu] oracle on all {inp['q'].shape[0] * inp['q'].shape[1]} heads")
+    ref = _oracle_forward(inp)
+    e_o = normwise(o, ref["o"])
+    e_s = normwise(S_T, ref["S_T"])
+    e_l = elementwise(lam, ref["lambda_T"])
+    r_o, r_i, r_frac = row_errors(o, ref["o"])
+    say(f"    all heads: err o {e_o:.2e}  S_T {e_s:.2e}  lambda_T {e_l:.2e}; worst token row "
+        f"of o {r_o:.2e} (row {r_i}), rows above 1e-2: {r_frac:.1e}")
     assert e_o <= TOL_BF16 and e_s <= TOL_BF16 and e_l <= TOL_LAMBDA
-    return inp, o, S_T, lam
 
 
-def test_workload_diag_bf16_B8_H16_T4096_d128_sampled_heads():
-    _sampled_full_size(2, "diagonal", [(0, 0), (3, 7), (5, 12), (7, 15)])
+def test_workload_diag_bf16_B8_H16_T4096_d128_all_heads():
+    _full_size_all_heads(2, "diagonal")
+
+
+def test_workload_iso_bf16_B8_H16_T4096_d128_all_heads():
+    """The isotropic forward at the layer workload (the benchmark times it too)."""
+    _full_size_all_heads(2, "isotropic")
 
 
 @pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
-def test_workload_long_bf16_B1_H16_T65536_d128_sampled_heads(variant):
-    _sampled_full_size(3, variant, [(0, 11)])
+def test_workload_long_bf16_B1_H16_T65536_d128_all_heads(variant):
+    _full_size_all_heads(3, variant)
 
 
-def test_workload_decode_N256_H16_d128_128_steps_sampled_states():
-    d = config_inputs(4)
+def test_workload_decode_N256_H16_d128_128_steps_all_states():
+    """128 in-place decode steps on all 256 x 16 cached states: o of every
+    state at every step against the oracle's step, and the whole cache (S and
+    lambda) after steps 1, 64 and 128."""
+    d = cached_config(4)
     steps = d["q"].shape[0]
-    N, H = d["q"].shape[1:3]
     S = torch.from_numpy(d["S0"]).cuda()
     lam = torch.from_numpy(d["lambda0"]).cuda()
     dev = {n: torch.from_numpy(d[n]).cuda().to(torch.bfloat16 if n in ("q", "k", "v")
                                                else torch.float32)
            for n in ("q", "k", "v", "a", "nu", "r")}
-    pick = [(0, 0), (17, 3), (100, 9), (255, 15), (128, 8), (31, 1)]
-    Ss = np.stack([d["S0"][n, h] for n, h in pick])[:, None].astype(np.float64).copy()
-    ls = np.stack([d["lambda0"][n, h] for n, h in pick])[:, None].astype(np.float64).copy()
-    say(f"[gpu] decode {steps} steps on S{tuple(S.shape)}")
-    worst_o = 0.0
+    Sr = d["S0"].astype(np.float64)
+    lr = d["lambda0"].astype(np.float64)
+    say(f"[gpu] decode {steps} steps on S{tuple(S.shape)}, every state checked")
+    worst_o, worst_s, worst_l = 0.0, 0.0, 0.0
     for s in range(steps):
         o = kdn.decode_step(dev["q"][s], dev["k"][s], dev["v"][s], dev["a"][s], dev["nu"][s],
                             dev["r"][s], S, lam, "diagonal")
-        sub = {n: np.stack([d[n][s, a, b] for a, b in pick])[:, None] for n in
-               ("q", "k", "v", "a", "nu", "r")}
-        o_ref = oracle.decode_step(sub["q"], sub["k"], sub["v"], sub["a"], sub["nu"], sub["r"],
-                                   Ss, ls, "diagonal")
-        o_h = host(o)
-        worst_o = max(worst_o, normwise(np.stack([o_h[a, b] for a, b in pick])[:, None], o_ref))
-    torch.cuda.synchronize()
-    S_h, l_h = host(S), host(lam)
-    e_s = normwise(np.stack([S_h[a, b] for a, b in pick])[:, None], Ss)
-    e_l = elementwise(np.stack([l_h[a, b] for a, b in pick])[:, None], ls)
-    say(f"    err o {worst_o:.2e}  S {e_s:.2e}  lambda {e_l:.2e}")
-    assert np.all(np.isfinite(S_h))
-    assert worst_o <= TOL_BF16 and e_s <= TOL_BF16 and e_l <= TOL_LAMBDA
+        o_ref = oracle.decode_step(*(d[n][s] for n in ("q", "k", "v", "a", "nu", "r")), Sr, lr,
+                                   "diagonal")
+        worst_o = max(worst_o, normwise(host(o), o_ref))
+        if s in (0, 63, steps - 1):
+            torch.cuda.synchronize()
+            S_h, l_h = host(S), host(lam)
+            assert np.all(np.isfinite(S_h))
+            e_s, e_l = normwise(S_h, Sr), elementwise(l_h, lr)
+            say(f"    after step {s + 1}: err o (worst so far) {worst_o:.2e}  S {e_s:.2e}  "
+                f"lambda {e_l:.2e}")
+            worst_s, worst_l = max(worst_s, e_s), max(worst_l, e_l)
+    assert worst_o <= TOL_BF16 and worst_s <= TOL_BF16 and worst_l <= TOL_LAMBDA
 
 
 # ----------------------------------------------------- the separate steps
@@ -466,12 +472,12 @@ def test_dense_exact_kdn_extreme_decays(dk):
     assert e_o <= TOL_F32 and e_s <= TOL_F32 and e_p <= 1e-4
 
 
-def test_dense_exact_kdn_workload_bf16_B8_H16_T4096_d128_sampled_heads():
+def test_dense_exact_kdn_workload_bf16_B8_H16_T4096_d128_all_heads():
     """The exact forward at the layer workload's full size, in the launch
-    configuration the benchmark times (P0 = I, chunk 64); three sampled heads
-    against the oracle's dense filter."""
+    configuration the benchmark times (P0 = I, chunk 64); every head against
+    the oracle's dense filter."""
     say("[gpu] generating workload 2 for the exact filter")
-    inp = config_inputs(2)
+    inp = cached_config(2)
     t = forward_tensors(inp)
     say(f"[gpu] exact forward full size {inp['q'].shape}")
     o, S_T, P_T = kdn.forward_dense(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], None,
@@ -479,14 +485,11 @@ def test_dense_exact_kdn_workload_bf16_B8_H16_T4096_d128_sampled_heads():
     torch.cuda.synchronize()
     o, S_T, P_T = host(o), host(S_T), host(P_T)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(P_T))
-    heads = [(0, 0), (3, 7), (7, 15)]
-    sub = head_slice(inp, heads)
-    say(f"[cpu] dense oracle on heads {heads}")
-    ref = oracle.forward_dense(sub["q"], sub["k"], sub["v"], sub["a"], sub["nu"], sub["r"],
-                               None, sub["S0"])
-    idx = tuple(np.array(heads).T)
-    e_o = normwise(o[idx][:, None], ref["o"])
-    e_s = normwise(S_T[idx][:, None], ref["S_T"])
-    e_p = normwise(P_T[idx][:, None], ref["P_T"])
-    say(f"    sampled heads: err o {e_o:.2e}  S_T {e_s:.2e}  P_T {e_p:.2e}")
+    say("[cpu] dense oracle on all heads")
+    ref = oracle.forward_dense(inp["q"], inp["k"], inp["v"], inp["a"], inp["nu"], inp["r"],
+                               None, inp["S0"])
+    e_o = normwise(o, ref["o"])
+    e_s = normwise(S_T, ref["S_T"])
+    e_p = normwise(P_T, ref["P_T"])
+    say(f"    all heads: err o {e_o:.2e}  S_T {e_s:.2e}  P_T {e_p:.2e}")
     assert e_o <= TOL_BF16 and e_s <= TOL_BF16 and e_p <= 1e-4

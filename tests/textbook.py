@@ -7,8 +7,8 @@ different formulation of something the KDN pages fix:
   (predict variance a^2 P + nu, gain P k / (k^2 P + r), posterior variance
   (1 - K k) P).  With one key dimension the mean-field projection is exact, so
   both KDN variants must reduce to it ("Kalman Delta Networks", English
-  abstract: the Kalman filter is the optimal recursive estimator of the
-  linear-Gaussian memory model).
+  abstract: for the linear-Gaussian memory model no recursive estimator
+  beats the Kalman filter).
 * ``dense_kalman``: the full-covariance Kalman filter (covariance form, Joseph
   update) that the pages call the exact, dense Riccati recursion.  With
   axis-aligned keys the exact posterior precision stays diagonal, so Diagonal
