@@ -38,7 +38,7 @@ F32, BF16 = 0, 1
 
 EXPORTS = (
     "kdn_status_string", "kdn_validate", "kdn_forward_workspace_bytes", "kdn_forward",
-    "kdn_forward_events",
+    "kdn_forward_events", "kdn_forward_segments",
     "kdn_mobius_scan_workspace_bytes", "kdn_mobius_scan", "kdn_gain",
     "kdn_chunk_delta_workspace_bytes", "kdn_chunk_delta", "kdn_decode_step",
     "kdn_backward_workspace_bytes", "kdn_backward", "kdn_backward_events",
@@ -85,6 +85,8 @@ def load_library(path: str = LIB_PATH):
               "kdn_chunk_delta_workspace_bytes"):
         getattr(lib, n).argtypes = [D]
         getattr(lib, n).restype = S
+    lib.kdn_forward_segments.argtypes = [D]
+    lib.kdn_forward_segments.restype = ctypes.c_int32
     lib.kdn_forward.argtypes = [D] + [P] * 11 + [P, S, P]
     lib.kdn_forward.restype = I
     lib.kdn_forward_events.argtypes = [D] + [P] * 11 + [P, S, P, ctypes.POINTER(P)]
@@ -177,6 +179,12 @@ def make_desc(B, H, T, d_k, d_v, chunk, variant, qkv_dtype, gate_dtype, gain_dty
 
 def validate(desc: KdnDesc) -> int:
     return load_library().kdn_validate(ctypes.byref(desc))
+
+
+def forward_segments(desc: KdnDesc) -> int:
+    """Sequence segments of kdn_forward's state pass for this descriptor (1:
+    the plain sequential pass; 0: invalid descriptor)."""
+    return load_library().kdn_forward_segments(ctypes.byref(desc))
 
 
 def forward_workspace_bytes(desc: KdnDesc) -> int:

@@ -76,20 +76,31 @@ kdn::Shape make_shape(const kdn_desc* d) {
 }
 
 struct ForwardWs {
-    size_t agg, lam_chunk, w, tm, g, total;
+    size_t agg, lam_chunk, w, tm, g, seg_S, seg_A, total;
+    int nseg, Lc;
 };
 
-// workspace offsets: [agg | lam_chunk | w | T | g]; kdn_chunk_delta uses [T | g]
+// workspace offsets: [agg | lam_chunk | w | T | g | segment states | segment
+// maps]; kdn_chunk_delta uses [T | g].  The segment arrays are empty unless
+// the state pass runs over sequence segments (few heads, many chunks).
 ForwardWs forward_ws(const kdn_desc* d) {
     const kdn::Shape s = make_shape(d);
     const size_t nl = s.diag ? s.dk : 1;
     ForwardWs w;
+    w.nseg = kdn::chunk_supported(s) ? kdn::state_segments(s, &w.Lc) : 1;
+    if (w.nseg <= 1) {
+        w.nseg = 1;
+        w.Lc = s.nc;
+    }
+    const size_t segs = w.nseg > 1 ? (size_t)s.BH * w.nseg : 0;
     w.agg = 0;
     w.lam_chunk = w.agg + round_up((size_t)s.BH * s.nc * nl * 16);
     w.w = w.lam_chunk + round_up((size_t)s.BH * (s.nc + 1) * nl * 4);
     w.tm = w.w + round_up((size_t)s.BH * s.T * s.dk * esize(d->qkv_dtype));
     w.g = w.tm + round_up((size_t)s.BH * s.nc * s.chunk * s.chunk * esize(d->qkv_dtype));
-    w.total = w.g + round_up((size_t)s.BH * s.nc * s.chunk * 4);
+    w.seg_S = w.g + round_up((size_t)s.BH * s.nc * s.chunk * 4);
+    w.seg_A = w.seg_S + round_up(segs * s.dv * s.dk * 4);
+    w.total = w.seg_A + round_up(segs * s.dk * s.dk * 4);
     return w;
 }
 
@@ -179,6 +190,11 @@ size_t kdn_forward_workspace_bytes(const kdn_desc* d) {
     return forward_ws(d).total;
 }
 
+int32_t kdn_forward_segments(const kdn_desc* d) {
+    if (kdn_validate(d) != KDN_OK) return 0;
+    return forward_ws(d).nseg;
+}
+
 size_t kdn_mobius_scan_workspace_bytes(const kdn_desc* d) {
     if (check_chunked(d) != KDN_OK) return 0;
     const ForwardWs w = forward_ws(d);
@@ -224,8 +240,14 @@ kdn_status kdn_forward_events(const kdn_desc* d, const void* q, const void* k, c
     sw.gain_bf16 = s.qkv_bf16;
     timed(2);
     if (e == hipSuccess) e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, g, hs);
+    kdn::SegWs seg;
+    seg.nseg = w.nseg;
+    seg.Lc = w.Lc;
+    seg.Sseg = reinterpret_cast<float*>(at(ws, w.seg_S));
+    seg.Aseg = reinterpret_cast<float*>(at(ws, w.seg_A));
     timed(3);
-    if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs);
+    if (e == hipSuccess)
+        e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs, nullptr, &seg);
     kdn::launch_timing() = kdn::LaunchTiming{};
     return hip_status(e);
 }
@@ -437,7 +459,7 @@ kdn_status kdn_gain(const kdn_desc* d, const void* k, const void* r, const float
 size_t kdn_chunk_delta_workspace_bytes(const kdn_desc* d) {
     if (kdn_validate(d) != KDN_OK) return 0;
     const ForwardWs w = forward_ws(d);
-    return w.total - w.tm;  // T and g
+    return w.seg_S - w.tm;  // T and g
 }
 
 kdn_status kdn_chunk_delta(const kdn_desc* d, const void* q, const void* k, const void* v,
@@ -452,7 +474,7 @@ kdn_status kdn_chunk_delta(const kdn_desc* d, const void* q, const void* k, cons
     if (s.BH == 0) return KDN_OK;
     if (s.T > 0 && (!q || !k || !v || !a || !w || !o)) return KDN_ERR_NULL;
     if (!ws) return KDN_ERR_NULL;
-    if (ws_bytes < fw.total - fw.tm) return KDN_ERR_WORKSPACE;
+    if (ws_bytes < fw.seg_S - fw.tm) return KDN_ERR_WORKSPACE;
     for (const void* p : {q, k, v, w, (const void*)o, (const void*)S0, (const void*)S_T, (const void*)ws})
         if (p && !aligned16(p)) return KDN_ERR_ALIGN;
     hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -682,9 +682,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
                 for (int b = 0; b < BKI; ++b) {
                     const int i = 16 * (ib + b) + (lane & 15);
-                    // s_t from dW as the gain pass will read it (input dtype)
+                    // s_t from the unrounded dW (dW itself is stored in the input dtype)
                     const E dw = from_f<E>(aw[x][0][b][e]);
-                    sd += to_f<E>(dw) * to_f<E>(L.W[t * LDK + i]);
+                    sd += aw[x][0][b][e] * to_f<E>(L.W[t * LDK + i]);
                     if (t < n) {
                         const size_t o = (row0 + t) * DK + i;
                         dq[o] = aq[x][0][b][e];

@@ -29,6 +29,8 @@
 // Operand arrays in LDS are row-major with the contraction index contiguous,
 // so every MFMA fragment is one 16-byte (bf16) or 4-byte (fp32) LDS read; the
 // transposed copy of W needed by the state update is written when staged.
+#include <algorithm>
+
 #include "kdn_device.h"
 #include "kdn_launch.h"
 #include "kdn_tiles.h"
@@ -582,19 +584,32 @@ template <typename E, int DK, int DVT, int C> struct StateLds {
     float del[C];        // gamma_C / gamma_t
 };
 
+// A state pass over sequence segments (kernel argument): each head's chunks
+// cut into nseg runs of Lc chunks (the last may be shorter); this launch runs
+// segments g0 .. g0 + nsegL - 1 of every head, each with ntv value-row tiles
+// and nta identity-row tiles.
+struct SegPlan {
+    int nseg = 1, Lc = 0, g0 = 0, nsegL = 1, ntv = 1, nta = 0;
+    float* Sseg = nullptr;        // [BH][nseg][DV][DK]: start state of each segment
+    float* Aseg = nullptr;        // [BH][nseg][DK][DK]: linear part of each segment's map
+};
+
 // what every wave of a state workgroup knows about its problem
 template <typename E> struct StateArgs {
     const E *q, *k, *v, *w, *Tm;
     const float* gin;
     E* o;
-    Slab sl;  // the head's rows and chunks
+    Slab sl;  // the rows and chunks of the head (or of one segment of it)
     int j0, DV, tid, lane, wave;
+    int jv;       // first column of V read for this tile (j0, or 0 for identity rows)
+    bool zero_v;  // identity rows of a segment map: V is zero
 };
 
 // One chunk c of the state pass.  LDS holds chunk c on entry.  The register
 // set (lk..lg) has been staged already and now receives chunk c + 2 from HBM;
 // the set (nk..ng) holds chunk c + 1 and is staged into LDS in phase C.
-template <typename E, int DK, int DVT, int C>
+// OUT = false: no read-out (Y, M and O are not formed, Q is not loaded).
+template <typename E, int DK, int DVT, int C, bool OUT>
 __device__ __forceinline__ void state_chunk(
     const StateArgs<E>& A, StateLds<E, DK, DVT, C>& L, StateAcc<E, DK, DVT, C>& accS, int c,
     u32x4 (&lk)[StateCfg<E, DK, DVT, C>::PK], u32x4 (&lq)[StateCfg<E, DK, DVT, C>::PK],
@@ -612,7 +627,7 @@ __device__ __forceinline__ void state_chunk(
     const size_t row0 = A.sl.row0 + t0;
     E* sWc = L.W[c & 1];
     __builtin_amdgcn_sched_barrier(0);
-    state_prefetch<E, DK, DVT, C, kLoadKQ>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.sl, A.j0, A.DV,
+    state_prefetch<E, DK, DVT, C, kLoadKQ, OUT>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.sl, A.jv, A.DV,
                                            c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
     __builtin_amdgcn_sched_barrier(0);  // keep the three load bursts apart
 
@@ -656,11 +671,16 @@ __device__ __forceinline__ void state_chunk(
                 for (int bv = 0; bv < BVA; ++bv)
                     fs[bv] = M::frag(L.S, LDK, 16 * (jb + bv), kk, lane);
                 const auto fk = M::frag(L.K, LDK, 16 * tb, kk, lane);
-                const auto fq = M::frag(L.Q, LDK, 16 * tb, kk, lane);
+                if constexpr (OUT) {
+                    const auto fq = M::frag(L.Q, LDK, 16 * tb, kk, lane);
 #pragma unroll
-                for (int bv = 0; bv < BVA; ++bv) {
-                    xt[bv][0] = M::mma(fs[bv], fk, xt[bv][0]);
-                    accY[x][bv][0] = M::mma(fs[bv], fq, accY[x][bv][0]);
+                    for (int bv = 0; bv < BVA; ++bv) {
+                        xt[bv][0] = M::mma(fs[bv], fk, xt[bv][0]);
+                        accY[x][bv][0] = M::mma(fs[bv], fq, accY[x][bv][0]);
+                    }
+                } else {
+#pragma unroll
+                    for (int bv = 0; bv < BVA; ++bv) xt[bv][0] = M::mma(fs[bv], fk, xt[bv][0]);
                 }
             }
             const int t = 16 * tb + (lane & 15);
@@ -675,13 +695,13 @@ __device__ __forceinline__ void state_chunk(
                 const floatx4 xv = xt[bv][0];
                 rv[bv] = floatx4{vv[0] - gt * xv[0], vv[1] - gt * xv[1], vv[2] - gt * xv[2],
                                  vv[3] - gt * xv[3]};
-                accY[x][bv][0] = accY[x][bv][0] * gt;
+                if constexpr (OUT) accY[x][bv][0] = accY[x][bv][0] * gt;
             }
             E* row = L.R + t * LDV + 16 * jb;
             store8x2<E>(row, row + 16, rv[0], rv[1], lane);
         }
     }
-    if constexpr (kMInA) {
+    if constexpr (kMInA && OUT) {
         // the ten lower tiles of M: waves 0-3 two tiles that share their W
         // fragments, (0,0)+(0,1), (0,2)+(0,3), (1,1)+(1,2), (2,2)+(2,3); waves 4
         // and 5 one tile, (1,3) and (3,3)
@@ -698,7 +718,7 @@ __device__ __forceinline__ void state_chunk(
         }
     }
     sync_lds();
-    state_prefetch<E, DK, DVT, C, kLoadW>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.sl, A.j0, A.DV,
+    state_prefetch<E, DK, DVT, C, kLoadW, OUT>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.sl, A.jv, A.DV,
                                           c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
     __builtin_amdgcn_sched_barrier(0);  // keep the three load bursts apart
 
@@ -726,9 +746,10 @@ __device__ __forceinline__ void state_chunk(
         // K, Q, V and W of chunk c + 1 (the first three were last read in phase A;
         // W goes to the other buffer): staged here, where the waves have slack
         if (c + 1 < A.sl.nc)
-            state_stage<E, DK, DVT, C, kStageKQWV>(
+            state_stage<E, DK, DVT, C, kStageKQWV, OUT>(
                 L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g, L.gam, L.del,
-                min(C, A.sl.T - (c + 1) * C), A.tid, lane, wave, nk, nq, nw, nv, nt, ng);
+                min(C, A.sl.T - (c + 1) * C), A.tid, lane, wave, nk, nq, nw, nv, nt, ng,
+                A.zero_v);
     } else if (wave < 4) {
         // U = T R (T lower triangular: contract only up to the block's last row)
 #pragma unroll
@@ -772,7 +793,7 @@ __device__ __forceinline__ void state_chunk(
             }
         }
     }
-    if (!kMInA && wave >= 4) {
+    if (OUT && !kMInA && wave >= 4) {
         // M^T = W Q^T on the lower block triangle, stored as M[t][s]
 #pragma unroll
         for (int x = 0; x < G::MPW; ++x) {
@@ -817,7 +838,7 @@ __device__ __forceinline__ void state_chunk(
         }
     }
     sync_lds();
-    state_prefetch<E, DK, DVT, C, kLoadVTG>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.sl, A.j0, A.DV,
+    state_prefetch<E, DK, DVT, C, kLoadVTG, OUT>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.sl, A.jv, A.DV,
                                             c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
     __builtin_amdgcn_sched_barrier(0);  // keep the three load bursts apart
 
@@ -825,7 +846,7 @@ __device__ __forceinline__ void state_chunk(
 #pragma unroll
     for (int x = 0; x < G::APW; ++x) {
         const int job = wave + G::NW * x;
-        if (job < G::NAJ) {
+        if (OUT && job < G::NAJ) {
             const int jb = (job / NT) * BVA, tb = a_tile<NT>(job);
             mma_block<E, BVA, 1>(accY[x], L.U, LDC, 16 * jb, L.M, LDC, 16 * tb, 0, 16 * (tb + 1),
                                  lane);
@@ -851,9 +872,9 @@ __device__ __forceinline__ void state_chunk(
     }
     // nothing staged here is read in phase C (W goes to the other buffer)
     if (c + 1 < A.sl.nc)
-        state_stage<E, DK, DVT, C, kMInA ? kStageT : kStageAll>(
+        state_stage<E, DK, DVT, C, kMInA ? kStageT : kStageAll, OUT>(
             L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g, L.gam, L.del, min(C, A.sl.T - (c + 1) * C),
-            A.tid, lane, wave, nk, nq, nw, nv, nt, ng);
+            A.tid, lane, wave, nk, nq, nw, nv, nt, ng, A.zero_v);
     state_write<E, DK, DVT, C>(accS, L.S, wave, lane);
     sync_lds();
 }
@@ -861,27 +882,64 @@ __device__ __forceinline__ void state_chunk(
 // One workgroup per CU (its LDS footprint) = two waves per SIMD: give each wave
 // the full 256-register budget instead of spilling to reach more waves.
 // VL: a packed batch, head = sequence * H + head within the sequence.
-template <typename E, int DK, int DVT, int C, bool VL>
+// OUT: the read-out o is formed and written.
+// SEG: the head's chunks are cut into segments (SegPlan) and each workgroup
+//   runs one (head, segment, tile).  With OUT, a segment starts from its true
+//   start state (S0, or the start state of segment g in seg.Sseg) and writes
+//   o, and the last segment S_T.  Without OUT it forms the segment's affine
+//   map S -> S A_g + B_g: value tiles run segment g from S0 (g = 0) or from
+//   zero (B_g) and write the end state into seg.Sseg[g + 1]; identity tiles
+//   (rows of the d_k x d_k identity, V = 0) write A_g into seg.Aseg[g].
+template <typename E, int DK, int DVT, int C, bool VL, bool OUT, bool SEG>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void state_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ gin, const E* __restrict__ w, const E* __restrict__ Tm,
     const float* S0, E* __restrict__ o, float* S_T, E* __restrict__ Sc, int BH, int T, int DV,
-    int NC, Packed pk) {
+    int NC, Packed pk, SegPlan seg) {
     using G = StateCfg<E, DK, DVT, C>;
     constexpr int BI = G::BI, BV = G::BV, NVB = G::NVB;
     __shared__ __align__(16) StateLds<E, DK, DVT, C> L;
     const int tid = threadIdx.x;
-    // Workgroups go to the 8 XCDs round-robin by linear id: the d_v tiles of one
-    // head get ids equal mod 8, so they share one XCD's L2 for K, Q, W and T.
-    const int ntile = DV / DVT, L_ = blockIdx.x, per = 8 * ntile;
-    const int head = (L_ / per) * 8 + (L_ % 8);
+    // Workgroups go to the 8 XCDs round-robin by linear id: the tiles of one
+    // unit (a head, or a (head, segment) pair) get ids equal mod 8, so they
+    // share one XCD's L2 for K, Q, W and T.
+    const int ntile = SEG ? seg.ntv + seg.nta : DV / DVT;
+    const int L_ = blockIdx.x, per = 8 * ntile;
+    const int unit = (L_ / per) * 8 + (L_ % 8), tile = (L_ % per) / 8;
+    const int head = SEG ? unit / seg.nsegL : unit;
+    const int g = SEG ? seg.g0 + unit % seg.nsegL : 0;
     if (head >= BH) return;
-    const StateArgs<E> A{q,  k,  v,      w,   Tm,       gin,      o, slab_of<VL>(head, T, NC, pk),
-                         ((L_ % per) / 8) * DVT, DV, tid, tid & 63, wave_id()};
-    const int lane = A.lane, wave = A.wave;
+    const bool idt = SEG && !OUT && tile >= seg.ntv;  // identity rows of a segment map
+    if (idt && g == 0) return;                        // segment 0 starts from S0: no map
+    Slab sl = slab_of<VL>(head, T, NC, pk);
+    if constexpr (SEG) {
+        const int cb = g * seg.Lc, ce = min(cb + seg.Lc, sl.nc);
+        sl.row0 += (size_t)cb * C;
+        sl.T = min(sl.T - cb * C, (ce - cb) * C);
+        sl.nc = ce - cb;
+        sl.c0 += cb;
+    }
     const size_t bh = head;
-    const int j0 = A.j0;
-    const Slab& sl = A.sl;
+    const int j0 = (idt ? tile - seg.ntv : tile) * DVT;  // first row of the tile
+    // the tile's start and end state rows (stride DK); NULL start: zero
+    const float* Sin = S0 ? S0 + (bh * DV + j0) * DK : nullptr;
+    float* Sout = S_T ? S_T + (bh * DV + j0) * DK : nullptr;
+    if constexpr (SEG) {
+        const size_t slot = bh * seg.nseg + g;
+        if constexpr (OUT) {
+            if (g > 0) Sin = seg.Sseg + (slot * DV + j0) * DK;
+            if (g != seg.nseg - 1) Sout = nullptr;
+        } else if (idt) {
+            Sin = nullptr;
+            Sout = seg.Aseg + (slot * DK + j0) * DK;
+        } else {
+            if (g > 0) Sin = nullptr;
+            Sout = seg.Sseg + ((slot + 1) * DV + j0) * DK;
+        }
+    }
+    const StateArgs<E> A{q,   k,    v,         w,    Tm,       gin,      o, sl, j0, DV, tid,
+                         tid & 63, wave_id(), idt ? 0 : j0, idt};
+    const int lane = A.lane, wave = A.wave;
 
     // two register sets receive chunks from HBM two chunks ahead of their use
     u32x4 pkA[G::PK], pqA[G::PK], pwA[G::PK], pvA[G::PV], ptA[G::PT];
@@ -898,24 +956,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
             for (int bv = 0; bv < BV; ++bv) {
                 accS[x][bi][bv] = floatx4{0.f, 0.f, 0.f, 0.f};
-                if (job < G::NSJ && S0) {
-                    const int i = 16 * (ib + bi) + 4 * (lane >> 4);
-                    const int j = 16 * (jb + bv) + (lane & 15);
-                    const float4 s4 =
-                        *reinterpret_cast<const float4*>(S0 + (bh * DV + j0 + j) * DK + i);
+                const int i = 16 * (ib + bi) + 4 * (lane >> 4);
+                const int j = 16 * (jb + bv) + (lane & 15);
+                if (job < G::NSJ && Sin) {
+                    const float4 s4 = *reinterpret_cast<const float4*>(Sin + (size_t)j * DK + i);
                     accS[x][bi][bv] = floatx4{s4.x, s4.y, s4.z, s4.w};
+                } else if (job < G::NSJ && idt) {
+                    const int r = j0 + j;  // identity row r: S[r][i] = (i == r)
+                    accS[x][bi][bv] = floatx4{i == r ? 1.f : 0.f, i + 1 == r ? 1.f : 0.f,
+                                              i + 2 == r ? 1.f : 0.f, i + 3 == r ? 1.f : 0.f};
                 }
             }
     }
 
     if (sl.nc > 0) {
-        state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, v, w, Tm, gin, sl, j0, DV, 0, tid, lane,
-                                                pkA, pqA, pwA, pvA, ptA, pgA);
-        state_prefetch<E, DK, DVT, C, kLoadAll>(q, k, v, w, Tm, gin, sl, j0, DV, 1, tid, lane,
-                                                pkB, pqB, pwB, pvB, ptB, pgB);
-        state_stage<E, DK, DVT, C, kStageAll>(L.K, L.Q, L.W[0], L.V, L.Tt, L.g, L.gam, L.del,
-                                              min(C, sl.T), tid, lane, wave, pkA, pqA, pwA, pvA,
-                                              ptA, pgA);
+        state_prefetch<E, DK, DVT, C, kLoadAll, OUT>(q, k, v, w, Tm, gin, sl, A.jv, DV, 0, tid,
+                                                     lane, pkA, pqA, pwA, pvA, ptA, pgA);
+        state_prefetch<E, DK, DVT, C, kLoadAll, OUT>(q, k, v, w, Tm, gin, sl, A.jv, DV, 1, tid,
+                                                     lane, pkB, pqB, pwB, pvB, ptB, pgB);
+        state_stage<E, DK, DVT, C, kStageAll, OUT>(L.K, L.Q, L.W[0], L.V, L.Tt, L.g, L.gam,
+                                                   L.del, min(C, sl.T), tid, lane, wave, pkA,
+                                                   pqA, pwA, pvA, ptA, pgA, idt);
     }
     state_write<E, DK, DVT, C>(accS, L.S, wave, lane);
     sync_lds();
@@ -924,16 +985,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     // (Sc: the state at every chunk start, kept for the backward pass)
     for (int c = 0; c < sl.nc; c += 2) {
         if (Sc) state_copy_out<E, DK, DVT, C>(L.S, Sc + ((sl.c0 + c) * DV + j0) * DK, tid);
-        state_chunk<E, DK, DVT, C>(A, L, accS, c, pkA, pqA, pwA, pvA, ptA, pgA, pkB, pqB, pwB,
-                                   pvB, ptB, pgB);
+        state_chunk<E, DK, DVT, C, OUT>(A, L, accS, c, pkA, pqA, pwA, pvA, ptA, pgA, pkB, pqB,
+                                        pwB, pvB, ptB, pgB);
         if (c + 1 < sl.nc) {
             if (Sc)
                 state_copy_out<E, DK, DVT, C>(L.S, Sc + ((sl.c0 + c + 1) * DV + j0) * DK, tid);
-            state_chunk<E, DK, DVT, C>(A, L, accS, c + 1, pkB, pqB, pwB, pvB, ptB, pgB, pkA, pqA,
-                                       pwA, pvA, ptA, pgA);
+            state_chunk<E, DK, DVT, C, OUT>(A, L, accS, c + 1, pkB, pqB, pwB, pvB, ptB, pgB, pkA,
+                                            pqA, pwA, pvA, ptA, pgA);
         }
     }
-    if (S_T) {
+    if (Sout) {
 #pragma unroll
         for (int x = 0; x < G::SPW; ++x) {
             const int job = wave + G::NW * x;
@@ -946,11 +1007,53 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                         const int i = 16 * (ib + bi) + 4 * (lane >> 4);
                         const int j = 16 * (jb + bv) + (lane & 15);
                         const floatx4 sv = accS[x][bi][bv];
-                        *reinterpret_cast<float4*>(S_T + (bh * DV + j0 + j) * DK + i) =
+                        *reinterpret_cast<float4*>(Sout + (size_t)j * DK + i) =
                             make_float4(sv[0], sv[1], sv[2], sv[3]);
                     }
             }
         }
+    }
+}
+
+// Start states of the segments: S_{g+1} = S_g A_g + B_g for g = 1 .. nseg - 2,
+// in order.  On entry Sseg[1] holds the true end state of segment 0 and
+// Sseg[g + 1] (g >= 1) the end state B_g of segment g from a zero start;
+// Aseg[g] holds A_g (d_k x d_k).  One workgroup per (16 rows of S, head): the
+// rows of S_g sit in LDS, A_g is read by columns (coalesced over the
+// threads), fp32 throughout.
+template <int DK>
+__global__ __launch_bounds__(256) void seg_combine_kernel(float* __restrict__ Sseg,
+                                                         const float* __restrict__ Aseg, int DV,
+                                                         int nseg) {
+    constexpr int R = 16, RG = 256 / DK, RPT = R / RG;  // rows per thread
+    __shared__ float sS[R][DK];
+    const int tid = threadIdx.x, i = tid % DK, rg = tid / DK;
+    const size_t bh = blockIdx.y;
+    const int j0 = blockIdx.x * R;
+    float* base = Sseg + bh * (size_t)nseg * DV * DK;
+    const float* abase = Aseg + bh * (size_t)nseg * DK * DK;
+    for (int e = tid; e < R * DK; e += 256)
+        sS[e / DK][e % DK] = base[((size_t)1 * DV + j0 + e / DK) * DK + e % DK];
+    __syncthreads();
+    for (int g = 1; g + 1 < nseg; ++g) {
+        float* out = base + ((size_t)(g + 1) * DV + j0) * DK;
+        const float* Ag = abase + (size_t)g * DK * DK;
+        float acc[RPT];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) acc[r] = out[(size_t)(rg * RPT + r) * DK + i];
+#pragma unroll 8
+        for (int m = 0; m < DK; ++m) {
+            const float a = Ag[(size_t)m * DK + i];
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) acc[r] = fmaf(sS[rg * RPT + r][m], a, acc[r]);
+        }
+        __syncthreads();  // every thread is done reading S_g
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            out[(size_t)(rg * RPT + r) * DK + i] = acc[r];
+            sS[rg * RPT + r][i] = acc[r];
+        }
+        __syncthreads();
     }
 }
 
@@ -1010,17 +1113,51 @@ hipError_t prep_t(const Shape& s, bool fuse, const void* k, const void* a, const
 template <typename E, int DK, int DVT, int C>
 hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, const float* g,
                    const void* w, const void* Tm, const float* S0, void* o, float* S_T, void* Sc,
-                   hipStream_t st) {
+                   const SegWs* sw, hipStream_t st) {
     if constexpr (state_fits<E, DK, DVT, C>()) {
-        const int groups = (s.BH + 7) / 8;
-#define KDN_STATE_L(VL_)                                                                     \
-    launch_k((state_kernel<E, DK, DVT, C, VL_>), dim3(groups * 8 * (s.dv / DVT)),           \
-             dim3(StateCfg<E, DK, DVT, C>::THREADS), 0, st, static_cast<const E*>(q),       \
-             static_cast<const E*>(k), static_cast<const E*>(v), g, static_cast<const E*>(w), \
-             static_cast<const E*>(Tm), S0, static_cast<E*>(o), S_T, static_cast<E*>(Sc),   \
-             s.BH, s.T, s.dv, s.nc, s.pk)
-        if (s.varlen) KDN_STATE_L(true);
-        else KDN_STATE_L(false);
+        const dim3 block(StateCfg<E, DK, DVT, C>::THREADS);
+        const int ntv = s.dv / DVT;
+        auto grid = [](int units, int ntile) { return dim3((units + 7) / 8 * 8 * ntile); };
+#define KDN_STATE_L(VL_, OUT_, SEG_, GRID_, PLAN_)                                            \
+    launch_k((state_kernel<E, DK, DVT, C, VL_, OUT_, SEG_>), GRID_, block, 0, st,             \
+             static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), g,  \
+             static_cast<const E*>(w), static_cast<const E*>(Tm), S0, static_cast<E*>(o), S_T, \
+             static_cast<E*>(Sc), s.BH, s.T, s.dv, s.nc, s.pk, PLAN_)
+        const SegPlan plain;
+        if (s.varlen) {
+            KDN_STATE_L(true, true, false, grid(s.BH, ntv), plain);
+        } else if (!sw || sw->nseg <= 1 || Sc || !o) {
+            if (o) KDN_STATE_L(false, true, false, grid(s.BH, ntv), plain);
+            else KDN_STATE_L(false, false, false, grid(s.BH, ntv), plain);
+        } else {
+            // segments: the maps of segments 0 .. nseg - 2, their composition
+            // into every segment's start state, then the read-out pass; the
+            // caller's timing events bracket the three launches
+            const LaunchTiming t = launch_timing();
+            SegPlan p;
+            p.nseg = sw->nseg;
+            p.Lc = sw->Lc;
+            p.Sseg = sw->Sseg;
+            p.Aseg = sw->Aseg;
+            p.g0 = 0;
+            p.nsegL = sw->nseg - 1;
+            p.ntv = ntv;
+            p.nta = DK / DVT;
+            launch_timing() = LaunchTiming{t.start, nullptr};
+            KDN_STATE_L(false, false, true, grid(s.BH * p.nsegL, p.ntv + p.nta), p);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            if (sw->nseg > 2) {
+                launch_k(seg_combine_kernel<DK>, dim3(s.dv / 16, s.BH), dim3(256), 0, st,
+                         sw->Sseg, static_cast<const float*>(sw->Aseg), s.dv, sw->nseg);
+                e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
+            p.nsegL = sw->nseg;
+            p.nta = 0;
+            launch_timing() = LaunchTiming{nullptr, t.stop};
+            KDN_STATE_L(false, true, true, grid(s.BH * p.nsegL, p.ntv), p);
+        }
 #undef KDN_STATE_L
         return hipGetLastError();
     } else {
@@ -1047,11 +1184,11 @@ hipError_t prep_e(const Shape& s, bool fuse, const void* k, const void* a, const
 template <typename E>
 hipError_t state_e(const Shape& s, const void* q, const void* k, const void* v, const float* g,
                    const void* w, const void* Tm, const float* S0, void* o, float* S_T, void* Sc,
-                   hipStream_t st) {
+                   const SegWs* sw, hipStream_t st) {
     const int dvt = dv_tile(s);
 #define KDN_ST(DK_, DVT_, C_)                                                             \
     if (s.dk == DK_ && dvt == DVT_ && s.chunk == C_)                                      \
-        return state_t<E, DK_, DVT_, C_>(s, q, k, v, g, w, Tm, S0, o, S_T, Sc, st);
+        return state_t<E, DK_, DVT_, C_>(s, q, k, v, g, w, Tm, S0, o, S_T, Sc, sw, st);
 #define KDN_ST_C(DK_, DVT_) KDN_ST(DK_, DVT_, 16) KDN_ST(DK_, DVT_, 32) KDN_ST(DK_, DVT_, 64)
     KDN_ST_C(32, 32) KDN_ST_C(32, 64) KDN_ST_C(64, 32) KDN_ST_C(64, 64)
     KDN_ST_C(128, 32) KDN_ST_C(128, 64)
@@ -1079,10 +1216,30 @@ hipError_t launch_chunk_prep(const Shape& s, bool fuse_gain, const void* k, cons
 
 hipError_t launch_chunk_state(const Shape& s, const void* q, const void* k, const void* v,
                               const float* g, const void* w, const void* Tm, const float* S0,
-                              void* o, float* S_T, hipStream_t st, void* Sc) {
+                              void* o, float* S_T, hipStream_t st, void* Sc, const SegWs* seg) {
     if (s.BH == 0) return hipSuccess;
-    return s.qkv_bf16 ? state_e<bf16_t>(s, q, k, v, g, w, Tm, S0, o, S_T, Sc, st)
-                      : state_e<float>(s, q, k, v, g, w, Tm, S0, o, S_T, Sc, st);
+    return s.qkv_bf16 ? state_e<bf16_t>(s, q, k, v, g, w, Tm, S0, o, S_T, Sc, seg, st)
+                      : state_e<float>(s, q, k, v, g, w, Tm, S0, o, S_T, Sc, seg, st);
+}
+
+int state_segments(const Shape& s, int* chunks_per_segment) {
+    int Lc = s.nc, nseg = 1;
+    const int dvt = dv_tile(s);
+    // at low B*H the plain pass runs B*H*(dv/dvt) workgroups, one per CU:
+    // cut each head into segments until about one workgroup per CU runs the
+    // read-out pass, keeping at least 8 chunks per segment
+    if (!s.varlen && s.BH > 0 && dvt > 0 && s.nc >= 16) {
+        const int units = s.BH * (s.dv / dvt);
+        if (units < 128) {
+            const int want = std::min(256 / units, s.nc / 8);
+            if (want >= 2) {
+                Lc = (s.nc + want - 1) / want;
+                nseg = (s.nc + Lc - 1) / Lc;
+            }
+        }
+    }
+    if (chunks_per_segment) *chunks_per_segment = Lc;
+    return nseg;
 }
 
 }  // namespace kdn

@@ -72,13 +72,30 @@ hipError_t launch_gain(const Shape& s, const void* k, const void* r, const float
 hipError_t launch_chunk_prep(const Shape& s, bool fuse_gain, const void* k, const void* a,
                              const void* nu, const void* r, const float* lam_chunk, void* w,
                              void* Tm, float* g, hipStream_t st, float* dinv = nullptr);
+// Workspace of a state pass over sequence segments: nseg segments of Lc
+// chunks per head (state_segments), the start state of every segment
+// Sseg [BH][nseg][dv][dk] and the linear part of every segment's affine map
+// Aseg [BH][nseg][dk][dk], both float32.
+struct SegWs {
+    int nseg = 1, Lc = 0;
+    float* Sseg = nullptr;
+    float* Aseg = nullptr;
+};
+// Segments per head that the state pass uses for this shape (1: the plain
+// sequential pass); *chunks_per_segment (may be NULL) receives Lc.
+int state_segments(const Shape& s, int* chunks_per_segment);
 // Sequential chunk pass: memory write and read-out (g from the prep pass).
 // Sc (may be NULL): the state at every chunk start, [BH][nc][dv][dk] in qkv
 // dtype, kept for the backward pass.
 // o may be NULL (not written) when only Sc is wanted.
+// seg (may be NULL): with seg->nseg > 1 (and o given, Sc NULL, a fixed-length
+// batch) the pass runs over sequence segments in three launches: each
+// segment's affine map, their composition in order, and the read-out of every
+// segment from its start state.
 hipError_t launch_chunk_state(const Shape& s, const void* q, const void* k, const void* v,
                               const float* g, const void* w, const void* Tm, const float* S0,
-                              void* o, float* S_T, hipStream_t st, void* Sc = nullptr);
+                              void* o, float* S_T, hipStream_t st, void* Sc = nullptr,
+                              const SegWs* seg = nullptr);
 // One decode step in place.  slot (may be NULL): per active sequence, the
 // cache slot of its state among n_slots (H heads each); outside [0, n_slots):
 // idle, nothing read or written for that sequence.

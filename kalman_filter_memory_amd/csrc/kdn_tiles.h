@@ -173,8 +173,9 @@ template <typename E, int DK, int DVT, int C> struct StateCfg {
 // through W, whose padded rows are stored as zeros).  The loads come in three
 // parts issued at the starts of the three phases of a chunk: a burst of every
 // wave's loads at once would stall the waves on the vector-memory issue queue.
+// WQ = false: Q is neither loaded nor staged (a pass with no read-out).
 enum { kLoadKQ = 0, kLoadW = 1, kLoadVTG = 2, kLoadAll = 3 };
-template <typename E, int DK, int DVT, int C, int PART>
+template <typename E, int DK, int DVT, int C, int PART, bool WQ = true>
 __device__ __forceinline__ void state_prefetch(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ w, const E* __restrict__ Tm, const float* __restrict__ gin,
@@ -196,7 +197,7 @@ __device__ __forceinline__ void state_prefetch(
                 const size_t off = (row0 + min(t, n - 1)) * DK + c0;
                 if constexpr (PART != kLoadW) {
                     pk[x] = *reinterpret_cast<const u32x4*>(k + off);
-                    pq[x] = *reinterpret_cast<const u32x4*>(q + off);
+                    if constexpr (WQ) pq[x] = *reinterpret_cast<const u32x4*>(q + off);
                 }
                 if constexpr (PART != kLoadKQ) pw[x] = *reinterpret_cast<const u32x4*>(w + off);
             }
@@ -224,15 +225,15 @@ __device__ __forceinline__ void state_prefetch(
 }
 
 // parts of a chunk staged from registers into LDS: K, Q, W and V; T and the
-// decay tables
+// decay tables.  zero_v: V is staged as zeros (the loaded values are dropped).
 enum { kStageKQWV = 1, kStageT = 2, kStageAll = 3 };
-template <typename E, int DK, int DVT, int C, int PARTS>
+template <typename E, int DK, int DVT, int C, int PARTS, bool WQ = true>
 __device__ __forceinline__ void state_stage(
     E* sK, E* sQ, E* sWc, E* sV, E* sT, float* sg, float* sgam, float* sdel, int n, int tid,
     int lane, int wave, const u32x4 (&pk)[StateCfg<E, DK, DVT, C>::PK],
     const u32x4 (&pq)[StateCfg<E, DK, DVT, C>::PK], const u32x4 (&pw)[StateCfg<E, DK, DVT, C>::PK],
     const u32x4 (&pv)[StateCfg<E, DK, DVT, C>::PV], const u32x4 (&pt)[StateCfg<E, DK, DVT, C>::PT],
-    float pg) {
+    float pg, bool zero_v = false) {
     using G = StateCfg<E, DK, DVT, C>;
     constexpr int VEC = G::VEC, LDK = G::LDK, LDC = G::LDC, LDV = G::LDV;
     if constexpr ((PARTS & kStageKQWV) != 0) {
@@ -242,7 +243,7 @@ __device__ __forceinline__ void state_stage(
             if (G::NVK % G::THREADS == 0 || e < G::NVK) {
                 const int t = e / (DK / VEC), c0 = (e % (DK / VEC)) * VEC;
                 *reinterpret_cast<u32x4*>(sK + t * LDK + c0) = pk[x];
-                *reinterpret_cast<u32x4*>(sQ + t * LDK + c0) = pq[x];
+                if constexpr (WQ) *reinterpret_cast<u32x4*>(sQ + t * LDK + c0) = pq[x];
                 // padded rows of W are zero (a select at staging time, when the
                 // loaded row has to have arrived anyway)
                 const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -254,7 +255,8 @@ __device__ __forceinline__ void state_stage(
             const int e = tid + G::THREADS * x;
             if (G::NVV % G::THREADS == 0 || e < G::NVV) {
                 const int t = e / (DVT / VEC), c0 = (e % (DVT / VEC)) * VEC;
-                *reinterpret_cast<u32x4*>(sV + t * LDV + c0) = pv[x];
+                const u32x4 zero = {0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4*>(sV + t * LDV + c0) = zero_v ? zero : pv[x];
             }
         }
     }

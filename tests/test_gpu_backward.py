@@ -45,13 +45,23 @@ def _oracle_backward(inp, cot):
                            variant=inp["variant"])
 
 
-def _errors(got, ref, heads=None):
+def _errors(got, ref):
+    """Normwise error per (b, h) slice.  A per-head scalar (the isotropic
+    dlambda0, shape [B, H]) has one element per slice, where the normwise
+    ratio degenerates into the elementwise one that is ill-posed near zero; it
+    is taken over the H heads of each batch element instead (max over heads of
+    |x - ref| divided by the max over heads of |ref|).  Its per-head relative
+    errors are printed as a diagnostic."""
     err = {}
     for n in GRADS:
         x = got[n]
-        if heads is not None:
-            x = x[tuple(np.array(heads).T)][:, None]
-        err[n] = normwise(x, ref[n])
+        if ref[n].ndim == 2:
+            err[n] = normwise(x[None], ref[n][None])
+            rel = np.abs(x - ref[n]) / np.maximum(np.abs(ref[n]), 1e-300)
+            say(f"    {n} per head: worst relative {rel.max():.1e}, median {np.median(rel):.1e}, "
+                f"|ref| from {np.abs(ref[n]).min():.2e} to {np.abs(ref[n]).max():.2e}")
+        else:
+            err[n] = normwise(x, ref[n])
     return err
 
 

@@ -90,6 +90,33 @@ def test_forward_no_heads_is_a_no_op():
     assert o.size == 0 and S_T.size == 0
 
 
+# ------------------------------------------- the segmented state pass
+# Few heads, many chunks: the state pass is cut into sequence segments (each
+# segment's affine map, their composition, then the read-out).  Shapes with a
+# ragged last chunk, several segment counts, both variants and dtypes.
+SEGMENTED = [
+    # B, H, T, dk, dv, chunk, variant, dtype
+    (1, 1, 16 * 64 + 37, 64, 64, 64, "diagonal", "f32"),
+    (1, 2, 40 * 32 + 5, 128, 64, 32, "isotropic", "f32"),
+    (2, 1, 24 * 16 + 9, 32, 128, 16, "diagonal", "bf16"),
+    (1, 3, 20 * 64, 128, 128, 64, "diagonal", "bf16"),
+    (1, 1, 70 * 64 + 63, 128, 32, 64, "isotropic", "bf16"),
+    (1, 2, 33 * 32, 32, 32, 32, "diagonal", "f32"),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SEGMENTED)),
+                         ids=["seg_B{}H{}T{}k{}v{}C{}_{}_{}".format(*c) for c in SEGMENTED])
+def test_segmented_state_pass_matches_oracle(idx):
+    B, H, T, dk, dv, C, variant, dtype = SEGMENTED[idx]
+    inp = forward_inputs(B, H, T, dk, dv, variant=variant, dtype=dtype, seed=150 + idx)
+    td = kdn.BF16 if dtype == "bf16" else kdn.F32
+    nseg = kdn.forward_segments(kdn.make_desc(B, H, T, dk, dv, C, variant, td, td))
+    say(f"[gpu] segmented state pass: {nseg} segments")
+    assert nseg > 1
+    _check_forward(inp, C, f"segmented ({nseg} segments)")
+
+
 # ---------------------------------------------------- the named workloads
 def test_workload_iso_f32_B1_H2_T256_d32():
     _check_forward(config_inputs(0), 32, "iso f32 [1,2,256,32]")
