@@ -921,6 +921,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
     const size_t bh = head;
     const int j0 = (idt ? tile - seg.ntv : tile) * DVT;  // first row of the tile
+    // rows of the tile that exist: identity tiles hold the d_k rows of A_g,
+    // and with d_k < DVT only the first d_k of their rows
+    const int nrows = idt ? min(DVT, DK - j0) : DVT;
     // the tile's start and end state rows (stride DK); NULL start: zero
     const float* Sin = S0 ? S0 + (bh * DV + j0) * DK : nullptr;
     float* Sout = S_T ? S_T + (bh * DV + j0) * DK : nullptr;
@@ -1007,8 +1010,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                         const int i = 16 * (ib + bi) + 4 * (lane >> 4);
                         const int j = 16 * (jb + bv) + (lane & 15);
                         const floatx4 sv = accS[x][bi][bv];
-                        *reinterpret_cast<float4*>(Sout + (size_t)j * DK + i) =
-                            make_float4(sv[0], sv[1], sv[2], sv[3]);
+                        if (j < nrows)
+                            *reinterpret_cast<float4*>(Sout + (size_t)j * DK + i) =
+                                make_float4(sv[0], sv[1], sv[2], sv[3]);
                     }
             }
         }
@@ -1142,7 +1146,7 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
             p.g0 = 0;
             p.nsegL = sw->nseg - 1;
             p.ntv = ntv;
-            p.nta = DK / DVT;
+            p.nta = (DK + DVT - 1) / DVT;  // identity rows past d_k are not written
             launch_timing() = LaunchTiming{t.start, nullptr};
             KDN_STATE_L(false, false, true, grid(s.BH * p.nsegL, p.ntv + p.nta), p);
             hipError_t e = hipGetLastError();
