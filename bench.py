@@ -114,6 +114,8 @@ def bytes_8d(B, H, T, dk, dv):
 def _stats(xs):
     import numpy as np
 
+    if len(xs) == 0:
+        return None
     a = np.asarray(xs, dtype=np.float64)
     return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
             "p90": round(float(np.percentile(a, 90)), 2), "mean": round(float(a.mean()), 2),

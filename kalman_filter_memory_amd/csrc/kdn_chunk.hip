@@ -1022,41 +1022,69 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 // Start states of the segments: S_{g+1} = S_g A_g + B_g for g = 1 .. nseg - 2,
 // in order.  On entry Sseg[1] holds the true end state of segment 0 and
 // Sseg[g + 1] (g >= 1) the end state B_g of segment g from a zero start;
-// Aseg[g] holds A_g (d_k x d_k).  One workgroup per (16 rows of S, head): the
-// rows of S_g sit in LDS, A_g is read by columns (coalesced over the
-// threads), fp32 throughout.
+// Aseg[g] holds A_g (d_k x d_k).  One workgroup per (kCombRows rows of S,
+// head), fp32 throughout.  A_g sits in LDS, and A_{g+1} is loaded into the
+// other LDS buffer (through registers, every load issued at once) while step g
+// computes, so each step waits for global memory at most once.
+constexpr int kCombRows = 8, kCombThreads = 256;
+
 template <int DK>
-__global__ __launch_bounds__(256) void seg_combine_kernel(float* __restrict__ Sseg,
-                                                         const float* __restrict__ Aseg, int DV,
-                                                         int nseg) {
-    constexpr int R = 16, RG = 256 / DK, RPT = R / RG;  // rows per thread
-    __shared__ float sS[R][DK];
+__global__ __launch_bounds__(kCombThreads) void seg_combine_kernel(float* __restrict__ Sseg,
+                                                                  const float* __restrict__ Aseg,
+                                                                  int DV, int nseg) {
+    constexpr int R = kCombRows, RG = kCombThreads / DK, RPT = R / RG;  // rows per thread
+    constexpr int NV = DK * DK / 4 / kCombThreads;  // float4 pieces of A per thread
+    static_assert(RPT * RG == R && NV * 4 * kCombThreads == DK * DK, "combine tiling");
+    __shared__ __align__(16) float sA[2][DK * DK];
+    __shared__ __align__(16) float sS[R][DK];
     const int tid = threadIdx.x, i = tid % DK, rg = tid / DK;
     const size_t bh = blockIdx.y;
     const int j0 = blockIdx.x * R;
     float* base = Sseg + bh * (size_t)nseg * DV * DK;
     const float* abase = Aseg + bh * (size_t)nseg * DK * DK;
-    for (int e = tid; e < R * DK; e += 256)
+    float4 pre[NV];
+    auto fetch = [&](int g) {
+        const float4* src = reinterpret_cast<const float4*>(abase + (size_t)g * DK * DK);
+#pragma unroll
+        for (int x = 0; x < NV; ++x) pre[x] = src[tid + kCombThreads * x];
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int x = 0; x < NV; ++x)
+            reinterpret_cast<float4*>(sA[buf])[tid + kCombThreads * x] = pre[x];
+    };
+    fetch(1);
+    for (int e = tid; e < R * DK; e += kCombThreads)
         sS[e / DK][e % DK] = base[((size_t)1 * DV + j0 + e / DK) * DK + e % DK];
+    stage(1 & 1);
     __syncthreads();
     for (int g = 1; g + 1 < nseg; ++g) {
+        if (g + 2 < nseg) fetch(g + 1);  // in flight during this step
         float* out = base + ((size_t)(g + 1) * DV + j0) * DK;
-        const float* Ag = abase + (size_t)g * DK * DK;
+        const float* A = sA[g & 1];
         float acc[RPT];
 #pragma unroll
         for (int r = 0; r < RPT; ++r) acc[r] = out[(size_t)(rg * RPT + r) * DK + i];
-#pragma unroll 8
-        for (int m = 0; m < DK; ++m) {
-            const float a = Ag[(size_t)m * DK + i];
+#pragma unroll 4
+        for (int m = 0; m < DK; m += 4) {
+            const float a0 = A[(m + 0) * DK + i], a1 = A[(m + 1) * DK + i];
+            const float a2 = A[(m + 2) * DK + i], a3 = A[(m + 3) * DK + i];
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) acc[r] = fmaf(sS[rg * RPT + r][m], a, acc[r]);
+            for (int r = 0; r < RPT; ++r) {
+                const float4 sv = *reinterpret_cast<const float4*>(&sS[rg * RPT + r][m]);
+                acc[r] = fmaf(sv.x, a0, acc[r]);
+                acc[r] = fmaf(sv.y, a1, acc[r]);
+                acc[r] = fmaf(sv.z, a2, acc[r]);
+                acc[r] = fmaf(sv.w, a3, acc[r]);
+            }
         }
-        __syncthreads();  // every thread is done reading S_g
+        __syncthreads();  // every thread is done reading S_g and A_g
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
             out[(size_t)(rg * RPT + r) * DK + i] = acc[r];
             sS[rg * RPT + r][i] = acc[r];
         }
+        if (g + 2 < nseg) stage((g + 1) & 1);
         __syncthreads();
     }
 }
@@ -1152,7 +1180,7 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             if (sw->nseg > 2) {
-                launch_k(seg_combine_kernel<DK>, dim3(s.dv / 16, s.BH), dim3(256), 0, st,
+                launch_k(seg_combine_kernel<DK>, dim3(s.dv / kCombRows, s.BH), dim3(kCombThreads), 0, st,
                          sw->Sseg, static_cast<const float*>(sw->Aseg), s.dv, sw->nseg);
                 e = hipGetLastError();
                 if (e != hipSuccess) return e;

@@ -15,8 +15,10 @@
 //   reduce: one wave per chunk of `chunk` tokens forms the chunk's matrix
 //           product (diagonal: lane = key dimension, sequential over tokens;
 //           isotropic: lane = token, ordered wave-wide tree product);
-//   carry:  one thread per (head, key dim) applies the chunk products in order
-//           and writes the precision at every chunk boundary and lambda_T;
+//   carry:  lanes over (segment of chunks, scan): segment products, a
+//           log-depth scan of them across lanes, then each lane's walk over
+//           its segment, writing the precision at every chunk boundary and
+//           lambda_T;
 //   emit:   one wave per chunk replays its tokens from the boundary value and
 //           writes every predictive precision lambda^-.
 // The gain kernel forms w = P^- k / (k^T P^- k + r) from given lambda^-.
@@ -261,14 +263,18 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_iso_kernel(
 
 // ------------------------------------------------------------------- carry
 // Each scan (one per (head, key dim) or per head) runs over the chunk maps in
-// order.  A wave takes 16 scans and cuts each into kCarrySeg segments of
-// consecutive chunks, one lane per (segment, scan): rows of 16 lanes are
-// segments.  A lane composes its segment's maps, takes the products of the
-// segments before its own from the lanes of its scan, carries the starting
-// precision through them, and walks its segment writing the precision at each
-// chunk start.  Segments of up to kCarryGroup chunks stay in registers between
-// the two passes; longer ones are read twice, kCarryGroup maps at a time.
-constexpr int kCarrySeg = 4, kCarryScans = kWave / kCarrySeg, kCarryGroup = 16;
+// order.  A wave takes 64 / SEG scans and cuts each into SEG segments of
+// consecutive chunks, one lane per (segment, scan): rows of 64 / SEG lanes are
+// segments, so the lanes of a row read neighbouring scans' maps together.  A
+// lane composes its segment's maps; the segment products are then scanned
+// across the rows of lanes in log2(SEG) steps (Hillis-Steele, later segments on
+// the left); each lane carries the starting precision through the product of
+// the segments before its own and walks its segment writing the precision at
+// each chunk start.  Segments of up to kCarryGroup chunks stay in registers
+// between the two passes; longer ones are read twice, kCarryGroup maps at a
+// time.  SEG grows with the chunk count (4 at 64 chunks, 64 at 1,024), so that
+// long sequences spread over more lanes and waves.
+constexpr int kCarryGroup = 16;
 
 __device__ __forceinline__ M2 as_m2(const float4& v) { return {v.x, v.y, v.z, v.w}; }
 
@@ -276,22 +282,23 @@ __device__ __forceinline__ float mob_apply_fast(const float4& m, float x) {
     return fmaf(m.x, x, m.y) * __builtin_amdgcn_rcpf(fmaf(m.z, x, m.w));
 }
 
-template <bool ONE_GROUP, bool VL>
+template <int SEG, bool ONE_GROUP, bool VL>
 __global__ __launch_bounds__(kWave) void carry_kernel(const float4* __restrict__ agg,
                                                       const float* __restrict__ lambda0, int BH,
                                                       int NL, int T, int NC_all,
                                                       float* __restrict__ lam_chunk,
                                                       float* __restrict__ lambda_T, Packed pk) {
-    const int lane = threadIdx.x, seg = lane / kCarryScans, sl = lane % kCarryScans;
+    constexpr int SC = kWave / SEG;  // scans per wave
+    const int lane = threadIdx.x, seg = lane / SC, sl = lane % SC;
     const size_t n_scan = (size_t)BH * NL;
-    const size_t idx = blockIdx.x * (size_t)kCarryScans + sl;  // bh * NL + i
+    const size_t idx = blockIdx.x * (size_t)SC + sl;  // bh * NL + i
     const bool valid = idx < n_scan;
     const size_t id = valid ? idx : n_scan - 1;  // loads of lanes past the end stay in range
     const size_t bh = id / NL, i = id % NL;
     const Slab sb = slab_of<VL>(bh, T, NC_all, pk);
     const int NC = sb.nc;
     const float4* src = agg + sb.c0 * NL + i;
-    const int SL = (NC + kCarrySeg - 1) / kCarrySeg;
+    const int SL = (NC + SEG - 1) / SEG;
     const int c0 = min(seg * SL, NC), c1 = min(c0 + SL, NC);  // this lane's chunks [c0, c1)
     auto map_at = [&](int c) { return src[(size_t)min(c, NC - 1) * NL]; };
 
@@ -309,16 +316,18 @@ __global__ __launch_bounds__(kWave) void carry_kernel(const float4* __restrict__
         if (ONE_GROUP) break;
     }
     P = mob_renorm(P);
-    // (2) precision at the segment start: the starting one carried through the
-    // products of the earlier segments of the same scan
-    float lam = lambda0 ? lambda0[id] : 1.f;
+    // (2) inclusive scan of the segment products over the segments of a scan
+    // (lane seg then holds segments seg..0), then the exclusive one: the
+    // product of the segments before this lane's
 #pragma unroll
-    for (int j = 0; j < kCarrySeg - 1; ++j) {
-        const int from = j * kCarryScans + sl;
-        const float4 q = make_float4(__shfl(P.a, from, kWave), __shfl(P.b, from, kWave),
-                                     __shfl(P.c, from, kWave), __shfl(P.d, from, kWave));
-        if (j < seg) lam = mob_apply_fast(q, lam);
+    for (int off = 1; off < SEG; off <<= 1) {
+        const M2 q = shfl_up_m2(P, off * SC);
+        if (seg >= off) P = mob_renorm(mob_mul(P, q));
     }
+    M2 E = shfl_up_m2(P, SC);
+    if (seg == 0) E = M2{1.f, 0.f, 0.f, 1.f};
+    float lam = lambda0 ? lambda0[id] : 1.f;
+    lam = mob_apply_fast(make_float4(E.a, E.b, E.c, E.d), lam);
     // (3) walk the segment
     float* out = lam_chunk ? lam_chunk + sb.l0 * NL + i : nullptr;
     for (int g = c0; g < c1; g += kCarryGroup) {
@@ -335,7 +344,7 @@ __global__ __launch_bounds__(kWave) void carry_kernel(const float4* __restrict__
         }
         if (ONE_GROUP) break;
     }
-    if (seg == kCarrySeg - 1 && valid) {  // the last segment ends at chunk NC
+    if (seg == SEG - 1 && valid) {  // the last segment ends at chunk NC
         if (out) out[(size_t)NC * NL] = lam;
         if (lambda_T) lambda_T[id] = lam;
     }
@@ -567,19 +576,26 @@ hipError_t launch_scan_carry(const Shape& s, const float* agg, const float* lamb
     const int NL = s.diag ? s.dk : 1;
     const size_t n = (size_t)s.BH * NL;
     if (n == 0) return hipSuccess;
-    const dim3 grid((unsigned)((n + kCarryScans - 1) / kCarryScans)), block(kWave);
+    // segments per scan: about 16 chunks each, 4 to 64
+    int seg = 4;
+    while (seg < 64 && seg * kCarryGroup < s.nc) seg *= 2;
+    const bool one = s.nc <= seg * kCarryGroup;
     const float4* a4 = reinterpret_cast<const float4*>(agg);
-#define KDN_CARRY_L(ONE_, VL_)                                                             \
-    launch_k(carry_kernel<ONE_, VL_>, grid, block, 0, st, a4, lambda0, s.BH, NL, s.T, s.nc, \
-             lam_chunk, lambda_T, s.pk)
-    const bool one = s.nc <= kCarrySeg * kCarryGroup;
-    if (s.varlen) {
-        if (one) KDN_CARRY_L(true, true);
-        else KDN_CARRY_L(false, true);
-    } else {
-        if (one) KDN_CARRY_L(true, false);
-        else KDN_CARRY_L(false, false);
+#define KDN_CARRY_L(SEG_, ONE_, VL_)                                                           \
+    launch_k(carry_kernel<SEG_, ONE_, VL_>, dim3((unsigned)((n + kWave / SEG_ - 1) / (kWave / SEG_))), \
+             dim3(kWave), 0, st, a4, lambda0, s.BH, NL, s.T, s.nc, lam_chunk, lambda_T, s.pk)
+#define KDN_CARRY_S(SEG_)                                                                      \
+    if (seg == SEG_) {                                                                         \
+        if (s.varlen) {                                                                        \
+            if (one) KDN_CARRY_L(SEG_, true, true);                                            \
+            else KDN_CARRY_L(SEG_, false, true);                                               \
+        } else {                                                                               \
+            if (one) KDN_CARRY_L(SEG_, true, false);                                           \
+            else KDN_CARRY_L(SEG_, false, false);                                              \
+        }                                                                                      \
     }
+    KDN_CARRY_S(4) KDN_CARRY_S(8) KDN_CARRY_S(16) KDN_CARRY_S(32) KDN_CARRY_S(64)
+#undef KDN_CARRY_S
 #undef KDN_CARRY_L
     return hipGetLastError();
 }

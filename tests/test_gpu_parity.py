@@ -213,6 +213,25 @@ def test_mobius_scan_matches_oracle_precisions(variant, dtype):
 
 
 @pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+@pytest.mark.parametrize("T,chunk", [(200 * 16 + 7, 16), (20000, 16), (1500 * 64 + 5, 64)])
+def test_mobius_scan_carry_over_many_chunks(variant, T, chunk):
+    """The carry splits each scan into more segments as the chunk count grows
+    (16 at 201 chunks, 64 at 1,250 and 1,501 chunks, where a segment no longer
+    fits in registers and is read twice)."""
+    inp = forward_inputs(1, 2, T, 32, 32, variant=variant, dtype="bf16", seed=29, a_mu=4.0)
+    say(f"[gpu] mobius_scan carry, {variant}, T={T} chunk={chunk}")
+    t = forward_tensors(inp)
+    out = kdn.mobius_scan(t["k"], t["a"], t["nu"], t["r"], t["lambda0"], variant=variant,
+                          chunk=chunk, lambda_minus=True, lambda_chunk=True)
+    torch.cuda.synchronize()
+    ref = _oracle_forward(inp, debug=True)
+    e_lm = elementwise(host(out["lambda_minus"]), ref["lambda_minus"])
+    e_lt = elementwise(host(out["lambda_T"]), ref["lambda_T"])
+    say(f"    err lambda_minus {e_lm:.2e}  lambda_T {e_lt:.2e}")
+    assert e_lm <= TOL_LAMBDA and e_lt <= TOL_LAMBDA
+
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
 @pytest.mark.parametrize("dtype,gain_dtype", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
 def test_gain_matches_oracle(variant, dtype, gain_dtype):
     inp = forward_inputs(1, 3, 150, 128, 32, variant=variant, dtype=dtype, seed=22)
