@@ -124,6 +124,27 @@ kdn_status kdn_forward_events(const kdn_desc *d, const void *q, const void *k, c
                               float *lambda_T, void *ws, size_t ws_bytes, void *stream,
                               void *const *events);
 
+/* ------------------------------------------------------------------------
+ * Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  kdn_forward_noalloc is kdn_forward (same arguments, same
+ * kernels, same results bit for bit) with its workspace in a static device
+ * array of KDN_NOALLOC_SCRATCH_BYTES instead of a caller buffer; it calls no
+ * allocating routine.  Each GPU it runs on holds its own copy of the array
+ * until the process ends; the array's device address is looked up once per
+ * device (hipGetSymbolAddress) on the first call on it, with the device
+ * current.  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (other streams, other threads) race on it and must be ordered by
+ * the caller.  Returns KDN_ERR_WORKSPACE when kdn_forward_workspace_bytes(d)
+ * exceeds the array (B8 H16 T4096 d128 chunk 64 fits; B1 H16 T65536 does
+ * not), KDN_ERR_HIP if the array's address cannot be obtained. */
+#define KDN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+size_t kdn_noalloc_scratch_bytes(void);
+kdn_status kdn_forward_noalloc(const kdn_desc *d, const void *q, const void *k, const void *v,
+                               const void *a, const void *qnoise, const void *r,
+                               const float *lambda0, const float *S0, void *o, float *S_T,
+                               float *lambda_T, void *stream);
+
 /* Bytes of workspace kdn_mobius_scan needs (0 if invalid). */
 size_t kdn_mobius_scan_workspace_bytes(const kdn_desc *d);
 

@@ -46,6 +46,7 @@ EXPORTS = (
     "kdn_decode_step_indexed", "kdn_forward_varlen_workspace_bytes", "kdn_forward_varlen",
     "kdn_dense_gain", "kdn_blas_create", "kdn_blas_destroy", "kdn_layer_workspace_bytes",
     "kdn_layer_forward", "kdn_layer_forward_events",
+    "kdn_noalloc_scratch_bytes", "kdn_forward_noalloc",
 )
 
 
@@ -116,6 +117,10 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_backward_kept.argtypes = [D] + [P] * 19 + [P, S, P]
     lib.kdn_backward_kept_events.argtypes = [D] + [P] * 19 + [P, S, P, ctypes.POINTER(P)]
     lib.kdn_decode_step.restype = I
+    lib.kdn_noalloc_scratch_bytes.argtypes = []
+    lib.kdn_noalloc_scratch_bytes.restype = S
+    lib.kdn_forward_noalloc.argtypes = [D] + [P] * 11 + [P]
+    lib.kdn_forward_noalloc.restype = I
     _lib = lib
     return lib
 
@@ -261,6 +266,36 @@ def forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", ch
             raise ValueError("events: 8 entries (start and stop of four kernels)")
         arr = (ctypes.c_void_p * 8)(*[None if e is None else e.cuda_event for e in events])
         _check(lib.kdn_forward_events(*args, arr), "kdn_forward_events")
+    return o, S_T, lam_T
+
+
+def forward_noalloc(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", chunk=64,
+                    out=None):
+    """kdn_forward_noalloc: the forward with the library's static device
+    scratch array as its workspace (the C call allocates nothing).  out:
+    optional preallocated (o, S_T, lambda_T); otherwise they are allocated
+    here, by torch, before the call.  Calls on one GPU share the array and must
+    not overlap."""
+    lib = load_library()
+    d = _forward_desc(q, k, v, a, qnoise, r, variant, chunk)
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    lam_shape = (B, H, dk) if d.variant == DIAGONAL else (B, H)
+    for x, name, shape in ((lambda0, "lambda0", lam_shape), (S0, "S0", (B, H, dv, dk))):
+        if x is not None:
+            _gpu(x, name)
+            if x.dtype != torch.float32 or tuple(x.shape) != shape:
+                raise ValueError(f"{name} must be float32 {shape}")
+    if out is not None:
+        o, S_T, lam_T = out
+    else:
+        dev = k.device
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        lam_T = torch.empty(lam_shape, dtype=torch.float32, device=dev)
+    _check(lib.kdn_forward_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                   _ptr(qnoise), _ptr(r), _ptr(lambda0), _ptr(S0), _ptr(o),
+                                   _ptr(S_T), _ptr(lam_T), _stream()), "kdn_forward_noalloc")
     return o, S_T, lam_T
 
 
