@@ -49,14 +49,18 @@ def algorithmic(B, H, T, dk, dv, C, variant="diagonal"):
     e = 2                   # bf16 bytes
     g = 3 * e               # a, nu, r per token-head
     nl = dk if variant == "diagonal" else 1  # precisions per token
+    ns = C // 16 if variant == "diagonal" else 1  # products kept per (chunk, precision)
     by = {
-        # read k and the three gates, write one float4 Moebius product per (chunk, precision)
-        "scan_reduce": n * (dk * e + g) + bh * nc * nl * 16,
+        # read k and the three gates, write the float4 Moebius products per
+        # (chunk, precision): the prefixes after every 16 tokens (diagonal), the
+        # last being the chunk's product
+        "scan_reduce": n * (dk * e + g) + bh * nc * ns * nl * 16,
         # read the chunk products, write chunk-boundary precisions
         "scan_carry": bh * nc * nl * 16 + bh * (nc + 1) * nl * 4 + bh * nl * 4 * 2,
-        # read k, gates, boundary precisions; write w, T and the log2 decays
-        "chunk_prep": n * (dk * e + g) + bh * nc * nl * 4 + n * dk * e + bh * nc * C * C * e
-        + n * 4,
+        # read k, gates, boundary precisions and the sub-block prefixes; write w,
+        # T and the log2 decays
+        "chunk_prep": n * (dk * e + g) + bh * nc * nl * 4 + bh * nc * (ns - 1) * nl * 16
+        + n * dk * e + bh * nc * C * C * e + n * 4,
         # read q, k, v, w, T, log2 decays, S0; write o, S_T
         "chunk_state": n * (3 * dk + dv) * e + n * 4 + bh * nc * C * C * e + n * dv * e
         + 2 * bh * dv * dk * 4,

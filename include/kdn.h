@@ -138,7 +138,7 @@ kdn_status kdn_forward_events(const kdn_desc *d, const void *q, const void *k, c
  * the caller.  Returns KDN_ERR_WORKSPACE when kdn_forward_workspace_bytes(d)
  * exceeds the array (B8 H16 T4096 d128 chunk 64 fits; B1 H16 T65536 does
  * not), KDN_ERR_HIP if the array's address cannot be obtained. */
-#define KDN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+#define KDN_NOALLOC_SCRATCH_BYTES ((size_t)320 << 20)
 size_t kdn_noalloc_scratch_bytes(void);
 kdn_status kdn_forward_noalloc(const kdn_desc *d, const void *q, const void *k, const void *v,
                                const void *a, const void *qnoise, const void *r,

@@ -94,7 +94,7 @@ ForwardWs forward_ws(const kdn_desc* d) {
     }
     const size_t segs = w.nseg > 1 ? (size_t)s.BH * w.nseg : 0;
     w.agg = 0;
-    w.lam_chunk = w.agg + round_up((size_t)s.BH * s.nc * nl * 16);
+    w.lam_chunk = w.agg + round_up((size_t)s.BH * s.nc * kdn::agg_subs(s) * nl * 16);
     w.w = w.lam_chunk + round_up((size_t)s.BH * (s.nc + 1) * nl * 4);
     w.tm = w.w + round_up((size_t)s.BH * s.T * s.dk * esize(d->qkv_dtype));
     w.g = w.tm + round_up((size_t)s.BH * s.nc * s.chunk * s.chunk * esize(d->qkv_dtype));
@@ -149,7 +149,7 @@ PackedWs packed_ws(const kdn_desc* d) {
     w.cu = 0;
     w.cc = round_up((N + 1) * 4);
     w.agg = w.cc + round_up((N + 1) * 4);
-    w.lam_chunk = w.agg + round_up(H * ncb * nl * 16);
+    w.lam_chunk = w.agg + round_up(H * ncb * kdn::agg_subs(s) * nl * 16);
     w.w = w.lam_chunk + round_up(H * (ncb + N) * nl * 4);
     w.tm = w.w + round_up(H * s.T * s.dk * esize(d->qkv_dtype));
     w.g = w.tm + round_up(H * ncb * s.chunk * s.chunk * esize(d->qkv_dtype));
@@ -239,7 +239,8 @@ kdn_status kdn_forward_events(const kdn_desc* d, const void* q, const void* k, c
     kdn::Shape sw = s;
     sw.gain_bf16 = s.qkv_bf16;
     timed(2);
-    if (e == hipSuccess) e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, g, hs);
+    if (e == hipSuccess)
+        e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, agg, wk, tm, g, hs);
     kdn::SegWs seg;
     seg.nseg = w.nseg;
     seg.Lc = w.Lc;
@@ -330,7 +331,7 @@ kdn_status backward_impl(const kdn_desc* d, const void* q, const void* k, const 
         sw.gain_bf16 = s.qkv_bf16;
         timed(2);
         if (e == hipSuccess)
-            e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, g, hs, dinv);
+            e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, agg, wk, tm, g, hs, dinv);
         timed(3);
         if (e == hipSuccess)
             e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs, at(ws, w.Sc));
@@ -481,7 +482,7 @@ kdn_status kdn_chunk_delta(const kdn_desc* d, const void* q, const void* k, cons
     void* wk = const_cast<void*>(w);  // read only when fuse_gain is false
     float* g = reinterpret_cast<float*>(at(ws, fw.g - fw.tm));
     hipError_t e =
-        kdn::launch_chunk_prep(s, false, k, a, nullptr, nullptr, nullptr, wk, ws, g, hs);
+        kdn::launch_chunk_prep(s, false, k, a, nullptr, nullptr, nullptr, nullptr, wk, ws, g, hs);
     if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, g, w, ws, S0, o, S_T, hs);
     return hip_status(e);
 }
@@ -566,7 +567,7 @@ kdn_status kdn_forward_varlen(const kdn_desc* d, const int32_t* cu_seqlens, int3
     kdn::Shape sw = s;
     sw.gain_bf16 = s.qkv_bf16;
     if (e == hipSuccess && s.nc > 0)
-        e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, wk, tm, g, hs);
+        e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, agg, wk, tm, g, hs);
     if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs);
     return hip_status(e);
 }

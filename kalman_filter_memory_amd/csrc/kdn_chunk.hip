@@ -97,9 +97,8 @@ __device__ __forceinline__ void store_ct(float* dst, floatx4 v, int lane) {
 // LDS of the prep kernel: two regions reused as the chunk proceeds.
 //   region 1: K [C][LDK] (input dtype), then A with the diagonal blocks of T
 //             [C][LDA] (fp32)
-//   region 2: the sub-block Moebius maps of the gain pass, then W [C][LDK]
-//             (input dtype), then the off-diagonal blocks of T and the
-//             per-wave scratch of the solve (fp32)
+//   region 2: W [C][LDK] (input dtype), then the off-diagonal blocks of T
+//             and the per-wave scratch of the solve (fp32)
 template <typename E, int DK, int C> struct PrepLds {
     // rows padded by 32 bytes (a stride of 8 mod 16 dwords: conflict-free MFMA
     // fragment reads)
@@ -111,8 +110,7 @@ template <typename E, int DK, int C> struct PrepLds {
     // region 2 also holds the off-diagonal blocks of T and one 16x16 fp32
     // scratch block per wave while T is formed
     static constexpr int R2 =
-        cmax(cmax(C * LDK * (int)sizeof(E), (NT * (NT - 1) / 2 + NT + 4) * kBlk * 4),
-             (NT > 1 ? NT - 1 : 1) * DK * 16);
+        cmax(C * LDK * (int)sizeof(E), (NT * (NT - 1) / 2 + NT + 4) * kBlk * 4);
     static constexpr int BYTES = R1 + R2 + 2 * C * (int)sizeof(float);
     // 16-byte pieces of one chunk's K per thread
     static constexpr int NV = C * DK / Vec16<E>::N;
@@ -122,12 +120,12 @@ template <typename E, int DK, int C> struct PrepLds {
 // ------------------------------------------------------------ prep kernel
 // One workgroup (4 waves) per chunk.
 //   gain (fuse_gain), diagonal: wave w takes the 16-token sub-block w and each
-//     lane NPL key dimensions.  (1) Each wave composes the Moebius maps of its
-//     sub-block; (2) wave w carries the chunk-boundary precision through the
-//     maps of sub-blocks 0..w-1 to its own start; (3) it walks its 16 tokens
-//     (predictive precision, P^- k); (4) the per-token sums k^T P^- k come from a
+//     lane NPL key dimensions.  (1) Wave w > 0 carries the chunk-boundary
+//     precision through the scan's prefix product of the chunk's first 16 w
+//     tokens to its own start; (2) it walks its 16 tokens (predictive
+//     precision, P^- k); (3) the per-token sums k^T P^- k come from a
 //     transposing butterfly inside 16-lane groups and two cross-group
-//     exchanges; (5) w = P^- k / (k^T P^- k + r) is written by rows.
+//     exchanges; (4) w = P^- k / (k^T P^- k + r) is written by rows.
 //     Isotropic: |k|^2 per token, one scalar chain, w = k / (|k|^2 + r lambda^-).
 //   A = strict_tril(K W^T * Gamma) on MFMA and T = (I + A)^{-1} in fp32:
 //     16x16 diagonal blocks in place by forward substitution (one lane per
@@ -136,21 +134,23 @@ template <typename E, int DK, int C> struct PrepLds {
 
 // One chunk's inputs, loaded into registers ahead of their use: K rows, the
 // gates of token `lane` (in their storage type G, widened only when used, so
-// that no wait for the load is forced early) and the chunk-boundary precision
-// of the lane's key dimensions.  Rows past the end of the sequence load the
-// last valid row and are zeroed when staged.
+// that no wait for the load is forced early), the chunk-boundary precision of
+// the lane's key dimensions and (diagonal, waves past the first) the scan's
+// prefix product of the tokens before the wave's sub-block.  Rows past the end
+// of the sequence load the last valid row and are zeroed when staged.
 template <typename E, typename G, int DK, int C> struct PrepIn {
     u32x4 k[PrepLds<E, DK, C>::IT];
     G a, nu, r;
     float lam[PrepLds<E, DK, C>::NPL];
+    float4 pre[PrepLds<E, DK, C>::NPL];
 };
 
 template <typename E, typename G, int DK, int C, bool FUSE>
 __device__ __forceinline__ void prep_fetch(const E* __restrict__ k, const G* __restrict__ a,
                                            const G* __restrict__ nu, const G* __restrict__ r,
                                            bool diag, const float* __restrict__ lam_chunk,
-                                           const Slab& sl, int c, int tid,
-                                           PrepIn<E, G, DK, C>& in) {
+                                           const float4* __restrict__ agg, const Slab& sl,
+                                           int c, int tid, PrepIn<E, G, DK, C>& in) {
     using L = PrepLds<E, DK, C>;
     constexpr int V = Vec16<E>::N, VPR = DK / V, NPL = L::NPL;
     const int lane = tid & 63, wave = wave_id();
@@ -169,7 +169,10 @@ __device__ __forceinline__ void prep_fetch(const E* __restrict__ k, const G* __r
     in.nu = from_f<G>(0.f);
     in.r = from_f<G>(1.f);
 #pragma unroll
-    for (int d = 0; d < NPL; ++d) in.lam[d] = 1.f;
+    for (int d = 0; d < NPL; ++d) {
+        in.lam[d] = 1.f;
+        in.pre[d] = make_float4(1.f, 0.f, 0.f, 1.f);
+    }
     if constexpr (FUSE) {
         in.nu = nu[tok];
         in.r = r[tok];
@@ -179,6 +182,11 @@ __device__ __forceinline__ void prep_fetch(const E* __restrict__ k, const G* __r
 #pragma unroll
                 for (int d = 0; d < NPL; ++d)
                     in.lam[d] = lam_chunk[(sl.l0 + c) * DK + i0 + d];
+                if (wave > 0) {
+#pragma unroll
+                    for (int d = 0; d < NPL; ++d)
+                        in.pre[d] = agg[((sl.c0 + c) * L::NT + wave - 1) * DK + i0 + d];
+                }
             }
         } else if (wave == 0) {
             in.lam[0] = lam_chunk[sl.l0 + c];
@@ -241,48 +249,23 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
         if (diag) {
             const int i0 = lane * NPL, tb0 = 16 * wave;
             const bool act = wave < NT && i0 < DK;
-            float4* sprod = reinterpret_cast<float4*>(smem + L::R1);  // [NT-1][DK] maps
             float kc[16][NPL];
-            M2 m[NPL];
             if (act) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) load_dims<E, NPL>(sK + (tb0 + j) * LDK + i0, kc[j]);
             }
-            if (act && wave < NT - 1) {
-                // (1) the sub-block's 16 token maps composed, renormalised every 8 (the
-                // last sub-block's product is not needed)
-#pragma unroll
-                for (int d = 0; d < NPL; ++d) m[d] = M2{1.f, 0.f, 0.f, 1.f};
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const float4 gv = sgt[tb0 + j];
-                    const float a2 = gv.x, nut = gv.y, ir = gv.z;
-#pragma unroll
-                    for (int d = 0; d < NPL; ++d) {
-                        m[d] = mob_step(m[d], kc[j][d] * kc[j][d] * ir, a2, nut);
-                        if ((j & 7) == 7) m[d] = mob_renorm(m[d]);
-                    }
-                }
-#pragma unroll
-                for (int d = 0; d < NPL; ++d)
-                    sprod[wave * DK + i0 + d] = make_float4(m[d].a, m[d].b, m[d].c, m[d].d);
-            }
-            sync_lds();
             float pk[16][NPL];
             float den = 0.f;
             if (act) {
-                // (2) precision at the sub-block start
+                // (1) precision at the sub-block start: the chunk-boundary value
+                // through the scan's prefix product of the tokens before it
                 float lam[NPL];
 #pragma unroll
-                for (int d = 0; d < NPL; ++d) lam[d] = in.lam[d];
-                for (int sb = 0; sb < wave; ++sb) {
-#pragma unroll
-                    for (int d = 0; d < NPL; ++d) {
-                        const float4 q4 = sprod[sb * DK + i0 + d];
-                        lam[d] = fmaf(q4.x, lam[d], q4.y) * rcp(fmaf(q4.z, lam[d], q4.w));
-                    }
+                for (int d = 0; d < NPL; ++d) {
+                    const float4 p = in.pre[d];  // the identity on wave 0
+                    lam[d] = fmaf(p.x, in.lam[d], p.y) * rcp(fmaf(p.z, in.lam[d], p.w));
                 }
-                // (3) walk in variance form, P = 1 / lambda: P^- = a^2 P + nu, then
+                // (2) walk in variance form, P = 1 / lambda: P^- = a^2 P + nu, then
                 // P = P^- / (1 + b P^-) (one reciprocal per token); P^- k per token
                 float pv[NPL];
 #pragma unroll
@@ -302,7 +285,7 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
                         pv[d] = pm * rcp(fmaf(pm, kv * kv * ir, 1.f));
                     }
                 }
-                // (4) k^T P^- k of token tb0 + (lane % 16), summed over all lanes
+                // (3) k^T P^- k of token tb0 + (lane % 16), summed over all lanes
                 den = transpose_sum16(v, lane);
             }
             den += __shfl_xor(den, 16, kWave);
@@ -311,11 +294,10 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
             // with every lane active (with d_k < 64 the lanes past d_k are off
             // inside the branch below, and a shuffle reads nothing from them)
             const float rt = __shfl(gr, tb0 + (lane & 15), kWave);
-            sync_lds();  // W overwrites the sub-block maps
             if (act) {
                 const float rden = 1.f / (den + rt);
                 if (dinv && lane < 16 && tb0 + lane < n) dinv[row0 + tb0 + lane] = rden;
-                // (5) w rows
+                // (4) w rows
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const float rd = lane_value(rden, j);
@@ -512,9 +494,9 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
 template <typename E, typename G, int DK, int C, bool FUSE, bool VL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void prep_kernel(
     const E* __restrict__ k, const G* __restrict__ a, const G* __restrict__ nu,
-    const G* __restrict__ r, bool diag, const float* __restrict__ lam_chunk, E* __restrict__ w,
-    E* __restrict__ Tm, float* __restrict__ gout, float* __restrict__ dinv, int T, int NC,
-    Packed pk) {
+    const G* __restrict__ r, bool diag, const float* __restrict__ lam_chunk,
+    const float4* __restrict__ agg, E* __restrict__ w, E* __restrict__ Tm,
+    float* __restrict__ gout, float* __restrict__ dinv, int T, int NC, Packed pk) {
     using L = PrepLds<E, DK, C>;
     __shared__ __align__(16) unsigned char smem[L::R1 + L::R2];
     __shared__ __align__(16) float sden[C];
@@ -525,8 +507,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int c0 = 2 * blockIdx.x, c1 = c0 + 1;
     if (VL && c0 >= sl.nc) return;
     PrepIn<E, G, DK, C> in0, in1;
-    prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, sl, c0, tid, in0);
-    prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, sl, min(c1, sl.nc - 1), tid, in1);
+    prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, agg, sl, c0, tid, in0);
+    prep_fetch<E, G, DK, C, FUSE>(k, a, nu, r, diag, lam_chunk, agg, sl, min(c1, sl.nc - 1), tid,
+                                  in1);
     prep_chunk<E, G, DK, C, FUSE>(w, diag, w, Tm, gout, dinv, sl, c0, in0, smem, sden, sg, sgt);
     if (c1 < sl.nc) {
         sync_lds();  // the second chunk's staging overwrites K / A / T
@@ -1022,19 +1005,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 // Start states of the segments: S_{g+1} = S_g A_g + B_g for g = 1 .. nseg - 2,
 // in order.  On entry Sseg[1] holds the true end state of segment 0 and
 // Sseg[g + 1] (g >= 1) the end state B_g of segment g from a zero start;
-// Aseg[g] holds A_g (d_k x d_k).  One workgroup per (kCombRows rows of S,
-// head), fp32 throughout.  A_g sits in LDS, and A_{g+1} is loaded into the
-// other LDS buffer (through registers, every load issued at once) while step g
-// computes, so each step waits for global memory at most once.
-constexpr int kCombRows = 8, kCombThreads = 256;
+// Aseg[g] holds A_g (d_k x d_k).  One workgroup of 8 waves per (kCombRows rows
+// of S, head), fp32 throughout.  A_g sits in LDS; A_{g+1} and the rows of
+// B_{g+1} are loaded (every load issued at once) while step g computes, so the
+// steps do not wait for global memory.
+constexpr int kCombThreads = 512;
+template <int DK> constexpr int comb_rows() { return DK >= 64 ? 8 : kCombThreads / DK; }
 
 template <int DK>
 __global__ __launch_bounds__(kCombThreads) void seg_combine_kernel(float* __restrict__ Sseg,
                                                                   const float* __restrict__ Aseg,
                                                                   int DV, int nseg) {
-    constexpr int R = kCombRows, RG = kCombThreads / DK, RPT = R / RG;  // rows per thread
-    constexpr int NV = DK * DK / 4 / kCombThreads;  // float4 pieces of A per thread
-    static_assert(RPT * RG == R && NV * 4 * kCombThreads == DK * DK, "combine tiling");
+    constexpr int R = comb_rows<DK>(), RG = kCombThreads / DK, RPT = R / RG;  // rows per thread
+    constexpr int NA = DK * DK / 4;                             // float4 pieces of A
+    constexpr int NV = (NA + kCombThreads - 1) / kCombThreads;  // ... per thread
+    static_assert(RPT * RG == R && RPT >= 1, "combine tiling");
     __shared__ __align__(16) float sA[2][DK * DK];
     __shared__ __align__(16) float sS[R][DK];
     const int tid = threadIdx.x, i = tid % DK, rg = tid / DK;
@@ -1042,29 +1027,36 @@ __global__ __launch_bounds__(kCombThreads) void seg_combine_kernel(float* __rest
     const int j0 = blockIdx.x * R;
     float* base = Sseg + bh * (size_t)nseg * DV * DK;
     const float* abase = Aseg + bh * (size_t)nseg * DK * DK;
-    float4 pre[NV];
-    auto fetch = [&](int g) {
+    float4 preA[NV];
+    float preB[RPT];
+    auto fetch = [&](int g) {  // A_g and the rows of B_g (held in Sseg[g + 1])
         const float4* src = reinterpret_cast<const float4*>(abase + (size_t)g * DK * DK);
 #pragma unroll
-        for (int x = 0; x < NV; ++x) pre[x] = src[tid + kCombThreads * x];
+        for (int x = 0; x < NV; ++x)
+            if (NA % kCombThreads == 0 || tid + kCombThreads * x < NA)
+                preA[x] = src[tid + kCombThreads * x];
+        const float* bsrc = base + ((size_t)(g + 1) * DV + j0) * DK;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) preB[r] = bsrc[(size_t)(rg * RPT + r) * DK + i];
     };
     auto stage = [&](int buf) {
 #pragma unroll
         for (int x = 0; x < NV; ++x)
-            reinterpret_cast<float4*>(sA[buf])[tid + kCombThreads * x] = pre[x];
+            if (NA % kCombThreads == 0 || tid + kCombThreads * x < NA)
+                reinterpret_cast<float4*>(sA[buf])[tid + kCombThreads * x] = preA[x];
     };
     fetch(1);
     for (int e = tid; e < R * DK; e += kCombThreads)
         sS[e / DK][e % DK] = base[((size_t)1 * DV + j0 + e / DK) * DK + e % DK];
-    stage(1 & 1);
+    stage(1);
     __syncthreads();
     for (int g = 1; g + 1 < nseg; ++g) {
+        float acc[RPT];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) acc[r] = preB[r];
         if (g + 2 < nseg) fetch(g + 1);  // in flight during this step
         float* out = base + ((size_t)(g + 1) * DV + j0) * DK;
         const float* A = sA[g & 1];
-        float acc[RPT];
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) acc[r] = out[(size_t)(rg * RPT + r) * DK + i];
 #pragma unroll 4
         for (int m = 0; m < DK; m += 4) {
             const float a0 = A[(m + 0) * DK + i], a1 = A[(m + 1) * DK + i];
@@ -1121,14 +1113,15 @@ int dv_tile(const Shape& s) {
 
 template <typename E, typename G, int DK, int C>
 hipError_t prep_t(const Shape& s, bool fuse, const void* k, const void* a, const void* nu,
-                  const void* r, const float* lc, void* w, void* Tm, float* g, float* dinv,
-                  hipStream_t st) {
+                  const void* r, const float* lc, const float* agg, void* w, void* Tm, float* g,
+                  float* dinv, hipStream_t st) {
     static_assert(PrepLds<E, DK, C>::BYTES <= kLdsLimit, "prep LDS");
     const dim3 grid((s.nc + 1) / 2, s.BH);
 #define KDN_PREP_L(FUSE_, VL_)                                                                \
     launch_k((prep_kernel<E, G, DK, C, FUSE_, VL_>), grid, dim3(kThreads), 0, st,            \
              static_cast<const E*>(k), static_cast<const G*>(a), static_cast<const G*>(nu),  \
-             static_cast<const G*>(r), s.diag, lc, static_cast<E*>(w), static_cast<E*>(Tm), g, \
+             static_cast<const G*>(r), s.diag, lc, reinterpret_cast<const float4*>(agg),         \
+             static_cast<E*>(w), static_cast<E*>(Tm), g,                                         \
              dinv, s.T, s.nc, s.pk)
     if (s.varlen) {
         if (!fuse) return hipErrorInvalidValue;  // packed batches: the forward only
@@ -1180,7 +1173,7 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             if (sw->nseg > 2) {
-                launch_k(seg_combine_kernel<DK>, dim3(s.dv / kCombRows, s.BH), dim3(kCombThreads), 0, st,
+                launch_k(seg_combine_kernel<DK>, dim3(s.dv / comb_rows<DK>(), s.BH), dim3(kCombThreads), 0, st,
                          sw->Sseg, static_cast<const float*>(sw->Aseg), s.dv, sw->nseg);
                 e = hipGetLastError();
                 if (e != hipSuccess) return e;
@@ -1199,13 +1192,13 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
 
 template <typename E>
 hipError_t prep_e(const Shape& s, bool fuse, const void* k, const void* a, const void* nu,
-                  const void* r, const float* lc, void* w, void* Tm, float* g, float* dinv,
-                  hipStream_t st) {
+                  const void* r, const float* lc, const float* agg, void* w, void* Tm, float* g,
+                  float* dinv, hipStream_t st) {
 #define KDN_PREP(DK_, C_)                                                                   \
     if (s.dk == DK_ && s.chunk == C_)                                                       \
         return s.gate_bf16                                                                  \
-                   ? prep_t<E, bf16_t, DK_, C_>(s, fuse, k, a, nu, r, lc, w, Tm, g, dinv, st) \
-                   : prep_t<E, float, DK_, C_>(s, fuse, k, a, nu, r, lc, w, Tm, g, dinv, st);
+                   ? prep_t<E, bf16_t, DK_, C_>(s, fuse, k, a, nu, r, lc, agg, w, Tm, g, dinv, st) \
+                   : prep_t<E, float, DK_, C_>(s, fuse, k, a, nu, r, lc, agg, w, Tm, g, dinv, st);
 #define KDN_PREP_C(DK_) KDN_PREP(DK_, 16) KDN_PREP(DK_, 32) KDN_PREP(DK_, 64)
     KDN_PREP_C(32) KDN_PREP_C(64) KDN_PREP_C(128)
 #undef KDN_PREP_C
@@ -1239,11 +1232,14 @@ bool chunk_supported(const Shape& s) {
 }
 
 hipError_t launch_chunk_prep(const Shape& s, bool fuse_gain, const void* k, const void* a,
-                             const void* nu, const void* r, const float* lam_chunk, void* w,
-                             void* Tm, float* g, hipStream_t st, float* dinv) {
+                             const void* nu, const void* r, const float* lam_chunk,
+                             const float* agg, void* w, void* Tm, float* g, hipStream_t st,
+                             float* dinv) {
     if (s.BH == 0 || s.nc == 0) return hipSuccess;
-    return s.qkv_bf16 ? prep_e<bf16_t>(s, fuse_gain, k, a, nu, r, lam_chunk, w, Tm, g, dinv, st)
-                      : prep_e<float>(s, fuse_gain, k, a, nu, r, lam_chunk, w, Tm, g, dinv, st);
+    if (fuse_gain && s.diag && !agg) return hipErrorInvalidValue;
+    return s.qkv_bf16
+               ? prep_e<bf16_t>(s, fuse_gain, k, a, nu, r, lam_chunk, agg, w, Tm, g, dinv, st)
+               : prep_e<float>(s, fuse_gain, k, a, nu, r, lam_chunk, agg, w, Tm, g, dinv, st);
 }
 
 hipError_t launch_chunk_state(const Shape& s, const void* q, const void* k, const void* v,

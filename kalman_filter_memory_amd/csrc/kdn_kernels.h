@@ -43,8 +43,17 @@ struct Shape {
 // Each launcher returns hipSuccess or the launch error.  Pointers are device
 // pointers with the layouts documented in include/kdn.h.
 
-// Moebius scan, pass 1: per-chunk product of the 2x2 token matrices.
-// agg: [BH][nc][nl] float4 (nl = dk for diagonal, 1 for isotropic).
+// Moebius products the scan keeps per (chunk, precision): for the diagonal
+// variant the prefix products of the chunk's tokens after every 16 tokens
+// (16, 32, ..., the last one being the chunk's product), which the prep pass
+// starts its 16-token sub-blocks from; for the isotropic variant the chunk's
+// product alone.
+inline int agg_subs(const Shape& s) { return s.diag ? s.chunk / 16 : 1; }
+
+// Moebius scan, pass 1: per-chunk products of the 2x2 token matrices.
+// agg: [BH][nc][agg_subs][nl] float4 (nl = dk for diagonal, 1 for isotropic);
+// entry s of a chunk is the product of its first 16 (s + 1) tokens (later
+// tokens on the left), the last entry the chunk's whole product.
 hipError_t launch_scan_reduce(const Shape& s, const void* k, const void* a, const void* nu,
                               const void* r, float* agg, hipStream_t st);
 // Offsets of a packed batch (cu_in: the caller's N + 1 sequence offsets):
@@ -69,9 +78,13 @@ hipError_t launch_gain(const Shape& s, const void* k, const void* r, const float
 // decay g [BH][nc][chunk] (float32).  fuse_gain = false reads w instead.
 // dinv (diagonal, fused gain; may be NULL): 1 / (k^T P^- k + r) per token
 // [BH][T] (float32), kept for the backward pass.
+// agg (the scan's products; may be NULL without the fused gain): each
+// 16-token sub-block of a diagonal chunk starts from the chunk-boundary
+// precision carried through the prefix product before it.
 hipError_t launch_chunk_prep(const Shape& s, bool fuse_gain, const void* k, const void* a,
-                             const void* nu, const void* r, const float* lam_chunk, void* w,
-                             void* Tm, float* g, hipStream_t st, float* dinv = nullptr);
+                             const void* nu, const void* r, const float* lam_chunk,
+                             const float* agg, void* w, void* Tm, float* g, hipStream_t st,
+                             float* dinv = nullptr);
 // Workspace of a state pass over sequence segments: nseg segments of Lc
 // chunks per head (state_segments), the start state of every segment
 // Sseg [BH][nseg][dv][dk] and the linear part of every segment's affine map

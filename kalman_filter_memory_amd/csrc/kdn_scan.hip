@@ -112,7 +112,10 @@ template <> struct GateRaw<float> {
 
 // A chunk of 64 tokens is split over two waves of a workgroup (32 keys in
 // registers each, eight waves per SIMD); the second wave multiplies the first
-// one's product in through LDS.
+// one's product in through LDS.  Besides the chunk's product the kernel stores
+// the prefix products after every 16 tokens (agg_subs per chunk): a wave
+// records its running product at its 16th token, and the second wave of a
+// chunk multiplies the first wave's product into that one too.
 template <int C> struct RedSplit {
     static constexpr int SPLIT = C >= 64 ? 2 : 1;       // waves per chunk
     static constexpr int TPW = C / SPLIT;               // tokens per wave
@@ -167,7 +170,15 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
         if (lane < TPW) sgate[wave][lane] = g;
     }
     __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in order
-    M2 P[L::IPL];
+    constexpr int NS = C / 16;  // products kept per (chunk, dim)
+    float4* dst = agg + (size_t)(sl.c0 + c) * NS * DK + lane * L::IPL;
+    auto put = [&](int s_, int j, const M2& m) {
+        if (act && live) {
+            const M2 q = mob_renorm(m);
+            dst[(size_t)s_ * DK + j] = make_float4(q.a, q.b, q.c, q.d);
+        }
+    };
+    M2 P[L::IPL], mid[L::IPL];
 #pragma unroll
     for (int j = 0; j < L::IPL; ++j) P[j] = {1.f, 0.f, 0.f, 1.f};
 #pragma unroll
@@ -180,13 +191,22 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
         if ((t & 7) == 7)
 #pragma unroll
             for (int j = 0; j < L::IPL; ++j) P[j] = mob_renorm(P[j]);
+        if (t == 15 && TPW > 16)  // the wave's first 16 tokens
+#pragma unroll
+            for (int j = 0; j < L::IPL; ++j) mid[j] = P[j];
     }
+    // the prefix after the first 16 tokens of the chunk (wave 0 of a chunk)
+    if (part == 0 && TPW > 16)
+#pragma unroll
+        for (int j = 0; j < L::IPL; ++j) put(0, j, mid[j]);
     if constexpr (RS::SPLIT > 1) {
         static_assert(RS::SPLIT == 2, "two waves per chunk");
         if (part == 0 && act) {
 #pragma unroll
-            for (int j = 0; j < L::IPL; ++j)
+            for (int j = 0; j < L::IPL; ++j) {
                 spart[cb][lane * L::IPL + j] = make_float4(P[j].a, P[j].b, P[j].c, P[j].d);
+                put(1, j, P[j]);  // the prefix after 32 tokens
+            }
         }
         __syncthreads();
         if (part == 0) return;
@@ -194,16 +214,15 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
 #pragma unroll
             for (int j = 0; j < L::IPL; ++j) {
                 const float4 f = spart[cb][lane * L::IPL + j];
-                P[j] = mob_mul(P[j], M2{f.x, f.y, f.z, f.w});
+                const M2 first = {f.x, f.y, f.z, f.w};
+                put(2, j, mob_mul(mid[j], first));  // the prefix after 48 tokens
+                P[j] = mob_mul(P[j], first);
             }
         }
     }
-    if (act && live) {
+    {
 #pragma unroll
-        for (int j = 0; j < L::IPL; ++j) {
-            const M2 m = mob_renorm(P[j]);
-            agg[(sl.c0 + c) * DK + lane * L::IPL + j] = make_float4(m.a, m.b, m.c, m.d);
-        }
+        for (int j = 0; j < L::IPL; ++j) put(NS - 1, j, P[j]);  // the chunk's product
     }
 }
 
@@ -282,10 +301,11 @@ __device__ __forceinline__ float mob_apply_fast(const float4& m, float x) {
     return fmaf(m.x, x, m.y) * __builtin_amdgcn_rcpf(fmaf(m.z, x, m.w));
 }
 
+// agg holds NS products per (chunk, scan), the chunk's own product last.
 template <int SEG, bool ONE_GROUP, bool VL>
 __global__ __launch_bounds__(kWave) void carry_kernel(const float4* __restrict__ agg,
                                                       const float* __restrict__ lambda0, int BH,
-                                                      int NL, int T, int NC_all,
+                                                      int NL, int NS, int T, int NC_all,
                                                       float* __restrict__ lam_chunk,
                                                       float* __restrict__ lambda_T, Packed pk) {
     constexpr int SC = kWave / SEG;  // scans per wave
@@ -297,10 +317,10 @@ __global__ __launch_bounds__(kWave) void carry_kernel(const float4* __restrict__
     const size_t bh = id / NL, i = id % NL;
     const Slab sb = slab_of<VL>(bh, T, NC_all, pk);
     const int NC = sb.nc;
-    const float4* src = agg + sb.c0 * NL + i;
+    const float4* src = agg + (sb.c0 * NS + NS - 1) * NL + i;
     const int SL = (NC + SEG - 1) / SEG;
     const int c0 = min(seg * SL, NC), c1 = min(c0 + SL, NC);  // this lane's chunks [c0, c1)
-    auto map_at = [&](int c) { return src[(size_t)min(c, NC - 1) * NL]; };
+    auto map_at = [&](int c) { return src[(size_t)min(c, NC - 1) * NS * NL]; };
 
     // (1) the segment's product, later chunks on the left
     float4 buf[kCarryGroup];
@@ -345,6 +365,77 @@ __global__ __launch_bounds__(kWave) void carry_kernel(const float4* __restrict__
         if (ONE_GROUP) break;
     }
     if (seg == SEG - 1 && valid) {  // the last segment ends at chunk NC
+        if (out) out[(size_t)NC * NL] = lam;
+        if (lambda_T) lambda_T[id] = lam;
+    }
+}
+
+// The carry of a diagonal head over many chunks: one workgroup of
+// kWideWaves waves takes 16 neighbouring key dimensions of one head; lane l
+// holds dimension l % 16 of segment 4 w + l / 16 (w the wave), so the head's
+// chunks are cut into 4 kWideWaves segments and every load and store of a wave
+// covers 16 neighbouring dimensions (64 contiguous bytes per segment).  The
+// segment products are scanned inside a wave (2 steps over its 4 segments) and
+// across the waves through LDS (each wave composes the totals of the waves
+// before it), then each lane walks its segment.
+constexpr int kWideWaves = 16, kWideSeg = 4 * kWideWaves;
+
+__global__ __launch_bounds__(kWave * kWideWaves) void carry_wide_kernel(
+    const float4* __restrict__ agg, const float* __restrict__ lambda0, int NL, int NS, int NC,
+    float* __restrict__ lam_chunk, float* __restrict__ lambda_T) {
+    __shared__ float4 tot[kWideWaves][16];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int sl = lane & 15, seg = wave * 4 + (lane >> 4);
+    const size_t id = blockIdx.x * (size_t)16 + sl;  // bh * NL + i (NL a multiple of 16)
+    const size_t bh = id / NL, i = id % NL;
+    const float4* src = agg + (bh * (size_t)NC * NS + NS - 1) * NL + i;
+    const int SL = (NC + kWideSeg - 1) / kWideSeg;
+    const int c0 = min(seg * SL, NC), c1 = min(c0 + SL, NC);
+    auto map_at = [&](int c) { return src[(size_t)min(c, NC - 1) * NS * NL]; };
+
+    // (1) the segment's product, later chunks on the left
+    float4 buf[kCarryGroup];
+    M2 P = {1.f, 0.f, 0.f, 1.f};
+    for (int g = c0; g < c1; g += kCarryGroup) {
+#pragma unroll
+        for (int u = 0; u < kCarryGroup; ++u) buf[u] = map_at(g + u);
+#pragma unroll
+        for (int u = 0; u < kCarryGroup; ++u) {
+            if (g + u < c1) P = mob_mul(as_m2(buf[u]), P);
+            if ((u & 7) == 7) P = mob_renorm(P);
+        }
+    }
+    P = mob_renorm(P);
+    // (2) inclusive scan over the wave's four segments, the wave's total to LDS
+#pragma unroll
+    for (int off = 16; off < kWave; off <<= 1) {
+        const M2 q = shfl_up_m2(P, off);
+        if (lane >= off) P = mob_renorm(mob_mul(P, q));
+    }
+    if (lane >= 48) tot[wave][sl] = make_float4(P.a, P.b, P.c, P.d);
+    M2 E = shfl_up_m2(P, 16);  // the segments before this lane's within the wave
+    if (lane < 16) E = M2{1.f, 0.f, 0.f, 1.f};
+    __syncthreads();
+    // (3) the totals of the waves before this one, later waves on the left
+    M2 W = {1.f, 0.f, 0.f, 1.f};
+    for (int w = 0; w < wave; ++w) W = mob_renorm(mob_mul(as_m2(tot[w][sl]), W));
+    E = mob_renorm(mob_mul(E, W));
+    float lam = lambda0 ? lambda0[id] : 1.f;
+    lam = mob_apply_fast(make_float4(E.a, E.b, E.c, E.d), lam);
+    // (4) walk the segment
+    float* out = lam_chunk ? lam_chunk + bh * (size_t)(NC + 1) * NL + i : nullptr;
+    for (int g = c0; g < c1; g += kCarryGroup) {
+#pragma unroll
+        for (int u = 0; u < kCarryGroup; ++u) buf[u] = map_at(g + u);
+#pragma unroll
+        for (int u = 0; u < kCarryGroup; ++u) {
+            if (g + u < c1) {
+                if (out) out[(size_t)(g + u) * NL] = lam;
+                lam = mob_apply_fast(buf[u], lam);
+            }
+        }
+    }
+    if (seg == kWideSeg - 1) {  // the last segment ends at chunk NC
         if (out) out[(size_t)NC * NL] = lam;
         if (lambda_T) lambda_T[id] = lam;
     }
@@ -576,6 +667,13 @@ hipError_t launch_scan_carry(const Shape& s, const float* agg, const float* lamb
     const int NL = s.diag ? s.dk : 1;
     const size_t n = (size_t)s.BH * NL;
     if (n == 0) return hipSuccess;
+    // many chunks and at least 16 key dimensions per head: the wide carry
+    if (!s.varlen && NL % 16 == 0 && s.nc > 4 * kCarryGroup) {
+        launch_k(carry_wide_kernel, dim3((unsigned)(n / 16)), dim3(kWave * kWideWaves), 0, st,
+                 reinterpret_cast<const float4*>(agg), lambda0, NL, agg_subs(s), s.nc, lam_chunk,
+                 lambda_T);
+        return hipGetLastError();
+    }
     // segments per scan: about 16 chunks each, 4 to 64
     int seg = 4;
     while (seg < 64 && seg * kCarryGroup < s.nc) seg *= 2;
@@ -583,7 +681,8 @@ hipError_t launch_scan_carry(const Shape& s, const float* agg, const float* lamb
     const float4* a4 = reinterpret_cast<const float4*>(agg);
 #define KDN_CARRY_L(SEG_, ONE_, VL_)                                                           \
     launch_k(carry_kernel<SEG_, ONE_, VL_>, dim3((unsigned)((n + kWave / SEG_ - 1) / (kWave / SEG_))), \
-             dim3(kWave), 0, st, a4, lambda0, s.BH, NL, s.T, s.nc, lam_chunk, lambda_T, s.pk)
+             dim3(kWave), 0, st, a4, lambda0, s.BH, NL, agg_subs(s), s.T, s.nc, lam_chunk, lambda_T, \
+             s.pk)
 #define KDN_CARRY_S(SEG_)                                                                      \
     if (seg == SEG_) {                                                                         \
         if (s.varlen) {                                                                        \

@@ -307,22 +307,29 @@ __device__ __forceinline__ void state_write(const StateAcc<E, DK, DVT, C>& accS,
 }
 
 // v[j] summed over the 16 lanes of each 16-lane group: on return lane l holds
-// in v[0] the group total of v[l % 16] (15 exchanges instead of 16 reductions)
-template <int H>
+// in v[0] the group total of v[l % 16] (15 exchanges instead of 16 reductions).
+// Step H pairs every lane with one whose bit H differs and whose higher bits
+// agree: the lane keeps the half of its values selected by its own bit H and
+// adds the partner's copy of that half.  Lane l therefore ends with index
+// l % 16 whatever the pairing, so each step uses the DPP move that pairs such
+// lanes within the row of 16: row_mirror (l <-> 15 - l) for bit 3,
+// row_half_mirror (l <-> 7 - l in each 8) for bit 2, quad permutes (xor 2,
+// xor 1) for bits 1 and 0 -- one VALU move each, no LDS traffic.
+template <int H, int CTRL>
 __device__ __forceinline__ void transpose_sum_step(float (&v)[16], int lane) {
     const bool upper = (lane & H) != 0;
 #pragma unroll
     for (int j = 0; j < H; ++j) {
         const float keep = upper ? v[j + H] : v[j];
         const float send = upper ? v[j] : v[j + H];
-        v[j] = keep + __shfl_xor(send, H, kWave);
+        v[j] = keep + dpp<CTRL>(send);
     }
 }
 __device__ __forceinline__ float transpose_sum16(float (&v)[16], int lane) {
-    transpose_sum_step<8>(v, lane);
-    transpose_sum_step<4>(v, lane);
-    transpose_sum_step<2>(v, lane);
-    transpose_sum_step<1>(v, lane);
+    transpose_sum_step<8, 0x140>(v, lane);  // row_mirror
+    transpose_sum_step<4, 0x141>(v, lane);  // row_half_mirror
+    transpose_sum_step<2, 0x4E>(v, lane);   // quad_perm [2, 3, 0, 1]
+    transpose_sum_step<1, 0xB1>(v, lane);   // quad_perm [1, 0, 3, 2]
     return v[0];
 }
 

@@ -114,7 +114,7 @@ int state_segments(const Shape& s, int* Lc_out) {
 hipError_t launch_scan_reduce(const Shape& s, const void*, const void*, const void*,
                               const void*, float* agg, hipStream_t) {
     ++g_launches;
-    in_ws(agg, chunks(s) * nl(s) * 16, "agg", true);
+    in_ws(agg, chunks(s) * agg_subs(s) * nl(s) * 16, "agg", true);
     return hipSuccess;
 }
 hipError_t launch_packed_table(const int32_t*, int N, int, int, int32_t* cu, int32_t* cc,
@@ -127,7 +127,7 @@ hipError_t launch_packed_table(const int32_t*, int N, int, int, int32_t* cu, int
 hipError_t launch_scan_carry(const Shape& s, const float* agg, const float*, float* lc,
                              float*, hipStream_t) {
     ++g_launches;
-    in_ws(agg, chunks(s) * nl(s) * 16, "agg", false);
+    in_ws(agg, chunks(s) * agg_subs(s) * nl(s) * 16, "agg", false);
     in_ws(lc, bounds(s) * nl(s) * 4, "lam_chunk", true);
     return hipSuccess;
 }
@@ -143,10 +143,12 @@ hipError_t launch_gain(const Shape&, const void*, const void*, const float*, voi
     return hipSuccess;
 }
 hipError_t launch_chunk_prep(const Shape& s, bool fuse, const void*, const void*, const void*,
-                             const void*, const float* lc, void* w, void* Tm, float* g,
-                             hipStream_t, float* dinv) {
+                             const void*, const float* lc, const float* agg, void* w, void* Tm,
+                             float* g, hipStream_t, float* dinv) {
     ++g_launches;
     if (fuse) {
+        if (s.diag && !agg) fail("fused diagonal prep without the scan's products");
+        in_ws(agg, chunks(s) * agg_subs(s) * nl(s) * 16, "agg", false);
         in_ws(lc, bounds(s) * nl(s) * 4, "lam_chunk", false);
         in_ws(w, rows(s) * s.dk * esz(s.gain_bf16), "w", true);
     }

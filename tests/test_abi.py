@@ -70,7 +70,7 @@ def test_workspace_sizes(lib):
     d = _desc(B=8, H=16, T=4096, d_k=128, d_v=128, chunk=64)
     ws = kdn.forward_workspace_bytes(d)
     bh, nc = 128, 64
-    expect = (bh * nc * 128 * 16 + bh * (nc + 1) * 128 * 4 + bh * 4096 * 128 * 2
+    expect = (bh * nc * 4 * 128 * 16 + bh * (nc + 1) * 128 * 4 + bh * 4096 * 128 * 2
               + bh * nc * 64 * 64 * 2 + bh * nc * 64 * 4)
     assert expect <= ws <= expect + 5 * 256
     assert kdn.forward_workspace_bytes(_desc(d_k=48)) == 0
@@ -218,7 +218,7 @@ def test_state_pass_segments_follow_the_head_count(lib):
     long = _desc(B=1, H=16, T=65536, d_k=128, d_v=128, chunk=64)
     nseg = kdn.forward_segments(long)
     assert nseg == 8
-    plain = 16 * 1024 * (128 * 16 + 128 * 4 + 64 * 128 * 2 + 64 * 64 * 2 + 64 * 4) + 16 * 128 * 4
+    plain = 16 * 1024 * (4 * 128 * 16 + 128 * 4 + 64 * 128 * 2 + 64 * 64 * 2 + 64 * 4) + 16 * 128 * 4
     seg_bytes = 16 * nseg * (128 * 128 + 128 * 128) * 4
     assert plain + seg_bytes <= kdn.forward_workspace_bytes(long) <= plain + seg_bytes + 8 * 256
     few_chunks = _desc(B=1, H=2, T=15 * 64, d_k=64, d_v=64, chunk=64)

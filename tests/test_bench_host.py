@@ -25,11 +25,13 @@ def test_forward_algorithmic_bytes_at_the_layer_workload():
     B, H, T, d, C = 8, 16, 4096, 128, 64
     by, _ = bench.algorithmic(B, H, T, d, d, C)
     n, bh, nc = B * H * T, B * H, T // C
-    # keys (bf16) and three bf16 gates in, one fp32 Moebius product (4 floats)
-    # per (head, chunk, key dim) out
-    assert by["scan_reduce"] == n * d * 2 + 3 * n * 2 + bh * nc * d * 16
+    # keys (bf16) and three bf16 gates in, four fp32 Moebius products (4 floats
+    # each: the prefixes after 16, 32, 48 and 64 tokens) per (head, chunk, key
+    # dim) out
+    assert by["scan_reduce"] == n * d * 2 + 3 * n * 2 + bh * nc * 4 * d * 16
     # per token-head: k 256 + gates 6 + w 256 + T 128 + g 4 + boundary precision 8
-    assert by["chunk_prep"] == pytest.approx(n * (256 + 6 + 256 + 128 + 4 + 8), rel=1e-3)
+    # + three sub-block prefixes 96
+    assert by["chunk_prep"] == pytest.approx(n * (256 + 6 + 256 + 128 + 4 + 8 + 96), rel=1e-3)
     # q, k, w, v 1024 + T 128 + g 4 + o 256 per token-head, plus S0 and S_T
     assert by["chunk_state"] == pytest.approx(n * (1024 + 128 + 4 + 256)
                                               + 2 * bh * d * d * 4, rel=1e-3)
@@ -60,6 +62,6 @@ def test_isotropic_scan_bytes_hold_one_precision_per_chunk():
     by_d, _ = bench.algorithmic(1, 16, 65536, 128, 128, 64, "diagonal")
     by_i, _ = bench.algorithmic(1, 16, 65536, 128, 128, 64, "isotropic")
     n, nc = 16 * 65536, 1024
-    assert by_d["scan_reduce"] - by_i["scan_reduce"] == 16 * nc * 127 * 16
+    assert by_d["scan_reduce"] - by_i["scan_reduce"] == 16 * nc * (4 * 128 - 1) * 16
     assert by_i["scan_carry"] < by_d["scan_carry"] / 100
     assert bench.scan_bytes_8d(1, 16, 65536, 128, "isotropic") == n * (256 + 6 + 4)
