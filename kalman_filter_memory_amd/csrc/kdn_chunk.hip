@@ -214,15 +214,17 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
     const int t0 = c * C, n = min(C, sl.T - t0);
     const size_t row0 = sl.row0 + t0;
 
-    // stage K; rows past the end of the sequence are zero.  A given W (no fused
-    // gain: a stage call, not the forward) is read here directly.
+    // stage K; rows past the end of the sequence are zero (a full chunk, the
+    // common case, stores without selects).  A given W (no fused gain: a stage
+    // call, not the forward) is read here directly.
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    const bool full = n == C;
 #pragma unroll
     for (int x = 0; x < L::IT; ++x) {
         const int e = tid + kThreads * x;
         if (L::NV % kThreads == 0 || e < L::NV) {
             const int t = e / VPR, c0 = (e % VPR) * V;
-            *reinterpret_cast<u32x4*>(sK + t * LDK + c0) = (t < n) ? in.k[x] : zero;
+            *reinterpret_cast<u32x4*>(sK + t * LDK + c0) = (full || t < n) ? in.k[x] : zero;
         }
     }
     if constexpr (!FUSE) stage_rows<E, C, DK>(sW, LDK, w_in + row0 * DK, DK, n);
@@ -233,7 +235,7 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
         ga2 = ga * ga;
         gnu = to_f<G>(in.nu);
         gr = to_f<G>(in.r);
-        gir = 1.f / gr;
+        gir = rcp(gr);
     }
     if (wave == 0) {
         const float g = wave_incl_sum(lane < C ? log2_hw(ga) : 0.f);
@@ -295,18 +297,26 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
             // inside the branch below, and a shuffle reads nothing from them)
             const float rt = __shfl(gr, tb0 + (lane & 15), kWave);
             if (act) {
-                const float rden = 1.f / (den + rt);
+                const float rden = rcp(den + rt);
                 if (dinv && lane < 16 && tb0 + lane < n) dinv[row0 + tb0 + lane] = rden;
-                // (4) w rows
+                // (4) w rows: converted once, stored to LDS and to HBM (a full
+                // chunk with one base address and constant row offsets)
+                E out[16][NPL];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const float rd = lane_value(rden, j);
-                    E out[NPL];
 #pragma unroll
-                    for (int d = 0; d < NPL; ++d) out[d] = from_f<E>(pk[j][d] * rd);
-                    const int t = tb0 + j;
-                    store_dims<E, NPL>(sW + t * LDK + i0, out);
-                    if (t < n) store_dims<E, NPL>(w + (row0 + t) * DK + i0, out);
+                    for (int d = 0; d < NPL; ++d) out[j][d] = from_f<E>(pk[j][d] * rd);
+                    store_dims<E, NPL>(sW + (tb0 + j) * LDK + i0, out[j]);
+                }
+                E* wrow = w + (row0 + tb0) * DK + i0;
+                if (full) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) store_dims<E, NPL>(wrow + j * DK, out[j]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (tb0 + j < n) store_dims<E, NPL>(wrow + j * DK, out[j]);
                 }
             }
         } else {
@@ -383,11 +393,8 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
         if (id < NTILE) at[x] = mma_tile<E>(at[x], sW, LDK, 16 * sb, sK, LDK, 16 * tb, 0, DK, lane);
     }
     sync_lds();
-    for (int e = tid; e < C * C / 4; e += kThreads) {  // zero the upper part first
-        const int t = e / (C / 4), s0 = (e % (C / 4)) * 4;
-        if ((s0 >> 4) > (t >> 4))
-            *reinterpret_cast<float4*>(sAT + t * LDA + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    // (the blocks above the diagonal are never read: neither the solve nor the
+    // store of T touches them)
 #pragma unroll
     for (int x = 0; x < TPW; ++x) {
         const int id = wave + 4 * x;

@@ -125,14 +125,23 @@ __device__ __forceinline__ void load8x2<bf16_t>(const bf16_t* p0, const bf16_t* 
     b[3] = __uint_as_float(s1[1] & 0xFFFF0000u);
 }
 
-// inclusive prefix sum over the 64 lanes of a wave
+// inclusive prefix sum over the 64 lanes of a wave, in DPP moves: row_shr 1,
+// 2, 4, 8 (lanes shifted in from outside the row of 16 read 0) give every row's
+// own prefix; row_bcast 15 adds the last lane of row 0 to row 1 and of row 2 to
+// row 3, then row_bcast 31 adds lane 31 (the sum of rows 0-1) to rows 2 and 3.
+// Rows a move leaves out (its row mask) receive the `old` operand, 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, true));
+}
 __device__ __forceinline__ float wave_incl_sum(float x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const float y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
+    x += dpp_or_zero<0x111, 0xF>(x);
+    x += dpp_or_zero<0x112, 0xF>(x);
+    x += dpp_or_zero<0x114, 0xF>(x);
+    x += dpp_or_zero<0x118, 0xF>(x);
+    x += dpp_or_zero<0x142, 0xA>(x);
+    x += dpp_or_zero<0x143, 0xC>(x);
     return x;
 }
 
