@@ -283,8 +283,9 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
                         const float kv = kc[j][d];
                         const float pm = fmaf(a2, pv[d], nut);
                         pk[j][d] = kv * pm;
-                        v[j] = fmaf(kv, pk[j][d], v[j]);
-                        pv[d] = pm * rcp(fmaf(pm, kv * kv * ir, 1.f));
+                        const float kpk = kv * pk[j][d];  // k_i^2 P^-_i
+                        v[j] += kpk;
+                        pv[d] = pm * rcp(fmaf(kpk, ir, 1.f));
                     }
                 }
                 // (3) k^T P^- k of token tb0 + (lane % 16), summed over all lanes
