@@ -35,6 +35,74 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+_HIP = None
+
+
+def _hip():
+    """The HIP runtime this process already runs on (the one torch loaded)."""
+    global _HIP
+    if _HIP is None:
+        import ctypes
+
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        _HIP = ctypes.CDLL(path)
+    return _HIP
+
+
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence:
+    recording it performs no system-scope fence, so it neither writes back and
+    invalidates the caches between the timed kernels (which slows the kernel
+    that follows) nor adds that flush to the measured interval.  Same use as
+    torch.cuda.Event: record(), elapsed_time(end) in ms, and .cuda_event (the
+    hipEvent_t), which the binding hands to the library's timed entry points.
+    Read elapsed times only after a device synchronisation."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        h = ctypes.c_void_p()
+        rc = _hip().hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.cuda_event = h.value
+
+    def record(self):
+        import ctypes
+
+        import torch
+
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        rc = _hip().hipEventRecord(ctypes.c_void_p(self.cuda_event), stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+
+        ms = ctypes.c_float()
+        rc = _hip().hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.cuda_event),
+                                        ctypes.c_void_p(end.cuda_event))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        import ctypes
+
+        if getattr(self, "cuda_event", None) and _HIP is not None:
+            _HIP.hipEventDestroy(ctypes.c_void_p(self.cuda_event))
+
+
 def algorithmic(B, H, T, dk, dv, C, variant="diagonal"):
     """Design bytes and flops of each forward kernel (bf16 inputs): what this
     design's kernels read and write, the intermediates it passes between
@@ -91,8 +159,8 @@ def chunk_flops_full(n, dk, dv, C):
 # 512 MiB (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0), with the SHA-256 of the
 # kernel source they were taken on: reported only while the source is unchanged.
 TRAFFIC = {"kernel": "chunk_state",
-           "src_sha256": "5322a78de064bc1773690479d86a5753a538509f6332af7aa73c39641e564eb2",
-           "fetch_bytes": 614604501, "write_bytes": 142606409}
+           "src_sha256": "ef61607136181b039cebe7403385ba60b5903e06f4c7c2a78eeafb0e92ec5561",
+           "fetch_bytes": 614604406, "write_bytes": 142606336}
 
 
 def _traffic():
@@ -130,8 +198,9 @@ def bench_forward(args, inp, variant, steps, cold_reps, label):
     """One forward workload: wall-clock mean over `steps` back-to-back steps;
     per-step times (warm: back to back; cold: each step after a 512 MiB write
     that evicts the L2 and Infinity caches) as median / p10 / p90 from HIP
-    events; per-kernel times from the start and stop events that each kernel's
-    own dispatch records on the launch stream."""
+    events; per-kernel times from HIP events around back-to-back passes over
+    the forward's first kernels on the launch stream (kdn_forward_repeat), as
+    differences of prefixes that end one kernel apart."""
     import numpy as np
     import torch
 
@@ -169,7 +238,7 @@ def bench_forward(args, inp, variant, steps, cold_reps, label):
     ms = (time.perf_counter() - t0) * 1e3 / steps
 
     # warm per-step distribution (back to back, one event pair per step)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev = [(TimingEvent(), TimingEvent())
           for _ in range(steps)]
     for a0, a1 in ev:
         a0.record()
@@ -182,7 +251,7 @@ def bench_forward(args, inp, variant, steps, cold_reps, label):
     cold_us = []
     for _ in range(cold_reps):
         flush.fill_(1.0)
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0, a1 = TimingEvent(), TimingEvent()
         a0.record()
         step()
         a1.record()
@@ -190,18 +259,27 @@ def bench_forward(args, inp, variant, steps, cold_reps, label):
         cold_us.append(a0.elapsed_time(a1) * 1e3)
     del flush
 
-    # per-kernel durations from the dispatches' own events
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(KERNELS))]
-           for _ in range(steps)]
-    for row in evs:
-        for e in row:
-            e.record()
-    torch.cuda.synchronize()
-    for row in evs:
-        step(events=row)
-    torch.cuda.synchronize()
-    kern_us = {k: [row[2 * i].elapsed_time(row[2 * i + 1]) * 1e3 for row in evs]
-               for i, k in enumerate(KERNELS)}
+    # per-kernel durations as they run in the forward: the forward's kernels
+    # 0..i back to back, REPS passes between two events (kdn_forward_repeat on
+    # the workspace the steps above left), and kernel i's time the difference
+    # between the prefixes that end at i and at i - 1, in rounds.  Events
+    # between the kernels of a step would add packets of the runtime's own
+    # there and slow the kernel that follows; a kernel repeated alone would
+    # find other data in the caches than the one before it in the forward left.
+    reps, rounds = 10, max(3, steps // 10)
+    kern_us = {k: [] for k in KERNELS}
+    for _ in range(rounds):
+        pre = []
+        for last in range(len(KERNELS)):
+            a0, a1 = TimingEvent(), TimingEvent()
+            a0.record()
+            kdn.forward(t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], lam0, S0, variant, C,
+                        workspace=ws, out=out, repeat=(0, last, reps))
+            a1.record()
+            torch.cuda.synchronize()
+            pre.append(a0.elapsed_time(a1) * 1e3 / reps)
+        for i, kname in enumerate(KERNELS):
+            kern_us[kname].append(pre[i] - (pre[i - 1] if i else 0.0))
     kern_mean = {k: float(np.mean(v)) for k, v in kern_us.items()}
     by, fl = algorithmic(B, H, T, dk, dv, C, variant)
     kernels = {}
@@ -423,7 +501,7 @@ def bench_backward(args, inp):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(BWD_STAGES))]
+    evs = [[TimingEvent() for _ in range(2 * len(BWD_STAGES))]
            for _ in range(steps)]
     for row in evs:
         for e in row:
@@ -542,7 +620,7 @@ def bench_dense(args, inp):
         fwd()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = TimingEvent(), TimingEvent()
     e0.record()
     for _ in range(steps):
         gain()
@@ -596,7 +674,7 @@ def bench_layer(args):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(steps)]
+    evs = [[TimingEvent() for _ in range(10)] for _ in range(steps)]
     for row in evs:
         for e in row:
             e.record()
@@ -653,7 +731,7 @@ def bench_decode(args):
     for s in range(4):
         one(s)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = TimingEvent(), TimingEvent()
     e0.record()
     for s in range(steps):
         one(s)

@@ -115,14 +115,36 @@ kdn_status kdn_forward(const kdn_desc *d, const void *q, const void *k, const vo
 /* kdn_forward with timing: events is NULL or an array of 8 hipEvent_t
  * (entries may be NULL) created by the caller; events 2i and 2i + 1 are the
  * start and stop of kernel i (0 scan reduce, 1 scan carry, 2 chunk prep,
- * 3 chunk state), recorded by the kernel dispatches themselves on `stream`
- * (no extra packets between the kernels), so that a caller can time each
- * kernel of the forward.  Otherwise identical to kdn_forward. */
+ * 3 chunk state), handed to the kernel dispatches (hipExtLaunchKernel) on
+ * `stream`.  The HIP runtime records them with packets of its own around each
+ * dispatch, which put a few microseconds between the kernels and can slow the
+ * kernel that follows; kdn_forward_repeat times the kernels without them.
+ * Otherwise identical to kdn_forward. */
 kdn_status kdn_forward_events(const kdn_desc *d, const void *q, const void *k, const void *v,
                               const void *a, const void *qnoise, const void *r,
                               const float *lambda0, const float *S0, void *o, float *S_T,
                               float *lambda_T, void *ws, size_t ws_bytes, void *stream,
                               void *const *events);
+
+/* Timing aid: kernels first..last of kdn_forward (0 scan reduce, 1 scan
+ * carry, 2 chunk prep, 3 chunk state -- for few heads over long sequences the
+ * three launches of the segmented state pass), in order, `reps` times over,
+ * back to back on `stream`, with the arguments kdn_forward takes.  The time
+ * between two events around a call, divided by reps, is the time of those
+ * kernels as they run in the forward; differences between calls that stop one
+ * kernel apart give each kernel's own duration without events between the
+ * kernels (the HIP runtime records such events with packets of its own, which
+ * put microseconds between the kernels and slow the one that follows).  A
+ * range not starting at 0 reads what the kernels before it left in ws: ws must
+ * hold what a kdn_forward call with the same arguments left there.  Every pass
+ * rewrites the same values into ws and the outputs.  S_T must not alias S0 nor
+ * lambda_T alias lambda0 here (KDN_ERR_SHAPE, as for a range outside 0-3 or
+ * reps < 0); otherwise the argument checks and errors are kdn_forward's. */
+kdn_status kdn_forward_repeat(const kdn_desc *d, const void *q, const void *k, const void *v,
+                              const void *a, const void *qnoise, const void *r,
+                              const float *lambda0, const float *S0, void *o, float *S_T,
+                              float *lambda_T, void *ws, size_t ws_bytes, void *stream,
+                              int32_t first, int32_t last, int32_t reps);
 
 /* ------------------------------------------------------------------------
  * Allocation-free forward, for callers that cannot allocate device memory:

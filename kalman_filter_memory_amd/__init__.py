@@ -38,7 +38,7 @@ F32, BF16 = 0, 1
 
 EXPORTS = (
     "kdn_status_string", "kdn_validate", "kdn_forward_workspace_bytes", "kdn_forward",
-    "kdn_forward_events", "kdn_forward_segments",
+    "kdn_forward_events", "kdn_forward_repeat", "kdn_forward_segments",
     "kdn_mobius_scan_workspace_bytes", "kdn_mobius_scan", "kdn_gain",
     "kdn_chunk_delta_workspace_bytes", "kdn_chunk_delta", "kdn_decode_step",
     "kdn_backward_workspace_bytes", "kdn_backward", "kdn_backward_events",
@@ -92,6 +92,8 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_forward.restype = I
     lib.kdn_forward_events.argtypes = [D] + [P] * 11 + [P, S, P, ctypes.POINTER(P)]
     lib.kdn_forward_events.restype = I
+    lib.kdn_forward_repeat.argtypes = [D] + [P] * 11 + [P, S, P] + [ctypes.c_int32] * 3
+    lib.kdn_forward_repeat.restype = I
     lib.kdn_mobius_scan.argtypes = [D] + [P] * 8 + [P, S, P]
     lib.kdn_mobius_scan.restype = I
     lib.kdn_gain.argtypes = [D, P, P, P, P, P]
@@ -218,14 +220,17 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 def forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", chunk=64,
             workspace: torch.Tensor | None = None, out=None, events=None,
-            keep: torch.Tensor | None = None):
+            keep: torch.Tensor | None = None, repeat: tuple[int, int, int] | None = None):
     """KDN layer forward on the GPU.  Returns (o, S_T, lambda_T).
 
     out: optional preallocated (o, S_T, lambda_T); events: optional list of 8
-    torch.cuda.Event (already recorded once): the start and stop of each of the
-    four kernels, recorded by the kernel dispatches.  keep: a uint8 tensor of
-    backward_workspace_bytes: the forward keeps in it what backward(...,
-    kept=keep) needs (kdn_forward_keep)."""
+    events (objects with a .cuda_event handle, already created): the start and
+    stop of each of the four kernels, handed to the kernel dispatches.  keep: a
+    uint8 tensor of backward_workspace_bytes: the forward keeps in it what
+    backward(..., kept=keep) needs (kdn_forward_keep).  repeat: (first, last,
+    reps): kernels first..last of the forward, in order, reps times over, back
+    to back (kdn_forward_repeat; workspace must hold what a forward with the
+    same arguments left)."""
     lib = load_library()
     d = _forward_desc(q, k, v, a, qnoise, r, variant, chunk)
     B, H, T, dk = k.shape
@@ -259,7 +264,12 @@ def forward(q, k, v, a, qnoise, r, lambda0=None, S0=None, variant="diagonal", ch
     args = (ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(qnoise), _ptr(r),
             _ptr(lambda0), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(lam_T), _ptr(ws),
             ws.numel() * ws.element_size(), _stream())
-    if events is None:
+    if repeat is not None:
+        if workspace is None:
+            raise ValueError("repeat needs the workspace of an earlier forward")
+        first, last, reps = (int(x) for x in repeat)
+        _check(lib.kdn_forward_repeat(*args, first, last, reps), "kdn_forward_repeat")
+    elif events is None:
         _check(lib.kdn_forward(*args), "kdn_forward")
     else:
         if len(events) != 8:

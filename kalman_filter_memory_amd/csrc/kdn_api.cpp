@@ -201,11 +201,15 @@ size_t kdn_mobius_scan_workspace_bytes(const kdn_desc* d) {
     return w.w;  // aggregates + boundary precisions
 }
 
-kdn_status kdn_forward_events(const kdn_desc* d, const void* q, const void* k, const void* v,
-                              const void* a, const void* qnoise, const void* r,
-                              const float* lambda0, const float* S0, void* o, float* S_T,
-                              float* lambda_T, void* ws, size_t ws_bytes, void* stream,
-                              void* const* events) {
+namespace {
+
+// The forward's kernels first..last in order, `reps` times over; with
+// timing events (events NULL: none) on the kernels of one pass.
+kdn_status forward_run(const kdn_desc* d, const void* q, const void* k, const void* v,
+                       const void* a, const void* qnoise, const void* r, const float* lambda0,
+                       const float* S0, void* o, float* S_T, float* lambda_T, void* ws,
+                       size_t ws_bytes, void* stream, void* const* events, int first, int last,
+                       int reps) {
     kdn_status st = kdn_validate(d);
     if (st != KDN_OK) return st;
     const kdn::Shape s = make_shape(d);
@@ -232,25 +236,54 @@ kdn_status kdn_forward_events(const kdn_desc* d, const void* q, const void* k, c
         }
         kdn::launch_timing() = t;
     };
-    timed(0);
-    hipError_t e = kdn::launch_scan_reduce(s, k, a, qnoise, r, agg, hs);
-    timed(1);
-    if (e == hipSuccess) e = kdn::launch_scan_carry(s, agg, lambda0, lc, lambda_T, hs);
     kdn::Shape sw = s;
     sw.gain_bf16 = s.qkv_bf16;
-    timed(2);
-    if (e == hipSuccess)
-        e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, agg, wk, tm, g, hs);
     kdn::SegWs seg;
     seg.nseg = w.nseg;
     seg.Lc = w.Lc;
     seg.Sseg = reinterpret_cast<float*>(at(ws, w.seg_S));
     seg.Aseg = reinterpret_cast<float*>(at(ws, w.seg_A));
-    timed(3);
-    if (e == hipSuccess)
-        e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs, nullptr, &seg);
+    auto launch = [&](int i) -> hipError_t {
+        switch (i) {
+            case 0: return kdn::launch_scan_reduce(s, k, a, qnoise, r, agg, hs);
+            case 1: return kdn::launch_scan_carry(s, agg, lambda0, lc, lambda_T, hs);
+            case 2: return kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, agg, wk, tm, g, hs);
+            default:
+                return kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs, nullptr, &seg);
+        }
+    };
+    hipError_t e = hipSuccess;
+    for (int rep = 0; rep < reps && e == hipSuccess; ++rep)
+        for (int i = first; i <= last && e == hipSuccess; ++i) {
+            timed(i);
+            e = launch(i);
+        }
     kdn::launch_timing() = kdn::LaunchTiming{};
     return hip_status(e);
+}
+
+}  // namespace
+
+kdn_status kdn_forward_events(const kdn_desc* d, const void* q, const void* k, const void* v,
+                              const void* a, const void* qnoise, const void* r,
+                              const float* lambda0, const float* S0, void* o, float* S_T,
+                              float* lambda_T, void* ws, size_t ws_bytes, void* stream,
+                              void* const* events) {
+    return forward_run(d, q, k, v, a, qnoise, r, lambda0, S0, o, S_T, lambda_T, ws, ws_bytes,
+                       stream, events, 0, 3, 1);
+}
+
+kdn_status kdn_forward_repeat(const kdn_desc* d, const void* q, const void* k, const void* v,
+                              const void* a, const void* qnoise, const void* r,
+                              const float* lambda0, const float* S0, void* o, float* S_T,
+                              float* lambda_T, void* ws, size_t ws_bytes, void* stream,
+                              int32_t first, int32_t last, int32_t reps) {
+    if (first < 0 || last > 3 || first > last || reps < 0) return KDN_ERR_SHAPE;
+    // a repeated launch must read what the first one read
+    if ((S_T && S0 && S_T == S0) || (lambda_T && lambda0 && lambda_T == lambda0))
+        return KDN_ERR_SHAPE;
+    return forward_run(d, q, k, v, a, qnoise, r, lambda0, S0, o, S_T, lambda_T, ws, ws_bytes,
+                       stream, nullptr, first, last, reps);
 }
 
 size_t kdn_backward_workspace_bytes(const kdn_desc* d) {

@@ -261,6 +261,21 @@ void forward_case(const kdn_desc& d) {
            KDN_OK, "forward " + name(d));
     if (d.B * d.H > 0 && d.T > 0 && g_launches - before != 4)
         fail("forward launched " + std::to_string(g_launches - before) + " kernels: " + name(d));
+    // the timing aid: a range of the forward's kernels, reps passes, outputs
+    // apart from the inputs (aliasing ones are refused)
+    float* lamT = static_cast<float*>(fake(10));
+    float* ST = static_cast<float*>(fake(11));
+    begin_call(ws);
+    const int before_rep = g_launches;
+    expect(kdn_forward_repeat(&d, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), lam, S,
+                              fake(6), ST, lamT, W, ws, nullptr, 1, 3, 2),
+           KDN_OK, "forward repeat " + name(d));
+    if (d.B * d.H > 0 && d.T > 0 && g_launches - before_rep != 6)
+        fail("forward repeat launched " + std::to_string(g_launches - before_rep) +
+             " kernels: " + name(d));
+    expect(kdn_forward_repeat(&d, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), lam, S,
+                              fake(6), S, lamT, W, ws, nullptr, 3, 3, 1),
+           KDN_ERR_SHAPE, "forward repeat with S_T aliasing S0 " + name(d));
     begin_call(ws);
     expect(kdn_forward(&d, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), lam, S,
                        fake(6), S, lam, W, ws ? ws - 1 : 0, nullptr),

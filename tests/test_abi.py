@@ -111,6 +111,20 @@ def test_host_side_errors_return_before_any_launch(lib):
     g = _desc()
     g.gain_dtype = kdn.F32
     assert lib.kdn_chunk_delta(ctypes.byref(g), *([fake] * 8), ws, 1 << 30, None) == 3
+    # the repeat timing aid: kernel index, repeat count and aliasing outputs
+    # are refused, and its other checks are the forward's
+    rep = lib.kdn_forward_repeat
+    c = ctypes.c_void_p
+    # q k v a nu r, then lambda0, S0, o, S_T, lambda_T at distinct addresses
+    ok = [fake] * 6 + [c(0x3000), c(0x4000), c(0x5000), c(0x6000), c(0x7000)]
+    assert rep(ctypes.byref(d), *ok, ws, need, None, 0, 4, 1) == 2
+    assert rep(ctypes.byref(d), *ok, ws, need, None, -1, 3, 1) == 2
+    assert rep(ctypes.byref(d), *ok, ws, need, None, 2, 1, 1) == 2
+    assert rep(ctypes.byref(d), *ok, ws, need, None, 3, 3, -1) == 2
+    assert rep(ctypes.byref(d), *(ok[:9] + [ok[7], ok[10]]), ws, need, None, 3, 3, 1) == 2
+    assert rep(ctypes.byref(d), *(ok[:10] + [ok[6]]), ws, need, None, 0, 1, 1) == 2
+    assert rep(ctypes.byref(d), *ok, ws, need - 1, None, 0, 3, 1) == 4
+    assert rep(ctypes.byref(d), None, *ok[1:], ws, need, None, 0, 0, 1) == 1
     # empty problems are a no-op success without touching the GPU
     e = _desc(B=0)
     assert lib.kdn_forward(ctypes.byref(e), *([None] * 11), None, 0, None) == 0

@@ -117,6 +117,31 @@ def test_segmented_state_pass_matches_oracle(idx):
     _check_forward(inp, C, f"segmented ({nseg} segments)")
 
 
+# ------------------------------------------- the repeat timing aid
+# kdn_forward_repeat relaunches a range of the forward's kernels on the
+# workspace a forward left: every relaunch must leave the forward's outputs
+# bit for bit (the plain state pass, the segmented one, both variants).
+@pytest.mark.parametrize("shape", [(2, 2, 300, 128, 128, 64, "diagonal"),
+                                   (2, 2, 300, 128, 128, 64, "isotropic"),
+                                   (1, 1, 64 * 40 + 9, 128, 128, 64, "diagonal")],
+                         ids=["plain_diag", "plain_iso", "segmented_diag"])
+def test_forward_repeat_rewrites_the_same_results(shape):
+    B, H, T, dk, dv, C, variant = shape
+    inp = forward_inputs(B, H, T, dk, dv, variant=variant, dtype="bf16", seed=170)
+    t = forward_tensors(inp)
+    d = kdn.make_desc(B, H, T, dk, dv, C, variant, kdn.BF16, kdn.BF16)
+    say(f"[gpu] repeat {shape}: {kdn.forward_segments(d)} segments")
+    ws = torch.empty(kdn.forward_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    args = (t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], t["lambda0"], t["S0"], variant, C)
+    out = kdn.forward(*args, workspace=ws)
+    ref = [host(x).copy() for x in out]
+    for first, last in [(0, 3), (0, 2), (1, 3), (2, 2), (3, 3), (0, 0)]:
+        kdn.forward(*args, workspace=ws, out=out, repeat=(first, last, 3))
+        torch.cuda.synchronize()
+        for name, got, want in zip(("o", "S_T", "lambda_T"), out, ref):
+            assert np.array_equal(host(got), want), (first, last, name)
+
+
 # ---------------------------------------------------- the named workloads
 def test_workload_iso_f32_B1_H2_T256_d32():
     _check_forward(config_inputs(0), 32, "iso f32 [1,2,256,32]")
