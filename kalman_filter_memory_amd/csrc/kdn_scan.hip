@@ -231,19 +231,25 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_diag_kernel(
 // vector load of d_k/16 elements per lane), add them with DPP over their row
 // of 16 lanes, and hand the sum to the token's lane through the wave's LDS
 // slice `sq` (written and read by this wave only, in order).
-template <typename E, int DK>
+template <typename E, int DK, int C = 64>
 __device__ __forceinline__ float chunk_row_sq(const E* __restrict__ k0, int n, int lane,
                                               float* sq) {
-    constexpr int EPL = DK / 16;
+    constexpr int EPL = DK / 16, IT = (C + 3) / 4;
     const int g = lane >> 4, l16 = lane & 15;
-    for (int t = g; t < n; t += 4) {  // uniform within each row of 16 lanes
-        float x[EPL];
-        load_vec<E, EPL>(k0 + size_t(t) * DK + l16 * EPL, x);
+    // every row load is issued before the first is used (rows past the end
+    // reload the last one; their sums are not stored)
+    float x[IT][EPL];
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+        load_vec<E, EPL>(k0 + size_t(min(g + 4 * it, n - 1)) * DK + l16 * EPL, x[it]);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
         float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) s = fmaf(x[i], x[i], s);
+        for (int i = 0; i < EPL; ++i) s = fmaf(x[it][i], x[it][i], s);
         s = group_sum<16>(s);
-        if (l16 == 0) sq[t] = s;
+        const int t = g + 4 * it;
+        if (l16 == 0 && t < n) sq[t] = s;
     }
     // the stores above and the read below are by different lanes of this
     // wave: keep the compiler from moving the read ahead of the stores
@@ -251,23 +257,24 @@ __device__ __forceinline__ float chunk_row_sq(const E* __restrict__ k0, int n, i
     return lane < n ? sq[lane] : 0.f;
 }
 
-template <typename E, int DK, bool VL>
+template <typename E, int DK, int C, bool VL>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void reduce_iso_kernel(
     const E* __restrict__ k, const void* __restrict__ a, const void* __restrict__ nu,
-    const void* __restrict__ r, bool gate_bf16, int T, int C, int NC,
-    float4* __restrict__ agg, Packed pk) {
+    const void* __restrict__ r, bool gate_bf16, int T, int NC, float4* __restrict__ agg,
+    Packed pk) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int c = blockIdx.x * kWavesPerBlock + wave;
     const Slab sl = slab_of<VL>(blockIdx.y, T, NC, pk);
     if (c >= sl.nc) return;
     const int t0 = c * C, n = min(C, sl.T - t0);
+    // the gates first, so that their loads fly with the key rows'
+    const size_t tok = sl.row0 + t0 + min(lane, n - 1);
+    const float at = load_gate(a, tok, gate_bf16), nut = load_gate(nu, tok, gate_bf16);
+    const float rt = load_gate(r, tok, gate_bf16);
     __shared__ float sq[kWavesPerBlock][kWave];
-    const float kk = chunk_row_sq<E, DK>(k + (sl.row0 + t0) * DK, n, lane, sq[wave]);
+    const float kk = chunk_row_sq<E, DK, C>(k + (sl.row0 + t0) * DK, n, lane, sq[wave]);
     M2 P = {1.f, 0.f, 0.f, 1.f};
     if (lane < n) {
-        const size_t tok = sl.row0 + t0 + lane;
-        const float at = load_gate(a, tok, gate_bf16), nut = load_gate(nu, tok, gate_bf16);
-        const float rt = load_gate(r, tok, gate_bf16);
         const float b = kk / (static_cast<float>(DK) * rt);
         P = token_matrix(b, at * at, nut);
     }
@@ -568,21 +575,23 @@ hipError_t reduce_e(const Shape& s, const void* k, const void* a, const void* nu
         }                                                                                     \
         return hipGetLastError();                                                             \
     }
-#define KDN_RED_I(DK_)                                                                        \
-    if (!s.diag && s.dk == DK_) {                                                             \
+#define KDN_RED_IC(DK_, C_)                                                                   \
+    if (!s.diag && s.dk == DK_ && s.chunk == C_) {                                            \
         if (s.varlen)                                                                         \
-            launch_k((reduce_iso_kernel<E, DK_, true>), grid, block, 0, st, kk, a, nu, r,     \
-                     s.gate_bf16, s.T, s.chunk, s.nc, g, s.pk);                               \
+            launch_k((reduce_iso_kernel<E, DK_, C_, true>), grid, block, 0, st, kk, a, nu, r, \
+                     s.gate_bf16, s.T, s.nc, g, s.pk);                                        \
         else                                                                                  \
-            launch_k((reduce_iso_kernel<E, DK_, false>), grid, block, 0, st, kk, a, nu, r,    \
-                     s.gate_bf16, s.T, s.chunk, s.nc, g, s.pk);                               \
+            launch_k((reduce_iso_kernel<E, DK_, C_, false>), grid, block, 0, st, kk, a, nu,   \
+                     r, s.gate_bf16, s.T, s.nc, g, s.pk);                                     \
         return hipGetLastError();                                                             \
     }
+#define KDN_RED_I(DK_) KDN_RED_IC(DK_, 16) KDN_RED_IC(DK_, 32) KDN_RED_IC(DK_, 64)
 #define KDN_RED_DC(DK_) KDN_RED_D(DK_, 16) KDN_RED_D(DK_, 32) KDN_RED_D(DK_, 64)
     KDN_RED_DC(32) KDN_RED_DC(64) KDN_RED_DC(128)
     KDN_RED_I(32) KDN_RED_I(64) KDN_RED_I(128)
 #undef KDN_RED_DC
 #undef KDN_RED_I
+#undef KDN_RED_IC
 #undef KDN_RED_D
 #undef KDN_RED_DL
     return hipErrorInvalidValue;
