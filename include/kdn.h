@@ -309,8 +309,9 @@ kdn_status kdn_forward_varlen(const kdn_desc *d, const int32_t *cu_seqlens, int3
                               size_t ws_bytes, void *stream);
 
 /* Continuous-batching decode step (serving; "Kalman Delta Networks", English
- * abstract: constant-memory decoding): kdn_decode_step for d->B active sequences whose
- * states live in a cache of n_slots entries.  S_cache [n_slots,H,d_v,d_k] and
+ * abstract: decoding whose memory does not grow with the context):
+ * kdn_decode_step for d->B active sequences whose states live in a cache of
+ * n_slots entries.  S_cache [n_slots,H,d_v,d_k] and
  * lambda_cache [n_slots,H,d_k] (or [n_slots,H]) float32 are read and updated in
  * place at the slots slot[0..B-1] (device int32); q, k, v, a, qnoise, r and o
  * are indexed by the active sequence as in kdn_decode_step.  A slot outside
