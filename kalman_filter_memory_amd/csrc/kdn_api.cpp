@@ -136,16 +136,31 @@ BackwardWs backward_ws(const kdn_desc* d) {
 // lengths, which sizes the per-chunk arrays.  Layout: [cu | cc | agg |
 // lam_chunk | w | T | g].
 struct PackedWs {
-    size_t cu, cc, agg, lam_chunk, w, tm, g, total;
-    int nc_bound;
+    size_t cu, cc, agg, lam_chunk, w, tm, g, seg_S, seg_A, total;
+    int nc_bound, nseg_max;
 };
 
+// the segment count of the state pass for a packed batch of N sequences whose
+// longest has max_chunks chunks (1: no segments)
+int packed_segments(const kdn_desc* d, int max_chunks) {
+    kdn::Shape s = make_shape(d);
+    s.varlen = true;
+    s.BH = d->B * d->H;
+    s.nc = max_chunks;
+    return kdn::chunk_supported(s) ? std::max(1, kdn::state_segments(s, nullptr)) : 1;
+}
+
+// workspace offsets: [cu | cc | agg | lam_chunk | w | T | g | segment states |
+// segment maps]; the segment arrays are sized for the largest segment count any
+// split of the T tokens could ask for (one sequence holding them all)
 PackedWs packed_ws(const kdn_desc* d) {
     const kdn::Shape s = make_shape(d);
     const size_t N = d->B > 0 ? d->B : 0, H = d->H, nl = s.diag ? s.dk : 1;
     const size_t ncb = (s.T + N * (s.chunk - 1)) / s.chunk;
     PackedWs w;
     w.nc_bound = static_cast<int>(ncb);
+    w.nseg_max = N > 0 && H > 0 ? packed_segments(d, (s.T + s.chunk - 1) / s.chunk) : 1;
+    const size_t segs = w.nseg_max > 1 ? N * H * w.nseg_max : 0;
     w.cu = 0;
     w.cc = round_up((N + 1) * 4);
     w.agg = w.cc + round_up((N + 1) * 4);
@@ -153,7 +168,9 @@ PackedWs packed_ws(const kdn_desc* d) {
     w.w = w.lam_chunk + round_up(H * (ncb + N) * nl * 4);
     w.tm = w.w + round_up(H * s.T * s.dk * esize(d->qkv_dtype));
     w.g = w.tm + round_up(H * ncb * s.chunk * s.chunk * esize(d->qkv_dtype));
-    w.total = w.g + round_up(H * ncb * s.chunk * 4);
+    w.seg_S = w.g + round_up(H * ncb * s.chunk * 4);
+    w.seg_A = w.seg_S + round_up(segs * s.dv * s.dk * 4);
+    w.total = w.seg_A + round_up(segs * s.dk * s.dk * 4);
     return w;
 }
 
@@ -601,7 +618,15 @@ kdn_status kdn_forward_varlen(const kdn_desc* d, const int32_t* cu_seqlens, int3
     sw.gain_bf16 = s.qkv_bf16;
     if (e == hipSuccess && s.nc > 0)
         e = kdn::launch_chunk_prep(sw, true, k, a, qnoise, r, lc, agg, wk, tm, g, hs);
-    if (e == hipSuccess) e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs);
+    // few (sequence, head) slabs over long sequences: the segmented state pass,
+    // each slab cut into the same number of segments
+    kdn::SegWs seg;
+    seg.nseg = std::min(packed_segments(d, s.nc), w.nseg_max);
+    seg.Lc = 0;  // per slab, from its own chunk count
+    seg.Sseg = reinterpret_cast<float*>(at(ws, w.seg_S));
+    seg.Aseg = reinterpret_cast<float*>(at(ws, w.seg_A));
+    if (e == hipSuccess)
+        e = kdn::launch_chunk_state(s, q, k, v, g, wk, tm, S0, o, S_T, hs, nullptr, &seg);
     return hip_status(e);
 }
 

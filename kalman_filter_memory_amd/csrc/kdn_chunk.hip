@@ -904,9 +904,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     if (idt && g == 0) return;                        // segment 0 starts from S0: no map
     Slab sl = slab_of<VL>(head, T, NC, pk);
     if constexpr (SEG) {
-        const int cb = g * seg.Lc, ce = min(cb + seg.Lc, sl.nc);
+        // packed batches cut each sequence into the call's segment count (a
+        // short sequence's last segments may be empty: identity maps)
+        const int Lc = VL ? (sl.nc + seg.nseg - 1) / seg.nseg : seg.Lc;
+        const int cb = min(g * Lc, sl.nc), ce = min(cb + Lc, sl.nc);
         sl.row0 += (size_t)cb * C;
-        sl.T = min(sl.T - cb * C, (ce - cb) * C);
+        sl.T = max(0, min(sl.T - cb * C, (ce - cb) * C));
         sl.nc = ce - cb;
         sl.c0 += cb;
     }
@@ -1157,10 +1160,9 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
              static_cast<const E*>(w), static_cast<const E*>(Tm), S0, static_cast<E*>(o), S_T, \
              static_cast<E*>(Sc), s.BH, s.T, s.dv, s.nc, s.pk, PLAN_)
         const SegPlan plain;
-        if (s.varlen) {
-            KDN_STATE_L(true, true, false, grid(s.BH, ntv), plain);
-        } else if (!sw || sw->nseg <= 1 || Sc || !o) {
-            if (o) KDN_STATE_L(false, true, false, grid(s.BH, ntv), plain);
+        if (!sw || sw->nseg <= 1 || Sc || !o) {
+            if (s.varlen) KDN_STATE_L(true, true, false, grid(s.BH, ntv), plain);
+            else if (o) KDN_STATE_L(false, true, false, grid(s.BH, ntv), plain);
             else KDN_STATE_L(false, false, false, grid(s.BH, ntv), plain);
         } else {
             // segments: the maps of segments 0 .. nseg - 2, their composition
@@ -1177,7 +1179,8 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
             p.ntv = ntv;
             p.nta = (DK + DVT - 1) / DVT;  // identity rows past d_k are not written
             launch_timing() = LaunchTiming{t.start, nullptr};
-            KDN_STATE_L(false, false, true, grid(s.BH * p.nsegL, p.ntv + p.nta), p);
+            if (s.varlen) KDN_STATE_L(true, false, true, grid(s.BH * p.nsegL, p.ntv + p.nta), p);
+            else KDN_STATE_L(false, false, true, grid(s.BH * p.nsegL, p.ntv + p.nta), p);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             if (sw->nseg > 2) {
@@ -1189,7 +1192,8 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
             p.nsegL = sw->nseg;
             p.nta = 0;
             launch_timing() = LaunchTiming{nullptr, t.stop};
-            KDN_STATE_L(false, true, true, grid(s.BH * p.nsegL, p.ntv), p);
+            if (s.varlen) KDN_STATE_L(true, true, true, grid(s.BH * p.nsegL, p.ntv), p);
+            else KDN_STATE_L(false, true, true, grid(s.BH * p.nsegL, p.ntv), p);
         }
 #undef KDN_STATE_L
         return hipGetLastError();
@@ -1264,7 +1268,7 @@ int state_segments(const Shape& s, int* chunks_per_segment) {
     // at low B*H the plain pass runs B*H*(dv/dvt) workgroups, one per CU:
     // cut each head into segments until about one workgroup per CU runs the
     // read-out pass, keeping at least 8 chunks per segment
-    if (!s.varlen && s.BH > 0 && dvt > 0 && s.nc >= 16) {
+    if (s.BH > 0 && dvt > 0 && s.nc >= 16) {
         const int units = s.BH * (s.dv / dvt);
         if (units < 128) {
             const int want = std::min(256 / units, s.nc / 8);

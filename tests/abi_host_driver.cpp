@@ -21,6 +21,7 @@ namespace {
 
 int g_fail = 0;
 int g_launches = 0;
+int g_seg_packed = 0;  // segmented state passes of packed batches seen
 // fake device addresses: tensors far below the workspace, never dereferenced
 const uintptr_t kTensorBase = uintptr_t(1) << 40;
 const uintptr_t kWsBase = uintptr_t(1) << 44;
@@ -96,7 +97,7 @@ bool backward_supported(const Shape& s) { return chunk_supported(s); }
 int state_segments(const Shape& s, int* Lc_out) {
     int Lc = s.nc, nseg = 1;
     const int dvt = dvt_of(s);
-    if (!s.varlen && s.BH > 0 && dvt > 0 && s.nc >= 16) {
+    if (s.BH > 0 && dvt > 0 && s.nc >= 16) {
         const int units = s.BH * (s.dv / dvt);
         if (units < 128) {
             int want = 256 / units;
@@ -168,9 +169,15 @@ hipError_t launch_chunk_state(const Shape& s, const void*, const void*, const vo
     if (seg && seg->nseg > 1) {
         int Lc = 0;
         const int nseg = state_segments(s, &Lc);
-        if (nseg != seg->nseg || Lc != seg->Lc) fail("segment plan differs from state_segments");
-        if ((size_t)(seg->nseg - 1) * seg->Lc >= (size_t)s.nc || (size_t)seg->nseg * seg->Lc < (size_t)s.nc)
-            fail("segments do not cover the chunks with a non-empty last segment");
+        if (s.varlen) {
+            // packed: every slab cuts its own chunks into nseg segments
+            ++g_seg_packed;
+            if (seg->Lc != 0 || seg->nseg > nseg) fail("packed segment plan");
+        } else {
+            if (nseg != seg->nseg || Lc != seg->Lc) fail("segment plan differs from state_segments");
+            if ((size_t)(seg->nseg - 1) * seg->Lc >= (size_t)s.nc || (size_t)seg->nseg * seg->Lc < (size_t)s.nc)
+                fail("segments do not cover the chunks with a non-empty last segment");
+        }
         in_ws(seg->Sseg, (size_t)s.BH * seg->nseg * s.dv * s.dk * 4, "Sseg", true);
         in_ws(seg->Aseg, (size_t)s.BH * seg->nseg * s.dk * s.dk * 4, "Aseg", true);
     }
@@ -390,7 +397,11 @@ int main() {
             varlen_case(8, 3, 502, 64, 32, C, var, 1);
             varlen_case(1, 1, 1, 32, 32, C, var, 0);
             varlen_case(5, 2, 0, 128, 128, C, var, 1);
+            // one long sequence over few heads: the segmented state pass
+            varlen_case(1, 2, 5000, 128, 128, C, var, 1);
+            varlen_case(3, 1, 4100, 64, 128, C, var, 0);
         }
+    if (g_seg_packed == 0) fail("no packed batch took the segmented state pass");
     std::printf("%d launches checked, %d failures\n", g_launches, g_fail);
     return g_fail == 0 ? 0 : 1;
 }

@@ -476,6 +476,47 @@ def test_forward_varlen_matches_oracle_per_sequence(variant, dtype, chunk):
     np.testing.assert_array_equal(l_h[1], init["lambda0"][1])
 
 
+@pytest.mark.parametrize("variant,dtype,chunk,dk,lens,H", [
+    ("diagonal", "bf16", 64, 128, [3000, 0, 1, 700, 64 * 20 + 5], 2),
+    ("isotropic", "f32", 32, 64, [2100, 33, 0], 1),
+], ids=["diag_bf16_C64", "iso_f32_C32"])
+def test_forward_varlen_long_sequences_take_the_segmented_state_pass(variant, dtype, chunk, dk,
+                                                                     lens, H):
+    """Few (sequence, head) slabs with a long sequence: the packed forward cuts
+    every slab into the same number of segments (short and empty sequences get
+    empty ones, which act as identity maps); each sequence still matches the
+    oracle on its own."""
+    N, T = len(lens), sum(lens)
+    td = kdn.BF16 if dtype == "bf16" else kdn.F32
+    nseg = kdn.forward_segments(kdn.make_desc(N, H, max(lens), dk, dk, chunk, variant, td, td))
+    say(f"[gpu] forward_varlen {variant} {dtype} C={chunk} lens={lens}: {nseg} segments")
+    assert nseg > 1
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    inp = forward_inputs(1, H, T, dk, dk, variant=variant, dtype=dtype, seed=93)
+    init = forward_inputs(N, H, 1, dk, dk, variant=variant, dtype=dtype, seed=94)
+    t = forward_tensors(inp)
+    o, S_T, lam_T = kdn.forward_varlen(t["q"][0], t["k"][0], t["v"][0], t["a"][0], t["nu"][0],
+                                       t["r"][0], torch.from_numpy(cu).cuda(), max(lens),
+                                       torch.from_numpy(init["lambda0"]).cuda(),
+                                       torch.from_numpy(init["S0"]).cuda(), variant=variant,
+                                       chunk=chunk)
+    torch.cuda.synchronize()
+    o_h, S_h, l_h = host(o), host(S_T), host(lam_T)
+    tol = _tol(dtype)
+    for s_, L in enumerate(lens):
+        sl = slice(cu[s_], cu[s_ + 1])
+        sub = {n: inp[n][:, :, sl] for n in ("q", "k", "v", "a", "nu", "r")}
+        ref = oracle.forward(sub["q"], sub["k"], sub["v"], sub["a"], sub["nu"], sub["r"],
+                             init["lambda0"][s_:s_ + 1], init["S0"][s_:s_ + 1], variant)
+        e_o = normwise(o_h[:, sl][None], ref["o"]) if L else 0.0
+        e_s = normwise(S_h[s_:s_ + 1], ref["S_T"])
+        e_l = elementwise(l_h[s_:s_ + 1], ref["lambda_T"])
+        say(f"    seq {s_} (L={L}): err o {e_o:.2e}  S_T {e_s:.2e}  lambda_T {e_l:.2e}")
+        assert e_o <= tol and e_s <= tol and e_l <= TOL_LAMBDA
+        if L == 0:  # an empty sequence passes its state through unchanged
+            np.testing.assert_array_equal(S_h[s_], init["S0"][s_])
+
+
 @pytest.mark.parametrize("dk,dtype,T,chunk", [(32, "f32", 300, 64), (64, "f32", 257, 64),
                                               (64, "bf16", 200, 64), (128, "f32", 96, 32),
                                               (128, "bf16", 150, 64), (32, "bf16", 5, 16)])
