@@ -97,8 +97,8 @@ __device__ __forceinline__ void store_ct(float* dst, floatx4 v, int lane) {
 // LDS of the prep kernel: two regions reused as the chunk proceeds.
 //   region 1: K [C][LDK] (input dtype), then A with the diagonal blocks of T
 //             [C][LDA] (fp32)
-//   region 2: W [C][LDK] (input dtype), then the off-diagonal blocks of T
-//             and the per-wave scratch of the solve (fp32)
+//   region 2: W [C][LDK] (input dtype), then the blocks of the solve
+//             (fp32)
 template <typename E, int DK, int C> struct PrepLds {
     // rows padded by 32 bytes (a stride of 8 mod 16 dwords: conflict-free MFMA
     // fragment reads)
@@ -107,10 +107,10 @@ template <typename E, int DK, int C> struct PrepLds {
     static constexpr int NT = C / 16;  // 16-token sub-blocks = waves of the gain pass
     static constexpr int NPL = DK >= 64 ? DK / 64 : 1;  // key dims per lane (gain pass)
     static constexpr int R1 = cmax(C * LDK * (int)sizeof(E), C * LDA * 4);
-    // region 2 also holds the off-diagonal blocks of T and one 16x16 fp32
-    // scratch block per wave while T is formed
+    // region 2 also holds the blocks of T (off-diagonal, and the diagonal ones
+    // transposed) while T is formed
     static constexpr int R2 =
-        cmax(C * LDK * (int)sizeof(E), (NT * (NT - 1) / 2 + NT + 4) * kBlk * 4);
+        cmax(C * LDK * (int)sizeof(E), (NT * (NT - 1) / 2 + NT) * kBlk * 4);
     static constexpr int BYTES = R1 + R2 + 2 * C * (int)sizeof(float);
     // 16-byte pieces of one chunk's K per thread
     static constexpr int NV = C * DK / Vec16<E>::N;
@@ -423,7 +423,6 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
     // is written)
     float* sTo = sZ;                                      // [NT (NT - 1) / 2] blocks
     float* sTd = sZ + kBlk * (NT * (NT - 1) / 2);          // [NT] blocks
-    float* sZw = sTd + kBlk * NT + kBlk * wave;            // per-wave scratch block
     if (wave == 0 && (lane >> 4) < NT) {
         const int b0 = 16 * (lane >> 4), col = lane & 15;
         float x[16];
@@ -453,25 +452,51 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
     }
     sync_lds();
     // off-diagonal blocks by block columns: wave j forms T_ij for i = j+1, j+2, ...
-    // in order, T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, on fp32 MFMA.  A stays in
-    // place (the other waves still read it); the T_ij (and Z) are kept
-    // transposed, [n][k], in blocks of their own, so every operand fragment is
-    // one 16-byte read and a wave depends only on its own earlier blocks: no
-    // barrier between steps.
+    // in order, T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, on fp32 MFMA.  A 16x16
+    // MFMA result (lane l: rows 4 (l / 16) + e of column l % 16) is, lane for
+    // lane, the B operand of the next product (step e contracts over row
+    // 4 (l / 16) + e), so the column's blocks T_mj stay in registers and the
+    // chain has no LDS round trip; each product splits its four steps over two
+    // accumulators.  A and the diagonal inverses are read from LDS (A row-major
+    // in place, T_jj transposed in its own block); the T_ij are stored
+    // transposed, [n][k], for the output below.
     if (wave < NT - 1) {
         const int j = wave;
-        for (int i = j + 1; i < NT; ++i) {
-            floatx4 z = {0.f, 0.f, 0.f, 0.f};
-            z = mma16_f32(z, sAT + 16 * i * LDA + 16 * j, LDA, sTd + kBlk * j, lane);
-            for (int m = j + 1; m < i; ++m)
-                z = mma16_f32(z, sAT + 16 * i * LDA + 16 * m, LDA, sTo + kBlk * tri_index(m, j),
-                              lane);
-            store_ct(sZw, z, lane);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // Z is read back below
-            floatx4 tij = {0.f, 0.f, 0.f, 0.f};
-            tij = mma16_f32(tij, sAT + 16 * i * LDA + 16 * i, LDA, sZw, lane);
-            store_ct(sTo + kBlk * tri_index(i, j), -tij, lane);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read in the next step
+        floatx4 tc[NT];  // tc[m]: T_mj in the MFMA result layout, m = j .. i - 1
+        {
+            const float4 d4 = *reinterpret_cast<const float4*>(sTd + kBlk * j + (lane & 15) * kBld +
+                                                               4 * (lane >> 4));
+#pragma unroll
+            for (int m = 0; m < NT; ++m) tc[m] = floatx4{d4.x, d4.y, d4.z, d4.w};
+        }
+        const int r = lane & 15, k4 = 4 * (lane >> 4);
+#pragma unroll
+        for (int i = 1; i < NT; ++i) {
+            if (i <= j) continue;
+            floatx4 za = {0.f, 0.f, 0.f, 0.f}, zb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NT - 1; ++m) {
+                if (m < j || m >= i) continue;
+                const float4 a4 =
+                    *reinterpret_cast<const float4*>(sAT + (16 * i + r) * LDA + 16 * m + k4);
+                za = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, tc[m][0], za, 0, 0, 0);
+                zb = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, tc[m][2], zb, 0, 0, 0);
+                za = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, tc[m][1], za, 0, 0, 0);
+                zb = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, tc[m][3], zb, 0, 0, 0);
+            }
+            const floatx4 z = za + zb;
+            const float4 t4 =
+                *reinterpret_cast<const float4*>(sAT + (16 * i + r) * LDA + 16 * i + k4);
+            floatx4 ta = {0.f, 0.f, 0.f, 0.f}, tb = {0.f, 0.f, 0.f, 0.f};
+            ta = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.x, z[0], ta, 0, 0, 0);
+            tb = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.z, z[2], tb, 0, 0, 0);
+            ta = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.y, z[1], ta, 0, 0, 0);
+            tb = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.w, z[3], tb, 0, 0, 0);
+            const floatx4 tij = -(ta + tb);
+#pragma unroll
+            for (int m = 1; m < NT; ++m)
+                if (m == i) tc[m] = tij;
+            store_ct(sTo + kBlk * tri_index(i, j), tij, lane);
         }
     }
     sync_lds();
