@@ -87,6 +87,32 @@ __device__ __forceinline__ floatx4 mma16_f32(floatx4 acc, const float* A, int ld
     return acc;
 }
 
+// four floats split as hi + lo, both bfloat16 (hi rounded to nearest, lo the
+// rounded remainder), packed as 16x16x16 MFMA operands: products of splits
+// dropping lo * lo are exact to about 2^-17 relative
+struct Bf16Split {
+    short4x hi, lo;
+};
+__device__ __forceinline__ Bf16Split split_bf16(float a, float b, float c, float d) {
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    const uint32_t h01 = pack_bf16(a, b), h23 = pack_bf16(c, d);
+    const uint32_t l01 = pack_bf16(a - __uint_as_float(h01 << 16),
+                                   b - __uint_as_float(h01 & 0xFFFF0000u));
+    const uint32_t l23 = pack_bf16(c - __uint_as_float(h23 << 16),
+                                   d - __uint_as_float(h23 & 0xFFFF0000u));
+    return Bf16Split{__builtin_bit_cast(short4x, u32x2_t{h01, h23}),
+                     __builtin_bit_cast(short4x, u32x2_t{l01, l23})};
+}
+// acc + X Y for 16x16 blocks given X's operand piece (lane l: row l % 16, k
+// 4 (l / 16) .. + 3) and Y split; three bf16 MFMAs
+__device__ __forceinline__ floatx4 mma16_split(floatx4 acc, const float4& x, const Bf16Split& y) {
+    const Bf16Split xs = split_bf16(x.x, x.y, x.z, x.w);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xs.hi, y.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xs.lo, y.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xs.hi, y.lo, acc, 0, 0, 0);
+    return acc;
+}
+
 // a 16x16 MFMA result (lane l: rows 4 (l / 16) + e, column l % 16) stored
 // transposed, [n][m], one 16-byte store per lane
 __device__ __forceinline__ void store_ct(float* dst, floatx4 v, int lane) {
@@ -452,51 +478,78 @@ __device__ __forceinline__ void prep_chunk(const E* w_in, bool diag, E* w,
     }
     sync_lds();
     // off-diagonal blocks by block columns: wave j forms T_ij for i = j+1, j+2, ...
-    // in order, T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, on fp32 MFMA.  A 16x16
-    // MFMA result (lane l: rows 4 (l / 16) + e of column l % 16) is, lane for
-    // lane, the B operand of the next product (step e contracts over row
-    // 4 (l / 16) + e), so the column's blocks T_mj stay in registers and the
-    // chain has no LDS round trip; each product splits its four steps over two
-    // accumulators.  A and the diagonal inverses are read from LDS (A row-major
-    // in place, T_jj transposed in its own block); the T_ij are stored
-    // transposed, [n][k], for the output below.
+    // in order, T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj.  A 16x16 MFMA result
+    // (lane l: rows 4 (l / 16) + e of column l % 16) is, lane for lane, the B
+    // operand of the next product (its contraction index 4 (l / 16) + e), so the
+    // column's blocks T_mj stay in registers and the chain has no LDS round
+    // trip.  A and the diagonal inverses are read from LDS (A row-major in
+    // place, T_jj transposed in its own block); the T_ij are stored transposed,
+    // [n][k], for the output below.  bf16 inputs (T is stored in bf16): each
+    // 16x16x16 product as three bf16 MFMAs on hi / lo splits, about 2^-17
+    // relative, a quarter of the issue time of four fp32 16x16x4 steps; fp32
+    // inputs: fp32 MFMA, the steps over two accumulators.
     if (wave < NT - 1) {
         const int j = wave;
-        floatx4 tc[NT];  // tc[m]: T_mj in the MFMA result layout, m = j .. i - 1
-        {
-            const float4 d4 = *reinterpret_cast<const float4*>(sTd + kBlk * j + (lane & 15) * kBld +
-                                                               4 * (lane >> 4));
+        const int r = lane & 15, k4 = 4 * (lane >> 4);
+        const float4 d4 =
+            *reinterpret_cast<const float4*>(sTd + kBlk * j + r * kBld + k4);  // T_jj as B
+        if constexpr (sizeof(E) == 2) {
+            Bf16Split tc[NT];  // T_mj split, m = j .. i - 1
+#pragma unroll
+            for (int m = 0; m < NT; ++m) tc[m] = split_bf16(d4.x, d4.y, d4.z, d4.w);
+#pragma unroll
+            for (int i = 1; i < NT; ++i) {
+                if (i <= j) continue;
+                floatx4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < NT - 1; ++m) {
+                    if (m < j || m >= i) continue;
+                    z = mma16_split(
+                        z, *reinterpret_cast<const float4*>(sAT + (16 * i + r) * LDA + 16 * m + k4),
+                        tc[m]);
+                }
+                const floatx4 t = mma16_split(
+                    floatx4{0.f, 0.f, 0.f, 0.f},
+                    *reinterpret_cast<const float4*>(sAT + (16 * i + r) * LDA + 16 * i + k4),
+                    split_bf16(z[0], z[1], z[2], z[3]));
+                const floatx4 tij = -t;
+#pragma unroll
+                for (int m = 1; m < NT; ++m)
+                    if (m == i) tc[m] = split_bf16(tij[0], tij[1], tij[2], tij[3]);
+                store_ct(sTo + kBlk * tri_index(i, j), tij, lane);
+            }
+        } else {
+            floatx4 tc[NT];  // T_mj in the MFMA result layout, m = j .. i - 1
 #pragma unroll
             for (int m = 0; m < NT; ++m) tc[m] = floatx4{d4.x, d4.y, d4.z, d4.w};
-        }
-        const int r = lane & 15, k4 = 4 * (lane >> 4);
 #pragma unroll
-        for (int i = 1; i < NT; ++i) {
-            if (i <= j) continue;
-            floatx4 za = {0.f, 0.f, 0.f, 0.f}, zb = {0.f, 0.f, 0.f, 0.f};
+            for (int i = 1; i < NT; ++i) {
+                if (i <= j) continue;
+                floatx4 za = {0.f, 0.f, 0.f, 0.f}, zb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < NT - 1; ++m) {
-                if (m < j || m >= i) continue;
-                const float4 a4 =
-                    *reinterpret_cast<const float4*>(sAT + (16 * i + r) * LDA + 16 * m + k4);
-                za = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, tc[m][0], za, 0, 0, 0);
-                zb = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, tc[m][2], zb, 0, 0, 0);
-                za = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, tc[m][1], za, 0, 0, 0);
-                zb = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, tc[m][3], zb, 0, 0, 0);
+                for (int m = 0; m < NT - 1; ++m) {
+                    if (m < j || m >= i) continue;
+                    const float4 a4 =
+                        *reinterpret_cast<const float4*>(sAT + (16 * i + r) * LDA + 16 * m + k4);
+                    za = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, tc[m][0], za, 0, 0, 0);
+                    zb = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, tc[m][2], zb, 0, 0, 0);
+                    za = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, tc[m][1], za, 0, 0, 0);
+                    zb = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, tc[m][3], zb, 0, 0, 0);
+                }
+                const floatx4 z = za + zb;
+                const float4 t4 =
+                    *reinterpret_cast<const float4*>(sAT + (16 * i + r) * LDA + 16 * i + k4);
+                floatx4 ta = {0.f, 0.f, 0.f, 0.f}, tb = {0.f, 0.f, 0.f, 0.f};
+                ta = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.x, z[0], ta, 0, 0, 0);
+                tb = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.z, z[2], tb, 0, 0, 0);
+                ta = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.y, z[1], ta, 0, 0, 0);
+                tb = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.w, z[3], tb, 0, 0, 0);
+                const floatx4 tij = -(ta + tb);
+#pragma unroll
+                for (int m = 1; m < NT; ++m)
+                    if (m == i) tc[m] = tij;
+                store_ct(sTo + kBlk * tri_index(i, j), tij, lane);
             }
-            const floatx4 z = za + zb;
-            const float4 t4 =
-                *reinterpret_cast<const float4*>(sAT + (16 * i + r) * LDA + 16 * i + k4);
-            floatx4 ta = {0.f, 0.f, 0.f, 0.f}, tb = {0.f, 0.f, 0.f, 0.f};
-            ta = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.x, z[0], ta, 0, 0, 0);
-            tb = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.z, z[2], tb, 0, 0, 0);
-            ta = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.y, z[1], ta, 0, 0, 0);
-            tb = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.w, z[3], tb, 0, 0, 0);
-            const floatx4 tij = -(ta + tb);
-#pragma unroll
-            for (int m = 1; m < NT; ++m)
-                if (m == i) tc[m] = tij;
-            store_ct(sTo + kBlk * tri_index(i, j), tij, lane);
         }
     }
     sync_lds();
