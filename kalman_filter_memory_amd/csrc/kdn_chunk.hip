@@ -18,8 +18,9 @@
 //   prep_kernel   two chunks per workgroup, all chunks in parallel: optionally
 //                 the gain w from the chunk-boundary precision, then A and the
 //                 unit-lower-triangular inverse T (16x16 diagonal blocks by
-//                 forward substitution, off-diagonal blocks by block columns),
-//                 all in fp32; T is stored in the input dtype.
+//                 forward substitution, off-diagonal blocks by block columns
+//                 on MFMA), in fp32 or fp32-accurate arithmetic; T is stored
+//                 in the input dtype.
 //   state_kernel  one workgroup per (head, d_v tile), sequential over chunks:
 //                 the S0-dependent products on MFMA (bf16 inputs: 16x16x32
 //                 bf16 MFMA with fp32 accumulation; fp32 inputs: 16x16x4 fp32
@@ -27,8 +28,9 @@
 //                 whole sequence; an input-dtype copy of it is kept in LDS as
 //                 the operand of the next chunk.
 // Operand arrays in LDS are row-major with the contraction index contiguous,
-// so every MFMA fragment is one 16-byte (bf16) or 4-byte (fp32) LDS read; the
-// transposed copy of W needed by the state update is written when staged.
+// so every MFMA fragment is one 16-byte (bf16) or 4-byte (fp32) LDS read;
+// operands needed with the contraction index strided (W in the state update,
+// the token-major R) are read with transposing LDS reads.
 #include <algorithm>
 
 #include "kdn_device.h"
@@ -153,10 +155,12 @@ template <typename E, int DK, int C> struct PrepLds {
 //     transposing butterfly inside 16-lane groups and two cross-group
 //     exchanges; (4) w = P^- k / (k^T P^- k + r) is written by rows.
 //     Isotropic: |k|^2 per token, one scalar chain, w = k / (|k|^2 + r lambda^-).
-//   A = strict_tril(K W^T * Gamma) on MFMA and T = (I + A)^{-1} in fp32:
-//     16x16 diagonal blocks in place by forward substitution (one lane per
+//   A = strict_tril(K W^T * Gamma) on MFMA and T = (I + A)^{-1}: 16x16
+//     diagonal blocks in place by forward substitution in fp32 (one lane per
 //     column, all blocks in one wave), then block columns T_ij = -T_ii
-//     sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA, one wave per block column.
+//     sum_{m=j}^{i-1} A_im T_mj on MFMA, one wave per block column (fp32
+//     MFMA for fp32 inputs; for bf16 inputs three bf16 MFMAs per product on
+//     hi / lo splits, about 2^-17 relative).
 
 // One chunk's inputs, loaded into registers ahead of their use: K rows, the
 // gates of token `lane` (in their storage type G, widened only when used, so
