@@ -327,7 +327,10 @@ def bench_forward(args, inp, variant, steps, cold_reps, label):
                         "bytes": scan_by, "GB/s": round(scan_by / scan_s / 1e9, 1),
                         "frac": round(scan_by / scan_s / 1e9 / PEAK_HBM_GBS, 4),
                         "bytes_8d": scan8,
-                        "frac_8d": round(scan8 / scan_s / 1e9 / PEAK_HBM_GBS, 4)},
+                        "note_8d": "bytes_8d counts a scan that also writes every predictive "
+                                   "precision; this design's scan does not (the prep derives them "
+                                   "inside each chunk), so bytes_8d over its time is no fraction "
+                                   "of anything it moves"},
            "kernels": kernels}
     del t, ws, out
     torch.cuda.empty_cache()
