@@ -157,6 +157,28 @@ __device__ __forceinline__ float group16_sum(float x) {
     return x;
 }
 
+// The elements of a row-major LDS array X that lane l holds in a 16x16 MFMA
+// result tile at (r0, c0): x[e] = X[r0 + 4 (l/16) + e][c0 + l % 16].  bfloat16:
+// one transposing read (lane 4 j + p addresses row r0 + 4 (l/16) + j, columns
+// c0 + 4 p .. + 3, and receives column c0 + l % 16 of the four rows).
+template <typename E>
+__device__ __forceinline__ void tile_col4(const E* X, int ld, int r0, int c0, int lane,
+                                          float (&x)[4]);
+template <>
+__device__ __forceinline__ void tile_col4<bf16_t>(const bf16_t* X, int ld, int r0, int c0,
+                                                  int lane, float (&x)[4]) {
+    const short4x v =
+        read_tr16(X + (r0 + 4 * (lane >> 4) + ((lane & 15) >> 2)) * ld + c0 + 4 * (lane & 3));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = bf2f(static_cast<bf16_t>(v[e]));
+}
+template <>
+__device__ __forceinline__ void tile_col4<float>(const float* X, int ld, int r0, int c0,
+                                                 int lane, float (&x)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = X[(r0 + 4 * (lane >> 4) + e) * ld + c0 + (lane & 15)];
+}
+
 // ======================================================= reverse state pass
 template <typename E, int DK, int DVT, int C> struct BStateLds {
     using G = StateCfg<E, DK, DVT, C>;
@@ -520,14 +542,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
                 for (int b = 0; b < BJX; ++b) ax[0][b] = floatx4{0.f, 0.f, 0.f, 0.f};
                 mma_block<E, 1, BJX>(ax, L.K, LDK, 16 * tt, L.Sj, LDK, 16 * jb, 0, DK, lane);
+                // each lane rewrites only the elements of V it read itself
+                const int t4 = 16 * tt + 4 * (lane >> 4);
+                const float4 gm4 = *reinterpret_cast<const float4*>(L.gam + t4);
+                const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
 #pragma unroll
-                for (int b = 0; b < BJX; ++b)
+                for (int b = 0; b < BJX; ++b) {
+                    float vv[4];
+                    tile_col4<E>(L.R, LDJ, 16 * tt, 16 * (jb + b), lane, vv);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 16 * tt + 4 * (lane >> 4) + e;
-                        E* p = L.R + t * LDJ + 16 * (jb + b) + (lane & 15);
-                        *p = from_f<E>(to_f<E>(*p) - L.gam[t] * ax[0][b][e]);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        L.R[(t4 + e) * LDJ + 16 * (jb + b) + (lane & 15)] =
+                            from_f<E>(vv[e] - gm[e] * ax[0][b][e]);
+                }
             }
         }
         sync_lds();
@@ -537,30 +564,33 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             const int job = wave + 8 * x;
             if (job < NXJ) {
                 const int tt = job / NXB, jb = (job % NXB) * BJX;
-                floatx4 au[1][BJX];
+                // formed transposed, U^T = R^T T^T (lane l: j = 4 (l/16) + e, t = l % 16),
+                // so that each lane stores four consecutive j of a row of U
+                floatx4 au[BJX][1];
 #pragma unroll
-                for (int b = 0; b < BJX; ++b) au[0][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-                mma_block<E, 1, BJX, false, true>(au, L.Tt, LDC, 16 * tt, L.R, LDJ, 16 * jb, 0,
+                for (int b = 0; b < BJX; ++b) au[b][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+                mma_block<E, BJX, 1, true, false>(au, L.R, LDJ, 16 * jb, L.Tt, LDC, 16 * tt, 0,
                                                   16 * (tt + 1), lane);
+                const int t = 16 * tt + (lane & 15);
 #pragma unroll
-                for (int b = 0; b < BJX; ++b)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 16 * tt + 4 * (lane >> 4) + e;
-                        L.U[t * LDJ + 16 * (jb + b) + (lane & 15)] = from_f<E>(au[0][b][e]);
-                    }
+                for (int b = 0; b < BJX; ++b) {
+                    const floatx4 uv = au[b][0];
+                    store4<E>(L.U + t * LDJ + 16 * (jb + b) + 4 * (lane >> 4), uv[0], uv[1], uv[2],
+                              uv[3]);
+                }
             }
         }
         sync_lds();
-        // dM += dO U^T, dA' += dR U^T (negated later); dO S, dR S, U dS'
+        // dM^T += U dO^T, dA'^T += U dR^T (dA' negated later), transposed so that a
+        // lane holds four consecutive s of one row t; dO S, dR S, U dS'
 #pragma unroll
         for (int x = 0; x < MPW; ++x) {
             const int job = wave + 8 * x;
             if (job < NMT) {
                 int tt, ss;
                 tri_pair(job, tt, ss);
-                am[x] = mma_tile<E>(am[x], L.dO, LDJ, 16 * tt, L.U, LDJ, 16 * ss, 0, JT, lane);
-                aa[x] = mma_tile<E>(aa[x], L.dR, LDJ, 16 * tt, L.U, LDJ, 16 * ss, 0, JT, lane);
+                am[x] = mma_tile<E>(am[x], L.U, LDJ, 16 * ss, L.dO, LDJ, 16 * tt, 0, JT, lane);
+                aa[x] = mma_tile<E>(aa[x], L.U, LDJ, 16 * ss, L.dR, LDJ, 16 * tt, 0, JT, lane);
             }
         }
 #pragma unroll
@@ -597,6 +627,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         if (job < NQJ) {
             const int tt = job / NKB, ib = (job % NKB) * BKI;
             float wsum = 0.f;
+            // q, k and w at the lane's elements of the tiles
+            float qv[BKI][4], kv[BKI][4], wv[BKI][4];
+#pragma unroll
+            for (int b = 0; b < BKI; ++b) {
+                tile_col4<E>(L.Q, LDK, 16 * tt, 16 * (ib + b), lane, qv[b]);
+                tile_col4<E>(L.K, LDK, 16 * tt, 16 * (ib + b), lane, kv[b]);
+                tile_col4<E>(L.W, LDK, 16 * tt, 16 * (ib + b), lane, wv[b]);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * tt + 4 * (lane >> 4) + e;
@@ -604,13 +642,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                 float row = 0.f, roww = 0.f;
 #pragma unroll
                 for (int b = 0; b < BKI; ++b) {
-                    const int i = 16 * (ib + b) + (lane & 15);
                     aq[x][0][b][e] *= gt;
                     ak[x][0][b][e] *= -gt;
                     aw[x][0][b][e] *= dt;
-                    row += to_f<E>(L.Q[t * LDK + i]) * aq[x][0][b][e] +
-                           to_f<E>(L.K[t * LDK + i]) * ak[x][0][b][e];
-                    roww += to_f<E>(L.W[t * LDK + i]) * aw[x][0][b][e];
+                    row += qv[b][e] * aq[x][0][b][e] + kv[b][e] * ak[x][0][b][e];
+                    roww += wv[b][e] * aw[x][0][b][e];
                 }
                 row = group16_sum(row - roww);
                 roww = group16_sum(roww);
@@ -622,41 +658,45 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             if (lane == 0) L.misc[wave][0] += wsum;
         }
     }
-    // M and A tiles; dM * Gamma and dA * Gamma; decay derivative: for each pair
-    // (t, s) of M (and A), z = dM_ts M_ts adds to token t and subtracts from s
+    // M and A tiles, transposed like dM and dA (lane l: s = 16 ss + 4 (l/16) + e,
+    // t = 16 tt + l % 16); dM * Gamma and dA * Gamma stored as rows t, four
+    // consecutive s per lane; decay derivative: for each pair (t, s) of M (and
+    // A), z = dM_ts M_ts adds to token t and subtracts from s
 #pragma unroll
     for (int x = 0; x < MPW; ++x) {
         const int job = wave + 8 * x;
         if (job < NMT) {
             int tt, ss;
             tri_pair(job, tt, ss);
-            const floatx4 mq = mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, L.Q, LDK, 16 * tt, L.W,
-                                           LDK, 16 * ss, 0, DK, lane);
-            const floatx4 mk = mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, L.K, LDK, 16 * tt, L.W,
-                                           LDK, 16 * ss, 0, DK, lane);
-            const int s = 16 * ss + (lane & 15);
-            const float gs = L.g[s];
-            float col = 0.f, rowz[4];
+            const floatx4 mq = mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, L.W, LDK, 16 * ss, L.Q,
+                                           LDK, 16 * tt, 0, DK, lane);
+            const floatx4 mk = mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, L.W, LDK, 16 * ss, L.K,
+                                           LDK, 16 * tt, 0, DK, lane);
+            const int t = 16 * tt + (lane & 15), s4 = 16 * ss + 4 * (lane >> 4);
+            const float gt = L.g[t];
+            float row = 0.f, colz[4], vm[4], va[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int t = 16 * tt + 4 * (lane >> 4) + e;
-                const float gm = s <= t ? exp2_hw(L.g[t] - gs) : 0.f;
+                const int s = s4 + e;
+                const float gm = s <= t ? exp2_hw(gt - L.g[s]) : 0.f;
                 const float ga = s < t ? gm : 0.f;
                 const float dm = am[x][e], dA = -aa[x][e];
                 const float z = dm * mq[e] * gm + dA * mk[e] * ga;
-                rowz[e] = z;
-                col += z;
-                L.Tt[t * LDC + s] = from_f<E>(dm * gm);
-                L.dAG[t * LDC + s] = from_f<E>(dA * ga);
+                colz[e] = z;
+                row += z;
+                vm[e] = dm * gm;
+                va[e] = dA * ga;
             }
+            store4<E>(L.Tt + t * LDC + s4, vm[0], vm[1], vm[2], vm[3]);
+            store4<E>(L.dAG + t * LDC + s4, va[0], va[1], va[2], va[3]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float zr = group16_sum(rowz[e]);
-                if ((lane & 15) == 0) L.dlg[wave][16 * tt + 4 * (lane >> 4) + e] += zr;
+                const float zc = group16_sum(colz[e]);
+                if ((lane & 15) == 0) L.dlg[wave][s4 + e] -= zc;
             }
-            col += __shfl_xor(col, 16, kWave);
-            col += __shfl_xor(col, 32, kWave);
-            if (lane < 16) L.dlg[wave][s] -= col;
+            row += __shfl_xor(row, 16, kWave);
+            row += __shfl_xor(row, 32, kWave);
+            if (lane < 16) L.dlg[wave][t] += row;
         }
     }
     sync_lds();
@@ -675,6 +715,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                                              16 * tt, C, lane);
             mma_block<E, 1, BKI, true, true>(aw[x], L.dAG, LDC, 16 * tt, L.K, LDK, 16 * ib,
                                              16 * tt, C, lane);
+            float wv[BKI][4];
+#pragma unroll
+            for (int b = 0; b < BKI; ++b)
+                tile_col4<E>(L.W, LDK, 16 * tt, 16 * (ib + b), lane, wv[b]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * tt + 4 * (lane >> 4) + e;
@@ -684,7 +728,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                     const int i = 16 * (ib + b) + (lane & 15);
                     // s_t from the unrounded dW (dW itself is stored in the input dtype)
                     const E dw = from_f<E>(aw[x][0][b][e]);
-                    sd += aw[x][0][b][e] * to_f<E>(L.W[t * LDK + i]);
+                    sd += aw[x][0][b][e] * wv[b][e];
                     if (t < n) {
                         const size_t o = (row0 + t) * DK + i;
                         dq[o] = aq[x][0][b][e];
