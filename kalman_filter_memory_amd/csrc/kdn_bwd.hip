@@ -298,27 +298,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                 }
             }
         }
+        // M tiles formed transposed (lane l: s = 16 ss + 4 (l/16) + e, t = 16 tt +
+        // l % 16), so that each lane stores four consecutive s of a row t
 #pragma unroll
         for (int x = 0; x < MPW; ++x) {
             const int job = wave + 8 * x;
             if (job < NMT) {
                 int tt, ss;
                 tri_pair(job, tt, ss);
-                const floatx4 m = mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, L.Q, LDK, 16 * tt, L.W,
-                                              LDK, 16 * ss, 0, DK, lane);
-                const int s = 16 * ss + (lane & 15);
-                const float gs = L.g[s];
+                const floatx4 m = mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, L.W, LDK, 16 * ss, L.Q,
+                                              LDK, 16 * tt, 0, DK, lane);
+                const int t = 16 * tt + (lane & 15), s4 = 16 * ss + 4 * (lane >> 4);
+                const float gt = L.g[t];
+                float val[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * tt + 4 * (lane >> 4) + e;
-                    const float val = s <= t ? m[e] * exp2_hw(L.g[t] - gs) : 0.f;
-                    L.M[t * LDC + s] = from_f<E>(val);
-                }
+                for (int e = 0; e < 4; ++e)
+                    val[e] = s4 + e <= t ? m[e] * exp2_hw(gt - L.g[s4 + e]) : 0.f;
+                store4<E>(L.M + t * LDC + s4, val[0], val[1], val[2], val[3]);
             }
         }
-        for (int e = tid; e < C * DVT; e += kBThreads) {
-            const int t = e / DVT, j = e % DVT;
-            L.dOg[j * LDC + t] = from_f<E>(L.gam[t] * to_f<E>(L.dO[t * LDV + j]));
+        // gamma_t dO[t][j] as [j][t]: per 16 x 16 tile, each lane reads four t of
+        // a column j (one transposing read) and stores them as part of row j
+#pragma unroll
+        for (int x = 0; x < (NT * NV + 7) / 8; ++x) {
+            const int job = wave + 8 * x;
+            if (job < NT * NV) {
+                const int tt = job / NV, jj = job % NV;
+                float dv4[4];
+                tile_col4<E>(L.dO, LDV, 16 * tt, 16 * jj, lane, dv4);
+                const int t4 = 16 * tt + 4 * (lane >> 4);
+                const float4 gm = *reinterpret_cast<const float4*>(L.gam + t4);
+                store4<E>(L.dOg + (16 * jj + (lane & 15)) * LDC + t4, gm.x * dv4[0],
+                          gm.y * dv4[1], gm.z * dv4[2], gm.w * dv4[3]);
+            }
         }
         sync_lds();
         // 2: dU += M^T dO  (M[t][s] = 0 for t < s)
