@@ -811,6 +811,7 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
     const size_t tk = row0 + min(lane, n - 1);
     const float ta = to_f<G>(a[tk]), tnu = to_f<G>(nu[tk]), tr = to_f<G>(r[tk]);
     const float tir = 1.f / tr, tdi = dinv[tk], tsd = sdot[tk];
+    const float tia = 1.f / ta;  // one division per token, not per (token, dimension)
     // forward: P^- of every token from the chunk-boundary precision
     float P = 1.f / lam_chunk[(bh * (NC + 1) + c) * DK + ic];
     float pms[C];  // P^- of every token (both walks fully unrolled: static indices)
@@ -857,8 +858,9 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
                 const float sdt = lane_value(tsd, t);
                 const float kv = kg[h], pm = pms[t];
                 const float b = kv * kv * irt;
-                const float Pt = pm * rcp(fmaf(b, pm, 1.f));
-                const float rat = Pt * rcp(pm), c2 = rat * rat;
+                // P / P^- = 1 / (1 + b P^-): one reciprocal for both
+                const float rat = rcp(fmaf(b, pm, 1.f)), c2 = rat * rat;
+                const float Pt = pm * rat;
                 const float gainP = kv * dit * (dwg[h] - kv * sdt);
                 if constexpr (APPLY) {
                     const float H = fmaf(c2, Gv, gainP);
@@ -866,7 +868,7 @@ __global__ __launch_bounds__(DK < 64 ? 64 : DK) void bgain_kernel(
                     dkg[h] += pm * dit * (dwg[h] - 2.f * kv * sdt) + db * 2.f * kv * irt;
                     if (act) {
                         hv[h] = H;
-                        ha[h] = 2.f * (pm - nut) * H / at;
+                        ha[h] = 2.f * (pm - nut) * H * lane_value(tia, t);
                         hr[h] = -db * b * irt;
                     }
                     Gv = at * at * H;
