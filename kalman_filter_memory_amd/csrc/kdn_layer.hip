@@ -267,6 +267,21 @@ rocblas_status gemm_rows(rocblas_handle h, int M, int N, int K, const void* X, i
                            0, 0);
 }
 
+// The same product with the columns split at the last multiple of 128: the
+// library's kernels run the aligned block faster on its own than the whole
+// product with a ragged edge (at the layer shape the 48 gate columns after the
+// 6,144 q, k, v columns: 0.69 + 0.02 ms against 0.75 ms).
+template <typename E>
+rocblas_status gemm_rows_split(rocblas_handle h, int M, int N, int K, const void* X, int ldx,
+                               const void* W, int ldw, void* Y, int ldy) {
+    const int N1 = N / 128 * 128;
+    if (N1 == 0 || N1 == N) return gemm_rows<E>(h, M, N, K, X, ldx, W, ldw, Y, ldy);
+    const rocblas_status s = gemm_rows<E>(h, M, N1, K, X, ldx, W, ldw, Y, ldy);
+    if (s != rocblas_status_success) return s;
+    return gemm_rows<E>(h, M, N - N1, K, X, ldx, static_cast<const E*>(W) + N1, ldw,
+                        static_cast<E*>(Y) + N1, ldy);
+}
+
 template <typename E>
 kdn_status layer_forward_t(const kdn_layer_desc* d, rocblas_handle hb, const void* x,
                            const void* W_in, const float* b_gate, const void* W_out,
@@ -283,7 +298,8 @@ kdn_status layer_forward_t(const kdn_layer_desc* d, rocblas_handle hb, const voi
     void *q = at(ws, w.q), *k = at(ws, w.k), *v = at(ws, w.v);
     void *a = at(ws, w.a), *nu = at(ws, w.nu), *r = at(ws, w.r), *o = at(ws, w.o);
     if (!mark(0)) return KDN_ERR_HIP;
-    kdn_status s = blas_status(gemm_rows<E>(hb, M, n_in(d), D, x, D, W_in, n_in(d), Z, w.ldz));
+    kdn_status s =
+        blas_status(gemm_rows_split<E>(hb, M, n_in(d), D, x, D, W_in, n_in(d), Z, w.ldz));
     if (s != KDN_OK || !mark(1) || !mark(2)) return s != KDN_OK ? s : KDN_ERR_HIP;
     if (launch_in<E>(dk, dv, Z, w.ldz, b_gate, M, H, d->T, q, k, v, a, nu, r, st) != hipSuccess)
         return KDN_ERR_HIP;
