@@ -259,6 +259,24 @@ def bench_forward(args, inp, variant, steps, cold_reps, label):
         cold_us.append(a0.elapsed_time(a1) * 1e3)
     del flush
 
+    # the same step captured once in a HIP graph and replayed back to back
+    # (the library launches kernels only, so the graph holds the forward's
+    # kernels and nothing else)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    g0, g1 = TimingEvent(), TimingEvent()
+    g0.record()
+    for _ in range(steps):
+        g.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / steps
+    del g
+
     # per-kernel durations as they run in the forward: the forward's kernels
     # 0..i back to back, REPS passes between two events (kdn_forward_repeat on
     # the workspace the steps above left), and kernel i's time the difference
@@ -322,6 +340,10 @@ def bench_forward(args, inp, variant, steps, cold_reps, label):
            "variant": variant, "ms_per_step": round(ms, 4),
            "tokens/s": round(B * T / (ms * 1e-3), 1),
            "step_us_warm": _stats(warm_us), "step_us_cold": _stats(cold_us),
+           "graph": {"ms_per_step": round(graph_ms, 4),
+                     "tokens/s": round(B * T / (graph_ms * 1e-3), 1), "replays": steps,
+                     "what": "the step captured once in a HIP graph (torch.cuda.graph around "
+                             "the binding), replayed back to back between two HIP events"},
            "roofline": roofline, "mfma_chunk": mfma,
            "scan_hbm": {"kernels": "scan_reduce+scan_carry", "us": round(scan_s * 1e6, 2),
                         "bytes": scan_by, "GB/s": round(scan_by / scan_s / 1e9, 1),
@@ -386,6 +408,7 @@ def run(args):
                    "chunk": args.chunk, "state_dtype": "f32"},
         "roofline": roofline,
         "step_us_warm": head["step_us_warm"], "step_us_cold": head["step_us_cold"],
+        "graph": head["graph"],
         "mfma_chunk": head["mfma_chunk"],
         "scan_hbm": head["scan_hbm"],
         "kernels": head["kernels"],
