@@ -666,7 +666,7 @@ LAYER_STAGES = ("gemm_in", "norm_gates", "recurrence", "readout_rows", "gemm_out
 
 
 def bench_layer(args):
-    """The KDN layer on random weights (kdn_layer_forward): input GEMM (rocBLAS),
+    """The KDN layer on random weights (kdn_layer_forward): input GEMM (hipBLASLt),
     normalisation and gates, the recurrence, the read-out to token rows, output
     GEMM; per-stage times from events recorded between the stages."""
     import numpy as np
@@ -680,7 +680,10 @@ def bench_layer(args):
     log("generating layer inputs")
     p = layer_inputs(B, T, H, D, dk, dv, dtype="bf16", seed=1003)
     bf = torch.bfloat16
-    t = {n: torch.from_numpy(p[n]).to(dev, bf) for n in ("x", "W_in", "W_out")}
+    # the library takes the weights out-features major (y = x W^T)
+    t = {"x": torch.from_numpy(p["x"]).to(dev, bf)}
+    t.update({n: torch.from_numpy(np.ascontiguousarray(p[n].T)).to(dev, bf)
+              for n in ("W_in", "W_out")})
     t.update({n: torch.from_numpy(p[n]).to(dev) for n in ("b_gate", "lambda0", "S0")})
     d = kdn.make_layer_desc(B, T, H, D, dk, dv, C, "diagonal", kdn.BF16)
     ws = torch.empty(kdn.layer_workspace_bytes(d), dtype=torch.uint8, device=dev)
@@ -726,7 +729,7 @@ def bench_layer(args):
             stages[k].update({"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
     return {"workload": f"layer_diag_bf16_B{B}_T{T}_H{H}_D{D}_d{dk}", "ms_per_step": round(ms, 4),
             "tokens/s": round(M / (ms * 1e-3), 1), "stages": stages,
-            "gemm": "rocBLAS gemm_ex, bf16 in and out, fp32 accumulation",
+            "gemm": "hipBLASLt matmul, weights out-features major (x W^T), bf16 in and out, fp32 accumulation",
             "weights": "random (kdn_inputs.layer_inputs), no trained checkpoint"}
 
 

@@ -237,27 +237,30 @@ kdn_status kdn_dense_gain(const kdn_desc *d, const void *k, const void *a, const
  * The KDN layer around the recurrence, on caller-given weights ("Kalman Delta
  * Networks", English abstract: a drop-in replacement for linear attention;
  * KDN summary, 关键模块: queries, keys, values and the gates a, nu, r):
- *   Z = x W_in, with the columns of W_in [d_model, H(2 d_k + d_v) + 3H] in the
- *       order q (head-major), k, v, then the logits of a, nu and r (H each);
+ *   Z = x W_in^T, with W_in [H(2 d_k + d_v) + 3H, d_model] stored out-features
+ *       major (row i of W_in gives column i of Z), the rows in the order q
+ *       (head-major), k, v, then the logits of a, nu and r (H each);
  *   q_h, k_h divided by max(|q_h|, 1e-6) and max(|k_h|, 1e-6);
  *   a = sigmoid(z_a + b_a), nu = softplus(z_nu + b_nu), r = softplus(z_r + b_r),
  *       b_gate [3H] float32 in the same order;
  *   o = kdn_forward(q, k, v, a, nu, r, lambda0, S0) over B*H heads;
- *   y = [o_1 .. o_H] W_out, W_out [H d_v, d_model].
+ *   y = [o_1 .. o_H] W_out^T, W_out [d_model, H d_v] (out-features major).
  * x [B, T, d_model] and y [B, T, d_model] are token rows.  Every tensor but
  * b_gate, lambda0, S0, S_T and lambda_T is in `dtype`; the GEMMs accumulate in
- * float32 and round their outputs to dtype.  The two GEMMs run in rocBLAS on a
- * handle from kdn_blas_create; the rest in this library's kernels. */
+ * float32 and round their outputs to dtype.  The two GEMMs run in hipBLASLt on
+ * a handle from kdn_blas_create; the rest in this library's kernels. */
 typedef struct {
     int32_t B, T, H, d_model, d_k, d_v, chunk;
     int32_t variant; /* kdn_variant of the recurrence */
     int32_t dtype;   /* kdn_dtype of x, the weights, y and every activation */
 } kdn_layer_desc;
 
-/* A rocBLAS handle for kdn_layer_forward (atomics off, so that results do not
- * depend on the run).  Creating it allocates (inside rocBLAS); the caller owns
- * it, creates it once and frees it with kdn_blas_destroy.  A handle serves one
- * call at a time; each call sets its stream. */
+/* A hipBLASLt context for kdn_layer_forward: the library handle and the GEMM
+ * algorithm chosen per shape (hipBLASLt's first heuristic choice within a
+ * 32 MiB workspace, which is part of the layer workspace; chosen on the first
+ * call with a shape and kept).  Creating it allocates (inside hipBLASLt); the
+ * caller owns it, creates it once and frees it with kdn_blas_destroy.  A
+ * context serves one call at a time; each call runs on its own stream. */
 kdn_status kdn_blas_create(void **handle);
 kdn_status kdn_blas_destroy(void *handle);
 

@@ -341,7 +341,7 @@ _blas = None
 
 
 def blas_handle():
-    """This process's rocBLAS handle for the layer's GEMMs (created on first use,
+    """This process's hipBLASLt context for the layer's GEMMs (created on first use,
     freed at exit)."""
     global _blas
     if _blas is None:
@@ -368,8 +368,9 @@ def layer_workspace_bytes(d: KdnLayerDesc) -> int:
 def layer_forward(x, W_in, b_gate, W_out, H, d_k, d_v, lambda0=None, S0=None,
                   variant="diagonal", chunk=64, workspace=None, events=None):
     """KDN layer on given weights (kdn_layer_forward): x [B,T,D] -> y [B,T,D].
-    W_in [D, H(2 d_k + d_v) + 3H], b_gate float32 [3H], W_out [H d_v, D], all
-    but b_gate in x's dtype.  Returns (y, S_T, lambda_T).  events: optional 10
+    W_in [H(2 d_k + d_v) + 3H, D] and W_out [D, H d_v], out-features major (a
+    linear layer's weight layout: y = x W^T), b_gate float32 [3H]; all but
+    b_gate in x's dtype.  Returns (y, S_T, lambda_T).  events: optional 10
     torch.cuda.Event around the five stages."""
     lib = load_library()
     for n, t in (("x", x), ("W_in", W_in), ("b_gate", b_gate), ("W_out", W_out)):
@@ -377,10 +378,10 @@ def layer_forward(x, W_in, b_gate, W_out, H, d_k, d_v, lambda0=None, S0=None,
     B, T, D = x.shape
     code = _dtype_code(x.dtype)
     n_in = H * (2 * d_k + d_v) + 3 * H
-    if W_in.dtype != x.dtype or tuple(W_in.shape) != (D, n_in):
-        raise ValueError(f"W_in must be {x.dtype} [{D}, {n_in}]")
-    if W_out.dtype != x.dtype or tuple(W_out.shape) != (H * d_v, D):
-        raise ValueError(f"W_out must be {x.dtype} [{H * d_v}, {D}]")
+    if W_in.dtype != x.dtype or tuple(W_in.shape) != (n_in, D):
+        raise ValueError(f"W_in must be {x.dtype} [{n_in}, {D}] (out-features major)")
+    if W_out.dtype != x.dtype or tuple(W_out.shape) != (D, H * d_v):
+        raise ValueError(f"W_out must be {x.dtype} [{D}, {H * d_v}] (out-features major)")
     if b_gate.dtype != torch.float32 or tuple(b_gate.shape) != (3 * H,):
         raise ValueError(f"b_gate must be float32 [{3 * H}]")
     d = make_layer_desc(B, T, H, D, d_k, d_v, chunk, variant, code)

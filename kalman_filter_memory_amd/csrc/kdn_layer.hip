@@ -3,21 +3,27 @@
 // drop-in replacement for linear attention in a language model; KDN summary,
 // 关键模块: the layer's queries, keys, values and its three gates a, nu, r).
 //
-//   Z = x W_in                      (one library GEMM: q, k, v and the gate logits)
+//   Z = x W_in^T                    (one library GEMM: q, k, v and the gate logits)
 //   q_h, k_h = L2-normalised per head; v_h as is
 //   a = sigmoid(z_a + b_a), nu = softplus(z_nu + b_nu), r = softplus(z_r + b_r)
 //   o = KDN forward (kdn_forward)
-//   y = concat_h(o_h) W_out         (one library GEMM)
+//   y = concat_h(o_h) W_out^T       (one library GEMM)
 //
-// The two GEMMs are plain dense products and run in rocBLAS (fp32
-// accumulation).  The normalisation, the gate activations and the change of
-// layout from token rows [B*T, .] to the recurrence's per-head rows
+// The weights are stored out-features major (W_in [n_in][d_model], W_out
+// [d_model][H d_v], a linear layer's usual layout), so both GEMMs contract
+// two operands that are contiguous along the reduction index; they run in
+// hipBLASLt (fp32 accumulation), whose kernels for that layout are the fastest
+// on this GPU (1.43-1.45 PFLOP/s at the layer shape against 1.16-1.21 for the
+// input-major weight layout).  The normalisation, the gate activations and the
+// change of layout from token rows [B*T, .] to the recurrence's per-head rows
 // [B, H, T, .] are one pass (layer_in_kernel); the read-out goes back to token
 // rows in another (layer_out_kernel).  Both are HBM-bound copies with 16-byte
 // accesses.
-#include <rocblas/rocblas.h>
+#include <hipblaslt/hipblaslt.h>
 
 #include <algorithm>
+#include <mutex>
+#include <new>
 
 #include "kdn.h"
 #include "kdn_device.h"
@@ -29,11 +35,30 @@ using kdn::bf16_t;
 template <typename E> struct Io;
 template <> struct Io<float> {
     static constexpr int code = KDN_F32;
-    static constexpr rocblas_datatype blas = rocblas_datatype_f32_r;
+    static constexpr hipDataType blas = HIP_R_32F;
 };
 template <> struct Io<bf16_t> {
     static constexpr int code = KDN_BF16;
-    static constexpr rocblas_datatype blas = rocblas_datatype_bf16_r;
+    static constexpr hipDataType blas = HIP_R_16BF;
+};
+
+// Device workspace of a GEMM, a slice of the layer workspace (the library
+// allocates nothing per call); algorithms needing more are not chosen.
+constexpr size_t kGemmWs = size_t(32) << 20;
+
+// What kdn_blas_create returns: a hipBLASLt handle and the algorithm chosen
+// for each GEMM shape seen so far (the heuristic query runs on the host once
+// per shape, not per call).
+struct BlasCtx {
+    hipblasLtHandle_t lt = nullptr;
+    std::mutex mu;
+    struct Entry {
+        int M, N, K, ldx, ldw, ldy;
+        hipDataType type;
+        hipblasLtMatmulAlgo_t algo;
+    };
+    Entry cache[16];
+    int n = 0;
 };
 
 // N contiguous elements of E at p (16-byte aligned when N * sizeof(E) >= 16,
@@ -189,7 +214,7 @@ hipError_t launch_out(int dv, const void* o, void* o2, int M, int H, int T, hipS
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct LayerWs {
-    size_t z, q, k, v, a, nu, r, o, core, total;
+    size_t z, q, k, v, a, nu, r, o, gemm, core, total;
     int ldz;
 };
 
@@ -230,6 +255,7 @@ LayerWs layer_ws(const kdn_layer_desc* d) {
     w.nu = take(BH * d->T * es);
     w.r = take(BH * d->T * es);
     w.o = take(BH * d->T * d->d_v * es);
+    w.gemm = take(kGemmWs);
     const kdn_desc c = core_desc(d);
     w.core = take(kdn_forward_workspace_bytes(&c));
     w.total = off;
@@ -243,7 +269,7 @@ kdn_status check_layer(const kdn_layer_desc* d) {
     // every row of the GEMM operands starts 16-byte aligned
     if (d->d_model % 8 != 0 || d->d_model == 0) return KDN_ERR_UNSUPPORTED;
     if (3 * d->H > 256) return KDN_ERR_UNSUPPORTED;  // gate threads of layer_in_kernel
-    // token rows index grid.x and rocBLAS's 32-bit sizes
+    // token rows index grid.x and 32-bit GEMM sizes
     if (int64_t(d->B) * d->T > INT32_MAX) return KDN_ERR_UNSUPPORTED;
     if (int64_t(d->H) * (2 * d->d_k + d->d_v + 3) > INT32_MAX / 16) return KDN_ERR_UNSUPPORTED;
     const kdn_desc c = core_desc(d);
@@ -254,36 +280,96 @@ char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-kdn_status blas_status(rocblas_status s) { return s == rocblas_status_success ? KDN_OK : KDN_ERR_HIP; }
+// The descriptors of one product (destroyed with the object)
+struct GemmDescs {
+    hipblasLtMatmulDesc_t op = nullptr;
+    hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
+    ~GemmDescs() {
+        if (c) hipblasLtMatrixLayoutDestroy(c);
+        if (b) hipblasLtMatrixLayoutDestroy(b);
+        if (a) hipblasLtMatrixLayoutDestroy(a);
+        if (op) hipblasLtMatmulDescDestroy(op);
+    }
+};
 
-// row-major Y[M,N] = X[M,K] W[K,N] as the column-major product Y^T = W^T X^T
+// row-major Y[M,N] = X[M,K] W^T, with W [N,K] row-major: in hipBLASLt's
+// column-major terms Y^T (N x M, ld ldy) = op(A) B, A = W read as K x N (ld
+// ldw) and transposed, B = X read as K x M (ld ldx): both operands contiguous
+// along K.  The algorithm is hipBLASLt's first heuristic choice for the shape
+// within kGemmWs of workspace, cached in the context.
 template <typename E>
-rocblas_status gemm_rows(rocblas_handle h, int M, int N, int K, const void* X, int ldx,
-                         const void* W, int ldw, void* Y, int ldy) {
+kdn_status gemm_rows(BlasCtx* bc, int M, int N, int K, const void* X, int ldx, const void* W,
+                     int ldw, void* Y, int ldy, void* gws, hipStream_t st) {
+    const hipDataType ty = Io<E>::blas;
+    GemmDescs g;
+    const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+    if (hipblasLtMatmulDescCreate(&g.op, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatmulDescSetAttribute(g.op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) !=
+            HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatmulDescSetAttribute(g.op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) !=
+            HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&g.a, ty, K, N, ldw) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&g.b, ty, K, M, ldx) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&g.c, ty, N, M, ldy) != HIPBLAS_STATUS_SUCCESS)
+        return KDN_ERR_HIP;
+    hipblasLtMatmulAlgo_t algo;
+    {
+        std::lock_guard<std::mutex> lock(bc->mu);
+        int found = -1;
+        for (int i = 0; i < bc->n; ++i) {
+            const BlasCtx::Entry& e = bc->cache[i];
+            if (e.M == M && e.N == N && e.K == K && e.ldx == ldx && e.ldw == ldw &&
+                e.ldy == ldy && e.type == ty) {
+                found = i;
+                break;
+            }
+        }
+        if (found >= 0) {
+            algo = bc->cache[found].algo;
+        } else {
+            hipblasLtMatmulPreference_t pref = nullptr;
+            if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS)
+                return KDN_ERR_HIP;
+            const uint64_t cap = kGemmWs;
+            hipblasLtMatmulHeuristicResult_t res[1];
+            int got = 0;
+            const bool ok =
+                hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
+                                                      &cap, sizeof(cap)) == HIPBLAS_STATUS_SUCCESS &&
+                hipblasLtMatmulAlgoGetHeuristic(bc->lt, g.op, g.a, g.b, g.c, g.c, pref, 1, res,
+                                                &got) == HIPBLAS_STATUS_SUCCESS &&
+                got > 0 && res[0].state == HIPBLAS_STATUS_SUCCESS && res[0].workspaceSize <= cap;
+            hipblasLtMatmulPreferenceDestroy(pref);
+            if (!ok) return KDN_ERR_HIP;
+            algo = res[0].algo;
+            const int slot = bc->n < 16 ? bc->n++ : 15;  // (a layer uses three shapes)
+            bc->cache[slot] = {M, N, K, ldx, ldw, ldy, ty, algo};
+        }
+    }
     const float one = 1.f, zero = 0.f;
-    return rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, N, M, K, &one, W,
-                           Io<E>::blas, ldw, X, Io<E>::blas, ldx, &zero, Y, Io<E>::blas, ldy, Y,
-                           Io<E>::blas, ldy, rocblas_datatype_f32_r, rocblas_gemm_algo_standard,
-                           0, 0);
+    return hipblasLtMatmul(bc->lt, g.op, &one, W, g.a, X, g.b, &zero, Y, g.c, Y, g.c, &algo, gws,
+                           kGemmWs, st) == HIPBLAS_STATUS_SUCCESS
+               ? KDN_OK
+               : KDN_ERR_HIP;
 }
 
-// The same product with the columns split at the last multiple of 128: the
-// library's kernels run the aligned block faster on its own than the whole
-// product with a ragged edge (at the layer shape the 48 gate columns after the
-// 6,144 q, k, v columns: 0.69 + 0.02 ms against 0.75 ms).
+// The same product with the output columns split at the last multiple of 128:
+// the aligned block and the ragged rest as two products (at the layer shape
+// the 48 gate columns after the 6,144 q, k, v columns).  W's rows are the
+// output columns, so the second product starts N1 rows into W.
 template <typename E>
-rocblas_status gemm_rows_split(rocblas_handle h, int M, int N, int K, const void* X, int ldx,
-                               const void* W, int ldw, void* Y, int ldy) {
+kdn_status gemm_rows_split(BlasCtx* bc, int M, int N, int K, const void* X, int ldx,
+                           const void* W, int ldw, void* Y, int ldy, void* gws, hipStream_t st) {
     const int N1 = N / 128 * 128;
-    if (N1 == 0 || N1 == N) return gemm_rows<E>(h, M, N, K, X, ldx, W, ldw, Y, ldy);
-    const rocblas_status s = gemm_rows<E>(h, M, N1, K, X, ldx, W, ldw, Y, ldy);
-    if (s != rocblas_status_success) return s;
-    return gemm_rows<E>(h, M, N - N1, K, X, ldx, static_cast<const E*>(W) + N1, ldw,
-                        static_cast<E*>(Y) + N1, ldy);
+    if (N1 == 0 || N1 == N) return gemm_rows<E>(bc, M, N, K, X, ldx, W, ldw, Y, ldy, gws, st);
+    const kdn_status s = gemm_rows<E>(bc, M, N1, K, X, ldx, W, ldw, Y, ldy, gws, st);
+    if (s != KDN_OK) return s;
+    return gemm_rows<E>(bc, M, N - N1, K, X, ldx, static_cast<const E*>(W) + size_t(N1) * ldw,
+                        ldw, static_cast<E*>(Y) + N1, ldy, gws, st);
 }
 
 template <typename E>
-kdn_status layer_forward_t(const kdn_layer_desc* d, rocblas_handle hb, const void* x,
+kdn_status layer_forward_t(const kdn_layer_desc* d, BlasCtx* hb, const void* x,
                            const void* W_in, const float* b_gate, const void* W_out,
                            const float* lambda0, const float* S0, void* y, float* S_T,
                            float* lambda_T, void* ws, const LayerWs& w, hipStream_t st,
@@ -293,13 +379,12 @@ kdn_status layer_forward_t(const kdn_layer_desc* d, rocblas_handle hb, const voi
         return !events || !events[i] ||
                hipEventRecord(static_cast<hipEvent_t>(events[i]), st) == hipSuccess;
     };
-    if (rocblas_set_stream(hb, st) != rocblas_status_success) return KDN_ERR_HIP;
     void* Z = at(ws, w.z);
+    void* gws = at(ws, w.gemm);
     void *q = at(ws, w.q), *k = at(ws, w.k), *v = at(ws, w.v);
     void *a = at(ws, w.a), *nu = at(ws, w.nu), *r = at(ws, w.r), *o = at(ws, w.o);
     if (!mark(0)) return KDN_ERR_HIP;
-    kdn_status s =
-        blas_status(gemm_rows_split<E>(hb, M, n_in(d), D, x, D, W_in, n_in(d), Z, w.ldz));
+    kdn_status s = gemm_rows_split<E>(hb, M, n_in(d), D, x, D, W_in, D, Z, w.ldz, gws, st);
     if (s != KDN_OK || !mark(1) || !mark(2)) return s != KDN_OK ? s : KDN_ERR_HIP;
     if (launch_in<E>(dk, dv, Z, w.ldz, b_gate, M, H, d->T, q, k, v, a, nu, r, st) != hipSuccess)
         return KDN_ERR_HIP;
@@ -311,7 +396,7 @@ kdn_status layer_forward_t(const kdn_layer_desc* d, rocblas_handle hb, const voi
     if (!mark(5) || !mark(6)) return KDN_ERR_HIP;
     if (launch_out<E>(dv, o, Z, M, H, d->T, st) != hipSuccess) return KDN_ERR_HIP;
     if (!mark(7) || !mark(8)) return KDN_ERR_HIP;
-    s = blas_status(gemm_rows<E>(hb, M, D, H * dv, Z, H * dv, W_out, D, y, D));
+    s = gemm_rows<E>(hb, M, D, H * dv, Z, H * dv, W_out, H * dv, y, D, gws, st);
     if (s != KDN_OK || !mark(9)) return s != KDN_OK ? s : KDN_ERR_HIP;
     return KDN_OK;
 }
@@ -322,20 +407,22 @@ extern "C" {
 
 kdn_status kdn_blas_create(void** handle) {
     if (!handle) return KDN_ERR_NULL;
-    rocblas_handle h = nullptr;
-    if (rocblas_create_handle(&h) != rocblas_status_success) return KDN_ERR_HIP;
-    // a GEMM's result must not depend on the run
-    if (rocblas_set_atomics_mode(h, rocblas_atomics_not_allowed) != rocblas_status_success) {
-        rocblas_destroy_handle(h);
+    BlasCtx* bc = new (std::nothrow) BlasCtx;
+    if (!bc) return KDN_ERR_HIP;
+    if (hipblasLtCreate(&bc->lt) != HIPBLAS_STATUS_SUCCESS) {
+        delete bc;
         return KDN_ERR_HIP;
     }
-    *handle = h;
+    *handle = bc;
     return KDN_OK;
 }
 
 kdn_status kdn_blas_destroy(void* handle) {
     if (!handle) return KDN_OK;
-    return blas_status(rocblas_destroy_handle(static_cast<rocblas_handle>(handle)));
+    BlasCtx* bc = static_cast<BlasCtx*>(handle);
+    const bool ok = hipblasLtDestroy(bc->lt) == HIPBLAS_STATUS_SUCCESS;
+    delete bc;
+    return ok ? KDN_OK : KDN_ERR_HIP;
 }
 
 size_t kdn_layer_workspace_bytes(const kdn_layer_desc* d) {
@@ -366,7 +453,7 @@ kdn_status kdn_layer_forward_events(const kdn_layer_desc* d, void* blas, const v
     for (const void* p : {x, W_in, W_out, (const void*)y, (const void*)ws})
         if (!aligned16(p)) return KDN_ERR_ALIGN;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    rocblas_handle hb = static_cast<rocblas_handle>(blas);
+    BlasCtx* hb = static_cast<BlasCtx*>(blas);
     return d->dtype == KDN_BF16
                ? layer_forward_t<bf16_t>(d, hb, x, W_in, b_gate, W_out, lambda0, S0, y, S_T,
                                          lambda_T, ws, w, hs, events)

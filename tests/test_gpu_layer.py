@@ -21,8 +21,13 @@ TOL_LAYER_BF16 = 3e-2
 
 
 def _tensors(p):
+    """Device copies of the layer inputs.  The oracle takes the weights
+    input-features major (Z = x W_in); the library takes them out-features
+    major (Z = x W_in^T), so they go to the GPU transposed."""
     dt = torch.bfloat16 if p["dtype"] == "bf16" else torch.float32
-    t = {n: torch.from_numpy(p[n]).cuda().to(dt) for n in ("x", "W_in", "W_out")}
+    t = {"x": torch.from_numpy(p["x"]).cuda().to(dt)}
+    t.update({n: torch.from_numpy(np.ascontiguousarray(p[n].T)).cuda().to(dt)
+              for n in ("W_in", "W_out")})
     t.update({n: torch.from_numpy(p[n]).cuda() for n in ("b_gate", "lambda0", "S0")})
     return t
 
