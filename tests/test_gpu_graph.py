@@ -4,8 +4,11 @@ stream there) and replayed: every replay equals the eager call bit for bit
 (same kernels, same inputs), with eager work and synchronisations of the
 program's own between the replays.  The library records nothing but kernel
 launches (no memsets, allocations or synchronisations), so a captured forward
-is its four kernels (six with the segmented state pass)."""
+is its four kernels (six with the segmented state pass); the backward and
+the layer (whose GEMMs hipBLASLt records) are captured the same way."""
 from __future__ import annotations
+
+import ctypes
 
 import numpy as np
 import pytest
@@ -14,7 +17,7 @@ import torch
 import kalman_filter_memory_amd as kdn
 import oracle
 from gpu_util import TOL_BF16, TOL_LAMBDA, forward_tensors, host, normwise, say
-from kdn_inputs import decode_inputs, forward_inputs
+from kdn_inputs import decode_inputs, forward_inputs, layer_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -119,3 +122,63 @@ def test_decode_graph_replays_equal_eager_steps():
         torch.cuda.synchronize()
         assert torch.equal(o_g, eager_o[s]), f"step {s}: o differs from the eager step"
     assert torch.equal(S_g, S_e) and torch.equal(lam_g, lam_e)
+
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+def test_backward_graph_replays_equal_eager(variant):
+    """The backward (recompute and the three gradient stages) captured and
+    replayed: every gradient equals the eager call's bit for bit."""
+    B, H, T, dk, dv = 2, 2, 300, 128, 64
+    inp = forward_inputs(B, H, T, dk, dv, variant=variant, dtype="bf16", seed=914)
+    say(f"[gpu] graph backward: {variant} B{B} H{H} T{T} d_k {dk} d_v {dv}")
+    t = forward_tensors(inp)
+    gen = torch.Generator(device="cpu").manual_seed(915)
+    dO = torch.randn((B, H, T, dv), generator=gen).cuda().to(torch.bfloat16)
+    args = (t["q"], t["k"], t["v"], t["a"], t["nu"], t["r"], dO)
+    kw = dict(lambda0=t["lambda0"], S0=t["S0"], variant=variant, chunk=64)
+    ref = kdn.backward(*args, **kw)
+    torch.cuda.synchronize()
+    d = kdn.make_desc(B, H, T, dk, dv, 64, variant, kdn.BF16, kdn.BF16)
+    lib = kdn.load_library()
+    ws = torch.empty(lib.kdn_backward_workspace_bytes(ctypes.byref(d)), dtype=torch.uint8,
+                     device="cuda")
+    out = {n: torch.empty_like(x) for n, x in ref.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kdn.backward(*args, **kw, workspace=ws, out=out)
+    for i in range(REPLAYS):
+        for x in out.values():
+            x.fill_(float("nan"))
+        g.replay()
+        kdn.backward(*args, **kw)  # eager work between the replays
+        torch.cuda.synchronize()
+        for n in ref:
+            assert torch.equal(out[n], ref[n]), f"replay {i}: {n} differs from the eager call"
+
+
+def test_layer_graph_replays_equal_eager():
+    """The layer (two hipBLASLt GEMMs around the library's kernels) captured
+    after one eager call with the same shapes (which chooses and keeps the
+    GEMM algorithms) and replayed: y, S_T and lambda_T equal the eager call's."""
+    p = layer_inputs(1, 200, 2, 128, 64, 64, dtype="bf16", seed=916)
+    say("[gpu] graph layer: B1 T200 H2 D128 d 64 bf16")
+    bf = torch.bfloat16
+    x = torch.from_numpy(p["x"]).cuda().to(bf)
+    W_in = torch.from_numpy(np.ascontiguousarray(p["W_in"].T)).cuda().to(bf)
+    W_out = torch.from_numpy(np.ascontiguousarray(p["W_out"].T)).cuda().to(bf)
+    b, lam0, S0 = (torch.from_numpy(p[n]).cuda() for n in ("b_gate", "lambda0", "S0"))
+    ref = kdn.layer_forward(x, W_in, b, W_out, 2, 64, 64, lam0, S0)
+    torch.cuda.synchronize()
+    d = kdn.make_layer_desc(1, 200, 2, 128, 64, 64, 64, "diagonal", kdn.BF16)
+    ws = torch.empty(kdn.layer_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        got = kdn.layer_forward(x, W_in, b, W_out, 2, 64, 64, lam0, S0, workspace=ws)
+    for i in range(REPLAYS):
+        for y in got:
+            y.fill_(float("nan"))
+        g.replay()
+        kdn.layer_forward(x, W_in, b, W_out, 2, 64, 64, lam0, S0)
+        torch.cuda.synchronize()
+        for name, a_, b_ in zip(("y", "S_T", "lambda_T"), got, ref):
+            assert torch.equal(a_, b_), f"replay {i}: {name} differs from the eager call"
