@@ -652,10 +652,58 @@ template <typename E, int DK, int DVT, int C> struct StateLds {
     E Tt[C * G::LDC];    // (I + A)^{-1}  [t][s]
     E M[C * G::LDC];     // tril(Q W^T) * Gamma  [t][s]
     E V[C * G::LDV];
-    float g[C];          // g_t (base 2)
-    float gam[C];        // gamma_t = 2^g_t
-    float del[C];        // gamma_C / gamma_t
+    float g[2][C];       // g_t (base 2)
+    float gam[2][C];     // gamma_t = 2^g_t
+    float del[2][C];     // gamma_C / gamma_t
+    // (two sets of decay tables, used by alternate chunks when the M tiles of
+    // the next chunk are formed ahead; set 0 only otherwise)
 };
+
+// The layer shape with a read-out (four t-tiles, four j-tiles, eight waves):
+// the M tiles of chunk c + 1 are formed in phase C of chunk c, into the
+// buffer that held chunk c's R, so that phase A holds the two contractions of
+// the state alone; R and M trade buffers from chunk to chunk, and the decay
+// tables of chunk c + 1 go to the other table set in phase B.
+#ifndef KDN_M_AHEAD
+#define KDN_M_AHEAD 1
+#endif
+template <typename E, int DK, int DVT, int C, bool OUT>
+constexpr bool state_m_ahead() {
+    using G = StateCfg<E, DK, DVT, C>;
+    return KDN_M_AHEAD && OUT && G::NT == 4 && G::NV == 4 && G::BT == 2 && G::BV == 2 &&
+           G::NW == 8;
+}
+
+// The ten lower 16 x 16 tiles of M = tril(Q W^T) * Gamma at the layer shape,
+// each formed transposed (W Q^T, full depth), masked and scaled, and stored as
+// M[t][s] (element e <-> s = 16 ss + 4 (lane/16) + e, t = 16 tt + lane % 16):
+// waves 0-3 two tiles that share their W fragments, (0,0)+(0,1), (0,2)+(0,3),
+// (1,1)+(1,2), (2,2)+(2,3); waves 4 and 5 one tile, (1,3) and (3,3).
+template <typename E, int DK, int LDK, int LDC>
+__device__ __forceinline__ void state_m_tiles(E* sM, const E* sW, const E* sQ, const float* g,
+                                              int wave, int lane) {
+    auto m_store = [&](int ss, int tt, floatx4 mv) __attribute__((always_inline)) {
+        const int s0 = 16 * ss + 4 * (lane >> 4);
+        const int t = 16 * tt + (lane & 15);
+        const float gt = g[t];
+        const float4 gs = *reinterpret_cast<const float4*>(g + s0);
+        store4<E>(sM + t * LDC + s0, (s0 + 0 <= t) ? exp2_hw(gt - gs.x) * mv[0] : 0.f,
+                  (s0 + 1 <= t) ? exp2_hw(gt - gs.y) * mv[1] : 0.f,
+                  (s0 + 2 <= t) ? exp2_hw(gt - gs.z) * mv[2] : 0.f,
+                  (s0 + 3 <= t) ? exp2_hw(gt - gs.w) * mv[3] : 0.f);
+    };
+    if (wave < 4) {
+        const int ss = wave < 2 ? 0 : wave - 1, tt = wave == 1 ? 2 : ss;
+        floatx4 m[1][2] = {{floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}}};
+        mma_block<E, 1, 2>(m, sW, LDK, 16 * ss, sQ, LDK, 16 * tt, 0, DK, lane);
+        m_store(ss, tt, m[0][0]);
+        m_store(ss, tt + 1, m[0][1]);
+    } else if (wave < 6) {
+        const int ss = wave == 4 ? 1 : 3;
+        m_store(ss, 3, mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, sW, LDK, 16 * ss, sQ, LDK, 48, 0,
+                                   DK, lane));
+    }
+}
 
 // A state pass over sequence segments (kernel argument): each head's chunks
 // cut into nseg runs of Lc chunks (the last may be shorter); this launch runs
@@ -704,22 +752,20 @@ __device__ __forceinline__ void state_chunk(
                                            c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
     __builtin_amdgcn_sched_barrier(0);  // keep the three load bursts apart
 
-    // one 16x16 tile of M^T = W Q^T (full depth), masked and scaled, stored as
-    // M[t][s] (element e <-> s = 16 ss + 4 (lane/16) + e, t = 16 tt + lane % 16)
-    auto m_store = [&](int ss, int tt, floatx4 mv) __attribute__((always_inline)) {
-        const int s0 = 16 * ss + 4 * (lane >> 4);
-        const int t = 16 * tt + (lane & 15);
-        const float gt = L.g[t];
-        const float4 gs = *reinterpret_cast<const float4*>(L.g + s0);
-        store4<E>(L.M + t * LDC + s0, (s0 + 0 <= t) ? exp2_hw(gt - gs.x) * mv[0] : 0.f,
-                  (s0 + 1 <= t) ? exp2_hw(gt - gs.y) * mv[1] : 0.f,
-                  (s0 + 2 <= t) ? exp2_hw(gt - gs.z) * mv[2] : 0.f,
-                  (s0 + 3 <= t) ? exp2_hw(gt - gs.w) * mv[3] : 0.f);
-    };
     // the layer shape (four t-tiles, four j-tiles, eight waves): M is formed in
-    // phase A, where the first wave of each SIMD has slack, and U = T R takes all
-    // eight waves in phase B
+    // phase A, where the first wave of each SIMD has slack, or (kAhead, with a
+    // read-out) in phase C of the chunk before; U = T R takes all eight waves in
+    // phase B
     constexpr bool kMInA = NT == 4 && G::NV == 4 && BT == 2 && BV == 2 && G::NW == 8;
+    constexpr bool kAhead = state_m_ahead<E, DK, DVT, C, OUT>();
+    static_assert(!kAhead || (kMInA && LDV == LDC), "R and M trade buffers");
+    // this chunk's decay tables and the next chunk's; its R and M buffers
+    const int tc = kAhead ? (c & 1) : 0, tn = kAhead ? ((c + 1) & 1) : 0;
+    const float* gT = L.g[tc];
+    const float* gamT = L.gam[tc];
+    const float* delT = L.del[tc];
+    E* const Rb = kAhead && (c & 1) ? L.M : L.R;
+    E* const Mb = kAhead && (c & 1) ? L.R : L.M;
 
     // ---------------- phase A: X^T = S K^T -> R ;  Y = S Q^T
     // block (jb: BVA j-tiles, tb: one t-tile); C-layout element e <->
@@ -757,7 +803,7 @@ __device__ __forceinline__ void state_chunk(
                 }
             }
             const int t = 16 * tb + (lane & 15);
-            const float gt = L.gam[t];
+            const float gt = gamT[t];
             static_assert(BVA == 2, "R and V tiles pair along j");
             float vt[BVA][4];
             load8x2<E>(L.V + t * LDV + 16 * jb, L.V + t * LDV + 16 * jb + 16, vt[0], vt[1], lane);
@@ -770,46 +816,32 @@ __device__ __forceinline__ void state_chunk(
                                  vv[3] - gt * xv[3]};
                 if constexpr (OUT) accY[x][bv][0] = accY[x][bv][0] * gt;
             }
-            E* row = L.R + t * LDV + 16 * jb;
+            E* row = Rb + t * LDV + 16 * jb;
             store8x2<E>(row, row + 16, rv[0], rv[1], lane);
         }
     }
-    if constexpr (kMInA && OUT) {
-        // the ten lower tiles of M: waves 0-3 two tiles that share their W
-        // fragments, (0,0)+(0,1), (0,2)+(0,3), (1,1)+(1,2), (2,2)+(2,3); waves 4
-        // and 5 one tile, (1,3) and (3,3)
-        if (wave < 4) {
-            const int ss = wave < 2 ? 0 : wave - 1, tt = wave == 1 ? 2 : ss;
-            floatx4 m[1][2] = {{floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}}};
-            mma_block<E, 1, 2>(m, sWc, LDK, 16 * ss, L.Q, LDK, 16 * tt, 0, DK, lane);
-            m_store(ss, tt, m[0][0]);
-            m_store(ss, tt + 1, m[0][1]);
-        } else if (wave < 6) {
-            const int ss = wave == 4 ? 1 : 3;
-            m_store(ss, 3, mma_tile<E>(floatx4{0.f, 0.f, 0.f, 0.f}, sWc, LDK, 16 * ss, L.Q, LDK,
-                                       48, 0, DK, lane));
-        }
-    }
+    if constexpr (kMInA && OUT && !kAhead)
+        state_m_tiles<E, DK, LDK, LDC>(L.M, sWc, L.Q, gT, wave, lane);
     sync_lds();
     state_prefetch<E, DK, DVT, C, kLoadW, OUT>(A.q, A.k, A.v, A.w, A.Tm, A.gin, A.sl, A.jv, A.DV,
                                           c + 2, A.tid, lane, lk, lq, lw, lv, lt, lg);
     __builtin_amdgcn_sched_barrier(0);  // keep the three load bursts apart
 
     // ---------------- phase B
-    const float gC = L.gam[C - 1];  // read before phase C restages the tables
+    const float gC = gamT[C - 1];  // read before the tables are restaged
     if constexpr (kMInA) {
         // U = T R (T lower triangular: contract only up to the block's last row):
         // a pair of t-tiles x one j-tile per wave, the deep pair on the first
         // wave of each SIMD; stored as U^T and as U^T scaled by gamma_C / gamma_t
         const int tb = wave < 4 ? 2 : 0, jv = wave & 3;
         floatx4 u[2][1] = {{floatx4{0.f, 0.f, 0.f, 0.f}}, {floatx4{0.f, 0.f, 0.f, 0.f}}};
-        mma_block<E, 2, 1, false, true>(u, L.Tt, LDC, 16 * tb, L.R, LDV, 16 * jv, 0,
+        mma_block<E, 2, 1, false, true>(u, L.Tt, LDC, 16 * tb, Rb, LDV, 16 * jv, 0,
                                         16 * (tb + 2), lane);
         floatx4 us[2];
 #pragma unroll
         for (int bt = 0; bt < 2; ++bt) {
             const int t = 16 * (tb + bt) + 4 * (lane >> 4);
-            const float4 d4 = *reinterpret_cast<const float4*>(L.del + t);
+            const float4 d4 = *reinterpret_cast<const float4*>(delT + t);
             const floatx4 uv = u[bt][0];
             us[bt] = floatx4{d4.x * uv[0], d4.y * uv[1], d4.z * uv[2], d4.w * uv[3]};
         }
@@ -817,10 +849,11 @@ __device__ __forceinline__ void state_chunk(
         store8x2<E>(L.U + j * LDC + 16 * tb, L.U + j * LDC + 16 * tb + 16, u[0][0], u[1][0], lane);
         store8x2<E>(L.Us + j * LDC + 16 * tb, L.Us + j * LDC + 16 * tb + 16, us[0], us[1], lane);
         // K, Q, V and W of chunk c + 1 (the first three were last read in phase A;
-        // W goes to the other buffer): staged here, where the waves have slack
+        // W goes to the other buffer), and with kAhead its decay tables (to the
+        // other set): staged here, where the waves have slack
         if (c + 1 < A.sl.nc)
-            state_stage<E, DK, DVT, C, kStageKQWV, OUT>(
-                L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g, L.gam, L.del,
+            state_stage<E, DK, DVT, C, kAhead ? (kStageKQWV | kStageTab) : kStageKQWV, OUT>(
+                L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g[tn], L.gam[tn], L.del[tn],
                 min(C, A.sl.T - (c + 1) * C), A.tid, lane, wave, nk, nq, nw, nv, nt, ng,
                 A.zero_v);
     } else if (wave < 4) {
@@ -835,13 +868,13 @@ __device__ __forceinline__ void state_chunk(
                 for (int bt = 0; bt < BT; ++bt)
 #pragma unroll
                     for (int bv = 0; bv < BV; ++bv) u[bt][bv] = floatx4{0.f, 0.f, 0.f, 0.f};
-                mma_block<E, BT, BV, false, true>(u, L.Tt, LDC, 16 * tb, L.R, LDV, 16 * jb, 0,
+                mma_block<E, BT, BV, false, true>(u, L.Tt, LDC, 16 * tb, Rb, LDV, 16 * jb, 0,
                                                   16 * (tb + BT), lane);
                 floatx4 us[BT][BV];
 #pragma unroll
                 for (int bt = 0; bt < BT; ++bt) {
                     const int t = 16 * (tb + bt) + 4 * (lane >> 4);
-                    const float4 d4 = *reinterpret_cast<const float4*>(L.del + t);
+                    const float4 d4 = *reinterpret_cast<const float4*>(delT + t);
 #pragma unroll
                     for (int bv = 0; bv < BV; ++bv) {
                         const floatx4 uv = u[bt][bv];
@@ -887,12 +920,12 @@ __device__ __forceinline__ void state_chunk(
 #pragma unroll
                 for (int bt = 0; bt < BT; ++bt) {
                     const int t = 16 * (tbb * BT + bt) + (lane & 15);
-                    const float gt = L.g[t];
+                    const float gt = gT[t];
                     floatx4 mm[BT];
 #pragma unroll
                     for (int bs = 0; bs < BT; ++bs) {
                         const int s0 = 16 * (sbb * BT + bs) + 4 * (lane >> 4);
-                        const float4 gs = *reinterpret_cast<const float4*>(L.g + s0);
+                        const float4 gs = *reinterpret_cast<const float4*>(gT + s0);
                         const floatx4 mv = m[bs][bt];
                         mm[bs] = floatx4{(s0 + 0 <= t) ? exp2_hw(gt - gs.x) * mv[0] : 0.f,
                                          (s0 + 1 <= t) ? exp2_hw(gt - gs.y) * mv[1] : 0.f,
@@ -921,7 +954,7 @@ __device__ __forceinline__ void state_chunk(
         const int job = wave + G::NW * x;
         if (OUT && job < G::NAJ) {
             const int jb = (job / NT) * BVA, tb = a_tile<NT>(job);
-            mma_block<E, BVA, 1>(accY[x], L.U, LDC, 16 * jb, L.M, LDC, 16 * tb, 0, 16 * (tb + 1),
+            mma_block<E, BVA, 1>(accY[x], L.U, LDC, 16 * jb, Mb, LDC, 16 * tb, 0, 16 * (tb + 1),
                                  lane);
             const int t = 16 * tb + (lane & 15);
             E* orow = A.o + (row0 + t) * A.DV + A.j0 + 16 * jb;
@@ -943,10 +976,16 @@ __device__ __forceinline__ void state_chunk(
                                        lane);
         }
     }
+    // kAhead: the M tiles of chunk c + 1 (its Q, W and tables were staged in
+    // phase B) into the buffer that held this chunk's R
+    if constexpr (kAhead)
+        if (c + 1 < A.sl.nc)
+            state_m_tiles<E, DK, LDK, LDC>(Rb, L.W[(c + 1) & 1], L.Q, L.g[tn], wave, lane);
     // nothing staged here is read in phase C (W goes to the other buffer)
     if (c + 1 < A.sl.nc)
-        state_stage<E, DK, DVT, C, kMInA ? kStageT : kStageAll, OUT>(
-            L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g, L.gam, L.del, min(C, A.sl.T - (c + 1) * C),
+        state_stage<E, DK, DVT, C, kMInA ? (kAhead ? kStageTm : kStageT) : kStageAll, OUT>(
+            L.K, L.Q, L.W[(c + 1) & 1], L.V, L.Tt, L.g[tn], L.gam[tn], L.del[tn],
+            min(C, A.sl.T - (c + 1) * C),
             A.tid, lane, wave, nk, nq, nw, nv, nt, ng, A.zero_v);
     state_write<E, DK, DVT, C>(accS, L.S, wave, lane);
     sync_lds();
@@ -1053,12 +1092,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                                                      lane, pkA, pqA, pwA, pvA, ptA, pgA);
         state_prefetch<E, DK, DVT, C, kLoadAll, OUT>(q, k, v, w, Tm, gin, sl, A.jv, DV, 1, tid,
                                                      lane, pkB, pqB, pwB, pvB, ptB, pgB);
-        state_stage<E, DK, DVT, C, kStageAll, OUT>(L.K, L.Q, L.W[0], L.V, L.Tt, L.g, L.gam,
-                                                   L.del, min(C, sl.T), tid, lane, wave, pkA,
-                                                   pqA, pwA, pvA, ptA, pgA, idt);
+        state_stage<E, DK, DVT, C, kStageAll, OUT>(L.K, L.Q, L.W[0], L.V, L.Tt, L.g[0],
+                                                   L.gam[0], L.del[0], min(C, sl.T), tid, lane,
+                                                   wave, pkA, pqA, pwA, pvA, ptA, pgA, idt);
     }
     state_write<E, DK, DVT, C>(accS, L.S, wave, lane);
     sync_lds();
+    if constexpr (state_m_ahead<E, DK, DVT, C, OUT>()) {
+        // the first chunk's M tiles (later chunks form the next chunk's in phase C)
+        if (sl.nc > 0) state_m_tiles<E, DK, G::LDK, G::LDC>(L.M, L.W[0], L.Q, L.g[0], wave, lane);
+        sync_lds();
+    }
 
     // the two sets alternate roles from chunk to chunk
     // (Sc: the state at every chunk start, kept for the backward pass)

@@ -171,7 +171,7 @@ template <typename E, int DK, int DVT, int C> struct StateCfg {
     static constexpr int BYTES =
         (4 * C * LDK + DVT * LDK + C * LDV + 2 * DVT * LDC + 2 * C * LDC + C * LDV) *
             (int)sizeof(E) +
-        3 * C * (int)sizeof(float);
+        6 * C * (int)sizeof(float);  // two sets of the three decay tables
 };
 
 // Loads of one chunk into registers, two chunks before its use, and their
@@ -235,7 +235,8 @@ __device__ __forceinline__ void state_prefetch(
 
 // parts of a chunk staged from registers into LDS: K, Q, W and V; T and the
 // decay tables.  zero_v: V is staged as zeros (the loaded values are dropped).
-enum { kStageKQWV = 1, kStageT = 2, kStageAll = 3 };
+// parts: K, Q, W, V; the T matrix; the decay tables (g, gamma, gamma_C / gamma)
+enum { kStageKQWV = 1, kStageTm = 2, kStageTab = 4, kStageT = 6, kStageAll = 7 };
 template <typename E, int DK, int DVT, int C, int PARTS, bool WQ = true>
 __device__ __forceinline__ void state_stage(
     E* sK, E* sQ, E* sWc, E* sV, E* sT, float* sg, float* sgam, float* sdel, int n, int tid,
@@ -269,7 +270,7 @@ __device__ __forceinline__ void state_stage(
             }
         }
     }
-    if constexpr ((PARTS & kStageT) != 0) {
+    if constexpr ((PARTS & kStageTm) != 0) {
 #pragma unroll
         for (int x = 0; x < G::PT; ++x) {
             const int e = tid + G::THREADS * x;
@@ -278,6 +279,8 @@ __device__ __forceinline__ void state_stage(
                 *reinterpret_cast<u32x4*>(sT + t * LDC + c0) = pt[x];
             }
         }
+    }
+    if constexpr ((PARTS & kStageTab) != 0) {
         if (wave == 0) {
             const float glast = lane_value(pg, C - 1);
             if (lane < C) {
