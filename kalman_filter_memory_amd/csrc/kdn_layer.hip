@@ -125,27 +125,36 @@ __global__ __launch_bounds__(256) void layer_in_kernel(
     const int row = blockIdx.x, b = row / T, t = row % T;
     const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
     const E* z = Z + size_t(row) * ldz;
-    for (int vi = grp; vi < 3 * H; vi += 16) {
-        if (vi < 2 * H) {  // q or k: x / max(|x|, 1e-6)
-            constexpr int N = DK / 16;
-            const int h = vi < H ? vi : vi - H;
-            float x[N];
-            load_n<E, N>(z + vi * DK + l16 * N, x);
-            float ss = 0.f;
+    // up to four vectors per 16-lane group at a time, every load issued before
+    // the first is used
+    constexpr int NK = DK / 16, NV = DV / 16, NM = NK > NV ? NK : NV, U = 4;
+    for (int base = 0; base < 3 * H; base += 16 * U) {
+        float xs[U][NM];
 #pragma unroll
-            for (int i = 0; i < N; ++i) ss = fmaf(x[i], x[i], ss);
-            ss = kdn::group_sum<16>(ss);
-            const float sc = 1.f / sqrtf(fmaxf(ss, 1e-12f));
+        for (int u = 0; u < U; ++u) {
+            const int vi = base + grp + 16 * u;
+            if (vi < 2 * H) load_n<E, NK>(z + vi * DK + l16 * NK, xs[u]);
+            else if (vi < 3 * H) load_n<E, NV>(z + 2 * H * DK + (vi - 2 * H) * DV + l16 * NV, xs[u]);
+        }
 #pragma unroll
-            for (int i = 0; i < N; ++i) x[i] *= sc;
-            E* dst = (vi < H ? q : k) + ((size_t(b) * H + h) * T + t) * DK + l16 * N;
-            store_n<E, N>(dst, x);
-        } else {
-            constexpr int N = DV / 16;
-            const int h = vi - 2 * H;
-            float x[N];
-            load_n<E, N>(z + 2 * H * DK + h * DV + l16 * N, x);
-            store_n<E, N>(v + ((size_t(b) * H + h) * T + t) * DV + l16 * N, x);
+        for (int u = 0; u < U; ++u) {
+            const int vi = base + grp + 16 * u;
+            if (vi < 2 * H) {  // q or k: x / max(|x|, 1e-6)
+                const int h = vi < H ? vi : vi - H;
+                float* x = xs[u];
+                float ss = 0.f;
+#pragma unroll
+                for (int i = 0; i < NK; ++i) ss = fmaf(x[i], x[i], ss);
+                ss = kdn::group_sum<16>(ss);
+                const float sc = 1.f / sqrtf(fmaxf(ss, 1e-12f));
+#pragma unroll
+                for (int i = 0; i < NK; ++i) x[i] *= sc;
+                E* dst = (vi < H ? q : k) + ((size_t(b) * H + h) * T + t) * DK + l16 * NK;
+                store_n<E, NK>(dst, x);
+            } else if (vi < 3 * H) {
+                const int h = vi - 2 * H;
+                store_n<E, NV>(v + ((size_t(b) * H + h) * T + t) * DV + l16 * NV, xs[u]);
+            }
         }
     }
     if (tid < 3 * H) {
