@@ -77,7 +77,7 @@ kdn::Shape make_shape(const kdn_desc* d) {
 
 struct ForwardWs {
     size_t agg, lam_chunk, w, tm, g, seg_S, seg_A, total;
-    int nseg, Lc;
+    int nseg, Lc, L0;
 };
 
 // workspace offsets: [agg | lam_chunk | w | T | g | segment states | segment
@@ -87,11 +87,11 @@ ForwardWs forward_ws(const kdn_desc* d) {
     const kdn::Shape s = make_shape(d);
     const size_t nl = s.diag ? s.dk : 1;
     ForwardWs w;
-    w.nseg = kdn::chunk_supported(s) ? kdn::state_segments(s, &w.Lc) : 1;
-    if (w.nseg <= 1) {
-        w.nseg = 1;
-        w.Lc = s.nc;
-    }
+    const kdn::SegSplit sp = kdn::chunk_supported(s) ? kdn::state_split(s)
+                                                     : kdn::SegSplit{1, s.nc, s.nc};
+    w.nseg = sp.nseg > 1 ? sp.nseg : 1;
+    w.Lc = w.nseg > 1 ? sp.Lc : s.nc;
+    w.L0 = w.nseg > 1 ? sp.L0 : s.nc;
     const size_t segs = w.nseg > 1 ? (size_t)s.BH * w.nseg : 0;
     w.agg = 0;
     w.lam_chunk = w.agg + round_up((size_t)s.BH * s.nc * kdn::agg_subs(s) * nl * 16);
@@ -147,7 +147,7 @@ int packed_segments(const kdn_desc* d, int max_chunks) {
     s.varlen = true;
     s.BH = d->B * d->H;
     s.nc = max_chunks;
-    return kdn::chunk_supported(s) ? std::max(1, kdn::state_segments(s, nullptr)) : 1;
+    return kdn::chunk_supported(s) ? std::max(1, kdn::state_split(s).nseg) : 1;
 }
 
 // workspace offsets: [cu | cc | agg | lam_chunk | w | T | g | segment states |
@@ -258,6 +258,7 @@ kdn_status forward_run(const kdn_desc* d, const void* q, const void* k, const vo
     kdn::SegWs seg;
     seg.nseg = w.nseg;
     seg.Lc = w.Lc;
+    seg.L0 = w.L0;
     seg.Sseg = reinterpret_cast<float*>(at(ws, w.seg_S));
     seg.Aseg = reinterpret_cast<float*>(at(ws, w.seg_A));
     auto launch = [&](int i) -> hipError_t {

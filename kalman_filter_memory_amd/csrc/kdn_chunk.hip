@@ -32,6 +32,7 @@
 // operands needed with the contraction index strided (W in the state update,
 // the token-major R) are read with transposing LDS reads.
 #include <algorithm>
+#include <cmath>
 
 #include "kdn_device.h"
 #include "kdn_launch.h"
@@ -706,11 +707,14 @@ __device__ __forceinline__ void state_m_tiles(E* sM, const E* sW, const E* sQ, c
 }
 
 // A state pass over sequence segments (kernel argument): each head's chunks
-// cut into nseg runs of Lc chunks (the last may be shorter); this launch runs
-// segments g0 .. g0 + nsegL - 1 of every head, each with ntv value-row tiles
-// and nta identity-row tiles.
+// cut into nseg runs, the first of L0 chunks and the others of Lc (the last
+// may be shorter); this launch runs segments g0 .. g0 + nsegL - 1 of every
+// head, each with ntv value-row tiles and nta identity-row tiles.
+constexpr int kStateCUs = 256;  // compute units: one state workgroup each
+
 struct SegPlan {
-    int nseg = 1, Lc = 0, g0 = 0, nsegL = 1, ntv = 1, nta = 0;
+    int nseg = 1, Lc = 0, L0 = 0, g0 = 0, nsegL = 1, ntv = 1, nta = 0;
+    int map_wgs = 0, map_jobs = 0;  // maps launch: workgroups running maps, jobs per workgroup
     float* Sseg = nullptr;        // [BH][nseg][DV][DK]: start state of each segment
     float* Aseg = nullptr;        // [BH][nseg][DK][DK]: linear part of each segment's map
 };
@@ -991,44 +995,39 @@ __device__ __forceinline__ void state_chunk(
     sync_lds();
 }
 
-// One workgroup per CU (its LDS footprint) = two waves per SIMD: give each wave
-// the full 256-register budget instead of spilling to reach more waves.
 // VL: a packed batch, head = sequence * H + head within the sequence.
 // OUT: the read-out o is formed and written.
 // SEG: the head's chunks are cut into segments (SegPlan) and each workgroup
 //   runs one (head, segment, tile).  With OUT, a segment starts from its true
 //   start state (S0, or the start state of segment g in seg.Sseg) and writes
-//   o, and the last segment S_T.  Without OUT it forms the segment's affine
-//   map S -> S A_g + B_g: value tiles run segment g from S0 (g = 0) or from
-//   zero (B_g) and write the end state into seg.Sseg[g + 1]; identity tiles
-//   (rows of the d_k x d_k identity, V = 0) write A_g into seg.Aseg[g].
+//   o, and the last segment S_T; segment 0 (run by the maps launch) also
+//   writes its end state, the start state of segment 1, into seg.Sseg[1].
+//   Without OUT it forms the segment's affine map S -> S A_g + B_g: value
+//   tiles run segment g from zero (B_g) and write the end state into
+//   seg.Sseg[g + 1]; identity tiles (rows of the d_k x d_k identity, V = 0)
+//   write A_g into seg.Aseg[g].
 template <typename E, int DK, int DVT, int C, bool VL, bool OUT, bool SEG>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void state_kernel(
-    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const float* __restrict__ gin, const E* __restrict__ w, const E* __restrict__ Tm,
-    const float* S0, E* __restrict__ o, float* S_T, E* __restrict__ Sc, int BH, int T, int DV,
-    int NC, Packed pk, SegPlan seg) {
+__device__ __forceinline__ void state_body(StateLds<E, DK, DVT, C>& L, const E* __restrict__ q,
+                                           const E* __restrict__ k, const E* __restrict__ v,
+                                           const float* __restrict__ gin,
+                                           const E* __restrict__ w, const E* __restrict__ Tm,
+                                           const float* S0, E* __restrict__ o, float* S_T,
+                                           E* __restrict__ Sc, int T, int DV, int NC, Packed pk,
+                                           const SegPlan& seg, int head, int g, int tile) {
     using G = StateCfg<E, DK, DVT, C>;
     constexpr int BI = G::BI, BV = G::BV, NVB = G::NVB;
-    __shared__ __align__(16) StateLds<E, DK, DVT, C> L;
     const int tid = threadIdx.x;
-    // Workgroups go to the 8 XCDs round-robin by linear id: the tiles of one
-    // unit (a head, or a (head, segment) pair) get ids equal mod 8, so they
-    // share one XCD's L2 for K, Q, W and T.
-    const int ntile = SEG ? seg.ntv + seg.nta : DV / DVT;
-    const int L_ = blockIdx.x, per = 8 * ntile;
-    const int unit = (L_ / per) * 8 + (L_ % 8), tile = (L_ % per) / 8;
-    const int head = SEG ? unit / seg.nsegL : unit;
-    const int g = SEG ? seg.g0 + unit % seg.nsegL : 0;
-    if (head >= BH) return;
     const bool idt = SEG && !OUT && tile >= seg.ntv;  // identity rows of a segment map
-    if (idt && g == 0) return;                        // segment 0 starts from S0: no map
     Slab sl = slab_of<VL>(head, T, NC, pk);
     if constexpr (SEG) {
-        // packed batches cut each sequence into the call's segment count (a
-        // short sequence's last segments may be empty: identity maps)
+        // segment 0 holds L0 chunks, the others Lc each (the last may be
+        // shorter); packed batches cut each sequence into the call's segment
+        // count, all of one length (a short sequence's last segments may be
+        // empty: identity maps)
         const int Lc = VL ? (sl.nc + seg.nseg - 1) / seg.nseg : seg.Lc;
-        const int cb = min(g * Lc, sl.nc), ce = min(cb + Lc, sl.nc);
+        const int L0 = VL ? Lc : seg.L0;
+        const int cb = g == 0 ? 0 : min(L0 + (g - 1) * Lc, sl.nc);
+        const int ce = min(cb + (g == 0 ? L0 : Lc), sl.nc);
         sl.row0 += (size_t)cb * C;
         sl.T = max(0, min(sl.T - cb * C, (ce - cb) * C));
         sl.nc = ce - cb;
@@ -1046,12 +1045,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         const size_t slot = bh * seg.nseg + g;
         if constexpr (OUT) {
             if (g > 0) Sin = seg.Sseg + (slot * DV + j0) * DK;
-            if (g != seg.nseg - 1) Sout = nullptr;
+            if (g != seg.nseg - 1) Sout = g == 0 ? seg.Sseg + ((slot + 1) * DV + j0) * DK : nullptr;
         } else if (idt) {
             Sin = nullptr;
             Sout = seg.Aseg + (slot * DK + j0) * DK;
         } else {
-            if (g > 0) Sin = nullptr;
+            Sin = nullptr;
             Sout = seg.Sseg + ((slot + 1) * DV + j0) * DK;
         }
     }
@@ -1136,6 +1135,58 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                     }
             }
         }
+    }
+}
+
+// One workgroup per CU (its LDS footprint) = two waves per SIMD: give each wave
+// the full 256-register budget instead of spilling to reach more waves.
+// Workgroups go to the 8 XCDs round-robin by linear id: the tiles of one unit
+// (a head, or a (segment, head) pair) get ids equal mod 8, so they share one
+// XCD's L2 for K, Q, W and T.  Segmented launches number their units segment
+// by segment.  The maps launch has at most one workgroup per CU, so that no
+// run waits for a CU to come free: its first seg.map_wgs workgroups each form
+// seg.map_jobs (segment, head, tile) maps of segments 1 .. nseg - 2 in turn
+// (job r of workgroup x is job x + r * map_wgs), the rest run segment 0's
+// value tiles with read-out.
+template <typename E, int DK, int DVT, int C, bool VL, bool OUT, bool SEG>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void state_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ gin, const E* __restrict__ w, const E* __restrict__ Tm,
+    const float* S0, E* __restrict__ o, float* S_T, E* __restrict__ Sc, int BH, int T, int DV,
+    int NC, Packed pk, SegPlan seg) {
+    __shared__ __align__(16) StateLds<E, DK, DVT, C> L;
+    const int ntile = SEG ? seg.ntv + seg.nta : DV / DVT;
+    const int L_ = blockIdx.x, per = 8 * ntile;
+    const int unit = (L_ / per) * 8 + (L_ % 8), tile = (L_ % per) / 8;
+    if constexpr (SEG && !OUT) {
+        if (L_ >= seg.map_wgs) {
+            // segment 0 starts from S0: its value tiles run it with read-out
+            // (and keep its end state); it has no map to form
+            const int i = L_ - seg.map_wgs, per0 = 8 * seg.ntv;
+            const int head = (i / per0) * 8 + (i % 8);
+            if (head >= BH) return;
+            state_body<E, DK, DVT, C, VL, true, true>(L, q, k, v, gin, w, Tm, S0, o, S_T, Sc, T,
+                                                      DV, NC, pk, seg, head, 0, (i % per0) / 8);
+            return;
+        }
+        const int units = BH * (seg.nseg - 2);  // the maps of segments 1 .. nseg - 2
+        for (int r = 0; r < seg.map_jobs; ++r) {
+            const int i = L_ + r * seg.map_wgs;
+            const int u = (i / per) * 8 + (i % 8);
+            if (u >= units) continue;
+            if (r > 0) sync_lds();  // the previous job's last LDS reads are done
+            state_body<E, DK, DVT, C, VL, false, true>(L, q, k, v, gin, w, Tm, S0, o, S_T, Sc, T,
+                                                       DV, NC, pk, seg, u % BH, 1 + u / BH,
+                                                       (i % per) / 8);
+        }
+    } else if constexpr (SEG) {
+        if (unit >= BH * seg.nsegL) return;
+        state_body<E, DK, DVT, C, VL, true, true>(L, q, k, v, gin, w, Tm, S0, o, S_T, Sc, T, DV,
+                                                  NC, pk, seg, unit % BH, seg.g0 + unit / BH, tile);
+    } else {
+        if (unit >= BH) return;
+        state_body<E, DK, DVT, C, VL, OUT, false>(L, q, k, v, gin, w, Tm, S0, o, S_T, Sc, T, DV,
+                                                  NC, pk, seg, unit, 0, tile);
     }
 }
 
@@ -1291,22 +1342,37 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
             else if (o) KDN_STATE_L(false, true, false, grid(s.BH, ntv), plain);
             else KDN_STATE_L(false, false, false, grid(s.BH, ntv), plain);
         } else {
-            // segments: the maps of segments 0 .. nseg - 2, their composition
-            // into every segment's start state, then the read-out pass; the
-            // caller's timing events bracket the three launches
+            // segments: segment 0 with read-out beside the maps of segments
+            // 1 .. nseg - 2, their composition into every segment's start
+            // state, then the read-out of segments 1 .. nseg - 1; the caller's
+            // timing events bracket the three launches
             const LaunchTiming t = launch_timing();
             SegPlan p;
             p.nseg = sw->nseg;
             p.Lc = sw->Lc;
+            p.L0 = sw->L0 > 0 ? sw->L0 : sw->Lc;
             p.Sseg = sw->Sseg;
             p.Aseg = sw->Aseg;
             p.g0 = 0;
             p.nsegL = sw->nseg - 1;
             p.ntv = ntv;
             p.nta = (DK + DVT - 1) / DVT;  // identity rows past d_k are not written
+            // the maps launch: segment 0's value tiles, and as many map
+            // workgroups as the other CUs hold, each taking the fewest jobs
+            // that cover the maps (a whole number of units per round if that fits)
+            const int per = 8 * (p.ntv + p.nta);
+            const long jobs = (long)(s.BH * (sw->nseg - 2) + 7) / 8 * per;
+            const int nv0 = (s.BH + 7) / 8 * 8 * ntv;
+            const int avail = std::max(8, (kStateCUs - nv0) / 8 * 8);
+            p.map_jobs = jobs > 0 ? static_cast<int>((jobs + avail - 1) / avail) : 0;
+            p.map_wgs = jobs > 0 ? static_cast<int>((jobs + p.map_jobs - 1) / p.map_jobs) : 0;
+            p.map_wgs = (p.map_wgs + per - 1) / per * per <= avail
+                            ? (p.map_wgs + per - 1) / per * per
+                            : (p.map_wgs + 7) / 8 * 8;
+            const dim3 gmaps(p.map_wgs + nv0);
             launch_timing() = LaunchTiming{t.start, nullptr};
-            if (s.varlen) KDN_STATE_L(true, false, true, grid(s.BH * p.nsegL, p.ntv + p.nta), p);
-            else KDN_STATE_L(false, false, true, grid(s.BH * p.nsegL, p.ntv + p.nta), p);
+            if (s.varlen) KDN_STATE_L(true, false, true, gmaps, p);
+            else KDN_STATE_L(false, false, true, gmaps, p);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             if (sw->nseg > 2) {
@@ -1315,7 +1381,8 @@ hipError_t state_t(const Shape& s, const void* q, const void* k, const void* v, 
                 e = hipGetLastError();
                 if (e != hipSuccess) return e;
             }
-            p.nsegL = sw->nseg;
+            p.g0 = 1;
+            p.nsegL = sw->nseg - 1;
             p.nta = 0;
             launch_timing() = LaunchTiming{nullptr, t.stop};
             if (s.varlen) KDN_STATE_L(true, true, true, grid(s.BH * p.nsegL, p.ntv), p);
@@ -1388,24 +1455,41 @@ hipError_t launch_chunk_state(const Shape& s, const void* q, const void* k, cons
                       : state_e<float>(s, q, k, v, g, w, Tm, S0, o, S_T, Sc, seg, st);
 }
 
-int state_segments(const Shape& s, int* chunks_per_segment) {
-    int Lc = s.nc, nseg = 1;
+// The segmented pass costs, in time: the maps launch (segment 0 with read-out
+// on BH * ntv CUs, beside rounds of the other segments' maps on the remaining
+// CUs), the composition (nseg - 2 dependent steps) and the read-out launch
+// (rounds of segments 1 .. nseg - 1).  Per chunk a map step takes about 1.6 us
+// and a read-out step 2.5 us (d 128, chunk 64, one workgroup per CU), a
+// composition step about 8.5 us, and the two extra launches about 5 us.  Given
+// nseg, segment 0 is made as long as the maps rounds beside it take, the other
+// segments share the rest; the plan with the least estimated time wins, the
+// plain pass (2.5 us per chunk on one round) included.
+SegSplit state_split(const Shape& s) {
+    SegSplit best{1, s.nc, s.nc};
     const int dvt = dv_tile(s);
-    // at low B*H the plain pass runs B*H*(dv/dvt) workgroups, one per CU:
-    // cut each head into segments until about one workgroup per CU runs the
-    // read-out pass, keeping at least 8 chunks per segment
-    if (s.BH > 0 && dvt > 0 && s.nc >= 16) {
-        const int units = s.BH * (s.dv / dvt);
-        if (units < 128) {
-            const int want = std::min(256 / units, s.nc / 8);
-            if (want >= 2) {
-                Lc = (s.nc + want - 1) / want;
-                nseg = (s.nc + Lc - 1) / Lc;
-            }
+    if (s.BH <= 0 || dvt <= 0 || s.nc < 16) return best;
+    constexpr double kMap = 1.6, kRead = 2.5, kComb = 8.5, kLaunch = 5.0;
+    constexpr int kCUs = kStateCUs, kMinLen = 2;
+    const int ntv = s.dv / dvt, nta = (s.dk + dvt - 1) / dvt;
+    const long seg0 = (long)s.BH * ntv;  // segment 0's workgroups in the maps launch
+    if (seg0 >= kCUs / 2) return best;   // enough heads to fill the GPU
+    double best_t = kRead * s.nc;
+    for (int n = 3; n <= 64 && (n - 1) * kMinLen + kMinLen <= s.nc; ++n) {
+        const long maps = (long)s.BH * (n - 2) * (ntv + nta);
+        const long rm = (maps + (kCUs - seg0) - 1) / (kCUs - seg0);
+        const long rr = ((long)s.BH * (n - 1) * ntv + kCUs - 1) / kCUs;
+        const double rho = kMap * rm / kRead;  // segment 0's length over the others'
+        const int Lc = static_cast<int>(std::ceil(s.nc / (rho + n - 1)));
+        const int L0 = s.nc - (n - 1) * Lc;
+        if (L0 < kMinLen || Lc < kMinLen) continue;
+        const double t = std::max(kRead * L0, kMap * rm * Lc) + kRead * rr * Lc +
+                         kComb * (n - 2) + kLaunch;
+        if (t < best_t) {
+            best_t = t;
+            best = SegSplit{n, Lc, L0};
         }
     }
-    if (chunks_per_segment) *chunks_per_segment = Lc;
-    return nseg;
+    return best;
 }
 
 }  // namespace kdn

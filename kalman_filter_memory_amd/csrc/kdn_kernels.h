@@ -85,18 +85,21 @@ hipError_t launch_chunk_prep(const Shape& s, bool fuse_gain, const void* k, cons
                              const void* nu, const void* r, const float* lam_chunk,
                              const float* agg, void* w, void* Tm, float* g, hipStream_t st,
                              float* dinv = nullptr);
-// Workspace of a state pass over sequence segments: nseg segments of Lc
-// chunks per head (state_segments), the start state of every segment
+// Workspace of a state pass over sequence segments: nseg segments per head
+// (state_split), the start state of every segment
 // Sseg [BH][nseg][dv][dk] and the linear part of every segment's affine map
 // Aseg [BH][nseg][dk][dk], both float32.
 struct SegWs {
-    int nseg = 1, Lc = 0;
+    int nseg = 1, Lc = 0, L0 = 0;  // L0: chunks of segment 0 (0: Lc)
     float* Sseg = nullptr;
     float* Aseg = nullptr;
 };
-// Segments per head that the state pass uses for this shape (1: the plain
-// sequential pass); *chunks_per_segment (may be NULL) receives Lc.
-int state_segments(const Shape& s, int* chunks_per_segment);
+// How the state pass cuts each head's chunks for this shape: nseg segments
+// (1: the plain sequential pass), the first of L0 chunks, the others of Lc.
+struct SegSplit {
+    int nseg, Lc, L0;
+};
+SegSplit state_split(const Shape& s);
 // Sequential chunk pass: memory write and read-out (g from the prep pass).
 // Sc (may be NULL): the state at every chunk start, [BH][nc][dv][dk] in qkv
 // dtype, kept for the backward pass.

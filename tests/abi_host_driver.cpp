@@ -94,22 +94,25 @@ bool chunk_supported(const Shape& s) {
 bool decode_supported(const Shape& s) { return s.dk >= 32 && s.dv >= 32; }
 bool backward_supported(const Shape& s) { return chunk_supported(s); }
 
-int state_segments(const Shape& s, int* Lc_out) {
-    int Lc = s.nc, nseg = 1;
+// A stand-in planner (the API only passes its plan through and sizes the
+// workspace by it): few units and many chunks give 3 .. 8 segments, the first
+// about 1.25 times as long as the others.
+SegSplit state_split(const Shape& s) {
     const int dvt = dvt_of(s);
     if (s.BH > 0 && dvt > 0 && s.nc >= 16) {
         const int units = s.BH * (s.dv / dvt);
         if (units < 128) {
-            int want = 256 / units;
-            if (s.nc / 8 < want) want = s.nc / 8;
-            if (want >= 2) {
-                Lc = (s.nc + want - 1) / want;
-                nseg = (s.nc + Lc - 1) / Lc;
+            int n = 256 / units;
+            if (n > 8) n = 8;
+            if (s.nc / 4 < n) n = s.nc / 4;
+            if (n >= 3) {
+                const int Lc = static_cast<int>((s.nc * 4L + 4L * (n - 1) + 4) / (4L * (n - 1) + 5));
+                const int L0 = s.nc - (n - 1) * Lc;
+                if (L0 >= 1) return SegSplit{n, Lc, L0};
             }
         }
     }
-    if (Lc_out) *Lc_out = Lc;
-    return nseg;
+    return SegSplit{1, s.nc, s.nc};
 }
 
 hipError_t launch_scan_reduce(const Shape& s, const void*, const void*, const void*,
@@ -167,16 +170,16 @@ hipError_t launch_chunk_state(const Shape& s, const void*, const void*, const vo
     in_ws(Tm, chunks(s) * s.chunk * s.chunk * esz(s.qkv_bf16), "T", false);
     in_ws(Sc, chunks(s) * s.dv * s.dk * esz(s.qkv_bf16), "Sc", true);
     if (seg && seg->nseg > 1) {
-        int Lc = 0;
-        const int nseg = state_segments(s, &Lc);
+        const SegSplit sp = state_split(s);
         if (s.varlen) {
             // packed: every slab cuts its own chunks into nseg segments
             ++g_seg_packed;
-            if (seg->Lc != 0 || seg->nseg > nseg) fail("packed segment plan");
+            if (seg->Lc != 0 || seg->nseg > sp.nseg) fail("packed segment plan");
         } else {
-            if (nseg != seg->nseg || Lc != seg->Lc) fail("segment plan differs from state_segments");
-            if ((size_t)(seg->nseg - 1) * seg->Lc >= (size_t)s.nc || (size_t)seg->nseg * seg->Lc < (size_t)s.nc)
-                fail("segments do not cover the chunks with a non-empty last segment");
+            if (sp.nseg != seg->nseg || sp.Lc != seg->Lc || sp.L0 != seg->L0)
+                fail("segment plan differs from state_split");
+            if (seg->L0 < 1 || seg->Lc < 1 || seg->L0 + (size_t)(seg->nseg - 1) * seg->Lc != (size_t)s.nc)
+                fail("segments do not cover the chunks exactly");
         }
         in_ws(seg->Sseg, (size_t)s.BH * seg->nseg * s.dv * s.dk * 4, "Sseg", true);
         in_ws(seg->Aseg, (size_t)s.BH * seg->nseg * s.dk * s.dk * 4, "Aseg", true);
