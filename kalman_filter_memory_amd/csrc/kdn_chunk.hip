@@ -1215,34 +1215,45 @@ __global__ __launch_bounds__(kCombThreads) void seg_combine_kernel(float* __rest
     const int j0 = blockIdx.x * R;
     float* base = Sseg + bh * (size_t)nseg * DV * DK;
     const float* abase = Aseg + bh * (size_t)nseg * DK * DK;
-    float4 preA[NV];
+    // A_{g+1} is prefetched into eight named registers: held in an array,
+    // even one indexed with constants only, the compiler kept it in scratch
+    // memory (a stack round trip per step)
+    static_assert(NV <= 8, "combine prefetch registers");
+    [[maybe_unused]] float4 pa0, pa1, pa2, pa3, pa4, pa5, pa6, pa7;
     float preB[RPT];
-    auto fetch = [&](int g) {  // A_g and the rows of B_g (held in Sseg[g + 1])
-        const float4* src = reinterpret_cast<const float4*>(abase + (size_t)g * DK * DK);
-#pragma unroll
-        for (int x = 0; x < NV; ++x)
-            if (NA % kCombThreads == 0 || tid + kCombThreads * x < NA)
-                preA[x] = src[tid + kCombThreads * x];
-        const float* bsrc = base + ((size_t)(g + 1) * DV + j0) * DK;
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) preB[r] = bsrc[(size_t)(rg * RPT + r) * DK + i];
-    };
-    auto stage = [&](int buf) {
-#pragma unroll
-        for (int x = 0; x < NV; ++x)
-            if (NA % kCombThreads == 0 || tid + kCombThreads * x < NA)
-                reinterpret_cast<float4*>(sA[buf])[tid + kCombThreads * x] = preA[x];
-    };
-    fetch(1);
+#define KDN_COMB_LD(X)                                                                   \
+    if constexpr (X < NV)                                                                \
+        if (NA % kCombThreads == 0 || tid + kCombThreads * X < NA)                       \
+            pa##X = src[tid + kCombThreads * X];
+#define KDN_COMB_ST(X)                                                                   \
+    if constexpr (X < NV)                                                                \
+        if (NA % kCombThreads == 0 || tid + kCombThreads * X < NA)                       \
+            dst[tid + kCombThreads * X] = pa##X;
+#define KDN_COMB_FETCH(G_)                                                                   \
+    {                                                                                        \
+        const float4* src = reinterpret_cast<const float4*>(abase + (size_t)(G_) * DK * DK); \
+        KDN_COMB_LD(0) KDN_COMB_LD(1) KDN_COMB_LD(2) KDN_COMB_LD(3)                          \
+        KDN_COMB_LD(4) KDN_COMB_LD(5) KDN_COMB_LD(6) KDN_COMB_LD(7)                          \
+        const float* bsrc = base + ((size_t)((G_) + 1) * DV + j0) * DK;                      \
+        _Pragma("unroll") for (int r = 0; r < RPT; ++r) preB[r] =                            \
+            bsrc[(size_t)(rg * RPT + r) * DK + i];                                           \
+    }
+#define KDN_COMB_STAGE(BUF_)                                                                 \
+    {                                                                                        \
+        float4* dst = reinterpret_cast<float4*>(sA[BUF_]);                                   \
+        KDN_COMB_ST(0) KDN_COMB_ST(1) KDN_COMB_ST(2) KDN_COMB_ST(3)                          \
+        KDN_COMB_ST(4) KDN_COMB_ST(5) KDN_COMB_ST(6) KDN_COMB_ST(7)                          \
+    }
+    KDN_COMB_FETCH(1)
     for (int e = tid; e < R * DK; e += kCombThreads)
         sS[e / DK][e % DK] = base[((size_t)1 * DV + j0 + e / DK) * DK + e % DK];
-    stage(1);
+    KDN_COMB_STAGE(1)
     __syncthreads();
     for (int g = 1; g + 1 < nseg; ++g) {
         float acc[RPT];
 #pragma unroll
         for (int r = 0; r < RPT; ++r) acc[r] = preB[r];
-        if (g + 2 < nseg) fetch(g + 1);  // in flight during this step
+        if (g + 2 < nseg) KDN_COMB_FETCH(g + 1)  // in flight during this step
         float* out = base + ((size_t)(g + 1) * DV + j0) * DK;
         const float* A = sA[g & 1];
 #pragma unroll 4
@@ -1264,9 +1275,13 @@ __global__ __launch_bounds__(kCombThreads) void seg_combine_kernel(float* __rest
             out[(size_t)(rg * RPT + r) * DK + i] = acc[r];
             sS[rg * RPT + r][i] = acc[r];
         }
-        if (g + 2 < nseg) stage((g + 1) & 1);
+        if (g + 2 < nseg) KDN_COMB_STAGE((g + 1) & 1)
         __syncthreads();
     }
+#undef KDN_COMB_FETCH
+#undef KDN_COMB_STAGE
+#undef KDN_COMB_LD
+#undef KDN_COMB_ST
 }
 
 // ---------------------------------------------------------------- dispatch
