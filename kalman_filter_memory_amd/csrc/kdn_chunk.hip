@@ -1475,7 +1475,7 @@ hipError_t launch_chunk_state(const Shape& s, const void* q, const void* k, cons
 // CUs), the composition (nseg - 2 dependent steps) and the read-out launch
 // (rounds of segments 1 .. nseg - 1).  Per chunk a map step takes about 1.6 us
 // and a read-out step 2.5 us (d 128, chunk 64, one workgroup per CU), a
-// composition step about 8.5 us, and the two extra launches about 5 us.  Given
+// composition step about 3.5 us, and the two extra launches about 5 us.  Given
 // nseg, segment 0 is made as long as the maps rounds beside it take, the other
 // segments share the rest; the plan with the least estimated time wins, the
 // plain pass (2.5 us per chunk on one round) included.
@@ -1483,7 +1483,7 @@ SegSplit state_split(const Shape& s) {
     SegSplit best{1, s.nc, s.nc};
     const int dvt = dv_tile(s);
     if (s.BH <= 0 || dvt <= 0 || s.nc < 16) return best;
-    constexpr double kMap = 1.6, kRead = 2.5, kComb = 8.5, kLaunch = 5.0;
+    constexpr double kMap = 1.6, kRead = 2.5, kComb = 3.5, kLaunch = 5.0;
     constexpr int kCUs = kStateCUs, kMinLen = 2;
     const int ntv = s.dv / dvt, nta = (s.dk + dvt - 1) / dvt;
     const long seg0 = (long)s.BH * ntv;  // segment 0's workgroups in the maps launch

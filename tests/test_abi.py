@@ -243,7 +243,7 @@ def test_state_pass_segments_follow_the_head_count(lib):
     assert kdn.forward_segments(few_chunks) == 1
     ragged = _desc(B=1, H=1, T=16 * 64 + 37, d_k=64, d_v=64, chunk=64)
     n = kdn.forward_segments(ragged)
-    assert n == 3          # 17 chunks: segment 0 of 3, two of 7
+    assert n == 4          # 17 chunks: segment 0 of 2, three of 5
     assert kdn.forward_segments(_desc(d_k=48)) == 0
     # the stage call (given gains) keeps the plain pass and its workspace
     assert lib.kdn_chunk_delta_workspace_bytes(ctypes.byref(long)) == 16 * 1024 * (
