@@ -91,12 +91,14 @@ size_t kdn_forward_workspace_bytes(const kdn_desc *d);
  * for this descriptor (host-only; 0 if the descriptor is invalid).  1: one
  * sequential pass per (head, d_v tile).  With few heads and many chunks
  * (fewer than 128 such workgroups and at least 16 chunks) each head's chunks
- * are cut into this many segments of consecutive chunks: every segment's
- * memory update is an affine map S -> S A + B of its start state (the rows of
- * S evolve independently, each by the same matrix A), so the maps of all
- * segments are formed in parallel, composed in order, and every segment then
- * runs its read-out from its own start state.  The result is the same
- * recurrence re-associated (up to rounding); the workspace holds the maps. */
+ * may be cut into segments of consecutive chunks, their count chosen by an
+ * estimate of each split's run time: every segment's memory update is an
+ * affine map S -> S A + B of its start state (the rows of S evolve
+ * independently, each by the same matrix A), so the maps of segments 1 ..
+ * n - 2 are formed in parallel beside segment 0's own read-out, composed in
+ * order, and segments 1 .. n - 1 then run their read-out from their own start
+ * states.  The result is the same recurrence re-associated (up to rounding);
+ * the workspace holds the maps. */
 int32_t kdn_forward_segments(const kdn_desc *d);
 
 /* Full layer forward (predict, gain, projection, chunkwise memory write and
