@@ -284,7 +284,9 @@ def bench_forward(args, inp, variant, steps, cold_reps, label):
     # between the kernels of a step would add packets of the runtime's own
     # there and slow the kernel that follows; a kernel repeated alone would
     # find other data in the caches than the one before it in the forward left.
-    reps, rounds = 10, max(3, steps // 10)
+    # At least 10 rounds: a kernel of a few us is a small difference of two
+    # prefixes whose run-to-run spread is of the same order.
+    reps, rounds = 10, max(10, steps // 10)
     kern_us = {k: [] for k in KERNELS}
     for _ in range(rounds):
         pre = []
